@@ -1,0 +1,240 @@
+/* moe.h — C ABI of the routed mixture-of-experts FFN library (libmoe.so).
+ *
+ * One routed MoE layer step on an AMD Instinct MI355X (gfx950):
+ *   moe_route       router logits, top-k, routing weights
+ *   moe_plan_union  expert-major union of the routed tokens
+ *   moe_slot_map    host LRU over a bounded pool of expert slots
+ *   moe_slot_fill   pinned-host -> slot copy on a side stream + page-table write
+ *   moe_expert_ffn  quantised SwiGLU experts read through the page table,
+ *                   shared expert, weighted combine
+ *
+ * Conventions for every entry point:
+ *  - Pointers named "device" are HIP device (or managed) memory; "host" is
+ *    ordinary host memory; "pinned" is host memory from hipHostMalloc.  All
+ *    buffers belong to the caller and must outlive the work enqueued on them.
+ *    The context owns only its page table, error word, workspace and events.
+ *  - Streams are hipStream_t values passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously; nothing waits for the GPU unless stated.
+ *  - Arguments are validated on the host before anything is enqueued: an
+ *    invalid call returns MOE_EINVAL and enqueues nothing.  HIP failures
+ *    return MOE_EHIP; moe_last_error() then holds the message.  Nothing
+ *    aborts, prints or throws across this boundary.
+ *  - Faults found on the device (an unmapped expert, a wait that gave up) set
+ *    the context's error word and make the affected output rows quiet NaN;
+ *    moe_check() reports them.
+ *  - A context is used by one host thread, and its calls are ordered on one
+ *    compute stream (plus side streams for fills); two calls that run at the
+ *    same time on different streams share its workspace and race.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_ctx moe_ctx;
+typedef void* moe_stream; /* hipStream_t */
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,   /* invalid argument; nothing was enqueued */
+    MOE_ENOMEM = -2,   /* device or host allocation failed */
+    MOE_EHIP = -3,     /* HIP runtime error (moe_last_error has the text) */
+    MOE_ENOSLOT = -4,  /* a step needs more slots than are free or unpinned */
+    MOE_EMISS = -5,    /* a kernel met an unmapped (layer, expert) page-table entry */
+    MOE_EBUSY = -6,    /* the slot is pinned by another (layer, expert) */
+    MOE_ETIMEOUT = -7  /* a kernel's bounded inter-workgroup wait gave up */
+} moe_status;
+
+enum { MOE_Q8_0 = 0, MOE_Q4_0 = 1 };          /* expert weight formats */
+enum { MOE_F32 = 0, MOE_BF16 = 1 };           /* activation element types */
+enum { MOE_PREC_F32 = 0, MOE_PREC_BF16 = 1 }; /* expert arithmetic modes (see moe_expert_ffn) */
+
+typedef struct moe_config {
+    int32_t n_layers;        /* routed layers sharing the slot pool (>= 1) */
+    int32_t n_experts;       /* routed experts per layer, 1..1024 */
+    int32_t top_k;           /* experts per token, 1..min(n_experts, 32) */
+    int32_t d_model;         /* model width; d_model/32 must be 1,2,4,..,64 */
+    int32_t d_ff;            /* expert hidden width; d_ff/32 must be 1,2,4,..,64 */
+    int32_t qtype;           /* MOE_Q8_0 or MOE_Q4_0 (routed and shared experts) */
+    int32_t n_slots;         /* slots in slot_pool (>= 1) */
+    int32_t max_tokens;      /* largest T of any call (sizes the workspace), 1..65536 */
+    int32_t norm_topk;       /* 1: weights = softmax over the k selected logits;
+                                0: weights = full softmax probability of each selected expert */
+    int32_t gemm_min_tokens; /* PREC_BF16 buckets with at least this many tokens use the
+                                MFMA grouped GEMM, smaller ones the GEMV (default 16; 0 = 16) */
+    int32_t device;          /* HIP device ordinal; -1 = host-only context (slot
+                                bookkeeping only; device entry points return MOE_EINVAL) */
+    int32_t reserved;        /* must be 0 */
+    void* slot_pool;         /* device, caller-owned, n_slots * moe_payload_bytes() bytes,
+                                256-byte aligned; NULL for a host-only context */
+} moe_config;
+
+/* Expert-major union ("Nanite for Experts", §5.3: experts are unioned across
+ * the tokens of a window and each distinct expert is scheduled once).  All
+ * device pointers, caller-owned; sizes from moe_plan_bytes(). */
+typedef struct moe_plan {
+    int32_t* n_active; /* [1]               number of distinct experts, A */
+    int32_t* experts;  /* [n_experts]       experts[0..A) ascending */
+    int32_t* offsets;  /* [n_experts + 1]   bucket a = entries[offsets[a] .. offsets[a+1]) */
+    int32_t* entries;  /* [max_tokens*top_k] t*top_k + j, ascending within each bucket */
+} moe_plan;
+
+/* ---- sizes and formats ------------------------------------------------- */
+
+/* Bytes of one expert's device payload (0 if cfg is invalid).  It equals the
+ * expert's GGUF block bytes: 34 (Q8_0) or 18 (Q4_0) bytes per 32 weights of
+ * gate [d_ff x d_model], up [d_ff x d_model] and down [d_model x d_ff].
+ *
+ * Payload layout (how slots hold an expert; "Nanite for Experts", §12 asks
+ * for cache geometry chosen with the kernels): each matrix's 32-element
+ * blocks, taken in row-major block order, are grouped into tiles of 64
+ * blocks.  A Q8_0 tile stores the first 16 codes of each of its 64 blocks
+ * (64 x 16 B), then the last 16 codes of each (64 x 16 B), then the 64 fp16
+ * scales (2176 B).  A Q4_0 tile stores each block's 16 nibble bytes in GGUF
+ * order (64 x 16 B), then the 64 scales (1152 B).  The payload is gate tile
+ * 0, up tile 0, gate tile 1, up tile 1, ..., then every down tile in order. */
+size_t moe_payload_bytes(const moe_config* cfg);
+
+/* Sizes in bytes of the moe_plan arrays for T tokens:
+ * out[0] n_active, out[1] experts, out[2] offsets, out[3] entries. */
+moe_status moe_plan_bytes(const moe_config* cfg, int64_t T, size_t out[4]);
+
+/* Host-side repack of one expert between GGUF blocks (gate, up, down, each
+ * row-major, blocks along rows: the per-(layer, expert) block of a split pack,
+ * "MawForge", §IV-B) and the device payload layout above.  Both buffers are
+ * host memory of moe_payload_bytes(cfg) bytes; nothing is enqueued. */
+moe_status moe_pack_expert(const moe_config* cfg, const void* gguf_blocks, void* payload);
+moe_status moe_unpack_expert(const moe_config* cfg, const void* payload, void* gguf_blocks);
+
+/* ---- context ------------------------------------------------------------ */
+
+/* Validates cfg, then (unless cfg->device == -1) allocates on that device the
+ * page table [n_layers x n_experts] int32, every entry -1 (the sentinel for an
+ * absent expert, "Nanite for Experts", §5.4), the error word and a workspace
+ * for max_tokens.  The slot pool stays the caller's. */
+moe_status moe_create(const moe_config* cfg, moe_ctx** out);
+/* Waits for the device, frees what moe_create allocated.  NULL is ignored. */
+void moe_destroy(moe_ctx* ctx);
+/* Text of the last failure on ctx (empty string if none); valid until the next call. */
+const char* moe_last_error(const moe_ctx* ctx);
+const char* moe_status_string(int status);
+
+/* ---- routing -------------------------------------------------------------- */
+
+/* Router decisions pick the experts; nothing else may change them ("Nanite for
+ * Experts", §3.1).  Per token t:
+ *   logits[t,e] = sum_i x[t,i] * w_router[e,i]   (fp32, fixed summation order)
+ *   ids[t,0..k) = the k largest logits, largest first, ties to the lower expert
+ *                 index (+0 and -0 equal)
+ *   w[t,j]      = exp(l_j - l_0) / sum_j' exp(l_j' - l_0) over the k selected
+ *                 (norm_topk = 1), or over all experts (norm_topk = 0).
+ * x: device [T, d_model] fp32 or bf16 (x_dtype).  w_router: device
+ * [n_experts, d_model] fp32.  Pass logits_in (device [T, n_experts] fp32, all
+ * finite) instead of x and w_router to route precomputed logits.
+ * topk_ids: device [T, top_k] int32; topk_w: device [T, top_k] fp32;
+ * logits_out: optional device [T, n_experts] fp32 (ignored with logits_in).
+ * 0 <= T <= max_tokens. */
+moe_status moe_route(moe_ctx* ctx, const void* x, int32_t x_dtype, const float* w_router,
+                     const float* logits_in, int64_t T, int32_t* topk_ids, float* topk_w,
+                     float* logits_out, moe_stream stream);
+
+/* Expert-major union of topk_ids (device [T, top_k], values in [0, n_experts)):
+ * a stable counting sort by expert id into *plan (device, caller-owned).
+ * Out-of-range ids set the error word and are dropped. */
+moe_status moe_plan_union(moe_ctx* ctx, const int32_t* topk_ids, int64_t T, const moe_plan* plan,
+                          moe_stream stream);
+
+/* ---- slots and page table ------------------------------------------------- */
+
+/* Bounded expert slots with route-to-slot metadata; a miss materialises the
+ * expert into a slot ("MawForge", §IV-C).  Entries stay pinned while their
+ * layer is evaluated ("Paging the Experts", §3.2).
+ *
+ * moe_slot_map: host only, no device work.  experts: host [n], distinct and
+ * ascending (e.g. the plan's experts copied back).  Each expert is touched
+ * once in that order: a mapped one is a hit; an unmapped one takes the lowest
+ * free slot, else the least recently touched unpinned slot (evicted).  Every
+ * listed expert is then pinned to `layer` until moe_slot_release(layer).
+ * slots_out: host [n]; miss_out: host [n], 1 where the caller must now call
+ * moe_slot_fill.  MOE_ENOSLOT (state unchanged) if misses exceed free plus
+ * unpinned slots. */
+moe_status moe_slot_map(moe_ctx* ctx, int32_t layer, const int32_t* experts, int32_t n,
+                        int32_t* slots_out, uint8_t* miss_out);
+
+/* Materialise a missed expert: on `side`, wait until every released reader of
+ * the slot has finished, mark the evicted expert's page-table entry absent,
+ * copy host_payload (pinned, moe_payload_bytes(), device payload layout) into
+ * the slot with hipMemcpyAsync, then write page_table[layer, expert] = slot
+ * and record a ready event ("Nanite for Experts", §3.4: asynchronous copies
+ * from pinned memory on non-default streams).  The next moe_expert_ffn waits
+ * for that event on its own stream.  (layer, expert) must be the slot's owner
+ * from moe_slot_map. */
+moe_status moe_slot_fill(moe_ctx* ctx, int32_t layer, int32_t expert, int32_t slot,
+                         const void* host_payload, moe_stream side);
+
+/* Unpin every slot pinned to `layer` and record, on `compute`, the point after
+ * which their readers are done (later fills into them wait for it). */
+moe_status moe_slot_release(moe_ctx* ctx, int32_t layer, moe_stream compute);
+
+/* Set page_table[layer, expert] = slot (-1 = absent) on `stream`, outside the
+ * LRU: the caller placed the payload itself.  MOE_EBUSY if the slot is pinned
+ * by another (layer, expert). */
+moe_status moe_slot_bind(moe_ctx* ctx, int32_t layer, int32_t expert, int32_t slot,
+                         moe_stream stream);
+
+/* ---- expert FFN ------------------------------------------------------------ */
+
+/* For every token t of the step:
+ *   y[t] = sum over its routed experts e (ascending e) of w[t,j] * FFN_e(x[t])
+ *          + FFN_shared(x[t])
+ *   FFN(x) = W_d (silu(W_g x) * (W_u x)),  silu(z) = z / (1 + exp(-z))
+ * with each expert read from its slot through page_table[layer, e] and the
+ * results merged into the tokens' own rows ("Nanite for Experts", §5.5), one
+ * launch over all experts of the step ("Nanite for Experts", §12).  The
+ * summation order depends only on expert ids and ranks, never on slots, so y
+ * is bitwise identical under any slot assignment.
+ * prec MOE_PREC_F32: weights dequantised exactly (d*q in fp32), fp32 hidden
+ *   state, fp32 accumulation.
+ * prec MOE_PREC_BF16: weights rounded to bf16 after dequantisation, x and the
+ *   hidden state rounded to bf16, fp32 accumulation; buckets of at least
+ *   gemm_min_tokens tokens run on the MFMA grouped GEMM, the others on the
+ *   GEMV, with the same roundings.
+ * x: device [T, d_model] (x_dtype).  plan: from moe_plan_union on the same
+ * topk ids.  topk_w: device [T, top_k] fp32.  shared_payload: device payload
+ * of the always-on shared expert ("Nanite for Experts", §1) or NULL.
+ * y: device [T, d_model] fp32.  Waits on `stream` for fills not yet awaited.
+ * Rows of tokens routed to an unmapped expert become NaN (MOE_EMISS at
+ * moe_check). */
+moe_status moe_expert_ffn(moe_ctx* ctx, int32_t layer, const void* x, int32_t x_dtype, int64_t T,
+                          const moe_plan* plan, const float* topk_w, const void* shared_payload,
+                          int32_t prec, float* y, moe_stream stream);
+
+/* ---- inspection ------------------------------------------------------------- */
+
+/* Dequantise one device payload into device out [3 * d_ff * d_model] fp32 in
+ * logical order: gate rows, up rows, down rows, each row-major.  prec
+ * MOE_PREC_F32 gives d*q exactly; MOE_PREC_BF16 gives it rounded to bf16. */
+moe_status moe_dequant(moe_ctx* ctx, const void* payload, int32_t prec, float* out,
+                       moe_stream stream);
+
+/* Counters since moe_create: out[0] hits, out[1] misses, out[2] bytes staged
+ * (= misses x payload bytes; "Paging the Experts", §4.2), out[3] evictions,
+ * out[4] fills enqueued. */
+moe_status moe_stats(const moe_ctx* ctx, uint64_t out[5]);
+
+/* Synchronise `stream`, read and clear the error word: MOE_OK, MOE_EMISS or
+ * MOE_ETIMEOUT. */
+moe_status moe_check(moe_ctx* ctx, moe_stream stream);
+
+/* Device address of the page table ([n_layers x n_experts] int32), for tests. */
+moe_status moe_page_table(const moe_ctx* ctx, int32_t** out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,509 @@
+// libmoe host side: context, argument validation, payload packing, the slot
+// manager (LRU with per-layer pins), page-table and fill ordering, dispatch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+using moe::Geom;
+
+struct moe_ctx {
+    moe_config cfg{};
+    Geom g;
+    bool host_only = true;
+    std::string err;
+
+    // device state
+    int32_t* pt = nullptr;     // [L x E]
+    int* err_word = nullptr;
+    unsigned* sync = nullptr;  // [2]
+    float* h = nullptr;        // [(max_T*k + max_T) * f]
+    float* logits_ws = nullptr;// [max_T * E]
+
+    // slot manager (host)
+    std::vector<int64_t> owner;     // slot -> key = layer*E + expert, or -1
+    std::vector<int32_t> slot_of;   // key -> slot, or -1
+    std::vector<uint64_t> last;     // recency stamp per slot
+    std::vector<int32_t> pin_layer; // layer pinning the slot, or -1
+    std::vector<int64_t> evicted;   // key evicted by the last map of this slot (fill invalidates it)
+    uint64_t clock = 0;
+    uint64_t stats[5] = {0, 0, 0, 0, 0};
+
+    // ordering
+    hipEvent_t release_ev = nullptr;  // last moe_slot_release point on the compute stream
+    bool release_recorded = false;
+    struct Pending { hipStream_t s; hipEvent_t ev; bool pending; };
+    std::vector<Pending> fills;       // one re-recorded event per side stream
+};
+
+namespace {
+
+moe_status fail(moe_ctx* c, moe_status st, const char* fmt, ...) __attribute__((format(printf, 3, 4)));
+moe_status fail(moe_ctx* c, moe_status st, const char* fmt, ...) {
+    if (c) {
+        char buf[512];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof buf, fmt, ap);
+        va_end(ap);
+        c->err = buf;
+    }
+    return st;
+}
+
+#define HIP_TRY(ctx, call)                                                                   \
+    do {                                                                                     \
+        hipError_t e_ = (call);                                                              \
+        if (e_ != hipSuccess)                                                                \
+            return fail((ctx), MOE_EHIP, "%s: %s (%s:%d)", #call, hipGetErrorString(e_),     \
+                        __FILE__, __LINE__);                                                 \
+    } while (0)
+
+bool cfg_valid(const moe_config* c, Geom* g, std::string* why) {
+    auto bad = [&](const char* m) { if (why) *why = m; return false; };
+    if (!c) return bad("null config");
+    if (c->n_layers < 1) return bad("n_layers must be >= 1");
+    if (c->n_experts < 1 || c->n_experts > 1024) return bad("n_experts must be in [1, 1024]");
+    if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > 32) return bad("top_k must be in [1, min(n_experts, 32)]");
+    if (c->n_slots < 1) return bad("n_slots must be >= 1");
+    if (c->max_tokens < 1 || c->max_tokens > 65536) return bad("max_tokens must be in [1, 65536]");
+    if (c->norm_topk != 0 && c->norm_topk != 1) return bad("norm_topk must be 0 or 1");
+    if (c->gemm_min_tokens < 0) return bad("gemm_min_tokens must be >= 0");
+    if (c->reserved != 0) return bad("reserved must be 0");
+    if (c->device < -1) return bad("device must be >= -1");
+    if ((int64_t)c->n_layers * c->n_experts > (1 << 26)) return bad("n_layers * n_experts too large");
+    Geom gg;
+    if (!gg.init(c->d_model, c->d_ff, c->qtype))
+        return bad("unsupported shape or qtype: d_model/32 and d_ff/32 must be powers of two <= 64, "
+                   "with whole 64-block tiles; qtype Q8_0 or Q4_0");
+    if (c->device >= 0) {
+        if (!c->slot_pool) return bad("slot_pool is NULL");
+        if (((uintptr_t)c->slot_pool) & 255) return bad("slot_pool must be 256-byte aligned");
+    }
+    if (g) *g = gg;
+    return true;
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    explicit DeviceGuard(int dev) {
+        if (dev >= 0 && hipGetDevice(&prev) == hipSuccess && prev != dev) {
+            changed = hipSetDevice(dev) == hipSuccess;
+        }
+    }
+    ~DeviceGuard() { if (changed) (void)hipSetDevice(prev); }
+};
+
+moe_status need_device(moe_ctx* c) {
+    if (!c) return MOE_EINVAL;
+    if (c->host_only) return fail(c, MOE_EINVAL, "host-only context has no device state");
+    return MOE_OK;
+}
+
+// Q8_0 / Q4_0 repack between GGUF blocks and the tile layout.
+void repack(const Geom& g, const uint8_t* src, uint8_t* dst, bool to_tiles) {
+    const int bb = moe::block_bytes(g.qtype);
+    struct Mat { int64_t rows, nb; int64_t first_tile; int64_t stride; int64_t gguf_off; };
+    const int64_t mat_gguf = (int64_t)g.f * g.nb_d * bb; // bytes of gate (= up) in GGUF order
+    // tile t of matrix m lives at payload offset m.first_tile + t * m.stride
+    Mat mats[3] = {
+        {g.f, g.nb_d, 0, 2 * g.tile_bytes, 0},
+        {g.f, g.nb_d, g.tile_bytes, 2 * g.tile_bytes, mat_gguf},
+        {g.d, g.nb_f, 2 * g.gu_tiles * g.tile_bytes, g.tile_bytes, 2 * mat_gguf},
+    };
+    for (const Mat& m : mats) {
+        const int64_t nblk = m.rows * m.nb;
+        for (int64_t L = 0; L < nblk; L++) {
+            const int64_t t = L / moe::kTileBlocks;
+            const int i = (int)(L % moe::kTileBlocks);
+            uint8_t* tile = nullptr;
+            const uint8_t* ctile = nullptr;
+            const int64_t toff = m.first_tile + t * m.stride;
+            const int64_t goff = m.gguf_off + L * bb;
+            if (to_tiles) tile = dst + toff; else ctile = src + toff;
+            const uint8_t* gsrc = to_tiles ? src + goff : nullptr;
+            uint8_t* gdst = to_tiles ? nullptr : dst + goff;
+            if (g.qtype == MOE_Q8_0) {
+                if (to_tiles) {
+                    memcpy(tile + moe::q8_scale(i), gsrc, 2);
+                    memcpy(tile + moe::q8_lo(i), gsrc + 2, 16);
+                    memcpy(tile + moe::q8_hi(i), gsrc + 18, 16);
+                } else {
+                    memcpy(gdst, ctile + moe::q8_scale(i), 2);
+                    memcpy(gdst + 2, ctile + moe::q8_lo(i), 16);
+                    memcpy(gdst + 18, ctile + moe::q8_hi(i), 16);
+                }
+            } else {
+                if (to_tiles) {
+                    memcpy(tile + moe::q4_scale(i), gsrc, 2);
+                    memcpy(tile + moe::q4_nib(i), gsrc + 2, 16);
+                } else {
+                    memcpy(gdst, ctile + moe::q4_scale(i), 2);
+                    memcpy(gdst + 2, ctile + moe::q4_nib(i), 16);
+                }
+            }
+        }
+    }
+}
+
+moe_status wait_pending_fills(moe_ctx* c, hipStream_t s) {
+    for (auto& p : c->fills) {
+        if (p.pending && p.s != s) HIP_TRY(c, hipStreamWaitEvent(s, p.ev, 0));
+        p.pending = false;
+    }
+    return MOE_OK;
+}
+
+constexpr int kSpinLimit = 1 << 22;
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int st) {
+    switch (st) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_ENOMEM: return "out of memory";
+        case MOE_EHIP: return "HIP error";
+        case MOE_ENOSLOT: return "no free or unpinned slot";
+        case MOE_EMISS: return "unmapped expert met by a kernel";
+        case MOE_EBUSY: return "slot pinned by another expert";
+        case MOE_ETIMEOUT: return "kernel wait timed out";
+        default: return "unknown status";
+    }
+}
+
+size_t moe_payload_bytes(const moe_config* cfg) {
+    Geom g;
+    if (!cfg || !g.init(cfg->d_model, cfg->d_ff, cfg->qtype)) return 0;
+    return (size_t)g.payload;
+}
+
+moe_status moe_plan_bytes(const moe_config* cfg, int64_t T, size_t out[4]) {
+    if (!cfg || !out || T < 0 || !cfg_valid(cfg, nullptr, nullptr)) return MOE_EINVAL;
+    out[0] = sizeof(int32_t);
+    out[1] = sizeof(int32_t) * (size_t)cfg->n_experts;
+    out[2] = sizeof(int32_t) * ((size_t)cfg->n_experts + 1);
+    out[3] = sizeof(int32_t) * (size_t)std::max<int64_t>(1, T * cfg->top_k);
+    return MOE_OK;
+}
+
+moe_status moe_pack_expert(const moe_config* cfg, const void* gguf_blocks, void* payload) {
+    Geom g;
+    if (!cfg || !gguf_blocks || !payload || !g.init(cfg->d_model, cfg->d_ff, cfg->qtype)) return MOE_EINVAL;
+    repack(g, (const uint8_t*)gguf_blocks, (uint8_t*)payload, true);
+    return MOE_OK;
+}
+
+moe_status moe_unpack_expert(const moe_config* cfg, const void* payload, void* gguf_blocks) {
+    Geom g;
+    if (!cfg || !gguf_blocks || !payload || !g.init(cfg->d_model, cfg->d_ff, cfg->qtype)) return MOE_EINVAL;
+    repack(g, (const uint8_t*)payload, (uint8_t*)gguf_blocks, false);
+    return MOE_OK;
+}
+
+void moe_destroy(moe_ctx* c) {
+    if (!c) return;
+    if (!c->host_only) {
+        DeviceGuard dg(c->cfg.device);
+        (void)hipDeviceSynchronize();
+        if (c->pt) (void)hipFree(c->pt);
+        if (c->err_word) (void)hipFree(c->err_word);
+        if (c->sync) (void)hipFree(c->sync);
+        if (c->h) (void)hipFree(c->h);
+        if (c->logits_ws) (void)hipFree(c->logits_ws);
+        if (c->release_ev) (void)hipEventDestroy(c->release_ev);
+        for (auto& p : c->fills) (void)hipEventDestroy(p.ev);
+    }
+    delete c;
+}
+
+moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
+    if (!out) return MOE_EINVAL;
+    *out = nullptr;
+    Geom g;
+    std::string why;
+    if (!cfg_valid(cfg, &g, &why)) return MOE_EINVAL;
+    moe_ctx* c = new (std::nothrow) moe_ctx();
+    if (!c) return MOE_ENOMEM;
+    c->cfg = *cfg;
+    if (c->cfg.gemm_min_tokens == 0) c->cfg.gemm_min_tokens = 16;
+    c->g = g;
+    c->host_only = cfg->device < 0;
+    const int64_t n_keys = (int64_t)cfg->n_layers * cfg->n_experts;
+    c->owner.assign(cfg->n_slots, -1);
+    c->slot_of.assign(n_keys, -1);
+    c->last.assign(cfg->n_slots, 0);
+    c->pin_layer.assign(cfg->n_slots, -1);
+    c->evicted.assign(cfg->n_slots, -1);
+    if (!c->host_only) {
+        DeviceGuard dg(cfg->device);
+        auto cleanup = [&](moe_status st) { moe_destroy(c); return st; };
+        int ndev = 0;
+        if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device >= ndev) return cleanup(MOE_EINVAL);
+        const int64_t T = cfg->max_tokens;
+        if (hipMalloc(&c->pt, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_ENOMEM);
+        if (hipMalloc(&c->err_word, sizeof(int)) != hipSuccess) return cleanup(MOE_ENOMEM);
+        if (hipMalloc(&c->sync, 4 * sizeof(unsigned)) != hipSuccess) return cleanup(MOE_ENOMEM);
+        if (hipMalloc(&c->h, sizeof(float) * (size_t)(T * cfg->top_k + T) * cfg->d_ff) != hipSuccess)
+            return cleanup(MOE_ENOMEM);
+        if (hipMalloc(&c->logits_ws, sizeof(float) * (size_t)T * cfg->n_experts) != hipSuccess)
+            return cleanup(MOE_ENOMEM);
+        if (hipMemset(c->pt, 0xFF, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_EHIP);
+        if (hipMemset(c->err_word, 0, sizeof(int)) != hipSuccess) return cleanup(MOE_EHIP);
+        if (hipMemset(c->sync, 0, 4 * sizeof(unsigned)) != hipSuccess) return cleanup(MOE_EHIP);
+        if (hipEventCreateWithFlags(&c->release_ev, hipEventDisableTiming) != hipSuccess) return cleanup(MOE_EHIP);
+        if (hipDeviceSynchronize() != hipSuccess) return cleanup(MOE_EHIP);
+    }
+    *out = c;
+    return MOE_OK;
+}
+
+const char* moe_last_error(const moe_ctx* c) { return c ? c->err.c_str() : ""; }
+
+moe_status moe_route(moe_ctx* c, const void* x, int32_t x_dtype, const float* w_router,
+                     const float* logits_in, int64_t T, int32_t* topk_ids, float* topk_w,
+                     float* logits_out, moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (T < 0 || T > cf.max_tokens) return fail(c, MOE_EINVAL, "moe_route: T=%lld outside [0, %d]", (long long)T, cf.max_tokens);
+    if (T == 0) return MOE_OK;
+    if (!topk_ids || !topk_w) return fail(c, MOE_EINVAL, "moe_route: null output");
+    if (!logits_in) {
+        if (!x || !w_router) return fail(c, MOE_EINVAL, "moe_route: need logits_in or both x and w_router");
+        if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(c, MOE_EINVAL, "moe_route: bad x_dtype");
+    }
+    DeviceGuard dg(cf.device);
+    hipStream_t s = (hipStream_t)stream;
+    const float* logits = logits_in;
+    if (!logits_in) {
+        float* lo = logits_out ? logits_out : c->logits_ws;
+        HIP_TRY(c, moe::launch_router_gemv(x, x_dtype == MOE_BF16, w_router, T, cf.n_experts, cf.d_model, lo, s));
+        logits = lo;
+    }
+    HIP_TRY(c, moe::launch_topk(logits, T, cf.n_experts, cf.top_k, cf.norm_topk, topk_ids, topk_w, s));
+    return MOE_OK;
+}
+
+moe_status moe_plan_union(moe_ctx* c, const int32_t* topk_ids, int64_t T, const moe_plan* plan,
+                          moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (T < 0 || T > cf.max_tokens) return fail(c, MOE_EINVAL, "moe_plan_union: T outside [0, max_tokens]");
+    if (!plan || !plan->n_active || !plan->experts || !plan->offsets || !plan->entries)
+        return fail(c, MOE_EINVAL, "moe_plan_union: null plan array");
+    if (T > 0 && !topk_ids) return fail(c, MOE_EINVAL, "moe_plan_union: null topk_ids");
+    DeviceGuard dg(cf.device);
+    HIP_TRY(c, moe::launch_plan(topk_ids, T, cf.top_k, cf.n_experts, *plan, c->err_word, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+moe_status moe_slot_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n,
+                        int32_t* slots_out, uint8_t* miss_out) {
+    if (!c) return MOE_EINVAL;
+    const moe_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers) return fail(c, MOE_EINVAL, "moe_slot_map: bad layer");
+    if (n < 0 || n > cf.n_experts) return fail(c, MOE_EINVAL, "moe_slot_map: bad n");
+    if (n > 0 && (!experts || !slots_out || !miss_out)) return fail(c, MOE_EINVAL, "moe_slot_map: null array");
+    for (int32_t i = 0; i < n; i++) {
+        if (experts[i] < 0 || experts[i] >= cf.n_experts) return fail(c, MOE_EINVAL, "moe_slot_map: expert id out of range");
+        if (i && experts[i] <= experts[i - 1]) return fail(c, MOE_EINVAL, "moe_slot_map: experts must be ascending and distinct");
+    }
+    const int64_t base = (int64_t)layer * cf.n_experts;
+    // capacity check first, so a refused step changes nothing
+    int need = 0;
+    std::vector<char> is_hit_slot(cf.n_slots, 0);
+    for (int32_t i = 0; i < n; i++) {
+        int32_t s = c->slot_of[base + experts[i]];
+        if (s < 0) need++; else is_hit_slot[s] = 1;
+    }
+    int avail = 0;
+    for (int s = 0; s < cf.n_slots; s++) avail += (c->pin_layer[s] < 0 && !is_hit_slot[s]);
+    if (need > avail) return fail(c, MOE_ENOSLOT, "moe_slot_map: %d misses but %d free or unpinned slots", need, avail);
+    for (int32_t i = 0; i < n; i++) {
+        const int64_t key = base + experts[i];
+        c->clock++;
+        int32_t s = c->slot_of[key];
+        if (s >= 0) {
+            c->stats[0]++;
+            miss_out[i] = 0;
+        } else {
+            int32_t pick = -1;
+            for (int q = 0; q < cf.n_slots; q++) if (c->owner[q] < 0) { pick = q; break; }
+            if (pick < 0) {
+                uint64_t best = UINT64_MAX;
+                for (int q = 0; q < cf.n_slots; q++)
+                    if (c->pin_layer[q] < 0 && c->last[q] < best) { best = c->last[q]; pick = q; }
+                c->slot_of[c->owner[pick]] = -1;
+                c->evicted[pick] = c->owner[pick];
+                c->stats[3]++;
+            } else {
+                c->evicted[pick] = -1;
+            }
+            s = pick;
+            c->owner[s] = key;
+            c->slot_of[key] = s;
+            c->stats[1]++;
+            c->stats[2] += (uint64_t)c->g.payload;
+            miss_out[i] = 1;
+        }
+        c->last[s] = c->clock;
+        c->pin_layer[s] = layer;
+        slots_out[i] = s;
+    }
+    return MOE_OK;
+}
+
+moe_status moe_slot_fill(moe_ctx* c, int32_t layer, int32_t expert, int32_t slot,
+                         const void* host_payload, moe_stream side) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers || expert < 0 || expert >= cf.n_experts || slot < 0 || slot >= cf.n_slots)
+        return fail(c, MOE_EINVAL, "moe_slot_fill: index out of range");
+    if (!host_payload) return fail(c, MOE_EINVAL, "moe_slot_fill: null payload");
+    const int64_t key = (int64_t)layer * cf.n_experts + expert;
+    if (c->owner[slot] != key) return fail(c, MOE_EINVAL, "moe_slot_fill: slot %d is not mapped to (layer %d, expert %d)", slot, layer, expert);
+    DeviceGuard dg(cf.device);
+    hipStream_t s = (hipStream_t)side;
+    if (c->release_recorded) HIP_TRY(c, hipStreamWaitEvent(s, c->release_ev, 0));
+    if (c->evicted[slot] >= 0) {
+        HIP_TRY(c, hipMemsetD32Async((hipDeviceptr_t)(c->pt + c->evicted[slot]), -1, 1, s));
+        c->evicted[slot] = -1;
+    }
+    uint8_t* dst = (uint8_t*)cf.slot_pool + (size_t)slot * (size_t)c->g.payload;
+    HIP_TRY(c, hipMemcpyAsync(dst, host_payload, (size_t)c->g.payload, hipMemcpyHostToDevice, s));
+    HIP_TRY(c, hipMemsetD32Async((hipDeviceptr_t)(c->pt + key), slot, 1, s));
+    moe_ctx::Pending* p = nullptr;
+    for (auto& q : c->fills) if (q.s == s) p = &q;
+    if (!p) {
+        hipEvent_t ev;
+        HIP_TRY(c, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+        c->fills.push_back({s, ev, false});
+        p = &c->fills.back();
+    }
+    HIP_TRY(c, hipEventRecord(p->ev, s));
+    p->pending = true;
+    c->stats[4]++;
+    return MOE_OK;
+}
+
+moe_status moe_slot_release(moe_ctx* c, int32_t layer, moe_stream compute) {
+    if (!c) return MOE_EINVAL;
+    const moe_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers) return fail(c, MOE_EINVAL, "moe_slot_release: bad layer");
+    for (int s = 0; s < cf.n_slots; s++) if (c->pin_layer[s] == layer) c->pin_layer[s] = -1;
+    if (!c->host_only) {
+        DeviceGuard dg(cf.device);
+        HIP_TRY(c, hipEventRecord(c->release_ev, (hipStream_t)compute));
+        c->release_recorded = true;
+    }
+    return MOE_OK;
+}
+
+moe_status moe_slot_bind(moe_ctx* c, int32_t layer, int32_t expert, int32_t slot, moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers || expert < 0 || expert >= cf.n_experts || slot < -1 || slot >= cf.n_slots)
+        return fail(c, MOE_EINVAL, "moe_slot_bind: index out of range");
+    const int64_t key = (int64_t)layer * cf.n_experts + expert;
+    if (slot >= 0 && c->pin_layer[slot] >= 0 && c->owner[slot] != key)
+        return fail(c, MOE_EBUSY, "moe_slot_bind: slot %d is pinned by another expert", slot);
+    DeviceGuard dg(cf.device);
+    HIP_TRY(c, hipMemsetD32Async((hipDeviceptr_t)(c->pt + key), slot, 1, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dtype, int64_t T,
+                          const moe_plan* plan, const float* topk_w, const void* shared_payload,
+                          int32_t prec, float* y, moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers) return fail(c, MOE_EINVAL, "moe_expert_ffn: bad layer");
+    if (T < 0 || T > cf.max_tokens) return fail(c, MOE_EINVAL, "moe_expert_ffn: T outside [0, max_tokens]");
+    if (prec != MOE_PREC_F32 && prec != MOE_PREC_BF16) return fail(c, MOE_EINVAL, "moe_expert_ffn: bad prec");
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(c, MOE_EINVAL, "moe_expert_ffn: bad x_dtype");
+    if (T > 0 && (!x || !plan || !plan->n_active || !plan->experts || !plan->offsets || !plan->entries || !topk_w || !y))
+        return fail(c, MOE_EINVAL, "moe_expert_ffn: null argument");
+    DeviceGuard dg(cf.device);
+    hipStream_t s = (hipStream_t)stream;
+    if (moe_status st = wait_pending_fills(c, s)) return st;
+    if (T == 0) return MOE_OK;
+    moe::FfnArgs a{};
+    a.pool = (const uint8_t*)cf.slot_pool;
+    a.payload_bytes = c->g.payload;
+    a.pt = c->pt;
+    a.layer = layer;
+    a.E = cf.n_experts;
+    a.n_slots = cf.n_slots;
+    a.shared = (const uint8_t*)shared_payload;
+    a.n_active = plan->n_active;
+    a.experts = plan->experts;
+    a.offsets = plan->offsets;
+    a.entries = plan->entries;
+    a.topk_w = topk_w;
+    a.k = cf.top_k;
+    a.x = x;
+    a.x_bf16 = x_dtype == MOE_BF16;
+    a.T = (int)T;
+    a.h = c->h;
+    a.y = y;
+    a.sync = c->sync;
+    a.err = c->err_word;
+    a.spin_limit = kSpinLimit;
+    if (T <= moe::kDecodeMaxT) {
+        HIP_TRY(c, moe::launch_ffn_decode(c->g, a, prec, s));
+        return MOE_OK;
+    }
+    return fail(c, MOE_EINVAL, "moe_expert_ffn: T > %d not available yet", moe::kDecodeMaxT);
+}
+
+moe_status moe_dequant(moe_ctx* c, const void* payload, int32_t prec, float* out, moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    if (!payload || !out) return fail(c, MOE_EINVAL, "moe_dequant: null argument");
+    if (prec != MOE_PREC_F32 && prec != MOE_PREC_BF16) return fail(c, MOE_EINVAL, "moe_dequant: bad prec");
+    DeviceGuard dg(c->cfg.device);
+    HIP_TRY(c, moe::launch_dequant(c->g, (const uint8_t*)payload, prec, out, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+moe_status moe_stats(const moe_ctx* c, uint64_t out[5]) {
+    if (!c || !out) return MOE_EINVAL;
+    for (int i = 0; i < 5; i++) out[i] = c->stats[i];
+    return MOE_OK;
+}
+
+moe_status moe_check(moe_ctx* c, moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    DeviceGuard dg(c->cfg.device);
+    hipStream_t s = (hipStream_t)stream;
+    HIP_TRY(c, hipStreamSynchronize(s));
+    int w = 0;
+    HIP_TRY(c, hipMemcpy(&w, c->err_word, sizeof(int), hipMemcpyDeviceToHost));
+    if (!w) return MOE_OK;
+    HIP_TRY(c, hipMemset(c->err_word, 0, sizeof(int)));
+    if (w & moe::kErrTimeout) {
+        // a wait gave up: the inter-workgroup counters may be left mid-count
+        HIP_TRY(c, hipMemset(c->sync, 0, 4 * sizeof(unsigned)));
+        HIP_TRY(c, hipDeviceSynchronize());
+        return fail(c, MOE_ETIMEOUT, "a kernel's inter-workgroup wait gave up (error word 0x%x)", w);
+    }
+    if (w & moe::kErrMiss) return fail(c, MOE_EMISS, "a kernel met an unmapped expert (error word 0x%x)", w);
+    return fail(c, MOE_EINVAL, "a plan input held an expert id out of range (error word 0x%x)", w);
+}
+
+moe_status moe_page_table(const moe_ctx* c, int32_t** out) {
+    if (!c || !out || c->host_only) return MOE_EINVAL;
+    *out = c->pt;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+// Expert-major union of the routed tokens ("Nanite for Experts", §5.3: the
+// expert ids of a multi-token window are unioned and each distinct expert is
+// scheduled once; §11.3: the union removes redundant work before any kernel).
+//
+// One workgroup of 1024 threads does a stable counting sort of the T*k
+// assignments by expert id, entirely in LDS:
+//   1. W waves each own a contiguous segment of the assignments and count it
+//      into their own LDS histogram row (integer LDS atomics; counts only).
+//   2. Per expert, the rows are turned into exclusive per-segment offsets.
+//   3. A block-wide prefix scan gives each expert's bucket start and its rank
+//      among the experts present; experts[], offsets[] and n_active are written.
+//   4. Each wave walks its segment 64 entries at a time; an entry's place is
+//      bucket start + its segment offset + the number of earlier lanes of the
+//      same 64 holding the same expert (found with wave ballots).  Segments
+//      are in entry order and lanes in entry order, so buckets list entries
+//      ascending: the result is unique and bit-reproducible.
+#include "device_util.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kHistInts = 8192;  // LDS ints for the per-wave histograms
+
+__device__ inline int block_exclusive_scan(int v, int* wave_tot, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int n = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += n;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        int t = lane < kThreads / 64 ? wave_tot[lane] : 0;
+        int ti = t;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            int n = __shfl_up(ti, o, 64);
+            if (lane >= o) ti += n;
+        }
+        if (lane < kThreads / 64) wave_tot[lane] = ti - t;  // exclusive wave offsets
+        if (lane == kThreads / 64 - 1) *total = ti;
+    }
+    __syncthreads();
+    int r = wave_tot[wave] + incl - v;
+    __syncthreads();
+    return r;
+}
+
+__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restrict__ ids, int N, int E,
+                                                        int32_t* __restrict__ n_active,
+                                                        int32_t* __restrict__ experts,
+                                                        int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ entries, int* err) {
+    __shared__ int hist[kHistInts];  // [W][E]
+    __shared__ int start[1024];      // bucket start per expert
+    __shared__ int wave_tot[kThreads / 64];
+    __shared__ int total_n, total_a;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int W = kHistInts / E;
+    if (W > kThreads / 64) W = kThreads / 64;
+    const int seg = (N + W - 1) / W;
+
+    for (int i = threadIdx.x; i < W * E; i += kThreads) hist[i] = 0;
+    __syncthreads();
+    if (wave < W) {
+        const int lo = wave * seg, hi = min(N, lo + seg);
+        for (int i = lo + lane; i < hi; i += 64) {
+            const int e = ids[i];
+            if (e >= 0 && e < E) atomicAdd(&hist[wave * E + e], 1);
+            else atomicOr(err, kErrBadId);
+        }
+    }
+    __syncthreads();
+    // per expert (E <= 1024 = one thread each): exclusive offsets of each segment inside the bucket
+    {
+        const int e = threadIdx.x;
+        int cnt = 0;
+        if (e < E) {
+            for (int w = 0; w < W; w++) {
+                const int c = hist[w * E + e];
+                hist[w * E + e] = cnt;
+                cnt += c;
+            }
+        }
+        const int first = block_exclusive_scan(cnt, wave_tot, &total_n);
+        const int rank = block_exclusive_scan(cnt > 0 ? 1 : 0, wave_tot, &total_a);
+        if (e < E) {
+            start[e] = first;
+            if (cnt > 0) {
+                experts[rank] = e;
+                offsets[rank] = first;
+            }
+        }
+    }
+    if (threadIdx.x == 0) {
+        *n_active = total_a;
+        offsets[total_a] = total_n;
+    }
+    __syncthreads();
+    // stable scatter
+    if (wave < W) {
+        const int lo = wave * seg, hi = min(N, lo + seg);
+        const uint64_t lt = (1ull << lane) - 1ull;
+        for (int i0 = lo; i0 < hi; i0 += 64) {
+            const int i = i0 + lane;
+            const bool valid = i < hi;
+            int e = valid ? ids[i] : -1;
+            const bool ok = valid && e >= 0 && e < E;
+            if (!ok) e = -1;
+            uint64_t mine = 0;
+            uint64_t rem = __ballot(ok);
+            while (rem) {
+                const int leader = __ffsll((unsigned long long)rem) - 1;
+                const int ve = __shfl(e, leader, 64);
+                const uint64_t m = __ballot(ok && e == ve);
+                if (ok && e == ve) mine = m;
+                rem &= ~m;
+            }
+            int pos = 0;
+            if (ok) pos = start[e] + hist[wave * E + e] + __popcll(mine & lt);
+            if (ok) {
+                entries[pos] = i;
+                if ((mine >> lane) == 1ull)  // highest lane holding this expert
+                    hist[wave * E + e] += __popcll(mine);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const int32_t* ids, int64_t T, int k, int E, const moe_plan& plan, int* err,
+                       hipStream_t s) {
+    const int N = (int)(T * k);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, s, ids, N, E, plan.n_active, plan.experts,
+                       plan.offsets, plan.entries, err);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: exported symbols, payload repacking, the host
+slot manager against the oracle's LRU model, and argument validation."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle.lru import LruModel, NoSlot
+from routed_expert_execution_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = _declared_symbols()
+    assert len(syms) >= 19
+    lib = moe.library()
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert sorted(moe.EXPORTS) == syms
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "mtp"])
+def test_pack_unpack_round_trip(name):
+    wl = synth.workload(name)
+    cfg = moe.make_config(1, wl["E"], wl["k"], wl["d"], wl["f"], wl["qtype"], 4, 4, device=-1)
+    n = moe.moe_payload_bytes(cfg)
+    assert n == synth.expert_record_bytes(wl["qtype"], wl["d"], wl["f"])
+    rec = synth.expert_record(wl["seed"], 0, 7, wl["qtype"], wl["d"], wl["f"])
+    pay = moe.moe_pack_expert(cfg, rec)
+    assert not np.array_equal(pay, rec)  # really re-laid
+    assert np.array_equal(moe.moe_unpack_expert(cfg, pay), rec)
+
+
+def test_payload_sizes_of_the_workloads():
+    """Q8_0 3,342,336 B and Q4_0 1,769,472 B per 2048x512 expert; both whole 64 KiB multiples."""
+    for qt, expect in ((moe.MOE_Q8_0, 3342336), (moe.MOE_Q4_0, 1769472)):
+        cfg = moe.make_config(1, 256, 8, 2048, 512, qt, 1, 1, device=-1)
+        assert moe.moe_payload_bytes(cfg) == expect and expect % 65536 == 0
+
+
+def _host_ctx(n_layers, E, n_slots, qtype=moe.MOE_Q8_0):
+    return moe.Context(n_layers, E, 8, 2048, 512, qtype, n_slots, 1, device=-1)
+
+
+def test_slot_manager_matches_lru_model_on_markov_trace():
+    """40 layers x 64 tokens of the stack workload's route chains through a 1,536-slot pool,
+    then a tighter 96-slot pool: every slot, miss and counter matches the model."""
+    wl = synth.workload("stack40")
+    for n_slots, n_layers, n_tok in ((1536, 40, 64), (96, 12, 40)):
+        ctx = _host_ctx(n_layers, wl["E"], n_slots)
+        model = LruModel(n_slots, ctx.payload_bytes)
+        chains = [synth.markov_route_sets(synth.rng(wl["seed"], 77, l), n_tok, wl["E"], wl["k"], wl["p_repeat"])
+                  for l in range(n_layers)]
+        for t in range(n_tok):
+            for l in range(n_layers):
+                ex = chains[l][t]
+                slots, miss = moe.moe_slot_map(ctx, l, ex)
+                ms, mm, _ = model.map(l, ex)
+                assert list(slots) == ms and list(miss) == mm
+                moe.moe_slot_release(ctx, l)
+                model.release(l)
+        st = moe.moe_stats(ctx)
+        c = model.counters()
+        assert (st["hits"], st["misses"], st["evictions"], st["bytes_staged"]) == \
+               (c["hits"], c["misses"], c["evictions"], c["bytes_staged"])
+        assert st["bytes_staged"] == st["misses"] * ctx.payload_bytes
+
+
+def test_slot_manager_refuses_when_pinned_full():
+    ctx = _host_ctx(2, 16, 3)
+    moe.moe_slot_map(ctx, 0, [1, 2, 3])
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_slot_map(ctx, 1, [4])
+    assert ei.value.status == moe.MOE_ENOSLOT
+    moe.moe_slot_release(ctx, 0)
+    slots, miss = moe.moe_slot_map(ctx, 1, [4])
+    assert list(slots) == [0] and list(miss) == [True]
+
+
+def test_slot_map_validation():
+    ctx = _host_ctx(1, 16, 4)
+    for bad in ([3, 3], [5, 2], [16], [-1]):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_slot_map(ctx, 0, bad)
+        assert ei.value.status == moe.MOE_EINVAL
+    with pytest.raises(moe.MoeError):
+        moe.moe_slot_map(ctx, 1, [0])  # layer out of range
+    assert moe.moe_stats(ctx)["misses"] == 0
+
+
+def test_host_only_context_rejects_device_calls():
+    ctx = _host_ctx(1, 16, 4)
+    lib = moe.library()
+    assert lib.moe_route(ctx.handle, None, 0, None, None, 1, None, None, None, None) == moe.MOE_EINVAL
+    assert lib.moe_check(ctx.handle, None) == moe.MOE_EINVAL
+    assert lib.moe_slot_fill(ctx.handle, 0, 0, 0, None, None) == moe.MOE_EINVAL
+    assert lib.moe_dequant(ctx.handle, None, 0, None, None) == moe.MOE_EINVAL
+
+
+@pytest.mark.parametrize("field,value", [("d_model", 96), ("d_ff", 100), ("top_k", 0), ("top_k", 33),
+                                         ("n_experts", 2000), ("qtype", 5), ("max_tokens", 0),
+                                         ("n_slots", 0), ("reserved", 1), ("norm_topk", 2)])
+def test_create_rejects_bad_configs(field, value):
+    cfg = moe.make_config(1, 256, 8, 2048, 512, moe.MOE_Q8_0, 4, 4, device=-1)
+    setattr(cfg, field, value)
+    h = C.c_void_p()
+    assert moe.library().moe_create(C.byref(cfg), C.byref(h)) == moe.MOE_EINVAL
+    assert h.value is None
+
+
+def test_device_config_needs_an_aligned_pool():
+    cfg = moe.make_config(1, 256, 8, 2048, 512, moe.MOE_Q8_0, 4, 4, device=0, slot_pool=None)
+    h = C.c_void_p()
+    assert moe.library().moe_create(C.byref(cfg), C.byref(h)) == moe.MOE_EINVAL
+    cfg.slot_pool = 0x1000010  # not 256-byte aligned
+    assert moe.library().moe_create(C.byref(cfg), C.byref(h)) == moe.MOE_EINVAL
+
+
+def test_plan_bytes():
+    cfg = moe.make_config(1, 256, 8, 2048, 512, moe.MOE_Q8_0, 4, 512, device=-1)
+    out = (C.c_size_t * 4)()
+    assert moe.library().moe_plan_bytes(C.byref(cfg), 512, out) == 0
+    assert list(out) == [4, 1024, 1028, 4 * 4096]
