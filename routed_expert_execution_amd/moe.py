@@ -43,6 +43,10 @@ class moe_plan(C.Structure):
 
 
 def _load() -> C.CDLL:
+    # torch ships its own HIP runtime.  Loading torch first makes libmoe's
+    # libamdhip64.so.7 dependency resolve (by soname) to that same runtime;
+    # the other order maps two HIP/HSA runtimes into the process.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m routed_expert_execution_amd.build`")
     lib = C.CDLL(LIB_PATH)

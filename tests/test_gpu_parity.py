@@ -103,12 +103,17 @@ def test_route_from_router_weights(name, T):
     r_ids, r_w = oracle.topk(g_lo, wl["k"])
     assert np.array_equal(g_ids, r_ids)
     np.testing.assert_allclose(g_w, r_w, rtol=1e-6, atol=1e-7)
-    # (ii) end to end: identical ids wherever the oracle's k-th gap exceeds the band
+    # (ii) end to end.  eps_t = this token's largest |gpu - oracle| logit difference
+    # (itself within the rounding band above).  Where every consecutive gap among the
+    # oracle's k+1 largest logits exceeds 2 eps_t, no perturbation of that size can
+    # change the ranked ids, so they must be identical; other tokens have several
+    # correct answers and are covered by (i).
     o_ids, _ = oracle.topk(o_lo, wl["k"])
-    srt = -np.sort(-o_lo.astype(np.float64), axis=1)
-    gap = srt[:, wl["k"] - 1] - srt[:, wl["k"]]
-    clear = gap > 2 * band
-    assert clear.mean() > 0.9
+    eps = np.abs(g_lo.astype(np.float64) - o_lo).max(axis=1)
+    srt = -np.sort(-o_lo.astype(np.float64), axis=1)[:, : wl["k"] + 1]
+    clear = (-np.diff(srt, axis=1)).min(axis=1) > 2 * eps
+    _say("  tokens with forced ranking:", int(clear.sum()), "of", T, "max eps", float(eps.max()))
+    assert clear.mean() >= 0.5
     assert np.array_equal(g_ids[clear], o_ids[clear])
 
 
@@ -160,7 +165,7 @@ def test_plan_union_bit_exact(T, k, E, kind):
     elif kind == "same":
         ids_np = np.tile(np.arange(k, dtype=np.int32), (T, 1))
     else:
-        ids_np = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32).reshape(T, k)
+        ids_np = np.array([g.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32).reshape(T, k)
     plan = moe.Plan(ctx, T)
     moe.moe_plan_union(ctx, torch.from_numpy(ids_np).cuda(), plan)
     n, ex, off, ent = plan.host()
