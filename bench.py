@@ -1,0 +1,273 @@
+"""Benchmark of one routed MoE layer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|mtp]
+
+A step is one pass of the whole hot path over one batch: router logits and
+top-k (moe_route), expert-major union (moe_plan_union) and the quantised
+SwiGLU experts with the shared expert and the weighted combine
+(moe_expert_ffn).  Default workload "decode": 256 experts, top-8 plus one
+shared expert, d_model 2048, d_ff 512, Q8_0, one token per step, 38-slot
+(15 %) cache.  "mtp": the same layer with Q4_0 weights, four tokens per step
+with overlapping routes, 89-slot (35 %) cache.
+
+Before each timed step (untimed): the step's experts are found by routing it
+once, mapped into the LRU slot cache and filled from the pinned host pack on a
+side stream, and then a 512 MiB buffer is read so that neither L2 nor the
+256 MB Infinity Cache holds any of the step's weights: the timed step reads
+every expert byte from HBM.  The flush reads rather than writes, so the
+Infinity Cache is left holding clean lines, as it is after other layers'
+weight reads; a written flush would leave 256 MB of dirty lines whose
+write-back would be charged to the timed step.  The timed region of a step is route + union + FFN, bracketed
+by HIP events on the stream the kernels run on; a second event pair brackets
+the FFN kernel alone for the roofline.  Inputs are resident in HBM when it
+starts.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_decode_traffic.json")
+
+
+def _kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("ffn_decode.hip", "device_util.h", "internal.h"):
+        h.update(open(os.path.join(ROOT, "routed_expert_execution_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str):
+    """HBM bytes per FFN launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    r = t.get(workload)
+    if not r or r.get("kernel_source_sha") != _kernel_source_digest():
+        return None
+    return r["fetch_bytes_per_launch"] + r["write_bytes_per_launch"]
+
+
+def cpu_baseline(wl: dict, budget_s: float = 10.0, max_steps: int = 200) -> dict:
+    """The oracle, as it stands, timed on a bounded sample of the same steps.
+
+    Only the oracle's own work is timed (router logits, top-k, union, the routed
+    and shared experts, the combine); drawing the synthetic inputs is not."""
+    import oracle
+    import synth
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    threads = oracle.set_threads(threads)
+    E, k, d, f, T = wl["E"], wl["k"], wl["d"], wl["f"], wl["T"]
+    wr = synth.router_weights(wl["seed"], E, d) if wl["name"] == "decode" else None
+    shared = synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True)
+    cache: dict = {}
+    steps, compute = 0, 0.0
+    while steps < max_steps and compute < budget_s:
+        s = 50_000 + steps
+        x = synth.activations(wl["seed"], T, d, wl["x_dtype"], s)
+        lg_in = None if wr is not None else synth.mtp_logits(wl["seed"], s, T, E, k, wl["p_shared_route"])
+        t0 = time.perf_counter()
+        x64 = oracle.x_to_f64(x, wl["x_dtype"])
+        lg = oracle.router_logits(x64, wr) if wr is not None else lg_in
+        ids, w = oracle.topk(lg, k)
+        oracle.plan_union(ids, E)
+        compute += time.perf_counter() - t0
+        recs = [None] * E
+        for e in set(ids.reshape(-1).tolist()):
+            if e not in cache:
+                cache[e] = synth.expert_record(wl["seed"], 0, e, wl["qtype"], d, f)
+            recs[e] = cache[e]
+        t0 = time.perf_counter()
+        oracle.moe_layer(wl["qtype"], oracle.PREC_F32, recs, shared, d, f, x64, ids, w)
+        compute += time.perf_counter() - t0
+        steps += 1
+    return {"value": steps * T / compute, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} {wl['name']} steps ({steps * T} tokens) of the same workload: fp64 C oracle, "
+                      f"router/top-k/union + {k} routed experts + shared expert per token, "
+                      f"{compute:.1f} s of CPU work"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=["decode", "mtp"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="leave L2 / Infinity Cache warm (labelled)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the routed-expert path; --gpus {args.gpus} is not "
+              f"available (one process, one GPU).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    from routed_expert_execution_amd import moe
+
+    wl = dict(synth.workload(args.workload), name=args.workload)
+    E, k, d, f, T = wl["E"], wl["k"], wl["d"], wl["f"], wl["T"]
+    qt = moe.MOE_Q8_0 if wl["qtype"] == synth.Q8_0 else moe.MOE_Q4_0
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    # ---- resident inputs -------------------------------------------------
+    cfg = moe.make_config(1, E, k, d, f, qt, wl["n_slots"], T, device=-1)
+    pb = moe.moe_payload_bytes(cfg)
+    pool = torch.zeros(wl["n_slots"] * pb, dtype=torch.uint8, device=dev)
+    ctx = moe.Context(1, E, k, d, f, qt, wl["n_slots"], T, device=0, slot_pool=pool)
+    t_gen = time.perf_counter()
+    pack = torch.empty((E, pb), dtype=torch.uint8).pin_memory()  # pinned host pack
+    pack_np = pack.numpy()
+    for e in range(E):
+        moe.moe_pack_expert(ctx.cfg, synth.expert_record(wl["seed"], 0, e, wl["qtype"], d, f), out=pack_np[e])
+    shared = torch.from_numpy(moe.moe_pack_expert(
+        ctx.cfg, synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True))).to(dev)
+    t_gen = time.perf_counter() - t_gen
+    wr = torch.from_numpy(synth.router_weights(wl["seed"], E, d)).to(dev) if args.workload == "decode" else None
+
+    n_steps = args.warmup + args.steps
+    x_all = torch.stack([
+        torch.from_numpy(synth.activations(wl["seed"], T, d, "bf16", s).view(np.int16)).view(torch.bfloat16)
+        for s in range(n_steps)]).to(dev)  # [steps, T, d]
+    lg_all = None
+    if args.workload == "mtp":
+        lg_all = torch.stack([torch.from_numpy(synth.mtp_logits(wl["seed"], s, T, E, k, wl["p_shared_route"]))
+                              for s in range(n_steps)]).to(dev)
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    y = torch.empty(T, d, dtype=torch.float32, device=dev)
+    plan = moe.Plan(ctx, T)
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)  # 512 MiB, read before every step
+    flush_sink = torch.empty((), dtype=torch.int32, device=dev)
+    spin_cycles = int(300e-6 * 2.4e9)  # ~300 us of GPU-side spin before each timed step
+    side = torch.cuda.Stream(device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def route_plan(s):
+        if lg_all is not None:
+            moe.moe_route(ctx, ids, w, logits_in=lg_all[s])
+        else:
+            moe.moe_route(ctx, ids, w, x=x_all[s], w_router=wr)
+        moe.moe_plan_union(ctx, ids, plan)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
+    n_unique = []
+    misses = 0
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for s in range(n_steps):
+        if s == args.warmup:
+            torch.cuda.synchronize()
+            wall_t0 = time.perf_counter()
+        # untimed: learn this step's experts, stage misses, flush caches
+        route_plan(s)
+        n, experts, _, _ = plan.host()
+        slots, miss = moe.moe_slot_map(ctx, 0, experts)
+        for e, sl, m in zip(experts, slots, miss):
+            if m:
+                moe.moe_slot_fill(ctx, 0, int(e), int(sl), pack[int(e)], stream=side)
+                misses += 1
+        side.synchronize()
+        if not args.no_flush:
+            flush_sink.copy_(flush.max())
+        # keep the GPU busy while the host enqueues the timed kernels, so the
+        # timed region measures GPU work, not Python launch latency
+        torch.cuda._sleep(spin_cycles)
+        # timed: the whole hot path of the step
+        e0, e1, e2 = ev[s]
+        e0.record(stream)
+        route_plan(s)
+        e1.record(stream)
+        moe.moe_expert_ffn(ctx, 0, x_all[s], plan, w, y, shared_payload=shared)
+        e2.record(stream)
+        moe.moe_slot_release(ctx, 0)
+        n_unique.append(n)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall_t0
+    st = moe.moe_check(ctx)
+    if st != moe.MOE_OK:
+        print(f"device error word set: status {st}", file=sys.stderr)
+        return 1
+
+    span = np.array([ev[s][0].elapsed_time(ev[s][2]) for s in range(args.warmup, n_steps)]) * 1e3  # us
+    ffn = np.array([ev[s][1].elapsed_time(ev[s][2]) for s in range(args.warmup, n_steps)]) * 1e3
+    uniq = np.array(n_unique[args.warmup:])
+    algo_bytes = (uniq + 1) * pb  # unique routed experts + the shared expert, per step
+    ffn_gbs = algo_bytes.mean() / (ffn.mean() * 1e-6) / 1e9
+    span_gbs = algo_bytes.mean() / (span.mean() * 1e-6) / 1e9
+    traffic = _traffic(args.workload)
+
+    line = {
+        "metric": "routed MoE-layer tokens/s (batch %d decode step: route + union + expert FFN)" % T,
+        "value": T / (span.mean() * 1e-6),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": span.mean() * 1e-3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (%s weights dequantised in registers)" % ("q8_0" if qt == moe.MOE_Q8_0 else "q4_0"),
+        "data": "synthetic (seeded; no checkpoint)",
+        "config": {
+            "workload": (f"{args.workload}: 1 MoE layer, {E} experts, top-{k} + 1 shared expert, d_model {d}, "
+                         f"d_ff {f}, {'Q8_0' if qt == moe.MOE_Q8_0 else 'Q4_0'}, {T} token(s)/step, "
+                         f"{wl['n_slots']}-slot LRU cache, "
+                         + ("512 MiB read before every step (weights cold in L2 and Infinity Cache)" if not args.no_flush
+                            else "caches warm")),
+            "global_batch": T,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "ffn_decode_kernel",
+            "achieved": ffn_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": ffn_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "detail": {
+            "layer_span_us_p50": float(np.percentile(span, 50)),
+            "layer_span_us_p90": float(np.percentile(span, 90)),
+            "ffn_us_mean": float(ffn.mean()),
+            "ffn_us_p50": float(np.percentile(ffn, 50)),
+            "ffn_us_p90": float(np.percentile(ffn, 90)),
+            "route_union_us_mean": float((span - ffn).mean()),
+            "expert_bytes_per_step": float(algo_bytes.mean()),
+            "layer_span_GBps": span_gbs,
+            "unique_experts_per_step": float(uniq.mean()),
+            "assignments_per_step": T * k,
+            "slot_misses_staged": misses,
+            "wall_s_timed_loop_incl_staging_and_flush": wall,
+            "setup_pack_s": t_gen,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+    ctx.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

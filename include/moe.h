@@ -19,7 +19,7 @@
  *    invalid call returns MOE_EINVAL and enqueues nothing.  HIP failures
  *    return MOE_EHIP; moe_last_error() then holds the message.  Nothing
  *    aborts, prints or throws across this boundary.
- *  - Faults found on the device (an unmapped expert, a wait that gave up) set
+ *  - Faults found on the device (an unmapped expert, an out-of-range id) set
  *    the context's error word and make the affected output rows quiet NaN;
  *    moe_check() reports them.
  *  - A context is used by one host thread, and its calls are ordered on one
@@ -47,7 +47,7 @@ typedef enum moe_status {
     MOE_ENOSLOT = -4,  /* a step needs more slots than are free or unpinned */
     MOE_EMISS = -5,    /* a kernel met an unmapped (layer, expert) page-table entry */
     MOE_EBUSY = -6,    /* the slot is pinned by another (layer, expert) */
-    MOE_ETIMEOUT = -7  /* a kernel's bounded inter-workgroup wait gave up */
+    MOE_ETIMEOUT = -7  /* reserved: no current kernel waits on another workgroup */
 } moe_status;
 
 enum { MOE_Q8_0 = 0, MOE_Q4_0 = 1 };          /* expert weight formats */
@@ -58,8 +58,8 @@ typedef struct moe_config {
     int32_t n_layers;        /* routed layers sharing the slot pool (>= 1) */
     int32_t n_experts;       /* routed experts per layer, 1..1024 */
     int32_t top_k;           /* experts per token, 1..min(n_experts, 32) */
-    int32_t d_model;         /* model width; d_model/32 must be 1,2,4,..,64 */
-    int32_t d_ff;            /* expert hidden width; d_ff/32 must be 1,2,4,..,64 */
+    int32_t d_model;         /* model width: 128, 256, 512, 1024 or 2048 */
+    int32_t d_ff;            /* expert hidden width: a multiple of 32 */
     int32_t qtype;           /* MOE_Q8_0 or MOE_Q4_0 (routed and shared experts) */
     int32_t n_slots;         /* slots in slot_pool (>= 1) */
     int32_t max_tokens;      /* largest T of any call (sizes the workspace), 1..65536 */
@@ -91,13 +91,16 @@ typedef struct moe_plan {
  * gate [d_ff x d_model], up [d_ff x d_model] and down [d_model x d_ff].
  *
  * Payload layout (how slots hold an expert; "Nanite for Experts", §12 asks
- * for cache geometry chosen with the kernels): each matrix's 32-element
- * blocks, taken in row-major block order, are grouped into tiles of 64
- * blocks.  A Q8_0 tile stores the first 16 codes of each of its 64 blocks
- * (64 x 16 B), then the last 16 codes of each (64 x 16 B), then the 64 fp16
- * scales (2176 B).  A Q4_0 tile stores each block's 16 nibble bytes in GGUF
- * order (64 x 16 B), then the 64 scales (1152 B).  The payload is gate tile
- * 0, up tile 0, gate tile 1, up tile 1, ..., then every down tile in order. */
+ * for cache geometry chosen with the kernels): the 32-element blocks of each
+ * matrix are grouped into tiles of 64 blocks.  gate and up take their blocks
+ * in row-major order; down takes them column-block-major (the d_model rows of
+ * column block 0, then of column block 1, ...), so that the 32 hidden units a
+ * gate/up tile pair run produces meet one contiguous run of down tiles.  A
+ * Q8_0 tile stores the first 16 codes of each of its 64 blocks (64 x 16 B),
+ * then the last 16 codes of each (64 x 16 B), then the 64 fp16 scales
+ * (2176 B).  A Q4_0 tile stores each block's 16 nibble bytes in GGUF order
+ * (64 x 16 B), then the 64 scales (1152 B).  The payload is gate tile 0, up
+ * tile 0, gate tile 1, up tile 1, ..., then every down tile in order. */
 size_t moe_payload_bytes(const moe_config* cfg);
 
 /* Sizes in bytes of the moe_plan arrays for T tokens:
@@ -227,8 +230,8 @@ moe_status moe_dequant(moe_ctx* ctx, const void* payload, int32_t prec, float* o
  * out[4] fills enqueued. */
 moe_status moe_stats(const moe_ctx* ctx, uint64_t out[5]);
 
-/* Synchronise `stream`, read and clear the error word: MOE_OK, MOE_EMISS or
- * MOE_ETIMEOUT. */
+/* Synchronise `stream`, read and clear the error word: MOE_OK, MOE_EMISS, or
+ * MOE_EINVAL for an out-of-range expert id met by moe_plan_union. */
 moe_status moe_check(moe_ctx* ctx, moe_stream stream);
 
 /* Device address of the page table ([n_layers x n_experts] int32), for tests. */

@@ -10,25 +10,33 @@ namespace moe {
 namespace {
 
 template <int QT>
-__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ payload, int f, int d,
-                                                      int nb_d, int nb_f, int64_t tile_bytes,
-                                                      int64_t gu_tiles, int prec, float* __restrict__ out) {
-    const int64_t gate_blocks = (int64_t)f * nb_d;
-    const int64_t total = 2 * gate_blocks + (int64_t)d * nb_f;
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ payload, Geom g, int prec,
+                                                      float* __restrict__ out) {
+    const int64_t gate_blocks = (int64_t)g.f * g.nb_d;
+    const int64_t total = 2 * gate_blocks + (int64_t)g.d * g.nb_f;
     const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= total) return;
+    // b enumerates logical blocks: gate rows, up rows, down rows, row-major
     int m;
     int64_t L;
     if (b < gate_blocks) { m = 0; L = b; }
     else if (b < 2 * gate_blocks) { m = 1; L = b - gate_blocks; }
     else { m = 2; L = b - 2 * gate_blocks; }
-    const int64_t t = L / kTileBlocks;
-    const int i = (int)(L % kTileBlocks);
-    const int64_t toff = m == 0 ? 2 * t * tile_bytes
-                       : m == 1 ? (2 * t + 1) * tile_bytes
-                                : (2 * gu_tiles + t) * tile_bytes;
+    const int nb = m < 2 ? g.nb_d : g.nb_f;
+    const int64_t r = L / nb;
+    const int cb = (int)(L % nb);
+    int64_t t;
+    int i;
+    int64_t toff;
+    if (m < 2) {
+        g.gu_block(r, cb, &t, &i);
+        toff = m == 0 ? g.gate_tile(t) : g.up_tile(t);
+    } else {
+        g.down_block(r, cb, &t, &i);
+        toff = g.down_tile(t);
+    }
     const uint8_t* tile = payload + toff;
-    float* o = out + (int64_t)m * f * d + L * kQK;
+    float* o = out + (int64_t)m * g.f * g.d + L * kQK;
     if (QT == MOE_Q8_0) {
         const float s = f16_bits_to_f32(*(const uint16_t*)(tile + q8_scale(i)));
         const int8_t* lo = (const int8_t*)(tile + q8_lo(i));
@@ -40,9 +48,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
         }
     } else {
         const float s = f16_bits_to_f32(*(const uint16_t*)(tile + q4_scale(i)));
-        const uint8_t* nb = tile + q4_nib(i);
+        const uint8_t* nbp = tile + q4_nib(i);
         for (int j = 0; j < 16; j++) {
-            float a = (float)((int)(nb[j] & 15) - 8) * s, c = (float)((int)(nb[j] >> 4) - 8) * s;
+            float a = (float)((int)(nbp[j] & 15) - 8) * s, c = (float)((int)(nbp[j] >> 4) - 8) * s;
             o[j] = prec ? round_bf16(a) : a;
             o[16 + j] = prec ? round_bf16(c) : c;
         }
@@ -55,11 +63,9 @@ hipError_t launch_dequant(const Geom& g, const uint8_t* payload, int prec, float
     const int64_t total = 2 * (int64_t)g.f * g.nb_d + (int64_t)g.d * g.nb_f;
     dim3 grid((unsigned)((total + 255) / 256));
     if (g.qtype == MOE_Q8_0)
-        hipLaunchKernelGGL(dequant_kernel<MOE_Q8_0>, grid, dim3(256), 0, s, payload, g.f, g.d, g.nb_d, g.nb_f,
-                           g.tile_bytes, g.gu_tiles, prec, out);
+        hipLaunchKernelGGL(dequant_kernel<MOE_Q8_0>, grid, dim3(256), 0, s, payload, g, prec, out);
     else
-        hipLaunchKernelGGL(dequant_kernel<MOE_Q4_0>, grid, dim3(256), 0, s, payload, g.f, g.d, g.nb_d, g.nb_f,
-                           g.tile_bytes, g.gu_tiles, prec, out);
+        hipLaunchKernelGGL(dequant_kernel<MOE_Q4_0>, grid, dim3(256), 0, s, payload, g, prec, out);
     return hipGetLastError();
 }
 

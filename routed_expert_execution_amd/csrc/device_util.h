@@ -19,13 +19,45 @@ __device__ inline float f16_bits_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
 }
 
-// Sum over aligned groups of SEG lanes (SEG a power of two <= 64); every lane
-// of a group ends with the group's sum, combined in one fixed order.
+// Lane permutation through DPP (no LDS traffic, folded into the consuming VALU op).
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of SEG lanes (SEG a power of two <= 64).  Every lane
+// of a group ends with the same bits (each step adds a lane and its partner,
+// and a + b == b + a exactly), in one fixed order: lane ^ 1, lane ^ 2, the other
+// quad of the 8 (row_half_mirror), the other 8 of the row (row_mirror), the
+// other row of the 32 (permlane16_swap), the other 32 (permlane32_swap).
 template <int SEG>
 __device__ inline float seg_sum(float v) {
-#pragma unroll
-    for (int m = SEG / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    if constexpr (SEG >= 2) v += dpp_f<0xB1>(v);
+    if constexpr (SEG >= 4) v += dpp_f<0x4E>(v);
+    if constexpr (SEG >= 8) v += dpp_f<0x141>(v);
+    if constexpr (SEG >= 16) v += dpp_f<0x140>(v);
+    if constexpr (SEG >= 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if constexpr (SEG >= 64) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
     return v;
+}
+
+// seg_sum with a wave-uniform group size.
+__device__ inline float seg_sum_rt(float v, int seg) {
+    switch (seg) {
+        case 1: return v;
+        case 2: return seg_sum<2>(v);
+        case 4: return seg_sum<4>(v);
+        case 8: return seg_sum<8>(v);
+        case 16: return seg_sum<16>(v);
+        case 32: return seg_sum<32>(v);
+        default: return seg_sum<64>(v);
+    }
 }
 
 __device__ inline uint64_t wave_max_u64(uint64_t v) {

@@ -1,46 +1,44 @@
-// Fused decode step of the routed experts: one launch over every expert the
-// step touches — the persistent expert-major operator that consumes routed
-// positions and page-table entries for several resident experts at once
-// ("Nanite for Experts", §12, milestone 1; §11.5: the execution unit should be
-// expert-major, not many independently orchestrated fragments).
+// Decode step of the routed experts (T <= 4 tokens): every expert of the step
+// in one launch — the expert-major operator that consumes routed positions and
+// page-table entries for several resident experts at once ("Nanite for
+// Experts", §12, milestone 1; §11.5: the unit of execution should be
+// expert-major, not many separately orchestrated fragments) — followed by a
+// small fixed-order combine launch.
 //
-// Work split (T <= 4 tokens, F32 or BF16 arithmetic):
-//  * gate/up waves (the lower workgroup ids): unit u (a routed expert of the
-//    plan, ascending, or the shared expert last) and a run of TPW gate/up tile
-//    pairs.  Each lane loads its block of every tile with 16-byte loads (a
-//    tile is 64 blocks = one 128-bit load per lane per code half, fully
-//    coalesced), dequantises in registers, dots it with the lane's 32-column
-//    slice of x, and the lanes of one row are summed by a fixed butterfly.
-//    h = silu(g) * u is written to the workspace, then the wave bumps a
-//    counter (release, agent scope).
-//  * down waves (the higher ids): one 64-block tile of W_d (64/nb_f rows) for
-//    every unit.  They issue their weight loads first, wait for all gate/up
-//    waves (acquire), stage every h row in LDS, then accumulate each token's
-//    output rows over its experts in ascending expert order, shared expert
-//    last, and write y directly — no float atomics, no second pass.
-// Workgroups are dispatched in id order on each XCD, so whenever a down
-// workgroup is resident every gate/up workgroup of its XCD has been
-// dispatched; gate/up waves never wait, so the waits always end.  The wait is
-// bounded anyway (spin_limit): on expiry the error word is set and the
-// affected rows are NaN.
-//
-// Expert weights come from slot_pool + page_table[layer, e] * payload_bytes
-// ("Nanite for Experts", §5.4: device page table with sentinels); a -1 entry
-// sets the error word and makes every row routed to it NaN (fail closed).
+// ffn_partial: one workgroup per (unit, chunk).  A unit is a routed expert of
+//   the plan (ascending expert id) or the shared expert (last); a chunk is
+//   ROWS consecutive hidden rows: 16 for Q8_0 (one code half of a 32-column
+//   block of W_d, which the tile layout stores contiguously) and 32 for Q4_0
+//   (whose nibble bytes hold both halves).  The workgroup
+//     1. resolves the unit's slot through the page table ("Nanite for
+//        Experts", §5.4; a -1 entry fails closed: NaN partials, error word),
+//     2. issues every weight load of the chunk at once — its gate and up rows
+//        and the matching columns of W_d (all d rows), one 16-byte load per
+//        lane per tile piece — plus the bucket's activations,
+//     3. computes h_c = silu(W_g[c] x) * (W_u[c] x) for each token of the bucket
+//        (lanes of a row summed by DPP), into LDS,
+//     4. after one workgroup barrier, each lane owns one output row of W_d's
+//        columns: ROWS codes times h_c broadcast from LDS, no cross-lane sum,
+//        and writes the partial row P[entry][chunk][row].
+//   No workgroup ever waits for another.
+// combine: y[t, i] = sum over t's entries in plan order (ascending expert) of
+//   w * (sum over chunks of P) + the shared expert's chunks, in one fixed
+//   order that depends only on expert ids and ranks, never on slots.
 #include "device_util.h"
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTPW = 4;  // gate/up tile pairs per wave
-constexpr int kPF = 8;   // down tiles kept in flight per wave
-
-struct DecodeGrid {
-    int n_gu_waves, n_gu_blocks, n_d_blocks, wpu;
-    int gu_tiles, d_tiles, nbd, nbf, d, f, n_h_rows;
-    int64_t tile_bytes, down_off;
-};
+// Workgroup shape: ROWS hidden rows per chunk, 8 waves.  With up to 4 tokens
+// per bucket the down tiles are loaded after the gate/up products, so that the
+// activations of four tokens and all tiles are not live at once.
+template <int QT> constexpr int chunk_rows() { return QT == MOE_Q8_0 ? 16 : 32; }
+template <int TG> constexpr int wg_waves() { return 8; }
+template <int TG> constexpr bool down_early() { return TG < 4; }
+// PPW gate/up tile pairs and DPW down tiles per wave are compile-time, so each
+// wave holds exactly its tiles in registers: (1,1) for small d_model, (2,4)
+// for Q8_0 at d_model 2048 (16-row chunks), (4,4) otherwise.
 
 template <int QT> struct Tile;
 template <> struct Tile<MOE_Q8_0> {
@@ -52,6 +50,11 @@ template <> struct Tile<MOE_Q8_0> {
         s = *(const uint16_t*)(t + q8_scale(i));
     }
     __device__ void clear() { lo = hi = make_uint4(0, 0, 0, 0); s = 0; }
+    // one code half (codes 0..15 or 16..31 of the lane's block) into lo
+    __device__ void load_half(const uint8_t* t, int i, int half) {
+        lo = *(const uint4*)(t + (half ? q8_hi(i) : q8_lo(i)));
+        s = *(const uint16_t*)(t + q8_scale(i));
+    }
 };
 template <> struct Tile<MOE_Q4_0> {
     uint4 nib;
@@ -63,13 +66,13 @@ template <> struct Tile<MOE_Q4_0> {
     __device__ void clear() { nib = make_uint4(0, 0, 0, 0); s = 0; }
 };
 
-// Dot products of the lane's block with N column slices v[n][0..32).
-// PREC_F32: sum of code * v, then one multiply by the scale (the products
-// d*q*v are the exact dequantised weights times v); PREC_BF16: each exact d*q
-// is rounded to bf16 first.  Codes are converted one 32-bit word at a time.
+// Weight as multiplied: PREC_F32 keeps the code (the scale is applied once after
+// the dot product, so each product is the exact dequantised weight times v up
+// to rounding); PREC_BF16 rounds each exact d*q to bf16.
 template <int PREC>
 __device__ inline float wq(float code, float s) { return PREC == MOE_PREC_BF16 ? round_bf16(code * s) : code; }
 
+// Dot products of the lane's block with N 32-float vectors v[n].
 template <int QT, int PREC, int N>
 __device__ inline void tile_dots(const Tile<QT>& t, const float (&v)[N][32], float (&acc)[N]) {
     const float s = f16_bits_to_f32(t.s);
@@ -107,35 +110,26 @@ __device__ inline void tile_dots(const Tile<QT>& t, const float (&v)[N][32], flo
     }
 }
 
-// The lane's 32 weights as the kernel multiplies them (codes for PREC_F32,
-// whose scale is applied after the dot product; bf16-rounded d*q for
-// PREC_BF16).  Returns the factor to apply after the dot product.
-template <int QT, int PREC>
-__device__ inline float tile_weights(const Tile<QT>& t, float (&w)[32]) {
+// Dot products of the 16 codes held in t.lo (a Q8_0 half block) with N
+// 16-float vectors.
+template <int PREC, int N>
+__device__ inline void half_dots(const Tile<MOE_Q8_0>& t, const float (&v)[N][16], float (&acc)[N]) {
     const float s = f16_bits_to_f32(t.s);
-    if constexpr (QT == MOE_Q8_0) {
-        const uint32_t c[8] = {t.lo.x, t.lo.y, t.lo.z, t.lo.w, t.hi.x, t.hi.y, t.hi.z, t.hi.w};
 #pragma unroll
-        for (int m = 0; m < 8; m++)
+    for (int n = 0; n < N; n++) acc[n] = 0.f;
+    const uint32_t w[4] = {t.lo.x, t.lo.y, t.lo.z, t.lo.w};
 #pragma unroll
-            for (int j = 0; j < 4; j++) w[4 * m + j] = wq<PREC>(i8(c[m], j), s);
-    } else {
-        const uint32_t c[4] = {t.nib.x, t.nib.y, t.nib.z, t.nib.w};
+    for (int m = 0; m < 4; m++)
 #pragma unroll
-        for (int m = 0; m < 4; m++)
+        for (int j = 0; j < 4; j++) {
+            const float c = wq<PREC>(i8(w[m], j), s);
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const uint32_t b = (c[m] >> (8 * j)) & 0xFF;
-                w[4 * m + j] = wq<PREC>((float)((int)(b & 15) - 8), s);
-                w[16 + 4 * m + j] = wq<PREC>((float)((int)(b >> 4) - 8), s);
-            }
+            for (int n = 0; n < N; n++) acc[n] = fmaf(c, v[n][4 * m + j], acc[n]);
+        }
+    if (PREC == MOE_PREC_F32) {
+#pragma unroll
+        for (int n = 0; n < N; n++) acc[n] *= s;
     }
-    return PREC == MOE_PREC_F32 ? s : 1.0f;
-}
-
-__device__ inline float seg_sum_rt(float v, int seg) {
-    for (int m = seg >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
 }
 
 template <int PREC>
@@ -166,249 +160,264 @@ __device__ inline void load_x(const FfnArgs& a, int d, int t, int cb, float (&xs
     }
 }
 
-__device__ inline const uint8_t* unit_base(const FfnArgs& a, int u, int na) {
-    if (u == na) return a.shared;
-    const int e = a.experts[u];
-    if (e < 0 || e >= a.E) return nullptr;
-    const int s = a.pt[(int64_t)a.layer * a.E + e];
-    if (s < 0 || s >= a.n_slots) return nullptr;
-    return a.pool + (int64_t)s * a.payload_bytes;
-}
+struct Grid {
+    int units_max;  // routed units allotted (the plan may use fewer) + shared
+    int n_chunks;   // d_ff / ROWS
+    int pairs;      // gate/up tile pairs per chunk = ROWS * (d_model/32) / 64
+    int dtiles;     // down tiles per W_d column block = d_model / 64
+    int nbd, d, d_ff;
+    int64_t tile_bytes, down_off;
+};
 
-template <int QT, int PREC, int TG>
-__device__ void gate_up_wave(const FfnArgs& a, const DecodeGrid& g, int u, int part, int na, int lane) {
-    const uint8_t* base = unit_base(a, u, na);
-    if (!base && lane == 0) atomicOr(a.err, kErrMiss);
+template <int QT, int PREC, int TG, int PPW, int DPW>
+__global__ __launch_bounds__(wg_waves<TG>() * 64, TG == 1 ? 4 : 2) void ffn_partial_kernel(FfnArgs a, Grid g) {
+    constexpr int ROWS = chunk_rows<QT>();
+    constexpr int WAVES = wg_waves<TG>();
+    __shared__ float h_c[TG][ROWS];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int u = blockIdx.x / g.n_chunks, c = blockIdx.x - u * g.n_chunks;
+
+    // Level 1: small-table loads that do not depend on each other (indices
+    // clamped into range so all can be in flight together).
+    const int na = *a.n_active;
+    const int e = a.experts[min(u, a.E - 1)];
+    const int o0 = a.offsets[min(u, a.E)];
+    const int o1 = a.offsets[min(u + 1, a.E)];
+    const bool has_shared = a.shared != nullptr;
+    if (u >= na + (has_shared ? 1 : 0)) return;  // uniform over the workgroup
     const bool routed = u < na;
-    const int b0 = routed ? a.offsets[u] : 0;
-    const int b1 = routed ? a.offsets[u + 1] : a.T;
-    const int tile0 = part * kTPW;
-    const int nt = min(kTPW, g.gu_tiles - tile0);
-
-    Tile<QT> tg[kTPW], tu[kTPW];
+    // Level 2: the page-table entry and the bucket's token ids.
+    const bool e_ok = e >= 0 && e < a.E;
+    const int slot = a.pt[(int64_t)a.layer * a.E + (e_ok ? e : 0)];
+    const int b0 = routed ? o0 : 0;
+    const int nb = routed ? o1 - o0 : a.T;  // tokens in the bucket, <= T <= TG
+    int tok[TG], prow[TG];
 #pragma unroll
-    for (int q = 0; q < kTPW; q++) {
-        if (q < nt && base) {
-            tg[q].load(base + 2 * (int64_t)(tile0 + q) * g.tile_bytes, lane);
-            tu[q].load(base + (2 * (int64_t)(tile0 + q) + 1) * g.tile_bytes, lane);
+    for (int gi = 0; gi < TG; gi++) {
+        const bool in = gi < nb;
+        tok[gi] = !in ? -1 : !routed ? gi : a.T == 1 ? 0 : a.entries[b0 + gi] / a.k;
+        prow[gi] = !in ? -1 : routed ? b0 + gi : a.T * a.k + gi;
+    }
+    const uint8_t* base = !routed ? a.shared
+                        : (e_ok && slot >= 0 && slot < a.n_slots) ? a.pool + (int64_t)slot * a.payload_bytes
+                                                                  : nullptr;
+    if (!base && threadIdx.x == 0) atomicOr(a.err, kErrMiss);
+    const float qnan = __uint_as_float(0x7FC00000u);
+
+    // Level 3: every weight load of the chunk, then the activations.  The
+    // chunk's gate/up rows are tiles [c*pairs, (c+1)*pairs) of each matrix.
+    // Its W_d columns: Q8_0 chunk c is code half c%2 of column block c/2;
+    // Q4_0 chunk c is column block c.  A column block is dtiles tiles.
+    const int colblk = QT == MOE_Q8_0 ? c >> 1 : c;
+    Tile<QT> tg[PPW], tu[PPW], td[DPW];
+#pragma unroll
+    for (int q = 0; q < PPW; q++) {
+        const int pi = wave + q * WAVES;
+        if (base && pi < g.pairs) {
+            const int64_t t = (int64_t)c * g.pairs + pi;
+            tg[q].load(base + 2 * t * g.tile_bytes, lane);
+            tu[q].load(base + (2 * t + 1) * g.tile_bytes, lane);
         } else {
             tg[q].clear();
             tu[q].clear();
         }
     }
-    const int cb = lane & (g.nbd - 1);     // column block of this lane within its row
-    const bool writer = cb == 0;
-    const float qnan = __uint_as_float(0x7FC00000u);
-
-    // a bucket holds at most T <= TG tokens: one pass covers it
+    auto load_down = [&]() {
+#pragma unroll
+        for (int q = 0; q < DPW; q++) {
+            const int pi = wave + q * WAVES;
+            if (base && pi < g.dtiles) {
+                const uint8_t* tp = base + g.down_off + ((int64_t)colblk * g.dtiles + pi) * g.tile_bytes;
+                if constexpr (QT == MOE_Q8_0) td[q].load_half(tp, lane, c & 1);
+                else td[q].load(tp, lane);
+            } else {
+                td[q].clear();
+            }
+        }
+    };
+    if constexpr (down_early<TG>()) load_down();
+    const int cb = lane & (g.nbd - 1);  // column block of this lane within its gate/up row
     float xs[TG][32];
-    int hrow[TG];
 #pragma unroll
     for (int gi = 0; gi < TG; gi++) {
-        const int p = b0 + gi;
-        if (p < b1) {
-            const int t = routed ? a.entries[p] / a.k : p;
-            hrow[gi] = routed ? p : a.T * a.k + p;
-            load_x<PREC>(a, g.d, t, cb, xs[gi]);
+        if (tok[gi] >= 0) {
+            load_x<PREC>(a, g.d, tok[gi], cb, xs[gi]);
         } else {
-            hrow[gi] = -1;
 #pragma unroll
             for (int j = 0; j < 32; j++) xs[gi][j] = 0.f;
         }
     }
+
+    // gate/up: this chunk's hidden rows into LDS
+    const int rows_per_tile = kTileBlocks / g.nbd;
 #pragma unroll
-    for (int q = 0; q < kTPW; q++) {
-        if (q >= nt) break;
-        const int row = ((tile0 + q) * kTileBlocks + lane) / g.nbd;
+    for (int q = 0; q < PPW; q++) {
+        const int pi = wave + q * WAVES;
+        if (pi >= g.pairs) break;
         float accg[TG], accu[TG];
         tile_dots<QT, PREC, TG>(tg[q], xs, accg);
         tile_dots<QT, PREC, TG>(tu[q], xs, accu);
+        const int r = pi * rows_per_tile + lane / g.nbd;  // row within the chunk
 #pragma unroll
         for (int gi = 0; gi < TG; gi++) {
             const float gs = seg_sum_rt(accg[gi], g.nbd);
             const float us = seg_sum_rt(accu[gi], g.nbd);
-            if (writer && hrow[gi] >= 0) {
+            if (cb == 0) {
                 float hv = silu(gs) * us;
                 if (PREC == MOE_PREC_BF16) hv = round_bf16(hv);
-                a.h[(int64_t)hrow[gi] * g.f + row] = base ? hv : qnan;
+                h_c[gi][r] = base ? hv : qnan;
             }
         }
     }
+    if constexpr (!down_early<TG>()) load_down();
+    __syncthreads();
+
+    // down: the lane owns output row (pi * 64 + lane)
+    float hv[TG][ROWS];
+#pragma unroll
+    for (int gi = 0; gi < TG; gi++)
+#pragma unroll
+        for (int j = 0; j < ROWS; j++) hv[gi][j] = h_c[gi][j];
+#pragma unroll
+    for (int q = 0; q < DPW; q++) {
+        const int pi = wave + q * WAVES;
+        if (pi >= g.dtiles) break;
+        float acc[TG];
+        if constexpr (QT == MOE_Q8_0) half_dots<PREC, TG>(td[q], hv, acc);
+        else tile_dots<QT, PREC, TG>(td[q], hv, acc);
+        const int row = pi * kTileBlocks + lane;
+#pragma unroll
+        for (int gi = 0; gi < TG; gi++)
+            if (prow[gi] >= 0) a.part[((int64_t)prow[gi] * g.n_chunks + c) * g.d + row] = base ? acc[gi] : qnan;
+    }
 }
 
-template <int QT, int PREC>
-__device__ void down_block(const FfnArgs& a, const DecodeGrid& g, int na, int n_units, int lane, int wave,
-                           float* hlds) {
-    __shared__ int s_timeout;
-    const int dt = (blockIdx.x - g.n_gu_blocks) * 4 + wave;
-    const bool active = dt < g.d_tiles;
-    const int cb = lane & (g.nbf - 1);
-    const int row = active ? (dt * kTileBlocks + lane) / g.nbf : 0;
-    const int64_t toff = g.down_off + (int64_t)dt * g.tile_bytes;
+// combine: a workgroup of 256 threads covers 64 outputs of one token as 16
+// float4 quads x 16 entry slots.  Token t's entries are found in plan order
+// (ascending expert) with one ballot; each thread sums every chunk of its
+// (quad, entry) with all loads in flight, and the per-entry sums are then
+// weighted and added per output in plan order, shared expert last.
+constexpr int kCombineQuads = 16;
+constexpr int kCombineSlots = 16;
+constexpr int kMaxCombine = 33;  // top_k <= 32 entries + shared
+constexpr int kChunkBatch = 16;
 
-    // 1. weight loads first: they do not depend on h
-    Tile<QT> tl[kPF];
-    bool ok[kPF];
-#pragma unroll
-    for (int p = 0; p < kPF; p++) {
-        const uint8_t* b = (active && p < n_units) ? unit_base(a, p, na) : nullptr;
-        ok[p] = b != nullptr;
-        if (b) tl[p].load(b + toff, lane); else tl[p].clear();
-    }
-    // 2. wait for every gate/up wave
-    if (threadIdx.x == 0) {
-        s_timeout = 0;
-        int it = 0;
-        while (__hip_atomic_load(&a.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-               (unsigned)g.n_gu_waves) {
-            if (++it > a.spin_limit) {
-                atomicOr(a.err, kErrTimeout);
-                s_timeout = 1;
-                break;
+__global__ __launch_bounds__(kCombineQuads * kCombineSlots) void combine_kernel(FfnArgs a, int n_chunks, int d) {
+    __shared__ int s_q[kMaxCombine];
+    __shared__ float s_w[kMaxCombine];
+    __shared__ int s_cnt;
+    __shared__ float4 red[kMaxCombine][kCombineQuads];
+    const int t = blockIdx.y;
+    const int qd = threadIdx.x % kCombineQuads, slot = threadIdx.x / kCombineQuads;
+    const int i4 = blockIdx.x * kCombineQuads + qd;  // output quad
+    const int n_ent = a.T * a.k;
+    if (threadIdx.x < 64) {
+        int base = 0;
+        for (int q0 = 0; q0 < n_ent; q0 += 64) {
+            const int q = q0 + threadIdx.x;
+            const int ent = q < n_ent ? a.entries[q] : -1;
+            const bool mine = q < n_ent && ent / a.k == t;
+            const uint64_t m = __ballot(mine);
+            if (mine) {
+                const int r = base + __popcll(m & ((1ull << threadIdx.x) - 1ull));
+                s_q[r] = q;
+                s_w[r] = a.topk_w[ent];
             }
-            __builtin_amdgcn_s_sleep(2);
+            base += __popcll(m);
+        }
+        if (threadIdx.x == 0) {
+            int cnt = base;
+            if (a.shared) {
+                s_q[cnt] = n_ent + t;
+                s_w[cnt] = 1.0f;
+                cnt++;
+            }
+            s_cnt = cnt;
         }
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    // 3. stage all hidden states
-    const int nh = g.n_h_rows * g.f;
-    for (int i = threadIdx.x * 4; i < nh; i += blockDim.x * 4)
-        *(float4*)(hlds + i) = *(const float4*)(a.h + i);
-    __syncthreads();
-
-    if (active) {
-        const float qnan = __uint_as_float(0x7FC00000u);
-        float acc[kDecodeMaxT];
+    const int cnt = s_cnt;
+    const bool in = i4 * 4 < d;
+    for (int j = slot; j < cnt; j += kCombineSlots) {
+        const float4* p = (const float4*)(a.part + (int64_t)s_q[j] * n_chunks * d) + i4;
+        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int c0 = 0; c0 < n_chunks; c0 += kChunkBatch) {
+            float4 v[kChunkBatch];
 #pragma unroll
-        for (int t = 0; t < kDecodeMaxT; t++) acc[t] = 0.f;
-        for (int u0 = 0; u0 < n_units; u0 += kPF) {
+            for (int b = 0; b < kChunkBatch; b++)
+                v[b] = (in && c0 + b < n_chunks) ? p[(int64_t)(c0 + b) * (d / 4)] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-            for (int p = 0; p < kPF; p++) {
-                const int u = u0 + p;
-                if (u >= n_units) break;
-                const bool okp = ok[p];
-                float wf[32];
-                const float post = tile_weights<QT, PREC>(tl[p], wf);
-                const bool routed = u < na;
-                const int b0 = routed ? a.offsets[u] : 0;
-                const int b1 = routed ? a.offsets[u + 1] : a.T;
-                for (int q = b0; q < b1; q++) {
-                    int t, hr;
-                    float rw;
-                    if (routed) {
-                        const int ent = a.entries[q];
-                        t = ent / a.k;
-                        rw = a.topk_w[ent];
-                        hr = q;
-                    } else {
-                        t = q;
-                        rw = 1.0f;
-                        hr = a.T * a.k + q;
-                    }
-                    const float4* h4 = (const float4*)(hlds + hr * g.f + cb * kQK);
-                    float dot = 0.f;
-#pragma unroll
-                    for (int m = 0; m < 8; m++) {
-                        const float4 v = h4[m];
-                        dot = fmaf(wf[4 * m], v.x, dot);
-                        dot = fmaf(wf[4 * m + 1], v.y, dot);
-                        dot = fmaf(wf[4 * m + 2], v.z, dot);
-                        dot = fmaf(wf[4 * m + 3], v.w, dot);
-                    }
-                    dot = seg_sum_rt(dot * post, g.nbf);
-                    if (!okp) dot = qnan;
-#pragma unroll
-                    for (int tt = 0; tt < kDecodeMaxT; tt++)
-                        if (tt == t) acc[tt] = fmaf(rw, dot, acc[tt]);
-                }
-                // refill this register slot with the unit kPF ahead
-                const int un = u + kPF;
-                if (un < n_units) {
-                    const uint8_t* b = unit_base(a, un, na);
-                    ok[p] = b != nullptr;
-                    if (b) tl[p].load(b + toff, lane); else tl[p].clear();
-                }
+            for (int b = 0; b < kChunkBatch; b++) {
+                sum.x += v[b].x; sum.y += v[b].y; sum.z += v[b].z; sum.w += v[b].w;
             }
         }
-        if (cb == 0) {
-            const bool bad = s_timeout != 0;
-#pragma unroll
-            for (int t = 0; t < kDecodeMaxT; t++)
-                if (t < a.T) a.y[(int64_t)t * g.d + row] = bad ? qnan : acc[t];
-        }
+        red[j][qd] = sum;
     }
-    // 4. the last down workgroup re-arms the counters for the next launch
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(&a.sync[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == (unsigned)g.n_d_blocks - 1) {
-            __hip_atomic_store(&a.sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.sync[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (slot == 0 && in) {
+        const int n_routed = a.shared ? cnt - 1 : cnt;
+        float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < cnt; j++) {
+            const float4 s4 = red[j][qd];
+            const float wj = j < n_routed ? s_w[j] : 1.0f;
+            if (j < n_routed) {
+                y.x = fmaf(wj, s4.x, y.x); y.y = fmaf(wj, s4.y, y.y);
+                y.z = fmaf(wj, s4.z, y.z); y.w = fmaf(wj, s4.w, y.w);
+            } else {
+                y.x += s4.x; y.y += s4.y; y.z += s4.z; y.w += s4.w;
+            }
         }
+        *(float4*)(a.y + (int64_t)t * d + i4 * 4) = y;
     }
 }
 
-template <int QT, int PREC, int TG>
-__global__ __launch_bounds__(256) void ffn_decode_kernel(FfnArgs a, DecodeGrid g) {
-    extern __shared__ float hlds[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int na = *a.n_active;
-    const int n_units = na + (a.shared ? 1 : 0);
-    if ((int)blockIdx.x < g.n_gu_blocks) {
-        const int gw = blockIdx.x * 4 + wave;
-        if (gw >= g.n_gu_waves) return;
-        const int u = gw / g.wpu, part = gw - u * g.wpu;
-        if (u < n_units) gate_up_wave<QT, PREC, TG>(a, g, u, part, na, lane);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        if (lane == 0) __hip_atomic_fetch_add(&a.sync[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
-    }
-    down_block<QT, PREC>(a, g, na, n_units, lane, wave, hlds);
-}
-
-template <int QT, int PREC, int TG>
-hipError_t launch_t(const DecodeGrid& dg, const FfnArgs& a, size_t lds, hipStream_t s) {
-    auto kern = ffn_decode_kernel<QT, PREC, TG>;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(kern, dim3(dg.n_gu_blocks + dg.n_d_blocks), dim3(256), lds, s, a, dg);
+template <int QT, int PREC, int TG, int PPW, int DPW>
+hipError_t launch_t(const Grid& g, const FfnArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((ffn_partial_kernel<QT, PREC, TG, PPW, DPW>), dim3(g.units_max * g.n_chunks),
+                       dim3(wg_waves<TG>() * 64), 0, s, a, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(combine_kernel, dim3((g.d / 4 + kCombineQuads - 1) / kCombineQuads, a.T),
+                       dim3(kCombineQuads * kCombineSlots), 0, s, a, g.n_chunks, g.d);
     return hipGetLastError();
 }
 
+template <int QT, int PREC, int TG>
+hipError_t launch_w(Grid g, const FfnArgs& a, hipStream_t s) {
+    constexpr int ROWS = chunk_rows<QT>();
+    constexpr int W = wg_waves<TG>();
+    g.n_chunks = g.d_ff / ROWS;
+    g.pairs = ROWS * g.nbd / kTileBlocks;
+    if (g.pairs < 1) return hipErrorInvalidValue;
+    if (g.pairs <= W && g.dtiles <= W) return launch_t<QT, PREC, TG, 1, 1>(g, a, s);
+    if (g.pairs <= 2 * W && g.dtiles <= 4 * W) return launch_t<QT, PREC, TG, 2, 4>(g, a, s);
+    if (g.pairs <= 4 * W && g.dtiles <= 4 * W) return launch_t<QT, PREC, TG, 4, 4>(g, a, s);
+    return hipErrorInvalidValue;
+}
+
 template <int QT, int PREC>
-hipError_t launch_tg(const DecodeGrid& dg, const FfnArgs& a, size_t lds, hipStream_t s) {
-    if (a.T <= 1) return launch_t<QT, PREC, 1>(dg, a, lds, s);
-    if (a.T <= 2) return launch_t<QT, PREC, 2>(dg, a, lds, s);
-    return launch_t<QT, PREC, 4>(dg, a, lds, s);
+hipError_t launch_tg(const Grid& g, const FfnArgs& a, hipStream_t s) {
+    if (a.T <= 1) return launch_w<QT, PREC, 1>(g, a, s);
+    if (a.T <= 2) return launch_w<QT, PREC, 2>(g, a, s);
+    return launch_w<QT, PREC, 4>(g, a, s);
 }
 
 }  // namespace
 
 hipError_t launch_ffn_decode(const Geom& g, const FfnArgs& a, int prec, hipStream_t s) {
-    DecodeGrid dg{};
-    const int units_max = min(a.T * a.k, a.E) + (a.shared ? 1 : 0);
-    dg.gu_tiles = (int)g.gu_tiles;
-    dg.d_tiles = (int)g.d_tiles;
-    dg.wpu = (dg.gu_tiles + kTPW - 1) / kTPW;
-    dg.n_gu_waves = units_max * dg.wpu;
-    dg.n_gu_blocks = (dg.n_gu_waves + 3) / 4;
-    dg.n_d_blocks = (dg.d_tiles + 3) / 4;
-    dg.nbd = g.nb_d;
-    dg.nbf = g.nb_f;
-    dg.d = g.d;
-    dg.f = g.f;
-    dg.n_h_rows = a.T * a.k + (a.shared ? a.T : 0);
-    dg.tile_bytes = g.tile_bytes;
-    dg.down_off = 2 * g.gu_tiles * g.tile_bytes;
-    const size_t lds = (size_t)dg.n_h_rows * g.f * sizeof(float);
+    Grid gr{};
+    gr.units_max = min(a.T * a.k, a.E) + (a.shared ? 1 : 0);
+    gr.dtiles = g.d / kTileBlocks;
+    gr.nbd = g.nb_d;
+    gr.d = g.d;
+    gr.d_ff = g.f;
+    gr.tile_bytes = g.tile_bytes;
+    gr.down_off = 2 * g.gu_tiles * g.tile_bytes;
     if (g.qtype == MOE_Q8_0)
-        return prec == MOE_PREC_BF16 ? launch_tg<MOE_Q8_0, MOE_PREC_BF16>(dg, a, lds, s)
-                                     : launch_tg<MOE_Q8_0, MOE_PREC_F32>(dg, a, lds, s);
-    return prec == MOE_PREC_BF16 ? launch_tg<MOE_Q4_0, MOE_PREC_BF16>(dg, a, lds, s)
-                                 : launch_tg<MOE_Q4_0, MOE_PREC_F32>(dg, a, lds, s);
+        return prec == MOE_PREC_BF16 ? launch_tg<MOE_Q8_0, MOE_PREC_BF16>(gr, a, s)
+                                     : launch_tg<MOE_Q8_0, MOE_PREC_F32>(gr, a, s);
+    return prec == MOE_PREC_BF16 ? launch_tg<MOE_Q4_0, MOE_PREC_BF16>(gr, a, s)
+                                 : launch_tg<MOE_Q4_0, MOE_PREC_F32>(gr, a, s);
 }
 
 }  // namespace moe

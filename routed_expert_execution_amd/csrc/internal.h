@@ -28,19 +28,32 @@ struct Geom {
         if (qt != MOE_Q8_0 && qt != MOE_Q4_0) return false;
         if (d <= 0 || f <= 0 || d % kQK || f % kQK) return false;
         nb_d = d / kQK; nb_f = f / kQK;
-        auto pow2_le64 = [](int v) { return v >= 1 && v <= 64 && (v & (v - 1)) == 0; };
-        if (!pow2_le64(nb_d) || !pow2_le64(nb_f)) return false;
-        // whole tiles only: rows per tile = 64 / blocks per row
-        if (f % (kTileBlocks / nb_d) || d % (kTileBlocks / nb_f)) return false;
+        // gate/up rows: 4..64 blocks, a power of two, so 16 rows are whole tiles;
+        // down: column blocks of d rows, d a multiple of 64 and at most 32 tiles
+        if (nb_d < 4 || nb_d > 64 || (nb_d & (nb_d - 1))) return false;
+        if (d % kTileBlocks || d / kTileBlocks > 32) return false;
         tile_bytes = (int64_t)kTileBlocks * block_bytes(qt);
         gu_tiles = (int64_t)f * nb_d / kTileBlocks;
         d_tiles = (int64_t)d * nb_f / kTileBlocks;
         payload = (2 * gu_tiles + d_tiles) * tile_bytes;
         return true;
     }
-    int64_t gate_tile(int64_t t) const { return 2 * t * tile_bytes; }
-    int64_t up_tile(int64_t t) const { return (2 * t + 1) * tile_bytes; }
-    int64_t down_tile(int64_t t) const { return (2 * gu_tiles + t) * tile_bytes; }
+    __host__ __device__ int64_t gate_tile(int64_t t) const { return 2 * t * tile_bytes; }
+    __host__ __device__ int64_t up_tile(int64_t t) const { return (2 * t + 1) * tile_bytes; }
+    __host__ __device__ int64_t down_tile(int64_t t) const { return (2 * gu_tiles + t) * tile_bytes; }
+    // Block (row r, column block cb) of each matrix -> (tile, lane).  gate/up:
+    // row-major block order; down: column-block-major (all d rows of column
+    // block 0, then column block 1, ...), so one column block is d/64 whole tiles.
+    __host__ __device__ void gu_block(int64_t r, int cb, int64_t* tile, int* lane) const {
+        const int64_t L = r * nb_d + cb;
+        *tile = L / kTileBlocks;
+        *lane = (int)(L % kTileBlocks);
+    }
+    __host__ __device__ void down_block(int64_t r, int cb, int64_t* tile, int* lane) const {
+        const int64_t L = (int64_t)cb * d + r;
+        *tile = L / kTileBlocks;
+        *lane = (int)(L % kTileBlocks);
+    }
 };
 
 // Byte offsets inside one tile for block i (0..63).
@@ -52,7 +65,6 @@ __host__ __device__ inline int q4_scale(int i) { return 16 * kTileBlocks + 2 * i
 
 // Device error word bits.
 constexpr int kErrMiss = 1;     // unmapped expert met by a kernel
-constexpr int kErrTimeout = 2;  // bounded wait gave up
 constexpr int kErrBadId = 4;    // expert id out of range in a plan input
 
 // ---- launchers (return hipError_t of the launch) ----
@@ -84,15 +96,18 @@ struct FfnArgs {
     int x_bf16;
     int T;
     // outputs and workspace
-    float* h;               // [T*k + T, f] hidden states
+    float* part;            // [(T*k + T) * (d_ff/16) * d_model] partial rows
     float* y;               // [T, d]
-    unsigned* sync;         // [2] inter-workgroup counters, zero between launches
     int* err;
-    int spin_limit;
 };
 
-// Largest step the fused single-launch decode kernel takes.
+// Largest step the decode kernels take.
 constexpr int kDecodeMaxT = 4;
+
+// Floats of partial-row workspace the decode kernels need for top_k, d_ff, d_model.
+inline int64_t decode_part_floats(int k, int f, int d) {
+    return (int64_t)kDecodeMaxT * (k + 1) * (f / 16) * d;
+}
 
 hipError_t launch_ffn_decode(const Geom& g, const FfnArgs& a, int prec, hipStream_t s);
 

@@ -23,8 +23,7 @@ struct moe_ctx {
     // device state
     int32_t* pt = nullptr;     // [L x E]
     int* err_word = nullptr;
-    unsigned* sync = nullptr;  // [2]
-    float* h = nullptr;        // [(max_T*k + max_T) * f]
+    float* part = nullptr;     // decode partial rows
     float* logits_ws = nullptr;// [max_T * E]
 
     // slot manager (host)
@@ -81,8 +80,8 @@ bool cfg_valid(const moe_config* c, Geom* g, std::string* why) {
     if ((int64_t)c->n_layers * c->n_experts > (1 << 26)) return bad("n_layers * n_experts too large");
     Geom gg;
     if (!gg.init(c->d_model, c->d_ff, c->qtype))
-        return bad("unsupported shape or qtype: d_model/32 and d_ff/32 must be powers of two <= 64, "
-                   "with whole 64-block tiles; qtype Q8_0 or Q4_0");
+        return bad("unsupported shape or qtype: d_model/32 must be a power of two in [4, 64] "
+                   "(d_model 128..2048), d_ff a multiple of 32; qtype Q8_0 or Q4_0");
     if (c->device >= 0) {
         if (!c->slot_pool) return bad("slot_pool is NULL");
         if (((uintptr_t)c->slot_pool) & 255) return bad("slot_pool must be 256-byte aligned");
@@ -108,49 +107,48 @@ moe_status need_device(moe_ctx* c) {
     return MOE_OK;
 }
 
-// Q8_0 / Q4_0 repack between GGUF blocks and the tile layout.
+// Q8_0 / Q4_0 repack between GGUF blocks (row-major, blocks along rows) and
+// the tile layout.
 void repack(const Geom& g, const uint8_t* src, uint8_t* dst, bool to_tiles) {
     const int bb = moe::block_bytes(g.qtype);
-    struct Mat { int64_t rows, nb; int64_t first_tile; int64_t stride; int64_t gguf_off; };
-    const int64_t mat_gguf = (int64_t)g.f * g.nb_d * bb; // bytes of gate (= up) in GGUF order
-    // tile t of matrix m lives at payload offset m.first_tile + t * m.stride
-    Mat mats[3] = {
-        {g.f, g.nb_d, 0, 2 * g.tile_bytes, 0},
-        {g.f, g.nb_d, g.tile_bytes, 2 * g.tile_bytes, mat_gguf},
-        {g.d, g.nb_f, 2 * g.gu_tiles * g.tile_bytes, g.tile_bytes, 2 * mat_gguf},
-    };
-    for (const Mat& m : mats) {
-        const int64_t nblk = m.rows * m.nb;
-        for (int64_t L = 0; L < nblk; L++) {
-            const int64_t t = L / moe::kTileBlocks;
-            const int i = (int)(L % moe::kTileBlocks);
-            uint8_t* tile = nullptr;
-            const uint8_t* ctile = nullptr;
-            const int64_t toff = m.first_tile + t * m.stride;
-            const int64_t goff = m.gguf_off + L * bb;
-            if (to_tiles) tile = dst + toff; else ctile = src + toff;
-            const uint8_t* gsrc = to_tiles ? src + goff : nullptr;
-            uint8_t* gdst = to_tiles ? nullptr : dst + goff;
-            if (g.qtype == MOE_Q8_0) {
-                if (to_tiles) {
-                    memcpy(tile + moe::q8_scale(i), gsrc, 2);
-                    memcpy(tile + moe::q8_lo(i), gsrc + 2, 16);
-                    memcpy(tile + moe::q8_hi(i), gsrc + 18, 16);
+    const int64_t mat_gguf = (int64_t)g.f * g.nb_d * bb;  // bytes of gate (= up) in GGUF order
+    for (int m = 0; m < 3; m++) {
+        const int64_t rows = m < 2 ? g.f : g.d;
+        const int nb = m < 2 ? g.nb_d : g.nb_f;
+        for (int64_t r = 0; r < rows; r++)
+            for (int cb = 0; cb < nb; cb++) {
+                int64_t t;
+                int i;
+                int64_t toff;
+                if (m < 2) {
+                    g.gu_block(r, cb, &t, &i);
+                    toff = m == 0 ? g.gate_tile(t) : g.up_tile(t);
                 } else {
-                    memcpy(gdst, ctile + moe::q8_scale(i), 2);
-                    memcpy(gdst + 2, ctile + moe::q8_lo(i), 16);
-                    memcpy(gdst + 18, ctile + moe::q8_hi(i), 16);
+                    g.down_block(r, cb, &t, &i);
+                    toff = g.down_tile(t);
                 }
-            } else {
-                if (to_tiles) {
-                    memcpy(tile + moe::q4_scale(i), gsrc, 2);
-                    memcpy(tile + moe::q4_nib(i), gsrc + 2, 16);
+                const int64_t goff = m * mat_gguf + (r * nb + cb) * bb;
+                const uint8_t* gs = src + goff;
+                uint8_t* gd = dst + goff;
+                if (g.qtype == MOE_Q8_0) {
+                    const int off[3] = {moe::q8_scale(i), moe::q8_lo(i), moe::q8_hi(i)};
+                    const int len[3] = {2, 16, 16};
+                    int gpos = 0;
+                    for (int k = 0; k < 3; k++) {
+                        if (to_tiles) memcpy(dst + toff + off[k], gs + gpos, len[k]);
+                        else memcpy(gd + gpos, src + toff + off[k], len[k]);
+                        gpos += len[k];
+                    }
                 } else {
-                    memcpy(gdst, ctile + moe::q4_scale(i), 2);
-                    memcpy(gdst + 2, ctile + moe::q4_nib(i), 16);
+                    if (to_tiles) {
+                        memcpy(dst + toff + moe::q4_scale(i), gs, 2);
+                        memcpy(dst + toff + moe::q4_nib(i), gs + 2, 16);
+                    } else {
+                        memcpy(gd, src + toff + moe::q4_scale(i), 2);
+                        memcpy(gd + 2, src + toff + moe::q4_nib(i), 16);
+                    }
                 }
             }
-        }
     }
 }
 
@@ -161,8 +159,6 @@ moe_status wait_pending_fills(moe_ctx* c, hipStream_t s) {
     }
     return MOE_OK;
 }
-
-constexpr int kSpinLimit = 1 << 22;
 
 }  // namespace
 
@@ -218,8 +214,7 @@ void moe_destroy(moe_ctx* c) {
         (void)hipDeviceSynchronize();
         if (c->pt) (void)hipFree(c->pt);
         if (c->err_word) (void)hipFree(c->err_word);
-        if (c->sync) (void)hipFree(c->sync);
-        if (c->h) (void)hipFree(c->h);
+        if (c->part) (void)hipFree(c->part);
         if (c->logits_ws) (void)hipFree(c->logits_ws);
         if (c->release_ev) (void)hipEventDestroy(c->release_ev);
         for (auto& p : c->fills) (void)hipEventDestroy(p.ev);
@@ -253,14 +248,13 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         const int64_t T = cfg->max_tokens;
         if (hipMalloc(&c->pt, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->err_word, sizeof(int)) != hipSuccess) return cleanup(MOE_ENOMEM);
-        if (hipMalloc(&c->sync, 4 * sizeof(unsigned)) != hipSuccess) return cleanup(MOE_ENOMEM);
-        if (hipMalloc(&c->h, sizeof(float) * (size_t)(T * cfg->top_k + T) * cfg->d_ff) != hipSuccess)
+        if (hipMalloc(&c->part, sizeof(float) * (size_t)moe::decode_part_floats(cfg->top_k, cfg->d_ff, cfg->d_model)) !=
+            hipSuccess)
             return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->logits_ws, sizeof(float) * (size_t)T * cfg->n_experts) != hipSuccess)
             return cleanup(MOE_ENOMEM);
         if (hipMemset(c->pt, 0xFF, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_EHIP);
         if (hipMemset(c->err_word, 0, sizeof(int)) != hipSuccess) return cleanup(MOE_EHIP);
-        if (hipMemset(c->sync, 0, 4 * sizeof(unsigned)) != hipSuccess) return cleanup(MOE_EHIP);
         if (hipEventCreateWithFlags(&c->release_ev, hipEventDisableTiming) != hipSuccess) return cleanup(MOE_EHIP);
         if (hipDeviceSynchronize() != hipSuccess) return cleanup(MOE_EHIP);
     }
@@ -454,11 +448,9 @@ moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     a.x = x;
     a.x_bf16 = x_dtype == MOE_BF16;
     a.T = (int)T;
-    a.h = c->h;
+    a.part = c->part;
     a.y = y;
-    a.sync = c->sync;
     a.err = c->err_word;
-    a.spin_limit = kSpinLimit;
     if (T <= moe::kDecodeMaxT) {
         HIP_TRY(c, moe::launch_ffn_decode(c->g, a, prec, s));
         return MOE_OK;
@@ -490,12 +482,6 @@ moe_status moe_check(moe_ctx* c, moe_stream stream) {
     HIP_TRY(c, hipMemcpy(&w, c->err_word, sizeof(int), hipMemcpyDeviceToHost));
     if (!w) return MOE_OK;
     HIP_TRY(c, hipMemset(c->err_word, 0, sizeof(int)));
-    if (w & moe::kErrTimeout) {
-        // a wait gave up: the inter-workgroup counters may be left mid-count
-        HIP_TRY(c, hipMemset(c->sync, 0, 4 * sizeof(unsigned)));
-        HIP_TRY(c, hipDeviceSynchronize());
-        return fail(c, MOE_ETIMEOUT, "a kernel's inter-workgroup wait gave up (error word 0x%x)", w);
-    }
     if (w & moe::kErrMiss) return fail(c, MOE_EMISS, "a kernel met an unmapped expert (error word 0x%x)", w);
     return fail(c, MOE_EINVAL, "a plan input held an expert id out of range (error word 0x%x)", w);
 }
