@@ -239,7 +239,7 @@ def main() -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "ffn_decode_kernel",
+            "kernel": "moe_expert_ffn (ffn_partial_kernel + combine_kernel, one call)",
             "achieved": ffn_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
