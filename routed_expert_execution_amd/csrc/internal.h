@@ -111,4 +111,36 @@ inline int64_t decode_part_floats(int k, int f, int d) {
 
 hipError_t launch_ffn_decode(const Geom& g, const FfnArgs& a, int prec, hipStream_t s);
 
+// Prefill (T > kDecodeMaxT): bucket tile products; see ffn_prefill.hip.
+constexpr int kPrefillBM = 64;
+
+struct PrefillArgs {
+    Geom g;
+    const uint8_t* pool;
+    int64_t payload_bytes;
+    const int32_t* pt;
+    int layer, E, n_slots;
+    const uint8_t* shared;
+    const int32_t* n_active;
+    const int32_t* experts;
+    const int32_t* offsets;
+    const int32_t* entries;
+    const float* topk_w;
+    int k;
+    const void* x;
+    int x_bf16;
+    int T, d, f;
+    int gemm_min;       // buckets with at least this many tokens use the matrix cores (bf16 mode)
+    float* h;           // [T*k + T, f] hidden rows per bucket entry (+ shared per token)
+    float* part;        // [T*k + T, d] partial output rows
+    int32_t* inv;       // [T*k] plan position of entry t*k + j
+    int32_t* sched;     // [2 * max_tiles] (unit, first row) per m-tile
+    int32_t* n_tiles;   // [1]
+    float* y;
+    int* err;
+};
+
+int prefill_max_tiles(int64_t T, int k, int E, bool shared);
+hipError_t launch_ffn_prefill(const PrefillArgs& a, int prec, hipStream_t s);
+
 }  // namespace moe

@@ -24,6 +24,12 @@ struct moe_ctx {
     int32_t* pt = nullptr;     // [L x E]
     int* err_word = nullptr;
     float* part = nullptr;     // decode partial rows
+    // prefill workspace (max_tokens > 4)
+    float* ph = nullptr;
+    float* ppart = nullptr;
+    int32_t* pinv = nullptr;
+    int32_t* psched = nullptr;  // 2 * max_tiles + 1 (last: tile count)
+    int p_max_tiles = 0;
     float* logits_ws = nullptr;// [max_T * E]
 
     // slot manager (host)
@@ -215,6 +221,10 @@ void moe_destroy(moe_ctx* c) {
         if (c->pt) (void)hipFree(c->pt);
         if (c->err_word) (void)hipFree(c->err_word);
         if (c->part) (void)hipFree(c->part);
+        if (c->ph) (void)hipFree(c->ph);
+        if (c->ppart) (void)hipFree(c->ppart);
+        if (c->pinv) (void)hipFree(c->pinv);
+        if (c->psched) (void)hipFree(c->psched);
         if (c->logits_ws) (void)hipFree(c->logits_ws);
         if (c->release_ev) (void)hipEventDestroy(c->release_ev);
         for (auto& p : c->fills) (void)hipEventDestroy(p.ev);
@@ -253,6 +263,15 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
             return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->logits_ws, sizeof(float) * (size_t)T * cfg->n_experts) != hipSuccess)
             return cleanup(MOE_ENOMEM);
+        if (T > moe::kDecodeMaxT) {
+            const size_t rows = (size_t)(T * cfg->top_k + T);
+            c->p_max_tiles = moe::prefill_max_tiles(T, cfg->top_k, cfg->n_experts, true);
+            if (hipMalloc(&c->ph, sizeof(float) * rows * cfg->d_ff) != hipSuccess) return cleanup(MOE_ENOMEM);
+            if (hipMalloc(&c->ppart, sizeof(float) * rows * cfg->d_model) != hipSuccess) return cleanup(MOE_ENOMEM);
+            if (hipMalloc(&c->pinv, sizeof(int32_t) * (size_t)T * cfg->top_k) != hipSuccess) return cleanup(MOE_ENOMEM);
+            if (hipMalloc(&c->psched, sizeof(int32_t) * (2 * (size_t)c->p_max_tiles + 1)) != hipSuccess)
+                return cleanup(MOE_ENOMEM);
+        }
         if (hipMemset(c->pt, 0xFF, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_EHIP);
         if (hipMemset(c->err_word, 0, sizeof(int)) != hipSuccess) return cleanup(MOE_EHIP);
         if (hipEventCreateWithFlags(&c->release_ev, hipEventDisableTiming) != hipSuccess) return cleanup(MOE_EHIP);
@@ -455,7 +474,36 @@ moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
         HIP_TRY(c, moe::launch_ffn_decode(c->g, a, prec, s));
         return MOE_OK;
     }
-    return fail(c, MOE_EINVAL, "moe_expert_ffn: T > %d not available yet", moe::kDecodeMaxT);
+    moe::PrefillArgs p{};
+    p.g = c->g;
+    p.pool = a.pool;
+    p.payload_bytes = a.payload_bytes;
+    p.pt = a.pt;
+    p.layer = layer;
+    p.E = cf.n_experts;
+    p.n_slots = cf.n_slots;
+    p.shared = a.shared;
+    p.n_active = a.n_active;
+    p.experts = a.experts;
+    p.offsets = a.offsets;
+    p.entries = a.entries;
+    p.topk_w = topk_w;
+    p.k = cf.top_k;
+    p.x = x;
+    p.x_bf16 = a.x_bf16;
+    p.T = (int)T;
+    p.d = cf.d_model;
+    p.f = cf.d_ff;
+    p.gemm_min = cf.gemm_min_tokens;
+    p.h = c->ph;
+    p.part = c->ppart;
+    p.inv = c->pinv;
+    p.sched = c->psched;
+    p.n_tiles = c->psched + 2 * (size_t)c->p_max_tiles;
+    p.y = y;
+    p.err = c->err_word;
+    HIP_TRY(c, moe::launch_ffn_prefill(p, prec, s));
+    return MOE_OK;
 }
 
 moe_status moe_dequant(moe_ctx* c, const void* payload, int32_t prec, float* out, moe_stream stream) {

@@ -1,0 +1,159 @@
+"""GPU parity of the chunk (T > 4) path: bucket tile products on the matrix
+cores (buckets of at least gemm_min tokens, bf16 mode) or FMA dots (smaller
+buckets, and fp32 mode), against the CPU oracle.
+
+Bar: 1e-3 maximum relative error per token row; bitwise-identical outputs
+under any slot assignment.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not H.gpu_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from routed_expert_execution_amd import moe  # noqa: E402
+
+FFN_TOL = 1e-3
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+class Chunk:
+    def __init__(self, wl, T, logits, prec, gemm_min=16, perm_seed=None, x_dtype=None):
+        self.wl, self.T, self.prec = wl, T, prec
+        E, k, d, f = wl["E"], wl["k"], wl["d"], wl["f"]
+        self.x_dtype = x_dtype or wl["x_dtype"]
+        self.x = synth.activations(wl["seed"], T, d, self.x_dtype, 777)
+        self.ids, self.w = oracle.topk(logits, k)
+        self.used = sorted(set(self.ids.reshape(-1).tolist()))
+        self.recs = {e: synth.expert_record(wl["seed"], 0, e, wl["qtype"], d, f) for e in self.used}
+        self.shared = synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True) if wl["shared"] else None
+        n = len(self.used)
+        from routed_expert_execution_amd import moe as m
+        cfg = m.make_config(1, E, k, d, f, H.QT[wl["qtype"]], n, T, device=-1)
+        pb = m.moe_payload_bytes(cfg)
+        self.pool = torch.zeros(n * pb, dtype=torch.uint8, device="cuda")
+        self.ctx = m.Context(1, E, k, d, f, H.QT[wl["qtype"]], n, T, gemm_min_tokens=gemm_min, device=0,
+                             slot_pool=self.pool)
+        self.payloads = {e: torch.from_numpy(H.payload(self.ctx, r)).cuda() for e, r in self.recs.items()}
+        self.sh_dev = H.device_payload(self.ctx, self.shared) if self.shared is not None else None
+        self.x_dev = H.torch_x(self.x, self.x_dtype)
+        self.w_dev = torch.from_numpy(self.w).cuda()
+        self.plan = moe.Plan(self.ctx, T)
+        moe.moe_plan_union(self.ctx, torch.from_numpy(self.ids).cuda(), self.plan)
+
+    def place(self, perm):
+        for i, e in enumerate(self.used):
+            self.ctx.slot(int(perm[i])).copy_(self.payloads[e])
+            moe.moe_slot_bind(self.ctx, 0, e, int(perm[i]))
+
+    def run(self):
+        y = torch.full((self.T, self.wl["d"]), float("nan"), dtype=torch.float32, device="cuda")
+        moe.moe_expert_ffn(self.ctx, 0, self.x_dev, self.plan, self.w_dev, y, shared_payload=self.sh_dev,
+                           prec=self.prec)
+        torch.cuda.synchronize()
+        assert moe.moe_check(self.ctx) == moe.MOE_OK
+        return y.cpu().numpy()
+
+    def reference(self, tokens):
+        wl = self.wl
+        records = [self.recs.get(e) for e in range(wl["E"])]
+        x64 = oracle.x_to_f64(self.x, self.x_dtype)[tokens]
+        return oracle.moe_layer(wl["qtype"], self.prec, records, self.shared, wl["d"], wl["f"], x64,
+                                self.ids[tokens], self.w[tokens])
+
+    def bucket_sizes(self):
+        return np.bincount(self.ids.reshape(-1), minlength=self.wl["E"])
+
+
+@pytest.mark.parametrize("T,prec,gemm_min", [(37, oracle.PREC_BF16, 16), (37, oracle.PREC_F32, 16),
+                                             (100, oracle.PREC_BF16, 16), (100, oracle.PREC_BF16, 1000),
+                                             (5, oracle.PREC_BF16, 2), (200, oracle.PREC_F32, 16)])
+def test_prefill_tiny_shape(T, prec, gemm_min):
+    """Tiny layer (8 experts, top-2, d 256, d_ff 128): buckets of ~9-50 tokens cover
+    both the matrix-core and the FMA tiles, ragged m-tiles and fp32 mode."""
+    wl = dict(synth.workload("tiny"), shared=True)
+    lg = synth.zipf_gumbel_logits(wl["seed"] + T, T, wl["E"], 1.1)
+    _say("prefill tiny", T, prec, gemm_min)
+    c = Chunk(wl, T, lg, prec, gemm_min)
+    c.place(list(range(len(c.used))))
+    y = c.run()
+    tokens = np.arange(T)
+    err = H.max_rel_row_err(y, c.reference(tokens))
+    _say("  buckets", sorted(c.bucket_sizes()[c.used].tolist()), "max rel row err", err)
+    assert np.isfinite(y).all() and err <= FFN_TOL
+
+
+@pytest.mark.parametrize("T,prec", [(24, oracle.PREC_BF16), (24, oracle.PREC_F32)])
+def test_prefill_mtp_q4(T, prec):
+    """Q4_0 experts through the chunk path."""
+    wl = synth.workload("mtp")
+    lg = synth.zipf_gumbel_logits(wl["seed"], T, wl["E"], 1.1)
+    _say("prefill q4", T, prec)
+    c = Chunk(wl, T, lg, prec, gemm_min=4)
+    c.place(list(range(len(c.used))))
+    y = c.run()
+    err = H.max_rel_row_err(y, c.reference(np.arange(T)))
+    _say("  max rel row err", err)
+    assert np.isfinite(y).all() and err <= FFN_TOL
+
+
+def test_prefill_workload_sampled():
+    """The prefill workload at full size: 512 tokens, Zipf(1.1) routes over 256
+    experts, Q8_0, bf16 mode; oracle on 40 sampled tokens (the busiest expert's
+    bucket spans several matrix-core m-tiles, most buckets are under 16)."""
+    wl = synth.workload("prefill")
+    lg = synth.zipf_gumbel_logits(wl["seed"], wl["T"], wl["E"], wl["zipf_s"])
+    c = Chunk(wl, wl["T"], lg, oracle.PREC_BF16)
+    sizes = c.bucket_sizes()
+    _say("prefill full: experts used", len(c.used), "largest buckets", sorted(sizes)[-3:],
+         ">=16:", int((sizes >= 16).sum()))
+    c.place(list(range(len(c.used))))
+    y = c.run()
+    assert np.isfinite(y).all()
+    g = np.random.default_rng(4)
+    tokens = np.sort(g.choice(wl["T"], size=40, replace=False))
+    err = H.max_rel_row_err(y[tokens], c.reference(tokens))
+    _say("  max rel row err", err)
+    assert err <= FFN_TOL
+
+
+def test_prefill_cache_transparency():
+    wl = dict(synth.workload("tiny"), shared=True)
+    T = 150
+    lg = synth.zipf_gumbel_logits(wl["seed"] + 5, T, wl["E"], 1.1)
+    c = Chunk(wl, T, lg, oracle.PREC_BF16)
+    n = len(c.used)
+    c.place(list(range(n)))
+    y0 = c.run()
+    c.place(list(range(n))[::-1])
+    y1 = c.run()
+    c.place(list(np.random.default_rng(2).permutation(n)))
+    y2 = c.run()
+    assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+    assert np.array_equal(y0.view(np.uint32), y2.view(np.uint32))
+
+
+def test_prefill_unmapped_expert_fails_closed():
+    wl = dict(synth.workload("tiny"), shared=True)
+    T = 60
+    lg = synth.zipf_gumbel_logits(wl["seed"] + 9, T, wl["E"], 1.1)
+    c = Chunk(wl, T, lg, oracle.PREC_BF16)
+    c.place(list(range(len(c.used))))
+    victim = c.used[-1]
+    moe.moe_slot_bind(c.ctx, 0, victim, -1)
+    y = torch.empty((T, wl["d"]), dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn(c.ctx, 0, c.x_dev, c.plan, c.w_dev, y, shared_payload=c.sh_dev, prec=oracle.PREC_BF16)
+    assert moe.moe_check(c.ctx) == moe.MOE_EMISS
+    y = y.cpu().numpy()
+    hit = (c.ids == victim).any(axis=1)
+    assert hit.any() and np.isnan(y[hit]).all(axis=1).all() and np.isfinite(y[~hit]).all()
