@@ -1,6 +1,6 @@
 """Benchmark of one routed MoE layer step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|mtp]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|mtp|prefill]
 
 A step is one pass of the whole hot path over one batch: router logits and
 top-k (moe_route), expert-major union (moe_plan_union) and the quantised
@@ -8,7 +8,9 @@ SwiGLU experts with the shared expert and the weighted combine
 (moe_expert_ffn).  Default workload "decode": 256 experts, top-8 plus one
 shared expert, d_model 2048, d_ff 512, Q8_0, one token per step, 38-slot
 (15 %) cache.  "mtp": the same layer with Q4_0 weights, four tokens per step
-with overlapping routes, 89-slot (35 %) cache.
+with overlapping routes, 89-slot (35 %) cache.  "prefill": the same layer,
+Q8_0, 512 tokens per step with Zipf(1.1)-skewed routes, all experts resident,
+bf16 arithmetic on the matrix cores for buckets of 16+ tokens.
 
 Before each timed step (untimed): the step's experts are found by routing it
 once, mapped into the LRU slot cache and filled from the pinned host pack on a
@@ -75,12 +77,21 @@ def cpu_baseline(wl: dict, budget_s: float = 10.0, max_steps: int = 200) -> dict
     E, k, d, f, T = wl["E"], wl["k"], wl["d"], wl["f"], wl["T"]
     wr = synth.router_weights(wl["seed"], E, d) if wl["name"] == "decode" else None
     shared = synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True)
+    prec = oracle.PREC_BF16 if wl["prec"] == "bf16" else oracle.PREC_F32
+    if wl["name"] == "prefill":  # a bounded sample: groups of 8 tokens of one chunk
+        T = 8
+        chunk_x = synth.activations(wl["seed"], wl["T"], d, wl["x_dtype"], 0)
+        chunk_lg = synth.zipf_gumbel_logits(wl["seed"], wl["T"], E, wl["zipf_s"])
     cache: dict = {}
     steps, compute = 0, 0.0
     while steps < max_steps and compute < budget_s:
         s = 50_000 + steps
-        x = synth.activations(wl["seed"], T, d, wl["x_dtype"], s)
-        lg_in = None if wr is not None else synth.mtp_logits(wl["seed"], s, T, E, k, wl["p_shared_route"])
+        if wl["name"] == "prefill":
+            rows = slice((steps * T) % wl["T"], (steps * T) % wl["T"] + T)
+            x, lg_in = chunk_x[rows], chunk_lg[rows]
+        else:
+            x = synth.activations(wl["seed"], T, d, wl["x_dtype"], s)
+            lg_in = None if wr is not None else synth.mtp_logits(wl["seed"], s, T, E, k, wl["p_shared_route"])
         t0 = time.perf_counter()
         x64 = oracle.x_to_f64(x, wl["x_dtype"])
         lg = oracle.router_logits(x64, wr) if wr is not None else lg_in
@@ -93,13 +104,14 @@ def cpu_baseline(wl: dict, budget_s: float = 10.0, max_steps: int = 200) -> dict
                 cache[e] = synth.expert_record(wl["seed"], 0, e, wl["qtype"], d, f)
             recs[e] = cache[e]
         t0 = time.perf_counter()
-        oracle.moe_layer(wl["qtype"], oracle.PREC_F32, recs, shared, d, f, x64, ids, w)
+        oracle.moe_layer(wl["qtype"], prec, recs, shared, d, f, x64, ids, w)
         compute += time.perf_counter() - t0
         steps += 1
     return {"value": steps * T / compute, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{steps} {wl['name']} steps ({steps * T} tokens) of the same workload: fp64 C oracle, "
-                      f"router/top-k/union + {k} routed experts + shared expert per token, "
-                      f"{compute:.1f} s of CPU work"}
+            "sample": (f"{steps} groups of {T} tokens of one 512-token chunk" if wl["name"] == "prefill"
+                       else f"{steps} {wl['name']} steps ({steps * T} tokens)")
+                      + f" of the same workload: fp64 C oracle, router/top-k/union + {k} routed experts + "
+                      f"shared expert per token, {compute:.1f} s of CPU work"}
 
 
 def main() -> int:
@@ -107,7 +119,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=["decode", "mtp"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "mtp", "prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="leave L2 / Infinity Cache warm (labelled)")
     args = ap.parse_args()
@@ -141,6 +153,7 @@ def main() -> int:
         ctx.cfg, synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True))).to(dev)
     t_gen = time.perf_counter() - t_gen
     wr = torch.from_numpy(synth.router_weights(wl["seed"], E, d)).to(dev) if args.workload == "decode" else None
+    prec = moe.MOE_PREC_BF16 if wl["prec"] == "bf16" else moe.MOE_PREC_F32
 
     n_steps = args.warmup + args.steps
     x_all = torch.stack([
@@ -149,6 +162,9 @@ def main() -> int:
     lg_all = None
     if args.workload == "mtp":
         lg_all = torch.stack([torch.from_numpy(synth.mtp_logits(wl["seed"], s, T, E, k, wl["p_shared_route"]))
+                              for s in range(n_steps)]).to(dev)
+    elif args.workload == "prefill":
+        lg_all = torch.stack([torch.from_numpy(synth.zipf_gumbel_logits(wl["seed"] + s, T, E, wl["zipf_s"]))
                               for s in range(n_steps)]).to(dev)
     ids = torch.empty(T, k, dtype=torch.int32, device=dev)
     w = torch.empty(T, k, dtype=torch.float32, device=dev)
@@ -196,7 +212,7 @@ def main() -> int:
         e0.record(stream)
         route_plan(s)
         e1.record(stream)
-        moe.moe_expert_ffn(ctx, 0, x_all[s], plan, w, y, shared_payload=shared)
+        moe.moe_expert_ffn(ctx, 0, x_all[s], plan, w, y, shared_payload=shared, prec=prec)
         e2.record(stream)
         moe.moe_slot_release(ctx, 0)
         n_unique.append(n)
@@ -216,7 +232,8 @@ def main() -> int:
     traffic = _traffic(args.workload)
 
     line = {
-        "metric": "routed MoE-layer tokens/s (batch %d decode step: route + union + expert FFN)" % T,
+        "metric": "routed MoE-layer tokens/s (batch %d %s step: route + union + expert FFN)"
+                  % (T, "prefill" if args.workload == "prefill" else "decode"),
         "value": T / (span.mean() * 1e-6),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -226,7 +243,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 (%s weights dequantised in registers)" % ("q8_0" if qt == moe.MOE_Q8_0 else "q4_0"),
+        "dtype": ("bf16 x bf16 -> f32 (matrix cores), %s weights" if prec == moe.MOE_PREC_BF16
+                  else "f32 (%s weights dequantised in registers)") % ("q8_0" if qt == moe.MOE_Q8_0 else "q4_0"),
         "data": "synthetic (seeded; no checkpoint)",
         "config": {
             "workload": (f"{args.workload}: 1 MoE layer, {E} experts, top-{k} + 1 shared expert, d_model {d}, "
