@@ -65,8 +65,9 @@ typedef struct moe_config {
     int32_t max_tokens;      /* largest T of any call (sizes the workspace), 1..65536 */
     int32_t norm_topk;       /* 1: weights = softmax over the k selected logits;
                                 0: weights = full softmax probability of each selected expert */
-    int32_t gemm_min_tokens; /* PREC_BF16 buckets with at least this many tokens use the
-                                MFMA grouped GEMM, smaller ones the GEMV (default 16; 0 = 16) */
+    int32_t gemm_min_tokens; /* calls of more than 4 tokens, PREC_BF16: buckets with at least
+                                this many tokens run in 64-token MFMA tiles, smaller ones in
+                                16-token tiles (default 16; 0 = 16) */
     int32_t device;          /* HIP device ordinal; -1 = host-only context (slot
                                 bookkeeping only; device entry points return MOE_EINVAL) */
     int32_t reserved;        /* must be 0 */
@@ -204,9 +205,11 @@ moe_status moe_slot_bind(moe_ctx* ctx, int32_t layer, int32_t expert, int32_t sl
  * prec MOE_PREC_F32: weights dequantised exactly (d*q in fp32), fp32 hidden
  *   state, fp32 accumulation.
  * prec MOE_PREC_BF16: weights rounded to bf16 after dequantisation, x and the
- *   hidden state rounded to bf16, fp32 accumulation; buckets of at least
- *   gemm_min_tokens tokens run on the MFMA grouped GEMM, the others on the
- *   GEMV, with the same roundings.
+ *   hidden state rounded to bf16, fp32 accumulation.
+ * Calls of more than 4 tokens run every bucket on the matrix cores (bf16 MFMA,
+ *   or fp32 MFMA in MOE_PREC_F32) in tiles of 16 tokens, or of 64 for buckets
+ *   of at least gemm_min_tokens tokens in MOE_PREC_BF16; up to 4 tokens run
+ *   the GEMV.
  * x: device [T, d_model] (x_dtype).  plan: from moe_plan_union on the same
  * topk ids.  topk_w: device [T, top_k] fp32.  shared_payload: device payload
  * of the always-on shared expert ("Nanite for Experts", §1) or NULL.

@@ -111,8 +111,8 @@ inline int64_t decode_part_floats(int k, int f, int d) {
 
 hipError_t launch_ffn_decode(const Geom& g, const FfnArgs& a, int prec, hipStream_t s);
 
-// Prefill (T > kDecodeMaxT): bucket tile products; see ffn_prefill.hip.
-constexpr int kPrefillBM = 64;
+// Prefill (T > kDecodeMaxT): bucket tiles on the matrix cores; see ffn_prefill.hip.
+constexpr int kPrefillBM = 64;  // tokens per large tile
 
 struct PrefillArgs {
     Geom g;
@@ -130,17 +130,20 @@ struct PrefillArgs {
     const void* x;
     int x_bf16;
     int T, d, f;
-    int gemm_min;       // buckets with at least this many tokens use the matrix cores (bf16 mode)
-    float* h;           // [T*k + T, f] hidden rows per bucket entry (+ shared per token)
-    float* part;        // [T*k + T, d] partial output rows
-    int32_t* inv;       // [T*k] plan position of entry t*k + j
-    int32_t* sched;     // [2 * max_tiles] (unit, first row) per m-tile
-    int32_t* n_tiles;   // [1]
+    int gemm_min;          // bf16 mode: buckets with at least this many tokens use 64-token tiles
+    void* h;               // [T*k + T, f] hidden rows per bucket entry (+ shared per token):
+                           // bf16 in bf16 mode, fp32 otherwise
+    float* part;           // [T*k + T, d] partial output rows
+    int32_t* inv;          // [T*k] plan position of entry t*k + j
+    int32_t* sched_big;    // [2 * big_tiles] (unit, first row) per 64-token tile
+    int32_t* sched_small;  // [2 * small_tiles] (unit, first row) per 16-token tile
+    int32_t* n_tiles;      // [2] tiles of each size
     float* y;
     int* err;
 };
 
-int prefill_max_tiles(int64_t T, int k, int E, bool shared);
+// Upper bounds on the tiles of each size a call of T tokens can need.
+void prefill_max_tiles(int64_t T, int k, int E, bool shared, int* big_tiles, int* small_tiles);
 hipError_t launch_ffn_prefill(const PrefillArgs& a, int prec, hipStream_t s);
 
 }  // namespace moe

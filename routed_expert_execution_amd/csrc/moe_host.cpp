@@ -28,8 +28,8 @@ struct moe_ctx {
     float* ph = nullptr;
     float* ppart = nullptr;
     int32_t* pinv = nullptr;
-    int32_t* psched = nullptr;  // 2 * max_tiles + 1 (last: tile count)
-    int p_max_tiles = 0;
+    int32_t* psched = nullptr;  // big tiles, small tiles, 2 counts
+    int p_big = 0, p_small = 0;
     float* logits_ws = nullptr;// [max_T * E]
 
     // slot manager (host)
@@ -265,11 +265,11 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
             return cleanup(MOE_ENOMEM);
         if (T > moe::kDecodeMaxT) {
             const size_t rows = (size_t)(T * cfg->top_k + T);
-            c->p_max_tiles = moe::prefill_max_tiles(T, cfg->top_k, cfg->n_experts, true);
+            moe::prefill_max_tiles(T, cfg->top_k, cfg->n_experts, true, &c->p_big, &c->p_small);
             if (hipMalloc(&c->ph, sizeof(float) * rows * cfg->d_ff) != hipSuccess) return cleanup(MOE_ENOMEM);
             if (hipMalloc(&c->ppart, sizeof(float) * rows * cfg->d_model) != hipSuccess) return cleanup(MOE_ENOMEM);
             if (hipMalloc(&c->pinv, sizeof(int32_t) * (size_t)T * cfg->top_k) != hipSuccess) return cleanup(MOE_ENOMEM);
-            if (hipMalloc(&c->psched, sizeof(int32_t) * (2 * (size_t)c->p_max_tiles + 1)) != hipSuccess)
+            if (hipMalloc(&c->psched, sizeof(int32_t) * (2 * ((size_t)c->p_big + c->p_small) + 2)) != hipSuccess)
                 return cleanup(MOE_ENOMEM);
         }
         if (hipMemset(c->pt, 0xFF, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_EHIP);
@@ -498,8 +498,9 @@ moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     p.h = c->ph;
     p.part = c->ppart;
     p.inv = c->pinv;
-    p.sched = c->psched;
-    p.n_tiles = c->psched + 2 * (size_t)c->p_max_tiles;
+    p.sched_big = c->psched;
+    p.sched_small = c->psched + 2 * (size_t)c->p_big;
+    p.n_tiles = p.sched_small + 2 * (size_t)c->p_small;
     p.y = y;
     p.err = c->err_word;
     HIP_TRY(c, moe::launch_ffn_prefill(p, prec, s));

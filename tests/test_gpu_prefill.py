@@ -1,6 +1,6 @@
 """GPU parity of the chunk (T > 4) path: bucket tile products on the matrix
-cores (buckets of at least gemm_min tokens, bf16 mode) or FMA dots (smaller
-buckets, and fp32 mode), against the CPU oracle.
+cores: 64-token tiles for buckets of at least gemm_min tokens (bf16 mode), 16-token
+tiles for the rest and for fp32 mode, against the CPU oracle.
 
 Bar: 1e-3 maximum relative error per token row; bitwise-identical outputs
 under any slot assignment.
@@ -80,7 +80,7 @@ class Chunk:
                                              (5, oracle.PREC_BF16, 2), (200, oracle.PREC_F32, 16)])
 def test_prefill_tiny_shape(T, prec, gemm_min):
     """Tiny layer (8 experts, top-2, d 256, d_ff 128): buckets of ~9-50 tokens cover
-    both the matrix-core and the FMA tiles, ragged m-tiles and fp32 mode."""
+    both tile sizes, ragged tiles and fp32 mode."""
     wl = dict(synth.workload("tiny"), shared=True)
     lg = synth.zipf_gumbel_logits(wl["seed"] + T, T, wl["E"], 1.1)
     _say("prefill tiny", T, prec, gemm_min)
@@ -110,7 +110,7 @@ def test_prefill_mtp_q4(T, prec):
 def test_prefill_workload_sampled():
     """The prefill workload at full size: 512 tokens, Zipf(1.1) routes over 256
     experts, Q8_0, bf16 mode; oracle on 40 sampled tokens (the busiest expert's
-    bucket spans several matrix-core m-tiles, most buckets are under 16)."""
+    bucket spans several 64-token tiles, most buckets are under 16)."""
     wl = synth.workload("prefill")
     lg = synth.zipf_gumbel_logits(wl["seed"], wl["T"], wl["E"], wl["zipf_s"])
     c = Chunk(wl, wl["T"], lg, oracle.PREC_BF16)
