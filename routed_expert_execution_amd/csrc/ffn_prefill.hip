@@ -41,26 +41,33 @@ constexpr int SMALL = 16;        // tokens per small tile
 constexpr int WAVES = 4;         // waves per workgroup, 16 features / rows each
 constexpr int COLS = WAVES * 16; // features / output rows per workgroup item
 
-__device__ inline const uint8_t* unit_base(const PrefillArgs& a, int u, int na) {
-    if (u == na) return a.shared;
-    const int e = a.experts[u];
-    if (e < 0 || e >= a.E) return nullptr;
-    const int s = a.pt[(int64_t)a.layer * a.E + e];
-    return (s >= 0 && s < a.n_slots) ? a.pool + (int64_t)s * a.payload_bytes : nullptr;
+// A tile: up to 16 or 64 rows of one bucket (or of the shared expert), as the
+// schedule resolves it, so that a tile kernel reads one record before streaming.
+//   slot  >= 0: the expert's pool slot; kUnmapped: not resident (fail closed);
+//         kShared: the shared expert
+//   first plan position of the tile's first row (routed), or its first token
+//   M     rows in the tile
+struct TileRec {
+    int slot, first, M, pad;
+};
+constexpr int kUnmapped = -1, kShared = -2;
+
+__device__ inline TileRec load_rec(const int32_t* recs, int i) {
+    const int4 v = ((const int4*)recs)[i];
+    return TileRec{v.x, v.y, v.z, v.w};
 }
 
-// Bucket geometry of unit u: first plan position and size.
-__device__ inline void unit_rows(const PrefillArgs& a, int u, int na, int* p0, int* M) {
-    if (u == na) { *p0 = 0; *M = a.T; }
-    else { *p0 = a.offsets[u]; *M = a.offsets[u + 1] - a.offsets[u]; }
+__device__ inline const uint8_t* tile_base(const PrefillArgs& a, const TileRec& t) {
+    if (t.slot == kShared) return a.shared;
+    return t.slot >= 0 ? a.pool + (int64_t)t.slot * a.payload_bytes : nullptr;
 }
 
-// Token and workspace row of bucket row m.
-__device__ inline int row_token(const PrefillArgs& a, int u, int na, int p0, int m) {
-    return u == na ? m : a.entries[p0 + m] / a.k;
+// Token and workspace row of tile row m.
+__device__ inline int row_token(const PrefillArgs& a, const TileRec& t, int m) {
+    return t.slot == kShared ? t.first + m : a.entries[t.first + m] / a.k;
 }
-__device__ inline int row_slot(const PrefillArgs& a, int u, int na, int p0, int m) {
-    return u == na ? a.T * a.k + m : p0 + m;
+__device__ inline int row_slot(const PrefillArgs& a, const TileRec& t, int m) {
+    return t.slot == kShared ? a.T * a.k + t.first + m : t.first + m;
 }
 
 // ---- schedule --------------------------------------------------------------
@@ -86,7 +93,8 @@ __device__ int block_prefix(int v, int* wave_tot, int* total) {
     return r;
 }
 
-// sched_big / sched_small: (unit, first row) per tile; n_tiles = {big, small}.
+// Tile records of each size (sched_big, sched_small) and their counts (n_tiles);
+// the page table is read here, once per bucket.
 __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec) {
     __shared__ int wave_tot[16];
     __shared__ int tot_b, tot_s;
@@ -95,23 +103,30 @@ __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec)
     int base_b = 0, base_s = 0;
     for (int u0 = 0; u0 < n_units; u0 += 1024) {
         const int u = u0 + threadIdx.x;
-        int tb = 0, ts = 0;
+        int tb = 0, ts = 0, slot = kShared, p0 = 0, M = 0;
         if (u < n_units) {
-            int p0, M;
-            unit_rows(a, u, na, &p0, &M);
+            if (u == na) {
+                M = a.T;
+            } else {
+                p0 = a.offsets[u];
+                M = a.offsets[u + 1] - p0;
+                const int e = a.experts[u];
+                slot = kUnmapped;
+                if (e >= 0 && e < a.E) {
+                    const int sl = a.pt[(int64_t)a.layer * a.E + e];
+                    if (sl >= 0 && sl < a.n_slots) slot = sl;
+                }
+                if (slot == kUnmapped) atomicOr(a.err, kErrMiss);
+            }
             if (prec == MOE_PREC_BF16 && M >= a.gemm_min) tb = (M + BIG - 1) / BIG;
             else ts = (M + SMALL - 1) / SMALL;
         }
         const int fb = base_b + block_prefix(tb, wave_tot, &tot_b);
         const int fs = base_s + block_prefix(ts, wave_tot, &tot_s);
-        for (int i = 0; i < tb; i++) {
-            a.sched_big[2 * (fb + i)] = u;
-            a.sched_big[2 * (fb + i) + 1] = i * BIG;
-        }
-        for (int i = 0; i < ts; i++) {
-            a.sched_small[2 * (fs + i)] = u;
-            a.sched_small[2 * (fs + i) + 1] = i * SMALL;
-        }
+        for (int i = 0; i < tb; i++)
+            ((int4*)a.sched_big)[fb + i] = make_int4(slot, p0 + i * BIG, min(BIG, M - i * BIG), 0);
+        for (int i = 0; i < ts; i++)
+            ((int4*)a.sched_small)[fs + i] = make_int4(slot, p0 + i * SMALL, min(SMALL, M - i * SMALL), 0);
         base_b += tot_b;
         base_s += tot_s;
         __syncthreads();
@@ -140,6 +155,13 @@ template <> struct Raw<MOE_Q8_0> {
         s = *(const uint16_t*)(t + q8_scale(i));
     }
     __device__ void zero() { lo = hi = make_uint4(0, 0, 0, 0); s = 0; }
+    // Elements 8j..8j+7 as biased bytes (q + 128), 4 per word.
+    __device__ void biased8(int j, uint32_t& w0, uint32_t& w1) const {
+        const uint4 h = j < 2 ? lo : hi;
+        w0 = ((j & 1) ? h.z : h.x) ^ 0x80808080u;
+        w1 = ((j & 1) ? h.w : h.y) ^ 0x80808080u;
+    }
+    static constexpr float kBias = 128.f;
     // The 32 weights d*q, exact in fp32 (an fp16 scale times an 8-bit code needs
     // 19 significant bits).  Codes are biased to unsigned bytes (q + 128) so each
     // converts in one step; fma(d, q + 128, -128 d) rounds once, to d*q itself.
@@ -162,6 +184,15 @@ template <> struct Raw<MOE_Q4_0> {
         s = *(const uint16_t*)(t + q4_scale(i));
     }
     __device__ void zero() { nib = make_uint4(0, 0, 0, 0); s = 0; }
+    // Elements 8j..8j+7 as biased bytes (q + 8), 4 per word: low nibbles of
+    // bytes 8j.. for j < 2, high nibbles of bytes 8(j - 2).. otherwise.
+    __device__ void biased8(int j, uint32_t& w0, uint32_t& w1) const {
+        const uint32_t a = (j & 1) ? nib.z : nib.x, b = (j & 1) ? nib.w : nib.y;
+        const int sh = j < 2 ? 0 : 4;
+        w0 = (a >> sh) & 0x0F0F0F0Fu;
+        w1 = (b >> sh) & 0x0F0F0F0Fu;
+    }
+    static constexpr float kBias = 8.f;
     // Byte b holds element b (low nibble) and element b + 16 (high nibble),
     // each as q + 8.
     __device__ void values(float (&v)[32]) const {
@@ -184,168 +215,287 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// B operands of the 4 bf16 MFMAs of a block: weights rounded to bf16, MFMA s
-// taking elements 8s..8s+7.
+// B operand of bf16 MFMA j of a block: elements 8j..8j+7, each d*q (exact in
+// fp32: fma(d, q + bias, -bias d) rounds once) rounded to bf16.
 template <int QT>
-__device__ inline void b_operands(const Raw<QT>& r, bf16x8 (&b)[4]) {
-    float v[32];
-    r.values(v);
-#pragma unroll
-    for (int s = 0; s < 4; s++) {
-        const uint4 q = make_uint4(pack_bf16(v[8 * s], v[8 * s + 1]), pack_bf16(v[8 * s + 2], v[8 * s + 3]),
-                                   pack_bf16(v[8 * s + 4], v[8 * s + 5]), pack_bf16(v[8 * s + 6], v[8 * s + 7]));
-        b[s] = __builtin_bit_cast(bf16x8, q);
-    }
-}
-
-// ---- activation rows ------------------------------------------------------------
-
-// 8 consecutive values of a row starting at column c, as bf16 (fp32 rows are
-// rounded to nearest even); zero for a padding row (row < 0).
-__device__ inline bf16x8 row8_bf16(const void* base, bool is_bf16, int64_t pitch, int row, int c) {
-    uint4 q = make_uint4(0, 0, 0, 0);
-    if (row >= 0) {
-        if (is_bf16) {
-            q = *(const uint4*)((const uint16_t*)base + row * pitch + c);
-        } else {
-            const float* p = (const float*)base + row * pitch + c;
-            const float4 f0 = *(const float4*)p, f1 = *(const float4*)(p + 4);
-            q = make_uint4(pack_bf16(f0.x, f0.y), pack_bf16(f0.z, f0.w), pack_bf16(f1.x, f1.y),
-                           pack_bf16(f1.z, f1.w));
-        }
-    }
+__device__ inline bf16x8 b_operand(const Raw<QT>& r, int j) {
+    const float d = f16_bits_to_f32(r.s), o = -Raw<QT>::kBias * d;
+    uint32_t w0, w1;
+    r.biased8(j, w0, w1);
+    auto v = [&](uint32_t w, int i) { return fmaf(d, (float)((w >> (8 * i)) & 0xFF), o); };
+    const uint4 q = make_uint4(pack_bf16(v(w0, 0), v(w0, 1)), pack_bf16(v(w0, 2), v(w0, 3)),
+                               pack_bf16(v(w1, 0), v(w1, 1)), pack_bf16(v(w1, 2), v(w1, 3)));
     return __builtin_bit_cast(bf16x8, q);
 }
 
-// 32 consecutive values of a row starting at column c, as fp32 (bf16 widened
-// exactly); zero for a padding row.
-__device__ inline void row32_f32(const void* base, bool is_bf16, int64_t pitch, int row, int c, float (&v)[32]) {
-    if (row < 0) {
-#pragma unroll
-        for (int j = 0; j < 32; j++) v[j] = 0.f;
-        return;
-    }
-    if (is_bf16) {
+// ---- activation rows ------------------------------------------------------------
+//
+// The 32 values of one row in one K block, as loaded (bf16 pairs or fp32), and
+// converted only when used.  Loads are unconditional (a padding row reads a
+// valid row and is zeroed at conversion) so that a step's loads issue back to
+// back.
+template <bool XB> struct ARaw;
+template <> struct ARaw<true> {
+    uint4 q[4];
+    __device__ void load(const void* base, int64_t pitch, int row, int c) {
         const uint4* p = (const uint4*)((const uint16_t*)base + row * pitch + c);
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const uint4 w = p[q];
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        for (int i = 0; i < 4; i++) q[i] = p[i];
+    }
+    // values 8s..8s+7 as bf16
+    __device__ bf16x8 bf16(int s, bool keep) const {
+        return __builtin_bit_cast(bf16x8, keep ? q[s] : make_uint4(0, 0, 0, 0));
+    }
+    __device__ void f32(float (&v)[32], bool keep) const {
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            const uint32_t w[4] = {q[s].x, q[s].y, q[s].z, q[s].w};
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                v[8 * q + 2 * i] = __uint_as_float(ww[i] << 16);
-                v[8 * q + 2 * i + 1] = __uint_as_float(ww[i] & 0xFFFF0000u);
+                v[8 * s + 2 * i] = keep ? __uint_as_float(w[i] << 16) : 0.f;
+                v[8 * s + 2 * i + 1] = keep ? __uint_as_float(w[i] & 0xFFFF0000u) : 0.f;
             }
         }
-    } else {
+    }
+};
+template <> struct ARaw<false> {
+    float4 f[8];
+    __device__ void load(const void* base, int64_t pitch, int row, int c) {
         const float4* p = (const float4*)((const float*)base + row * pitch + c);
 #pragma unroll
-        for (int q = 0; q < 8; q++) {
-            const float4 f = p[q];
-            v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+        for (int i = 0; i < 8; i++) f[i] = p[i];
+    }
+    // values 8s..8s+7 rounded to bf16 (nearest even)
+    __device__ bf16x8 bf16(int s, bool keep) const {
+        const float4 a = f[2 * s], b = f[2 * s + 1];
+        const uint4 q = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
+        return __builtin_bit_cast(bf16x8, keep ? q : make_uint4(0, 0, 0, 0));
+    }
+    __device__ void f32(float (&v)[32], bool keep) const {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            v[4 * i] = keep ? f[i].x : 0.f;
+            v[4 * i + 1] = keep ? f[i].y : 0.f;
+            v[4 * i + 2] = keep ? f[i].z : 0.f;
+            v[4 * i + 3] = keep ? f[i].w : 0.f;
         }
     }
-}
+};
 
 // ---- the tile product ------------------------------------------------------------
 //
 // One wave: C[16 R tokens][16 columns] for MATS weight matrices sharing the
 // A operand (gate and up: 2; down: 1), over nkb K blocks.  Lane (n, g) owns
 // block g of each step for column n; lane (m, g) the same block of token rows
-// m, m + 16, ...  blk(mat, col, kb, &tile_ptr, &lane_in_tile) locates a block.
+// m, m + 16, ... (arow[r]: a valid row; alive[r]: whether it is a real one).
+// blk(mat, col, kb, &tile_ptr, &lane_in_tile) locates a block.
+//
+// Pipelining: loads complete in order, so a step's compute waits for every load
+// issued before its last operand.  With one row group, a step's weights and
+// activations are both fetched one step ahead; with four (whose activations
+// would need 64 more registers per buffer), the step's activations are issued
+// before the next step's weights.
 
-template <int QT, int PREC, int R, int MATS, class BlockAt>
-__device__ void tile_product(const void* A, bool a_bf16, int64_t a_pitch, const int (&arow)[R], int nkb,
+template <int QT, int PREC, bool XB, int R, int MATS, class BlockAt>
+__device__ void tile_product(const void* A, int64_t a_pitch, const int (&arow)[R], const bool (&alive)[R], int nkb,
                              BlockAt blk, f32x4 (&acc)[MATS][R]) {
+    constexpr bool AHEAD = R == 1;  // activations fetched a step ahead
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int mt = 0; mt < MATS; mt++)
 #pragma unroll
         for (int r = 0; r < R; r++) acc[mt][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kb0 = 0; kb0 < nkb; kb0 += 4) {
-        const int kb = kb0 + g;
-        const bool live = kb < nkb;
-        Raw<QT> raw[MATS];
+    struct Stage {
+        Raw<QT> w[MATS];
+        ARaw<XB> x[AHEAD ? R : 1];
+    };
+    // kb0 + g clamped: a fetch past the end re-reads the last block.
+    auto fetch_w = [&](int kb0, Stage& st) {
+        const int kb = min(kb0 + g, nkb - 1);
 #pragma unroll
         for (int mt = 0; mt < MATS; mt++) {
-            if (live) {
-                const uint8_t* t;
-                int i;
-                blk(mt, n, kb, &t, &i);
-                raw[mt].load(t, i);
-            } else {
-                raw[mt].zero();
-            }
+            const uint8_t* t;
+            int i;
+            blk(mt, n, kb, &t, &i);
+            st.w[mt].load(t, i);
         }
-        const int c = (live ? kb : 0) * kQK;
+    };
+    auto fetch_x = [&](int kb0, ARaw<XB>(&x)[R]) {
+        const int c = min(kb0 + g, nkb - 1) * kQK;
+#pragma unroll
+        for (int r = 0; r < R; r++) x[r].load(A, a_pitch, arow[r], c);
+    };
+    auto compute = [&](int kb0, const Raw<QT>(&w)[MATS], const ARaw<XB>(&x)[R]) {
+        const bool live = kb0 + g < nkb;
         if constexpr (PREC == MOE_PREC_BF16) {
-            bf16x8 b[MATS][4];
 #pragma unroll
-            for (int mt = 0; mt < MATS; mt++) b_operands<QT>(raw[mt], b[mt]);
+            for (int s = 0; s < 4; s++) {
+                bf16x8 b[MATS];
 #pragma unroll
-            for (int r = 0; r < R; r++) {
-                const int row = live ? arow[r] : -1;
+                for (int mt = 0; mt < MATS; mt++) b[mt] = b_operand<QT>(w[mt], s);
 #pragma unroll
-                for (int s = 0; s < 4; s++) {
-                    const bf16x8 av = row8_bf16(A, a_bf16, a_pitch, row, c + 8 * s);
+                for (int r = 0; r < R; r++) {
+                    const bf16x8 av = x[r].bf16(s, live && alive[r]);
 #pragma unroll
                     for (int mt = 0; mt < MATS; mt++)
-                        acc[mt][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[mt][s], acc[mt][r], 0, 0, 0);
+                        acc[mt][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[mt], acc[mt][r], 0, 0, 0);
                 }
             }
         } else {
             static_assert(R == 1, "fp32 tiles are 16 tokens");
-            float w[MATS][32], x[32];
+            float xv[32];
+            x[0].f32(xv, live && alive[0]);
 #pragma unroll
-            for (int mt = 0; mt < MATS; mt++) raw[mt].values(w[mt]);
-            row32_f32(A, a_bf16, a_pitch, live ? arow[0] : -1, c, x);
+            for (int mt = 0; mt < MATS; mt++) {
+                float wv[32];
+                w[mt].values(wv);
 #pragma unroll
-            for (int j = 0; j < 32; j++)
-#pragma unroll
-                for (int mt = 0; mt < MATS; mt++)
-                    acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[j], w[mt][j], acc[mt][0], 0, 0, 0);
+                for (int j = 0; j < 32; j++)
+                    acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[j], wv[j], acc[mt][0], 0, 0, 0);
+            }
         }
+    };
+    // One step: operands of step kb0 in cur; next step's loads into nxt.
+    auto one = [&](int kb0, Stage& cur, Stage& nxt) {
+        if constexpr (AHEAD) {
+            fetch_w(kb0 + 4, nxt);
+            fetch_x(kb0 + 4, nxt.x);
+            compute(kb0, cur.w, cur.x);
+        } else {
+            ARaw<XB> x[R];
+            fetch_x(kb0, x);
+            fetch_w(kb0 + 4, nxt);
+            compute(kb0, cur.w, x);
+        }
+    };
+    // Two stages, alternating; the loop body has no exit between a fetch and
+    // its use, so the compiler keeps the loads where they are issued.
+    Stage sa, sb;
+    fetch_w(0, sa);
+    if constexpr (AHEAD) fetch_x(0, sa.x);
+    const int n_steps = (nkb + 3) / 4;
+    int kb0 = 0;
+    for (int i = 0; i < n_steps / 2; i++, kb0 += 8) {
+        one(kb0, sa, sb);
+        one(kb0 + 4, sb, sa);
     }
+    if (n_steps & 1) one(kb0, sa, sb);
 }
 
-// Work item i of a launch: (tile, column group of COLS).  Big tiles first.
-struct Item {
-    int u, m0, M, p0;
-    bool big;
-};
+// ---- the bf16 tile product: activations staged through LDS -------------------------
+//
+// The four waves of a workgroup share the tile's token rows, so each step's
+// activation block (16 R rows x 128 columns, bf16) is loaded once per workgroup,
+// 256 contiguous bytes per row, into one of two LDS buffers, and each wave reads
+// its A fragments from there.  One barrier per step: the buffer written during
+// step k was last read during step k - 1.  The barrier orders LDS only, so the
+// next step's weight loads stay in flight across it.
 
-__device__ inline bool item_at(const PrefillArgs& a, int na, int i, int ngroups, Item* it, int* col0) {
-    const int nb = a.n_tiles[0] * ngroups;
-    int ti, rows;
-    const int32_t* sched;
-    if (i < nb) {
-        ti = i / ngroups; sched = a.sched_big; rows = BIG; it->big = true;
-    } else {
-        i -= nb;
-        ti = i / ngroups;
-        if (ti >= a.n_tiles[1]) return false;
-        sched = a.sched_small; rows = SMALL; it->big = false;
+constexpr int APITCH = 128 + 8;  // bf16 per LDS row: 272 bytes, conflict-free 16-byte reads
+
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// srow[q]: source row of tile row threadIdx.x / 16 + 16 q (a valid row; skeep[q]
+// false for padding rows, staged as zeros).  Waves with wlive false take part in
+// the staging and barriers only.
+template <int QT, bool XB, int R, int MATS, class BlockAt>
+__device__ void tile_product_lds(const void* A, int64_t a_pitch, const int (&srow)[R], const bool (&skeep)[R],
+                                 int nkb, bool wlive, BlockAt blk, f32x4 (&acc)[MATS][R]) {
+    __shared__ __attribute__((aligned(16))) __bf16 abuf[2][16 * R][APITCH];
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    const int srow_t = threadIdx.x >> 4, scol = (threadIdx.x & 15) * 8;  // staging: 8 columns per thread
+#pragma unroll
+    for (int mt = 0; mt < MATS; mt++)
+#pragma unroll
+        for (int r = 0; r < R; r++) acc[mt][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto fetch_w = [&](int kb0, Raw<QT>(&w)[MATS]) {
+        const int kb = min(kb0 + g, nkb - 1);
+#pragma unroll
+        for (int mt = 0; mt < MATS; mt++) {
+            const uint8_t* t;
+            int i;
+            blk(mt, n, kb, &t, &i);
+            w[mt].load(t, i);
+        }
+    };
+    // columns [kb0 * 32, kb0 * 32 + 128) of this thread's staging rows; blocks
+    // past nkb (a ragged last step) are zeros
+    struct AStage {
+        uint4 q[R];
+    };
+    auto fetch_a = [&](int kb0, AStage& st) {
+        const int c = kb0 * kQK + scol;
+        const bool in = (kb0 + scol / kQK) < nkb;
+        const int cc = in ? c : 0;
+#pragma unroll
+        for (int q = 0; q < R; q++) {
+            uint4 v;
+            if constexpr (XB) {
+                v = *(const uint4*)((const uint16_t*)A + srow[q] * a_pitch + cc);
+            } else {
+                const float* p = (const float*)A + srow[q] * a_pitch + cc;
+                const float4 f0 = *(const float4*)p, f1 = *(const float4*)(p + 4);
+                v = make_uint4(pack_bf16(f0.x, f0.y), pack_bf16(f0.z, f0.w), pack_bf16(f1.x, f1.y),
+                               pack_bf16(f1.z, f1.w));
+            }
+            st.q[q] = (skeep[q] && in) ? v : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_a = [&](int buf, const AStage& st) {
+#pragma unroll
+        for (int q = 0; q < R; q++) *(uint4*)&abuf[buf][srow_t + 16 * q][scol] = st.q[q];
+    };
+    auto compute = [&](int buf, const Raw<QT>(&w)[MATS]) {
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            bf16x8 b[MATS];
+#pragma unroll
+            for (int mt = 0; mt < MATS; mt++) b[mt] = b_operand<QT>(w[mt], s);
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                const bf16x8 av = *(const bf16x8*)&abuf[buf][16 * r + n][kQK * g + 8 * s];
+#pragma unroll
+                for (int mt = 0; mt < MATS; mt++)
+                    acc[mt][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[mt], acc[mt][r], 0, 0, 0);
+            }
+        }
+    };
+    // step k: weights of k in wc, activations of k in LDS buffer k & 1; loads
+    // for k + 1 issued first
+    auto one = [&](int kb0, int buf, Raw<QT>(&wc)[MATS], Raw<QT>(&wn)[MATS]) {
+        AStage st;
+        fetch_a(kb0 + 4, st);
+        if (wlive) fetch_w(kb0 + 4, wn);
+        if (wlive) compute(buf, wc);
+        store_a(buf ^ 1, st);
+        lds_barrier();
+    };
+    Raw<QT> wa[MATS], wb[MATS];
+    {
+        AStage st;
+        fetch_a(0, st);
+        if (wlive) fetch_w(0, wa);
+        store_a(0, st);
+        lds_barrier();
     }
-    *col0 = (i % ngroups) * COLS;
-    it->u = sched[2 * ti];
-    it->m0 = sched[2 * ti + 1];
-    int Mu;
-    unit_rows(a, it->u, na, &it->p0, &Mu);
-    it->M = min(rows, Mu - it->m0);
-    return true;
+    const int n_steps = (nkb + 3) / 4;
+    int kb0 = 0;
+    for (int i = 0; i < n_steps / 2; i++, kb0 += 8) {
+        one(kb0, 0, wa, wb);
+        one(kb0 + 4, 1, wb, wa);
+    }
+    if (n_steps & 1) one(kb0, 0, wa, wb);
 }
 
 // ---- gate/up ------------------------------------------------------------------------
 
-template <int QT, int PREC, int R>
-__device__ void gate_up_item(const PrefillArgs& a, int na, const Item& it, const uint8_t* base, int n0) {
+template <int QT, int PREC, bool XB, int R>
+__device__ void gate_up_item(const PrefillArgs& a, const TileRec& t, const uint8_t* base, int n0, bool wlive) {
     const int lane = threadIdx.x & 63, n = lane & 15;
-    int arow[R];
-#pragma unroll
-    for (int r = 0; r < R; r++) {
-        const int m = 16 * r + n;
-        arow[r] = m < it.M ? row_token(a, it.u, na, it.p0, it.m0 + m) : -1;
-    }
     const Geom& G = a.g;
     auto blk = [&](int mt, int col, int kb, const uint8_t** t, int* i) {
         int64_t tile;
@@ -353,15 +503,36 @@ __device__ void gate_up_item(const PrefillArgs& a, int na, const Item& it, const
         *t = base + (mt == 0 ? G.gate_tile(tile) : G.up_tile(tile));
     };
     f32x4 acc[2][R];
-    tile_product<QT, PREC, R, 2>(a.x, a.x_bf16 != 0, a.d, arow, G.nb_d, blk, acc);
+    if constexpr (PREC == MOE_PREC_BF16) {
+        int srow[R];
+        bool skeep[R];
+#pragma unroll
+        for (int q = 0; q < R; q++) {
+            const int m = (threadIdx.x >> 4) + 16 * q;
+            skeep[q] = m < t.M;
+            srow[q] = row_token(a, t, skeep[q] ? m : 0);
+        }
+        tile_product_lds<QT, XB, R, 2>(a.x, a.d, srow, skeep, G.nb_d, wlive, blk, acc);
+    } else {
+        int arow[R];
+        bool alive[R];
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int m = 16 * r + n;
+            alive[r] = m < t.M;
+            arow[r] = row_token(a, t, alive[r] ? m : 0);
+        }
+        tile_product<QT, PREC, XB, R, 2>(a.x, a.d, arow, alive, G.nb_d, blk, acc);
+    }
+    if (!wlive) return;
     // C register e of row group r: token row 16 r + 4 (lane / 16) + e, feature lane % 16
 #pragma unroll
     for (int r = 0; r < R; r++)
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             const int m = 16 * r + 4 * (lane >> 4) + e;
-            if (m < it.M) {
-                const int64_t idx = (int64_t)row_slot(a, it.u, na, it.p0, it.m0 + m) * a.f + n0 + n;
+            if (m < t.M) {
+                const int64_t idx = (int64_t)row_slot(a, t, m) * a.f + n0 + n;
                 const float hv = silu(acc[0][r][e]) * acc[1][r][e];
                 if (PREC == MOE_PREC_BF16) ((__bf16*)a.h)[idx] = (__bf16)hv;
                 else ((float*)a.h)[idx] = hv;
@@ -369,48 +540,40 @@ __device__ void gate_up_item(const PrefillArgs& a, int na, const Item& it, const
         }
 }
 
-template <int QT, int PREC>
-__global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
-    const int na = *a.n_active;
+// BIGT: the 64-token tiles (bf16 mode), else the 16-token tiles.  Each size is
+// its own launch so that the 16-token one keeps to 128 registers.
+template <int QT, int PREC, bool XB, bool BIGT>
+__global__ __launch_bounds__(256, BIGT ? 2 : (PREC == MOE_PREC_BF16 ? 4 : 3)) void prefill_gate_up_kernel(PrefillArgs a) {
     const int ngroups = (a.f + COLS - 1) / COLS;
     const int wave = threadIdx.x >> 6;
-    for (int i = blockIdx.x;; i += gridDim.x) {
-        Item it;
-        int c0;
-        if (!item_at(a, na, i, ngroups, &it, &c0)) return;
-        const int n0 = c0 + 16 * wave;
-        if (n0 >= a.f) continue;
-        const uint8_t* base = unit_base(a, it.u, na);
-        if (!base) {  // fail closed: NaN hidden rows, error word
-            if ((threadIdx.x & 63) == 0) atomicOr(a.err, kErrMiss);
-            for (int j = threadIdx.x & 63; j < it.M * 16; j += 64) {
-                const int64_t idx = (int64_t)row_slot(a, it.u, na, it.p0, it.m0 + j / 16) * a.f + n0 + j % 16;
+    const int n_items = a.n_tiles[BIGT ? 0 : 1] * ngroups;
+    const int32_t* recs = BIGT ? a.sched_big : a.sched_small;
+    for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
+        const TileRec t = load_rec(recs, i / ngroups);
+        const int c0 = (i % ngroups) * COLS;
+        // a wave past d_ff (d_ff not a multiple of COLS) still takes part in the
+        // workgroup's staging, on a valid column group, and stores nothing
+        const bool wlive = c0 + 16 * wave < a.f;
+        const int n0 = wlive ? c0 + 16 * wave : a.f - 16;
+        const uint8_t* base = tile_base(a, t);
+        if (!base) {  // fail closed: NaN hidden rows (the schedule set the error word)
+            if (!wlive) continue;
+            for (int j = threadIdx.x & 63; j < t.M * 16; j += 64) {
+                const int64_t idx = (int64_t)row_slot(a, t, j / 16) * a.f + n0 + j % 16;
                 if (PREC == MOE_PREC_BF16) ((uint16_t*)a.h)[idx] = 0x7FC0;
                 else ((float*)a.h)[idx] = __uint_as_float(0x7FC00000u);
             }
             continue;
         }
-        if constexpr (PREC == MOE_PREC_BF16) {
-            if (it.big) {
-                gate_up_item<QT, PREC, BIG / 16>(a, na, it, base, n0);
-                continue;
-            }
-        }
-        gate_up_item<QT, PREC, 1>(a, na, it, base, n0);
+        gate_up_item<QT, PREC, XB, BIGT ? BIG / 16 : 1>(a, t, base, n0, wlive);
     }
 }
 
 // ---- down ---------------------------------------------------------------------------
 
 template <int QT, int PREC, int R>
-__device__ void down_item(const PrefillArgs& a, int na, const Item& it, const uint8_t* base, int r0) {
+__device__ void down_item(const PrefillArgs& a, const TileRec& t, const uint8_t* base, int r0) {
     const int lane = threadIdx.x & 63, n = lane & 15;
-    int arow[R];
-#pragma unroll
-    for (int r = 0; r < R; r++) {
-        const int m = 16 * r + n;
-        arow[r] = m < it.M ? row_slot(a, it.u, na, it.p0, it.m0 + m) : -1;
-    }
     const Geom& G = a.g;
     auto blk = [&](int, int col, int kb, const uint8_t** t, int* i) {
         int64_t tile;
@@ -418,41 +581,52 @@ __device__ void down_item(const PrefillArgs& a, int na, const Item& it, const ui
         *t = base + G.down_tile(tile);
     };
     f32x4 acc[1][R];
-    tile_product<QT, PREC, R, 1>(a.h, PREC == MOE_PREC_BF16, a.f, arow, G.nb_f, blk, acc);
+    if constexpr (PREC == MOE_PREC_BF16) {
+        int srow[R];
+        bool skeep[R];
+#pragma unroll
+        for (int q = 0; q < R; q++) {
+            const int m = (threadIdx.x >> 4) + 16 * q;
+            skeep[q] = m < t.M;
+            srow[q] = row_slot(a, t, skeep[q] ? m : 0);
+        }
+        tile_product_lds<QT, true, R, 1>(a.h, a.f, srow, skeep, G.nb_f, true, blk, acc);
+    } else {
+        int arow[R];
+        bool alive[R];
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int m = 16 * r + n;
+            alive[r] = m < t.M;
+            arow[r] = row_slot(a, t, alive[r] ? m : 0);
+        }
+        tile_product<QT, PREC, false, R, 1>(a.h, a.f, arow, alive, G.nb_f, blk, acc);
+    }
 #pragma unroll
     for (int r = 0; r < R; r++)
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             const int m = 16 * r + 4 * (lane >> 4) + e;
-            if (m < it.M)
-                a.part[(int64_t)row_slot(a, it.u, na, it.p0, it.m0 + m) * a.d + r0 + n] = acc[0][r][e];
+            if (m < t.M) a.part[(int64_t)row_slot(a, t, m) * a.d + r0 + n] = acc[0][r][e];
         }
 }
 
-template <int QT, int PREC>
-__global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
-    const int na = *a.n_active;
+template <int QT, int PREC, bool BIGT>
+__global__ __launch_bounds__(256, BIGT ? 2 : (PREC == MOE_PREC_BF16 ? 4 : 3)) void prefill_down_kernel(PrefillArgs a) {
     const int ngroups = a.d / COLS;
     const int wave = threadIdx.x >> 6;
-    for (int i = blockIdx.x;; i += gridDim.x) {
-        Item it;
-        int c0;
-        if (!item_at(a, na, i, ngroups, &it, &c0)) return;
-        const int r0 = c0 + 16 * wave;
-        const uint8_t* base = unit_base(a, it.u, na);
+    const int n_items = a.n_tiles[BIGT ? 0 : 1] * ngroups;
+    const int32_t* recs = BIGT ? a.sched_big : a.sched_small;
+    for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
+        const TileRec t = load_rec(recs, i / ngroups);
+        const int r0 = (i % ngroups) * COLS + 16 * wave;
+        const uint8_t* base = tile_base(a, t);
         if (!base) {
-            for (int j = threadIdx.x & 63; j < it.M * 16; j += 64)
-                a.part[(int64_t)row_slot(a, it.u, na, it.p0, it.m0 + j / 16) * a.d + r0 + j % 16] =
-                    __uint_as_float(0x7FC00000u);
+            for (int j = threadIdx.x & 63; j < t.M * 16; j += 64)
+                a.part[(int64_t)row_slot(a, t, j / 16) * a.d + r0 + j % 16] = __uint_as_float(0x7FC00000u);
             continue;
         }
-        if constexpr (PREC == MOE_PREC_BF16) {
-            if (it.big) {
-                down_item<QT, PREC, BIG / 16>(a, na, it, base, r0);
-                continue;
-            }
-        }
-        down_item<QT, PREC, 1>(a, na, it, base, r0);
+        down_item<QT, PREC, BIGT ? BIG / 16 : 1>(a, t, base, r0);
     }
 }
 
@@ -479,20 +653,26 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
 // Workgroups per product launch: several per CU; each loops over the items.
 constexpr int kGrid = 2048;
 
-template <int QT, int PREC>
+template <class K>
+hipError_t launch_items(K kernel, int64_t items, const PrefillArgs& a, hipStream_t s) {
+    if (items <= 0) return hipSuccess;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)std::min<int64_t>(items, kGrid)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int QT, int PREC, bool XB>
 hipError_t launch_qp(const PrefillArgs& a, int big_tiles, int small_tiles, hipStream_t s) {
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, s, a, PREC);
     hipError_t e = hipGetLastError();
+    const int gf = (a.f + COLS - 1) / COLS, gd = a.d / COLS;
+    constexpr bool BF = PREC == MOE_PREC_BF16;  // 64-token tiles only in bf16 mode
+    if constexpr (BF)
+        if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, true>, (int64_t)big_tiles * gf, a, s);
+    if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, false>, (int64_t)small_tiles * gf, a, s);
+    if constexpr (BF)
+        if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, true>, (int64_t)big_tiles * gd, a, s);
+    if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, false>, (int64_t)small_tiles * gd, a, s);
     if (e != hipSuccess) return e;
-    const int bt = PREC == MOE_PREC_BF16 ? big_tiles : 0;
-    const int64_t gu_items = (int64_t)(bt + small_tiles) * ((a.f + COLS - 1) / COLS);
-    const int64_t dn_items = (int64_t)(bt + small_tiles) * (a.d / COLS);
-    hipLaunchKernelGGL((prefill_gate_up_kernel<QT, PREC>), dim3((unsigned)std::min<int64_t>(gu_items, kGrid)),
-                       dim3(256), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_down_kernel<QT, PREC>), dim3((unsigned)std::min<int64_t>(dn_items, kGrid)),
-                       dim3(256), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(prefill_combine_kernel, dim3((a.d / 4 + 255) / 256, a.T), dim3(256), 0, s, a);
     return hipGetLastError();
 }
@@ -510,11 +690,17 @@ hipError_t launch_ffn_prefill(const PrefillArgs& a, int prec, hipStream_t s) {
     if (a.d % COLS || a.f % 16) return hipErrorInvalidValue;
     int bt, st;
     prefill_max_tiles(a.T, a.k, a.E, a.shared != nullptr, &bt, &st);
-    if (a.g.qtype == MOE_Q8_0)
-        return prec == MOE_PREC_BF16 ? launch_qp<MOE_Q8_0, MOE_PREC_BF16>(a, bt, st, s)
-                                     : launch_qp<MOE_Q8_0, MOE_PREC_F32>(a, bt, st, s);
-    return prec == MOE_PREC_BF16 ? launch_qp<MOE_Q4_0, MOE_PREC_BF16>(a, bt, st, s)
-                                 : launch_qp<MOE_Q4_0, MOE_PREC_F32>(a, bt, st, s);
+    const bool xb = a.x_bf16 != 0, bf = prec == MOE_PREC_BF16;
+    if (a.g.qtype == MOE_Q8_0) {
+        if (bf) return xb ? launch_qp<MOE_Q8_0, MOE_PREC_BF16, true>(a, bt, st, s)
+                          : launch_qp<MOE_Q8_0, MOE_PREC_BF16, false>(a, bt, st, s);
+        return xb ? launch_qp<MOE_Q8_0, MOE_PREC_F32, true>(a, bt, st, s)
+                  : launch_qp<MOE_Q8_0, MOE_PREC_F32, false>(a, bt, st, s);
+    }
+    if (bf) return xb ? launch_qp<MOE_Q4_0, MOE_PREC_BF16, true>(a, bt, st, s)
+                      : launch_qp<MOE_Q4_0, MOE_PREC_BF16, false>(a, bt, st, s);
+    return xb ? launch_qp<MOE_Q4_0, MOE_PREC_F32, true>(a, bt, st, s)
+              : launch_qp<MOE_Q4_0, MOE_PREC_F32, false>(a, bt, st, s);
 }
 
 }  // namespace moe

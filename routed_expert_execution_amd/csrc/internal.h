@@ -135,8 +135,8 @@ struct PrefillArgs {
                            // bf16 in bf16 mode, fp32 otherwise
     float* part;           // [T*k + T, d] partial output rows
     int32_t* inv;          // [T*k] plan position of entry t*k + j
-    int32_t* sched_big;    // [2 * big_tiles] (unit, first row) per 64-token tile
-    int32_t* sched_small;  // [2 * small_tiles] (unit, first row) per 16-token tile
+    int32_t* sched_big;    // [4 * big_tiles] tile records (16-byte aligned), 64-token tiles
+    int32_t* sched_small;  // [4 * small_tiles] tile records (16-byte aligned), 16-token tiles
     int32_t* n_tiles;      // [2] tiles of each size
     float* y;
     int* err;

@@ -269,7 +269,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
             if (hipMalloc(&c->ph, sizeof(float) * rows * cfg->d_ff) != hipSuccess) return cleanup(MOE_ENOMEM);
             if (hipMalloc(&c->ppart, sizeof(float) * rows * cfg->d_model) != hipSuccess) return cleanup(MOE_ENOMEM);
             if (hipMalloc(&c->pinv, sizeof(int32_t) * (size_t)T * cfg->top_k) != hipSuccess) return cleanup(MOE_ENOMEM);
-            if (hipMalloc(&c->psched, sizeof(int32_t) * (2 * ((size_t)c->p_big + c->p_small) + 2)) != hipSuccess)
+            if (hipMalloc(&c->psched, sizeof(int32_t) * (4 * ((size_t)c->p_big + c->p_small) + 2)) != hipSuccess)
                 return cleanup(MOE_ENOMEM);
         }
         if (hipMemset(c->pt, 0xFF, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_EHIP);
@@ -499,8 +499,8 @@ moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     p.part = c->ppart;
     p.inv = c->pinv;
     p.sched_big = c->psched;
-    p.sched_small = c->psched + 2 * (size_t)c->p_big;
-    p.n_tiles = p.sched_small + 2 * (size_t)c->p_small;
+    p.sched_small = c->psched + 4 * (size_t)c->p_big;
+    p.n_tiles = p.sched_small + 4 * (size_t)c->p_small;
     p.y = y;
     p.err = c->err_word;
     HIP_TRY(c, moe::launch_ffn_prefill(p, prec, s));
