@@ -93,10 +93,12 @@ typedef struct moe_plan {
  *
  * Payload layout (how slots hold an expert; "Nanite for Experts", §12 asks
  * for cache geometry chosen with the kernels): the 32-element blocks of each
- * matrix are grouped into tiles of 64 blocks.  gate and up take their blocks
- * in row-major order; down takes them column-block-major (the d_model rows of
- * column block 0, then of column block 1, ...), so that the 32 hidden units a
- * gate/up tile pair run produces meet one contiguous run of down tiles.  A
+ * matrix are grouped into tiles of 64 blocks.  A gate or up tile is 16 rows x
+ * 4 column blocks (block (r, cb) at position 16 * (cb % 4) + r % 16), tiles in
+ * order of row group, then column group; down takes its blocks column-block-
+ * major (the d_model rows of column block 0, then of column block 1, ...), so
+ * that the hidden units a run of gate/up tiles produces meet one contiguous
+ * run of down tiles.  A
  * Q8_0 tile stores the first 16 codes of each of its 64 blocks (64 x 16 B),
  * then the last 16 codes of each (64 x 16 B), then the 64 fp16 scales
  * (2176 B).  A Q4_0 tile stores each block's 16 nibble bytes in GGUF order

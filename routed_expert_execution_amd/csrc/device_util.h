@@ -47,6 +47,15 @@ __device__ inline float seg_sum(float v) {
     return v;
 }
 
+// Sum over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48): the last two
+// steps of seg_sum<64>, same fixed order.
+__device__ inline float cross_row_sum(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // seg_sum with a wave-uniform group size.
 __device__ inline float seg_sum_rt(float v, int seg) {
     switch (seg) {
@@ -58,6 +67,14 @@ __device__ inline float seg_sum_rt(float v, int seg) {
         case 32: return seg_sum<32>(v);
         default: return seg_sum<64>(v);
     }
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS writes but
+// leaves its global loads in flight.
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ inline uint64_t wave_max_u64(uint64_t v) {

@@ -14,9 +14,10 @@
 //        Experts", §5.4; a -1 entry fails closed: NaN partials, error word),
 //     2. issues every weight load of the chunk at once — its gate and up rows
 //        and the matching columns of W_d (all d rows), one 16-byte load per
-//        lane per tile piece — plus the bucket's activations,
+//        lane per tile piece — plus the bucket's activations (into LDS),
 //     3. computes h_c = silu(W_g[c] x) * (W_u[c] x) for each token of the bucket
-//        (lanes of a row summed by DPP), into LDS,
+//        (each lane's blocks summed over its tiles, then the four lanes of a
+//        row and the waves, in fixed order), into LDS,
 //     4. after one workgroup barrier, each lane owns one output row of W_d's
 //        columns: ROWS codes times h_c broadcast from LDS, no cross-lane sum,
 //        and writes the partial row P[entry][chunk][row].
@@ -34,6 +35,7 @@ namespace {
 // per bucket the down tiles are loaded after the gate/up products, so that the
 // activations of four tokens and all tiles are not live at once.
 template <int QT> constexpr int chunk_rows() { return QT == MOE_Q8_0 ? 16 : 32; }
+constexpr int kMaxD = 2048;  // largest d_model
 template <int TG> constexpr int wg_waves() { return 8; }
 template <int TG> constexpr bool down_early() { return TG < 4; }
 // PPW gate/up tile pairs and DPW down tiles per wave are compile-time, so each
@@ -132,34 +134,6 @@ __device__ inline void half_dots(const Tile<MOE_Q8_0>& t, const float (&v)[N][16
     }
 }
 
-template <int PREC>
-__device__ inline void load_x(const FfnArgs& a, int d, int t, int cb, float (&xs)[32]) {
-    if (a.x_bf16) {
-        const uint4* p = (const uint4*)((const uint16_t*)a.x + (int64_t)t * d + cb * kQK);
-#pragma unroll
-        for (int m = 0; m < 4; m++) {
-            const uint4 v = p[m];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                xs[8 * m + 2 * j] = bf16_bits_to_f32(w[j] & 0xFFFF);
-                xs[8 * m + 2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
-            }
-        }
-    } else {
-        const float4* p = (const float4*)((const float*)a.x + (int64_t)t * d + cb * kQK);
-#pragma unroll
-        for (int m = 0; m < 8; m++) {
-            const float4 v = p[m];
-            xs[4 * m] = v.x; xs[4 * m + 1] = v.y; xs[4 * m + 2] = v.z; xs[4 * m + 3] = v.w;
-        }
-        if (PREC == MOE_PREC_BF16) {
-#pragma unroll
-            for (int j = 0; j < 32; j++) xs[j] = round_bf16(xs[j]);
-        }
-    }
-}
-
 struct Grid {
     int units_max;  // routed units allotted (the plan may use fewer) + shared
     int n_chunks;   // d_ff / ROWS
@@ -174,6 +148,8 @@ __global__ __launch_bounds__(wg_waves<TG>() * 64, TG == 1 ? 4 : 2) void ffn_part
     constexpr int ROWS = chunk_rows<QT>();
     constexpr int WAVES = wg_waves<TG>();
     __shared__ float h_c[TG][ROWS];
+    __shared__ __attribute__((aligned(16))) float xl[TG][kMaxD];
+    __shared__ float red[2][WAVES][ROWS / 16][TG][16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int u = blockIdx.x / g.n_chunks, c = blockIdx.x - u * g.n_chunks;
 
@@ -236,40 +212,86 @@ __global__ __launch_bounds__(wg_waves<TG>() * 64, TG == 1 ? 4 : 2) void ffn_part
         }
     };
     if constexpr (down_early<TG>()) load_down();
-    const int cb = lane & (g.nbd - 1);  // column block of this lane within its gate/up row
-    float xs[TG][32];
-#pragma unroll
-    for (int gi = 0; gi < TG; gi++) {
-        if (tok[gi] >= 0) {
-            load_x<PREC>(a, g.d, tok[gi], cb, xs[gi]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 32; j++) xs[gi][j] = 0.f;
+    // The bucket's activations into LDS, fp32 (bf16-rounded in bf16 mode).
+    for (int gi = 0; gi < TG; gi++)
+        for (int i = threadIdx.x * 4; i < g.d; i += WAVES * 64 * 4) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (tok[gi] >= 0) {
+                if (a.x_bf16) {
+                    const uint2 w = *(const uint2*)((const uint16_t*)a.x + (int64_t)tok[gi] * g.d + i);
+                    v = make_float4(bf16_bits_to_f32(w.x & 0xFFFF), bf16_bits_to_f32(w.x >> 16),
+                                    bf16_bits_to_f32(w.y & 0xFFFF), bf16_bits_to_f32(w.y >> 16));
+                } else {
+                    v = *(const float4*)((const float*)a.x + (int64_t)tok[gi] * g.d + i);
+                    if (PREC == MOE_PREC_BF16)
+                        v = make_float4(round_bf16(v.x), round_bf16(v.y), round_bf16(v.z), round_bf16(v.w));
+                }
+            }
+            *(float4*)&xl[gi][i] = v;
         }
-    }
+    lds_barrier();
 
-    // gate/up: this chunk's hidden rows into LDS
-    const int rows_per_tile = kTileBlocks / g.nbd;
+    // gate/up.  Pair pi of the chunk is tile (row group pi / K4, column group
+    // pi % K4); lane (n, j) = (lane % 16, lane / 16) holds column block
+    // 4 (pi % K4) + j of row n.  Each lane sums its blocks' dot products over the
+    // wave's pairs; the four lanes of a row, then the waves (through LDS), are
+    // added in fixed order.
+    constexpr int RG = ROWS / 16;
+    const int K4 = g.nbd >> 2;
+    const int nrow = lane & 15, jb = lane >> 4;
+    float accg[RG][TG], accu[RG][TG];
+#pragma unroll
+    for (int r = 0; r < RG; r++)
+#pragma unroll
+        for (int gi = 0; gi < TG; gi++) accg[r][gi] = accu[r][gi] = 0.f;
 #pragma unroll
     for (int q = 0; q < PPW; q++) {
         const int pi = wave + q * WAVES;
         if (pi >= g.pairs) break;
-        float accg[TG], accu[TG];
-        tile_dots<QT, PREC, TG>(tg[q], xs, accg);
-        tile_dots<QT, PREC, TG>(tu[q], xs, accu);
-        const int r = pi * rows_per_tile + lane / g.nbd;  // row within the chunk
+        const int rgl = pi / K4, cb = 4 * (pi - rgl * K4) + jb;
+        float xs[TG][32];
+#pragma unroll
+        for (int gi = 0; gi < TG; gi++)
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                const float4 v = *(const float4*)&xl[gi][cb * kQK + 4 * m];
+                xs[gi][4 * m] = v.x; xs[gi][4 * m + 1] = v.y; xs[gi][4 * m + 2] = v.z; xs[gi][4 * m + 3] = v.w;
+            }
+        float dg[TG], du[TG];
+        tile_dots<QT, PREC, TG>(tg[q], xs, dg);
+        tile_dots<QT, PREC, TG>(tu[q], xs, du);
+#pragma unroll
+        for (int r = 0; r < RG; r++)
+            if (r == rgl)
+#pragma unroll
+                for (int gi = 0; gi < TG; gi++) {
+                    accg[r][gi] += dg[gi];
+                    accu[r][gi] += du[gi];
+                }
+    }
+#pragma unroll
+    for (int r = 0; r < RG; r++)
 #pragma unroll
         for (int gi = 0; gi < TG; gi++) {
-            const float gs = seg_sum_rt(accg[gi], g.nbd);
-            const float us = seg_sum_rt(accu[gi], g.nbd);
-            if (cb == 0) {
-                float hv = silu(gs) * us;
-                if (PREC == MOE_PREC_BF16) hv = round_bf16(hv);
-                h_c[gi][r] = base ? hv : qnan;
+            const float gs = cross_row_sum(accg[r][gi]), us = cross_row_sum(accu[r][gi]);
+            if (jb == 0) {
+                red[0][wave][r][gi][nrow] = gs;
+                red[1][wave][r][gi][nrow] = us;
             }
         }
-    }
     if constexpr (!down_early<TG>()) load_down();
+    lds_barrier();
+    if (threadIdx.x < ROWS * TG) {
+        const int gi = threadIdx.x / ROWS, rr = threadIdx.x - gi * ROWS, r = rr >> 4, n = rr & 15;
+        float gs = 0.f, us = 0.f;
+        for (int w = 0; w < WAVES; w++) {
+            gs += red[0][w][r][gi][n];
+            us += red[1][w][r][gi][n];
+        }
+        float hv = silu(gs) * us;
+        if (PREC == MOE_PREC_BF16) hv = round_bf16(hv);
+        h_c[gi][rr] = base ? hv : qnan;
+    }
     __syncthreads();
 
     // down: the lane owns output row (pi * 64 + lane)

@@ -393,12 +393,6 @@ __device__ void tile_product(const void* A, int64_t a_pitch, const int (&arow)[R
 
 constexpr int APITCH = 128 + 8;  // bf16 per LDS row: 272 bytes, conflict-free 16-byte reads
 
-__device__ inline void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // srow[q]: source row of tile row threadIdx.x / 16 + 16 q (a valid row; skeep[q]
 // false for padding rows, staged as zeros).  Waves with wlive false take part in
 // the staging and barriers only.

@@ -28,7 +28,7 @@ struct Geom {
         if (qt != MOE_Q8_0 && qt != MOE_Q4_0) return false;
         if (d <= 0 || f <= 0 || d % kQK || f % kQK) return false;
         nb_d = d / kQK; nb_f = f / kQK;
-        // gate/up rows: 4..64 blocks, a power of two, so 16 rows are whole tiles;
+        // gate/up rows: 4..64 blocks, a power of two (whole 4-block column groups);
         // down: column blocks of d rows, d a multiple of 64 and at most 32 tiles
         if (nb_d < 4 || nb_d > 64 || (nb_d & (nb_d - 1))) return false;
         if (d % kTileBlocks || d / kTileBlocks > 32) return false;
@@ -42,12 +42,13 @@ struct Geom {
     __host__ __device__ int64_t up_tile(int64_t t) const { return (2 * t + 1) * tile_bytes; }
     __host__ __device__ int64_t down_tile(int64_t t) const { return (2 * gu_tiles + t) * tile_bytes; }
     // Block (row r, column block cb) of each matrix -> (tile, lane).  gate/up:
-    // row-major block order; down: column-block-major (all d rows of column
-    // block 0, then column block 1, ...), so one column block is d/64 whole tiles.
+    // a tile is 16 rows x 4 column blocks, lane = 16 * (cb % 4) + r % 16, tiles
+    // ordered by row group then column group, so a row group's tiles are
+    // consecutive; down: column-block-major (all d rows of column block 0, then
+    // column block 1, ...), so one column block is d/64 whole tiles.
     __host__ __device__ void gu_block(int64_t r, int cb, int64_t* tile, int* lane) const {
-        const int64_t L = r * nb_d + cb;
-        *tile = L / kTileBlocks;
-        *lane = (int)(L % kTileBlocks);
+        *tile = (r / 16) * (nb_d / 4) + cb / 4;
+        *lane = 16 * (cb % 4) + (int)(r % 16);
     }
     __host__ __device__ void down_block(int64_t r, int cb, int64_t* tile, int* lane) const {
         const int64_t L = (int64_t)cb * d + r;
