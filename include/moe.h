@@ -3,6 +3,7 @@
  * One routed MoE layer step on an AMD Instinct MI355X (gfx950):
  *   moe_route       router logits, top-k, routing weights
  *   moe_plan_union  expert-major union of the routed tokens
+ *   moe_route_union both of the above in one call (fewer launches for <= 4 tokens)
  *   moe_slot_map    host LRU over a bounded pool of expert slots
  *   moe_slot_fill   pinned-host -> slot copy on a side stream + page-table write
  *   moe_expert_ffn  quantised SwiGLU experts read through the page table,
@@ -154,6 +155,16 @@ moe_status moe_route(moe_ctx* ctx, const void* x, int32_t x_dtype, const float* 
  * Out-of-range ids set the error word and are dropped. */
 moe_status moe_plan_union(moe_ctx* ctx, const int32_t* topk_ids, int64_t T, const moe_plan* plan,
                           moe_stream stream);
+
+/* moe_route followed by moe_plan_union on its topk_ids, with the same arguments
+ * and bit-identical results.  The union is the step that turns the tokens'
+ * routes into the expert-major set the experts run over ("Nanite for Experts",
+ * §5.3); for T <= 4 the top-k and the union run in one single-workgroup launch
+ * after the router logits, which saves the launch a decode step would otherwise
+ * pay.  Calls on one context must not overlap (they share its logits workspace). */
+moe_status moe_route_union(moe_ctx* ctx, const void* x, int32_t x_dtype, const float* w_router,
+                           const float* logits_in, int64_t T, int32_t* topk_ids, float* topk_w,
+                           float* logits_out, const moe_plan* plan, moe_stream stream);
 
 /* ---- slots and page table ------------------------------------------------- */
 

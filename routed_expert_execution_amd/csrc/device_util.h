@@ -77,15 +77,27 @@ __device__ inline void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Maximum over the wave of an unsigned 64-bit value, returned to every lane:
+// the partner exchanges of seg_sum<64> (DPP within rows, then the row and
+// half-wave swaps), each keeping the larger value.
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ inline uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ inline uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+    v = max_u64(v, dpp_u64<0xB1>(v));
+    v = max_u64(v, dpp_u64<0x4E>(v));
+    v = max_u64(v, dpp_u64<0x141>(v));
+    v = max_u64(v, dpp_u64<0x140>(v));
+    auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    v = max_u64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);
+    lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    return max_u64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);
 }
 
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }

@@ -535,9 +535,10 @@ __device__ void gate_up_item(const PrefillArgs& a, const TileRec& t, const uint8
 }
 
 // BIGT: the 64-token tiles (bf16 mode), else the 16-token tiles.  Each size is
-// its own launch so that the 16-token one keeps to 128 registers.
+// its own launch so that the 16-token one keeps to 128 registers (the 64-token
+// one to 168).
 template <int QT, int PREC, bool XB, bool BIGT>
-__global__ __launch_bounds__(256, BIGT ? 2 : (PREC == MOE_PREC_BF16 ? 4 : 3)) void prefill_gate_up_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, BIGT ? 3 : (PREC == MOE_PREC_BF16 ? 4 : 3)) void prefill_gate_up_kernel(PrefillArgs a) {
     const int ngroups = (a.f + COLS - 1) / COLS;
     const int wave = threadIdx.x >> 6;
     const int n_items = a.n_tiles[BIGT ? 0 : 1] * ngroups;

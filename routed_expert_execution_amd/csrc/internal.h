@@ -77,6 +77,13 @@ hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int norm, i
 hipError_t launch_plan(const int32_t* ids, int64_t T, int k, int E, const moe_plan& plan, int* err,
                        hipStream_t s);
 hipError_t launch_dequant(const Geom& g, const uint8_t* payload, int prec, float* out, hipStream_t s);
+// Route and union of at most kFusedMaxT tokens: router logits (unless
+// logits_in), then top-k and the union in one single-workgroup launch.  Same
+// results as launch_router_gemv + launch_topk + launch_plan.
+constexpr int kFusedMaxT = 4;
+hipError_t launch_route_union(const void* x, int x_bf16, const float* w_r, const float* logits_in, int64_t T,
+                              int E, int d, int k, int norm, float* logits, int32_t* ids, float* w,
+                              const moe_plan& plan, hipStream_t s);
 
 struct FfnArgs {
     // experts

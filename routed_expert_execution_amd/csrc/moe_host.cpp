@@ -320,6 +320,32 @@ moe_status moe_plan_union(moe_ctx* c, const int32_t* topk_ids, int64_t T, const 
     return MOE_OK;
 }
 
+moe_status moe_route_union(moe_ctx* c, const void* x, int32_t x_dtype, const float* w_router,
+                           const float* logits_in, int64_t T, int32_t* topk_ids, float* topk_w,
+                           float* logits_out, const moe_plan* plan, moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (T < 0 || T > cf.max_tokens)
+        return fail(c, MOE_EINVAL, "moe_route_union: T=%lld outside [0, %d]", (long long)T, cf.max_tokens);
+    if (!plan || !plan->n_active || !plan->experts || !plan->offsets || !plan->entries)
+        return fail(c, MOE_EINVAL, "moe_route_union: null plan array");
+    if (T == 0 || T > moe::kFusedMaxT) {
+        if (moe_status st = moe_route(c, x, x_dtype, w_router, logits_in, T, topk_ids, topk_w, logits_out, stream))
+            return st;
+        return moe_plan_union(c, topk_ids, T, plan, stream);
+    }
+    if (!topk_ids || !topk_w) return fail(c, MOE_EINVAL, "moe_route_union: null output");
+    if (!logits_in) {
+        if (!x || !w_router) return fail(c, MOE_EINVAL, "moe_route_union: need logits_in or both x and w_router");
+        if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(c, MOE_EINVAL, "moe_route_union: bad x_dtype");
+    }
+    DeviceGuard dg(cf.device);
+    float* lo = logits_out ? logits_out : c->logits_ws;
+    HIP_TRY(c, moe::launch_route_union(x, x_dtype == MOE_BF16, w_router, logits_in, T, cf.n_experts, cf.d_model,
+                                       cf.top_k, cf.norm_topk, lo, topk_ids, topk_w, *plan, (hipStream_t)stream));
+    return MOE_OK;
+}
+
 moe_status moe_slot_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n,
                         int32_t* slots_out, uint8_t* miss_out) {
     if (!c) return MOE_EINVAL;

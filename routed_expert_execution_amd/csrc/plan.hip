@@ -11,9 +11,10 @@
 //      among the experts present; experts[], offsets[] and n_active are written.
 //   4. Each wave walks its segment 64 entries at a time; an entry's place is
 //      bucket start + its segment offset + the number of earlier lanes of the
-//      same 64 holding the same expert (found with wave ballots).  Segments
-//      are in entry order and lanes in entry order, so buckets list entries
-//      ascending: the result is unique and bit-reproducible.
+//      same 64 holding the same expert (one wave ballot per bit of the expert
+//      id finds them).  Segments are in entry order and lanes in entry order,
+//      so buckets list entries ascending: the result is unique and
+//      bit-reproducible.
 #include "device_util.h"
 #include "internal.h"
 
@@ -22,6 +23,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kHistInts = 8192;  // LDS ints for the per-wave histograms
+constexpr int kIdsPerLane = 4;   // ids each lane loads at once
 
 __device__ inline int block_exclusive_scan(int v, int* wave_tot, int* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -68,10 +70,19 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
     __syncthreads();
     if (wave < W) {
         const int lo = wave * seg, hi = min(N, lo + seg);
-        for (int i = lo + lane; i < hi; i += 64) {
-            const int e = ids[i];
-            if (e >= 0 && e < E) atomicAdd(&hist[wave * E + e], 1);
-            else atomicOr(err, kErrBadId);
+        for (int i0 = lo; i0 < hi; i0 += 64 * kIdsPerLane) {
+            int e[kIdsPerLane];
+#pragma unroll
+            for (int u = 0; u < kIdsPerLane; u++) {
+                const int i = i0 + 64 * u + lane;
+                e[u] = i < hi ? ids[i] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < kIdsPerLane; u++) {
+                if (i0 + 64 * u + lane >= hi) continue;
+                if (e[u] >= 0 && e[u] < E) atomicAdd(&hist[wave * E + e[u]], 1);
+                else atomicOr(err, kErrBadId);
+            }
         }
     }
     __syncthreads();
@@ -105,27 +116,33 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
     if (wave < W) {
         const int lo = wave * seg, hi = min(N, lo + seg);
         const uint64_t lt = (1ull << lane) - 1ull;
-        for (int i0 = lo; i0 < hi; i0 += 64) {
-            const int i = i0 + lane;
-            const bool valid = i < hi;
-            int e = valid ? ids[i] : -1;
-            const bool ok = valid && e >= 0 && e < E;
-            if (!ok) e = -1;
-            uint64_t mine = 0;
-            uint64_t rem = __ballot(ok);
-            while (rem) {
-                const int leader = __ffsll((unsigned long long)rem) - 1;
-                const int ve = __shfl(e, leader, 64);
-                const uint64_t m = __ballot(ok && e == ve);
-                if (ok && e == ve) mine = m;
-                rem &= ~m;
+        int nbits = 0;
+        while ((1 << nbits) < E) nbits++;
+        for (int i00 = lo; i00 < hi; i00 += 64 * kIdsPerLane) {
+            int ev[kIdsPerLane];
+#pragma unroll
+            for (int u = 0; u < kIdsPerLane; u++) {
+                const int i = i00 + 64 * u + lane;
+                ev[u] = i < hi ? ids[i] : -1;
             }
-            int pos = 0;
-            if (ok) pos = start[e] + hist[wave * E + e] + __popcll(mine & lt);
-            if (ok) {
-                entries[pos] = i;
-                if ((mine >> lane) == 1ull)  // highest lane holding this expert
-                    hist[wave * E + e] += __popcll(mine);
+#pragma unroll
+            for (int u = 0; u < kIdsPerLane; u++) {
+                const int i = i00 + 64 * u + lane;
+                int e = ev[u];
+                const bool ok = i < hi && e >= 0 && e < E;
+                if (!ok) e = 0;
+                // lanes holding the same expert: agree on every bit of the id
+                uint64_t mine = __ballot(ok);
+                for (int b = 0; b < nbits; b++) {
+                    const bool bit = (e >> b) & 1;
+                    const uint64_t m = __ballot(ok && bit);
+                    mine &= bit ? m : ~m;
+                }
+                if (ok) {
+                    entries[start[e] + hist[wave * E + e] + __popcll(mine & lt)] = i;
+                    if ((mine >> lane) == 1ull)  // highest lane holding this expert
+                        hist[wave * E + e] += __popcll(mine);
+                }
             }
         }
     }

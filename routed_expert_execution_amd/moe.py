@@ -64,6 +64,7 @@ def _load() -> C.CDLL:
         "moe_status_string": (C.c_char_p, [C.c_int]),
         "moe_route": (C.c_int, [P, P, I32, P, P, I64, P, P, P, P]),
         "moe_plan_union": (C.c_int, [P, P, I64, planp, P]),
+        "moe_route_union": (C.c_int, [P, P, C.c_int32, P, P, I64, P, P, P, planp, P]),
         "moe_slot_map": (C.c_int, [P, I32, P, I32, P, P]),
         "moe_slot_fill": (C.c_int, [P, I32, I32, I32, P, P]),
         "moe_slot_release": (C.c_int, [P, I32, P]),
@@ -83,7 +84,7 @@ def _load() -> C.CDLL:
 
 _lib = _load()
 EXPORTS = ("moe_payload_bytes", "moe_plan_bytes", "moe_pack_expert", "moe_unpack_expert", "moe_create",
-           "moe_destroy", "moe_last_error", "moe_status_string", "moe_route", "moe_plan_union",
+           "moe_destroy", "moe_last_error", "moe_status_string", "moe_route", "moe_plan_union", "moe_route_union",
            "moe_slot_map", "moe_slot_fill", "moe_slot_release", "moe_slot_bind", "moe_expert_ffn",
            "moe_dequant", "moe_stats", "moe_check", "moe_page_table")
 
@@ -233,6 +234,14 @@ class Plan:
 
 def moe_route(ctx: Context, topk_ids, topk_w, x=None, w_router=None, logits_in=None, logits_out=None,
               stream=None) -> None:
+    T = topk_ids.shape[0]
+    xd = _route_args(ctx, topk_ids, topk_w, x, w_router, logits_in, logits_out)
+    _call(ctx, _lib.moe_route(ctx.handle, _ptr(x), xd, _ptr(w_router), _ptr(logits_in), T, _ptr(topk_ids),
+                              _ptr(topk_w), _ptr(logits_out), _stream(stream)))
+
+
+def _route_args(ctx: Context, topk_ids, topk_w, x, w_router, logits_in, logits_out) -> int:
+    """Shape and dtype checks shared by moe_route and moe_route_union; returns x's dtype code."""
     import torch
     T = topk_ids.shape[0]
     if topk_ids.dtype != torch.int32 or topk_w.dtype != torch.float32:
@@ -251,8 +260,17 @@ def moe_route(ctx: Context, topk_ids, topk_w, x=None, w_router=None, logits_in=N
             raise ValueError("x must be [T, d_model]; w_router float32 [n_experts, d_model]")
     if logits_out is not None and (logits_out.dtype != torch.float32 or tuple(logits_out.shape) != (T, ctx.n_experts)):
         raise ValueError("logits_out must be float32 [T, n_experts]")
-    _call(ctx, _lib.moe_route(ctx.handle, _ptr(x), xd, _ptr(w_router), _ptr(logits_in), T, _ptr(topk_ids),
-                              _ptr(topk_w), _ptr(logits_out), _stream(stream)))
+    return xd
+
+
+def moe_route_union(ctx: Context, topk_ids, topk_w, plan: Plan, x=None, w_router=None, logits_in=None,
+                    logits_out=None, stream=None) -> None:
+    T = topk_ids.shape[0]
+    xd = _route_args(ctx, topk_ids, topk_w, x, w_router, logits_in, logits_out)
+    if plan.entries.numel() < T * ctx.top_k:
+        raise ValueError("plan is too small for T")
+    _call(ctx, _lib.moe_route_union(ctx.handle, _ptr(x), xd, _ptr(w_router), _ptr(logits_in), T, _ptr(topk_ids),
+                                    _ptr(topk_w), _ptr(logits_out), C.byref(plan.c), _stream(stream)))
 
 
 def moe_plan_union(ctx: Context, topk_ids, plan: Plan, stream=None) -> None:
