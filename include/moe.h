@@ -48,7 +48,7 @@ typedef enum moe_status {
     MOE_ENOSLOT = -4,  /* a step needs more slots than are free or unpinned */
     MOE_EMISS = -5,    /* a kernel met an unmapped (layer, expert) page-table entry */
     MOE_EBUSY = -6,    /* the slot is pinned by another (layer, expert) */
-    MOE_ETIMEOUT = -7  /* reserved: no current kernel waits on another workgroup */
+    MOE_ETIMEOUT = -7  /* a decode workgroup's bounded wait for the hidden rows ran out */
 } moe_status;
 
 enum { MOE_Q8_0 = 0, MOE_Q4_0 = 1 };          /* expert weight formats */
@@ -60,7 +60,7 @@ typedef struct moe_config {
     int32_t n_experts;       /* routed experts per layer, 1..1024 */
     int32_t top_k;           /* experts per token, 1..min(n_experts, 32) */
     int32_t d_model;         /* model width: 128, 256, 512, 1024 or 2048 */
-    int32_t d_ff;            /* expert hidden width: a multiple of 32 */
+    int32_t d_ff;            /* expert hidden width: a multiple of 128, at most 2048 */
     int32_t qtype;           /* MOE_Q8_0 or MOE_Q4_0 (routed and shared experts) */
     int32_t n_slots;         /* slots in slot_pool (>= 1) */
     int32_t max_tokens;      /* largest T of any call (sizes the workspace), 1..65536 */
@@ -94,12 +94,10 @@ typedef struct moe_plan {
  *
  * Payload layout (how slots hold an expert; "Nanite for Experts", §12 asks
  * for cache geometry chosen with the kernels): the 32-element blocks of each
- * matrix are grouped into tiles of 64 blocks.  A gate or up tile is 16 rows x
- * 4 column blocks (block (r, cb) at position 16 * (cb % 4) + r % 16), tiles in
- * order of row group, then column group; down takes its blocks column-block-
- * major (the d_model rows of column block 0, then of column block 1, ...), so
- * that the hidden units a run of gate/up tiles produces meet one contiguous
- * run of down tiles.  A
+ * matrix are grouped into tiles of 64 blocks.  Every tile is 16 rows x 4
+ * column blocks (block (r, cb) at position 16 * (cb % 4) + r % 16), tiles in
+ * order of row group, then column group, so 16 consecutive rows of a matrix
+ * are one contiguous run of tiles.  A
  * Q8_0 tile stores the first 16 codes of each of its 64 blocks (64 x 16 B),
  * then the last 16 codes of each (64 x 16 B), then the 64 fp16 scales
  * (2176 B).  A Q4_0 tile stores each block's 16 nibble bytes in GGUF order
@@ -246,8 +244,10 @@ moe_status moe_dequant(moe_ctx* ctx, const void* payload, int32_t prec, float* o
  * out[4] fills enqueued. */
 moe_status moe_stats(const moe_ctx* ctx, uint64_t out[5]);
 
-/* Synchronise `stream`, read and clear the error word: MOE_OK, MOE_EMISS, or
- * MOE_EINVAL for an out-of-range expert id met by moe_plan_union. */
+/* Synchronise `stream`, read and clear the error word: MOE_OK, MOE_EMISS,
+ * MOE_ETIMEOUT (a decode launch's wait for its gate/up workgroups ran out, about
+ * 200 ms; its rows are NaN; the counters are reset here), or MOE_EINVAL for an
+ * out-of-range expert id met by moe_plan_union. */
 moe_status moe_check(moe_ctx* ctx, moe_stream stream);
 
 /* Device address of the page table ([n_layers x n_experts] int32), for tests. */

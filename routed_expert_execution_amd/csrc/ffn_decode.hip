@@ -1,46 +1,80 @@
-// Decode step of the routed experts (T <= 4 tokens): every expert of the step
-// in one launch — the expert-major operator that consumes routed positions and
-// page-table entries for several resident experts at once ("Nanite for
-// Experts", §12, milestone 1; §11.5: the unit of execution should be
-// expert-major, not many separately orchestrated fragments) — followed by a
-// small fixed-order combine launch.
+// Decode step of the routed experts (T <= 4 tokens) in ONE launch: every
+// expert of the step and the weighted merge into the tokens' rows — the
+// expert-major operator that consumes routed positions and page-table entries
+// for several resident experts at once ("Nanite for Experts", §12, milestone
+// 1; §11.5: one expert-major unit of execution rather than many separately
+// orchestrated fragments; §5.5: results merged into the original positions).
 //
-// ffn_partial: one workgroup per (unit, chunk).  A unit is a routed expert of
-//   the plan (ascending expert id) or the shared expert (last); a chunk is
-//   ROWS consecutive hidden rows: 16 for Q8_0 (one code half of a 32-column
-//   block of W_d, which the tile layout stores contiguously) and 32 for Q4_0
-//   (whose nibble bytes hold both halves).  The workgroup
-//     1. resolves the unit's slot through the page table ("Nanite for
-//        Experts", §5.4; a -1 entry fails closed: NaN partials, error word),
-//     2. issues every weight load of the chunk at once — its gate and up rows
-//        and the matching columns of W_d (all d rows), one 16-byte load per
-//        lane per tile piece — plus the bucket's activations (into LDS),
-//     3. computes h_c = silu(W_g[c] x) * (W_u[c] x) for each token of the bucket
-//        (each lane's blocks summed over its tiles, then the four lanes of a
-//        row and the waves, in fixed order), into LDS,
-//     4. after one workgroup barrier, each lane owns one output row of W_d's
-//        columns: ROWS codes times h_c broadcast from LDS, no cross-lane sum,
-//        and writes the partial row P[entry][chunk][row].
-//   No workgroup ever waits for another.
-// combine: y[t, i] = sum over t's entries in plan order (ascending expert) of
-//   w * (sum over chunks of P) + the shared expert's chunks, in one fixed
-//   order that depends only on expert ids and ranks, never on slots.
+// A unit is a routed expert of the plan (ascending expert id) or the shared
+// expert (last).  A hidden row is one (unit, token) pair: row q < T*k is plan
+// position q, row T*k + t is the shared expert on token t.  The launch has two
+// kinds of workgroups:
+//
+//   gate/up workgroup (u, g), one per unit and 16 hidden units: its 16 rows of
+//     W_g and W_u dequantised in registers against the bucket's activations
+//     (LDS); h = silu(W_g x) * (W_u x) for each token of the bucket, stored to
+//     the hidden-row workspace.  Nothing waits for the stores.
+//   down workgroup R, one per 16 output rows: reads the page-table row and the
+//     plan, issues the loads of its 16 rows of every unit's W_d (d_ff/128
+//     contiguous tiles per unit), then polls the hidden rows it needs until
+//     every value has been written, stages them in LDS multiplied by the row's
+//     routing weight (1 for the shared expert), and sums
+//     y[t, rows] = sum over t's hidden rows of W_d[rows] (w h)
+//     in one fixed order that depends only on expert ids and ranks, never on
+//     slots: per lane over its tiles in order, then the four lanes of a row,
+//     then the waves.
+//
+// Every weight byte of the step is requested as soon as its workgroup has the
+// unit's slot: each role reads what it needs from the plan and the whole
+// page-table row in one round of independent loads.  Gate/up workgroups take
+// the first block indices, so their weights lead the memory queue and the down
+// weights arrive about when the hidden rows are ready; they never wait, so the
+// hand-off always completes.
+//
+// Hand-off without counters or cache-wide fences: the workspace holds two
+// halves of hidden rows.  A launch writes h into half p with device-scope (sc1)
+// stores, which are coherent across the XCDs' L2 caches; the down workgroups
+// read half p with device-scope loads until no "pending" word 0xFFFFFFFF (a
+// NaN no arithmetic on finite values produces) is left, and refill half p ^ 1
+// with it for the next launch.  p is the parity of the launch count, a device
+// word each down workgroup increments (without return) when it is done: it
+// reaches the next launch's value only once every down workgroup of this one
+// has read it, and every gate/up workgroup with rows to write has read it
+// before any down workgroup can finish, so it needs no host input.  The poll
+// is bounded in time: past it the error word gets kErrSync and the rows are NaN.
 #include "device_util.h"
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-// Workgroup shape: ROWS hidden rows per chunk, 8 waves.  With up to 4 tokens
-// per bucket the down tiles are loaded after the gate/up products, so that the
-// activations of four tokens and all tiles are not live at once.
-template <int QT> constexpr int chunk_rows() { return QT == MOE_Q8_0 ? 16 : 32; }
-constexpr int kMaxD = 2048;  // largest d_model
-template <int TG> constexpr int wg_waves() { return 8; }
-template <int TG> constexpr bool down_early() { return TG < 4; }
-// PPW gate/up tile pairs and DPW down tiles per wave are compile-time, so each
-// wave holds exactly its tiles in registers: (1,1) for small d_model, (2,4)
-// for Q8_0 at d_model 2048 (16-row chunks), (4,4) otherwise.
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxE = 1024;                       // page-table row staged in LDS (2 words per thread)
+constexpr int kMaxUnits = kDecodeMaxT * 32 + 1;   // routed units (<= T * top_k) + shared
+constexpr int kMaxEnt = kDecodeMaxT * 32;         // plan positions (T * top_k)
+constexpr int kMaxRows = kMaxEnt + kDecodeMaxT;   // hidden rows: plan positions + shared rows
+constexpr int kHCap = 40 * 1024;                  // LDS bytes for staged hidden rows
+static_assert(kMaxUnits + 1 <= kThreads && kMaxRows <= kThreads, "one plan word per thread");
+constexpr int kHPerThread = (kHCap / 16 + kThreads - 1) / kThreads;  // float4 of staged h per thread
+constexpr int kRsrcWord3 = 0x00020000;            // buffer resource: raw 32-bit dwords
+constexpr int kDeviceScope = 16;                  // buffer load cache policy: sc1 (device scope)
+constexpr uint32_t kPending = 0xFFFFFFFFu;        // hidden-row word not yet written in this launch
+
+// LDS of a down workgroup (the gate/up role uses a prefix of the same bytes).
+struct DownLds {
+    int pts[kMaxE];
+    int exp[kMaxUnits + 3];
+    int off[kMaxUnits + 3];
+    int ent[kMaxEnt];                 // plan position -> entry t * k + j
+    float wbe[kMaxEnt];               // routing weight by entry
+    int tok[kMaxRows];                // hidden row -> token
+    float w[kMaxRows];                // hidden row -> weight
+    int flag[4];
+    float red[kWaves][kDecodeMaxT][16];
+    float hs[kHCap / 4];
+};
+constexpr int kLdsBytes = sizeof(DownLds);
 
 template <int QT> struct Tile;
 template <> struct Tile<MOE_Q8_0> {
@@ -52,11 +86,6 @@ template <> struct Tile<MOE_Q8_0> {
         s = *(const uint16_t*)(t + q8_scale(i));
     }
     __device__ void clear() { lo = hi = make_uint4(0, 0, 0, 0); s = 0; }
-    // one code half (codes 0..15 or 16..31 of the lane's block) into lo
-    __device__ void load_half(const uint8_t* t, int i, int half) {
-        lo = *(const uint4*)(t + (half ? q8_hi(i) : q8_lo(i)));
-        s = *(const uint16_t*)(t + q8_scale(i));
-    }
 };
 template <> struct Tile<MOE_Q4_0> {
     uint4 nib;
@@ -74,123 +103,185 @@ template <> struct Tile<MOE_Q4_0> {
 template <int PREC>
 __device__ inline float wq(float code, float s) { return PREC == MOE_PREC_BF16 ? round_bf16(code * s) : code; }
 
-// Dot products of the lane's block with N 32-float vectors v[n].
-template <int QT, int PREC, int N>
-__device__ inline void tile_dots(const Tile<QT>& t, const float (&v)[N][32], float (&acc)[N]) {
-    const float s = f16_bits_to_f32(t.s);
-#pragma unroll
-    for (int n = 0; n < N; n++) acc[n] = 0.f;
-    if constexpr (QT == MOE_Q8_0) {
-        const uint32_t w[8] = {t.lo.x, t.lo.y, t.lo.z, t.lo.w, t.hi.x, t.hi.y, t.hi.z, t.hi.w};
-#pragma unroll
-        for (int m = 0; m < 8; m++)
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const float c = wq<PREC>(i8(w[m], j), s);
-#pragma unroll
-                for (int n = 0; n < N; n++) acc[n] = fmaf(c, v[n][4 * m + j], acc[n]);
-            }
-    } else {
-        const uint32_t w[4] = {t.nib.x, t.nib.y, t.nib.z, t.nib.w};
-#pragma unroll
-        for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const uint32_t b = (w[m] >> (8 * j)) & 0xFF;
-                const float clo = wq<PREC>((float)((int)(b & 15) - 8), s);
-                const float chi = wq<PREC>((float)((int)(b >> 4) - 8), s);
-#pragma unroll
-                for (int n = 0; n < N; n++) {
-                    acc[n] = fmaf(clo, v[n][4 * m + j], acc[n]);
-                    acc[n] = fmaf(chi, v[n][16 + 4 * m + j], acc[n]);
-                }
-            }
-    }
-    if (PREC == MOE_PREC_F32) {
-#pragma unroll
-        for (int n = 0; n < N; n++) acc[n] *= s;
-    }
+// Hides a value from the optimiser where it is used.  Loaded words pass through
+// it so that the compiler neither converts a tile's codes once, outside a loop
+// (32 live floats per tile), nor computes on a loaded value right where it is
+// loaded (a load issued under a condition, or used at once, makes the compiler
+// wait for it -- and, loads completing in order, for every load before it --
+// before the next load is even issued).
+__device__ inline uint32_t opaque(uint32_t w) {
+    asm volatile("" : "+v"(w));
+    return w;
 }
 
-// Dot products of the 16 codes held in t.lo (a Q8_0 half block) with N
-// 16-float vectors.
-template <int PREC, int N>
-__device__ inline void half_dots(const Tile<MOE_Q8_0>& t, const float (&v)[N][16], float (&acc)[N]) {
-    const float s = f16_bits_to_f32(t.s);
+// Dot product of the lane's block with 32 floats at v (LDS, 16-byte aligned),
+// codes in storage order, in two halves of 16 activations.
+template <int QT, int PREC>
+__device__ inline float block_dot(const Tile<QT>& t, const float* v) {
+    const float s = f16_bits_to_f32(opaque(t.s));
+    float acc = 0.f;
 #pragma unroll
-    for (int n = 0; n < N; n++) acc[n] = 0.f;
-    const uint32_t w[4] = {t.lo.x, t.lo.y, t.lo.z, t.lo.w};
+    for (int hf = 0; hf < 2; hf++) {
+        float x[16];
 #pragma unroll
-    for (int m = 0; m < 4; m++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const float c = wq<PREC>(i8(w[m], j), s);
-#pragma unroll
-            for (int n = 0; n < N; n++) acc[n] = fmaf(c, v[n][4 * m + j], acc[n]);
+        for (int m = 0; m < 4; m++) {
+            const float4 q = *(const float4*)(v + 16 * hf + 4 * m);
+            x[4 * m] = q.x; x[4 * m + 1] = q.y; x[4 * m + 2] = q.z; x[4 * m + 3] = q.w;
         }
-    if (PREC == MOE_PREC_F32) {
+        if constexpr (QT == MOE_Q8_0) {
+            const uint4 h4 = hf ? t.hi : t.lo;
+            const uint32_t w[4] = {opaque(h4.x), opaque(h4.y), opaque(h4.z), opaque(h4.w)};
 #pragma unroll
-        for (int n = 0; n < N; n++) acc[n] *= s;
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) acc = fmaf(wq<PREC>(i8(w[m], j), s), x[4 * m + j], acc);
+        } else {
+            // low nibbles are elements 0..15, high nibbles 16..31
+            const uint32_t w[4] = {opaque(t.nib.x), opaque(t.nib.y), opaque(t.nib.z), opaque(t.nib.w)};
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t b = (w[m] >> (8 * j + 4 * hf)) & 15;
+                    acc = fmaf(wq<PREC>((float)((int)b - 8), s), x[4 * m + j], acc);
+                }
+        }
     }
+    return PREC == MOE_PREC_F32 ? acc * s : acc;
 }
 
-struct Grid {
-    int units_max;  // routed units allotted (the plan may use fewer) + shared
-    int n_chunks;   // d_ff / ROWS
-    int pairs;      // gate/up tile pairs per chunk = ROWS * (d_model/32) / 64
-    int dtiles;     // down tiles per W_d column block = d_model / 64
-    int nbd, d, d_ff;
+struct DGrid {
+    int n_down;      // down workgroups: d / 16
+    int n_rg;        // gate/up workgroups per unit: d_ff / 16
+    int units_max;   // routed units allotted (T * top_k, at most E) + shared
+    int gu_tpr;      // gate (or up) tiles per 16 hidden units: d_model / 128
+    int dn_tpr;      // down tiles per 16 output rows: d_ff / 128
+    int nb_rows;     // hidden rows that fit the LDS at once
+    int reset_per;   // pending words each down workgroup writes into the other half
+    int64_t half;    // floats per workspace half
+    int d, f;
     int64_t tile_bytes, down_off;
 };
 
-template <int QT, int PREC, int TG, int PPW, int DPW>
-__global__ __launch_bounds__(wg_waves<TG>() * 64, TG == 1 ? 4 : 2) void ffn_partial_kernel(FfnArgs a, Grid g) {
-    constexpr int ROWS = chunk_rows<QT>();
-    constexpr int WAVES = wg_waves<TG>();
-    __shared__ float h_c[TG][ROWS];
-    __shared__ __attribute__((aligned(16))) float xl[TG][kMaxD];
-    __shared__ float red[2][WAVES][ROWS / 16][TG][16];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int u = blockIdx.x / g.n_chunks, c = blockIdx.x - u * g.n_chunks;
+__device__ inline const uint8_t* slot_base(const FfnArgs& a, int e, const int* pts) {
+    if (e < 0 || e >= a.E) return nullptr;
+    const int slot = pts[e];
+    return (slot >= 0 && slot < a.n_slots) ? a.pool + (int64_t)slot * a.payload_bytes : nullptr;
+}
+__device__ inline const uint8_t* unit_base(const FfnArgs& a, int u, int na, const int* exp, const int* pts) {
+    return u >= na ? a.shared : slot_base(a, exp[u], pts);
+}
 
-    // Level 1: small-table loads that do not depend on each other (indices
-    // clamped into range so all can be in flight together).
-    const int na = *a.n_active;
+// Launch parity: which workspace half this launch writes.
+__device__ inline int launch_parity(uint32_t count, int n_down) { return (int)((count / (uint32_t)n_down) & 1u); }
+
+// Global -> LDS copies issue every load of the thread before the first LDS
+// store, so they cost one memory round trip, not one per element.  Loads are
+// unconditional, from clamped (always valid) addresses.
+
+// The page-table row of the layer (E <= kMaxE = 2 words per thread).
+struct PtRow {
+    uint32_t v[kMaxE / kThreads];
+    __device__ void load(const FfnArgs& a) {
+        const int32_t* row = a.pt + (int64_t)a.layer * a.E;
+#pragma unroll
+        for (int j = 0; j < kMaxE / kThreads; j++) v[j] = (uint32_t)row[min((int)threadIdx.x + j * kThreads, a.E - 1)];
+    }
+    __device__ void store(const FfnArgs& a, int* pts) const {
+#pragma unroll
+        for (int j = 0; j < kMaxE / kThreads; j++) {
+            const int i = threadIdx.x + j * kThreads;
+            const uint32_t w = opaque(v[j]);
+            if (i < a.E) pts[i] = (int)w;
+        }
+    }
+};
+
+// One token's activations (d <= 2048: one 16-byte load per thread: 8 bf16 or 4
+// fp32 values), fp32 in LDS (bf16-rounded in bf16 mode); tok -1 gives zeros.
+template <int PREC>
+struct XRow {
+    uint4 raw;
+    int live;
+    __device__ void load(const FfnArgs& a, int d, int tok) {
+        const int per = a.x_bf16 ? 8 : 4, esz = a.x_bf16 ? 2 : 4;
+        const int i = threadIdx.x * per;
+        live = (tok >= 0 && i < d) ? 1 : 0;
+        const int64_t off = live ? ((int64_t)tok * d + i) * esz : 0;
+        raw = *(const uint4*)((const uint8_t*)a.x + off);
+    }
+    __device__ void store(const FfnArgs& a, int d, float* xr) const {
+        const uint4 w = make_uint4(opaque(raw.x), opaque(raw.y), opaque(raw.z), opaque(raw.w));
+        const bool z = live == 0;
+        if (a.x_bf16) {
+            const int i = threadIdx.x * 8;
+            if (i >= d) return;
+            *(float4*)&xr[i] = z ? make_float4(0.f, 0.f, 0.f, 0.f)
+                                 : make_float4(bf16_bits_to_f32(w.x & 0xFFFF), bf16_bits_to_f32(w.x >> 16),
+                                               bf16_bits_to_f32(w.y & 0xFFFF), bf16_bits_to_f32(w.y >> 16));
+            *(float4*)&xr[i + 4] = z ? make_float4(0.f, 0.f, 0.f, 0.f)
+                                     : make_float4(bf16_bits_to_f32(w.z & 0xFFFF), bf16_bits_to_f32(w.z >> 16),
+                                                   bf16_bits_to_f32(w.w & 0xFFFF), bf16_bits_to_f32(w.w >> 16));
+        } else {
+            const int i = threadIdx.x * 4;
+            if (i >= d) return;
+            float4 v = z ? make_float4(0.f, 0.f, 0.f, 0.f)
+                         : make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                                       __uint_as_float(w.w));
+            if (PREC == MOE_PREC_BF16)
+                v = make_float4(round_bf16(v.x), round_bf16(v.y), round_bf16(v.z), round_bf16(v.w));
+            *(float4*)&xr[i] = v;
+        }
+    }
+};
+
+// ---- gate/up ------------------------------------------------------------------------
+
+template <int QT, int PREC, int TG, int PPW>
+__device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int item, unsigned char* lds_raw) {
+    int* pts = (int*)lds_raw;
+    int* ents = pts + kMaxE;                                 // [T * k] (T > 1)
+    float* xl = (float*)(ents + kMaxEnt);                    // [TG][d]
+    float* red = xl + TG * g.d;                              // [2][kWaves][TG][16]
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int u = item / g.n_rg, rg = item - u * g.n_rg;
+    const bool has_shared = a.shared != nullptr;
+    const int n_ent = a.T * a.k;
+
+    // Level 1, all independent loads: the launch count, the unit's plan
+    // entries, the page-table row, and the activations (one token) or the
+    // step's entry list (several).
+    const uint32_t count = __hip_atomic_load(a.sync + kSyncCount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int na_raw = *a.n_active;
     const int e = a.experts[min(u, a.E - 1)];
     const int o0 = a.offsets[min(u, a.E)];
     const int o1 = a.offsets[min(u + 1, a.E)];
-    const bool has_shared = a.shared != nullptr;
-    if (u >= na + (has_shared ? 1 : 0)) return;  // uniform over the workgroup
-    const bool routed = u < na;
-    // Level 2: the page-table entry and the bucket's token ids.
-    const bool e_ok = e >= 0 && e < a.E;
-    const int slot = a.pt[(int64_t)a.layer * a.E + (e_ok ? e : 0)];
-    const int b0 = routed ? o0 : 0;
-    const int nb = routed ? o1 - o0 : a.T;  // tokens in the bucket, <= T <= TG
-    int tok[TG], prow[TG];
-#pragma unroll
-    for (int gi = 0; gi < TG; gi++) {
-        const bool in = gi < nb;
-        tok[gi] = !in ? -1 : !routed ? gi : a.T == 1 ? 0 : a.entries[b0 + gi] / a.k;
-        prow[gi] = !in ? -1 : routed ? b0 + gi : a.T * a.k + gi;
-    }
-    const uint8_t* base = !routed ? a.shared
-                        : (e_ok && slot >= 0 && slot < a.n_slots) ? a.pool + (int64_t)slot * a.payload_bytes
-                                                                  : nullptr;
-    if (!base && threadIdx.x == 0) atomicOr(a.err, kErrMiss);
-    const float qnan = __uint_as_float(0x7FC00000u);
+    PtRow ptr;
+    ptr.load(a);
+    XRow<PREC> x1;
+    int ent1 = 0;
+    if constexpr (TG == 1) x1.load(a, g.d, 0);
+    else ent1 = a.entries[min((int)threadIdx.x, n_ent - 1)];
+    ptr.store(a, pts);
+    if constexpr (TG == 1) x1.store(a, g.d, xl);
+    else if (threadIdx.x < n_ent) ents[threadIdx.x] = (int)opaque((uint32_t)ent1);
+    lds_barrier();
+    const int par = launch_parity(opaque(count), g.n_down);
+    const int na = min(max((int)opaque((uint32_t)na_raw), 0), g.units_max - (has_shared ? 1 : 0));
+    if (u >= na + (has_shared ? 1 : 0)) return;  // uniform: a unit the step does not have
 
-    // Level 3: every weight load of the chunk, then the activations.  The
-    // chunk's gate/up rows are tiles [c*pairs, (c+1)*pairs) of each matrix.
-    // Its W_d columns: Q8_0 chunk c is code half c%2 of column block c/2;
-    // Q4_0 chunk c is column block c.  A column block is dtiles tiles.
-    const int colblk = QT == MOE_Q8_0 ? c >> 1 : c;
-    Tile<QT> tg[PPW], tu[PPW], td[DPW];
+    // Level 2: the slot, then every weight load of the item.  Pair pi is column
+    // group pi of the row group (gate tile and up tile); lane (n, jb) =
+    // (lane % 16, lane / 16) holds block 4 pi + jb of hidden unit 16 rg + n.
+    const bool routed = u < na;
+    const uint8_t* base = routed ? slot_base(a, e, pts) : a.shared;
+    if (!base && threadIdx.x == 0) atomicOr(a.err, kErrMiss);
+    Tile<QT> tg[PPW], tu[PPW];
 #pragma unroll
     for (int q = 0; q < PPW; q++) {
-        const int pi = wave + q * WAVES;
-        if (base && pi < g.pairs) {
-            const int64_t t = (int64_t)c * g.pairs + pi;
+        const int pi = wave + q * kWaves;
+        if (base && pi < g.gu_tpr) {
+            const int64_t t = (int64_t)rg * g.gu_tpr + pi;
             tg[q].load(base + 2 * t * g.tile_bytes, lane);
             tu[q].load(base + (2 * t + 1) * g.tile_bytes, lane);
         } else {
@@ -198,227 +289,269 @@ __global__ __launch_bounds__(wg_waves<TG>() * 64, TG == 1 ? 4 : 2) void ffn_part
             tu[q].clear();
         }
     }
-    auto load_down = [&]() {
+    const int b0 = routed ? o0 : 0;
+    const int nb = routed ? min(max(o1 - o0, 0), TG) : a.T;  // tokens of the bucket
+    if constexpr (TG > 1) {
+        // the bucket's activations, issued after the weights (loads complete in order)
+        XRow<PREC> xs[TG];
 #pragma unroll
-        for (int q = 0; q < DPW; q++) {
-            const int pi = wave + q * WAVES;
-            if (base && pi < g.dtiles) {
-                const uint8_t* tp = base + g.down_off + ((int64_t)colblk * g.dtiles + pi) * g.tile_bytes;
-                if constexpr (QT == MOE_Q8_0) td[q].load_half(tp, lane, c & 1);
-                else td[q].load(tp, lane);
-            } else {
-                td[q].clear();
-            }
-        }
-    };
-    if constexpr (down_early<TG>()) load_down();
-    // The bucket's activations into LDS, fp32 (bf16-rounded in bf16 mode).
-    for (int gi = 0; gi < TG; gi++)
-        for (int i = threadIdx.x * 4; i < g.d; i += WAVES * 64 * 4) {
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (tok[gi] >= 0) {
-                if (a.x_bf16) {
-                    const uint2 w = *(const uint2*)((const uint16_t*)a.x + (int64_t)tok[gi] * g.d + i);
-                    v = make_float4(bf16_bits_to_f32(w.x & 0xFFFF), bf16_bits_to_f32(w.x >> 16),
-                                    bf16_bits_to_f32(w.y & 0xFFFF), bf16_bits_to_f32(w.y >> 16));
-                } else {
-                    v = *(const float4*)((const float*)a.x + (int64_t)tok[gi] * g.d + i);
-                    if (PREC == MOE_PREC_BF16)
-                        v = make_float4(round_bf16(v.x), round_bf16(v.y), round_bf16(v.z), round_bf16(v.w));
-                }
-            }
-            *(float4*)&xl[gi][i] = v;
-        }
-    lds_barrier();
+        for (int gi = 0; gi < TG; gi++)
+            xs[gi].load(a, g.d, gi >= nb ? -1 : !routed ? gi : min(max(ents[min(b0 + gi, n_ent - 1)] / a.k, 0), a.T - 1));
+#pragma unroll
+        for (int gi = 0; gi < TG; gi++) xs[gi].store(a, g.d, xl + gi * g.d);
+        lds_barrier();
+    }
 
-    // gate/up.  Pair pi of the chunk is tile (row group pi / K4, column group
-    // pi % K4); lane (n, j) = (lane % 16, lane / 16) holds column block
-    // 4 (pi % K4) + j of row n.  Each lane sums its blocks' dot products over the
-    // wave's pairs; the four lanes of a row, then the waves (through LDS), are
-    // added in fixed order.
-    constexpr int RG = ROWS / 16;
-    const int K4 = g.nbd >> 2;
-    const int nrow = lane & 15, jb = lane >> 4;
-    float accg[RG][TG], accu[RG][TG];
+    // Per lane: sum over the wave's pairs; then the four lanes of a row, then
+    // the waves (through LDS), in fixed order.
+    const int n = lane & 15, jb = lane >> 4;
+    float accg[TG], accu[TG];
 #pragma unroll
-    for (int r = 0; r < RG; r++)
-#pragma unroll
-        for (int gi = 0; gi < TG; gi++) accg[r][gi] = accu[r][gi] = 0.f;
+    for (int gi = 0; gi < TG; gi++) accg[gi] = accu[gi] = 0.f;
 #pragma unroll
     for (int q = 0; q < PPW; q++) {
-        const int pi = wave + q * WAVES;
-        if (pi >= g.pairs) break;
-        const int rgl = pi / K4, cb = 4 * (pi - rgl * K4) + jb;
-        float xs[TG][32];
-#pragma unroll
-        for (int gi = 0; gi < TG; gi++)
-#pragma unroll
-            for (int m = 0; m < 8; m++) {
-                const float4 v = *(const float4*)&xl[gi][cb * kQK + 4 * m];
-                xs[gi][4 * m] = v.x; xs[gi][4 * m + 1] = v.y; xs[gi][4 * m + 2] = v.z; xs[gi][4 * m + 3] = v.w;
-            }
-        float dg[TG], du[TG];
-        tile_dots<QT, PREC, TG>(tg[q], xs, dg);
-        tile_dots<QT, PREC, TG>(tu[q], xs, du);
-#pragma unroll
-        for (int r = 0; r < RG; r++)
-            if (r == rgl)
-#pragma unroll
-                for (int gi = 0; gi < TG; gi++) {
-                    accg[r][gi] += dg[gi];
-                    accu[r][gi] += du[gi];
-                }
-    }
-#pragma unroll
-    for (int r = 0; r < RG; r++)
+        const int pi = wave + q * kWaves;
+        if (pi >= g.gu_tpr) break;
+        const int cb = 4 * pi + jb;
 #pragma unroll
         for (int gi = 0; gi < TG; gi++) {
-            const float gs = cross_row_sum(accg[r][gi]), us = cross_row_sum(accu[r][gi]);
-            if (jb == 0) {
-                red[0][wave][r][gi][nrow] = gs;
-                red[1][wave][r][gi][nrow] = us;
-            }
+            const float* xv = xl + gi * g.d + cb * kQK;
+            accg[gi] += block_dot<QT, PREC>(tg[q], xv);
+            accu[gi] += block_dot<QT, PREC>(tu[q], xv);
         }
-    if constexpr (!down_early<TG>()) load_down();
-    lds_barrier();
-    if (threadIdx.x < ROWS * TG) {
-        const int gi = threadIdx.x / ROWS, rr = threadIdx.x - gi * ROWS, r = rr >> 4, n = rr & 15;
-        float gs = 0.f, us = 0.f;
-        for (int w = 0; w < WAVES; w++) {
-            gs += red[0][w][r][gi][n];
-            us += red[1][w][r][gi][n];
-        }
-        float hv = silu(gs) * us;
-        if (PREC == MOE_PREC_BF16) hv = round_bf16(hv);
-        h_c[gi][rr] = base ? hv : qnan;
     }
-    __syncthreads();
-
-    // down: the lane owns output row (pi * 64 + lane)
-    float hv[TG][ROWS];
 #pragma unroll
-    for (int gi = 0; gi < TG; gi++)
-#pragma unroll
-        for (int j = 0; j < ROWS; j++) hv[gi][j] = h_c[gi][j];
-#pragma unroll
-    for (int q = 0; q < DPW; q++) {
-        const int pi = wave + q * WAVES;
-        if (pi >= g.dtiles) break;
-        float acc[TG];
-        if constexpr (QT == MOE_Q8_0) half_dots<PREC, TG>(td[q], hv, acc);
-        else tile_dots<QT, PREC, TG>(td[q], hv, acc);
-        const int row = pi * kTileBlocks + lane;
-#pragma unroll
-        for (int gi = 0; gi < TG; gi++)
-            if (prow[gi] >= 0) a.part[((int64_t)prow[gi] * g.n_chunks + c) * g.d + row] = base ? acc[gi] : qnan;
+    for (int gi = 0; gi < TG; gi++) {
+        const float gs = cross_row_sum(accg[gi]), us = cross_row_sum(accu[gi]);
+        if (jb == 0) {
+            red[((0 * kWaves + wave) * TG + gi) * 16 + n] = gs;
+            red[((1 * kWaves + wave) * TG + gi) * 16 + n] = us;
+        }
+    }
+    lds_barrier();
+    // Wave 0 holds every (token, unit) of the item: 16 * TG <= 64 threads.
+    if (threadIdx.x < 16 * TG) {
+        const int gi = threadIdx.x >> 4, r = threadIdx.x & 15;
+        if (gi < nb) {
+            float gs = 0.f, us = 0.f;
+            for (int w = 0; w < kWaves; w++) {
+                gs += red[((0 * kWaves + w) * TG + gi) * 16 + r];
+                us += red[((1 * kWaves + w) * TG + gi) * 16 + r];
+            }
+            float hv = silu(gs) * us;
+            if (PREC == MOE_PREC_BF16) hv = round_bf16(hv);
+            const int row = routed ? b0 + gi : a.T * a.k + gi;
+            // device scope: written through to where every XCD reads it
+            __hip_atomic_store(a.hbuf + (int64_t)par * g.half + (int64_t)row * g.f + 16 * rg + r,
+                               base ? hv : __uint_as_float(0x7FC00000u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
-// combine: a workgroup of 256 threads covers 64 outputs of one token as 16
-// float4 quads x 16 entry slots.  Token t's entries are found in plan order
-// (ascending expert) with one ballot; each thread sums every chunk of its
-// (quad, entry) with all loads in flight, and the per-entry sums are then
-// weighted and added per output in plan order, shared expert last.
-constexpr int kCombineQuads = 16;
-constexpr int kCombineSlots = 16;
-constexpr int kMaxCombine = 33;  // top_k <= 32 entries + shared
-constexpr int kChunkBatch = 16;
+// ---- down + merge --------------------------------------------------------------------
 
-__global__ __launch_bounds__(kCombineQuads * kCombineSlots) void combine_kernel(FfnArgs a, int n_chunks, int d) {
-    __shared__ int s_q[kMaxCombine];
-    __shared__ float s_w[kMaxCombine];
-    __shared__ int s_cnt;
-    __shared__ float4 red[kMaxCombine][kCombineQuads];
-    const int t = blockIdx.y;
-    const int qd = threadIdx.x % kCombineQuads, slot = threadIdx.x / kCombineQuads;
-    const int i4 = blockIdx.x * kCombineQuads + qd;  // output quad
+template <int QT, int PREC, int TG, int DPW>
+__device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char* lds_raw) {
+    DownLds& L = *(DownLds*)lds_raw;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, jb = lane >> 4;
+    const bool has_shared = a.shared != nullptr;
     const int n_ent = a.T * a.k;
-    if (threadIdx.x < 64) {
-        int base = 0;
-        for (int q0 = 0; q0 < n_ent; q0 += 64) {
-            const int q = q0 + threadIdx.x;
-            const int ent = q < n_ent ? a.entries[q] : -1;
-            const bool mine = q < n_ent && ent / a.k == t;
-            const uint64_t m = __ballot(mine);
-            if (mine) {
-                const int r = base + __popcll(m & ((1ull << threadIdx.x) - 1ull));
-                s_q[r] = q;
-                s_w[r] = a.topk_w[ent];
-            }
-            base += __popcll(m);
+
+    // Level 1, all independent loads: the launch count, n_active, the
+    // page-table row and the whole plan (units, entry ranges, entries, weights).
+    const uint32_t count = __hip_atomic_load(a.sync + kSyncCount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int na_raw = *a.n_active;
+    PtRow ptr;
+    ptr.load(a);
+    const int i1 = threadIdx.x;
+    const uint32_t ex1 = (uint32_t)a.experts[min(i1, a.E - 1)];
+    const uint32_t of1 = (uint32_t)a.offsets[min(i1, a.E)];
+    const uint32_t en1 = (uint32_t)a.entries[min(i1, n_ent - 1)];
+    const uint32_t w1 = __float_as_uint(a.topk_w[min(i1, n_ent - 1)]);
+    ptr.store(a, L.pts);
+    if (i1 < kMaxUnits) L.exp[i1] = (int)opaque(ex1);
+    if (i1 < kMaxUnits + 1) L.off[i1] = min(max((int)opaque(of1), 0), n_ent);
+    if (i1 < n_ent) {
+        L.ent[i1] = min(max((int)opaque(en1), 0), n_ent - 1);
+        L.wbe[i1] = __uint_as_float(opaque(w1));
+    }
+    if (threadIdx.x == 0) L.flag[0] = 1;
+    lds_barrier();
+    const int par = launch_parity(opaque(count), g.n_down);
+    const int na = min(max((int)opaque((uint32_t)na_raw), 0), g.units_max - (has_shared ? 1 : 0));
+    // This workgroup's share of the other half back to pending for the next
+    // launch (no one uses that half during this one).
+    {
+        float* nxt = a.hbuf + (int64_t)(par ^ 1) * g.half;
+        const int64_t r0 = (int64_t)R * g.reset_per;
+        for (int j = threadIdx.x; j < g.reset_per; j += kThreads)
+            if (r0 + j < g.half) nxt[r0 + j] = __uint_as_float(kPending);
+    }
+
+    // Level 2: this workgroup's W_d tiles of every unit.  Tile p is (unit
+    // p / dn_tpr, column group p % dn_tpr); wave w holds tiles w + 8 i.
+    const int U = na + (has_shared ? 1 : 0);
+    const int P = U * g.dn_tpr;
+    auto tile_ptr = [&](int p) __attribute__((always_inline)) -> const uint8_t* {
+        const int u = p / g.dn_tpr, c = p - u * g.dn_tpr;
+        const uint8_t* b = unit_base(a, u, na, L.exp, L.pts);
+        return b ? b + g.down_off + ((int64_t)R * g.dn_tpr + c) * g.tile_bytes : nullptr;
+    };
+    Tile<QT> td[DPW];
+#pragma unroll
+    for (int i = 0; i < DPW; i++) {
+        const int p = wave + kWaves * i;
+        const uint8_t* tp = p < P ? tile_ptr(p) : nullptr;
+        if (tp) td[i].load(tp, lane);
+        else td[i].clear();
+    }
+    // Token and weight of every hidden row (the shared rows: token t, weight 1).
+    if (threadIdx.x < kMaxRows) {
+        const int v = threadIdx.x;
+        if (v < n_ent) {
+            const int ent = L.ent[v];
+            L.tok[v] = ent / a.k;
+            L.w[v] = L.wbe[ent];
+        } else {
+            L.tok[v] = v - n_ent;
+            L.w[v] = 1.f;
         }
-        if (threadIdx.x == 0) {
-            int cnt = base;
-            if (a.shared) {
-                s_q[cnt] = n_ent + t;
-                s_w[cnt] = 1.0f;
-                cnt++;
+    }
+
+    // Rows of unit u: its plan positions, or the shared rows.
+    auto v_begin = [&](int u) __attribute__((always_inline)) { return u < na ? L.off[u] : n_ent; };
+    auto v_end = [&](int u) __attribute__((always_inline)) { return u < na ? L.off[u + 1] : n_ent + a.T; };
+
+    const __amdgpu_buffer_rsrc_t hrs =
+        __builtin_amdgcn_make_buffer_rsrc(a.hbuf + (int64_t)par * g.half, 0, (int)(sizeof(float) * g.half), kRsrcWord3);
+    const uint64_t t0 = wall_clock64();
+    float acc[TG];
+#pragma unroll
+    for (int t = 0; t < TG; t++) acc[t] = 0.f;
+    // Groups of units whose hidden rows fit the LDS, in plan order.
+    int ua = 0;
+    while (ua < U) {
+        const int va = v_begin(ua);
+        int ub = ua + 1;
+        while (ub < U && v_end(ub) - va <= g.nb_rows) ub++;
+        const int vb = min(v_end(ub - 1), va + g.nb_rows);  // (a valid plan never clips)
+        // Poll rows [va, vb) until no pending word is left (every load of the
+        // thread, then the checks), then stage them scaled by the row weight.
+        const int n4 = max(vb - va, 0) * g.f / 4;
+        float4 hv[kHPerThread];
+        for (;;) {
+#pragma unroll
+            for (int j = 0; j < kHPerThread; j++) {
+                const int i = threadIdx.x + j * kThreads;
+                hv[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       hrs, (va * g.f + 4 * min(i, max(n4 - 1, 0))) * 4, 0, kDeviceScope));
             }
-            s_cnt = cnt;
+            int pend = 0;
+#pragma unroll
+            for (int j = 0; j < kHPerThread; j++) {
+                const int i = threadIdx.x + j * kThreads;
+                const uint4 b = __builtin_bit_cast(uint4, hv[j]);
+                pend |= (i < n4) & ((b.x == kPending) | (b.y == kPending) | (b.z == kPending) | (b.w == kPending));
+            }
+            if (!__syncthreads_or(pend)) break;
+            const int expired = threadIdx.x == 0 && (int64_t)(wall_clock64() - t0) > a.wait_ticks;
+            if (__syncthreads_or(expired)) {
+                if (threadIdx.x == 0) {
+                    atomicOr(a.err, kErrSync);
+                    L.flag[0] = 0;
+                }
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
         }
+#pragma unroll
+        for (int j = 0; j < kHPerThread; j++) {
+            const int i = threadIdx.x + j * kThreads;
+            if (i < n4) {
+                const float wr = L.w[va + 4 * i / g.f];
+                const float4 h = hv[j];
+                ((float4*)L.hs)[i] = make_float4(wr * h.x, wr * h.y, wr * h.z, wr * h.w);
+            }
+        }
+        __syncthreads();
+        // Per lane: the tiles of units [ua, ub), each with the unit's rows.
+        auto tile_sums = [&](const Tile<QT> t, int p) __attribute__((always_inline)) {
+            const int u = p / g.dn_tpr, c = p - u * g.dn_tpr;
+            const int v0 = max(v_begin(u), va), v1 = min(v_end(u), vb);
+            for (int v = v0; v < v1; v++) {
+                const float s = block_dot<QT, PREC>(t, L.hs + (v - va) * g.f + (4 * c + jb) * kQK);
+                const int tk = L.tok[v];
+#pragma unroll
+                for (int q = 0; q < TG; q++) acc[q] += tk == q ? s : 0.f;
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < DPW; i++) {
+            const int p = wave + kWaves * i;
+            if (p >= ua * g.dn_tpr && p < ub * g.dn_tpr) tile_sums(td[i], p);
+        }
+        // tiles beyond the registers (more units than DPW * 8 / dn_tpr)
+        for (int p = kWaves * DPW + wave; p < ub * g.dn_tpr; p += kWaves) {
+            if (p < ua * g.dn_tpr) continue;
+            const uint8_t* tp = tile_ptr(p);
+            Tile<QT> t;
+            if (tp) t.load(tp, lane);
+            else t.clear();
+            tile_sums(t, p);
+        }
+        __syncthreads();
+        ua = ub;
+    }
+    // The four lanes of a row, then the waves in order.
+#pragma unroll
+    for (int t = 0; t < TG; t++) {
+        const float s = cross_row_sum(acc[t]);
+        if (jb == 0) L.red[wave][t][n] = s;
     }
     __syncthreads();
-    const int cnt = s_cnt;
-    const bool in = i4 * 4 < d;
-    for (int j = slot; j < cnt; j += kCombineSlots) {
-        const float4* p = (const float4*)(a.part + (int64_t)s_q[j] * n_chunks * d) + i4;
-        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int c0 = 0; c0 < n_chunks; c0 += kChunkBatch) {
-            float4 v[kChunkBatch];
-#pragma unroll
-            for (int b = 0; b < kChunkBatch; b++)
-                v[b] = (in && c0 + b < n_chunks) ? p[(int64_t)(c0 + b) * (d / 4)] : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-            for (int b = 0; b < kChunkBatch; b++) {
-                sum.x += v[b].x; sum.y += v[b].y; sum.z += v[b].z; sum.w += v[b].w;
-            }
-        }
-        red[j][qd] = sum;
+    if (threadIdx.x < 16 * a.T) {
+        const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
+        float y = 0.f;
+        for (int w = 0; w < kWaves; w++) y += L.red[w][t][r];
+        a.y[(int64_t)t * g.d + 16 * R + r] = L.flag[0] ? y : __uint_as_float(0x7FC00000u);
     }
-    __syncthreads();
-    if (slot == 0 && in) {
-        const int n_routed = a.shared ? cnt - 1 : cnt;
-        float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < cnt; j++) {
-            const float4 s4 = red[j][qd];
-            const float wj = j < n_routed ? s_w[j] : 1.0f;
-            if (j < n_routed) {
-                y.x = fmaf(wj, s4.x, y.x); y.y = fmaf(wj, s4.y, y.y);
-                y.z = fmaf(wj, s4.z, y.z); y.w = fmaf(wj, s4.w, y.w);
-            } else {
-                y.x += s4.x; y.y += s4.y; y.z += s4.z; y.w += s4.w;
-            }
-        }
-        *(float4*)(a.y + (int64_t)t * d + i4 * 4) = y;
-    }
+    // This launch is done with its half: count it (no return needed).
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(a.sync + kSyncCount, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int QT, int PREC, int TG, int PPW, int DPW>
-hipError_t launch_t(const Grid& g, const FfnArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((ffn_partial_kernel<QT, PREC, TG, PPW, DPW>), dim3(g.units_max * g.n_chunks),
-                       dim3(wg_waves<TG>() * 64), 0, s, a, g);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(combine_kernel, dim3((g.d / 4 + kCombineQuads - 1) / kCombineQuads, a.T),
-                       dim3(kCombineQuads * kCombineSlots), 0, s, a, g.n_chunks, g.d);
+__global__ __launch_bounds__(kThreads, 4) void ffn_decode_kernel(FfnArgs a, DGrid g) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+    const int b = blockIdx.x, n_gu = g.units_max * g.n_rg;
+    if (b < n_gu) gate_up_role<QT, PREC, TG, PPW>(a, g, b, lds);
+    else down_role<QT, PREC, TG, DPW>(a, g, b - n_gu, lds);
+}
+
+template <int QT, int PREC, int TG, int PPW, int DPW>
+hipError_t launch_k(const DGrid& g, const FfnArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((ffn_decode_kernel<QT, PREC, TG, PPW, DPW>), dim3(g.units_max * g.n_rg + g.n_down),
+                       dim3(kThreads), 0, s, a, g);
     return hipGetLastError();
 }
 
+// Down tiles held in registers per wave: every tile of the step's units in the
+// usual cases (top-8: 9 units at T = 1, up to 10 (Q8_0) or 14 (Q4_0) at T = 2, 18
+// (Q4_0) or 10 (Q8_0) at T = 4, with d_ff 512); more are loaded after the wait.
+template <int QT, int TG> constexpr int down_per_wave() {
+    return TG == 1 ? 5 : QT == MOE_Q4_0 ? (TG == 2 ? 7 : 9) : 5;
+}
+
 template <int QT, int PREC, int TG>
-hipError_t launch_w(Grid g, const FfnArgs& a, hipStream_t s) {
-    constexpr int ROWS = chunk_rows<QT>();
-    constexpr int W = wg_waves<TG>();
-    g.n_chunks = g.d_ff / ROWS;
-    g.pairs = ROWS * g.nbd / kTileBlocks;
-    if (g.pairs < 1) return hipErrorInvalidValue;
-    if (g.pairs <= W && g.dtiles <= W) return launch_t<QT, PREC, TG, 1, 1>(g, a, s);
-    if (g.pairs <= 2 * W && g.dtiles <= 4 * W) return launch_t<QT, PREC, TG, 2, 4>(g, a, s);
-    if (g.pairs <= 4 * W && g.dtiles <= 4 * W) return launch_t<QT, PREC, TG, 4, 4>(g, a, s);
+hipError_t launch_w(const DGrid& g, const FfnArgs& a, hipStream_t s) {
+    constexpr int D = down_per_wave<QT, TG>();
+    if (g.gu_tpr <= kWaves) return launch_k<QT, PREC, TG, 1, D>(g, a, s);
+    if (g.gu_tpr <= 2 * kWaves) return launch_k<QT, PREC, TG, 2, D>(g, a, s);
     return hipErrorInvalidValue;
 }
 
 template <int QT, int PREC>
-hipError_t launch_tg(const Grid& g, const FfnArgs& a, hipStream_t s) {
+hipError_t launch_tg(const DGrid& g, const FfnArgs& a, hipStream_t s) {
     if (a.T <= 1) return launch_w<QT, PREC, 1>(g, a, s);
     if (a.T <= 2) return launch_w<QT, PREC, 2>(g, a, s);
     return launch_w<QT, PREC, 4>(g, a, s);
@@ -426,20 +559,29 @@ hipError_t launch_tg(const Grid& g, const FfnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_ffn_decode(const Geom& g, const FfnArgs& a, int prec, hipStream_t s) {
-    Grid gr{};
-    gr.units_max = min(a.T * a.k, a.E) + (a.shared ? 1 : 0);
-    gr.dtiles = g.d / kTileBlocks;
-    gr.nbd = g.nb_d;
-    gr.d = g.d;
-    gr.d_ff = g.f;
-    gr.tile_bytes = g.tile_bytes;
-    gr.down_off = 2 * g.gu_tiles * g.tile_bytes;
-    if (g.qtype == MOE_Q8_0)
-        return prec == MOE_PREC_BF16 ? launch_tg<MOE_Q8_0, MOE_PREC_BF16>(gr, a, s)
-                                     : launch_tg<MOE_Q8_0, MOE_PREC_F32>(gr, a, s);
-    return prec == MOE_PREC_BF16 ? launch_tg<MOE_Q4_0, MOE_PREC_BF16>(gr, a, s)
-                                 : launch_tg<MOE_Q4_0, MOE_PREC_F32>(gr, a, s);
+hipError_t launch_ffn_decode(const Geom& geo, const FfnArgs& a, int prec, hipStream_t s) {
+    if (a.T < 1 || a.T > kDecodeMaxT || a.E > kMaxE || a.k > 32) return hipErrorInvalidValue;
+    DGrid g{};
+    g.units_max = min(a.T * a.k, a.E) + (a.shared ? 1 : 0);
+    g.n_down = geo.d / 16;
+    g.n_rg = geo.f / 16;
+    g.gu_tpr = geo.nb_d / 4;
+    g.dn_tpr = geo.nb_f / 4;
+    g.d = geo.d;
+    g.f = geo.f;
+    g.tile_bytes = geo.tile_bytes;
+    g.down_off = 2 * geo.gu_tiles * geo.tile_bytes;
+    g.nb_rows = kHCap / (4 * geo.f);
+    g.half = decode_h_floats(a.k, geo.f) / 2;
+    g.reset_per = (int)((g.half + g.n_down - 1) / g.n_down);
+    // LDS: the gate/up role's page-table row, activations and sums fit the down role's layout
+    if (g.nb_rows < kDecodeMaxT || 4 * (kMaxE + kMaxEnt + kDecodeMaxT * geo.d + 2 * kWaves * kDecodeMaxT * 16) > kLdsBytes)
+        return hipErrorInvalidValue;
+    if (geo.qtype == MOE_Q8_0)
+        return prec == MOE_PREC_BF16 ? launch_tg<MOE_Q8_0, MOE_PREC_BF16>(g, a, s)
+                                     : launch_tg<MOE_Q8_0, MOE_PREC_F32>(g, a, s);
+    return prec == MOE_PREC_BF16 ? launch_tg<MOE_Q4_0, MOE_PREC_BF16>(g, a, s)
+                                 : launch_tg<MOE_Q4_0, MOE_PREC_F32>(g, a, s);
 }
 
 }  // namespace moe

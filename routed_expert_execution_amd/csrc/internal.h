@@ -29,9 +29,9 @@ struct Geom {
         if (d <= 0 || f <= 0 || d % kQK || f % kQK) return false;
         nb_d = d / kQK; nb_f = f / kQK;
         // gate/up rows: 4..64 blocks, a power of two (whole 4-block column groups);
-        // down: column blocks of d rows, d a multiple of 64 and at most 32 tiles
+        // down rows: whole 4-block column groups, at most 64 blocks
         if (nb_d < 4 || nb_d > 64 || (nb_d & (nb_d - 1))) return false;
-        if (d % kTileBlocks || d / kTileBlocks > 32) return false;
+        if (nb_f % 4 || nb_f > 64) return false;
         tile_bytes = (int64_t)kTileBlocks * block_bytes(qt);
         gu_tiles = (int64_t)f * nb_d / kTileBlocks;
         d_tiles = (int64_t)d * nb_f / kTileBlocks;
@@ -41,19 +41,18 @@ struct Geom {
     __host__ __device__ int64_t gate_tile(int64_t t) const { return 2 * t * tile_bytes; }
     __host__ __device__ int64_t up_tile(int64_t t) const { return (2 * t + 1) * tile_bytes; }
     __host__ __device__ int64_t down_tile(int64_t t) const { return (2 * gu_tiles + t) * tile_bytes; }
-    // Block (row r, column block cb) of each matrix -> (tile, lane).  gate/up:
-    // a tile is 16 rows x 4 column blocks, lane = 16 * (cb % 4) + r % 16, tiles
-    // ordered by row group then column group, so a row group's tiles are
-    // consecutive; down: column-block-major (all d rows of column block 0, then
-    // column block 1, ...), so one column block is d/64 whole tiles.
+    // Block (row r, column block cb) of each matrix -> (tile, lane).  Every
+    // matrix uses one tile shape: 16 rows x 4 column blocks, lane = 16 * (cb % 4)
+    // + r % 16, tiles ordered by row group then column group, so the tiles of
+    // 16 consecutive rows are consecutive: one MFMA step of 16 rows x 128
+    // columns reads one whole tile, and 16 rows of a GEMV one contiguous run.
     __host__ __device__ void gu_block(int64_t r, int cb, int64_t* tile, int* lane) const {
         *tile = (r / 16) * (nb_d / 4) + cb / 4;
         *lane = 16 * (cb % 4) + (int)(r % 16);
     }
     __host__ __device__ void down_block(int64_t r, int cb, int64_t* tile, int* lane) const {
-        const int64_t L = (int64_t)cb * d + r;
-        *tile = L / kTileBlocks;
-        *lane = (int)(L % kTileBlocks);
+        *tile = (r / 16) * (nb_f / 4) + cb / 4;
+        *lane = 16 * (cb % 4) + (int)(r % 16);
     }
 };
 
@@ -67,6 +66,7 @@ __host__ __device__ inline int q4_scale(int i) { return 16 * kTileBlocks + 2 * i
 // Device error word bits.
 constexpr int kErrMiss = 1;     // unmapped expert met by a kernel
 constexpr int kErrBadId = 4;    // expert id out of range in a plan input
+constexpr int kErrSync = 8;     // a decode workgroup's bounded wait for the hidden rows ran out
 
 // ---- launchers (return hipError_t of the launch) ----
 
@@ -104,18 +104,20 @@ struct FfnArgs {
     int x_bf16;
     int T;
     // outputs and workspace
-    float* part;            // [(T*k + T) * (d_ff/16) * d_model] partial rows
+    float* hbuf;            // two halves of [T*k + T, d_ff] hidden rows (plan positions, then the
+                            // shared rows), every word 0xFFFFFFFF at creation
+    uint32_t* sync;         // [kSyncInts], zero at creation: [kSyncCount] finished down workgroups
+    int64_t wait_ticks;     // bound of a down workgroup's wait (100 MHz wall-clock ticks)
     float* y;               // [T, d]
     int* err;
 };
 
-// Largest step the decode kernels take.
+// Largest step the decode kernel takes.
 constexpr int kDecodeMaxT = 4;
+constexpr int kSyncInts = 32, kSyncCount = 0;  // one 128-byte line
 
-// Floats of partial-row workspace the decode kernels need for top_k, d_ff, d_model.
-inline int64_t decode_part_floats(int k, int f, int d) {
-    return (int64_t)kDecodeMaxT * (k + 1) * (f / 16) * d;
-}
+// Floats of hidden-row workspace (both halves) the decode kernel needs for top_k and d_ff.
+__host__ __device__ inline int64_t decode_h_floats(int k, int f) { return 2 * (int64_t)kDecodeMaxT * (k + 1) * f; }
 
 hipError_t launch_ffn_decode(const Geom& g, const FfnArgs& a, int prec, hipStream_t s);
 

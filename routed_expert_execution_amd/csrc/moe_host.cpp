@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -23,7 +24,9 @@ struct moe_ctx {
     // device state
     int32_t* pt = nullptr;     // [L x E]
     int* err_word = nullptr;
-    float* part = nullptr;     // decode partial rows
+    float* hbuf = nullptr;     // decode hidden rows
+    uint32_t* sync = nullptr;  // decode launch count
+
     // prefill workspace (max_tokens > 4)
     float* ph = nullptr;
     float* ppart = nullptr;
@@ -87,7 +90,7 @@ bool cfg_valid(const moe_config* c, Geom* g, std::string* why) {
     Geom gg;
     if (!gg.init(c->d_model, c->d_ff, c->qtype))
         return bad("unsupported shape or qtype: d_model/32 must be a power of two in [4, 64] "
-                   "(d_model 128..2048), d_ff a multiple of 32; qtype Q8_0 or Q4_0");
+                   "(d_model 128..2048), d_ff a multiple of 128 up to 2048; qtype Q8_0 or Q4_0");
     if (c->device >= 0) {
         if (!c->slot_pool) return bad("slot_pool is NULL");
         if (((uintptr_t)c->slot_pool) & 255) return bad("slot_pool must be 256-byte aligned");
@@ -220,7 +223,8 @@ void moe_destroy(moe_ctx* c) {
         (void)hipDeviceSynchronize();
         if (c->pt) (void)hipFree(c->pt);
         if (c->err_word) (void)hipFree(c->err_word);
-        if (c->part) (void)hipFree(c->part);
+        if (c->hbuf) (void)hipFree(c->hbuf);
+        if (c->sync) (void)hipFree(c->sync);
         if (c->ph) (void)hipFree(c->ph);
         if (c->ppart) (void)hipFree(c->ppart);
         if (c->pinv) (void)hipFree(c->pinv);
@@ -258,9 +262,9 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         const int64_t T = cfg->max_tokens;
         if (hipMalloc(&c->pt, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->err_word, sizeof(int)) != hipSuccess) return cleanup(MOE_ENOMEM);
-        if (hipMalloc(&c->part, sizeof(float) * (size_t)moe::decode_part_floats(cfg->top_k, cfg->d_ff, cfg->d_model)) !=
-            hipSuccess)
+        if (hipMalloc(&c->hbuf, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff)) != hipSuccess)
             return cleanup(MOE_ENOMEM);
+        if (hipMalloc(&c->sync, sizeof(uint32_t) * moe::kSyncInts) != hipSuccess) return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->logits_ws, sizeof(float) * (size_t)T * cfg->n_experts) != hipSuccess)
             return cleanup(MOE_ENOMEM);
         if (T > moe::kDecodeMaxT) {
@@ -274,6 +278,9 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         }
         if (hipMemset(c->pt, 0xFF, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_EHIP);
         if (hipMemset(c->err_word, 0, sizeof(int)) != hipSuccess) return cleanup(MOE_EHIP);
+        if (hipMemset(c->sync, 0, sizeof(uint32_t) * moe::kSyncInts) != hipSuccess) return cleanup(MOE_EHIP);
+        if (hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff)) != hipSuccess)
+            return cleanup(MOE_EHIP);
         if (hipEventCreateWithFlags(&c->release_ev, hipEventDisableTiming) != hipSuccess) return cleanup(MOE_EHIP);
         if (hipDeviceSynchronize() != hipSuccess) return cleanup(MOE_EHIP);
     }
@@ -493,7 +500,12 @@ moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     a.x = x;
     a.x_bf16 = x_dtype == MOE_BF16;
     a.T = (int)T;
-    a.part = c->part;
+    a.hbuf = c->hbuf;
+    a.sync = c->sync;
+    // bound of the decode kernel's wait: 200 ms of the 100 MHz clock; tests of the
+    // time-out path shorten it through MOE_SYNC_WAIT_TICKS
+    a.wait_ticks = 20000000;
+    if (const char* e = getenv("MOE_SYNC_WAIT_TICKS")) a.wait_ticks = std::max<int64_t>(0, atoll(e));
     a.y = y;
     a.err = c->err_word;
     if (T <= moe::kDecodeMaxT) {
@@ -557,6 +569,14 @@ moe_status moe_check(moe_ctx* c, moe_stream stream) {
     HIP_TRY(c, hipMemcpy(&w, c->err_word, sizeof(int), hipMemcpyDeviceToHost));
     if (!w) return MOE_OK;
     HIP_TRY(c, hipMemset(c->err_word, 0, sizeof(int)));
+    if (w & moe::kErrSync) {
+        // after a timed-out wait the workspace halves may hold rows of the wrong
+        // launch: start both afresh (pending) with the count at zero
+        HIP_TRY(c, hipMemset(c->sync, 0, sizeof(uint32_t) * moe::kSyncInts));
+        HIP_TRY(c, hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(c->cfg.top_k, c->cfg.d_ff)));
+        HIP_TRY(c, hipDeviceSynchronize());
+        return fail(c, MOE_ETIMEOUT, "a decode workgroup timed out waiting for the hidden rows (error word 0x%x)", w);
+    }
     if (w & moe::kErrMiss) return fail(c, MOE_EMISS, "a kernel met an unmapped expert (error word 0x%x)", w);
     return fail(c, MOE_EINVAL, "a plan input held an expert id out of range (error word 0x%x)", w);
 }

@@ -180,8 +180,8 @@ def test_plan_union_bit_exact(T, k, E, kind):
 class Step:
     """One routed step on the GPU with every needed expert placed by the test."""
 
-    def __init__(self, name, T, step=0, prec=oracle.PREC_F32, n_slots=None):
-        wl = synth.workload(name)
+    def __init__(self, name, T, step=0, prec=oracle.PREC_F32, n_slots=None, **overrides):
+        wl = dict(synth.workload(name), **overrides)
         self.wl, self.T, self.prec = wl, T, prec
         E, k, d, f = wl["E"], wl["k"], wl["d"], wl["f"]
         self.x = synth.activations(wl["seed"], T, d, wl["x_dtype"], step)
@@ -236,6 +236,66 @@ def test_ffn_decode_parity(name, T, step):
     err = H.max_rel_row_err(y, ref)
     _say("  max rel row err", err)
     assert np.isfinite(y).all() and err <= FFN_TOL
+
+
+@pytest.mark.parametrize("k,T", [(32, 4), (16, 3), (32, 1)])
+def test_ffn_decode_wide_topk_parity(k, T):
+    """top-16/32 of 64 experts: more plan entries than the decode kernel stages at
+    once (several entry groups) and more down tiles than its registers hold."""
+    _say("ffn wide", k, T)
+    s = Step("decode", T, 11, E=64, k=k)
+    s.place()
+    y = s.run()
+    assert moe.moe_check(s.ctx) == moe.MOE_OK
+    err = H.max_rel_row_err(y, s.reference())
+    _say("  max rel row err", err)
+    assert np.isfinite(y).all() and err <= FFN_TOL
+
+
+@pytest.mark.parametrize("name,T", [("decode", 1), ("mtp", 4)])
+def test_decode_alternating_inputs_see_fresh_hidden_rows(name, T):
+    """Launches alternating between two activation sets on one context (same
+    experts, same hidden-row workspace): every output matches its own input's
+    reference and repeats bit for bit, so no launch reads a hidden row left by
+    the previous one."""
+    s = Step(name, T, 4)
+    s.place()
+    xs = [s.x, synth.activations(s.wl["seed"], T, s.wl["d"], s.wl["x_dtype"], 777)]
+    devs = [H.torch_x(x, s.wl["x_dtype"]) for x in xs]
+    refs = []
+    for x in xs:
+        s.x = x
+        refs.append(s.reference())
+    first = [None, None]
+    for i in range(8):
+        s.x_dev = devs[i % 2]
+        y = s.run()
+        assert H.max_rel_row_err(y, refs[i % 2]) <= FFN_TOL
+        if first[i % 2] is None:
+            first[i % 2] = y
+        assert np.array_equal(y.view(np.uint32), first[i % 2].view(np.uint32))
+    assert moe.moe_check(s.ctx) == moe.MOE_OK
+
+
+def test_decode_wait_timeout_fails_closed_and_recovers(monkeypatch):
+    """A wait bound of 0 ticks (set from the host) makes the down workgroups give up
+    at once: the launch still completes, rows whose wait ran out are NaN,
+    moe_check reports MOE_ETIMEOUT and resets the hand-off workspace, and the
+    next launches are exact again."""
+    s = Step("decode", 1, 0)
+    s.place()
+    ref = s.reference()
+    monkeypatch.setenv("MOE_SYNC_WAIT_TICKS", "0")
+    y = s.run()
+    monkeypatch.delenv("MOE_SYNC_WAIT_TICKS")
+    assert np.isnan(y).any()
+    assert moe.moe_check(s.ctx) == moe.MOE_ETIMEOUT
+    y2 = s.run()
+    assert moe.moe_check(s.ctx) == moe.MOE_OK
+    assert H.max_rel_row_err(y2, ref) <= FFN_TOL
+    y3 = s.run()
+    assert moe.moe_check(s.ctx) == moe.MOE_OK
+    assert np.array_equal(y3.view(np.uint32), y2.view(np.uint32))
 
 
 @pytest.mark.parametrize("name,T", [("decode", 1), ("decode", 4), ("mtp", 4), ("tiny", 4)])
