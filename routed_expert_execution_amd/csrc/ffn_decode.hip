@@ -71,6 +71,7 @@ struct DownLds {
     int tok[kMaxRows];                // hidden row -> token
     float w[kMaxRows];                // hidden row -> weight
     int flag[4];
+    int64_t uoff[kMaxUnits + 3];      // unit -> payload offset in the pool (-1 absent, -2 shared)
     float red[kWaves][kDecodeMaxT][16];
     float hs[kHCap / 4];
 };
@@ -85,7 +86,6 @@ template <> struct Tile<MOE_Q8_0> {
         hi = *(const uint4*)(t + q8_hi(i));
         s = *(const uint16_t*)(t + q8_scale(i));
     }
-    __device__ void clear() { lo = hi = make_uint4(0, 0, 0, 0); s = 0; }
 };
 template <> struct Tile<MOE_Q4_0> {
     uint4 nib;
@@ -94,7 +94,6 @@ template <> struct Tile<MOE_Q4_0> {
         nib = *(const uint4*)(t + q4_nib(i));
         s = *(const uint16_t*)(t + q4_scale(i));
     }
-    __device__ void clear() { nib = make_uint4(0, 0, 0, 0); s = 0; }
 };
 
 // Weight as multiplied: PREC_F32 keeps the code (the scale is applied once after
@@ -114,40 +113,72 @@ __device__ inline uint32_t opaque(uint32_t w) {
     return w;
 }
 
-// Dot product of the lane's block with 32 floats at v (LDS, 16-byte aligned),
-// codes in storage order, in two halves of 16 activations.
+// Code e (0..31) of the lane's block, as the weight multiplied (see wq).
 template <int QT, int PREC>
-__device__ inline float block_dot(const Tile<QT>& t, const float* v) {
-    const float s = f16_bits_to_f32(opaque(t.s));
-    float acc = 0.f;
-#pragma unroll
-    for (int hf = 0; hf < 2; hf++) {
-        float x[16];
-#pragma unroll
-        for (int m = 0; m < 4; m++) {
-            const float4 q = *(const float4*)(v + 16 * hf + 4 * m);
-            x[4 * m] = q.x; x[4 * m + 1] = q.y; x[4 * m + 2] = q.z; x[4 * m + 3] = q.w;
-        }
-        if constexpr (QT == MOE_Q8_0) {
-            const uint4 h4 = hf ? t.hi : t.lo;
-            const uint32_t w[4] = {opaque(h4.x), opaque(h4.y), opaque(h4.z), opaque(h4.w)};
-#pragma unroll
-            for (int m = 0; m < 4; m++)
-#pragma unroll
-                for (int j = 0; j < 4; j++) acc = fmaf(wq<PREC>(i8(w[m], j), s), x[4 * m + j], acc);
-        } else {
-            // low nibbles are elements 0..15, high nibbles 16..31
-            const uint32_t w[4] = {opaque(t.nib.x), opaque(t.nib.y), opaque(t.nib.z), opaque(t.nib.w)};
-#pragma unroll
-            for (int m = 0; m < 4; m++)
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const uint32_t b = (w[m] >> (8 * j + 4 * hf)) & 15;
-                    acc = fmaf(wq<PREC>((float)((int)b - 8), s), x[4 * m + j], acc);
-                }
-        }
+__device__ inline float code_at(const uint32_t (&w)[8], int e, float s) {
+    if constexpr (QT == MOE_Q8_0) {
+        return wq<PREC>(i8(w[e >> 2], e & 3), s);  // w: lo words, then hi words
+    } else {
+        const int b = e & 15;                     // w[0..3]: the 16 nibble bytes
+        const uint32_t nib = (w[b >> 2] >> (8 * (b & 3) + (e >> 4) * 4)) & 15;
+        return wq<PREC>((float)((int)nib - 8), s);
     }
-    return PREC == MOE_PREC_F32 ? acc * s : acc;
+}
+
+// Dot products of M tiles' blocks (one block per lane) with N activation
+// vectors of 32 floats (LDS, 16-byte aligned): out[m][n] = block_m . v_n.
+// The codes are taken in quarters of 8, each dequantised once for all N
+// vectors; each product chain is split into QA interleaved partial sums (code
+// e into partial e mod QA), added in fixed order at the end, so that the
+// chains are independent.  PREC_F32 multiplies by the scale at the end.
+template <int QT, int PREC, int M, int N, int QA>
+__device__ __forceinline__ void tile_dots(const Tile<QT> (&t)[M], const float* const (&v)[N], float (&out)[M][N]) {
+    float acc[M][N][QA];
+    uint32_t w[M][8];
+    float s[M];
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        s[m] = f16_bits_to_f32(opaque(t[m].s));
+        if constexpr (QT == MOE_Q8_0) {
+            w[m][0] = opaque(t[m].lo.x); w[m][1] = opaque(t[m].lo.y); w[m][2] = opaque(t[m].lo.z); w[m][3] = opaque(t[m].lo.w);
+            w[m][4] = opaque(t[m].hi.x); w[m][5] = opaque(t[m].hi.y); w[m][6] = opaque(t[m].hi.z); w[m][7] = opaque(t[m].hi.w);
+        } else {
+            w[m][0] = opaque(t[m].nib.x); w[m][1] = opaque(t[m].nib.y); w[m][2] = opaque(t[m].nib.z); w[m][3] = opaque(t[m].nib.w);
+            w[m][4] = w[m][5] = w[m][6] = w[m][7] = 0;
+        }
+#pragma unroll
+        for (int n = 0; n < N; n++)
+#pragma unroll
+            for (int r = 0; r < QA; r++) acc[m][n][r] = 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        float x[N][8];
+#pragma unroll
+        for (int n = 0; n < N; n++) {
+            const float4 a0 = *(const float4*)(v[n] + 8 * q), a1 = *(const float4*)(v[n] + 8 * q + 4);
+            x[n][0] = a0.x; x[n][1] = a0.y; x[n][2] = a0.z; x[n][3] = a0.w;
+            x[n][4] = a1.x; x[n][5] = a1.y; x[n][6] = a1.z; x[n][7] = a1.w;
+        }
+#pragma unroll
+        for (int m = 0; m < M; m++)
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const int e = 8 * q + j;
+                const float c = code_at<QT, PREC>(w[m], e, s[m]);
+#pragma unroll
+                for (int n = 0; n < N; n++) acc[m][n][e % QA] = fmaf(c, x[n][j], acc[m][n][e % QA]);
+            }
+    }
+#pragma unroll
+    for (int m = 0; m < M; m++)
+#pragma unroll
+        for (int n = 0; n < N; n++) {
+            float r = acc[m][n][0];
+#pragma unroll
+            for (int k = 1; k < QA; k++) r += acc[m][n][k];
+            out[m][n] = PREC == MOE_PREC_F32 ? r * s[m] : r;
+        }
 }
 
 struct DGrid {
@@ -167,9 +198,6 @@ __device__ inline const uint8_t* slot_base(const FfnArgs& a, int e, const int* p
     if (e < 0 || e >= a.E) return nullptr;
     const int slot = pts[e];
     return (slot >= 0 && slot < a.n_slots) ? a.pool + (int64_t)slot * a.payload_bytes : nullptr;
-}
-__device__ inline const uint8_t* unit_base(const FfnArgs& a, int u, int na, const int* exp, const int* pts) {
-    return u >= na ? a.shared : slot_base(a, exp[u], pts);
 }
 
 // Launch parity: which workspace half this launch writes.
@@ -276,18 +304,17 @@ __device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int item, unsigne
     const bool routed = u < na;
     const uint8_t* base = routed ? slot_base(a, e, pts) : a.shared;
     if (!base && threadIdx.x == 0) atomicOr(a.err, kErrMiss);
+    // Loads are unconditional: a pair past the row group reads the group's
+    // first pair again (its sums are skipped), a missing expert reads pool slot
+    // 0 (its rows become NaN below).
+    const uint8_t* src = base ? base : a.pool;
     Tile<QT> tg[PPW], tu[PPW];
 #pragma unroll
     for (int q = 0; q < PPW; q++) {
         const int pi = wave + q * kWaves;
-        if (base && pi < g.gu_tpr) {
-            const int64_t t = (int64_t)rg * g.gu_tpr + pi;
-            tg[q].load(base + 2 * t * g.tile_bytes, lane);
-            tu[q].load(base + (2 * t + 1) * g.tile_bytes, lane);
-        } else {
-            tg[q].clear();
-            tu[q].clear();
-        }
+        const int64_t t = (int64_t)rg * g.gu_tpr + (pi < g.gu_tpr ? pi : 0);
+        tg[q].load(src + 2 * t * g.tile_bytes, lane);
+        tu[q].load(src + (2 * t + 1) * g.tile_bytes, lane);
     }
     const int b0 = routed ? o0 : 0;
     const int nb = routed ? min(max(o1 - o0, 0), TG) : a.T;  // tokens of the bucket
@@ -313,11 +340,16 @@ __device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int item, unsigne
         const int pi = wave + q * kWaves;
         if (pi >= g.gu_tpr) break;
         const int cb = 4 * pi + jb;
+        const float* xv[TG];
+#pragma unroll
+        for (int gi = 0; gi < TG; gi++) xv[gi] = xl + gi * g.d + cb * kQK;
+        const Tile<QT> pair[2] = {tg[q], tu[q]};
+        float dd[2][TG];
+        tile_dots<QT, PREC, 2, TG, TG == 1 ? 4 : TG == 2 ? 2 : 1>(pair, xv, dd);
 #pragma unroll
         for (int gi = 0; gi < TG; gi++) {
-            const float* xv = xl + gi * g.d + cb * kQK;
-            accg[gi] += block_dot<QT, PREC>(tg[q], xv);
-            accu[gi] += block_dot<QT, PREC>(tu[q], xv);
+            accg[gi] += dd[0][gi];
+            accu[gi] += dd[1][gi];
         }
     }
 #pragma unroll
@@ -390,21 +422,39 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
     }
 
     // Level 2: this workgroup's W_d tiles of every unit.  Tile p is (unit
-    // p / dn_tpr, column group p % dn_tpr); wave w holds tiles w + 8 i.
+    // p / dn_tpr, column group p % dn_tpr); wave w holds tiles w + 8 i.  Each
+    // unit's payload offset is looked up once (-1: not resident).
     const int U = na + (has_shared ? 1 : 0);
     const int P = U * g.dn_tpr;
+    if (threadIdx.x < U) {
+        const int u = threadIdx.x;
+        int64_t off = -1;
+        if (u >= na) off = -2;  // shared expert
+        else {
+            const int ex = L.exp[u];
+            const int slot = (ex >= 0 && ex < a.E) ? L.pts[ex] : -1;
+            if (slot >= 0 && slot < a.n_slots) off = (int64_t)slot * a.payload_bytes;
+        }
+        L.uoff[u] = off;
+    }
+    lds_barrier();
+    // Address of tile p, or null for a unit that is not resident.
     auto tile_ptr = [&](int p) __attribute__((always_inline)) -> const uint8_t* {
         const int u = p / g.dn_tpr, c = p - u * g.dn_tpr;
-        const uint8_t* b = unit_base(a, u, na, L.exp, L.pts);
+        const int64_t off = L.uoff[u];
+        const uint8_t* b = off == -2 ? a.shared : off >= 0 ? a.pool + off : nullptr;
         return b ? b + g.down_off + ((int64_t)R * g.dn_tpr + c) * g.tile_bytes : nullptr;
     };
+    // Loads are unconditional: a slot past the last tile, or a unit that is
+    // not resident, reads pool slot 0 (no sums are taken from the former; the
+    // latter's rows are NaN through h).
+    const uint8_t* fallback = a.pool + g.down_off + (int64_t)R * g.dn_tpr * g.tile_bytes;
     Tile<QT> td[DPW];
 #pragma unroll
     for (int i = 0; i < DPW; i++) {
         const int p = wave + kWaves * i;
         const uint8_t* tp = p < P ? tile_ptr(p) : nullptr;
-        if (tp) td[i].load(tp, lane);
-        else td[i].clear();
+        td[i].load(tp ? tp : fallback, lane);
     }
     // Token and weight of every hidden row (the shared rows: token t, weight 1).
     if (threadIdx.x < kMaxRows) {
@@ -422,6 +472,23 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
     // Rows of unit u: its plan positions, or the shared rows.
     auto v_begin = [&](int u) __attribute__((always_inline)) { return u < na ? L.off[u] : n_ent; };
     auto v_end = [&](int u) __attribute__((always_inline)) { return u < na ? L.off[u + 1] : n_ent + a.T; };
+    lds_barrier();
+    // Per register slot, read before the wait (wave-uniform, so scalar): the
+    // unit's rows [sv0, sv1), their tokens (2 bits each; a bucket has at most
+    // 4 rows) and the tile's column group.
+    int sv0[DPW], sv1[DPW], stok[DPW], scol[DPW];
+#pragma unroll
+    for (int i = 0; i < DPW; i++) {
+        const int p = wave + kWaves * i;
+        const int u = min(p, max(P - 1, 0)) / g.dn_tpr;
+        const int v0 = v_begin(u), v1 = min(v_end(u), v0 + kDecodeMaxT);
+        int tp = 0;
+        for (int v = v0; v < v1; v++) tp |= (L.tok[v] & 3) << (2 * (v - v0));
+        sv0[i] = __builtin_amdgcn_readfirstlane(v0);
+        sv1[i] = __builtin_amdgcn_readfirstlane(p < P ? v1 : v0);
+        stok[i] = __builtin_amdgcn_readfirstlane(tp);
+        scol[i] = __builtin_amdgcn_readfirstlane(min(p, max(P - 1, 0)) - u * g.dn_tpr);
+    }
 
     const __amdgpu_buffer_rsrc_t hrs =
         __builtin_amdgcn_make_buffer_rsrc(a.hbuf + (int64_t)par * g.half, 0, (int)(sizeof(float) * g.half), kRsrcWord3);
@@ -429,9 +496,11 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
     float acc[TG];
 #pragma unroll
     for (int t = 0; t < TG; t++) acc[t] = 0.f;
-    // Groups of units whose hidden rows fit the LDS, in plan order.
-    int ua = 0;
-    while (ua < U) {
+    // Groups of units whose hidden rows fit the LDS, in plan order.  The first
+    // group is peeled out of the loop: computing on the tiles inside a loop lets
+    // the compiler hoist work on their loaded values above it, and so wait for
+    // the tiles before the poll.
+    auto group = [&](const int ua) __attribute__((always_inline)) -> int {
         const int va = v_begin(ua);
         int ub = ua + 1;
         while (ub < U && v_end(ub) - va <= g.nb_rows) ub++;
@@ -480,7 +549,11 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
             const int u = p / g.dn_tpr, c = p - u * g.dn_tpr;
             const int v0 = max(v_begin(u), va), v1 = min(v_end(u), vb);
             for (int v = v0; v < v1; v++) {
-                const float s = block_dot<QT, PREC>(t, L.hs + (v - va) * g.f + (4 * c + jb) * kQK);
+                const Tile<QT> one[1] = {t};
+                const float* hv1[1] = {L.hs + (v - va) * g.f + (4 * c + jb) * kQK};
+                float d1[1][1];
+                tile_dots<QT, PREC, 1, 1, 4>(one, hv1, d1);
+                const float s = d1[0][0];
                 const int tk = L.tok[v];
 #pragma unroll
                 for (int q = 0; q < TG; q++) acc[q] += tk == q ? s : 0.f;
@@ -488,21 +561,30 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
         };
 #pragma unroll
         for (int i = 0; i < DPW; i++) {
-            const int p = wave + kWaves * i;
-            if (p >= ua * g.dn_tpr && p < ub * g.dn_tpr) tile_sums(td[i], p);
+            const int v0 = max(sv0[i], va), v1 = min(sv1[i], vb);
+            for (int v = v0; v < v1; v++) {
+                const Tile<QT> one[1] = {td[i]};
+                const float* hv1[1] = {L.hs + (v - va) * g.f + (4 * scol[i] + jb) * kQK};
+                float d1[1][1];
+                tile_dots<QT, PREC, 1, 1, 4>(one, hv1, d1);
+                const int tk = (stok[i] >> (2 * (v - sv0[i]))) & 3;
+#pragma unroll
+                for (int q = 0; q < TG; q++) acc[q] += tk == q ? d1[0][0] : 0.f;
+            }
         }
         // tiles beyond the registers (more units than DPW * 8 / dn_tpr)
         for (int p = kWaves * DPW + wave; p < ub * g.dn_tpr; p += kWaves) {
             if (p < ua * g.dn_tpr) continue;
             const uint8_t* tp = tile_ptr(p);
             Tile<QT> t;
-            if (tp) t.load(tp, lane);
-            else t.clear();
+            t.load(tp ? tp : fallback, lane);
             tile_sums(t, p);
         }
         __syncthreads();
-        ua = ub;
-    }
+        return ub;
+    };
+    int ua = group(0);
+    while (ua < U) ua = group(ua);
     // The four lanes of a row, then the waves in order.
 #pragma unroll
     for (int t = 0; t < TG; t++) {
@@ -536,10 +618,10 @@ hipError_t launch_k(const DGrid& g, const FfnArgs& a, hipStream_t s) {
 }
 
 // Down tiles held in registers per wave: every tile of the step's units in the
-// usual cases (top-8: 9 units at T = 1, up to 10 (Q8_0) or 14 (Q4_0) at T = 2, 18
-// (Q4_0) or 10 (Q8_0) at T = 4, with d_ff 512); more are loaded after the wait.
+// usual cases with d_ff 512 (top-8: 9 units at T = 1; at T = 2, 10 (Q8_0) or
+// 14 (Q4_0); at T = 4, 8 (Q8_0) or 16 (Q4_0)); more are loaded after the wait.
 template <int QT, int TG> constexpr int down_per_wave() {
-    return TG == 1 ? 5 : QT == MOE_Q4_0 ? (TG == 2 ? 7 : 9) : 5;
+    return TG == 1 ? 5 : QT == MOE_Q4_0 ? (TG == 2 ? 7 : 8) : (TG == 2 ? 5 : 4);
 }
 
 template <int QT, int PREC, int TG>
