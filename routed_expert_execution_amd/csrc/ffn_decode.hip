@@ -42,6 +42,11 @@
 // has read it, and every gate/up workgroup with rows to write has read it
 // before any down workgroup can finish, so it needs no host input.  The poll
 // is bounded in time: past it the error word gets kErrSync and the rows are NaN.
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "device_util.h"
 #include "internal.h"
 
@@ -54,28 +59,11 @@ constexpr int kMaxE = 1024;                       // page-table row staged in LD
 constexpr int kMaxUnits = kDecodeMaxT * 32 + 1;   // routed units (<= T * top_k) + shared
 constexpr int kMaxEnt = kDecodeMaxT * 32;         // plan positions (T * top_k)
 constexpr int kMaxRows = kMaxEnt + kDecodeMaxT;   // hidden rows: plan positions + shared rows
-constexpr int kHCap = 40 * 1024;                  // LDS bytes for staged hidden rows
+constexpr int kMaxD = 2048;                       // largest d_model
+constexpr int kHCap = 72 * 1024;                  // LDS bytes for staged hidden rows
 static_assert(kMaxUnits + 1 <= kThreads && kMaxRows <= kThreads, "one plan word per thread");
-constexpr int kHPerThread = (kHCap / 16 + kThreads - 1) / kThreads;  // float4 of staged h per thread
-constexpr int kRsrcWord3 = 0x00020000;            // buffer resource: raw 32-bit dwords
-constexpr int kDeviceScope = 16;                  // buffer load cache policy: sc1 (device scope)
+constexpr int kDeviceScope = 16;                  // load cache policy: sc1 (device scope)
 constexpr uint32_t kPending = 0xFFFFFFFFu;        // hidden-row word not yet written in this launch
-
-// LDS of a down workgroup (the gate/up role uses a prefix of the same bytes).
-struct DownLds {
-    int pts[kMaxE];
-    int exp[kMaxUnits + 3];
-    int off[kMaxUnits + 3];
-    int ent[kMaxEnt];                 // plan position -> entry t * k + j
-    float wbe[kMaxEnt];               // routing weight by entry
-    int tok[kMaxRows];                // hidden row -> token
-    float w[kMaxRows];                // hidden row -> weight
-    int flag[4];
-    int64_t uoff[kMaxUnits + 3];      // unit -> payload offset in the pool (-1 absent, -2 shared)
-    float red[kWaves][kDecodeMaxT][16];
-    float hs[kHCap / 4];
-};
-constexpr int kLdsBytes = sizeof(DownLds);
 
 template <int QT> struct Tile;
 template <> struct Tile<MOE_Q8_0> {
@@ -127,11 +115,12 @@ __device__ inline float code_at(const uint32_t (&w)[8], int e, float s) {
 
 // Dot products of M tiles' blocks (one block per lane) with N activation
 // vectors of 32 floats (LDS, 16-byte aligned): out[m][n] = block_m . v_n.
-// The codes are taken in quarters of 8, each dequantised once for all N
-// vectors; each product chain is split into QA interleaved partial sums (code
-// e into partial e mod QA), added in fixed order at the end, so that the
-// chains are independent.  PREC_F32 multiplies by the scale at the end.
-template <int QT, int PREC, int M, int N, int QA>
+// The codes are taken in chunks of CH (4 or 8), each dequantised once for all
+// N vectors (a smaller chunk keeps fewer activations live); each product chain
+// is split into QA interleaved partial sums (code e into partial e mod QA),
+// added in fixed order at the end, so that the chains are independent.
+// PREC_F32 multiplies by the scale at the end.
+template <int QT, int PREC, int M, int N, int QA, int CH = 8>
 __device__ __forceinline__ void tile_dots(const Tile<QT> (&t)[M], const float* const (&v)[N], float (&out)[M][N]) {
     float acc[M][N][QA];
     uint32_t w[M][8];
@@ -152,19 +141,20 @@ __device__ __forceinline__ void tile_dots(const Tile<QT> (&t)[M], const float* c
             for (int r = 0; r < QA; r++) acc[m][n][r] = 0.f;
     }
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-        float x[N][8];
+    for (int q = 0; q < kQK / CH; q++) {
+        float x[N][CH];
 #pragma unroll
-        for (int n = 0; n < N; n++) {
-            const float4 a0 = *(const float4*)(v[n] + 8 * q), a1 = *(const float4*)(v[n] + 8 * q + 4);
-            x[n][0] = a0.x; x[n][1] = a0.y; x[n][2] = a0.z; x[n][3] = a0.w;
-            x[n][4] = a1.x; x[n][5] = a1.y; x[n][6] = a1.z; x[n][7] = a1.w;
-        }
+        for (int n = 0; n < N; n++)
+#pragma unroll
+            for (int c4 = 0; c4 < CH / 4; c4++) {
+                const float4 a0 = *(const float4*)(v[n] + CH * q + 4 * c4);
+                x[n][4 * c4] = a0.x; x[n][4 * c4 + 1] = a0.y; x[n][4 * c4 + 2] = a0.z; x[n][4 * c4 + 3] = a0.w;
+            }
 #pragma unroll
         for (int m = 0; m < M; m++)
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int e = 8 * q + j;
+            for (int j = 0; j < CH; j++) {
+                const int e = CH * q + j;
                 const float c = code_at<QT, PREC>(w[m], e, s[m]);
 #pragma unroll
                 for (int n = 0; n < N; n++) acc[m][n][e % QA] = fmaf(c, x[n][j], acc[m][n][e % QA]);
@@ -188,6 +178,7 @@ struct DGrid {
     int gu_tpr;      // gate (or up) tiles per 16 hidden units: d_model / 128
     int dn_tpr;      // down tiles per 16 output rows: d_ff / 128
     int nb_rows;     // hidden rows that fit the LDS at once
+    int n_gu_wg;     // gate/up workgroups (block indices [0, n_gu_wg))
     int reset_per;   // pending words each down workgroup writes into the other half
     int64_t half;    // floats per workspace half
     int d, f;
@@ -265,122 +256,161 @@ struct XRow {
 
 // ---- gate/up ------------------------------------------------------------------------
 
-template <int QT, int PREC, int TG, int PPW>
-__device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int item, unsigned char* lds_raw) {
-    int* pts = (int*)lds_raw;
-    int* ents = pts + kMaxE;                                 // [T * k] (T > 1)
-    float* xl = (float*)(ents + kMaxEnt);                    // [TG][d]
-    float* red = xl + TG * g.d;                              // [2][kWaves][TG][16]
+template <int TG, int RG>
+struct GuLds {
+    int pts[kMaxE];
+    int exp[kMaxUnits + 3];
+    int off[kMaxUnits + 3];
+    int ent[kMaxEnt];
+    float red[2][kWaves][RG * TG][16];
+    float x[TG][kMaxD];
+};
+
+// A gate/up workgroup works through items (unit u, RG groups of 16 hidden
+// units) w, w + G, w + 2G, ... of the step's units (G gate/up workgroups, as
+// many as the device holds beside the down workgroups).
+template <int QT, int PREC, int TG, int RG, int PPW>
+__device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int wg, unsigned char* lds_raw) {
+    GuLds<TG, RG>& L = *(GuLds<TG, RG>*)lds_raw;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int u = item / g.n_rg, rg = item - u * g.n_rg;
+    const int n = lane & 15, jb = lane >> 4;
     const bool has_shared = a.shared != nullptr;
     const int n_ent = a.T * a.k;
 
-    // Level 1, all independent loads: the launch count, the unit's plan
-    // entries, the page-table row, and the activations (one token) or the
-    // step's entry list (several).
+    // Level 1, all independent loads: the launch count, the plan (units, entry
+    // ranges, entries), the page-table row and, for one token, its activations.
     const uint32_t count = __hip_atomic_load(a.sync + kSyncCount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int na_raw = *a.n_active;
-    const int e = a.experts[min(u, a.E - 1)];
-    const int o0 = a.offsets[min(u, a.E)];
-    const int o1 = a.offsets[min(u + 1, a.E)];
     PtRow ptr;
     ptr.load(a);
+    const int i1 = threadIdx.x;
+    const uint32_t ex1 = (uint32_t)a.experts[min(i1, a.E - 1)];
+    const uint32_t of1 = (uint32_t)a.offsets[min(i1, a.E)];
+    const uint32_t en1 = (uint32_t)a.entries[min(i1, n_ent - 1)];
     XRow<PREC> x1;
-    int ent1 = 0;
     if constexpr (TG == 1) x1.load(a, g.d, 0);
-    else ent1 = a.entries[min((int)threadIdx.x, n_ent - 1)];
-    ptr.store(a, pts);
-    if constexpr (TG == 1) x1.store(a, g.d, xl);
-    else if (threadIdx.x < n_ent) ents[threadIdx.x] = (int)opaque((uint32_t)ent1);
+    ptr.store(a, L.pts);
+    if (i1 < kMaxUnits) L.exp[i1] = (int)opaque(ex1);
+    if (i1 < kMaxUnits + 1) L.off[i1] = min(max((int)opaque(of1), 0), n_ent);
+    if (i1 < n_ent) L.ent[i1] = min(max((int)opaque(en1), 0), n_ent - 1);
+    if constexpr (TG == 1) x1.store(a, g.d, L.x[0]);
     lds_barrier();
     const int par = launch_parity(opaque(count), g.n_down);
     const int na = min(max((int)opaque((uint32_t)na_raw), 0), g.units_max - (has_shared ? 1 : 0));
-    if (u >= na + (has_shared ? 1 : 0)) return;  // uniform: a unit the step does not have
+    const int per_unit = g.n_rg / RG;  // items per unit
+    const int n_items = (na + (has_shared ? 1 : 0)) * per_unit;
+    const int n_pairs = RG * g.gu_tpr;  // (gate, up) tile pairs per item
 
-    // Level 2: the slot, then every weight load of the item.  Pair pi is column
-    // group pi of the row group (gate tile and up tile); lane (n, jb) =
-    // (lane % 16, lane / 16) holds block 4 pi + jb of hidden unit 16 rg + n.
-    const bool routed = u < na;
-    const uint8_t* base = routed ? slot_base(a, e, pts) : a.shared;
-    if (!base && threadIdx.x == 0) atomicOr(a.err, kErrMiss);
-    // Loads are unconditional: a pair past the row group reads the group's
-    // first pair again (its sums are skipped), a missing expert reads pool slot
-    // 0 (its rows become NaN below).
-    const uint8_t* src = base ? base : a.pool;
-    Tile<QT> tg[PPW], tu[PPW];
+    for (int item = wg; item < n_items; item += g.n_gu_wg) {
+        const int u = item / per_unit, rg0 = (item - u * per_unit) * RG;
+        // The slot, then every weight load of the item.  Pair pi is column group
+        // pi % gu_tpr of row group rg0 + pi / gu_tpr (gate tile and up tile);
+        // lane (n, jb) holds block 4 (pi % gu_tpr) + jb of hidden unit n of that
+        // group.  Loads are unconditional: a pair past the item reads its first
+        // pair again (its sums are skipped), a missing expert reads pool slot 0
+        // (its rows become NaN).
+        const bool routed = u < na;
+        const uint8_t* base = routed ? slot_base(a, L.exp[u], L.pts) : a.shared;
+        if (!base && threadIdx.x == 0) atomicOr(a.err, kErrMiss);
+        const uint8_t* src = base ? base : a.pool;
+        Tile<QT> tg[PPW], tu[PPW];
 #pragma unroll
-    for (int q = 0; q < PPW; q++) {
-        const int pi = wave + q * kWaves;
-        const int64_t t = (int64_t)rg * g.gu_tpr + (pi < g.gu_tpr ? pi : 0);
-        tg[q].load(src + 2 * t * g.tile_bytes, lane);
-        tu[q].load(src + (2 * t + 1) * g.tile_bytes, lane);
-    }
-    const int b0 = routed ? o0 : 0;
-    const int nb = routed ? min(max(o1 - o0, 0), TG) : a.T;  // tokens of the bucket
-    if constexpr (TG > 1) {
-        // the bucket's activations, issued after the weights (loads complete in order)
-        XRow<PREC> xs[TG];
+        for (int q = 0; q < PPW; q++) {
+            const int pi = wave + q * kWaves;
+            const int64_t t = (int64_t)rg0 * g.gu_tpr + (pi < n_pairs ? pi : 0);
+            tg[q].load(src + 2 * t * g.tile_bytes, lane);
+            tu[q].load(src + (2 * t + 1) * g.tile_bytes, lane);
+        }
+        const int b0 = routed ? L.off[u] : 0;
+        const int nb = routed ? min(max(L.off[u + 1] - b0, 0), TG) : a.T;  // tokens of the bucket
+        if constexpr (TG > 1) {
+            // the bucket's activations, issued after the weights (loads complete in order)
+            XRow<PREC> xs[TG];
 #pragma unroll
-        for (int gi = 0; gi < TG; gi++)
-            xs[gi].load(a, g.d, gi >= nb ? -1 : !routed ? gi : min(max(ents[min(b0 + gi, n_ent - 1)] / a.k, 0), a.T - 1));
+            for (int gi = 0; gi < TG; gi++)
+                xs[gi].load(a, g.d, gi >= nb ? -1 : !routed ? gi : min(max(L.ent[min(b0 + gi, n_ent - 1)] / a.k, 0), a.T - 1));
 #pragma unroll
-        for (int gi = 0; gi < TG; gi++) xs[gi].store(a, g.d, xl + gi * g.d);
-        lds_barrier();
-    }
+            for (int gi = 0; gi < TG; gi++) xs[gi].store(a, g.d, L.x[gi]);
+            lds_barrier();
+        }
 
-    // Per lane: sum over the wave's pairs; then the four lanes of a row, then
-    // the waves (through LDS), in fixed order.
-    const int n = lane & 15, jb = lane >> 4;
-    float accg[TG], accu[TG];
+        // Per lane: sum over the wave's pairs of each row group; then the four
+        // lanes of a row, then the waves (through LDS), in fixed order.
+        float accg[RG][TG], accu[RG][TG];
 #pragma unroll
-    for (int gi = 0; gi < TG; gi++) accg[gi] = accu[gi] = 0.f;
+        for (int r = 0; r < RG; r++)
 #pragma unroll
-    for (int q = 0; q < PPW; q++) {
-        const int pi = wave + q * kWaves;
-        if (pi >= g.gu_tpr) break;
-        const int cb = 4 * pi + jb;
-        const float* xv[TG];
+            for (int gi = 0; gi < TG; gi++) accg[r][gi] = accu[r][gi] = 0.f;
 #pragma unroll
-        for (int gi = 0; gi < TG; gi++) xv[gi] = xl + gi * g.d + cb * kQK;
-        const Tile<QT> pair[2] = {tg[q], tu[q]};
-        float dd[2][TG];
-        tile_dots<QT, PREC, 2, TG, TG == 1 ? 4 : TG == 2 ? 2 : 1>(pair, xv, dd);
+        for (int q = 0; q < PPW; q++) {
+            const int pi = wave + q * kWaves;
+            if (pi >= n_pairs) break;
+            const int rr = pi / g.gu_tpr, cb = 4 * (pi - rr * g.gu_tpr) + jb;
+            const float* xv[TG];
 #pragma unroll
-        for (int gi = 0; gi < TG; gi++) {
-            accg[gi] += dd[0][gi];
-            accu[gi] += dd[1][gi];
+            for (int gi = 0; gi < TG; gi++) xv[gi] = L.x[gi] + cb * kQK;
+            const Tile<QT> pair[2] = {tg[q], tu[q]};
+            float dd[2][TG];
+            tile_dots<QT, PREC, 2, TG, TG == 1 ? 4 : TG == 2 ? 2 : 1, TG == 1 ? 8 : 4>(pair, xv, dd);
+#pragma unroll
+            for (int r = 0; r < RG; r++)
+#pragma unroll
+                for (int gi = 0; gi < TG; gi++) {
+                    accg[r][gi] += rr == r ? dd[0][gi] : 0.f;
+                    accu[r][gi] += rr == r ? dd[1][gi] : 0.f;
+                }
         }
-    }
 #pragma unroll
-    for (int gi = 0; gi < TG; gi++) {
-        const float gs = cross_row_sum(accg[gi]), us = cross_row_sum(accu[gi]);
-        if (jb == 0) {
-            red[((0 * kWaves + wave) * TG + gi) * 16 + n] = gs;
-            red[((1 * kWaves + wave) * TG + gi) * 16 + n] = us;
-        }
-    }
-    lds_barrier();
-    // Wave 0 holds every (token, unit) of the item: 16 * TG <= 64 threads.
-    if (threadIdx.x < 16 * TG) {
-        const int gi = threadIdx.x >> 4, r = threadIdx.x & 15;
-        if (gi < nb) {
-            float gs = 0.f, us = 0.f;
-            for (int w = 0; w < kWaves; w++) {
-                gs += red[((0 * kWaves + w) * TG + gi) * 16 + r];
-                us += red[((1 * kWaves + w) * TG + gi) * 16 + r];
+        for (int r = 0; r < RG; r++)
+#pragma unroll
+            for (int gi = 0; gi < TG; gi++) {
+                const float gs = cross_row_sum(accg[r][gi]), us = cross_row_sum(accu[r][gi]);
+                if (jb == 0) {
+                    L.red[0][wave][r * TG + gi][n] = gs;
+                    L.red[1][wave][r * TG + gi][n] = us;
+                }
             }
-            float hv = silu(gs) * us;
-            if (PREC == MOE_PREC_BF16) hv = round_bf16(hv);
-            const int row = routed ? b0 + gi : a.T * a.k + gi;
-            // device scope: written through to where every XCD reads it
-            __hip_atomic_store(a.hbuf + (int64_t)par * g.half + (int64_t)row * g.f + 16 * rg + r,
-                               base ? hv : __uint_as_float(0x7FC00000u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lds_barrier();
+        // Threads (row group, token, unit): 16 * TG * RG <= 128.
+        if (threadIdx.x < 16 * TG * RG) {
+            const int rt = threadIdx.x >> 4, hr = threadIdx.x & 15;
+            const int r = rt / TG, gi = rt - r * TG;
+            if (gi < nb) {
+                float gs = 0.f, us = 0.f;
+                for (int w = 0; w < kWaves; w++) {
+                    gs += L.red[0][w][rt][hr];
+                    us += L.red[1][w][rt][hr];
+                }
+                float hv = silu(gs) * us;
+                if (PREC == MOE_PREC_BF16) hv = round_bf16(hv);
+                const int row = routed ? b0 + gi : a.T * a.k + gi;
+                // device scope: written through to where every XCD reads it
+                __hip_atomic_store(a.hbuf + (int64_t)par * g.half + (int64_t)row * g.f + 16 * (rg0 + r) + hr,
+                                   base ? hv : __uint_as_float(0x7FC00000u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
+        lds_barrier();  // L.red and L.x are reused by the next item
     }
 }
 
 // ---- down + merge --------------------------------------------------------------------
+
+struct DownLds {
+    int exp[kMaxUnits + 3];
+    int off[kMaxUnits + 3];
+    int ent[kMaxEnt];                 // plan position -> entry t * k + j
+    float wbe[kMaxEnt];               // routing weight by entry
+    int tok[kMaxRows];                // hidden row -> token
+    float w[kMaxRows];                // hidden row -> weight
+    int flag[4];
+    int64_t uoff[kMaxUnits + 3];      // unit -> payload offset in the pool (-1 absent, -2 shared)
+    float red[kWaves][kDecodeMaxT][16];
+    float zero[kQK];                  // a zero block of activations (rows a bucket does not have)
+    union {                           // the page-table row is read only before staging starts
+        int pts[kMaxE];
+        float hs[kHCap / 4];
+    };
+};
 
 template <int QT, int PREC, int TG, int DPW>
 __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char* lds_raw) {
@@ -409,6 +439,7 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
         L.wbe[i1] = __uint_as_float(opaque(w1));
     }
     if (threadIdx.x == 0) L.flag[0] = 1;
+    if (threadIdx.x < kQK) L.zero[threadIdx.x] = 0.f;
     lds_barrier();
     const int par = launch_parity(opaque(count), g.n_down);
     const int na = min(max((int)opaque((uint32_t)na_raw), 0), g.units_max - (has_shared ? 1 : 0));
@@ -490,8 +521,7 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
         scol[i] = __builtin_amdgcn_readfirstlane(min(p, max(P - 1, 0)) - u * g.dn_tpr);
     }
 
-    const __amdgpu_buffer_rsrc_t hrs =
-        __builtin_amdgcn_make_buffer_rsrc(a.hbuf + (int64_t)par * g.half, 0, (int)(sizeof(float) * g.half), kRsrcWord3);
+    const float* hhalf = a.hbuf + (int64_t)par * g.half;
     const uint64_t t0 = wall_clock64();
     float acc[TG];
 #pragma unroll
@@ -505,23 +535,22 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
         int ub = ua + 1;
         while (ub < U && v_end(ub) - va <= g.nb_rows) ub++;
         const int vb = min(v_end(ub - 1), va + g.nb_rows);  // (a valid plan never clips)
-        // Poll rows [va, vb) until no pending word is left (every load of the
-        // thread, then the checks), then stage them scaled by the row weight.
-        const int n4 = max(vb - va, 0) * g.f / 4;
-        float4 hv[kHPerThread];
+        // Stage rows [va, vb) straight into LDS with device-scope loads (1 KB
+        // per wave instruction, no registers), until no pending word is left.
+        const int n16 = max(vb - va, 0) * g.f / 4;  // 16-byte pieces
+        const int n_ins = (n16 + 63) / 64;
+        const float* src = hhalf + (int64_t)va * g.f;
         for (;;) {
-#pragma unroll
-            for (int j = 0; j < kHPerThread; j++) {
-                const int i = threadIdx.x + j * kThreads;
-                hv[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                       hrs, (va * g.f + 4 * min(i, max(n4 - 1, 0))) * 4, 0, kDeviceScope));
-            }
+            for (int j = wave; j < n_ins; j += kWaves)
+                __builtin_amdgcn_global_load_lds(src + 4 * min(j * 64 + lane, n16 - 1),
+                                                  (__attribute__((address_space(3))) void*)(L.hs + j * 256), 16, 0,
+                                                  kDeviceScope);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
             int pend = 0;
-#pragma unroll
-            for (int j = 0; j < kHPerThread; j++) {
-                const int i = threadIdx.x + j * kThreads;
-                const uint4 b = __builtin_bit_cast(uint4, hv[j]);
-                pend |= (i < n4) & ((b.x == kPending) | (b.y == kPending) | (b.z == kPending) | (b.w == kPending));
+            for (int i = threadIdx.x; i < n16; i += kThreads) {
+                const uint4 b = *(const uint4*)(L.hs + 4 * i);
+                pend |= (b.x == kPending) | (b.y == kPending) | (b.z == kPending) | (b.w == kPending);
             }
             if (!__syncthreads_or(pend)) break;
             const int expired = threadIdx.x == 0 && (int64_t)(wall_clock64() - t0) > a.wait_ticks;
@@ -534,51 +563,60 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
             }
             __builtin_amdgcn_s_sleep(2);
         }
-#pragma unroll
-        for (int j = 0; j < kHPerThread; j++) {
-            const int i = threadIdx.x + j * kThreads;
-            if (i < n4) {
-                const float wr = L.w[va + 4 * i / g.f];
-                const float4 h = hv[j];
-                ((float4*)L.hs)[i] = make_float4(wr * h.x, wr * h.y, wr * h.z, wr * h.w);
-            }
-        }
-        __syncthreads();
-        // Per lane: the tiles of units [ua, ub), each with the unit's rows.
-        auto tile_sums = [&](const Tile<QT> t, int p) __attribute__((always_inline)) {
-            const int u = p / g.dn_tpr, c = p - u * g.dn_tpr;
-            const int v0 = max(v_begin(u), va), v1 = min(v_end(u), vb);
-            for (int v = v0; v < v1; v++) {
-                const Tile<QT> one[1] = {t};
-                const float* hv1[1] = {L.hs + (v - va) * g.f + (4 * c + jb) * kQK};
-                float d1[1][1];
-                tile_dots<QT, PREC, 1, 1, 4>(one, hv1, d1);
-                const float s = d1[0][0];
-                const int tk = L.tok[v];
-#pragma unroll
-                for (int q = 0; q < TG; q++) acc[q] += tk == q ? s : 0.f;
-            }
-        };
+        // Per lane: the tiles of units [ua, ub), each with the unit's rows:
+        // acc[token] += w * (block . h).
 #pragma unroll
         for (int i = 0; i < DPW; i++) {
             const int v0 = max(sv0[i], va), v1 = min(sv1[i], vb);
-            for (int v = v0; v < v1; v++) {
-                const Tile<QT> one[1] = {td[i]};
-                const float* hv1[1] = {L.hs + (v - va) * g.f + (4 * scol[i] + jb) * kQK};
-                float d1[1][1];
-                tile_dots<QT, PREC, 1, 1, 4>(one, hv1, d1);
-                const int tk = (stok[i] >> (2 * (v - sv0[i]))) & 3;
+            if (v0 >= v1) continue;
+            const Tile<QT> one[1] = {td[i]};
+            if constexpr (TG <= 2) {
+                // the unit's rows (at most TG), each block dequantised once for all
+                const float* hr[TG];
 #pragma unroll
-                for (int q = 0; q < TG; q++) acc[q] += tk == q ? d1[0][0] : 0.f;
+                for (int r = 0; r < TG; r++)
+                    hr[r] = v0 + r < v1 ? L.hs + (v0 + r - va) * g.f + (4 * scol[i] + jb) * kQK : L.zero;
+                float dr[1][TG];
+                tile_dots<QT, PREC, 1, TG, TG == 1 ? 4 : 2>(one, hr, dr);
+#pragma unroll
+                for (int r = 0; r < TG; r++) {
+                    if (v0 + r >= v1) break;
+                    const int tk = (stok[i] >> (2 * (v0 + r - sv0[i]))) & 3;
+                    const float dw = L.w[v0 + r] * dr[0][r];
+#pragma unroll
+                    for (int q = 0; q < TG; q++) acc[q] += tk == q ? dw : 0.f;
+                }
+            } else {
+                // one row at a time: four rows' dequantised codes do not fit
+                // beside DPW tiles in registers
+                for (int v = v0; v < v1; v++) {
+                    const float* hv1[1] = {L.hs + (v - va) * g.f + (4 * scol[i] + jb) * kQK};
+                    float d1[1][1];
+                    tile_dots<QT, PREC, 1, 1, 4>(one, hv1, d1);
+                    const int tk = (stok[i] >> (2 * (v - sv0[i]))) & 3;
+                    const float dw = L.w[v] * d1[0][0];
+#pragma unroll
+                    for (int q = 0; q < TG; q++) acc[q] += tk == q ? dw : 0.f;
+                }
             }
         }
         // tiles beyond the registers (more units than DPW * 8 / dn_tpr)
         for (int p = kWaves * DPW + wave; p < ub * g.dn_tpr; p += kWaves) {
             if (p < ua * g.dn_tpr) continue;
             const uint8_t* tp = tile_ptr(p);
-            Tile<QT> t;
-            t.load(tp ? tp : fallback, lane);
-            tile_sums(t, p);
+            Tile<QT> t[1];
+            t[0].load(tp ? tp : fallback, lane);
+            const int u = p / g.dn_tpr, c = p - u * g.dn_tpr;
+            const int v0 = max(v_begin(u), va), v1 = min(v_end(u), vb);
+            for (int v = v0; v < v1; v++) {
+                const float* hv1[1] = {L.hs + (v - va) * g.f + (4 * c + jb) * kQK};
+                float d1[1][1];
+                tile_dots<QT, PREC, 1, 1, 4>(t, hv1, d1);
+                const int tk = L.tok[v];
+                const float dw = L.w[v] * d1[0][0];
+#pragma unroll
+                for (int q = 0; q < TG; q++) acc[q] += tk == q ? dw : 0.f;
+            }
         }
         __syncthreads();
         return ub;
@@ -602,33 +640,65 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
     if (threadIdx.x == 0) __hip_atomic_fetch_add(a.sync + kSyncCount, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+constexpr int kLdsBytes = sizeof(DownLds) > sizeof(GuLds<kDecodeMaxT, 2>) ? sizeof(DownLds) : sizeof(GuLds<kDecodeMaxT, 2>);
+
+// Hidden-unit groups of 16 per gate/up item: 2 for steps of several tokens
+// (fewer, larger items: one round of workgroups holds the step).
+template <int QT, int TG> constexpr int rows_per_item() { return TG > 1 ? 2 : 1; }
+
 template <int QT, int PREC, int TG, int PPW, int DPW>
 __global__ __launch_bounds__(kThreads, 4) void ffn_decode_kernel(FfnArgs a, DGrid g) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-    const int b = blockIdx.x, n_gu = g.units_max * g.n_rg;
-    if (b < n_gu) gate_up_role<QT, PREC, TG, PPW>(a, g, b, lds);
-    else down_role<QT, PREC, TG, DPW>(a, g, b - n_gu, lds);
+    const int b = blockIdx.x;
+    if (b < g.n_gu_wg) gate_up_role<QT, PREC, TG, rows_per_item<QT, TG>(), PPW>(a, g, b, lds);
+    else down_role<QT, PREC, TG, DPW>(a, g, b - g.n_gu_wg, lds);
+}
+
+// Workgroups of `kern` the device holds at once (0 if unknown).
+int resident_capacity(const void* kern) {
+    static std::mutex mu;
+    static std::map<std::pair<const void*, int>, int> cap;  // (kernel, device) -> workgroups
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cap.find({kern, dev});
+    if (it == cap.end()) {
+        int occ = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            occ = cus = 0;
+        it = cap.emplace(std::make_pair(kern, dev), occ * cus).first;
+    }
+    return it->second;
 }
 
 template <int QT, int PREC, int TG, int PPW, int DPW>
-hipError_t launch_k(const DGrid& g, const FfnArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((ffn_decode_kernel<QT, PREC, TG, PPW, DPW>), dim3(g.units_max * g.n_rg + g.n_down),
-                       dim3(kThreads), 0, s, a, g);
+hipError_t launch_k(DGrid g, const FfnArgs& a, hipStream_t s) {
+    auto kern = ffn_decode_kernel<QT, PREC, TG, PPW, DPW>;
+    // As many gate/up workgroups as the device holds beside the down ones (all
+    // resident: no workgroup waits for a slot), at most one per item.
+    const int items = g.units_max * (g.n_rg / rows_per_item<QT, TG>());
+    const int cap = resident_capacity((const void*)kern);
+    g.n_gu_wg = cap > g.n_down ? std::min(items, cap - g.n_down) : items;
+    hipLaunchKernelGGL(kern, dim3(g.n_gu_wg + g.n_down), dim3(kThreads), 0, s, a, g);
     return hipGetLastError();
 }
 
 // Down tiles held in registers per wave: every tile of the step's units in the
-// usual cases with d_ff 512 (top-8: 9 units at T = 1; at T = 2, 10 (Q8_0) or
-// 14 (Q4_0); at T = 4, 8 (Q8_0) or 16 (Q4_0)); more are loaded after the wait.
+// usual cases with d_ff 512 (top-8: 9 units at T = 1; at T = 2, 6 (Q8_0) or
+// 12 (Q4_0); at T = 4, 6 (Q8_0) or 20 (Q4_0)); more are loaded after the wait.
 template <int QT, int TG> constexpr int down_per_wave() {
-    return TG == 1 ? 5 : QT == MOE_Q4_0 ? (TG == 2 ? 7 : 8) : (TG == 2 ? 5 : 4);
+    return TG == 1 ? 5 : QT == MOE_Q4_0 ? (TG == 2 ? 6 : 10) : 3;
 }
 
 template <int QT, int PREC, int TG>
 hipError_t launch_w(const DGrid& g, const FfnArgs& a, hipStream_t s) {
     constexpr int D = down_per_wave<QT, TG>();
-    if (g.gu_tpr <= kWaves) return launch_k<QT, PREC, TG, 1, D>(g, a, s);
-    if (g.gu_tpr <= 2 * kWaves) return launch_k<QT, PREC, TG, 2, D>(g, a, s);
+    const int pairs = rows_per_item<QT, TG>() * g.gu_tpr;  // tile pairs per gate/up item
+    if (g.n_rg % rows_per_item<QT, TG>()) return hipErrorInvalidValue;
+    if (pairs <= kWaves) return launch_k<QT, PREC, TG, 1, D>(g, a, s);
+    if (pairs <= 2 * kWaves) return launch_k<QT, PREC, TG, 2, D>(g, a, s);
+    if (pairs <= 4 * kWaves) return launch_k<QT, PREC, TG, 4, D>(g, a, s);
     return hipErrorInvalidValue;
 }
 
@@ -642,7 +712,7 @@ hipError_t launch_tg(const DGrid& g, const FfnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_ffn_decode(const Geom& geo, const FfnArgs& a, int prec, hipStream_t s) {
-    if (a.T < 1 || a.T > kDecodeMaxT || a.E > kMaxE || a.k > 32) return hipErrorInvalidValue;
+    if (a.T < 1 || a.T > kDecodeMaxT || a.E > kMaxE || a.k > 32 || geo.d > kMaxD) return hipErrorInvalidValue;
     DGrid g{};
     g.units_max = min(a.T * a.k, a.E) + (a.shared ? 1 : 0);
     g.n_down = geo.d / 16;
@@ -656,9 +726,7 @@ hipError_t launch_ffn_decode(const Geom& geo, const FfnArgs& a, int prec, hipStr
     g.nb_rows = kHCap / (4 * geo.f);
     g.half = decode_h_floats(a.k, geo.f) / 2;
     g.reset_per = (int)((g.half + g.n_down - 1) / g.n_down);
-    // LDS: the gate/up role's page-table row, activations and sums fit the down role's layout
-    if (g.nb_rows < kDecodeMaxT || 4 * (kMaxE + kMaxEnt + kDecodeMaxT * geo.d + 2 * kWaves * kDecodeMaxT * 16) > kLdsBytes)
-        return hipErrorInvalidValue;
+    if (g.nb_rows < kDecodeMaxT) return hipErrorInvalidValue;
     if (geo.qtype == MOE_Q8_0)
         return prec == MOE_PREC_BF16 ? launch_tg<MOE_Q8_0, MOE_PREC_BF16>(g, a, s)
                                      : launch_tg<MOE_Q8_0, MOE_PREC_F32>(g, a, s);
