@@ -3,9 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|mtp|prefill]
 
 A step is one pass of the whole hot path over one batch: router logits and
-top-k (moe_route), expert-major union (moe_plan_union) and the quantised
-SwiGLU experts with the shared expert and the weighted combine
-(moe_expert_ffn).  Default workload "decode": 256 experts, top-8 plus one
+top-k, the expert-major union and the quantised SwiGLU experts with the shared
+expert and the weighted combine.  Steps of up to 4 tokens (decode, mtp) run as
+ONE launch (moe_route_ffn); the prefill chunk as moe_route_union followed by
+moe_expert_ffn.  Default workload "decode": 256 experts, top-8 plus one
 shared expert, d_model 2048, d_ff 512, Q8_0, one token per step, 38-slot
 (15 %) cache.  "mtp": the same layer with Q4_0 weights, four tokens per step
 with overlapping routes, 89-slot (35 %) cache.  "prefill": the same layer,
@@ -20,12 +21,14 @@ side stream, and then a 512 MiB buffer is read so that neither L2 nor the
 every expert byte from HBM.  The flush reads rather than writes, so the
 Infinity Cache is left holding clean lines, as it is after other layers'
 weight reads; a written flush would leave 256 MB of dirty lines whose
-write-back would be charged to the timed step.  The timed region of a step is route + union (moe_route_union)
-+ FFN, bracketed by one pair of HIP events on the stream the kernels run on.
-For the roofline, a second pass over the first min(K, 100) of the same steps
-(same staging and flush) brackets the FFN launch alone; it is a separate pass
-because an event recorded between route and FFN adds idle time of its own.
-Inputs are resident in HBM when the timed region starts.
+write-back would be charged to the timed step.  The timed region of a step is
+the whole step (route + union + FFN), bracketed by one pair of HIP events on
+the stream the kernels run on.  Two more passes over the first min(K, 100) of
+the same steps (same staging and flush) time, for comparison, the separate
+calls (moe_route_union, then moe_expert_ffn) and the FFN launch alone (for the
+prefill chunk the latter is the roofline's kernel; an event recorded between
+route and FFN would add idle time of its own, hence separate passes).  Inputs
+are resident in HBM when the timed region starts.
 
 Prints one JSON line.
 """
@@ -49,7 +52,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_decode_traffic.json")
 
 def _kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("ffn_decode.hip", "device_util.h", "internal.h"):
+    for f in ("ffn_decode.hip", "device_util.h", "internal.h", "route_device.h"):
         h.update(open(os.path.join(ROOT, "routed_expert_execution_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -125,6 +128,8 @@ def main() -> int:
     ap.add_argument("--workload", default="decode", choices=["decode", "mtp", "prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="leave L2 / Infinity Cache warm (labelled)")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="time steps of up to 4 tokens as moe_route_union + moe_expert_ffn, not one launch")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the routed-expert path; --gpus {args.gpus} is not "
@@ -185,6 +190,16 @@ def main() -> int:
         else:
             moe.moe_route_union(ctx, ids, w, plan, x=x_all[s], w_router=wr)
 
+    one_launch = T <= 4 and not args.separate_calls  # the step as one moe_route_ffn launch
+
+    def whole_step(s):
+        if one_launch:
+            kw = dict(logits_in=lg_all[s]) if lg_all is not None else dict(w_router=wr)
+            moe.moe_route_ffn(ctx, 0, x_all[s], ids, w, plan, y, shared_payload=shared, prec=prec, **kw)
+        else:
+            route_plan(s)
+            moe.moe_expert_ffn(ctx, 0, x_all[s], plan, w, y, shared_payload=shared, prec=prec)
+
     misses = 0
 
     def prepare(s):
@@ -208,7 +223,7 @@ def main() -> int:
     def new_events(m):
         return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(m)]
 
-    # Pass 1 (the K timed steps): route + union + FFN between one event pair.
+    # Pass 1 (the K timed steps): the whole step between one event pair.
     ev = new_events(n_steps)
     n_unique = []
     torch.cuda.synchronize()
@@ -219,19 +234,26 @@ def main() -> int:
         n = prepare(s)
         e0, e2 = ev[s]
         e0.record(stream)
-        route_plan(s)
-        moe.moe_expert_ffn(ctx, 0, x_all[s], plan, w, y, shared_payload=shared, prec=prec)
+        whole_step(s)
         e2.record(stream)
         moe.moe_slot_release(ctx, 0)
         n_unique.append(n)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall_t0
-    # Pass 2 (roofline): the same steps, the FFN launch alone between the events
-    # (an event between route and FFN would add its own idle time to pass 1).
+    # Pass 2: the same steps as separate calls (route + union, then FFN).
+    # Pass 3: the FFN launch alone between the events (route and union before
+    # them, untimed).
     n_ffn = min(args.steps, 100)
-    ev_ffn = new_events(n_ffn)
+    ev_sep, ev_ffn = new_events(n_ffn), new_events(n_ffn)
     for i in range(n_ffn):
         s = args.warmup + i
+        prepare(s)
+        e1, e2 = ev_sep[i]
+        e1.record(stream)
+        route_plan(s)
+        moe.moe_expert_ffn(ctx, 0, x_all[s], plan, w, y, shared_payload=shared, prec=prec)
+        e2.record(stream)
+        moe.moe_slot_release(ctx, 0)
         prepare(s)
         route_plan(s)
         e1, e2 = ev_ffn[i]
@@ -246,12 +268,15 @@ def main() -> int:
         return 1
 
     span = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(args.warmup, n_steps)]) * 1e3  # us
+    sep = np.array([a.elapsed_time(b) for a, b in ev_sep]) * 1e3
     ffn = np.array([a.elapsed_time(b) for a, b in ev_ffn]) * 1e3
     uniq = np.array(n_unique[args.warmup:])
     uniq_ffn = uniq[:n_ffn]
     algo_bytes = (uniq + 1) * pb  # unique routed experts + the shared expert, per step
     ffn_gbs = ((uniq_ffn + 1) * pb).mean() / (ffn.mean() * 1e-6) / 1e9
     span_gbs = algo_bytes.mean() / (span.mean() * 1e-6) / 1e9
+    # roofline kernel: the one launch of the whole step (T <= 4), else the FFN launch
+    roof_gbs = span_gbs if one_launch else ffn_gbs
     traffic = _traffic(args.workload)
 
     line = {
@@ -280,20 +305,26 @@ def main() -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "moe_expert_ffn (one call: its expert kernels and the combine)",
-            "achieved": ffn_gbs,
+            "kernel": ("moe_route_ffn: one launch of router, top-k, union, routed + shared experts and "
+                       "the weighted merge; bytes = expert payloads only" if one_launch else
+                       "moe_expert_ffn (one call: its expert kernels and the combine)"),
+            "achieved": roof_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": ffn_gbs / HBM_PEAK_GBS,
+            "frac": roof_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
         },
         "detail": {
             "layer_span_us_p50": float(np.percentile(span, 50)),
             "layer_span_us_p90": float(np.percentile(span, 90)),
+            "one_launch": one_launch,
+            "separate_calls_span_us_mean": float(sep.mean()),
+            "separate_calls_span_us_p50": float(np.percentile(sep, 50)),
             "ffn_us_mean": float(ffn.mean()),
             "ffn_us_p50": float(np.percentile(ffn, 50)),
             "ffn_us_p90": float(np.percentile(ffn, 90)),
-            "route_union_us_mean_est": float(span.mean() - ffn.mean()),
+            "ffn_GBps": ffn_gbs,
+            "route_union_us_mean_est": float(sep.mean() - ffn.mean()),
             "ffn_timed_steps": int(n_ffn),
             "expert_bytes_per_step": float(algo_bytes.mean()),
             "layer_span_GBps": span_gbs,

@@ -231,6 +231,27 @@ moe_status moe_expert_ffn(moe_ctx* ctx, int32_t layer, const void* x, int32_t x_
                           const moe_plan* plan, const float* topk_w, const void* shared_payload,
                           int32_t prec, float* y, moe_stream stream);
 
+/* The whole decode step of up to 4 tokens in ONE launch: moe_route_union and
+ * then moe_expert_ffn, with the same results bit for bit ("Nanite for Experts",
+ * §12, milestone 1: one expert-major operator for the step; §3.1: the router's
+ * choice is authoritative).  Router workgroups compute the logits (from x and
+ * w_router, as moe_route; or logits_in [T, n_experts] is taken as given) and
+ * hand them to the expert workgroups through the context's workspace; each of
+ * those selects the top-k and forms the union itself, and the shared expert's
+ * work starts before routing ends.  Every expert the routing picks must already
+ * be mapped (moe_slot_map / moe_slot_fill, or moe_slot_bind): one that is not
+ * makes its tokens' rows NaN (MOE_EMISS at moe_check).
+ * x: device [T, d_model] (x_dtype), also the router's input.  w_router: device
+ * [n_experts, d_model] fp32, or NULL with logits_in.  Outputs: topk_ids [T,
+ * top_k] int32, topk_w [T, top_k] fp32 and plan, as moe_route_union writes
+ * them, and y [T, d_model] fp32 as moe_expert_ffn.  1 <= T <= min(4,
+ * max_tokens) and n_experts <= 256, else MOE_EINVAL.  Waits on `stream` for
+ * fills not yet awaited.  Calls on one context must not overlap. */
+moe_status moe_route_ffn(moe_ctx* ctx, int32_t layer, const void* x, int32_t x_dtype, const float* w_router,
+                         const float* logits_in, int64_t T, int32_t* topk_ids, float* topk_w,
+                         const moe_plan* plan, const void* shared_payload, int32_t prec, float* y,
+                         moe_stream stream);
+
 /* ---- inspection ------------------------------------------------------------- */
 
 /* Dequantise one device payload into device out [3 * d_ff * d_model] fp32 in
@@ -245,8 +266,8 @@ moe_status moe_dequant(moe_ctx* ctx, const void* payload, int32_t prec, float* o
 moe_status moe_stats(const moe_ctx* ctx, uint64_t out[5]);
 
 /* Synchronise `stream`, read and clear the error word: MOE_OK, MOE_EMISS,
- * MOE_ETIMEOUT (a decode launch's wait for its gate/up workgroups ran out, about
- * 200 ms; its rows are NaN; the counters are reset here), or MOE_EINVAL for an
+ * MOE_ETIMEOUT (a decode launch's wait for its gate/up or router workgroups ran
+ * out, about 200 ms; its rows are NaN; the counters are reset here), or MOE_EINVAL for an
  * out-of-range expert id met by moe_plan_union. */
 moe_status moe_check(moe_ctx* ctx, moe_stream stream);
 

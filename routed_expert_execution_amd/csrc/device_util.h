@@ -100,6 +100,24 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
     return max_u64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);
 }
 
+// Maximum over the wave of an unsigned 32-bit value, returned to every lane:
+// the same partner exchanges, one max each.
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, false));
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max((uint32_t)r[0], (uint32_t)r[1]);
+    r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max((uint32_t)r[0], (uint32_t)r[1]);
+}
+
+// Bits of the lanes below this one in a 64-lane mask.
+__device__ inline int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // int8 lane j of a 32-bit word -> float

@@ -1,54 +1,69 @@
 // Decode step of the routed experts (T <= 4 tokens) in ONE launch: every
-// expert of the step and the weighted merge into the tokens' rows — the
+// expert of the step and the weighted merge into the tokens' rows -- the
 // expert-major operator that consumes routed positions and page-table entries
 // for several resident experts at once ("Nanite for Experts", §12, milestone
 // 1; §11.5: one expert-major unit of execution rather than many separately
 // orchestrated fragments; §5.5: results merged into the original positions).
+// The launch can also route the step itself (moe_route_ffn).
 //
 // A unit is a routed expert of the plan (ascending expert id) or the shared
 // expert (last).  A hidden row is one (unit, token) pair: row q < T*k is plan
 // position q, row T*k + t is the shared expert on token t.  The launch has two
 // kinds of workgroups:
 //
-//   gate/up workgroup (u, g), one per unit and 16 hidden units: its 16 rows of
-//     W_g and W_u dequantised in registers against the bucket's activations
-//     (LDS); h = silu(W_g x) * (W_u x) for each token of the bucket, stored to
-//     the hidden-row workspace.  Nothing waits for the stores.
+//   gate/up workgroups, as many as stay resident beside the down ones, each
+//     working through items (a unit and 16 or 32 hidden units; the shared
+//     expert's items first): the item's rows of W_g and W_u dequantised in
+//     registers against the bucket's activations (LDS); h = silu(W_g x) *
+//     (W_u x) for each token of the bucket, stored to the hidden-row
+//     workspace.  Nothing waits for the stores.
 //   down workgroup R, one per 16 output rows: reads the page-table row and the
 //     plan, issues the loads of its 16 rows of every unit's W_d (d_ff/128
 //     contiguous tiles per unit), then polls the hidden rows it needs until
-//     every value has been written, stages them in LDS multiplied by the row's
-//     routing weight (1 for the shared expert), and sums
-//     y[t, rows] = sum over t's hidden rows of W_d[rows] (w h)
+//     every value has been written, stages them in LDS, and sums
+//     y[t, rows] = sum over t's hidden rows of w * (W_d[rows] h)
 //     in one fixed order that depends only on expert ids and ranks, never on
 //     slots: per lane over its tiles in order, then the four lanes of a row,
 //     then the waves.
+//
+// A launch that routes takes the caller's logits, or computes them: wave 0 (or
+// more waves) of each gate/up workgroup whose first item is routed computes
+// about one router row and stores it with device scope into the workspace.
+// Every workgroup then reads the logits (polling until none is pending),
+// selects each token's top-k and forms the union itself, with the same code as
+// the route kernels; down workgroup 0 also writes ids, weights and plan out.
+// The shared expert's items start before the routing is known.
 //
 // Every weight byte of the step is requested as soon as its workgroup has the
 // unit's slot: each role reads what it needs from the plan and the whole
 // page-table row in one round of independent loads.  Gate/up workgroups take
 // the first block indices, so their weights lead the memory queue and the down
-// weights arrive about when the hidden rows are ready; they never wait, so the
-// hand-off always completes.
+// weights arrive about when the hidden rows are ready.
 //
 // Hand-off without counters or cache-wide fences: the workspace holds two
-// halves of hidden rows.  A launch writes h into half p with device-scope (sc1)
-// stores, which are coherent across the XCDs' L2 caches; the down workgroups
-// read half p with device-scope loads until no "pending" word 0xFFFFFFFF (a
-// NaN no arithmetic on finite values produces) is left, and refill half p ^ 1
-// with it for the next launch.  p is the parity of the launch count, a device
-// word each down workgroup increments (without return) when it is done: it
-// reaches the next launch's value only once every down workgroup of this one
-// has read it, and every gate/up workgroup with rows to write has read it
-// before any down workgroup can finish, so it needs no host input.  The poll
-// is bounded in time: past it the error word gets kErrSync and the rows are NaN.
+// halves, each with hidden rows and logits.  A launch writes into half p with
+// device-scope (sc1) stores, which are coherent across the XCDs' L2 caches;
+// readers load half p with device-scope loads until no "pending" word
+// 0xFFFFFFFF (a NaN no arithmetic on finite values produces) is left, and the
+// down workgroups refill half p ^ 1 with it for the next launch.  p is the
+// parity of the launch count, a device word each down workgroup increments
+// (without return) when it is done: it reaches the next launch's value only
+// once every down workgroup of this one has read it.  Every gate/up workgroup
+// with rows to write has read it before any down workgroup can finish; in a
+// launch that routes from x, where a gate/up workgroup reads logits before it
+// knows whether it has items, the gate/up workgroups also count their arrival
+// (per parity) and the down workgroups count themselves done only after all
+// have arrived.  Every wait is bounded in time: past it the error word gets
+// kErrSync and the rows are NaN.
 #include <algorithm>
+#include <cstddef>
 #include <map>
 #include <mutex>
 #include <utility>
 
 #include "device_util.h"
 #include "internal.h"
+#include "route_device.h"
 
 namespace moe {
 namespace {
@@ -62,6 +77,7 @@ constexpr int kMaxRows = kMaxEnt + kDecodeMaxT;   // hidden rows: plan positions
 constexpr int kMaxD = 2048;                       // largest d_model
 constexpr int kHCap = 72 * 1024;                  // LDS bytes for staged hidden rows
 static_assert(kMaxUnits + 1 <= kThreads && kMaxRows <= kThreads, "one plan word per thread");
+static_assert(kMaxEnt <= 128, "union_small holds two entries per lane of one wave");
 constexpr int kDeviceScope = 16;                  // load cache policy: sc1 (device scope)
 constexpr uint32_t kPending = 0xFFFFFFFFu;        // hidden-row word not yet written in this launch
 
@@ -181,6 +197,8 @@ struct DGrid {
     int n_gu_wg;     // gate/up workgroups (block indices [0, n_gu_wg))
     int reset_per;   // pending words each down workgroup writes into the other half
     int64_t half;    // floats per workspace half
+    int64_t lg_off;  // offset of the logits in a copy (after the hidden rows)
+    int64_t copy;    // floats per copy of a half
     int d, f;
     int64_t tile_bytes, down_off;
 };
@@ -193,6 +211,123 @@ __device__ inline const uint8_t* slot_base(const FfnArgs& a, int e, const int* p
 
 // Launch parity: which workspace half this launch writes.
 __device__ inline int launch_parity(uint32_t count, int n_down) { return (int)((count / (uint32_t)n_down) & 1u); }
+
+// ---- routing inside the launch --------------------------------------------------
+
+// Experts a launch that routes takes: kRouteKpl logits per lane of a wave.
+constexpr int kRouteKpl = 4;
+
+// LDS of one workgroup's copy of the step's routing.
+struct PlanLds {
+    float* lg;    // [T, E] logits
+    int* ids;     // [T * k] selected experts by entry t * k + j
+    float* w;     // [T * k] routing weights by entry
+    int* exp;     // units: expert ids ascending
+    int* off;     // units: first plan position (and the end)
+    int* ent;     // plan position -> entry
+    int* na;      // [1] distinct experts
+};
+
+static_assert(kDecodeMaxT * kRouteKpl * 64 <= 2 * kThreads, "a step's logits are two words per thread");
+
+// The caller's logits (kRouteLogits), two words per thread, loaded with the
+// workgroup's first round of loads and stored to LDS after it.
+struct LgIn {
+    uint32_t v0, v1;
+    __device__ void load(const FfnArgs& a) {
+        const bool on = a.route == kRouteLogits;
+        const float* src = on ? a.logits_in : (const float*)a.pt;  // a valid address either way
+        const int n = on ? a.T * a.E : 1;
+        v0 = __float_as_uint(src[min((int)threadIdx.x, n - 1)]);
+        v1 = __float_as_uint(src[min((int)threadIdx.x + kThreads, n - 1)]);
+    }
+    __device__ void store(const FfnArgs& a, float* lg) const {
+        if (a.route != kRouteLogits) return;
+        const int n = a.T * a.E, i = threadIdx.x;
+        if (i < n) lg[i] = __uint_as_float(opaque(v0));
+        if (i + kThreads < n) lg[i + kThreads] = __uint_as_float(opaque(v1));
+    }
+};
+
+// Router rows of gate/up workgroup h of the H that take them, in a launch that
+// routes from x: experts h + j H (j = wave, wave + 8, ...), every token, with
+// the route kernel's row dot, stored with device scope into the logits of the
+// workspace half of this launch (from `count`).  Spread one row per workgroup
+// over the chip, the 2 MiB of router weights of a 256-expert layer stream at
+// once.  A gate/up workgroup is never late (see gate_up_role), so it writes
+// the half the others read.
+__device__ void router_rows(const FfnArgs& a, const DGrid& g, uint32_t count, int h, int H) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int e = h + wave * H; e < a.E; e += kWaves * H) {
+        const float* row = a.w_router + (int64_t)e * g.d;
+        for (int t = 0; t < a.T; t++) {
+            const float v = row_dot(row, a.x, a.x_bf16, t, g.d, lane);
+            float* dst = a.hbuf + (int64_t)launch_parity(count, g.n_down) * g.half + g.lg_off + (int64_t)t * a.E + e;
+            if (lane < kDecodeCopies)
+                __hip_atomic_store(dst + lane * g.copy, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// The step's routing, computed by this workgroup from the logits into LDS: the
+// top-k of token t on wave t, then the union (the same code and so the same
+// bits as the route kernels).  The logits are the caller's (kRouteLogits,
+// already in P.lg from LgIn) or the router rows' device-scope stores into the
+// workspace half `par` (copy `reader` mod kDecodeCopies), read until no
+// pending word is left.  A wait past the bound sets kErrSync and returns false
+// (the routing then comes from whatever was read; its ids are still in
+// range).  `publish`: also write ids, weights and plan to the caller's arrays.
+// Every thread of the workgroup calls it.
+__device__ bool plan_from_logits(const FfnArgs& a, const DGrid& g, int par, int reader, const PlanLds& P, bool publish) {
+    const int n = a.T * a.E;
+    bool ok = true;
+    if (a.route == kRouteRouter) {
+        const uint32_t* src = (const uint32_t*)(a.hbuf + (int64_t)par * g.half + (reader % kDecodeCopies) * g.copy +
+                                                g.lg_off);
+        const uint64_t t0 = wall_clock64();
+        for (;;) {
+            int pend = 0;
+            for (int i = threadIdx.x; i < n; i += 2 * kThreads) {
+                const int i2 = min(i + kThreads, n - 1);
+                const uint32_t v0 = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint32_t v1 = __hip_atomic_load(src + i2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                pend |= (v0 == kPending) | (v1 == kPending);
+                P.lg[i] = __uint_as_float(v0);
+                P.lg[i2] = __uint_as_float(v1);
+            }
+            if (!__syncthreads_or(pend) && a.wait_ticks >= 0) break;
+            const int expired = threadIdx.x == 0 && (a.wait_ticks < 0 || (int64_t)(wall_clock64() - t0) > a.wait_ticks);
+            if (__syncthreads_or(expired)) {
+                if (threadIdx.x == 0) atomicOr(a.err, kErrSync);
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    const int t = threadIdx.x >> 6;
+    if (t < a.T) {
+        topk_wave<kRouteKpl>(P.lg + t * a.E, a.E, a.k, a.norm, P.ids + t * a.k, P.w + t * a.k);
+    }
+    __syncthreads();
+    const int N = a.T * a.k;
+    union_small(P.ids, N, P.na, P.exp, P.off, P.ent);
+    __syncthreads();
+    if (publish) {
+        const int na = *P.na;
+        for (int i = threadIdx.x; i < N; i += kThreads) {
+            a.ids_out[i] = P.ids[i];
+            a.w_out[i] = P.w[i];
+            a.o_entries[i] = P.ent[i];
+        }
+        for (int i = threadIdx.x; i <= na; i += kThreads) {
+            if (i < na) a.o_experts[i] = P.exp[i];
+            a.o_offsets[i] = P.off[i];
+        }
+        if (threadIdx.x == 0) *a.o_n_active = na;
+    }
+    return ok;
+}
 
 // Global -> LDS copies issue every load of the thread before the first LDS
 // store, so they cost one memory round trip, not one per element.  Loads are
@@ -256,19 +391,28 @@ struct XRow {
 
 // ---- gate/up ------------------------------------------------------------------------
 
+// Arrays read as float4 (or written by 16-byte direct-to-LDS loads) are 16-byte
+// aligned: a misaligned 128-bit LDS access is split and costs several times more.
 template <int TG, int RG>
 struct GuLds {
     int pts[kMaxE];
     int exp[kMaxUnits + 3];
     int off[kMaxUnits + 3];
     int ent[kMaxEnt];
-    float red[2][kWaves][RG * TG][16];
-    float x[TG][kMaxD];
+    alignas(16) float red[2][kWaves][RG * TG][16];
+    alignas(16) float x[TG][kMaxD];  // read as float4
+    // routing inside the launch
+    alignas(16) float lg[kDecodeMaxT * kMaxE];
+    int ids[kMaxEnt];
+    float wr[kMaxEnt];
+    int na;
 };
 
-// A gate/up workgroup works through items (unit u, RG groups of 16 hidden
-// units) w, w + G, w + 2G, ... of the step's units (G gate/up workgroups, as
-// many as the device holds beside the down workgroups).
+// A gate/up workgroup works through items w, w + G, w + 2G, ... (G gate/up
+// workgroups, as many as the device holds beside the others).  An item is RG
+// groups of 16 hidden units of one unit: the shared expert's items come first
+// (they need no routing, so a launch that routes starts them at once), then
+// those of the routed units in plan order.
 template <int QT, int PREC, int TG, int RG, int PPW>
 __device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int wg, unsigned char* lds_raw) {
     GuLds<TG, RG>& L = *(GuLds<TG, RG>*)lds_raw;
@@ -278,8 +422,16 @@ __device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int wg, unsigned 
     const int n_ent = a.T * a.k;
 
     // Level 1, all independent loads: the launch count, the plan (units, entry
-    // ranges, entries), the page-table row and, for one token, its activations.
+    // ranges, entries) or the caller's logits, the page-table row and, for one
+    // token, its activations.
     const uint32_t count = __hip_atomic_load(a.sync + kSyncCount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int S = has_shared ? g.n_rg / RG : 0;  // items of the shared expert
+    if (a.route == kRouteRouter) {
+        // router rows go to the workgroups whose first item is routed (all of
+        // them if there are no such workgroups)
+        const int h0 = g.n_gu_wg > S ? S : 0;
+        if (wg >= h0) router_rows(a, g, count, wg - h0, g.n_gu_wg - h0);
+    }
     const int na_raw = *a.n_active;
     PtRow ptr;
     ptr.load(a);
@@ -289,27 +441,44 @@ __device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int wg, unsigned 
     const uint32_t en1 = (uint32_t)a.entries[min(i1, n_ent - 1)];
     XRow<PREC> x1;
     if constexpr (TG == 1) x1.load(a, g.d, 0);
+    LgIn lg1;
+    lg1.load(a);
     ptr.store(a, L.pts);
     if (i1 < kMaxUnits) L.exp[i1] = (int)opaque(ex1);
     if (i1 < kMaxUnits + 1) L.off[i1] = min(max((int)opaque(of1), 0), n_ent);
     if (i1 < n_ent) L.ent[i1] = min(max((int)opaque(en1), 0), n_ent - 1);
     if constexpr (TG == 1) x1.store(a, g.d, L.x[0]);
+    lg1.store(a, L.lg);
     lds_barrier();
-    const int par = launch_parity(opaque(count), g.n_down);
-    const int na = min(max((int)opaque((uint32_t)na_raw), 0), g.units_max - (has_shared ? 1 : 0));
-    const int per_unit = g.n_rg / RG;  // items per unit
-    const int n_items = (na + (has_shared ? 1 : 0)) * per_unit;
-    const int n_pairs = RG * g.gu_tpr;  // (gate, up) tile pairs per item
+    const int par = __builtin_amdgcn_readfirstlane(launch_parity(opaque(count), g.n_down));
+    // A launch that routes counts its gate/up workgroups in: the down workgroups
+    // finish (and so move the launch count) only once all have read it, so no
+    // workgroup, not even one left without items, reads the next launch's half.
+    if (a.route == kRouteRouter && threadIdx.x == 0)
+        __hip_atomic_fetch_add(a.sync + kSyncArrive + par, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int na_max = g.units_max - (has_shared ? 1 : 0);
+    int na = a.route == kRoutePlan ? min(max((int)opaque((uint32_t)na_raw), 0), na_max) : -1;
+    const int per_unit = g.n_rg / RG;             // items per unit
+    const int n_pairs = RG * g.gu_tpr;            // (gate, up) tile pairs per item
 
-    for (int item = wg; item < n_items; item += g.n_gu_wg) {
-        const int u = item / per_unit, rg0 = (item - u * per_unit) * RG;
+    for (int item = wg;; item += g.n_gu_wg) {
+        const bool routed = item >= S;
+        if (routed) {
+            if (na < 0) {
+                const PlanLds P{L.lg, L.ids, L.wr, L.exp, L.off, L.ent, &L.na};
+                plan_from_logits(a, g, par, wg, P, false);
+                na = min(L.na, na_max);
+            }
+            if (item >= S + na * per_unit) break;
+        }
+        const int ui = routed ? item - S : item;  // item within the routed items, or the shared ones
+        const int u = ui / per_unit, rg0 = (ui - u * per_unit) * RG;
         // The slot, then every weight load of the item.  Pair pi is column group
         // pi % gu_tpr of row group rg0 + pi / gu_tpr (gate tile and up tile);
         // lane (n, jb) holds block 4 (pi % gu_tpr) + jb of hidden unit n of that
         // group.  Loads are unconditional: a pair past the item reads its first
         // pair again (its sums are skipped), a missing expert reads pool slot 0
         // (its rows become NaN).
-        const bool routed = u < na;
         const uint8_t* base = routed ? slot_base(a, L.exp[u], L.pts) : a.shared;
         if (!base && threadIdx.x == 0) atomicOr(a.err, kErrMiss);
         const uint8_t* src = base ? base : a.pool;
@@ -384,9 +553,12 @@ __device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int wg, unsigned 
                 float hv = silu(gs) * us;
                 if (PREC == MOE_PREC_BF16) hv = round_bf16(hv);
                 const int row = routed ? b0 + gi : a.T * a.k + gi;
-                // device scope: written through to where every XCD reads it
-                __hip_atomic_store(a.hbuf + (int64_t)par * g.half + (int64_t)row * g.f + 16 * (rg0 + r) + hr,
-                                   base ? hv : __uint_as_float(0x7FC00000u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // device scope: written through to where every XCD reads it; every copy
+                float* dst = a.hbuf + (int64_t)par * g.half + (int64_t)row * g.f + 16 * (rg0 + r) + hr;
+                const float hw = base ? hv : __uint_as_float(0x7FC00000u);
+#pragma unroll
+                for (int c = 0; c < kDecodeCopies; c++)
+                    __hip_atomic_store(dst + c * g.copy, hw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         lds_barrier();  // L.red and L.x are reused by the next item
@@ -404,10 +576,16 @@ struct DownLds {
     float w[kMaxRows];                // hidden row -> weight
     int flag[4];
     int64_t uoff[kMaxUnits + 3];      // unit -> payload offset in the pool (-1 absent, -2 shared)
-    float red[kWaves][kDecodeMaxT][16];
-    float zero[kQK];                  // a zero block of activations (rows a bucket does not have)
-    union {                           // the page-table row is read only before staging starts
-        int pts[kMaxE];
+    alignas(16) float red[kWaves][kDecodeMaxT][16];
+    alignas(16) float zero[kQK];      // a zero block of activations (rows a bucket does not have)
+    int ids[kMaxEnt];                 // routing inside the launch: selected experts by entry
+    int na;
+    union alignas(16) {               // the page-table row and the logits are read before staging
+                                      // starts; hs is read as float4 and written 16 bytes per lane
+        struct {
+            int pts[kMaxE];
+            float lg[kDecodeMaxT * kMaxE];
+        } pre;
         float hs[kHCap / 4];
     };
 };
@@ -431,7 +609,10 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
     const uint32_t of1 = (uint32_t)a.offsets[min(i1, a.E)];
     const uint32_t en1 = (uint32_t)a.entries[min(i1, n_ent - 1)];
     const uint32_t w1 = __float_as_uint(a.topk_w[min(i1, n_ent - 1)]);
-    ptr.store(a, L.pts);
+    LgIn lg1;
+    lg1.load(a);
+    ptr.store(a, L.pre.pts);
+    lg1.store(a, L.pre.lg);
     if (i1 < kMaxUnits) L.exp[i1] = (int)opaque(ex1);
     if (i1 < kMaxUnits + 1) L.off[i1] = min(max((int)opaque(of1), 0), n_ent);
     if (i1 < n_ent) {
@@ -441,8 +622,18 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
     if (threadIdx.x == 0) L.flag[0] = 1;
     if (threadIdx.x < kQK) L.zero[threadIdx.x] = 0.f;
     lds_barrier();
-    const int par = launch_parity(opaque(count), g.n_down);
-    const int na = min(max((int)opaque((uint32_t)na_raw), 0), g.units_max - (has_shared ? 1 : 0));
+    const int par = __builtin_amdgcn_readfirstlane(launch_parity(opaque(count), g.n_down));
+    // the arrivals of the next launch start from zero
+    if (R == 0 && threadIdx.x == 0)
+        __hip_atomic_store(a.sync + kSyncArrive + (par ^ 1), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int na_max = g.units_max - (has_shared ? 1 : 0);
+    int na = min(max((int)opaque((uint32_t)na_raw), 0), na_max);
+    if (a.route != kRoutePlan) {
+        // the routing of the step, computed here (workgroup 0 also hands it to the caller)
+        const PlanLds P{L.pre.lg, L.ids, L.wbe, L.exp, L.off, L.ent, &L.na};
+        if (!plan_from_logits(a, g, par, g.n_gu_wg + R, P, R == 0) && threadIdx.x == 0) L.flag[0] = 0;
+        na = min(L.na, na_max);
+    }
     // This workgroup's share of the other half back to pending for the next
     // launch (no one uses that half during this one).
     {
@@ -463,7 +654,7 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
         if (u >= na) off = -2;  // shared expert
         else {
             const int ex = L.exp[u];
-            const int slot = (ex >= 0 && ex < a.E) ? L.pts[ex] : -1;
+            const int slot = (ex >= 0 && ex < a.E) ? L.pre.pts[ex] : -1;
             if (slot >= 0 && slot < a.n_slots) off = (int64_t)slot * a.payload_bytes;
         }
         L.uoff[u] = off;
@@ -521,7 +712,7 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
         scol[i] = __builtin_amdgcn_readfirstlane(min(p, max(P - 1, 0)) - u * g.dn_tpr);
     }
 
-    const float* hhalf = a.hbuf + (int64_t)par * g.half;
+    const float* hhalf = a.hbuf + (int64_t)par * g.half + (R % kDecodeCopies) * g.copy;
     const uint64_t t0 = wall_clock64();
     float acc[TG];
 #pragma unroll
@@ -552,8 +743,8 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
                 const uint4 b = *(const uint4*)(L.hs + 4 * i);
                 pend |= (b.x == kPending) | (b.y == kPending) | (b.z == kPending) | (b.w == kPending);
             }
-            if (!__syncthreads_or(pend)) break;
-            const int expired = threadIdx.x == 0 && (int64_t)(wall_clock64() - t0) > a.wait_ticks;
+            if (!__syncthreads_or(pend) && a.wait_ticks >= 0) break;
+            const int expired = threadIdx.x == 0 && (a.wait_ticks < 0 || (int64_t)(wall_clock64() - t0) > a.wait_ticks);
             if (__syncthreads_or(expired)) {
                 if (threadIdx.x == 0) {
                     atomicOr(a.err, kErrSync);
@@ -636,9 +827,29 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
         for (int w = 0; w < kWaves; w++) y += L.red[w][t][r];
         a.y[(int64_t)t * g.d + 16 * R + r] = L.flag[0] ? y : __uint_as_float(0x7FC00000u);
     }
-    // This launch is done with its half: count it (no return needed).
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(a.sync + kSyncCount, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // This launch is done with its half: count it (no return needed), once every
+    // gate/up workgroup of a launch that routes has arrived.
+    if (threadIdx.x == 0) {
+        if (a.route == kRouteRouter) {
+            const uint64_t t1 = wall_clock64();
+            while (a.wait_ticks < 0 ||
+                   __hip_atomic_load(a.sync + kSyncArrive + par, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                       (uint32_t)g.n_gu_wg) {
+                if (a.wait_ticks < 0 || (int64_t)(wall_clock64() - t1) > a.wait_ticks) {
+                    atomicOr(a.err, kErrSync);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __hip_atomic_fetch_add(a.sync + kSyncCount, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
+
+using GuLdsMax = GuLds<kDecodeMaxT, 2>;
+static_assert(offsetof(DownLds, hs) % 16 == 0 && offsetof(DownLds, zero) % 16 == 0 &&
+                  offsetof(GuLdsMax, x) % 16 == 0 && offsetof(GuLdsMax, lg) % 16 == 0,
+              "LDS arrays read as float4 must be 16-byte aligned");
 
 constexpr int kLdsBytes = sizeof(DownLds) > sizeof(GuLds<kDecodeMaxT, 2>) ? sizeof(DownLds) : sizeof(GuLds<kDecodeMaxT, 2>);
 
@@ -679,6 +890,9 @@ hipError_t launch_k(DGrid g, const FfnArgs& a, hipStream_t s) {
     // resident: no workgroup waits for a slot), at most one per item.
     const int items = g.units_max * (g.n_rg / rows_per_item<QT, TG>());
     const int cap = resident_capacity((const void*)kern);
+    // A launch that routes needs every workgroup resident: gate/up workgroups
+    // wait for router rows that other gate/up workgroups compute.
+    if (a.route != kRoutePlan && cap <= g.n_down) return hipErrorInvalidConfiguration;
     g.n_gu_wg = cap > g.n_down ? std::min(items, cap - g.n_down) : items;
     hipLaunchKernelGGL(kern, dim3(g.n_gu_wg + g.n_down), dim3(kThreads), 0, s, a, g);
     return hipGetLastError();
@@ -724,7 +938,9 @@ hipError_t launch_ffn_decode(const Geom& geo, const FfnArgs& a, int prec, hipStr
     g.tile_bytes = geo.tile_bytes;
     g.down_off = 2 * geo.gu_tiles * geo.tile_bytes;
     g.nb_rows = kHCap / (4 * geo.f);
-    g.half = decode_h_floats(a.k, geo.f) / 2;
+    g.half = decode_half_floats(a.k, geo.f, a.E);
+    g.copy = decode_copy_floats(a.k, geo.f, a.E);
+    g.lg_off = decode_h_rows_floats(a.k, geo.f);
     g.reset_per = (int)((g.half + g.n_down - 1) / g.n_down);
     if (g.nb_rows < kDecodeMaxT) return hipErrorInvalidValue;
     if (geo.qtype == MOE_Q8_0)

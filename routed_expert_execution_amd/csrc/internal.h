@@ -103,21 +103,48 @@ struct FfnArgs {
     const void* x;
     int x_bf16;
     int T;
+    // routing inside the decode launch (route != kRoutePlan): the plan above is
+    // then an output, computed from logits_in [T, E] (kRouteLogits) or from
+    // x . w_router^T (kRouteRouter, w_router [E, d] fp32)
+    int route, norm;
+    const float* logits_in;
+    const float* w_router;
+    int32_t* ids_out;       // [T, k]
+    float* w_out;           // [T, k]
+    int32_t *o_n_active, *o_experts, *o_offsets, *o_entries;
     // outputs and workspace
-    float* hbuf;            // two halves of [T*k + T, d_ff] hidden rows (plan positions, then the
-                            // shared rows), every word 0xFFFFFFFF at creation
-    uint32_t* sync;         // [kSyncInts], zero at creation: [kSyncCount] finished down workgroups
-    int64_t wait_ticks;     // bound of a down workgroup's wait (100 MHz wall-clock ticks)
+    float* hbuf;            // two halves, each kDecodeCopies copies of [T*k + T, d_ff] hidden rows
+                            // (plan positions, then the shared rows) and [T, E] logits; every
+                            // word 0xFFFFFFFF at creation
+    uint32_t* sync;         // [kSyncInts], zero at creation: [kSyncCount] finished down workgroups,
+                            // [kSyncArrive + p] gate/up workgroups arrived in a launch of parity p
+    int64_t wait_ticks;     // bound of a workgroup's wait (100 MHz wall-clock ticks); negative:
+                            // every wait gives up at its first check (tests of the time-out path)
     float* y;               // [T, d]
     int* err;
 };
 
+enum { kRoutePlan = 0, kRouteLogits = 1, kRouteRouter = 2 };
+
 // Largest step the decode kernel takes.
 constexpr int kDecodeMaxT = 4;
-constexpr int kSyncInts = 32, kSyncCount = 0;  // one 128-byte line
+constexpr int kSyncInts = 32, kSyncCount = 0, kSyncArrive = 16;  // one 128-byte line
 
-// Floats of hidden-row workspace (both halves) the decode kernel needs for top_k and d_ff.
-__host__ __device__ inline int64_t decode_h_floats(int k, int f) { return 2 * (int64_t)kDecodeMaxT * (k + 1) * f; }
+// A workspace half holds kDecodeCopies copies of the same words, each starting
+// on its own 4 KiB: every value is stored into all of them and each reader reads
+// one, so that hundreds of workgroups reading the same few KiB spread over
+// several memory channels instead of queueing on one.
+constexpr int kDecodeCopies = 8;
+// Floats of one copy: hidden rows for top_k and d_ff, then the logits of E experts.
+__host__ __device__ inline int64_t decode_h_rows_floats(int k, int f) { return (int64_t)kDecodeMaxT * (k + 1) * f; }
+__host__ __device__ inline int64_t decode_copy_floats(int k, int f, int E) {
+    return (decode_h_rows_floats(k, f) + (int64_t)kDecodeMaxT * E + 1023) / 1024 * 1024;
+}
+__host__ __device__ inline int64_t decode_half_floats(int k, int f, int E) {
+    return kDecodeCopies * decode_copy_floats(k, f, E);
+}
+// Floats of the whole decode workspace (both halves).
+__host__ __device__ inline int64_t decode_h_floats(int k, int f, int E) { return 2 * decode_half_floats(k, f, E); }
 
 hipError_t launch_ffn_decode(const Geom& g, const FfnArgs& a, int prec, hipStream_t s);
 

@@ -262,7 +262,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         const int64_t T = cfg->max_tokens;
         if (hipMalloc(&c->pt, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->err_word, sizeof(int)) != hipSuccess) return cleanup(MOE_ENOMEM);
-        if (hipMalloc(&c->hbuf, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff)) != hipSuccess)
+        if (hipMalloc(&c->hbuf, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff, cfg->n_experts)) != hipSuccess)
             return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->sync, sizeof(uint32_t) * moe::kSyncInts) != hipSuccess) return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->logits_ws, sizeof(float) * (size_t)T * cfg->n_experts) != hipSuccess)
@@ -279,7 +279,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         if (hipMemset(c->pt, 0xFF, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_EHIP);
         if (hipMemset(c->err_word, 0, sizeof(int)) != hipSuccess) return cleanup(MOE_EHIP);
         if (hipMemset(c->sync, 0, sizeof(uint32_t) * moe::kSyncInts) != hipSuccess) return cleanup(MOE_EHIP);
-        if (hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff)) != hipSuccess)
+        if (hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff, cfg->n_experts)) != hipSuccess)
             return cleanup(MOE_EHIP);
         if (hipEventCreateWithFlags(&c->release_ev, hipEventDisableTiming) != hipSuccess) return cleanup(MOE_EHIP);
         if (hipDeviceSynchronize() != hipSuccess) return cleanup(MOE_EHIP);
@@ -468,21 +468,10 @@ moe_status moe_slot_bind(moe_ctx* c, int32_t layer, int32_t expert, int32_t slot
     return MOE_OK;
 }
 
-moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dtype, int64_t T,
-                          const moe_plan* plan, const float* topk_w, const void* shared_payload,
-                          int32_t prec, float* y, moe_stream stream) {
-    if (moe_status st = need_device(c)) return st;
+// Arguments of the expert kernels common to every call.
+static moe::FfnArgs ffn_args(moe_ctx* c, int32_t layer, const void* x, int32_t x_dtype, int64_t T,
+                             const moe_plan* plan, const float* topk_w, const void* shared_payload, float* y) {
     const moe_config& cf = c->cfg;
-    if (layer < 0 || layer >= cf.n_layers) return fail(c, MOE_EINVAL, "moe_expert_ffn: bad layer");
-    if (T < 0 || T > cf.max_tokens) return fail(c, MOE_EINVAL, "moe_expert_ffn: T outside [0, max_tokens]");
-    if (prec != MOE_PREC_F32 && prec != MOE_PREC_BF16) return fail(c, MOE_EINVAL, "moe_expert_ffn: bad prec");
-    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(c, MOE_EINVAL, "moe_expert_ffn: bad x_dtype");
-    if (T > 0 && (!x || !plan || !plan->n_active || !plan->experts || !plan->offsets || !plan->entries || !topk_w || !y))
-        return fail(c, MOE_EINVAL, "moe_expert_ffn: null argument");
-    DeviceGuard dg(cf.device);
-    hipStream_t s = (hipStream_t)stream;
-    if (moe_status st = wait_pending_fills(c, s)) return st;
-    if (T == 0) return MOE_OK;
     moe::FfnArgs a{};
     a.pool = (const uint8_t*)cf.slot_pool;
     a.payload_bytes = c->g.payload;
@@ -500,14 +489,36 @@ moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     a.x = x;
     a.x_bf16 = x_dtype == MOE_BF16;
     a.T = (int)T;
+    a.route = moe::kRoutePlan;
+    a.norm = cf.norm_topk;
     a.hbuf = c->hbuf;
     a.sync = c->sync;
-    // bound of the decode kernel's wait: 200 ms of the 100 MHz clock; tests of the
-    // time-out path shorten it through MOE_SYNC_WAIT_TICKS
+    // bound of the decode kernel's waits: 200 ms of the 100 MHz clock; tests of the
+    // time-out path set MOE_SYNC_WAIT_TICKS (a negative value: every wait gives up
+    // at its first check, whatever has arrived)
     a.wait_ticks = 20000000;
-    if (const char* e = getenv("MOE_SYNC_WAIT_TICKS")) a.wait_ticks = std::max<int64_t>(0, atoll(e));
+    if (const char* e = getenv("MOE_SYNC_WAIT_TICKS")) a.wait_ticks = std::max<int64_t>(-1, atoll(e));
     a.y = y;
     a.err = c->err_word;
+    return a;
+}
+
+moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dtype, int64_t T,
+                          const moe_plan* plan, const float* topk_w, const void* shared_payload,
+                          int32_t prec, float* y, moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers) return fail(c, MOE_EINVAL, "moe_expert_ffn: bad layer");
+    if (T < 0 || T > cf.max_tokens) return fail(c, MOE_EINVAL, "moe_expert_ffn: T outside [0, max_tokens]");
+    if (prec != MOE_PREC_F32 && prec != MOE_PREC_BF16) return fail(c, MOE_EINVAL, "moe_expert_ffn: bad prec");
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(c, MOE_EINVAL, "moe_expert_ffn: bad x_dtype");
+    if (T > 0 && (!x || !plan || !plan->n_active || !plan->experts || !plan->offsets || !plan->entries || !topk_w || !y))
+        return fail(c, MOE_EINVAL, "moe_expert_ffn: null argument");
+    DeviceGuard dg(cf.device);
+    hipStream_t s = (hipStream_t)stream;
+    if (moe_status st = wait_pending_fills(c, s)) return st;
+    if (T == 0) return MOE_OK;
+    moe::FfnArgs a = ffn_args(c, layer, x, x_dtype, T, plan, topk_w, shared_payload, y);
     if (T <= moe::kDecodeMaxT) {
         HIP_TRY(c, moe::launch_ffn_decode(c->g, a, prec, s));
         return MOE_OK;
@@ -545,6 +556,38 @@ moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     return MOE_OK;
 }
 
+moe_status moe_route_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dtype, const float* w_router,
+                         const float* logits_in, int64_t T, int32_t* topk_ids, float* topk_w, const moe_plan* plan,
+                         const void* shared_payload, int32_t prec, float* y, moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers) return fail(c, MOE_EINVAL, "moe_route_ffn: bad layer");
+    if (T < 1 || T > moe::kDecodeMaxT || T > cf.max_tokens)
+        return fail(c, MOE_EINVAL, "moe_route_ffn: T=%lld outside [1, min(4, max_tokens)]", (long long)T);
+    if (cf.n_experts > 256) return fail(c, MOE_EINVAL, "moe_route_ffn: more than 256 experts (route separately)");
+    if (prec != MOE_PREC_F32 && prec != MOE_PREC_BF16) return fail(c, MOE_EINVAL, "moe_route_ffn: bad prec");
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(c, MOE_EINVAL, "moe_route_ffn: bad x_dtype");
+    if (!x || !topk_ids || !topk_w || !y || !plan || !plan->n_active || !plan->experts || !plan->offsets ||
+        !plan->entries)
+        return fail(c, MOE_EINVAL, "moe_route_ffn: null argument");
+    if (!logits_in && !w_router) return fail(c, MOE_EINVAL, "moe_route_ffn: need logits_in or w_router");
+    DeviceGuard dg(cf.device);
+    hipStream_t s = (hipStream_t)stream;
+    if (moe_status st = wait_pending_fills(c, s)) return st;
+    moe::FfnArgs a = ffn_args(c, layer, x, x_dtype, T, plan, topk_w, shared_payload, y);
+    a.route = logits_in ? moe::kRouteLogits : moe::kRouteRouter;
+    a.logits_in = logits_in;
+    a.w_router = w_router;
+    a.ids_out = topk_ids;
+    a.w_out = topk_w;
+    a.o_n_active = plan->n_active;
+    a.o_experts = plan->experts;
+    a.o_offsets = plan->offsets;
+    a.o_entries = plan->entries;
+    HIP_TRY(c, moe::launch_ffn_decode(c->g, a, prec, s));
+    return MOE_OK;
+}
+
 moe_status moe_dequant(moe_ctx* c, const void* payload, int32_t prec, float* out, moe_stream stream) {
     if (moe_status st = need_device(c)) return st;
     if (!payload || !out) return fail(c, MOE_EINVAL, "moe_dequant: null argument");
@@ -573,9 +616,9 @@ moe_status moe_check(moe_ctx* c, moe_stream stream) {
         // after a timed-out wait the workspace halves may hold rows of the wrong
         // launch: start both afresh (pending) with the count at zero
         HIP_TRY(c, hipMemset(c->sync, 0, sizeof(uint32_t) * moe::kSyncInts));
-        HIP_TRY(c, hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(c->cfg.top_k, c->cfg.d_ff)));
+        HIP_TRY(c, hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(c->cfg.top_k, c->cfg.d_ff, c->cfg.n_experts)));
         HIP_TRY(c, hipDeviceSynchronize());
-        return fail(c, MOE_ETIMEOUT, "a decode workgroup timed out waiting for the hidden rows (error word 0x%x)", w);
+        return fail(c, MOE_ETIMEOUT, "a decode workgroup timed out waiting for the hidden rows or the logits (error word 0x%x)", w);
     }
     if (w & moe::kErrMiss) return fail(c, MOE_EMISS, "a kernel met an unmapped expert (error word 0x%x)", w);
     return fail(c, MOE_EINVAL, "a plan input held an expert id out of range (error word 0x%x)", w);

@@ -1,0 +1,168 @@
+// Routing steps shared by the route kernels and the decode kernel that routes
+// in its own launch, so that both give the same bits: the router row dot, the
+// top-k of one token on one wave and the union of a few tokens' assignments
+// ("Nanite for Experts", §3.1 and §1; "Paging the Experts", §3.1: top-8 of
+// 256 routed experts; "Nanite for Experts", §5.3: the expert-major union).
+#pragma once
+#include "device_util.h"
+
+namespace moe {
+
+// Lane's share of row . x[t] (float4 slices at a 1 KiB stride, in order), then
+// the fixed lane butterfly: every lane returns the same bits.
+__device__ inline float row_dot(const float* row, const void* x, int x_bf16, int t, int d, int lane) {
+    constexpr int U = 8;  // slices in flight per lane (d_model 2048 is 8 slices)
+    float acc = 0.f;
+    for (int c0 = lane * 4; c0 < d; c0 += 256 * U) {
+        float4 wv[U], xv[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int c = c0 + 256 * u;
+            if (c < d) {
+                wv[u] = *(const float4*)(row + c);
+                if (x_bf16) {
+                    const uint2 b = *(const uint2*)((const uint16_t*)x + (int64_t)t * d + c);
+                    xv[u] = make_float4(bf16_bits_to_f32(b.x & 0xFFFF), bf16_bits_to_f32(b.x >> 16),
+                                        bf16_bits_to_f32(b.y & 0xFFFF), bf16_bits_to_f32(b.y >> 16));
+                } else {
+                    xv[u] = *(const float4*)((const float*)x + (int64_t)t * d + c);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            if (c0 + 256 * u < d) {
+                acc = fmaf(wv[u].x, xv[u].x, acc);
+                acc = fmaf(wv[u].y, xv[u].y, acc);
+                acc = fmaf(wv[u].z, xv[u].z, acc);
+                acc = fmaf(wv[u].w, xv[u].w, acc);
+            }
+        }
+    }
+    return seg_sum<64>(acc);
+}
+
+__device__ inline uint32_t order_bits(float v) {
+    uint32_t b = __float_as_uint(v);
+    if (b == 0x80000000u) b = 0;  // -0 ranks with +0
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ inline float unorder_bits(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// One wave: top-k of one token's E logits (KPL = ceil(E / 64) keys per lane).
+template <int KPL>
+__device__ inline void topk_wave(const float* l, int E, int k, int norm, int32_t* ids, float* w) {
+    const int lane = threadIdx.x & 63;
+    // Expert e = lane + 64 m is value val[m] (order-preserving bits) while bit m
+    // of avail is set.  Each round takes the wave's largest value (one 32-bit
+    // DPP max) and, among the experts holding it, the lowest index: the lowest
+    // m whose ballot is not empty, then its lowest lane.
+    uint32_t val[KPL];
+    uint32_t avail = 0;
+#pragma unroll
+    for (int m = 0; m < KPL; m++) {
+        const int e = lane + 64 * m;
+        val[m] = e < E ? order_bits(l[e]) : 0u;
+        avail |= (e < E ? 1u : 0u) << m;
+    }
+    float my_logit = 0.f;  // lane j keeps the j-th selected logit
+    int my_id = 0;
+    for (int j = 0; j < k; j++) {
+        uint32_t best = 0;
+#pragma unroll
+        for (int m = 0; m < KPL; m++) best = ((avail >> m) & 1u) ? max(best, val[m]) : best;
+        const uint32_t top = wave_max_u32(best);
+        int sel = -1;
+#pragma unroll
+        for (int m = 0; m < KPL; m++) {
+            const uint64_t b = __ballot(((avail >> m) & 1u) && val[m] == top);
+            if (sel < 0 && b) sel = 64 * m + (int)__builtin_ctzll(b);
+        }
+        if ((sel & 63) == lane) avail &= ~(1u << (sel >> 6));
+        if (lane == j) {
+            my_id = sel;
+            my_logit = unorder_bits(top);
+        }
+    }
+    const float lmax = __shfl(my_logit, 0, 64);
+    float z;
+    if (norm) {
+        float ex = lane < k ? expf(my_logit - lmax) : 0.f;
+        z = seg_sum<64>(ex);
+    } else {
+        float part = 0.f;
+#pragma unroll
+        for (int m = 0; m < KPL; m++) {
+            const int e = lane + 64 * m;
+            if (e < E) part += expf(l[e] - lmax);
+        }
+        z = seg_sum<64>(part);
+    }
+    if (lane < k) {
+        ids[lane] = my_id;
+        w[lane] = expf(my_logit - lmax) / z;
+    }
+}
+
+// The union of at most 128 assignments (a few tokens' top-k), computed by one
+// wave.  Entry i goes to place |{j : e_j < e_i or (e_j == e_i and j < i)}|,
+// its place in the stable order by expert, which is the same unique result
+// the counting sort gives; each bucket's first entry gives the bucket's
+// expert, its first place and its rank among the buckets.
+//
+// Lane l holds entries l and l + 64.  The relations come bit by bit from the
+// expert ids (10 bits, E <= 1024), most significant first, one ballot per bit:
+// for each of its entries a lane keeps the mask of entries equal so far and
+// the mask of those already found smaller.  Every thread of the workgroup
+// calls it; the outputs are complete after the caller's next barrier.
+__device__ inline void union_small(const int32_t* s_ids, int N, int32_t* n_active, int32_t* experts,
+                                   int32_t* offsets, int32_t* entries) {
+    const int l = threadIdx.x;
+    if (l >= 64) return;
+    const bool ok0 = l < N, ok1 = l + 64 < N;
+    const int e0 = ok0 ? s_ids[l] : 0, e1 = ok1 ? s_ids[l + 64] : 0;
+    const uint64_t V0 = __ballot(ok0), V1 = __ballot(ok1);
+    uint64_t q00 = V0, q01 = V1, q10 = V0, q11 = V1;  // equal so far (entry 0: words 0, 1; entry 1)
+    uint64_t s00 = 0, s01 = 0, s10 = 0, s11 = 0;      // found smaller
+#pragma unroll
+    for (int b = 9; b >= 0; b--) {
+        const uint64_t B0 = __ballot((e0 >> b) & 1), B1 = __ballot((e1 >> b) & 1);
+        if ((e0 >> b) & 1) {
+            s00 |= q00 & ~B0; s01 |= q01 & ~B1; q00 &= B0; q01 &= B1;
+        } else {
+            q00 &= ~B0; q01 &= ~B1;
+        }
+        if ((e1 >> b) & 1) {
+            s10 |= q10 & ~B0; s11 |= q11 & ~B1; q10 &= B0; q11 &= B1;
+        } else {
+            q10 &= ~B0; q11 &= ~B1;
+        }
+    }
+    // equal entries before each (entry l: only word 0 lies below it)
+    const int eqb0 = lanes_below(q00);
+    const int eqb1 = __popcll(q10) + lanes_below(q11);
+    const int less0 = __popcll(s00) + __popcll(s01), less1 = __popcll(s10) + __popcll(s11);
+    const bool first0 = ok0 && eqb0 == 0, first1 = ok1 && eqb1 == 0;
+    const uint64_t F0 = __ballot(first0), F1 = __ballot(first1);
+    if (ok0) entries[less0 + eqb0] = l;
+    if (ok1) entries[less1 + eqb1] = l + 64;
+    if (first0) {
+        const int r = __popcll(s00 & F0) + __popcll(s01 & F1);
+        experts[r] = e0;
+        offsets[r] = less0;
+    }
+    if (first1) {
+        const int r = __popcll(s10 & F0) + __popcll(s11 & F1);
+        experts[r] = e1;
+        offsets[r] = less1;
+    }
+    if (l == 0) {
+        const int nb = __popcll(F0) + __popcll(F1);
+        *n_active = nb;
+        offsets[nb] = N;
+    }
+}
+
+}  // namespace moe

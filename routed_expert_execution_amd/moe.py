@@ -70,6 +70,7 @@ def _load() -> C.CDLL:
         "moe_slot_release": (C.c_int, [P, I32, P]),
         "moe_slot_bind": (C.c_int, [P, I32, I32, I32, P]),
         "moe_expert_ffn": (C.c_int, [P, I32, P, I32, I64, planp, P, P, I32, P, P]),
+        "moe_route_ffn": (C.c_int, [P, I32, P, I32, P, P, I64, P, P, planp, P, I32, P, P]),
         "moe_dequant": (C.c_int, [P, P, I32, P, P]),
         "moe_stats": (C.c_int, [P, C.POINTER(C.c_uint64)]),
         "moe_check": (C.c_int, [P, P]),
@@ -86,7 +87,7 @@ _lib = _load()
 EXPORTS = ("moe_payload_bytes", "moe_plan_bytes", "moe_pack_expert", "moe_unpack_expert", "moe_create",
            "moe_destroy", "moe_last_error", "moe_status_string", "moe_route", "moe_plan_union", "moe_route_union",
            "moe_slot_map", "moe_slot_fill", "moe_slot_release", "moe_slot_bind", "moe_expert_ffn",
-           "moe_dequant", "moe_stats", "moe_check", "moe_page_table")
+           "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table")
 
 
 def library() -> C.CDLL:
@@ -322,6 +323,25 @@ def moe_expert_ffn(ctx: Context, layer: int, x, plan: Plan, topk_w, y, shared_pa
     _check_dev(ctx, x, topk_w, y, shared_payload)
     _call(ctx, _lib.moe_expert_ffn(ctx.handle, layer, _ptr(x), _x_dtype(x), T, C.byref(plan.c), _ptr(topk_w),
                                    _ptr(shared_payload), prec, _ptr(y), _stream(stream)))
+
+
+def moe_route_ffn(ctx: Context, layer: int, x, topk_ids, topk_w, plan: Plan, y, w_router=None, logits_in=None,
+                  shared_payload=None, prec: int = MOE_PREC_F32, stream=None) -> None:
+    """Route (from x . w_router^T, or from logits_in), union and expert FFN of at
+    most 4 tokens in one launch; topk_ids, topk_w and plan are outputs."""
+    import torch
+    T = x.shape[0]
+    _route_args(ctx, topk_ids, topk_w, x if logits_in is None else None, w_router, logits_in, None)
+    if tuple(x.shape) != (T, ctx.d_model) or tuple(y.shape) != (T, ctx.d_model) or y.dtype != torch.float32:
+        raise ValueError("x must be [T, d_model]; y float32 [T, d_model]")
+    if plan.entries.numel() < T * ctx.top_k:
+        raise ValueError("plan is too small for T")
+    if shared_payload is not None and shared_payload.numel() * shared_payload.element_size() < ctx.payload_bytes:
+        raise ValueError("shared payload too small")
+    _check_dev(ctx, x, y, shared_payload)
+    _call(ctx, _lib.moe_route_ffn(ctx.handle, layer, _ptr(x), _x_dtype(x), _ptr(w_router), _ptr(logits_in), T,
+                                  _ptr(topk_ids), _ptr(topk_w), C.byref(plan.c), _ptr(shared_payload), prec,
+                                  _ptr(y), _stream(stream)))
 
 
 def moe_dequant(ctx: Context, payload, out, prec: int = MOE_PREC_F32, stream=None) -> None:

@@ -278,14 +278,14 @@ def test_decode_alternating_inputs_see_fresh_hidden_rows(name, T):
 
 
 def test_decode_wait_timeout_fails_closed_and_recovers(monkeypatch):
-    """A wait bound of 0 ticks (set from the host) makes the down workgroups give up
-    at once: the launch still completes, rows whose wait ran out are NaN,
-    moe_check reports MOE_ETIMEOUT and resets the hand-off workspace, and the
-    next launches are exact again."""
+    """A negative wait bound (set from the host) makes every down workgroup give up
+    at its first check: the launch still completes, rows whose wait ran out are
+    NaN, moe_check reports MOE_ETIMEOUT and resets the hand-off workspace, and
+    the next launches are exact again."""
     s = Step("decode", 1, 0)
     s.place()
     ref = s.reference()
-    monkeypatch.setenv("MOE_SYNC_WAIT_TICKS", "0")
+    monkeypatch.setenv("MOE_SYNC_WAIT_TICKS", "-1")
     y = s.run()
     monkeypatch.delenv("MOE_SYNC_WAIT_TICKS")
     assert np.isnan(y).any()

@@ -1,0 +1,182 @@
+"""moe_route_ffn (routing, union and expert FFN in one launch) against
+moe_route_union followed by moe_expert_ffn: the same arguments must give
+bit-identical ids, weights, plans and outputs, and the outputs must meet the
+oracle's bar (1e-3 maximum relative error per token row) for the routing the
+GPU chose."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not H.gpu_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from routed_expert_execution_amd import moe  # noqa: E402
+
+FFN_TOL = 1e-3
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+class Layer:
+    """One layer whose routed experts for the given steps are all resident."""
+
+    def __init__(self, name, T, steps, prec=oracle.PREC_F32, use_logits=None, norm=1, **overrides):
+        wl = dict(synth.workload(name), **overrides)
+        self.wl, self.T, self.prec = wl, T, prec
+        E, k, d, f = wl["E"], wl["k"], wl["d"], wl["f"]
+        self.use_logits = (name not in ("tiny", "decode")) if use_logits is None else use_logits
+        self.xs = {s: synth.activations(wl["seed"], T, d, wl["x_dtype"], s) for s in steps}
+        self.wr = None if self.use_logits else torch.from_numpy(synth.router_weights(wl["seed"], E, d)).cuda()
+        self.lgs = {s: torch.from_numpy(synth.mtp_logits(wl["seed"], s, T, E, k, wl.get("p_shared_route", 0.5))
+                                        if name not in ("tiny", "decode") else
+                                        np.random.default_rng(s).standard_normal((T, E)).astype(np.float32)).cuda()
+                    for s in steps} if self.use_logits else None
+        self.ctx = H.make_ctx(wl, n_slots=min(E, T * k * len(steps)), max_tokens=T, norm_topk=norm)
+        self.shared = synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True) if wl["shared"] else None
+        self.sh_dev = H.device_payload(self.ctx, self.shared) if self.shared is not None else None
+        # route every step once (separate calls) to learn which experts to place
+        used = set()
+        for s in steps:
+            used |= set(self.route_plain(s)[0].reshape(-1).tolist())
+        self.used = sorted(used)
+        self.recs = {}
+        for i, e in enumerate(self.used):
+            self.recs[e] = synth.expert_record(wl["seed"], 0, e, wl["qtype"], d, f)
+            H.put_expert(self.ctx, i, self.recs[e])
+            moe.moe_slot_bind(self.ctx, 0, e, i)
+        torch.cuda.synchronize()
+
+    def _bufs(self):
+        T, k, E = self.T, self.wl["k"], self.wl["E"]
+        ids = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+        w = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+        y = torch.full((T, self.wl["d"]), float("nan"), dtype=torch.float32, device="cuda")
+        return ids, w, moe.Plan(self.ctx, T), y
+
+    def _route_kw(self, s):
+        x = H.torch_x(self.xs[s], self.wl["x_dtype"])
+        return x, (dict(logits_in=self.lgs[s]) if self.use_logits else dict(x=x, w_router=self.wr))
+
+    def route_plain(self, s):
+        ids, w, plan, _ = self._bufs()
+        x, kw = self._route_kw(s)
+        moe.moe_route_union(self.ctx, ids, w, plan, **kw)
+        torch.cuda.synchronize()
+        return ids.cpu().numpy(), w.cpu().numpy(), plan
+
+    def plain(self, s):
+        ids, w, plan, y = self._bufs()
+        x, kw = self._route_kw(s)
+        moe.moe_route_union(self.ctx, ids, w, plan, **kw)
+        moe.moe_expert_ffn(self.ctx, 0, x, plan, w, y, shared_payload=self.sh_dev, prec=self.prec)
+        return ids, w, plan, y
+
+    def fused(self, s):
+        ids, w, plan, y = self._bufs()
+        x, kw = self._route_kw(s)
+        kw.pop("x", None)
+        moe.moe_route_ffn(self.ctx, 0, x, ids, w, plan, y, shared_payload=self.sh_dev, prec=self.prec, **kw)
+        return ids, w, plan, y
+
+    def host(self, res):
+        torch.cuda.synchronize()
+        ids, w, plan, y = res
+        n, experts, offsets, entries = plan.host()
+        return dict(ids=ids.cpu().numpy(), w=w.cpu().numpy().view(np.uint32), n=n,
+                    experts=np.asarray(experts)[:n], offsets=np.asarray(offsets)[:n + 1],
+                    entries=np.asarray(entries)[: self.T * self.wl["k"]], y=y.cpu().numpy())
+
+    def reference(self, s, ids, w_bits):
+        wl = self.wl
+        records = [self.recs.get(e) for e in range(wl["E"])]
+        return oracle.moe_layer(wl["qtype"], self.prec, records, self.shared, wl["d"], wl["f"],
+                                oracle.x_to_f64(self.xs[s], wl["x_dtype"]), ids, w_bits.view(np.float32))
+
+
+def _same(a, b):
+    assert a["n"] == b["n"]
+    for key in ("ids", "w", "experts", "offsets", "entries"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.array_equal(a["y"].view(np.uint32), b["y"].view(np.uint32)), "y"
+
+
+CASES = [("tiny", 4, {}), ("tiny", 1, {}), ("decode", 1, {}), ("decode", 2, {}), ("decode", 3, {}),
+         ("decode", 4, {}), ("mtp", 4, {}), ("mtp", 3, {}), ("mtp", 1, {}),
+         ("decode", 4, dict(use_logits=True, E=64, k=32)), ("decode", 2, dict(prec=oracle.PREC_BF16)),
+         ("mtp", 4, dict(norm=0)), ("decode", 1, dict(E=100, k=7))]
+
+
+@pytest.mark.parametrize("name,T,kw", CASES)
+def test_route_ffn_matches_separate_calls(name, T, kw):
+    _say("route_ffn", name, T, kw)
+    L = Layer(name, T, [3], **kw)
+    a = L.host(L.plain(3))
+    for _ in range(2):
+        b = L.host(L.fused(3))
+        assert moe.moe_check(L.ctx) == moe.MOE_OK
+        _same(a, b)
+    ref = L.reference(3, b["ids"], b["w"])
+    err = H.max_rel_row_err(b["y"], ref)
+    _say("  max rel row err", err)
+    assert np.isfinite(b["y"]).all() and err <= FFN_TOL
+    if not L.use_logits:
+        # the router in the launch gives the same ids as the oracle's top-k of the
+        # GPU's own logits (ties to the lower index)
+        lo = torch.empty(T, L.wl["E"], dtype=torch.float32, device="cuda")
+        ids = torch.empty(T, L.wl["k"], dtype=torch.int32, device="cuda")
+        w = torch.empty(T, L.wl["k"], dtype=torch.float32, device="cuda")
+        x, rkw = L._route_kw(3)
+        moe.moe_route(L.ctx, ids, w, logits_out=lo, **rkw)
+        r_ids, _ = oracle.topk(lo.cpu().numpy(), L.wl["k"])
+        assert np.array_equal(b["ids"], r_ids)
+
+
+@pytest.mark.parametrize("name,T", [("decode", 1), ("mtp", 4), ("decode", 3)])
+def test_route_ffn_interleaved_with_separate_calls(name, T):
+    """Launches that route and launches that take a plan share the workspace halves
+    and the launch count: any sequence of them on one context stays exact."""
+    steps = [0, 1, 2]
+    L = Layer(name, T, steps)
+    want = {s: L.host(L.plain(s)) for s in steps}
+    order = [("f", 0), ("p", 1), ("f", 2), ("f", 1), ("p", 0), ("p", 2), ("f", 0), ("f", 0), ("p", 1), ("f", 2)]
+    for kind, s in order:
+        got = L.host(L.fused(s) if kind == "f" else L.plain(s))
+        _same(want[s], got)
+    assert moe.moe_check(L.ctx) == moe.MOE_OK
+
+
+def test_route_ffn_wait_timeout_fails_closed_and_recovers(monkeypatch):
+    """A negative wait bound makes every wait of the launch (logits, hidden rows,
+    arrivals) give up at its first check: its rows come out NaN, moe_check
+    reports MOE_ETIMEOUT and resets the workspace, and the next launches are
+    exact again."""
+    L = Layer("decode", 1, [0, 1])
+    want = {s: L.host(L.plain(s)) for s in (0, 1)}
+    monkeypatch.setenv("MOE_SYNC_WAIT_TICKS", "-1")
+    bad = L.host(L.fused(0))
+    monkeypatch.delenv("MOE_SYNC_WAIT_TICKS")
+    assert moe.moe_check(L.ctx) == moe.MOE_ETIMEOUT
+    assert np.isnan(bad["y"]).all()
+    for s in (1, 0, 1):
+        _same(want[s], L.host(L.fused(s)))
+    assert moe.moe_check(L.ctx) == moe.MOE_OK
+
+
+def test_route_ffn_validation():
+    L = Layer("tiny", 4, [0])
+    ids, w, plan, y = L._bufs()
+    x, _ = L._route_kw(0)
+    with pytest.raises(Exception):  # neither logits_in nor w_router
+        moe.moe_route_ffn(L.ctx, 0, x, ids, w, plan, y)
+    big = H.make_ctx(dict(synth.workload("tiny"), E=300), n_slots=1, max_tokens=4)
+    with pytest.raises(Exception):  # more than 256 experts
+        moe.moe_route_ffn(big, 0, x, ids, w, moe.Plan(big, 4), y,
+                          logits_in=torch.zeros(4, 300, dtype=torch.float32, device="cuda"))
