@@ -271,6 +271,22 @@ moe_status moe_stats(const moe_ctx* ctx, uint64_t out[5]);
  * out-of-range expert id met by moe_plan_union. */
 moe_status moe_check(moe_ctx* ctx, moe_stream stream);
 
+/* Peak references for measurement (not part of the routed path; no context).
+ * moe_probe_read: one launch of `workgroups` workgroups (0: 512) of 512
+ * threads, each reading its contiguous share of device src (bytes > 0, a
+ * multiple of 16) once with 16-byte loads, 8 in flight per thread; sink:
+ * device [1] uint32, written only on a value the caller cannot expect.  The
+ * achievable streaming-read rate, to compare the expert kernels' bytes per
+ * second with.
+ * moe_probe_mfma: grid workgroups of 4 waves, each running iters rounds of 4
+ * independent bf16 matrix-core products (shape 0: 16x16x32, 1: 32x32x16);
+ * *flops (host) receives the floating-point operations performed; sink:
+ * device [1] fp32.  Both enqueue on `stream` and return MOE_EINVAL (nothing
+ * enqueued) for bad arguments. */
+moe_status moe_probe_read(const void* src, int64_t bytes, int32_t workgroups, uint32_t* sink, moe_stream stream);
+moe_status moe_probe_mfma(int32_t iters, int32_t grid, int32_t shape, float* sink, int64_t* flops,
+                          moe_stream stream);
+
 /* Device address of the page table ([n_layers x n_experts] int32), for tests. */
 moe_status moe_page_table(const moe_ctx* ctx, int32_t** out);
 

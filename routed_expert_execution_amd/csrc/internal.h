@@ -183,4 +183,12 @@ struct PrefillArgs {
 void prefill_max_tiles(int64_t T, int k, int E, bool shared, int* big_tiles, int* small_tiles);
 hipError_t launch_ffn_prefill(const PrefillArgs& a, int prec, hipStream_t s);
 
+// Peak references (probe.hip): a streaming read of `bytes` (a multiple of 16)
+// by `wgs` workgroups, and `iters` rounds of bf16 matrix-core products (shape 0:
+// 16x16x32, 1: 32x32x16) over `grid` workgroups of 4 waves, with the flops the
+// latter performs.
+hipError_t launch_probe_read(const void* src, int64_t bytes, int wgs, uint32_t* sink, hipStream_t s);
+hipError_t launch_probe_mfma(int iters, int grid, int shape, float* sink, hipStream_t s);
+int64_t probe_mfma_flops(int iters, int grid, int shape);
+
 }  // namespace moe

@@ -624,6 +624,17 @@ moe_status moe_check(moe_ctx* c, moe_stream stream) {
     return fail(c, MOE_EINVAL, "a plan input held an expert id out of range (error word 0x%x)", w);
 }
 
+moe_status moe_probe_read(const void* src, int64_t bytes, int32_t workgroups, uint32_t* sink, moe_stream stream) {
+    if (!src || !sink || bytes <= 0 || bytes % 16 || workgroups < 0) return MOE_EINVAL;
+    return moe::launch_probe_read(src, bytes, workgroups, sink, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+moe_status moe_probe_mfma(int32_t iters, int32_t grid, int32_t shape, float* sink, int64_t* flops, moe_stream stream) {
+    if (iters < 1 || grid < 1 || (shape != 0 && shape != 1) || !sink || !flops) return MOE_EINVAL;
+    *flops = moe::probe_mfma_flops(iters, grid, shape);
+    return moe::launch_probe_mfma(iters, grid, shape, sink, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
 moe_status moe_page_table(const moe_ctx* c, int32_t** out) {
     if (!c || !out || c->host_only) return MOE_EINVAL;
     *out = c->pt;

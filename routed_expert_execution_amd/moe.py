@@ -75,6 +75,8 @@ def _load() -> C.CDLL:
         "moe_stats": (C.c_int, [P, C.POINTER(C.c_uint64)]),
         "moe_check": (C.c_int, [P, P]),
         "moe_page_table": (C.c_int, [P, C.POINTER(P)]),
+        "moe_probe_read": (C.c_int, [P, I64, I32, P, P]),
+        "moe_probe_mfma": (C.c_int, [I32, I32, I32, P, C.POINTER(I64), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -87,7 +89,8 @@ _lib = _load()
 EXPORTS = ("moe_payload_bytes", "moe_plan_bytes", "moe_pack_expert", "moe_unpack_expert", "moe_create",
            "moe_destroy", "moe_last_error", "moe_status_string", "moe_route", "moe_plan_union", "moe_route_union",
            "moe_slot_map", "moe_slot_fill", "moe_slot_release", "moe_slot_bind", "moe_expert_ffn",
-           "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table")
+           "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table", "moe_probe_read",
+           "moe_probe_mfma")
 
 
 def library() -> C.CDLL:
@@ -377,3 +380,19 @@ def moe_page_table(ctx: Context) -> np.ndarray:
     if st != 0:
         raise MoeError(MOE_EHIP, f"hipMemcpy of the page table failed ({st})")
     return out
+
+
+def moe_probe_read(src, sink, workgroups: int = 0, stream=None) -> None:
+    """One streaming-read launch over every byte of the device tensor src."""
+    n = src.numel() * src.element_size()
+    if _lib.moe_probe_read(_ptr(src), n, workgroups, _ptr(sink), _stream(stream)) != MOE_OK:
+        raise ValueError("moe_probe_read: bad arguments (bytes must be a positive multiple of 16)")
+
+
+def moe_probe_mfma(iters: int, grid: int, sink, shape: int = 0, stream=None) -> int:
+    """bf16 matrix-core loop (shape 0: 16x16x32, 1: 32x32x16); returns the
+    floating-point operations it performs."""
+    fl = C.c_int64()
+    if _lib.moe_probe_mfma(iters, grid, shape, _ptr(sink), C.byref(fl), _stream(stream)) != MOE_OK:
+        raise ValueError("moe_probe_mfma: bad arguments")
+    return int(fl.value)
