@@ -50,9 +50,13 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_decode_traffic.json")
 
 
-def _kernel_source_digest() -> str:
+CAL_BYTES = 64 << 20  # the plain device-to-device copy each run makes once, for counter calibration
+
+
+def _kernel_source_digest(workload: str = "decode") -> str:
     h = hashlib.sha256()
-    for f in ("ffn_decode.hip", "device_util.h", "internal.h", "route_device.h"):
+    main = "ffn_prefill.hip" if workload == "prefill" else "ffn_decode.hip"
+    for f in (main, "device_util.h", "internal.h", "route_device.h"):
         h.update(open(os.path.join(ROOT, "routed_expert_execution_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -65,9 +69,56 @@ def _traffic(workload: str):
     except (OSError, ValueError):
         return None
     r = t.get(workload)
-    if not r or r.get("kernel_source_sha") != _kernel_source_digest():
+    if not r or r.get("kernel_source_sha") != _kernel_source_digest(workload):
         return None
     return r["fetch_bytes_per_launch"] + r["write_bytes_per_launch"]
+
+
+def _counter_rows(d: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    out = {}  # dispatch -> (kernel name, value)
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            out[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]))
+    return [out[k] for k in sorted(out)]
+
+
+def traffic_from(fetch_dir: str, write_dir: str, workload: str, warmup: int, steps: int) -> int:
+    """HBM bytes per launch of the roofline kernel from two rocprofv3 --pmc runs of
+    this bench (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what
+    the same counter reads for the run's 64 MiB plain copy; written to
+    profiles/ffn_decode_traffic.json for the current kernel source."""
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d)
+        copies = [v for n, v in rows if "copyBuffer" in n]
+        cal = CAL_BYTES / (max(copies) * 1024.0)  # bytes per reported unit
+        if workload == "prefill":  # moe_expert_ffn = schedule + tile kernels + combine, per step
+            per = {}
+            for n, v in rows:
+                if any(x in n for x in ("schedule_kernel", "prefill_gate_up", "prefill_down", "prefill_combine")):
+                    key = n.replace("(anonymous namespace)::", "").split("(")[0]
+                    per.setdefault(key, []).append(v)
+            val = sum(float(np.mean(v)) for v in per.values())
+        else:  # the one-launch steps of the timed pass
+            vals = [v for n, v in rows if "ffn_decode_kernel" in n][warmup:warmup + steps]
+            val = float(np.mean(vals))
+        res[counter] = (val * 1024.0 * cal, cal)
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        t = {}
+    t[workload] = {"kernel_source_sha": _kernel_source_digest(workload),
+                   "fetch_bytes_per_launch": res["FETCH_SIZE"][0], "write_bytes_per_launch": res["WRITE_SIZE"][0],
+                   "calibration_bytes_per_unit": {"FETCH_SIZE": res["FETCH_SIZE"][1], "WRITE_SIZE": res["WRITE_SIZE"][1]},
+                   "calibration": f"{CAL_BYTES} B device-to-device copy in the same run"}
+    json.dump(t, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps({workload: t[workload]}))
+    return 0
 
 
 def cpu_baseline(wl: dict, budget_s: float = 10.0, max_steps: int = 200) -> dict:
@@ -204,6 +255,62 @@ def ceilings(torch, moe) -> int:
                       "hbm_streaming_read_cold": reads, "hbm_peak_spec_GBps": HBM_PEAK_GBS,
                       "pinned_h2d_hipMemcpyAsync": h2d,
                       "mfma_bf16_dense": dict(mfma, peak_spec_TFLOPs=2500.0)}), flush=True)
+    return 0
+
+
+def mfma_sweep(torch, moe, synth) -> int:
+    """Single-bucket sweep of the prefill path (bf16 mode, the layer of the
+    prefill chunk): all M tokens pick the same 8 experts, so the grouped GEMM
+    runs 8 buckets of M tokens plus the shared expert's M.  Cold (512 MiB read
+    first); the FFN launch between one event pair."""
+    wl = synth.workload("prefill")
+    E, k, d, f = wl["E"], wl["k"], wl["d"], wl["f"]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    Ms = (16, 32, 64, 128, 256, 512)
+    cfg = moe.make_config(1, E, k, d, f, moe.MOE_Q8_0, k, max(Ms), device=-1)
+    pb = moe.moe_payload_bytes(cfg)
+    pool = torch.zeros(k * pb, dtype=torch.uint8, device=dev)
+    ctx = moe.Context(1, E, k, d, f, moe.MOE_Q8_0, k, max(Ms), device=0, slot_pool=pool)
+    for e in range(k):
+        ctx.slot(e).copy_(torch.from_numpy(moe.moe_pack_expert(ctx.cfg, synth.expert_record(wl["seed"], 0, e, wl["qtype"], d, f))))
+        moe.moe_slot_bind(ctx, 0, e, e)
+    shared = torch.from_numpy(moe.moe_pack_expert(
+        ctx.cfg, synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True))).to(dev)
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    flush_sink = torch.empty((), dtype=torch.int32, device=dev)
+    rows = []
+    for M in Ms:
+        lg = torch.full((M, E), -4.0, dtype=torch.float32, device=dev)
+        lg[:, :k] = torch.arange(k, 0, -1, dtype=torch.float32, device=dev)  # experts 0..7, every token
+        x = torch.from_numpy(synth.activations(wl["seed"], M, d, "bf16", M).view(np.int16)).view(torch.bfloat16).to(dev)
+        ids = torch.empty(M, k, dtype=torch.int32, device=dev)
+        w = torch.empty(M, k, dtype=torch.float32, device=dev)
+        y = torch.empty(M, d, dtype=torch.float32, device=dev)
+        plan = moe.Plan(ctx, M)
+        moe.moe_route_union(ctx, ids, w, plan, logits_in=lg)
+        pairs = []
+        for _ in range(12):
+            flush_sink.copy_(flush.max())
+            torch.cuda._sleep(int(200e-6 * 2.4e9))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            moe.moe_expert_ffn(ctx, 0, x, plan, w, y, shared_payload=shared, prec=moe.MOE_PREC_BF16)
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = _median_us(pairs[2:])
+        flops = (k + 1) * M * 3 * 2 * d * f
+        tf = flops / (us * 1e-6) / 1e12
+        rows.append({"M": M, "us": round(us, 1), "TFLOPs": round(tf, 1), "mfma_frac_of_spec": round(tf / 2500.0, 3),
+                     "GBps": round((k + 1) * pb / (us * 1e-6) / 1e9, 1)})
+    assert moe.moe_check(ctx) == moe.MOE_OK
+    print(json.dumps({"metric": "prefill bucket sweep (bf16 matrix cores)", "n_gpus": 1, "data": "synthetic",
+                      "config": {"workload": f"{k} experts x M tokens + shared expert, d_model {d}, d_ff {f}, Q8_0, "
+                                             "bf16 mode, cold"},
+                      "peak_spec_TFLOPs": 2500.0, "rows": rows}), flush=True)
+    ctx.close()
     return 0
 
 
@@ -345,6 +452,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode", choices=["decode", "mtp", "prefill", "stack"])
+    ap.add_argument("--mfma-sweep", action="store_true",
+                    help="prefill buckets of M tokens (M = 16 .. 512) on the matrix cores: time and utilisation")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="parse two rocprofv3 --pmc runs of this bench into the traffic file (no GPU)")
     ap.add_argument("--ceilings", action="store_true",
                     help="print the peak references (streaming read, pinned H2D, matrix-core loop) instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -352,6 +463,8 @@ def main() -> int:
     ap.add_argument("--separate-calls", action="store_true",
                     help="time steps of up to 4 tokens as moe_route_union + moe_expert_ffn, not one launch")
     args = ap.parse_args()
+    if args.traffic_from:
+        return traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload, args.warmup, args.steps)
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the routed-expert path; --gpus {args.gpus} is not "
               f"available (one process, one GPU).", file=sys.stderr)
@@ -364,6 +477,8 @@ def main() -> int:
 
     if args.ceilings:
         return ceilings(torch, moe)
+    if args.mfma_sweep:
+        return mfma_sweep(torch, moe, synth)
     if args.workload == "stack":
         return run_stack(args, torch, moe, synth)
 
@@ -405,6 +520,8 @@ def main() -> int:
     y = torch.empty(T, d, dtype=torch.float32, device=dev)
     plan = moe.Plan(ctx, T)
     flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)  # 512 MiB, read before every step
+    cal = torch.empty(CAL_BYTES // 4, dtype=torch.int32, device=dev)
+    cal.copy_(flush[: CAL_BYTES // 4])  # a plain copy of known size (counter calibration)
     flush_sink = torch.empty((), dtype=torch.int32, device=dev)
     spin_cycles = int(300e-6 * 2.4e9)  # ~300 us of GPU-side spin before each timed step
     side = torch.cuda.Stream(device=dev)
