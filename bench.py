@@ -121,7 +121,7 @@ def traffic_from(fetch_dir: str, write_dir: str, workload: str, warmup: int, ste
     return 0
 
 
-def cpu_baseline(wl: dict, budget_s: float = 10.0, max_steps: int = 200) -> dict:
+def cpu_baseline(wl: dict, budget_s: float = 10.0, max_steps: int = 100_000) -> dict:
     """The oracle, as it stands, timed on a bounded sample of the same steps.
 
     Only the oracle's own work is timed (router logits, top-k, union, the routed
