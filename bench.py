@@ -314,6 +314,40 @@ def mfma_sweep(torch, moe, synth) -> int:
     return 0
 
 
+def replay_policies(args, synth, moe) -> int:
+    """Host only: the 40-layer stack's route trace (and a cyclic trace) replayed
+    against LRU (the library's slot manager), seeded random eviction, a static
+    per-layer working set and farthest-next-use.  One JSON line."""
+    from routed_expert_execution_amd import replay as R
+    wl = synth.workload("stack40")
+    L, E, k = wl["n_layers"], wl["E"], wl["k"]
+    cfg = moe.make_config(L, E, k, wl["d"], wl["f"], moe.MOE_Q8_0, wl["n_slots"], 1, device=-1)
+    pb = moe.moe_payload_bytes(cfg)
+    n_tok = args.steps if args.steps != 500 else wl["tokens"]
+    trace = R.markov_trace(wl["seed"], L, n_tok, E, k, wl["p_repeat"])
+    rows = []
+    for cap in (wl["n_slots"], 2 * wl["n_slots"]):
+        for pol, kw in (("lru", {}), ("random", dict(seed=1)), ("static", dict(width=16)),
+                        ("static", dict(width=20)), ("belady", {})):
+            t0 = time.perf_counter()
+            r = R.replay(trace, cap, pol, payload_bytes=pb, n_layers=L, n_experts=E, **kw)
+            r["bytes_staged_per_token"] = r.pop("bytes_staged") / n_tok
+            r["replay_s"] = round(time.perf_counter() - t0, 2)
+            rows.append(r)
+    cyc = []
+    for cap in (9, 10):
+        tr = R.cyclic_trace(10, 50)
+        for pol in ("lru", "belady"):
+            r = R.replay(tr, cap, pol)
+            cyc.append(dict(capacity=cap, policy=pol, hits=r["hits"], misses=r["misses"]))
+    print(json.dumps({"metric": "slot policy replay (host only)", "data": "synthetic",
+                      "config": {"workload": f"stack route trace: {L} layers x {n_tok} tokens, {E} experts, top-{k}, "
+                                             f"Markov p_repeat {wl['p_repeat']}; payload {pb} B",
+                                 "cyclic": "one layer cycling through 10 experts, 50 cycles"},
+                      "stack": rows, "cyclic": cyc}), flush=True)
+    return 0
+
+
 def run_stack(args, torch, moe, synth) -> int:
     """40 routed layers of the decode shape sharing one 1,536-slot LRU pool:
     per layer the step is routed (synthetic Markov logits), its plan read
@@ -451,7 +485,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=["decode", "mtp", "prefill", "stack"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "mtp", "prefill", "stack", "replay"])
     ap.add_argument("--mfma-sweep", action="store_true",
                     help="prefill buckets of M tokens (M = 16 .. 512) on the matrix cores: time and utilisation")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -475,6 +509,8 @@ def main() -> int:
     import synth
     from routed_expert_execution_amd import moe
 
+    if args.workload == "replay":
+        return replay_policies(args, synth, moe)
     if args.ceilings:
         return ceilings(torch, moe)
     if args.mfma_sweep:
