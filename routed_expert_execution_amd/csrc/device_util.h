@@ -113,6 +113,18 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
     return max((uint32_t)r[0], (uint32_t)r[1]);
 }
 
+// Minimum over the wave of an unsigned 32-bit value, returned to every lane.
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, v, 0xB1, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, v, 0x4E, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, v, 0x141, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, v, 0x140, 0xF, 0xF, false));
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = min((uint32_t)r[0], (uint32_t)r[1]);
+    r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return min((uint32_t)r[0], (uint32_t)r[1]);
+}
+
 // Bits of the lanes below this one in a 64-lane mask.
 __device__ inline int lanes_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));

@@ -269,6 +269,45 @@ __device__ void router_rows(const FfnArgs& a, const DGrid& g, uint32_t count, in
     }
 }
 
+// A router row whose weights are loaded with the workgroup's first loads and
+// whose dot product is taken against the token's activations once they are in
+// LDS (one token; each wave at most one row, d <= 2048): the same slices per
+// lane, in the same order, as the route kernel's row dot, so the same bits.
+struct RouterRowLds {
+    float4 wv[8];
+    int e;
+    __device__ void load(const FfnArgs& a, const DGrid& g, int h, int H) {
+        const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        e = h + wave * H;
+        const float* row = a.w_router + (int64_t)min(e, a.E - 1) * g.d;  // a valid row either way
+#pragma unroll
+        for (int u = 0; u < 8; u++) wv[u] = *(const float4*)(row + min(lane * 4 + 256 * u, g.d - 4));
+    }
+    __device__ void finish(const FfnArgs& a, const DGrid& g, uint32_t count, const float* xl) const {
+        const int lane = threadIdx.x & 63;
+        if (e >= a.E) return;
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int c = lane * 4 + 256 * u;
+            if (c < g.d) {
+                const float4 xv = *(const float4*)(xl + c);
+                const float4 w = make_float4(__uint_as_float(opaque(__float_as_uint(wv[u].x))),
+                                             __uint_as_float(opaque(__float_as_uint(wv[u].y))),
+                                             __uint_as_float(opaque(__float_as_uint(wv[u].z))),
+                                             __uint_as_float(opaque(__float_as_uint(wv[u].w))));
+                acc = fmaf(w.x, xv.x, acc);
+                acc = fmaf(w.y, xv.y, acc);
+                acc = fmaf(w.z, xv.z, acc);
+                acc = fmaf(w.w, xv.w, acc);
+            }
+        }
+        const float v = seg_sum<64>(acc);
+        float* dst = a.hbuf + (int64_t)launch_parity(count, g.n_down) * g.half + g.lg_off + e;
+        if (lane < kDecodeCopies) __hip_atomic_store(dst + lane * g.copy, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+};
+
 // The step's routing, computed by this workgroup from the logits into LDS: the
 // top-k of token t on wave t, then the union (the same code and so the same
 // bits as the route kernels).  The logits are the caller's (kRouteLogits,
@@ -426,12 +465,17 @@ __device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int wg, unsigned 
     // token, its activations.
     const uint32_t count = __hip_atomic_load(a.sync + kSyncCount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int S = has_shared ? g.n_rg / RG : 0;  // items of the shared expert
-    if (a.route == kRouteRouter) {
-        // router rows go to the workgroups whose first item is routed (all of
-        // them if there are no such workgroups)
-        const int h0 = g.n_gu_wg > S ? S : 0;
-        if (wg >= h0) router_rows(a, g, count, wg - h0, g.n_gu_wg - h0);
-    }
+    // router rows go to the workgroups whose first item is routed (all of them
+    // if there are no such workgroups); with one token and at most one row per
+    // wave, against the activations this workgroup stages in LDS anyway (exact
+    // values: bf16 input, or fp32 kept in fp32)
+    const int h0 = g.n_gu_wg > S ? S : 0, H = g.n_gu_wg - h0;
+    const bool rows_here = a.route == kRouteRouter && wg >= h0;
+    constexpr bool kOneToken = TG == 1;
+    const bool rows_lds = kOneToken && (a.x_bf16 || PREC == MOE_PREC_F32) && H * kWaves >= a.E && g.d <= 2048;
+    RouterRowLds rr;
+    if (rows_here && rows_lds) rr.load(a, g, wg - h0, H);
+    if (rows_here && !rows_lds) router_rows(a, g, count, wg - h0, H);
     const int na_raw = *a.n_active;
     PtRow ptr;
     ptr.load(a);
@@ -450,6 +494,8 @@ __device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int wg, unsigned 
     if constexpr (TG == 1) x1.store(a, g.d, L.x[0]);
     lg1.store(a, L.lg);
     lds_barrier();
+    if constexpr (kOneToken)
+        if (rows_here && rows_lds) rr.finish(a, g, count, L.x[0]);
     const int par = __builtin_amdgcn_readfirstlane(launch_parity(opaque(count), g.n_down));
     // A launch that routes counts its gate/up workgroups in: the down workgroups
     // finish (and so move the launch count) only once all have read it, so no

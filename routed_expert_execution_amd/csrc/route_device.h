@@ -56,9 +56,11 @@ template <int KPL>
 __device__ inline void topk_wave(const float* l, int E, int k, int norm, int32_t* ids, float* w) {
     const int lane = threadIdx.x & 63;
     // Expert e = lane + 64 m is value val[m] (order-preserving bits) while bit m
-    // of avail is set.  Each round takes the wave's largest value (one 32-bit
-    // DPP max) and, among the experts holding it, the lowest index: the lowest
-    // m whose ballot is not empty, then its lowest lane.
+    // of avail is set.  Each lane keeps the best of its available values.  A
+    // round takes the wave's largest value (one 32-bit DPP max); every lane
+    // offers its lowest expert index holding it, and one DPP min picks the
+    // lowest of all (ties to the lower index); only the winning lane then
+    // recomputes its best.
     uint32_t val[KPL];
     uint32_t avail = 0;
 #pragma unroll
@@ -67,22 +69,28 @@ __device__ inline void topk_wave(const float* l, int E, int k, int norm, int32_t
         val[m] = e < E ? order_bits(l[e]) : 0u;
         avail |= (e < E ? 1u : 0u) << m;
     }
+    auto lane_best = [&]() __attribute__((always_inline)) {
+        uint32_t b = 0;
+#pragma unroll
+        for (int m = 0; m < KPL; m++) b = ((avail >> m) & 1u) ? max(b, val[m]) : b;
+        return b;
+    };
+    uint32_t best = lane_best();
     float my_logit = 0.f;  // lane j keeps the j-th selected logit
     int my_id = 0;
     for (int j = 0; j < k; j++) {
-        uint32_t best = 0;
-#pragma unroll
-        for (int m = 0; m < KPL; m++) best = ((avail >> m) & 1u) ? max(best, val[m]) : best;
         const uint32_t top = wave_max_u32(best);
-        int sel = -1;
+        uint32_t cand = 0xFFFFFFFFu;  // 64 m + lane of this lane's lowest m holding top
 #pragma unroll
-        for (int m = 0; m < KPL; m++) {
-            const uint64_t b = __ballot(((avail >> m) & 1u) && val[m] == top);
-            if (sel < 0 && b) sel = 64 * m + (int)__builtin_ctzll(b);
+        for (int m = KPL - 1; m >= 0; m--)
+            cand = (((avail >> m) & 1u) && val[m] == top) ? (uint32_t)(64 * m + lane) : cand;
+        const uint32_t sel = wave_min_u32(cand);
+        if (sel != 0xFFFFFFFFu && (int)(sel & 63u) == lane) {  // (some key is always left: k <= E)
+            avail &= ~(1u << (sel >> 6));
+            best = lane_best();
         }
-        if ((sel & 63) == lane) avail &= ~(1u << (sel >> 6));
         if (lane == j) {
-            my_id = sel;
+            my_id = (int)sel;
             my_logit = unorder_bits(top);
         }
     }
@@ -113,7 +121,8 @@ __device__ inline void topk_wave(const float* l, int E, int k, int norm, int32_t
 // expert, its first place and its rank among the buckets.
 //
 // Lane l holds entries l and l + 64.  The relations come bit by bit from the
-// expert ids (10 bits, E <= 1024), most significant first, one ballot per bit:
+// expert ids (up to the highest bit any id has; E <= 1024), most significant
+// first, one ballot per bit (per word of 64 entries):
 // for each of its entries a lane keeps the mask of entries equal so far and
 // the mask of those already found smaller.  Every thread of the workgroup
 // calls it; the outputs are complete after the caller's next barrier.
@@ -126,18 +135,30 @@ __device__ inline void union_small(const int32_t* s_ids, int N, int32_t* n_activ
     const uint64_t V0 = __ballot(ok0), V1 = __ballot(ok1);
     uint64_t q00 = V0, q01 = V1, q10 = V0, q11 = V1;  // equal so far (entry 0: words 0, 1; entry 1)
     uint64_t s00 = 0, s01 = 0, s10 = 0, s11 = 0;      // found smaller
-#pragma unroll
-    for (int b = 9; b >= 0; b--) {
-        const uint64_t B0 = __ballot((e0 >> b) & 1), B1 = __ballot((e1 >> b) & 1);
-        if ((e0 >> b) & 1) {
-            s00 |= q00 & ~B0; s01 |= q01 & ~B1; q00 &= B0; q01 &= B1;
-        } else {
-            q00 &= ~B0; q01 &= ~B1;
+    // only the bits up to the highest set bit of any id matter (ids < 1024)
+    const int top_bit = 31 - __builtin_clz(wave_max_u32((uint32_t)(e0 | e1)) | 1u);
+    if (N <= 64) {  // one word of entries
+        for (int b = top_bit; b >= 0; b--) {
+            const uint64_t B0 = __ballot((e0 >> b) & 1);
+            if ((e0 >> b) & 1) {
+                s00 |= q00 & ~B0; q00 &= B0;
+            } else {
+                q00 &= ~B0;
+            }
         }
-        if ((e1 >> b) & 1) {
-            s10 |= q10 & ~B0; s11 |= q11 & ~B1; q10 &= B0; q11 &= B1;
-        } else {
-            q10 &= ~B0; q11 &= ~B1;
+    } else {
+        for (int b = top_bit; b >= 0; b--) {
+            const uint64_t B0 = __ballot((e0 >> b) & 1), B1 = __ballot((e1 >> b) & 1);
+            if ((e0 >> b) & 1) {
+                s00 |= q00 & ~B0; s01 |= q01 & ~B1; q00 &= B0; q01 &= B1;
+            } else {
+                q00 &= ~B0; q01 &= ~B1;
+            }
+            if ((e1 >> b) & 1) {
+                s10 |= q10 & ~B0; s11 |= q11 & ~B1; q10 &= B0; q11 &= B1;
+            } else {
+                q10 &= ~B0; q11 &= ~B1;
+            }
         }
     }
     // equal entries before each (entry l: only word 0 lies below it)
