@@ -476,13 +476,14 @@ __device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int wg, unsigned 
     RouterRowLds rr;
     if (rows_here && rows_lds) rr.load(a, g, wg - h0, H);
     if (rows_here && !rows_lds) router_rows(a, g, count, wg - h0, H);
-    const int na_raw = *a.n_active;
+    const bool plan_in = a.route == kRoutePlan;  // a launch that routes reads no plan
+    const int na_raw = plan_in ? *a.n_active : 0;
     PtRow ptr;
     ptr.load(a);
     const int i1 = threadIdx.x;
-    const uint32_t ex1 = (uint32_t)a.experts[min(i1, a.E - 1)];
-    const uint32_t of1 = (uint32_t)a.offsets[min(i1, a.E)];
-    const uint32_t en1 = (uint32_t)a.entries[min(i1, n_ent - 1)];
+    const uint32_t ex1 = plan_in ? (uint32_t)a.experts[min(i1, a.E - 1)] : 0u;
+    const uint32_t of1 = plan_in ? (uint32_t)a.offsets[min(i1, a.E)] : 0u;
+    const uint32_t en1 = plan_in ? (uint32_t)a.entries[min(i1, n_ent - 1)] : 0u;
     XRow<PREC> x1;
     if constexpr (TG == 1) x1.load(a, g.d, 0);
     LgIn lg1;
@@ -647,14 +648,15 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
     // Level 1, all independent loads: the launch count, n_active, the
     // page-table row and the whole plan (units, entry ranges, entries, weights).
     const uint32_t count = __hip_atomic_load(a.sync + kSyncCount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int na_raw = *a.n_active;
+    const bool plan_in = a.route == kRoutePlan;  // a launch that routes reads no plan
+    const int na_raw = plan_in ? *a.n_active : 0;
     PtRow ptr;
     ptr.load(a);
     const int i1 = threadIdx.x;
-    const uint32_t ex1 = (uint32_t)a.experts[min(i1, a.E - 1)];
-    const uint32_t of1 = (uint32_t)a.offsets[min(i1, a.E)];
-    const uint32_t en1 = (uint32_t)a.entries[min(i1, n_ent - 1)];
-    const uint32_t w1 = __float_as_uint(a.topk_w[min(i1, n_ent - 1)]);
+    const uint32_t ex1 = plan_in ? (uint32_t)a.experts[min(i1, a.E - 1)] : 0u;
+    const uint32_t of1 = plan_in ? (uint32_t)a.offsets[min(i1, a.E)] : 0u;
+    const uint32_t en1 = plan_in ? (uint32_t)a.entries[min(i1, n_ent - 1)] : 0u;
+    const uint32_t w1 = plan_in ? __float_as_uint(a.topk_w[min(i1, n_ent - 1)]) : 0u;
     LgIn lg1;
     lg1.load(a);
     ptr.store(a, L.pre.pts);
