@@ -385,6 +385,7 @@ def run_stack(args, torch, moe, synth) -> int:
     stream = torch.cuda.current_stream(dev)
     ffn_ev = []
     unique = 0
+    last_route = [None] * L  # per layer: (ids, weights) of its previous token
 
     def token(t, timed):
         nonlocal unique
@@ -395,6 +396,17 @@ def run_stack(args, torch, moe, synth) -> int:
             for e, sl, m in zip(experts, slots, miss):
                 if m:
                     moe.moe_slot_fill(ctx, l, int(e), int(sl), packs[l % n_alias][int(e)], stream=side)
+            if args.prefetch:
+                last_route[l] = (ids.cpu().numpy()[0], w.cpu().numpy()[0])
+                nl = (l + 1) % L  # the next layer to run (layer 0 of the next token after the last)
+                if last_route[nl] is not None:
+                    pid, pw = last_route[nl]
+                    pred = [int(e) for e, ww in sorted(zip(pid, pw), key=lambda q: -q[1]) if ww >= 0.20]
+                    if pred:
+                        ps, fill = moe.moe_slot_prefetch(ctx, nl, pred, args.prefetch * pb)
+                        for e, sl, fl in zip(pred, ps, fill):
+                            if fl:
+                                moe.moe_slot_fill(ctx, nl, e, int(sl), packs[nl % n_alias][e], stream=side)
             if timed:
                 # the FFN waits for the layer's fills anyway; waiting before the
                 # first event keeps the copies out of the kernel's own time
@@ -422,6 +434,7 @@ def run_stack(args, torch, moe, synth) -> int:
     if st != moe.MOE_OK:
         print(f"device error word set: status {st}", file=sys.stderr)
         return 1
+    pf = moe.moe_prefetch_stats(ctx)
     hits, misses = st1["hits"] - st0["hits"], st1["misses"] - st0["misses"]
     staged = st1["bytes_staged"] - st0["bytes_staged"]
     ffn = np.array([a.elapsed_time(b) for a, b in ffn_ev]) * 1e3
@@ -444,7 +457,9 @@ def run_stack(args, torch, moe, synth) -> int:
             "workload": (f"stack: {L} MoE layers, {E} experts, top-{k} + 1 shared expert, d_model {d}, d_ff {f}, "
                          f"Q8_0, 1 token/step, one {n_slots}-slot LRU pool shared by the layers, Markov routes "
                          f"(p_repeat {wl['p_repeat']}), misses staged from pinned host memory on a side stream "
-                         f"after each layer's plan readback; payload sets alias mod {n_alias} layers"),
+                         f"after each layer's plan readback; payload sets alias mod {n_alias} layers"
+                         + (f"; lookahead prefetch of up to {args.prefetch} predicted payloads per layer"
+                            if args.prefetch else "")),
             "global_batch": 1,
             "parallelism": "single GPU",
         },
@@ -467,6 +482,8 @@ def run_stack(args, torch, moe, synth) -> int:
             "ffn_GBps": ffn_gbs,
             "layer_steps_timed": len(ffn_ev),
             "setup_pack_s": t_gen,
+            "prefetch": ({"cap_payloads_per_layer": args.prefetch, "threshold": 0.20, **pf} if args.prefetch
+                         else None),
             "pages_context": "end-to-end 52.03 tok/s (best layer split) and 14.66 tok/s (exact RAM prefetch) "
                              "on an RTX 3080 PC, a different model and machine",
         },
@@ -486,6 +503,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode", choices=["decode", "mtp", "prefill", "stack", "replay"])
+    ap.add_argument("--prefetch", type=int, default=0, metavar="N",
+                    help="stack: after each layer's demand fills, prefetch the next layer's predicted experts "
+                         "(its previous token's experts with routing weight >= 0.20), at most N payloads")
     ap.add_argument("--mfma-sweep", action="store_true",
                     help="prefill buckets of M tokens (M = 16 .. 512) on the matrix cores: time and utilisation")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),

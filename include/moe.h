@@ -192,6 +192,27 @@ moe_status moe_slot_map(moe_ctx* ctx, int32_t layer, const int32_t* experts, int
 moe_status moe_slot_fill(moe_ctx* ctx, int32_t layer, int32_t expert, int32_t slot,
                          const void* host_payload, moe_stream side);
 
+/* Lookahead staging ahead of demand ("Paging the Experts", §3.3: predicted
+ * experts staged while the current layer computes; exact demand outranks
+ * prediction).  Host only, no device work.  experts: host [n], distinct, in
+ * priority order (e.g. highest routing weight first).  Each is mapped for
+ * `layer` WITHOUT pinning: a mapped one is only touched; an unmapped one takes
+ * the lowest free slot, else the least recently touched slot that no layer has
+ * pinned, while the fills so far stay within max_bytes.  It stops at the first
+ * expert that would exceed max_bytes or finds no such slot; *n_done (host)
+ * receives how many were processed.  slots_out / fill_out (host [n]): the slot,
+ * and 1 where the caller must now call moe_slot_fill (as for a miss).  A
+ * prefetched expert that a later moe_slot_map finds counts as a hit and as
+ * useful; one evicted before any use counts as wasted.  Demand counters keep
+ * their meaning (bytes_staged = misses x payload); prefetch fills also count
+ * in moe_stats' fills. */
+moe_status moe_slot_prefetch(moe_ctx* ctx, int32_t layer, const int32_t* experts, int32_t n, int64_t max_bytes,
+                             int32_t* slots_out, uint8_t* fill_out, int32_t* n_done);
+
+/* Prefetch counters since moe_create: out[0] prefetch fills, out[1] used by a
+ * later demand map, out[2] evicted unused, out[3] bytes prefetched. */
+moe_status moe_prefetch_stats(const moe_ctx* ctx, uint64_t out[4]);
+
 /* Unpin every slot pinned to `layer` and record, on `compute`, the point after
  * which their readers are done (later fills into them wait for it). */
 moe_status moe_slot_release(moe_ctx* ctx, int32_t layer, moe_stream compute);

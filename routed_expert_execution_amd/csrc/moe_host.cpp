@@ -41,8 +41,10 @@ struct moe_ctx {
     std::vector<uint64_t> last;     // recency stamp per slot
     std::vector<int32_t> pin_layer; // layer pinning the slot, or -1
     std::vector<int64_t> evicted;   // key evicted by the last map of this slot (fill invalidates it)
+    std::vector<char> spec;         // slot filled by a prefetch and not yet used by a demand map
     uint64_t clock = 0;
     uint64_t stats[5] = {0, 0, 0, 0, 0};
+    uint64_t pstats[4] = {0, 0, 0, 0};  // prefetch fills, useful, wasted, bytes
 
     // ordering
     hipEvent_t release_ev = nullptr;  // last moe_slot_release point on the compute stream
@@ -254,6 +256,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     c->last.assign(cfg->n_slots, 0);
     c->pin_layer.assign(cfg->n_slots, -1);
     c->evicted.assign(cfg->n_slots, -1);
+    c->spec.assign(cfg->n_slots, 0);
     if (!c->host_only) {
         DeviceGuard dg(cfg->device);
         auto cleanup = [&](moe_status st) { moe_destroy(c); return st; };
@@ -382,6 +385,10 @@ moe_status moe_slot_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32
         if (s >= 0) {
             c->stats[0]++;
             miss_out[i] = 0;
+            if (c->spec[s]) {  // a prefetch that demand now uses
+                c->pstats[1]++;
+                c->spec[s] = 0;
+            }
         } else {
             int32_t pick = -1;
             for (int q = 0; q < cf.n_slots; q++) if (c->owner[q] < 0) { pick = q; break; }
@@ -392,6 +399,10 @@ moe_status moe_slot_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32
                 c->slot_of[c->owner[pick]] = -1;
                 c->evicted[pick] = c->owner[pick];
                 c->stats[3]++;
+                if (c->spec[pick]) {  // a prefetch evicted before any use
+                    c->pstats[2]++;
+                    c->spec[pick] = 0;
+                }
             } else {
                 c->evicted[pick] = -1;
             }
@@ -406,6 +417,67 @@ moe_status moe_slot_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32
         c->pin_layer[s] = layer;
         slots_out[i] = s;
     }
+    return MOE_OK;
+}
+
+moe_status moe_slot_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int64_t max_bytes,
+                             int32_t* slots_out, uint8_t* fill_out, int32_t* n_done) {
+    if (!c) return MOE_EINVAL;
+    const moe_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers) return fail(c, MOE_EINVAL, "moe_slot_prefetch: bad layer");
+    if (n < 0 || n > cf.n_experts || max_bytes < 0) return fail(c, MOE_EINVAL, "moe_slot_prefetch: bad n or max_bytes");
+    if (!n_done || (n > 0 && (!experts || !slots_out || !fill_out)))
+        return fail(c, MOE_EINVAL, "moe_slot_prefetch: null array");
+    for (int32_t i = 0; i < n; i++) {
+        if (experts[i] < 0 || experts[i] >= cf.n_experts) return fail(c, MOE_EINVAL, "moe_slot_prefetch: expert id out of range");
+        for (int32_t j = 0; j < i; j++)
+            if (experts[j] == experts[i]) return fail(c, MOE_EINVAL, "moe_slot_prefetch: experts must be distinct");
+    }
+    const int64_t base = (int64_t)layer * cf.n_experts;
+    int64_t bytes = 0;
+    int32_t done = 0;
+    for (; done < n; done++) {
+        const int64_t key = base + experts[done];
+        int32_t s = c->slot_of[key];
+        if (s < 0) {
+            if (bytes + c->g.payload > max_bytes) break;
+            // a free slot, else the least recently touched unpinned one; never one
+            // that a layer in flight has pinned (demand outranks prediction)
+            int32_t pick = -1;
+            for (int q = 0; q < cf.n_slots; q++) if (c->owner[q] < 0) { pick = q; break; }
+            if (pick < 0) {
+                uint64_t best = UINT64_MAX;
+                for (int q = 0; q < cf.n_slots; q++)
+                    if (c->pin_layer[q] < 0 && c->last[q] < best) { best = c->last[q]; pick = q; }
+                if (pick < 0) break;
+                c->slot_of[c->owner[pick]] = -1;
+                c->evicted[pick] = c->owner[pick];
+                c->stats[3]++;
+                if (c->spec[pick]) c->pstats[2]++;
+            } else {
+                c->evicted[pick] = -1;
+            }
+            s = pick;
+            c->owner[s] = key;
+            c->slot_of[key] = s;
+            c->spec[s] = 1;
+            c->pstats[0]++;
+            c->pstats[3] += (uint64_t)c->g.payload;
+            bytes += c->g.payload;
+            fill_out[done] = 1;
+        } else {
+            fill_out[done] = 0;
+        }
+        c->last[s] = ++c->clock;  // predicted: kept until the demand that should follow
+        slots_out[done] = s;
+    }
+    *n_done = done;
+    return MOE_OK;
+}
+
+moe_status moe_prefetch_stats(const moe_ctx* c, uint64_t out[4]) {
+    if (!c || !out) return MOE_EINVAL;
+    for (int i = 0; i < 4; i++) out[i] = c->pstats[i];
     return MOE_OK;
 }
 

@@ -67,6 +67,8 @@ def _load() -> C.CDLL:
         "moe_route_union": (C.c_int, [P, P, C.c_int32, P, P, I64, P, P, P, planp, P]),
         "moe_slot_map": (C.c_int, [P, I32, P, I32, P, P]),
         "moe_slot_fill": (C.c_int, [P, I32, I32, I32, P, P]),
+        "moe_slot_prefetch": (C.c_int, [P, I32, P, I32, I64, P, P, P]),
+        "moe_prefetch_stats": (C.c_int, [P, C.POINTER(C.c_uint64)]),
         "moe_slot_release": (C.c_int, [P, I32, P]),
         "moe_slot_bind": (C.c_int, [P, I32, I32, I32, P]),
         "moe_expert_ffn": (C.c_int, [P, I32, P, I32, I64, planp, P, P, I32, P, P]),
@@ -88,7 +90,8 @@ def _load() -> C.CDLL:
 _lib = _load()
 EXPORTS = ("moe_payload_bytes", "moe_plan_bytes", "moe_pack_expert", "moe_unpack_expert", "moe_create",
            "moe_destroy", "moe_last_error", "moe_status_string", "moe_route", "moe_plan_union", "moe_route_union",
-           "moe_slot_map", "moe_slot_fill", "moe_slot_release", "moe_slot_bind", "moe_expert_ffn",
+           "moe_slot_map", "moe_slot_prefetch", "moe_prefetch_stats", "moe_slot_fill", "moe_slot_release",
+           "moe_slot_bind", "moe_expert_ffn",
            "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table", "moe_probe_read",
            "moe_probe_mfma")
 
@@ -294,6 +297,24 @@ def moe_slot_map(ctx: Context, layer: int, experts) -> tuple:
     miss = np.empty(e.size, dtype=np.uint8)
     _call(ctx, _lib.moe_slot_map(ctx.handle, layer, e.ctypes.data, e.size, slots.ctypes.data, miss.ctypes.data))
     return slots, miss.astype(bool)
+
+
+def moe_slot_prefetch(ctx: Context, layer: int, experts, max_bytes: int) -> tuple:
+    """Map predicted experts (priority order) without pinning; returns (slots,
+    fill) for the ones processed (fill: the caller now calls moe_slot_fill)."""
+    e = np.ascontiguousarray(experts, dtype=np.int32).reshape(-1)
+    slots = np.empty(e.size, dtype=np.int32)
+    fill = np.empty(e.size, dtype=np.uint8)
+    done = C.c_int32()
+    _call(ctx, _lib.moe_slot_prefetch(ctx.handle, layer, e.ctypes.data, e.size, int(max_bytes), slots.ctypes.data,
+                                      fill.ctypes.data, C.byref(done)))
+    return slots[: done.value], fill[: done.value].astype(bool)
+
+
+def moe_prefetch_stats(ctx: Context) -> dict:
+    out = (C.c_uint64 * 4)()
+    _call(ctx, _lib.moe_prefetch_stats(ctx.handle, out))
+    return dict(fills=out[0], useful=out[1], wasted=out[2], bytes=out[3])
 
 
 def moe_slot_fill(ctx: Context, layer: int, expert: int, slot: int, host_payload, stream=None) -> None:

@@ -1,0 +1,82 @@
+"""Lookahead staging is transparent ("Paging the Experts", §5.3: outputs are
+identical under any slot assignment, eviction order or prefetch): a staged
+layer stack run with and without prefetching the next layer's predicted
+experts gives bit-identical outputs, which also meet the oracle's bar."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not H.gpu_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from routed_expert_execution_amd import moe  # noqa: E402
+
+
+def _run_stack(prefetch: bool, L=3, n_tok=6, n_slots=24):
+    wl = synth.workload("stack40")
+    E, k, d, f = wl["E"], wl["k"], wl["d"], wl["f"]
+    ctx = H.make_ctx(wl, n_slots=n_slots, max_tokens=1, n_layers=L)
+    chains = [synth.markov_route_sets(synth.rng(wl["seed"], 77, l), n_tok, E, k, wl["p_repeat"]) for l in range(L)]
+    host = {}
+
+    def payload(l, e):
+        if (l, e) not in host:
+            rec = synth.expert_record(wl["seed"], l, e, wl["qtype"], d, f)
+            host[(l, e)] = (rec, torch.from_numpy(H.payload(ctx, rec)).pin_memory())
+        return host[(l, e)][1]
+
+    shared = synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True)
+    sh_dev = H.device_payload(ctx, shared)
+    side = torch.cuda.Stream()
+    plan = moe.Plan(ctx, 1)
+    outs = []
+    for t in range(n_tok):
+        for l in range(L):
+            lg = np.full((1, E), -1.0, np.float32)
+            lg[0, chains[l][t]] = 2.0 + np.arange(k, dtype=np.float32) / 16
+            ids = torch.empty(1, k, dtype=torch.int32, device="cuda")
+            w = torch.empty(1, k, dtype=torch.float32, device="cuda")
+            moe.moe_route_union(ctx, ids, w, plan, logits_in=torch.from_numpy(lg).cuda())
+            n, ex, _, _ = plan.host()
+            slots, miss = moe.moe_slot_map(ctx, l, ex)
+            for e, s_, m in zip(ex, slots, miss):
+                if m:
+                    moe.moe_slot_fill(ctx, l, int(e), int(s_), payload(l, int(e)), stream=side)
+            if prefetch and l + 1 < L and t > 0:
+                # predict layer l + 1 from its previous token's experts, cap: 3 payloads
+                pred = list(chains[l + 1][t - 1])
+                ps, fill = moe.moe_slot_prefetch(ctx, l + 1, pred, 3 * ctx.payload_bytes)
+                for e, s_, fl in zip(pred, ps, fill):
+                    if fl:
+                        moe.moe_slot_fill(ctx, l + 1, int(e), int(s_), payload(l + 1, int(e)), stream=side)
+            x = synth.activations(wl["seed"], 1, d, "bf16", t, l)
+            y = torch.empty(1, d, dtype=torch.float32, device="cuda")
+            moe.moe_expert_ffn(ctx, l, H.torch_x(x, "bf16"), plan, w, y, shared_payload=sh_dev)
+            moe.moe_slot_release(ctx, l)
+            outs.append((l, t, x, ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy()))
+    assert moe.moe_check(ctx) == moe.MOE_OK
+    return outs, moe.moe_stats(ctx), moe.moe_prefetch_stats(ctx), host, shared
+
+
+def test_prefetch_is_transparent_and_counted():
+    base, st0, ps0, _, _ = _run_stack(False)
+    pre, st1, ps1, host, shared = _run_stack(True)
+    assert ps0["fills"] == 0 and ps1["fills"] > 0
+    assert ps1["useful"] + ps1["wasted"] <= ps1["fills"]
+    assert st1["fills"] == st1["misses"] + ps1["fills"]
+    for (l, t, x, ids_a, w_a, y_a), (_, _, _, ids_b, w_b, y_b) in zip(base, pre):
+        assert np.array_equal(ids_a, ids_b)
+        assert np.array_equal(y_a.view(np.uint32), y_b.view(np.uint32)), (l, t)
+    wl = synth.workload("stack40")
+    # and the outputs are right (last token of every layer)
+    for l, t, x, ids, w, y in base[-3:]:
+        records = [host[(l, e)][0] if (l, e) in host else None for e in range(wl["E"])]
+        ref = oracle.moe_layer(wl["qtype"], oracle.PREC_F32, records, shared, wl["d"], wl["f"],
+                               oracle.x_to_f64(x, "bf16"), ids, w)
+        assert H.max_rel_row_err(y, ref) <= 1e-3
