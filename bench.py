@@ -381,21 +381,25 @@ def run_stack(args, torch, moe, synth) -> int:
     w = torch.empty(1, k, dtype=torch.float32, device=dev)
     y = torch.empty(1, d, dtype=torch.float32, device=dev)
     plan = moe.Plan(ctx, 1)
-    side = torch.cuda.Stream(device=dev)
+    sides = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.fill_streams))]
+    side = sides[0]
     stream = torch.cuda.current_stream(dev)
     ffn_ev = []
+    n_fill = 0
     unique = 0
     last_route = [None] * L  # per layer: (ids, weights) of its previous token
 
     def token(t, timed):
-        nonlocal unique
+        nonlocal unique, n_fill
         for l in range(L):
             moe.moe_route_union(ctx, ids, w, plan, logits_in=lg[l, t:t + 1])
-            n, experts, _, _ = plan.host()  # the host learns the layer's experts only now
+            n, experts = plan.experts_host()  # the host learns the layer's experts only now
             slots, miss = moe.moe_slot_map(ctx, l, experts)
             for e, sl, m in zip(experts, slots, miss):
-                if m:
-                    moe.moe_slot_fill(ctx, l, int(e), int(sl), packs[l % n_alias][int(e)], stream=side)
+                if m:  # fills alternate over the side streams (copy engines)
+                    moe.moe_slot_fill(ctx, l, int(e), int(sl), packs[l % n_alias][int(e)],
+                                      stream=sides[n_fill % len(sides)])
+                    n_fill += 1
             if args.prefetch:
                 last_route[l] = (ids.cpu().numpy()[0], w.cpu().numpy()[0])
                 nl = (l + 1) % L  # the next layer to run (layer 0 of the next token after the last)
@@ -406,11 +410,14 @@ def run_stack(args, torch, moe, synth) -> int:
                         ps, fill = moe.moe_slot_prefetch(ctx, nl, pred, args.prefetch * pb)
                         for e, sl, fl in zip(pred, ps, fill):
                             if fl:
-                                moe.moe_slot_fill(ctx, nl, e, int(sl), packs[nl % n_alias][e], stream=side)
+                                moe.moe_slot_fill(ctx, nl, e, int(sl), packs[nl % n_alias][e],
+                                                  stream=sides[n_fill % len(sides)])
+                                n_fill += 1
             if timed:
                 # the FFN waits for the layer's fills anyway; waiting before the
                 # first event keeps the copies out of the kernel's own time
-                stream.wait_stream(side)
+                for sd in sides:
+                    stream.wait_stream(sd)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
             moe.moe_expert_ffn(ctx, l, xs[t, l], plan, w, y, shared_payload=shared)
@@ -459,7 +466,8 @@ def run_stack(args, torch, moe, synth) -> int:
                          f"(p_repeat {wl['p_repeat']}), misses staged from pinned host memory on a side stream "
                          f"after each layer's plan readback; payload sets alias mod {n_alias} layers"
                          + (f"; lookahead prefetch of up to {args.prefetch} predicted payloads per layer"
-                            if args.prefetch else "")),
+                            if args.prefetch else "")
+                         + (f"; fills alternate over {args.fill_streams} side streams" if args.fill_streams > 1 else "")),
             "global_batch": 1,
             "parallelism": "single GPU",
         },
@@ -506,6 +514,8 @@ def main() -> int:
     ap.add_argument("--prefetch", type=int, default=0, metavar="N",
                     help="stack: after each layer's demand fills, prefetch the next layer's predicted experts "
                          "(its previous token's experts with routing weight >= 0.20), at most N payloads")
+    ap.add_argument("--fill-streams", type=int, default=2, metavar="S",
+                    help="stack: side streams the misses' copies alternate over")
     ap.add_argument("--mfma-sweep", action="store_true",
                     help="prefill buckets of M tokens (M = 16 .. 512) on the matrix cores: time and utilisation")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),

@@ -226,11 +226,32 @@ class Plan:
     def __init__(self, ctx: Context, T: int):
         import torch
         dev = torch.device("cuda", ctx.device)
-        self.n_active = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.experts = torch.zeros(ctx.n_experts, dtype=torch.int32, device=dev)
-        self.offsets = torch.zeros(ctx.n_experts + 1, dtype=torch.int32, device=dev)
-        self.entries = torch.zeros(max(1, T * ctx.top_k), dtype=torch.int32, device=dev)
+        E = ctx.n_experts
+        up = lambda n: (n + 63) // 64 * 64  # noqa: E731  (256-byte starts)
+        # one allocation; n_active sits in the word just before experts, so the
+        # two come back in one copy
+        o_ex, o_off = 64, 64 + up(E)
+        o_ent = o_off + up(E + 1)
+        self._buf = torch.zeros(o_ent + max(1, T * ctx.top_k), dtype=torch.int32, device=dev)
+        self.n_active = self._buf[o_ex - 1:o_ex]
+        self.experts = self._buf[o_ex:o_ex + E]
+        self.offsets = self._buf[o_off:o_off + E + 1]
+        self.entries = self._buf[o_ent:]
+        self._head = self._buf[o_ex - 1:o_ex + E]
+        self._pinned = torch.empty(1 + E, dtype=torch.int32).pin_memory()
         self.c = moe_plan(_ptr(self.n_active), _ptr(self.experts), _ptr(self.offsets), _ptr(self.entries))
+
+    def experts_host(self, stream=None):
+        """(n_active, experts[:n_active]) with one copy into pinned memory, after
+        the work enqueued on `stream` (default: the current stream)."""
+        import torch
+        st = stream or torch.cuda.current_stream(self._buf.device)
+        with torch.cuda.stream(st):
+            self._pinned.copy_(self._head, non_blocking=True)
+        st.synchronize()
+        h = self._pinned.numpy()
+        n = int(h[0])
+        return n, h[1:1 + n].copy()
 
     def host(self):
         """(n_active, experts, offsets, entries) copied to numpy (synchronises)."""
