@@ -381,10 +381,12 @@ def run_stack(args, torch, moe, synth) -> int:
     w = torch.empty(1, k, dtype=torch.float32, device=dev)
     y = torch.empty(1, d, dtype=torch.float32, device=dev)
     plan = moe.Plan(ctx, 1)
+    tables = [moe.payload_table(ctx, [packs[a][e] for e in range(E)]) for a in range(n_alias)]
     sides = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.fill_streams))]
     side = sides[0]
     stream = torch.cuda.current_stream(dev)
     ffn_ev = []
+    pull_ev = []  # (event before the pull, misses): the pull ends where the FFN's first event is
     n_fill = 0
     unique = 0
     last_route = [None] * L  # per layer: (ids, weights) of its previous token
@@ -393,13 +395,25 @@ def run_stack(args, torch, moe, synth) -> int:
         nonlocal unique, n_fill
         for l in range(L):
             moe.moe_route_union(ctx, ids, w, plan, logits_in=lg[l, t:t + 1])
-            n, experts = plan.experts_host()  # the host learns the layer's experts only now
-            slots, miss = moe.moe_slot_map(ctx, l, experts)
-            for e, sl, m in zip(experts, slots, miss):
-                if m:  # fills alternate over the side streams (copy engines)
-                    moe.moe_slot_fill(ctx, l, int(e), int(sl), packs[l % n_alias][int(e)],
-                                      stream=sides[n_fill % len(sides)])
-                    n_fill += 1
+            n, experts = plan.experts_host(spin=args.spin_readback)  # the host learns the layer's experts only now
+            ev = timed and l % 8 == 0  # kernel times on every 8th layer
+            if args.staging == "pull":  # map, then the misses copied by a kernel on the compute stream
+                if ev:
+                    ep = torch.cuda.Event(enable_timing=True)
+                    ep.record(stream)
+                slots, miss = moe.moe_slot_pull(ctx, l, experts, tables[l % n_alias], stream=stream)
+                if ev:
+                    pull_ev.append((ep, int(miss.sum())))
+            elif args.staging == "stage":  # map + copies over the side streams + one page-table launch
+                slots, miss = moe.moe_slot_stage(ctx, l, experts, tables[l % n_alias], sides)
+                n_fill += int(miss.sum())
+            else:
+                slots, miss = moe.moe_slot_map(ctx, l, experts)
+                for e, sl, m in zip(experts, slots, miss):
+                    if m:  # fills alternate over the side streams (copy engines)
+                        moe.moe_slot_fill(ctx, l, int(e), int(sl), packs[l % n_alias][int(e)],
+                                          stream=sides[n_fill % len(sides)])
+                        n_fill += 1
             if args.prefetch:
                 last_route[l] = (ids.cpu().numpy()[0], w.cpu().numpy()[0])
                 nl = (l + 1) % L  # the next layer to run (layer 0 of the next token after the last)
@@ -413,15 +427,16 @@ def run_stack(args, torch, moe, synth) -> int:
                                 moe.moe_slot_fill(ctx, nl, e, int(sl), packs[nl % n_alias][e],
                                                   stream=sides[n_fill % len(sides)])
                                 n_fill += 1
-            if timed:
-                # the FFN waits for the layer's fills anyway; waiting before the
-                # first event keeps the copies out of the kernel's own time
-                for sd in sides:
-                    stream.wait_stream(sd)
+            if ev:
+                # the FFN waits for the layer's side-stream fills anyway; waiting
+                # before the first event keeps the copies out of the kernel's time
+                if args.staging != "pull" or args.prefetch:
+                    for sd in sides:
+                        stream.wait_stream(sd)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
             moe.moe_expert_ffn(ctx, l, xs[t, l], plan, w, y, shared_payload=shared)
-            if timed:
+            if ev:
                 e1.record(stream)
                 ffn_ev.append((e0, e1))
                 unique += n
@@ -447,6 +462,15 @@ def run_stack(args, torch, moe, synth) -> int:
     ffn = np.array([a.elapsed_time(b) for a, b in ffn_ev]) * 1e3
     ffn_bytes = (unique + len(ffn_ev)) * pb  # unique routed experts + shared, over the timed layer steps
     ffn_gbs = ffn_bytes / (ffn.sum() * 1e-6) / 1e9
+    pull = None
+    if pull_ev:
+        pairs = [(p.elapsed_time(f[0]) * 1e3, m) for (p, m), f in zip(pull_ev, ffn_ev) if m]
+        if pairs:
+            us = sum(a for a, _ in pairs)
+            pull = {"layers_sampled": len(pairs), "us_mean": us / len(pairs),
+                    "GBps": sum(m for _, m in pairs) * pb / (us * 1e-6) / 1e9,
+                    "note": "moe_slot_pull kernels of every 8th layer with misses, payload bytes over their "
+                            "event time; link reference 57 GB/s (pinned host to device, peak_references.md)"}
     line = {
         "metric": "routed MoE tokens/s through a 40-layer decode stack (demand-staged slot cache)",
         "value": args.steps / wall,
@@ -463,17 +487,22 @@ def run_stack(args, torch, moe, synth) -> int:
         "config": {
             "workload": (f"stack: {L} MoE layers, {E} experts, top-{k} + 1 shared expert, d_model {d}, d_ff {f}, "
                          f"Q8_0, 1 token/step, one {n_slots}-slot LRU pool shared by the layers, Markov routes "
-                         f"(p_repeat {wl['p_repeat']}), misses staged from pinned host memory on a side stream "
+                         f"(p_repeat {wl['p_repeat']}), misses staged from pinned host memory "
                          f"after each layer's plan readback; payload sets alias mod {n_alias} layers"
                          + (f"; lookahead prefetch of up to {args.prefetch} predicted payloads per layer"
                             if args.prefetch else "")
-                         + (f"; fills alternate over {args.fill_streams} side streams" if args.fill_streams > 1 else "")),
+                         + (f"; copies alternate over {args.fill_streams} side streams"
+                            if args.fill_streams > 1 and args.staging != "pull" else "")
+                         + {"pull": "; one moe_slot_pull per layer: a kernel on the compute stream copies the misses",
+                            "stage": "; one moe_slot_stage call per layer",
+                            "fill": "; moe_slot_map + one moe_slot_fill per miss"}[args.staging]),
             "global_batch": 1,
             "parallelism": "single GPU",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "moe_expert_ffn per layer (one launch); expert payload bytes over its event time",
+            "kernel": "moe_expert_ffn per layer (one launch, every 8th layer timed); expert payload bytes "
+                      "over its event time",
             "achieved": ffn_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -489,6 +518,7 @@ def run_stack(args, torch, moe, synth) -> int:
             "ffn_us_mean": float(ffn.mean()),
             "ffn_GBps": ffn_gbs,
             "layer_steps_timed": len(ffn_ev),
+            "pull": pull,
             "setup_pack_s": t_gen,
             "prefetch": ({"cap_payloads_per_layer": args.prefetch, "threshold": 0.20, **pf} if args.prefetch
                          else None),
@@ -516,6 +546,12 @@ def main() -> int:
                          "(its previous token's experts with routing weight >= 0.20), at most N payloads")
     ap.add_argument("--fill-streams", type=int, default=2, metavar="S",
                     help="stack: side streams the misses' copies alternate over")
+    ap.add_argument("--spin-readback", action="store_true",
+                    help="stack: poll for the plan readback instead of a blocking synchronise")
+    ap.add_argument("--staging", choices=("pull", "stage", "fill"), default="pull",
+                    help="stack: one moe_slot_pull per layer (kernel copies on the compute stream), one "
+                         "moe_slot_stage per layer (copy engines on side streams), or moe_slot_map + one "
+                         "moe_slot_fill per miss")
     ap.add_argument("--mfma-sweep", action="store_true",
                     help="prefill buckets of M tokens (M = 16 .. 512) on the matrix cores: time and utilisation")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),

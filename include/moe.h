@@ -6,6 +6,8 @@
  *   moe_route_union both of the above in one call (fewer launches for <= 4 tokens)
  *   moe_slot_map    host LRU over a bounded pool of expert slots
  *   moe_slot_fill   pinned-host -> slot copy on a side stream + page-table write
+ *   moe_slot_stage  moe_slot_map and the fills of its misses in one call
+ *   moe_slot_pull   moe_slot_map, then one kernel copies the misses in
  *   moe_expert_ffn  quantised SwiGLU experts read through the page table,
  *                   shared expert, weighted combine
  *
@@ -54,6 +56,7 @@ typedef enum moe_status {
 enum { MOE_Q8_0 = 0, MOE_Q4_0 = 1 };          /* expert weight formats */
 enum { MOE_F32 = 0, MOE_BF16 = 1 };           /* activation element types */
 enum { MOE_PREC_F32 = 0, MOE_PREC_BF16 = 1 }; /* expert arithmetic modes (see moe_expert_ffn) */
+enum { MOE_MAX_STAGE_STREAMS = 8 };           /* side streams one moe_slot_stage call may use */
 
 typedef struct moe_config {
     int32_t n_layers;        /* routed layers sharing the slot pool (>= 1) */
@@ -173,8 +176,9 @@ moe_status moe_route_union(moe_ctx* ctx, const void* x, int32_t x_dtype, const f
  * moe_slot_map: host only, no device work.  experts: host [n], distinct and
  * ascending (e.g. the plan's experts copied back).  Each expert is touched
  * once in that order: a mapped one is a hit; an unmapped one takes the lowest
- * free slot, else the least recently touched unpinned slot (evicted).  Every
- * listed expert is then pinned to `layer` until moe_slot_release(layer).
+ * free slot, else the least recently touched slot that is unpinned and holds
+ * none of the listed experts (evicted).  Every listed expert is then pinned to
+ * `layer` until moe_slot_release(layer).
  * slots_out: host [n]; miss_out: host [n], 1 where the caller must now call
  * moe_slot_fill.  MOE_ENOSLOT (state unchanged) if misses exceed free plus
  * unpinned slots. */
@@ -182,7 +186,9 @@ moe_status moe_slot_map(moe_ctx* ctx, int32_t layer, const int32_t* experts, int
                         int32_t* slots_out, uint8_t* miss_out);
 
 /* Materialise a missed expert: on `side`, wait until every released reader of
- * the slot has finished, mark the evicted expert's page-table entry absent,
+ * the slot and every fill pending on another stream have finished (a pending
+ * fill may target the slot being reused), mark the evicted expert's
+ * page-table entry absent,
  * copy host_payload (pinned, moe_payload_bytes(), device payload layout) into
  * the slot with hipMemcpyAsync, then write page_table[layer, expert] = slot
  * and record a ready event ("Nanite for Experts", §3.4: asynchronous copies
@@ -191,6 +197,47 @@ moe_status moe_slot_map(moe_ctx* ctx, int32_t layer, const int32_t* experts, int
  * from moe_slot_map. */
 moe_status moe_slot_fill(moe_ctx* ctx, int32_t layer, int32_t expert, int32_t slot,
                          const void* host_payload, moe_stream side);
+
+/* moe_slot_map followed by the fills of its misses, in one call (a miss
+ * materialises the expert into its slot, "MawForge", §IV-C; copies from pinned
+ * memory on non-default streams, "Nanite for Experts", §3.4).
+ * host_payloads: host array of n_experts pointers indexed by expert id, each
+ *   to that expert's pinned payload (as for moe_slot_fill); only the entries of
+ *   experts that miss are read, the others may be NULL.
+ * sides: host array of n_sides (1..MOE_MAX_STAGE_STREAMS) side streams.  Each
+ *   stream that receives a copy first waits for every released reader (as in
+ *   moe_slot_fill); the misses' copies alternate over the streams in list
+ *   order.  Then sides[0] waits for the other streams, writes the page-table
+ *   entries of the evicted experts (absent) and of the filled ones (their
+ *   slots) in one launch, and records the ready event that the next
+ *   moe_expert_ffn waits for.
+ * experts, slots_out, miss_out and the mapping are those of moe_slot_map.  A
+ * missing expert whose payload pointer is NULL, or a map that moe_slot_map
+ * refuses, returns MOE_EINVAL / MOE_ENOSLOT with nothing mapped and nothing
+ * enqueued. */
+moe_status moe_slot_stage(moe_ctx* ctx, int32_t layer, const int32_t* experts, int32_t n,
+                          const void* const* host_payloads, int32_t* slots_out, uint8_t* miss_out,
+                          const moe_stream* sides, int32_t n_sides);
+
+/* moe_slot_map, then the misses materialised by the GPU itself ("MawForge",
+ * §IV-C: a miss brings the expert into its slot and updates the route-to-slot
+ * metadata): kernels on `stream` read each missing expert's payload over the
+ * host bus (or from device memory) and write it into its slot, and write the
+ * page-table entries of the evicted experts (absent) and of the new ones
+ * (their slots).  Work enqueued later on `stream` sees the experts resident
+ * without waiting for a copy engine; other streams wait for the ready event
+ * recorded on `stream` (moe_expert_ffn does).  Before its first write,
+ * `stream` waits for every released reader and for fills still pending on
+ * other streams.
+ * payloads: host array of n_experts pointers indexed by expert id, each to
+ *   that expert's payload (moe_payload_bytes(), device payload layout) in
+ *   pinned host memory (hipHostMalloc) or device memory; only the entries of
+ *   experts that miss are read, and each must be one of those two kinds, else
+ *   MOE_EINVAL with nothing mapped and nothing enqueued.
+ * experts, slots_out, miss_out and the mapping are those of moe_slot_map; a
+ * refused map changes nothing. */
+moe_status moe_slot_pull(moe_ctx* ctx, int32_t layer, const int32_t* experts, int32_t n,
+                         const void* const* payloads, int32_t* slots_out, uint8_t* miss_out, moe_stream stream);
 
 /* Lookahead staging ahead of demand ("Paging the Experts", §3.3: predicted
  * experts staged while the current layer computes; exact demand outranks

@@ -14,8 +14,11 @@ Readings where the pages are silent:
   - one step of one layer presents its distinct experts in ascending order;
     each is touched once, in that order, and pinned until that layer is
     released; a miss means "not mapped when the step presents it";
+  - the layer is evaluated with all of its experts resident at once, so the
+    whole step counts as pinned from its start: a slot that holds one of the
+    step's own experts is never a victim, even before that expert's turn;
   - a free slot is taken lowest index first; otherwise the victim is the
-    least recently touched unpinned slot;
+    least recently touched slot that is neither pinned nor one of the step's;
   - if the step has more misses than free plus evictable slots, the step is
     refused and nothing changes.
 """
@@ -61,7 +64,8 @@ class LruModel:
                 if free:
                     s = free[0]
                 else:
-                    cands = [s for s in range(self.n_slots) if self.pin_layer[s] is None]
+                    cands = [s for s in range(self.n_slots)
+                             if self.pin_layer[s] is None and s not in hit_slots]
                     s = min(cands, key=lambda c: self.last[c])
                     ev = self.owner[s]
                     del self.slot_of[ev]

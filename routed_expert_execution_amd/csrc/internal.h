@@ -187,6 +187,28 @@ hipError_t launch_ffn_prefill(const PrefillArgs& a, int prec, hipStream_t s);
 // by `wgs` workgroups, and `iters` rounds of bf16 matrix-core products (shape 0:
 // 16x16x32, 1: 32x32x16) over `grid` workgroups of 4 waves, with the flops the
 // latter performs.
+// Page-table writes (entry index, value) applied by one launch.
+constexpr int kPtBatch = 128;
+struct PtWrites {
+    int32_t n;
+    int32_t idx[kPtBatch];
+    int32_t val[kPtBatch];
+};
+hipError_t launch_pt_write(int32_t* pt, const PtWrites& w, hipStream_t s);
+
+// Payload copies of one pull launch: src[i] (pinned host or device memory, as
+// the kernel addresses it) -> dst[i] (a slot), `words` 16-byte words each.
+constexpr int kPullMax = 32;
+constexpr int kPullWorkgroups = 64;  // measured best for reads over the host bus
+struct PullArgs {
+    const uint4* src[kPullMax];
+    uint4* dst[kPullMax];
+    int32_t n;
+    uint32_t words;
+};
+static_assert(2 * kPullMax <= kPtBatch, "a pull launch writes up to two entries per copy");
+hipError_t launch_pull(const PullArgs& a, int32_t* pt, const PtWrites& w, hipStream_t s);
+
 hipError_t launch_probe_read(const void* src, int64_t bytes, int wgs, uint32_t* sink, hipStream_t s);
 hipError_t launch_probe_mfma(int iters, int grid, int shape, float* sink, hipStream_t s);
 int64_t probe_mfma_flops(int iters, int grid, int shape);

@@ -49,8 +49,19 @@ struct moe_ctx {
     // ordering
     hipEvent_t release_ev = nullptr;  // last moe_slot_release point on the compute stream
     bool release_recorded = false;
+    hipStream_t release_stream = nullptr;  // the stream release_ev was last recorded on
     struct Pending { hipStream_t s; hipEvent_t ev; bool pending; };
     std::vector<Pending> fills;       // one re-recorded event per side stream
+    // Completion marks of fill calls: a ring of events, each recorded after one
+    // call's writes (payloads and page-table entries); a slot remembers the mark
+    // and generation of its last fill, so that a later fill of the slot on
+    // another stream waits for exactly that one.  An entry is reused only after
+    // its previous recording has completed, so a stale generation means done.
+    struct Mark { hipEvent_t ev = nullptr; uint64_t gen = 0; hipStream_t s = nullptr; };
+    std::vector<Mark> marks;
+    uint32_t mark_next = 0;
+    std::vector<int32_t> slot_mark;   // slot -> mark index, or -1
+    std::vector<uint64_t> slot_gen;   // slot -> generation of that mark
 };
 
 namespace {
@@ -163,6 +174,78 @@ void repack(const Geom& g, const uint8_t* src, uint8_t* dst, bool to_tiles) {
     }
 }
 
+// The address under which a kernel reads p: p itself for device memory, the
+// mapped address for pinned host memory; false for anything else (pageable
+// host memory, which a kernel cannot read).
+bool device_view(const void* p, const void** out) {
+    hipPointerAttribute_t at{};
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    if (at.type == hipMemoryTypeDevice) {
+        *out = p;
+        return true;
+    }
+    if (at.type == hipMemoryTypeHost && at.devicePointer && at.hostPointer) {
+        *out = (const uint8_t*)at.devicePointer + ((const uint8_t*)p - (const uint8_t*)at.hostPointer);
+        return true;
+    }
+    return false;
+}
+
+// The re-recorded ready event of side stream s (created on first use).
+moe_status fill_event(moe_ctx* c, hipStream_t s, moe_ctx::Pending** out) {
+    for (auto& q : c->fills)
+        if (q.s == s) {
+            *out = &q;
+            return MOE_OK;
+        }
+    hipEvent_t ev;
+    HIP_TRY(c, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    c->fills.push_back({s, ev, false});
+    *out = &c->fills.back();
+    return MOE_OK;
+}
+
+constexpr int kMarks = 64;
+
+// Before stream s overwrites the given slots: every released reader has
+// finished, and the last fill of each slot, if another stream made it, has
+// landed (its copy and its page-table writes).
+moe_status order_before_fill(moe_ctx* c, hipStream_t s, const int32_t* slots, const uint8_t* use, int32_t n) {
+    if (c->release_recorded && c->release_stream != s) HIP_TRY(c, hipStreamWaitEvent(s, c->release_ev, 0));
+    uint64_t waited = 0;  // marks already waited for (kMarks <= 64)
+    for (int32_t i = 0; i < n; i++) {
+        if (use && !use[i]) continue;
+        const int32_t m = c->slot_mark[slots[i]];
+        if (m < 0 || c->slot_gen[slots[i]] != c->marks[m].gen || c->marks[m].s == s || (waited >> m & 1)) continue;
+        HIP_TRY(c, hipStreamWaitEvent(s, c->marks[m].ev, 0));
+        waited |= 1ull << m;
+    }
+    return MOE_OK;
+}
+
+// Records the next mark on s after a fill call's writes and assigns it to the
+// filled slots.
+moe_status mark_filled(moe_ctx* c, hipStream_t s, const int32_t* slots, const uint8_t* use, int32_t n) {
+    static_assert(kMarks <= 64, "order_before_fill keeps one bit per mark");
+    if (c->marks.empty()) c->marks.resize(kMarks);
+    const int32_t m = (int32_t)(c->mark_next++ % kMarks);
+    moe_ctx::Mark& k = c->marks[m];
+    if (!k.ev) HIP_TRY(c, hipEventCreateWithFlags(&k.ev, hipEventDisableTiming));
+    else HIP_TRY(c, hipEventSynchronize(k.ev));  // its previous fill is done before the entry is reused
+    HIP_TRY(c, hipEventRecord(k.ev, s));
+    k.gen++;
+    k.s = s;
+    for (int32_t i = 0; i < n; i++) {
+        if (use && !use[i]) continue;
+        c->slot_mark[slots[i]] = m;
+        c->slot_gen[slots[i]] = k.gen;
+    }
+    return MOE_OK;
+}
+
 moe_status wait_pending_fills(moe_ctx* c, hipStream_t s) {
     for (auto& p : c->fills) {
         if (p.pending && p.s != s) HIP_TRY(c, hipStreamWaitEvent(s, p.ev, 0));
@@ -234,6 +317,8 @@ void moe_destroy(moe_ctx* c) {
         if (c->logits_ws) (void)hipFree(c->logits_ws);
         if (c->release_ev) (void)hipEventDestroy(c->release_ev);
         for (auto& p : c->fills) (void)hipEventDestroy(p.ev);
+        for (auto& m : c->marks)
+            if (m.ev) (void)hipEventDestroy(m.ev);
     }
     delete c;
 }
@@ -257,6 +342,8 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     c->pin_layer.assign(cfg->n_slots, -1);
     c->evicted.assign(cfg->n_slots, -1);
     c->spec.assign(cfg->n_slots, 0);
+    c->slot_mark.assign(cfg->n_slots, -1);
+    c->slot_gen.assign(cfg->n_slots, 0);
     if (!c->host_only) {
         DeviceGuard dg(cfg->device);
         auto cleanup = [&](moe_status st) { moe_destroy(c); return st; };
@@ -392,10 +479,10 @@ moe_status moe_slot_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32
         } else {
             int32_t pick = -1;
             for (int q = 0; q < cf.n_slots; q++) if (c->owner[q] < 0) { pick = q; break; }
-            if (pick < 0) {
+            if (pick < 0) {  // never a slot holding one of this step's experts
                 uint64_t best = UINT64_MAX;
                 for (int q = 0; q < cf.n_slots; q++)
-                    if (c->pin_layer[q] < 0 && c->last[q] < best) { best = c->last[q]; pick = q; }
+                    if (c->pin_layer[q] < 0 && !is_hit_slot[q] && c->last[q] < best) { best = c->last[q]; pick = q; }
                 c->slot_of[c->owner[pick]] = -1;
                 c->evicted[pick] = c->owner[pick];
                 c->stats[3]++;
@@ -492,7 +579,7 @@ moe_status moe_slot_fill(moe_ctx* c, int32_t layer, int32_t expert, int32_t slot
     if (c->owner[slot] != key) return fail(c, MOE_EINVAL, "moe_slot_fill: slot %d is not mapped to (layer %d, expert %d)", slot, layer, expert);
     DeviceGuard dg(cf.device);
     hipStream_t s = (hipStream_t)side;
-    if (c->release_recorded) HIP_TRY(c, hipStreamWaitEvent(s, c->release_ev, 0));
+    if (moe_status st = order_before_fill(c, s, &slot, nullptr, 1)) return st;
     if (c->evicted[slot] >= 0) {
         HIP_TRY(c, hipMemsetD32Async((hipDeviceptr_t)(c->pt + c->evicted[slot]), -1, 1, s));
         c->evicted[slot] = -1;
@@ -500,17 +587,146 @@ moe_status moe_slot_fill(moe_ctx* c, int32_t layer, int32_t expert, int32_t slot
     uint8_t* dst = (uint8_t*)cf.slot_pool + (size_t)slot * (size_t)c->g.payload;
     HIP_TRY(c, hipMemcpyAsync(dst, host_payload, (size_t)c->g.payload, hipMemcpyHostToDevice, s));
     HIP_TRY(c, hipMemsetD32Async((hipDeviceptr_t)(c->pt + key), slot, 1, s));
+    if (moe_status st = mark_filled(c, s, &slot, nullptr, 1)) return st;
     moe_ctx::Pending* p = nullptr;
-    for (auto& q : c->fills) if (q.s == s) p = &q;
-    if (!p) {
-        hipEvent_t ev;
-        HIP_TRY(c, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
-        c->fills.push_back({s, ev, false});
-        p = &c->fills.back();
-    }
+    if (moe_status st = fill_event(c, s, &p)) return st;
     HIP_TRY(c, hipEventRecord(p->ev, s));
     p->pending = true;
     c->stats[4]++;
+    return MOE_OK;
+}
+
+moe_status moe_slot_stage(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n,
+                          const void* const* host_payloads, int32_t* slots_out, uint8_t* miss_out,
+                          const moe_stream* sides, int32_t n_sides) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (!host_payloads || !sides || n_sides < 1 || n_sides > MOE_MAX_STAGE_STREAMS)
+        return fail(c, MOE_EINVAL, "moe_slot_stage: null payload table or stream list, or n_sides not in 1..%d",
+                    MOE_MAX_STAGE_STREAMS);
+    if ((int64_t)cf.n_layers * cf.n_experts > INT32_MAX) return fail(c, MOE_EINVAL, "moe_slot_stage: page table too large");
+    if (layer >= 0 && layer < cf.n_layers && n > 0 && experts) {
+        // a miss without a payload is refused before anything is mapped
+        const int64_t base = (int64_t)layer * cf.n_experts;
+        for (int32_t i = 0; i < n; i++)
+            if (experts[i] >= 0 && experts[i] < cf.n_experts && c->slot_of[base + experts[i]] < 0 &&
+                !host_payloads[experts[i]])
+                return fail(c, MOE_EINVAL, "moe_slot_stage: expert %d misses but has no payload", experts[i]);
+    }
+    if (moe_status st = moe_slot_map(c, layer, experts, n, slots_out, miss_out)) return st;
+    int n_miss = 0;
+    for (int32_t i = 0; i < n; i++) n_miss += miss_out[i];
+    if (!n_miss) return MOE_OK;
+    DeviceGuard dg(cf.device);
+    const int used = std::min<int>(n_sides, n_miss);
+    for (int j = 0; j < used; j++)
+        if (moe_status st = order_before_fill(c, (hipStream_t)sides[j], slots_out, miss_out, n)) return st;
+    const int64_t base = (int64_t)layer * cf.n_experts;
+    int q = 0;
+    for (int32_t i = 0; i < n; i++) {
+        if (!miss_out[i]) continue;
+        uint8_t* dst = (uint8_t*)cf.slot_pool + (size_t)slots_out[i] * (size_t)c->g.payload;
+        HIP_TRY(c, hipMemcpyAsync(dst, host_payloads[experts[i]], (size_t)c->g.payload, hipMemcpyHostToDevice,
+                                  (hipStream_t)sides[q++ % used]));
+    }
+    hipStream_t s0 = (hipStream_t)sides[0];
+    for (int j = 1; j < used; j++) {  // the first stream writes the page table after every copy
+        moe_ctx::Pending* p = nullptr;
+        if (moe_status st = fill_event(c, (hipStream_t)sides[j], &p)) return st;
+        HIP_TRY(c, hipEventRecord(p->ev, (hipStream_t)sides[j]));
+        HIP_TRY(c, hipStreamWaitEvent(s0, p->ev, 0));
+    }
+    moe::PtWrites w{};
+    auto put = [&](int64_t idx, int32_t val) -> moe_status {
+        if (w.n == moe::kPtBatch) {
+            HIP_TRY(c, moe::launch_pt_write(c->pt, w, s0));
+            w.n = 0;
+        }
+        w.idx[w.n] = (int32_t)idx;
+        w.val[w.n++] = val;
+        return MOE_OK;
+    };
+    for (int32_t i = 0; i < n; i++) {
+        if (!miss_out[i]) continue;
+        const int32_t sl = slots_out[i];
+        if (c->evicted[sl] >= 0) {
+            if (moe_status st = put(c->evicted[sl], -1)) return st;
+            c->evicted[sl] = -1;
+        }
+        if (moe_status st = put(base + experts[i], sl)) return st;
+    }
+    HIP_TRY(c, moe::launch_pt_write(c->pt, w, s0));
+    if (moe_status st = mark_filled(c, s0, slots_out, miss_out, n)) return st;
+    moe_ctx::Pending* p = nullptr;
+    if (moe_status st = fill_event(c, s0, &p)) return st;
+    HIP_TRY(c, hipEventRecord(p->ev, s0));
+    p->pending = true;
+    c->stats[4] += (uint64_t)n_miss;
+    return MOE_OK;
+}
+
+moe_status moe_slot_pull(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n,
+                         const void* const* payloads, int32_t* slots_out, uint8_t* miss_out, moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (!payloads) return fail(c, MOE_EINVAL, "moe_slot_pull: null payload table");
+    if ((int64_t)cf.n_layers * cf.n_experts > INT32_MAX || c->g.payload % 16 ||
+        (uint64_t)moe::kPullMax * (c->g.payload / 16) > 0x7FFFFFFFull)
+        return fail(c, MOE_EINVAL, "moe_slot_pull: page table or payload size out of range");
+    // every payload a miss will read must be addressable by a kernel; checked
+    // before anything is mapped
+    std::vector<const uint4*> src(std::max<int32_t>(n, 0), nullptr);
+    if (layer >= 0 && layer < cf.n_layers && n > 0 && n <= cf.n_experts && experts) {
+        const int64_t base = (int64_t)layer * cf.n_experts;
+        for (int32_t i = 0; i < n; i++) {
+            const int32_t e = experts[i];
+            if (e < 0 || e >= cf.n_experts || c->slot_of[base + e] >= 0) continue;
+            const void* dv = nullptr;
+            if (!payloads[e] || !device_view(payloads[e], &dv))
+                return fail(c, MOE_EINVAL, "moe_slot_pull: payload of expert %d is not pinned host or device memory", e);
+            src[i] = (const uint4*)dv;
+        }
+    }
+    if (moe_status st = moe_slot_map(c, layer, experts, n, slots_out, miss_out)) return st;
+    int n_miss = 0;
+    for (int32_t i = 0; i < n; i++) n_miss += miss_out[i];
+    if (!n_miss) return MOE_OK;
+    DeviceGuard dg(cf.device);
+    hipStream_t s = (hipStream_t)stream;
+    if (moe_status st = order_before_fill(c, s, slots_out, miss_out, n)) return st;
+    const int64_t base = (int64_t)layer * cf.n_experts;
+    moe::PullArgs a{};
+    moe::PtWrites w{};
+    a.words = (uint32_t)(c->g.payload / 16);
+    auto flush = [&]() -> moe_status {
+        HIP_TRY(c, moe::launch_pull(a, c->pt, w, s));
+        a.n = 0;
+        w.n = 0;
+        return MOE_OK;
+    };
+    for (int32_t i = 0; i < n; i++) {
+        if (!miss_out[i]) continue;
+        const int32_t sl = slots_out[i];
+        a.src[a.n] = src[i];
+        a.dst[a.n++] = (uint4*)((uint8_t*)cf.slot_pool + (size_t)sl * (size_t)c->g.payload);
+        if (c->evicted[sl] >= 0) {
+            w.idx[w.n] = (int32_t)c->evicted[sl];
+            w.val[w.n++] = -1;
+            c->evicted[sl] = -1;
+        }
+        w.idx[w.n] = (int32_t)(base + experts[i]);
+        w.val[w.n++] = sl;
+        if (a.n == moe::kPullMax)
+            if (moe_status st = flush()) return st;
+    }
+    if (a.n)
+        if (moe_status st = flush()) return st;
+    if (moe_status st = mark_filled(c, s, slots_out, miss_out, n)) return st;
+    moe_ctx::Pending* p = nullptr;
+    if (moe_status st = fill_event(c, s, &p)) return st;
+    HIP_TRY(c, hipEventRecord(p->ev, s));
+    p->pending = true;
+    c->stats[4] += (uint64_t)n_miss;
     return MOE_OK;
 }
 
@@ -523,6 +739,7 @@ moe_status moe_slot_release(moe_ctx* c, int32_t layer, moe_stream compute) {
         DeviceGuard dg(cf.device);
         HIP_TRY(c, hipEventRecord(c->release_ev, (hipStream_t)compute));
         c->release_recorded = true;
+        c->release_stream = (hipStream_t)compute;
     }
     return MOE_OK;
 }
@@ -698,7 +915,9 @@ moe_status moe_check(moe_ctx* c, moe_stream stream) {
 
 moe_status moe_probe_read(const void* src, int64_t bytes, int32_t workgroups, uint32_t* sink, moe_stream stream) {
     if (!src || !sink || bytes <= 0 || bytes % 16 || workgroups < 0) return MOE_EINVAL;
-    return moe::launch_probe_read(src, bytes, workgroups, sink, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_EHIP;
+    const void* dsrc = nullptr;
+    if (!device_view(src, &dsrc)) return MOE_EINVAL;
+    return moe::launch_probe_read(dsrc, bytes, workgroups, sink, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 moe_status moe_probe_mfma(int32_t iters, int32_t grid, int32_t shape, float* sink, int64_t* flops, moe_stream stream) {

@@ -21,6 +21,7 @@ MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ENOSLOT, MOE_EMISS, MOE_EBUSY, MOE
 MOE_Q8_0, MOE_Q4_0 = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
 MOE_PREC_F32, MOE_PREC_BF16 = 0, 1
+MOE_MAX_STAGE_STREAMS = 8
 
 
 class MoeError(RuntimeError):
@@ -67,6 +68,8 @@ def _load() -> C.CDLL:
         "moe_route_union": (C.c_int, [P, P, C.c_int32, P, P, I64, P, P, P, planp, P]),
         "moe_slot_map": (C.c_int, [P, I32, P, I32, P, P]),
         "moe_slot_fill": (C.c_int, [P, I32, I32, I32, P, P]),
+        "moe_slot_stage": (C.c_int, [P, I32, P, I32, P, P, P, P, I32]),
+        "moe_slot_pull": (C.c_int, [P, I32, P, I32, P, P, P, P]),
         "moe_slot_prefetch": (C.c_int, [P, I32, P, I32, I64, P, P, P]),
         "moe_prefetch_stats": (C.c_int, [P, C.POINTER(C.c_uint64)]),
         "moe_slot_release": (C.c_int, [P, I32, P]),
@@ -90,7 +93,7 @@ def _load() -> C.CDLL:
 _lib = _load()
 EXPORTS = ("moe_payload_bytes", "moe_plan_bytes", "moe_pack_expert", "moe_unpack_expert", "moe_create",
            "moe_destroy", "moe_last_error", "moe_status_string", "moe_route", "moe_plan_union", "moe_route_union",
-           "moe_slot_map", "moe_slot_prefetch", "moe_prefetch_stats", "moe_slot_fill", "moe_slot_release",
+           "moe_slot_map", "moe_slot_prefetch", "moe_prefetch_stats", "moe_slot_fill", "moe_slot_stage", "moe_slot_pull", "moe_slot_release",
            "moe_slot_bind", "moe_expert_ffn",
            "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table", "moe_probe_read",
            "moe_probe_mfma")
@@ -241,14 +244,22 @@ class Plan:
         self._pinned = torch.empty(1 + E, dtype=torch.int32).pin_memory()
         self.c = moe_plan(_ptr(self.n_active), _ptr(self.experts), _ptr(self.offsets), _ptr(self.entries))
 
-    def experts_host(self, stream=None):
+    def experts_host(self, stream=None, spin=False):
         """(n_active, experts[:n_active]) with one copy into pinned memory, after
-        the work enqueued on `stream` (default: the current stream)."""
+        the work enqueued on `stream` (default: the current stream).  spin: poll
+        an event for the copy instead of a blocking synchronise."""
         import torch
         st = stream or torch.cuda.current_stream(self._buf.device)
         with torch.cuda.stream(st):
             self._pinned.copy_(self._head, non_blocking=True)
-        st.synchronize()
+        if spin:
+            if not hasattr(self, "_ev"):
+                self._ev = torch.cuda.Event()
+            self._ev.record(st)
+            while not self._ev.query():
+                pass
+        else:
+            st.synchronize()
         h = self._pinned.numpy()
         n = int(h[0])
         return n, h[1:1 + n].copy()
@@ -343,6 +354,50 @@ def moe_slot_fill(ctx: Context, layer: int, expert: int, slot: int, host_payload
     if host_payload.numel() * host_payload.element_size() < ctx.payload_bytes:
         raise ValueError("host payload too small")
     _call(ctx, _lib.moe_slot_fill(ctx.handle, layer, expert, slot, _ptr(host_payload), _stream(stream)))
+
+
+def payload_table(ctx: Context, payloads) -> np.ndarray:
+    """Addresses (int64 [n_experts]) of uint8 payload tensors indexed by expert
+    id (None: never staged) for moe_slot_stage (pinned host tensors) or
+    moe_slot_pull (pinned host or CUDA tensors)."""
+    t = np.zeros(ctx.n_experts, dtype=np.int64)
+    for e, p in enumerate(payloads):
+        if p is None:
+            continue
+        if not (p.is_pinned() or p.is_cuda) or p.numel() * p.element_size() < ctx.payload_bytes:
+            raise ValueError(f"payload of expert {e}: not pinned (or on the GPU), or too small")
+        t[e] = _ptr(p)
+    return t
+
+
+def _table(ctx, table):
+    if table.dtype != np.int64 or table.size != ctx.n_experts or not table.flags.c_contiguous:
+        raise ValueError("table: int64 [n_experts] from payload_table")
+
+
+def moe_slot_stage(ctx: Context, layer: int, experts, table: np.ndarray, streams) -> tuple:
+    """moe_slot_map plus the fills of its misses from `table` (payload_table),
+    the copies alternating over `streams`; returns (slots, miss)."""
+    e = np.ascontiguousarray(experts, dtype=np.int32).reshape(-1)
+    _table(ctx, table)
+    slots = np.empty(e.size, dtype=np.int32)
+    miss = np.empty(e.size, dtype=np.uint8)
+    st = (C.c_void_p * max(1, len(streams)))(*[_stream(x) for x in streams])
+    _call(ctx, _lib.moe_slot_stage(ctx.handle, layer, e.ctypes.data, e.size, table.ctypes.data, slots.ctypes.data,
+                                   miss.ctypes.data, st, len(streams)))
+    return slots, miss.astype(bool)
+
+
+def moe_slot_pull(ctx: Context, layer: int, experts, table: np.ndarray, stream=None) -> tuple:
+    """moe_slot_map, then kernels on `stream` copy the misses from `table`
+    (payload_table) into their slots; returns (slots, miss)."""
+    e = np.ascontiguousarray(experts, dtype=np.int32).reshape(-1)
+    _table(ctx, table)
+    slots = np.empty(e.size, dtype=np.int32)
+    miss = np.empty(e.size, dtype=np.uint8)
+    _call(ctx, _lib.moe_slot_pull(ctx.handle, layer, e.ctypes.data, e.size, table.ctypes.data, slots.ctypes.data,
+                                  miss.ctypes.data, _stream(stream)))
+    return slots, miss.astype(bool)
 
 
 def moe_slot_release(ctx: Context, layer: int, stream=None) -> None:

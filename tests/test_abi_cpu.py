@@ -76,6 +76,20 @@ def test_slot_manager_matches_lru_model_on_markov_trace():
         assert st["bytes_staged"] == st["misses"] * ctx.payload_bytes
 
 
+def test_slot_manager_keeps_the_steps_own_experts():
+    """The least recently touched slot holds an expert that the same step lists
+    later: the library, like the model, evicts the next one instead."""
+    ctx = _host_ctx(1, 16, 3)
+    model = LruModel(3, ctx.payload_bytes)
+    for ex in ([1, 2, 3], [0, 1], [1, 3, 4], [2, 5, 6]):
+        slots, miss = moe.moe_slot_map(ctx, 0, ex)
+        ms, mm, _ = model.map(0, ex)
+        assert list(slots) == ms and list(miss) == mm
+        moe.moe_slot_release(ctx, 0)
+        model.release(0)
+    assert moe.moe_stats(ctx)["misses"] == model.counters()["misses"] == 8
+
+
 def test_slot_manager_refuses_when_pinned_full():
     ctx = _host_ctx(2, 16, 3)
     moe.moe_slot_map(ctx, 0, [1, 2, 3])
@@ -104,6 +118,8 @@ def test_host_only_context_rejects_device_calls():
     assert lib.moe_route(ctx.handle, None, 0, None, None, 1, None, None, None, None) == moe.MOE_EINVAL
     assert lib.moe_check(ctx.handle, None) == moe.MOE_EINVAL
     assert lib.moe_slot_fill(ctx.handle, 0, 0, 0, None, None) == moe.MOE_EINVAL
+    assert lib.moe_slot_stage(ctx.handle, 0, None, 0, None, None, None, None, 0) == moe.MOE_EINVAL
+    assert lib.moe_slot_pull(ctx.handle, 0, None, 0, None, None, None, None) == moe.MOE_EINVAL
     assert lib.moe_dequant(ctx.handle, None, 0, None, None) == moe.MOE_EINVAL
     assert lib.moe_route_ffn(ctx.handle, 0, None, 0, None, None, 1, None, None, None, None, 0, None,
                              None) == moe.MOE_EINVAL

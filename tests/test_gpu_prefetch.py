@@ -18,7 +18,10 @@ if not H.gpu_available():  # pragma: no cover
 from routed_expert_execution_amd import moe  # noqa: E402
 
 
-def _run_stack(prefetch: bool, L=3, n_tok=6, n_slots=24):
+def _run_stack(prefetch: bool, L=3, n_tok=6, n_slots=24, stage_streams=0, pull=False):
+    """stage_streams 0: moe_slot_map + one moe_slot_fill per miss; else one
+    moe_slot_stage per layer over that many side streams.  pull: one
+    moe_slot_pull per layer on the compute stream instead."""
     wl = synth.workload("stack40")
     E, k, d, f = wl["E"], wl["k"], wl["d"], wl["f"]
     ctx = H.make_ctx(wl, n_slots=n_slots, max_tokens=1, n_layers=L)
@@ -34,6 +37,7 @@ def _run_stack(prefetch: bool, L=3, n_tok=6, n_slots=24):
     shared = synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True)
     sh_dev = H.device_payload(ctx, shared)
     side = torch.cuda.Stream()
+    sides = [side] + [torch.cuda.Stream() for _ in range(stage_streams - 1)]
     plan = moe.Plan(ctx, 1)
     outs = []
     for t in range(n_tok):
@@ -43,11 +47,19 @@ def _run_stack(prefetch: bool, L=3, n_tok=6, n_slots=24):
             ids = torch.empty(1, k, dtype=torch.int32, device="cuda")
             w = torch.empty(1, k, dtype=torch.float32, device="cuda")
             moe.moe_route_union(ctx, ids, w, plan, logits_in=torch.from_numpy(lg).cuda())
-            n, ex, _, _ = plan.host()
-            slots, miss = moe.moe_slot_map(ctx, l, ex)
-            for e, s_, m in zip(ex, slots, miss):
-                if m:
-                    moe.moe_slot_fill(ctx, l, int(e), int(s_), payload(l, int(e)), stream=side)
+            if stage_streams or pull:
+                n, ex = plan.experts_host()
+                table = moe.payload_table(ctx, [payload(l, e) if e in set(ex.tolist()) else None for e in range(E)])
+                if pull:
+                    moe.moe_slot_pull(ctx, l, ex, table)
+                else:
+                    moe.moe_slot_stage(ctx, l, ex, table, sides)
+            else:
+                n, ex, _, _ = plan.host()
+                slots, miss = moe.moe_slot_map(ctx, l, ex)
+                for e, s_, m in zip(ex, slots, miss):
+                    if m:
+                        moe.moe_slot_fill(ctx, l, int(e), int(s_), payload(l, int(e)), stream=side)
             if prefetch and l + 1 < L and t > 0:
                 # predict layer l + 1 from its previous token's experts, cap: 3 payloads
                 pred = list(chains[l + 1][t - 1])
@@ -61,12 +73,12 @@ def _run_stack(prefetch: bool, L=3, n_tok=6, n_slots=24):
             moe.moe_slot_release(ctx, l)
             outs.append((l, t, x, ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy()))
     assert moe.moe_check(ctx) == moe.MOE_OK
-    return outs, moe.moe_stats(ctx), moe.moe_prefetch_stats(ctx), host, shared
+    return outs, moe.moe_stats(ctx), moe.moe_prefetch_stats(ctx), host, shared, moe.moe_page_table(ctx)
 
 
 def test_prefetch_is_transparent_and_counted():
-    base, st0, ps0, _, _ = _run_stack(False)
-    pre, st1, ps1, host, shared = _run_stack(True)
+    base, st0, ps0, _, _, _ = _run_stack(False)
+    pre, st1, ps1, host, shared, _ = _run_stack(True)
     assert ps0["fills"] == 0 and ps1["fills"] > 0
     assert ps1["useful"] + ps1["wasted"] <= ps1["fills"]
     assert st1["fills"] == st1["misses"] + ps1["fills"]

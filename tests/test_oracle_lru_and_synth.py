@@ -52,6 +52,19 @@ def test_lru_hand_worked_example():
     assert m.counters() == dict(hits=1, misses=5, bytes_staged=50, evictions=2)
 
 
+def test_lru_never_evicts_an_expert_of_the_same_step():
+    """3 slots holding experts 1, 2, 3 (stamps 1, 2, 3), all released.  Step [0, 1]:
+    0 misses first, and the least recently touched slot is slot 0, but slot 0 holds
+    expert 1, which the same step needs: the layer runs with all of its experts
+    resident ('Paging the Experts', Section 3.2), so the victim is slot 1 (expert 2)
+    and 1 is a hit.  One miss, not two."""
+    m = LruModel(3, 10)
+    m.map(0, [1, 2, 3])
+    m.release(0)
+    assert m.map(0, [0, 1]) == ([1, 0], [True, False], [(0, 2), None])
+    assert m.counters() == dict(hits=1, misses=4, bytes_staged=40, evictions=1)
+
+
 def test_mtp_union_size_statistics():
     """Union of the 4-token window: about 19.5 distinct experts per step on average."""
     wl = synth.workload("mtp")
