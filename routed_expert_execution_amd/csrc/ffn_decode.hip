@@ -464,12 +464,13 @@ __device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int wg, unsigned 
     // ranges, entries) or the caller's logits, the page-table row and, for one
     // token, its activations.
     const uint32_t count = __hip_atomic_load(a.sync + kSyncCount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // router rows go to the first workgroups in dispatch order (one each on as
+    // many CUs as there are rows; later workgroups share CUs with the down
+    // workgroups and start later), the shared expert's included; with one token
+    // and at most one row per wave, against the activations this workgroup
+    // stages in LDS anyway (exact values: bf16 input, or fp32 kept in fp32)
     const int S = has_shared ? g.n_rg / RG : 0;  // items of the shared expert
-    // router rows go to the workgroups whose first item is routed (all of them
-    // if there are no such workgroups); with one token and at most one row per
-    // wave, against the activations this workgroup stages in LDS anyway (exact
-    // values: bf16 input, or fp32 kept in fp32)
-    const int h0 = g.n_gu_wg > S ? S : 0, H = g.n_gu_wg - h0;
+    const int h0 = 0, H = g.n_gu_wg;
     const bool rows_here = a.route == kRouteRouter && wg >= h0;
     constexpr bool kOneToken = TG == 1;
     const bool rows_lds = kOneToken && (a.x_bf16 || PREC == MOE_PREC_F32) && H * kWaves >= a.E && g.d <= 2048;
