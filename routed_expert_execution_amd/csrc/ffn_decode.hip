@@ -453,7 +453,7 @@ struct GuLds {
 // (they need no routing, so a launch that routes starts them at once), then
 // those of the routed units in plan order.
 template <int QT, int PREC, int TG, int RG, int PPW>
-__device__ void gate_up_role(const FfnArgs& a, const DGrid& g, int wg, unsigned char* lds_raw) {
+__device__ __forceinline__ void gate_up_role(const FfnArgs& a, const DGrid& g, int wg, unsigned char* lds_raw) {
     GuLds<TG, RG>& L = *(GuLds<TG, RG>*)lds_raw;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, jb = lane >> 4;
@@ -639,7 +639,7 @@ struct DownLds {
 };
 
 template <int QT, int PREC, int TG, int DPW>
-__device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char* lds_raw) {
+__device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char* lds_raw) {
     DownLds& L = *(DownLds*)lds_raw;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, jb = lane >> 4;
@@ -827,16 +827,33 @@ __device__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char
                     for (int q = 0; q < TG; q++) acc[q] += tk == q ? dw : 0.f;
                 }
             } else {
-                // one row at a time: four rows' dequantised codes do not fit
-                // beside DPW tiles in registers
-                for (int v = v0; v < v1; v++) {
-                    const float* hv1[1] = {L.hs + (v - va) * g.f + (4 * scol[i] + jb) * kQK};
-                    float d1[1][1];
-                    tile_dots<QT, PREC, 1, 1, 4>(one, hv1, d1);
-                    const int tk = (stok[i] >> (2 * (v - sv0[i]))) & 3;
-                    const float dw = L.w[v] * d1[0][0];
+                // the unit's rows two at a time, each block dequantised once per
+                // pair (a last odd row alone): two pairs' activations in chunks
+                // of 4 codes stay beside DPW tiles in registers
+                for (int r = v0; r < v1; r += 2) {
+                    float dr[2];
+                    const float* h0p = L.hs + (r - va) * g.f + (4 * scol[i] + jb) * kQK;
+                    if (r + 1 < v1) {
+                        const float* h2[2] = {h0p, h0p + g.f};
+                        float d[1][2];
+                        tile_dots<QT, PREC, 1, 2, 2, 4>(one, h2, d);
+                        dr[0] = d[0][0];
+                        dr[1] = d[0][1];
+                    } else {
+                        const float* h1[1] = {h0p};
+                        float d[1][1];
+                        tile_dots<QT, PREC, 1, 1, 4>(one, h1, d);
+                        dr[0] = d[0][0];
+                    }
 #pragma unroll
-                    for (int q = 0; q < TG; q++) acc[q] += tk == q ? dw : 0.f;
+                    for (int j = 0; j < 2; j++) {
+                        const int v = r + j;
+                        if (v >= v1) break;
+                        const int tk = (stok[i] >> (2 * (v - sv0[i]))) & 3;
+                        const float dw = L.w[v] * dr[j];
+#pragma unroll
+                        for (int q = 0; q < TG; q++) acc[q] += tk == q ? dw : 0.f;
+                    }
                 }
             }
         }
@@ -949,9 +966,10 @@ hipError_t launch_k(DGrid g, const FfnArgs& a, hipStream_t s) {
 
 // Down tiles held in registers per wave: every tile of the step's units in the
 // usual cases with d_ff 512 (top-8: 9 units at T = 1; at T = 2, 6 (Q8_0) or
-// 12 (Q4_0); at T = 4, 6 (Q8_0) or 20 (Q4_0)); more are loaded after the wait.
+// 12 (Q4_0); at T = 4, 6 (Q8_0)); more are loaded after the wait.  Four Q4_0
+// tokens (about 20 units) keep 8, so that two rows' activations fit beside them.
 template <int QT, int TG> constexpr int down_per_wave() {
-    return TG == 1 ? 5 : QT == MOE_Q4_0 ? (TG == 2 ? 6 : 10) : 3;
+    return TG == 1 ? 5 : QT == MOE_Q4_0 ? (TG == 2 ? 6 : 8) : 3;
 }
 
 template <int QT, int PREC, int TG>
