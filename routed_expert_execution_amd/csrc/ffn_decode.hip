@@ -683,6 +683,13 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         if (!plan_from_logits(a, g, par, g.n_gu_wg + R, P, R == 0) && threadIdx.x == 0) L.flag[0] = 0;
         na = min(L.na, na_max);
     }
+    // The arrivals of this launch's gate/up workgroups, read now (they arrive
+    // as they start, long before this) and checked at the end, so that the end
+    // does not wait for a round trip.
+    const uint32_t arrived0 = a.route == kRouteRouter && threadIdx.x == 0
+                                  ? __hip_atomic_load(a.sync + kSyncArrive + par, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                                  : 0u;
     // This workgroup's share of the other half back to pending for the next
     // launch (no one uses that half during this one).
     {
@@ -896,7 +903,7 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
     // This launch is done with its half: count it (no return needed), once every
     // gate/up workgroup of a launch that routes has arrived.
     if (threadIdx.x == 0) {
-        if (a.route == kRouteRouter) {
+        if (a.route == kRouteRouter && (a.wait_ticks < 0 || arrived0 < (uint32_t)g.n_gu_wg)) {
             const uint64_t t1 = wall_clock64();
             while (a.wait_ticks < 0 ||
                    __hip_atomic_load(a.sync + kSyncArrive + par, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
