@@ -656,17 +656,30 @@ hipError_t launch_items(K kernel, int64_t items, const PrefillArgs& a, hipStream
 }
 
 template <int QT, int PREC, bool XB>
-hipError_t launch_qp(const PrefillArgs& a, int big_tiles, int small_tiles, hipStream_t s) {
+hipError_t launch_qp(const PrefillArgs& a, int big_tiles, int small_tiles, const PrefillStreams& st) {
+    const hipStream_t s = st.s;
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, s, a, PREC);
     hipError_t e = hipGetLastError();
     const int gf = (a.f + COLS - 1) / COLS, gd = a.d / COLS;
     constexpr bool BF = PREC == MOE_PREC_BF16;  // 64-token tiles only in bf16 mode
-    if constexpr (BF)
-        if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, true>, (int64_t)big_tiles * gf, a, s);
-    if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, false>, (int64_t)small_tiles * gf, a, s);
-    if constexpr (BF)
-        if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, true>, (int64_t)big_tiles * gd, a, s);
-    if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, false>, (int64_t)small_tiles * gd, a, s);
+    if constexpr (BF) {
+        // The two tile sizes are independent chains (disjoint buckets: their own
+        // hidden and partial rows): the 64-token one on the auxiliary stream, so
+        // that the two share the GPU instead of running one after the other.
+        const bool two = st.aux != nullptr && big_tiles > 0;
+        const hipStream_t sb = two ? st.aux : s;
+        if (two && e == hipSuccess) e = hipEventRecord(st.fork, s);
+        if (two && e == hipSuccess) e = hipStreamWaitEvent(sb, st.fork, 0);
+        if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, true>, (int64_t)big_tiles * gf, a, sb);
+        if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, true>, (int64_t)big_tiles * gd, a, sb);
+        if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, false>, (int64_t)small_tiles * gf, a, s);
+        if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, false>, (int64_t)small_tiles * gd, a, s);
+        if (two && e == hipSuccess) e = hipEventRecord(st.join, sb);
+        if (two && e == hipSuccess) e = hipStreamWaitEvent(s, st.join, 0);
+    } else {
+        if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, false>, (int64_t)small_tiles * gf, a, s);
+        if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, false>, (int64_t)small_tiles * gd, a, s);
+    }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prefill_combine_kernel, dim3((a.d / 4 + 255) / 256, a.T), dim3(256), 0, s, a);
     return hipGetLastError();
@@ -681,7 +694,7 @@ void prefill_max_tiles(int64_t T, int k, int E, bool shared, int* big_tiles, int
     *small_tiles = (int)((rows + SMALL - 1) / SMALL + units);
 }
 
-hipError_t launch_ffn_prefill(const PrefillArgs& a, int prec, hipStream_t s) {
+hipError_t launch_ffn_prefill(const PrefillArgs& a, int prec, const PrefillStreams& s) {
     if (a.d % COLS || a.f % 16) return hipErrorInvalidValue;
     int bt, st;
     prefill_max_tiles(a.T, a.k, a.E, a.shared != nullptr, &bt, &st);

@@ -181,7 +181,15 @@ struct PrefillArgs {
 
 // Upper bounds on the tiles of each size a call of T tokens can need.
 void prefill_max_tiles(int64_t T, int k, int E, bool shared, int* big_tiles, int* small_tiles);
-hipError_t launch_ffn_prefill(const PrefillArgs& a, int prec, hipStream_t s);
+// Streams of a prefill call: the caller's, and an auxiliary one (null: all on
+// s) on which the 64-token tile chain runs beside the 16-token one, forked
+// from and joined back into s with the two events.
+struct PrefillStreams {
+    hipStream_t s;
+    hipStream_t aux;
+    hipEvent_t fork, join;
+};
+hipError_t launch_ffn_prefill(const PrefillArgs& a, int prec, const PrefillStreams& st);
 
 // Peak references (probe.hip): a streaming read of `bytes` (a multiple of 16)
 // by `wgs` workgroups, and `iters` rounds of bf16 matrix-core products (shape 0:

@@ -47,6 +47,8 @@ struct moe_ctx {
     uint64_t pstats[4] = {0, 0, 0, 0};  // prefetch fills, useful, wasted, bytes
 
     // ordering
+    hipStream_t aux = nullptr;        // prefill: the 64-token tile chain beside the caller's stream
+    hipEvent_t fork_ev = nullptr, join_ev = nullptr;
     hipEvent_t release_ev = nullptr;  // last moe_slot_release point on the compute stream
     bool release_recorded = false;
     hipStream_t release_stream = nullptr;  // the stream release_ev was last recorded on
@@ -316,6 +318,9 @@ void moe_destroy(moe_ctx* c) {
         if (c->psched) (void)hipFree(c->psched);
         if (c->logits_ws) (void)hipFree(c->logits_ws);
         if (c->release_ev) (void)hipEventDestroy(c->release_ev);
+        if (c->fork_ev) (void)hipEventDestroy(c->fork_ev);
+        if (c->join_ev) (void)hipEventDestroy(c->join_ev);
+        if (c->aux) (void)hipStreamDestroy(c->aux);
         for (auto& p : c->fills) (void)hipEventDestroy(p.ev);
         for (auto& m : c->marks)
             if (m.ev) (void)hipEventDestroy(m.ev);
@@ -372,6 +377,11 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         if (hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff, cfg->n_experts)) != hipSuccess)
             return cleanup(MOE_EHIP);
         if (hipEventCreateWithFlags(&c->release_ev, hipEventDisableTiming) != hipSuccess) return cleanup(MOE_EHIP);
+        // default priority (as every stream of the library)
+        if (hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&c->fork_ev, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&c->join_ev, hipEventDisableTiming) != hipSuccess)
+            return cleanup(MOE_EHIP);
         if (hipDeviceSynchronize() != hipSuccess) return cleanup(MOE_EHIP);
     }
     *out = c;
@@ -841,7 +851,7 @@ moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     p.n_tiles = p.sched_small + 4 * (size_t)c->p_small;
     p.y = y;
     p.err = c->err_word;
-    HIP_TRY(c, moe::launch_ffn_prefill(p, prec, s));
+    HIP_TRY(c, moe::launch_ffn_prefill(p, prec, moe::PrefillStreams{s, c->aux, c->fork_ev, c->join_ev}));
     return MOE_OK;
 }
 
