@@ -52,14 +52,24 @@ struct moe_ctx {
     hipEvent_t release_ev = nullptr;  // last moe_slot_release point on the compute stream
     bool release_recorded = false;
     hipStream_t release_stream = nullptr;  // the stream release_ev was last recorded on
-    struct Pending { hipStream_t s; hipEvent_t ev; bool pending; };
-    std::vector<Pending> fills;       // one re-recorded event per side stream
+    // One re-recorded event per stream and kind of fill: after copy-engine
+    // copies (the default event), or after kernels (moe_slot_pull: kernels of
+    // one device fence their own memory, so the event skips the system-scope
+    // fence, a cache write-back only the host and other devices would need).
+    struct Pending { hipStream_t s; hipEvent_t ev; bool pending; bool kern; };
+    std::vector<Pending> fills;
     // Completion marks of fill calls: a ring of events, each recorded after one
     // call's writes (payloads and page-table entries); a slot remembers the mark
     // and generation of its last fill, so that a later fill of the slot on
     // another stream waits for exactly that one.  An entry is reused only after
     // its previous recording has completed, so a stale generation means done.
-    struct Mark { hipEvent_t ev = nullptr; uint64_t gen = 0; hipStream_t s = nullptr; };
+    struct Mark {
+        hipEvent_t ev = nullptr, ev_kern = nullptr;  // copy-engine fill, kernel fill (as Pending)
+        uint64_t gen = 0;
+        hipStream_t s = nullptr;
+        bool kern = false;  // which of the two was recorded last
+        hipEvent_t last() const { return kern ? ev_kern : ev; }
+    };
     std::vector<Mark> marks;
     uint32_t mark_next = 0;
     std::vector<int32_t> slot_mark;   // slot -> mark index, or -1
@@ -196,16 +206,20 @@ bool device_view(const void* p, const void** out) {
     return false;
 }
 
-// The re-recorded ready event of side stream s (created on first use).
-moe_status fill_event(moe_ctx* c, hipStream_t s, moe_ctx::Pending** out) {
+// The re-recorded ready event of stream s for fills of one kind (created on
+// first use; kern: fills written by kernels).
+unsigned fill_event_flags(bool kern) {
+    return kern ? hipEventDisableTiming | hipEventDisableSystemFence : hipEventDisableTiming;
+}
+moe_status fill_event(moe_ctx* c, hipStream_t s, moe_ctx::Pending** out, bool kern = false) {
     for (auto& q : c->fills)
-        if (q.s == s) {
+        if (q.s == s && q.kern == kern) {
             *out = &q;
             return MOE_OK;
         }
     hipEvent_t ev;
-    HIP_TRY(c, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
-    c->fills.push_back({s, ev, false});
+    HIP_TRY(c, hipEventCreateWithFlags(&ev, fill_event_flags(kern)));
+    c->fills.push_back({s, ev, false, kern});
     *out = &c->fills.back();
     return MOE_OK;
 }
@@ -222,22 +236,25 @@ moe_status order_before_fill(moe_ctx* c, hipStream_t s, const int32_t* slots, co
         if (use && !use[i]) continue;
         const int32_t m = c->slot_mark[slots[i]];
         if (m < 0 || c->slot_gen[slots[i]] != c->marks[m].gen || c->marks[m].s == s || (waited >> m & 1)) continue;
-        HIP_TRY(c, hipStreamWaitEvent(s, c->marks[m].ev, 0));
+        HIP_TRY(c, hipStreamWaitEvent(s, c->marks[m].last(), 0));
         waited |= 1ull << m;
     }
     return MOE_OK;
 }
 
-// Records the next mark on s after a fill call's writes and assigns it to the
-// filled slots.
-moe_status mark_filled(moe_ctx* c, hipStream_t s, const int32_t* slots, const uint8_t* use, int32_t n) {
+// Records the next mark on s after a fill call's writes (kern: written by
+// kernels) and assigns it to the filled slots.
+moe_status mark_filled(moe_ctx* c, hipStream_t s, const int32_t* slots, const uint8_t* use, int32_t n,
+                       bool kern = false) {
     static_assert(kMarks <= 64, "order_before_fill keeps one bit per mark");
     if (c->marks.empty()) c->marks.resize(kMarks);
     const int32_t m = (int32_t)(c->mark_next++ % kMarks);
     moe_ctx::Mark& k = c->marks[m];
-    if (!k.ev) HIP_TRY(c, hipEventCreateWithFlags(&k.ev, hipEventDisableTiming));
-    else HIP_TRY(c, hipEventSynchronize(k.ev));  // its previous fill is done before the entry is reused
-    HIP_TRY(c, hipEventRecord(k.ev, s));
+    if (k.gen) HIP_TRY(c, hipEventSynchronize(k.last()));  // its previous fill is done before the entry is reused
+    hipEvent_t& ev = kern ? k.ev_kern : k.ev;
+    if (!ev) HIP_TRY(c, hipEventCreateWithFlags(&ev, fill_event_flags(kern)));
+    HIP_TRY(c, hipEventRecord(ev, s));
+    k.kern = kern;
     k.gen++;
     k.s = s;
     for (int32_t i = 0; i < n; i++) {
@@ -322,8 +339,10 @@ void moe_destroy(moe_ctx* c) {
         if (c->join_ev) (void)hipEventDestroy(c->join_ev);
         if (c->aux) (void)hipStreamDestroy(c->aux);
         for (auto& p : c->fills) (void)hipEventDestroy(p.ev);
-        for (auto& m : c->marks)
+        for (auto& m : c->marks) {
             if (m.ev) (void)hipEventDestroy(m.ev);
+            if (m.ev_kern) (void)hipEventDestroy(m.ev_kern);
+        }
     }
     delete c;
 }
@@ -734,9 +753,9 @@ moe_status moe_slot_pull(moe_ctx* c, int32_t layer, const int32_t* experts, int3
     }
     if (a.n)
         if (moe_status st = flush()) return st;
-    if (moe_status st = mark_filled(c, s, slots_out, miss_out, n)) return st;
+    if (moe_status st = mark_filled(c, s, slots_out, miss_out, n, true)) return st;
     moe_ctx::Pending* p = nullptr;
-    if (moe_status st = fill_event(c, s, &p)) return st;
+    if (moe_status st = fill_event(c, s, &p, true)) return st;
     HIP_TRY(c, hipEventRecord(p->ev, s));
     p->pending = true;
     c->stats[4] += (uint64_t)n_miss;
