@@ -394,10 +394,17 @@ def run_stack(args, torch, moe, synth) -> int:
     def token(t, timed):
         nonlocal unique, n_fill
         for l in range(L):
-            moe.moe_route_union(ctx, ids, w, plan, logits_in=lg[l, t:t + 1])
-            n, experts = plan.experts_host(spin=args.spin_readback)  # the host learns the layer's experts only now
             ev = timed and l % 8 == 0  # kernel times on every 8th layer
-            if args.staging == "pull":  # map, then the misses copied by a kernel on the compute stream
+            if args.staging == "native":  # route, mirror, host map and pull in one library call
+                experts, slots, miss = moe.moe_route_pull(ctx, l, ids, w, plan, tables[l % n_alias],
+                                                          logits_in=lg[l, t:t + 1], stream=stream)
+                n = len(experts)
+            else:
+                moe.moe_route_union(ctx, ids, w, plan, logits_in=lg[l, t:t + 1])
+                n, experts = plan.experts_host(spin=args.spin_readback)  # the host learns the experts only now
+            if args.staging == "native":
+                pass
+            elif args.staging == "pull":  # map, then the misses copied by a kernel on the compute stream
                 if ev:
                     ep = torch.cuda.Event(enable_timing=True)
                     ep.record(stream)
@@ -430,7 +437,7 @@ def run_stack(args, torch, moe, synth) -> int:
             if ev:
                 # the FFN waits for the layer's side-stream fills anyway; waiting
                 # before the first event keeps the copies out of the kernel's time
-                if args.staging != "pull" or args.prefetch:
+                if args.staging not in ("pull", "native") or args.prefetch:
                     for sd in sides:
                         stream.wait_stream(sd)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -493,7 +500,9 @@ def run_stack(args, torch, moe, synth) -> int:
                             if args.prefetch else "")
                          + (f"; copies alternate over {args.fill_streams} side streams"
                             if args.fill_streams > 1 and args.staging != "pull" else "")
-                         + {"pull": "; one moe_slot_pull per layer: a kernel on the compute stream copies the misses",
+                         + {"native": "; one moe_route_pull per layer: routing, expert readback through pinned "
+                                      "memory, mapping and a pull kernel in one library call",
+                            "pull": "; one moe_slot_pull per layer: a kernel on the compute stream copies the misses",
                             "stage": "; one moe_slot_stage call per layer",
                             "fill": "; moe_slot_map + one moe_slot_fill per miss"}[args.staging]),
             "global_batch": 1,
@@ -548,8 +557,9 @@ def main() -> int:
                     help="stack: side streams the misses' copies alternate over")
     ap.add_argument("--spin-readback", action="store_true",
                     help="stack: poll for the plan readback instead of a blocking synchronise")
-    ap.add_argument("--staging", choices=("pull", "stage", "fill"), default="pull",
-                    help="stack: one moe_slot_pull per layer (kernel copies on the compute stream), one "
+    ap.add_argument("--staging", choices=("native", "pull", "stage", "fill"), default="native",
+                    help="stack: one moe_route_pull per layer (routing, mapping and pull in one call), "
+                         "one moe_slot_pull per layer (kernel copies on the compute stream), one "
                          "moe_slot_stage per layer (copy engines on side streams), or moe_slot_map + one "
                          "moe_slot_fill per miss")
     ap.add_argument("--mfma-sweep", action="store_true",

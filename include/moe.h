@@ -8,6 +8,7 @@
  *   moe_slot_fill   pinned-host -> slot copy on a side stream + page-table write
  *   moe_slot_stage  moe_slot_map and the fills of its misses in one call
  *   moe_slot_pull   moe_slot_map, then one kernel copies the misses in
+ *   moe_route_pull  moe_route_union, then (host waits) moe_slot_pull of its experts
  *   moe_expert_ffn  quantised SwiGLU experts read through the page table,
  *                   shared expert, weighted combine
  *
@@ -238,6 +239,23 @@ moe_status moe_slot_stage(moe_ctx* ctx, int32_t layer, const int32_t* experts, i
  * refused map changes nothing. */
 moe_status moe_slot_pull(moe_ctx* ctx, int32_t layer, const int32_t* experts, int32_t n,
                          const void* const* payloads, int32_t* slots_out, uint8_t* miss_out, moe_stream stream);
+
+/* One demand-staged step of a layer for T <= 4 tokens, with the host in the
+ * loop only where the mapping needs it: moe_route_union (same arguments and
+ * results) on `stream`, whose union kernel also writes n_active and the
+ * experts into the context's pinned memory; the host waits for that (a busy
+ * wait on an event), then runs moe_slot_pull of those experts (same arguments
+ * and results) on `stream`.  The experts a layer runs with are known only
+ * after its routing ("MawForge", §IV-C: a miss materialises the expert into
+ * a slot before the layer reads it).
+ * n_out (host [1]), experts_out (host [n_experts]): the step's experts,
+ * ascending; slots_out, miss_out (host [n_experts]): as moe_slot_map.
+ * Blocks the calling thread until the routing is done.  MOE_EINVAL for T
+ * outside [1, min(4, max_tokens)], a bad layer or a null argument. */
+moe_status moe_route_pull(moe_ctx* ctx, int32_t layer, const void* x, int32_t x_dtype, const float* w_router,
+                          const float* logits_in, int64_t T, int32_t* topk_ids, float* topk_w, float* logits_out,
+                          const moe_plan* plan, const void* const* payloads, int32_t* n_out, int32_t* experts_out,
+                          int32_t* slots_out, uint8_t* miss_out, moe_stream stream);
 
 /* Lookahead staging ahead of demand ("Paging the Experts", §3.3: predicted
  * experts staged while the current layer computes; exact demand outranks

@@ -83,7 +83,7 @@ hipError_t launch_dequant(const Geom& g, const uint8_t* payload, int prec, float
 constexpr int kFusedMaxT = 4;
 hipError_t launch_route_union(const void* x, int x_bf16, const float* w_r, const float* logits_in, int64_t T,
                               int E, int d, int k, int norm, float* logits, int32_t* ids, float* w,
-                              const moe_plan& plan, hipStream_t s);
+                              const moe_plan& plan, hipStream_t s, int32_t* mirror = nullptr);
 
 struct FfnArgs {
     // experts

@@ -47,6 +47,8 @@ struct moe_ctx {
     uint64_t pstats[4] = {0, 0, 0, 0};  // prefetch fills, useful, wasted, bytes
 
     // ordering
+    int32_t* hmirror = nullptr;       // pinned [1 + E]: n_active and experts of the last moe_route_pull
+    hipEvent_t route_ev = nullptr;    // moe_route_pull: the routing is done
     hipStream_t aux = nullptr;        // prefill: the 64-token tile chain beside the caller's stream
     hipEvent_t fork_ev = nullptr, join_ev = nullptr;
     hipEvent_t release_ev = nullptr;  // last moe_slot_release point on the compute stream
@@ -336,6 +338,8 @@ void moe_destroy(moe_ctx* c) {
         if (c->logits_ws) (void)hipFree(c->logits_ws);
         if (c->release_ev) (void)hipEventDestroy(c->release_ev);
         if (c->fork_ev) (void)hipEventDestroy(c->fork_ev);
+        if (c->route_ev) (void)hipEventDestroy(c->route_ev);
+        if (c->hmirror) (void)hipHostFree(c->hmirror);
         if (c->join_ev) (void)hipEventDestroy(c->join_ev);
         if (c->aux) (void)hipStreamDestroy(c->aux);
         for (auto& p : c->fills) (void)hipEventDestroy(p.ev);
@@ -396,6 +400,10 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         if (hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff, cfg->n_experts)) != hipSuccess)
             return cleanup(MOE_EHIP);
         if (hipEventCreateWithFlags(&c->release_ev, hipEventDisableTiming) != hipSuccess) return cleanup(MOE_EHIP);
+        if (hipHostMalloc((void**)&c->hmirror, sizeof(int32_t) * (size_t)(cfg->n_experts + 1), hipHostMallocDefault) !=
+                hipSuccess ||
+            hipEventCreateWithFlags(&c->route_ev, hipEventDisableTiming) != hipSuccess)
+            return cleanup(MOE_EHIP);
         // default priority (as every stream of the library); the fork and join
         // order kernels of one device, whose launches fence their own memory,
         // so the events skip the system-scope fence (a cache write-back the
@@ -473,6 +481,44 @@ moe_status moe_route_union(moe_ctx* c, const void* x, int32_t x_dtype, const flo
     HIP_TRY(c, moe::launch_route_union(x, x_dtype == MOE_BF16, w_router, logits_in, T, cf.n_experts, cf.d_model,
                                        cf.top_k, cf.norm_topk, lo, topk_ids, topk_w, *plan, (hipStream_t)stream));
     return MOE_OK;
+}
+
+moe_status moe_route_pull(moe_ctx* c, int32_t layer, const void* x, int32_t x_dtype, const float* w_router,
+                          const float* logits_in, int64_t T, int32_t* topk_ids, float* topk_w, float* logits_out,
+                          const moe_plan* plan, const void* const* payloads, int32_t* n_out, int32_t* experts_out,
+                          int32_t* slots_out, uint8_t* miss_out, moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (T < 1 || T > moe::kFusedMaxT || T > cf.max_tokens)
+        return fail(c, MOE_EINVAL, "moe_route_pull: T=%lld outside [1, %d]", (long long)T,
+                    std::min(moe::kFusedMaxT, cf.max_tokens));
+    if (layer < 0 || layer >= cf.n_layers) return fail(c, MOE_EINVAL, "moe_route_pull: bad layer");
+    if (!plan || !plan->n_active || !plan->experts || !plan->offsets || !plan->entries || !topk_ids || !topk_w ||
+        !payloads || !n_out || !experts_out || !slots_out || !miss_out)
+        return fail(c, MOE_EINVAL, "moe_route_pull: null argument");
+    if (!logits_in) {
+        if (!x || !w_router) return fail(c, MOE_EINVAL, "moe_route_pull: need logits_in or both x and w_router");
+        if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(c, MOE_EINVAL, "moe_route_pull: bad x_dtype");
+    }
+    const void* mirror_dev = nullptr;
+    if (!device_view(c->hmirror, &mirror_dev)) return fail(c, MOE_EHIP, "moe_route_pull: mirror not mapped");
+    DeviceGuard dg(cf.device);
+    hipStream_t s = (hipStream_t)stream;
+    float* lo = logits_out ? logits_out : c->logits_ws;
+    c->hmirror[0] = -1;
+    HIP_TRY(c, moe::launch_route_union(x, x_dtype == MOE_BF16, w_router, logits_in, T, cf.n_experts, cf.d_model,
+                                       cf.top_k, cf.norm_topk, lo, topk_ids, topk_w, *plan, s,
+                                       (int32_t*)mirror_dev));
+    HIP_TRY(c, hipEventRecord(c->route_ev, s));
+    hipError_t q;
+    while ((q = hipEventQuery(c->route_ev)) == hipErrorNotReady) {
+    }
+    HIP_TRY(c, q);
+    const int32_t n = c->hmirror[0];
+    if (n < 0 || n > cf.n_experts) return fail(c, MOE_EHIP, "moe_route_pull: routing returned %d experts", n);
+    std::memcpy(experts_out, c->hmirror + 1, sizeof(int32_t) * (size_t)n);
+    *n_out = n;
+    return moe_slot_pull(c, layer, experts_out, n, payloads, slots_out, miss_out, stream);
 }
 
 moe_status moe_slot_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n,

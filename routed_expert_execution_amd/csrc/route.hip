@@ -52,6 +52,7 @@ struct RouteUnion {
     int32_t* experts;
     int32_t* offsets;
     int32_t* entries;
+    int32_t* mirror;  // or null: [0] n_active, [1 ..] the experts (pinned host memory)
 };
 
 // Top-k of the T tokens (one wave each), then the union; one workgroup of 256.
@@ -69,6 +70,11 @@ __device__ void topk_union_wg(const float* logits, const RouteUnion& r) {
         r.w[threadIdx.x] = s_w[threadIdx.x];
     }
     union_small(s_ids, N, r.n_active, r.experts, r.offsets, r.entries);
+    if (r.mirror) {  // the units, for a host that maps them (written after the union is complete)
+        __syncthreads();
+        const int na = *r.n_active;
+        for (int i = threadIdx.x; i <= na; i += blockDim.x) r.mirror[i] = i ? r.experts[i - 1] : na;
+    }
 }
 
 template <int KPL>
@@ -80,8 +86,8 @@ __global__ __launch_bounds__(256) void topk_union_kernel(const float* __restrict
 
 hipError_t launch_route_union(const void* x, int x_bf16, const float* w_r, const float* logits_in, int64_t T,
                               int E, int d, int k, int norm, float* logits, int32_t* ids, float* w,
-                              const moe_plan& plan, hipStream_t s) {
-    RouteUnion r{(int)T, E, k, norm, ids, w, plan.n_active, plan.experts, plan.offsets, plan.entries};
+                              const moe_plan& plan, hipStream_t s, int32_t* mirror) {
+    RouteUnion r{(int)T, E, k, norm, ids, w, plan.n_active, plan.experts, plan.offsets, plan.entries, mirror};
     if (!logits_in) {
         hipLaunchKernelGGL(router_gemv_kernel, dim3((E + 3) / 4, 1), dim3(256), 0, s, x, x_bf16, w_r, (int)T, E, d,
                            logits);

@@ -70,6 +70,7 @@ def _load() -> C.CDLL:
         "moe_slot_fill": (C.c_int, [P, I32, I32, I32, P, P]),
         "moe_slot_stage": (C.c_int, [P, I32, P, I32, P, P, P, P, I32]),
         "moe_slot_pull": (C.c_int, [P, I32, P, I32, P, P, P, P]),
+        "moe_route_pull": (C.c_int, [P, I32, P, I32, P, P, I64, P, P, P, planp, P, P, P, P, P, P]),
         "moe_slot_prefetch": (C.c_int, [P, I32, P, I32, I64, P, P, P]),
         "moe_prefetch_stats": (C.c_int, [P, C.POINTER(C.c_uint64)]),
         "moe_slot_release": (C.c_int, [P, I32, P]),
@@ -93,7 +94,7 @@ def _load() -> C.CDLL:
 _lib = _load()
 EXPORTS = ("moe_payload_bytes", "moe_plan_bytes", "moe_pack_expert", "moe_unpack_expert", "moe_create",
            "moe_destroy", "moe_last_error", "moe_status_string", "moe_route", "moe_plan_union", "moe_route_union",
-           "moe_slot_map", "moe_slot_prefetch", "moe_prefetch_stats", "moe_slot_fill", "moe_slot_stage", "moe_slot_pull", "moe_slot_release",
+           "moe_slot_map", "moe_slot_prefetch", "moe_prefetch_stats", "moe_slot_fill", "moe_slot_stage", "moe_slot_pull", "moe_route_pull", "moe_slot_release",
            "moe_slot_bind", "moe_expert_ffn",
            "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table", "moe_probe_read",
            "moe_probe_mfma")
@@ -398,6 +399,26 @@ def moe_slot_pull(ctx: Context, layer: int, experts, table: np.ndarray, stream=N
     _call(ctx, _lib.moe_slot_pull(ctx.handle, layer, e.ctypes.data, e.size, table.ctypes.data, slots.ctypes.data,
                                   miss.ctypes.data, _stream(stream)))
     return slots, miss.astype(bool)
+
+
+def moe_route_pull(ctx: Context, layer: int, topk_ids, topk_w, plan: "Plan", table: np.ndarray, *, x=None,
+                   w_router=None, logits_in=None, logits_out=None, stream=None) -> tuple:
+    """moe_route_union, then moe_slot_pull of the step's experts from `table`
+    (payload_table); returns (experts, slots, miss) for the step's units."""
+    _table(ctx, table)
+    T = int(topk_ids.shape[0])
+    xd = _route_args(ctx, topk_ids, topk_w, x, w_router, logits_in, logits_out)
+    if plan.entries.numel() < T * ctx.top_k:
+        raise ValueError("plan is too small for T")
+    n = C.c_int32()
+    ex = np.empty(ctx.n_experts, dtype=np.int32)
+    slots = np.empty(ctx.n_experts, dtype=np.int32)
+    miss = np.empty(ctx.n_experts, dtype=np.uint8)
+    _call(ctx, _lib.moe_route_pull(ctx.handle, layer, _ptr(x), xd, _ptr(w_router), _ptr(logits_in), T,
+                                   _ptr(topk_ids), _ptr(topk_w), _ptr(logits_out), C.byref(plan.c), table.ctypes.data,
+                                   C.byref(n), ex.ctypes.data, slots.ctypes.data, miss.ctypes.data, _stream(stream)))
+    k = n.value
+    return ex[:k], slots[:k], miss[:k].astype(bool)
 
 
 def moe_slot_release(ctx: Context, layer: int, stream=None) -> None:

@@ -120,6 +120,8 @@ def test_host_only_context_rejects_device_calls():
     assert lib.moe_slot_fill(ctx.handle, 0, 0, 0, None, None) == moe.MOE_EINVAL
     assert lib.moe_slot_stage(ctx.handle, 0, None, 0, None, None, None, None, 0) == moe.MOE_EINVAL
     assert lib.moe_slot_pull(ctx.handle, 0, None, 0, None, None, None, None) == moe.MOE_EINVAL
+    assert lib.moe_route_pull(ctx.handle, 0, None, 0, None, None, 1, None, None, None, None, None, None, None,
+                              None, None, None) == moe.MOE_EINVAL
     assert lib.moe_dequant(ctx.handle, None, 0, None, None) == moe.MOE_EINVAL
     assert lib.moe_route_ffn(ctx.handle, 0, None, 0, None, None, 1, None, None, None, None, 0, None,
                              None) == moe.MOE_EINVAL

@@ -18,10 +18,11 @@ if not H.gpu_available():  # pragma: no cover
 from routed_expert_execution_amd import moe  # noqa: E402
 
 
-def _run_stack(prefetch: bool, L=3, n_tok=6, n_slots=24, stage_streams=0, pull=False):
+def _run_stack(prefetch: bool, L=3, n_tok=6, n_slots=24, stage_streams=0, pull=False, native=False):
     """stage_streams 0: moe_slot_map + one moe_slot_fill per miss; else one
     moe_slot_stage per layer over that many side streams.  pull: one
-    moe_slot_pull per layer on the compute stream instead."""
+    moe_slot_pull per layer on the compute stream instead; native: one
+    moe_route_pull per layer (routing, readback, map and pull)."""
     wl = synth.workload("stack40")
     E, k, d, f = wl["E"], wl["k"], wl["d"], wl["f"]
     ctx = H.make_ctx(wl, n_slots=n_slots, max_tokens=1, n_layers=L)
@@ -46,8 +47,17 @@ def _run_stack(prefetch: bool, L=3, n_tok=6, n_slots=24, stage_streams=0, pull=F
             lg[0, chains[l][t]] = 2.0 + np.arange(k, dtype=np.float32) / 16
             ids = torch.empty(1, k, dtype=torch.int32, device="cuda")
             w = torch.empty(1, k, dtype=torch.float32, device="cuda")
-            moe.moe_route_union(ctx, ids, w, plan, logits_in=torch.from_numpy(lg).cuda())
-            if stage_streams or pull:
+            if native:
+                step = set(int(e) for e in chains[l][t])  # a miss is one of the step's own experts
+                full = moe.payload_table(ctx, [payload(l, e) if e in step else None for e in range(E)])
+                ex, slots_n, miss_n = moe.moe_route_pull(ctx, l, ids, w, plan, full,
+                                                         logits_in=torch.from_numpy(lg).cuda())
+                assert list(ex) == sorted(int(e) for e in chains[l][t])
+            else:
+                moe.moe_route_union(ctx, ids, w, plan, logits_in=torch.from_numpy(lg).cuda())
+            if native:
+                pass
+            elif stage_streams or pull:
                 n, ex = plan.experts_host()
                 table = moe.payload_table(ctx, [payload(l, e) if e in set(ex.tolist()) else None for e in range(E)])
                 if pull:

@@ -48,6 +48,52 @@ def test_pull_matches_map_and_fill():
         assert np.array_equal(y_a.view(np.uint32), y_b.view(np.uint32)), (l, t)
 
 
+def test_route_pull_matches_route_then_pull():
+    """moe_route_pull (the routing kernel writes the experts to pinned memory,
+    the host maps and pulls) equals moe_route_union + readback + moe_slot_pull:
+    same experts, slots, page table and output bits."""
+    _say("route_pull vs route + pull")
+    a, st_a, _, _, _, pt_a = _run_stack(False, n_tok=5, pull=True)
+    b, st_b, _, _, _, pt_b = _run_stack(False, n_tok=5, native=True)
+    assert st_a == st_b and st_a["evictions"] > 0
+    assert np.array_equal(pt_a, pt_b)
+    for (l, t, _, ids_a, w_a, y_a), (_, _, _, ids_b, w_b, y_b) in zip(a, b):
+        assert np.array_equal(ids_a, ids_b) and np.array_equal(w_a.view(np.uint32), w_b.view(np.uint32))
+        assert np.array_equal(y_a.view(np.uint32), y_b.view(np.uint32)), (l, t)
+
+
+def test_route_pull_from_router_weights_and_validation():
+    """Routing from x and router weights (one and four tokens) gives the
+    experts moe_route_union gives; bad arguments are refused before any work."""
+    wl = synth.workload("decode")
+    E, k, d = wl["E"], wl["k"], wl["d"]
+    ctx = H.make_ctx(wl, n_slots=64, max_tokens=4)
+    wr = torch.from_numpy(synth.router_weights(wl["seed"], E, d)).cuda()
+    pays = [torch.zeros(ctx.payload_bytes, dtype=torch.uint8).pin_memory() for _ in range(2)]
+    table = moe.payload_table(ctx, [pays[e % 2] for e in range(E)])
+    for step, T in ((0, 1), (1, 4), (2, 1)):
+        x = H.torch_x(synth.activations(wl["seed"], T, d, "bf16", step), "bf16")
+        ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+        plan = moe.Plan(ctx, T)
+        ex, slots, miss = moe.moe_route_pull(ctx, 0, ids, w, plan, table, x=x, w_router=wr)
+        ids2 = torch.empty(T, k, dtype=torch.int32, device="cuda")
+        w2 = torch.empty(T, k, dtype=torch.float32, device="cuda")
+        plan2 = moe.Plan(ctx, T)
+        moe.moe_route_union(ctx, ids2, w2, plan2, x=x, w_router=wr)
+        torch.cuda.synchronize()
+        n2, ex2 = plan2.experts_host()
+        assert list(ex) == list(ex2) and n2 == len(ex)
+        assert np.array_equal(ids.cpu().numpy(), ids2.cpu().numpy())
+        moe.moe_slot_release(ctx, 0)
+    x = H.torch_x(synth.activations(wl["seed"], 4, d, "bf16", 9), "bf16")
+    ids = torch.empty(4, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(4, k, dtype=torch.float32, device="cuda")
+    with pytest.raises(moe.MoeError):  # layer out of range
+        moe.moe_route_pull(ctx, 5, ids, w, moe.Plan(ctx, 4), table, x=x, w_router=wr)
+    assert moe.moe_check(ctx) == moe.MOE_OK
+
+
 def _small_ctx(n_slots, n_layers=2, E=256):
     wl = dict(synth.workload("tiny"), E=E, k=8, n_layers=n_layers)
     return wl, H.make_ctx(wl, n_slots=n_slots, max_tokens=1, n_layers=n_layers)
