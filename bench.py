@@ -555,6 +555,8 @@ def main() -> int:
                          "(its previous token's experts with routing weight >= 0.20), at most N payloads")
     ap.add_argument("--fill-streams", type=int, default=2, metavar="S",
                     help="stack: side streams the misses' copies alternate over")
+    ap.add_argument("--gemm-min", type=int, default=16, metavar="M",
+                    help="prefill, bf16 mode: buckets of at least M tokens use 64-token tiles")
     ap.add_argument("--spin-readback", action="store_true",
                     help="stack: poll for the plan readback instead of a blocking synchronise")
     ap.add_argument("--staging", choices=("native", "pull", "stage", "fill"), default="native",
@@ -604,7 +606,7 @@ def main() -> int:
     cfg = moe.make_config(1, E, k, d, f, qt, wl["n_slots"], T, device=-1)
     pb = moe.moe_payload_bytes(cfg)
     pool = torch.zeros(wl["n_slots"] * pb, dtype=torch.uint8, device=dev)
-    ctx = moe.Context(1, E, k, d, f, qt, wl["n_slots"], T, device=0, slot_pool=pool)
+    ctx = moe.Context(1, E, k, d, f, qt, wl["n_slots"], T, device=0, slot_pool=pool, gemm_min_tokens=args.gemm_min)
     t_gen = time.perf_counter()
     pack = torch.empty((E, pb), dtype=torch.uint8).pin_memory()  # pinned host pack
     pack_np = pack.numpy()
