@@ -48,6 +48,7 @@ struct moe_ctx {
 
     // ordering
     int32_t* hmirror = nullptr;       // pinned [1 + E]: n_active and experts of the last moe_route_pull
+    int32_t* hmirror_dev = nullptr;   // the same memory as kernels address it
     hipEvent_t route_ev = nullptr;    // moe_route_pull: the routing is done
     hipStream_t aux = nullptr;        // prefill: the 64-token tile chain beside the caller's stream
     hipEvent_t fork_ev = nullptr, join_ev = nullptr;
@@ -404,6 +405,9 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
                 hipSuccess ||
             hipEventCreateWithFlags(&c->route_ev, hipEventDisableTiming) != hipSuccess)
             return cleanup(MOE_EHIP);
+        const void* mdev = nullptr;
+        if (!device_view(c->hmirror, &mdev)) return cleanup(MOE_EHIP);
+        c->hmirror_dev = (int32_t*)mdev;
         // default priority (as every stream of the library); the fork and join
         // order kernels of one device, whose launches fence their own memory,
         // so the events skip the system-scope fence (a cache write-back the
@@ -500,15 +504,12 @@ moe_status moe_route_pull(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
         if (!x || !w_router) return fail(c, MOE_EINVAL, "moe_route_pull: need logits_in or both x and w_router");
         if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(c, MOE_EINVAL, "moe_route_pull: bad x_dtype");
     }
-    const void* mirror_dev = nullptr;
-    if (!device_view(c->hmirror, &mirror_dev)) return fail(c, MOE_EHIP, "moe_route_pull: mirror not mapped");
     DeviceGuard dg(cf.device);
     hipStream_t s = (hipStream_t)stream;
     float* lo = logits_out ? logits_out : c->logits_ws;
     c->hmirror[0] = -1;
     HIP_TRY(c, moe::launch_route_union(x, x_dtype == MOE_BF16, w_router, logits_in, T, cf.n_experts, cf.d_model,
-                                       cf.top_k, cf.norm_topk, lo, topk_ids, topk_w, *plan, s,
-                                       (int32_t*)mirror_dev));
+                                       cf.top_k, cf.norm_topk, lo, topk_ids, topk_w, *plan, s, c->hmirror_dev));
     HIP_TRY(c, hipEventRecord(c->route_ev, s));
     hipError_t q;
     while ((q = hipEventQuery(c->route_ev)) == hipErrorNotReady) {
