@@ -47,6 +47,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, AMD published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_decode_traffic.json")
 
 
@@ -119,6 +120,58 @@ def traffic_from(fetch_dir: str, write_dir: str, workload: str, warmup: int, ste
     json.dump(t, open(TRAFFIC_FILE, "w"), indent=1)
     print(json.dumps({workload: t[workload]}))
     return 0
+
+
+BIG_BUCKET = 167  # tokens from which a Q8_0 bucket of this shape is compute-bound on bf16 MFMA
+
+
+def big_buckets_mfma(experts, sizes, pack, wl, flush, flush_sink, spin_cycles, no_flush, reps: int = 20,
+                     gemm_min: int = 16) -> dict:
+    """The grouped GEMM on just the chunk's buckets of at least BIG_BUCKET
+    tokens: a context with one routed expert per token, sum(sizes) tokens,
+    token i in the bucket of its expert (no shared expert), bf16 mode, cold;
+    matrix-core utilisation = 3 d f 2 flops per token over the call's event
+    time, against the bf16 dense peak."""
+    import torch
+    from routed_expert_execution_amd import moe
+    import synth
+    E, d, f = len(experts), wl["d"], wl["f"]
+    T = int(sum(sizes))
+    dev = torch.device("cuda", 0)
+    cfg = moe.make_config(1, E, 1, d, f, moe.MOE_Q8_0, E, T, device=-1)
+    pb = moe.moe_payload_bytes(cfg)
+    pool = torch.zeros(E * pb, dtype=torch.uint8, device=dev)
+    ctx = moe.Context(1, E, 1, d, f, moe.MOE_Q8_0, E, T, device=0, slot_pool=pool, gemm_min_tokens=gemm_min)
+    try:
+        for i, e in enumerate(experts):
+            pool[i * pb:(i + 1) * pb].copy_(pack[e])
+            moe.moe_slot_bind(ctx, 0, i, i)
+        ids = torch.from_numpy(np.repeat(np.arange(E, dtype=np.int32), sizes).reshape(T, 1)).to(dev)
+        w = torch.ones(T, 1, dtype=torch.float32, device=dev)
+        x = torch.from_numpy(synth.activations(wl["seed"], T, d, "bf16", 7).view(np.int16)).view(torch.bfloat16).to(dev)
+        y = torch.empty(T, d, dtype=torch.float32, device=dev)
+        plan = moe.Plan(ctx, T)
+        moe.moe_plan_union(ctx, ids, plan)
+        stream = torch.cuda.current_stream(dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps + 2)]
+        for e0, e1 in evs:
+            if not no_flush:
+                flush_sink.copy_(flush.max())
+            torch.cuda._sleep(spin_cycles)
+            e0.record(stream)
+            moe.moe_expert_ffn(ctx, 0, x, plan, w, y, prec=moe.MOE_PREC_BF16)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        if moe.moe_check(ctx) != moe.MOE_OK:
+            return None
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs[2:]])) * 1e3
+    finally:
+        ctx.close()
+    flops = 3.0 * d * f * 2.0 * T
+    return {"sizes": [int(v) for v in sizes], "tokens": T, "us_mean": us, "tflops": flops / (us * 1e-6) / 1e12,
+            "mfma_frac": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, "gemm_min_tokens": gemm_min,
+            "note": "moe_expert_ffn on only the chunk's buckets of >= %d tokens (one routed expert per token, "
+                    "no shared expert), bf16 mode, weights cold" % BIG_BUCKET}
 
 
 def cpu_baseline(wl: dict, budget_s: float = 10.0, max_steps: int = 100_000) -> dict:
@@ -323,7 +376,7 @@ def replay_policies(args, synth, moe) -> int:
     L, E, k = wl["n_layers"], wl["E"], wl["k"]
     cfg = moe.make_config(L, E, k, wl["d"], wl["f"], moe.MOE_Q8_0, wl["n_slots"], 1, device=-1)
     pb = moe.moe_payload_bytes(cfg)
-    n_tok = args.steps if args.steps != 500 else wl["tokens"]
+    n_tok = args.steps
     trace = R.markov_trace(wl["seed"], L, n_tok, E, k, wl["p_repeat"])
     rows = []
     for cap in (wl["n_slots"], 2 * wl["n_slots"]):
@@ -547,7 +600,8 @@ def run_stack(args, torch, moe, synth) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 1000 decode/mtp steps, 200 prefill chunks, 256 stack tokens)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode", choices=["decode", "mtp", "prefill", "stack", "replay"])
     ap.add_argument("--prefetch", type=int, default=0, metavar="N",
@@ -555,6 +609,8 @@ def main() -> int:
                          "(its previous token's experts with routing weight >= 0.20), at most N payloads")
     ap.add_argument("--fill-streams", type=int, default=2, metavar="S",
                     help="stack: side streams the misses' copies alternate over")
+    ap.add_argument("--big-gemm-min", type=int, default=0, metavar="M",
+                    help="prefill: also time the big buckets with this gemm_min_tokens")
     ap.add_argument("--gemm-min", type=int, default=16, metavar="M",
                     help="prefill, bf16 mode: buckets of at least M tokens use 64-token tiles")
     ap.add_argument("--spin-readback", action="store_true",
@@ -575,6 +631,8 @@ def main() -> int:
     ap.add_argument("--separate-calls", action="store_true",
                     help="time steps of up to 4 tokens as moe_route_union + moe_expert_ffn, not one launch")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = {"decode": 1000, "mtp": 1000, "prefill": 200, "stack": 256, "replay": 256}.get(args.workload, 200)
     if args.traffic_from:
         return traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload, args.warmup, args.steps)
     if args.gpus != 1:
@@ -723,6 +781,19 @@ def main() -> int:
     if st != moe.MOE_OK:
         print(f"device error word set: status {st}", file=sys.stderr)
         return 1
+    big = None
+    if args.workload == "prefill":
+        route_plan(args.warmup)
+        n, experts, offsets, _ = plan.host()
+        sizes = np.diff(offsets)
+        sel = [i for i in range(n) if sizes[i] >= BIG_BUCKET]
+        if sel:
+            big = big_buckets_mfma([int(experts[i]) for i in sel], [int(sizes[i]) for i in sel], pack, wl,
+                                   flush, flush_sink, spin_cycles, args.no_flush)
+            if args.big_gemm_min:
+                big["alt"] = big_buckets_mfma([int(experts[i]) for i in sel], [int(sizes[i]) for i in sel], pack, wl,
+                                              flush, flush_sink, spin_cycles, args.no_flush,
+                                              gemm_min=args.big_gemm_min)
 
     span = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(args.warmup, n_steps)]) * 1e3  # us
     sep = np.array([a.elapsed_time(b) for a, b in ev_sep]) * 1e3
@@ -787,7 +858,9 @@ def main() -> int:
             "layer_span_GBps": span_gbs,
             "unique_experts_per_step": float(uniq.mean()),
             "assignments_per_step": T * k,
+            "dedupe_fraction": float(1.0 - uniq.mean() / (T * k)),
             "slot_misses_staged": misses,
+            "big_buckets": big,
             "wall_s_timed_loop_incl_staging_and_flush": wall,
             "setup_pack_s": t_gen,
         },
