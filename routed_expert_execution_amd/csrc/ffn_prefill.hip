@@ -390,13 +390,19 @@ __device__ void tile_product(const void* A, int64_t a_pitch, const int (&arow)[R
 // its A fragments from there.  One barrier per step: the buffer written during
 // step k was last read during step k - 1.  The barrier orders LDS only, so the
 // next step's weight loads stay in flight across it.
+//
+// NW weight stages: with 2, a step's weights are fetched one step ahead; with 3,
+// two steps ahead.  Loads complete in order, and each step waits for the next
+// step's activations (issued after the weights of the step after it), so with
+// 3 stages a weight fetch has two steps to arrive instead of one, for 9 (Q8_0)
+// or 5 (Q4_0) more registers per matrix.
 
 constexpr int APITCH = 128 + 8;  // bf16 per LDS row: 272 bytes, conflict-free 16-byte reads
 
 // srow[q]: source row of tile row threadIdx.x / 16 + 16 q (a valid row; skeep[q]
 // false for padding rows, staged as zeros).  Waves with wlive false take part in
 // the staging and barriers only.
-template <int QT, bool XB, int R, int MATS, class BlockAt>
+template <int QT, bool XB, int R, int MATS, int NW, class BlockAt>
 __device__ void tile_product_lds(const void* A, int64_t a_pitch, const int (&srow)[R], const bool (&skeep)[R],
                                  int nkb, bool wlive, BlockAt blk, f32x4 (&acc)[MATS][R]) {
     __shared__ __attribute__((aligned(16))) __bf16 abuf[2][16 * R][APITCH];
@@ -458,31 +464,53 @@ __device__ void tile_product_lds(const void* A, int64_t a_pitch, const int (&sro
             }
         }
     };
-    // step k: weights of k in wc, activations of k in LDS buffer k & 1; loads
-    // for k + 1 issued first
+    // step k: weights of k in wc, activations of k in LDS buffer k & 1; the
+    // activations of k + 1 and the weights of k + NW - 1 (into wn) issued first
     auto one = [&](int kb0, int buf, Raw<QT>(&wc)[MATS], Raw<QT>(&wn)[MATS]) {
         AStage st;
         fetch_a(kb0 + 4, st);
-        if (wlive) fetch_w(kb0 + 4, wn);
+        if (wlive) fetch_w(kb0 + 4 * (NW - 1), wn);
         if (wlive) compute(buf, wc);
         store_a(buf ^ 1, st);
         lds_barrier();
     };
-    Raw<QT> wa[MATS], wb[MATS];
-    {
-        AStage st;
-        fetch_a(0, st);
-        if (wlive) fetch_w(0, wa);
-        store_a(0, st);
-        lds_barrier();
-    }
     const int n_steps = (nkb + 3) / 4;
     int kb0 = 0;
-    for (int i = 0; i < n_steps / 2; i++, kb0 += 8) {
-        one(kb0, 0, wa, wb);
-        one(kb0 + 4, 1, wb, wa);
+    if constexpr (NW == 2) {
+        Raw<QT> wa[MATS], wb[MATS];
+        {
+            AStage st;
+            fetch_a(0, st);
+            if (wlive) fetch_w(0, wa);
+            store_a(0, st);
+            lds_barrier();
+        }
+        for (int i = 0; i < n_steps / 2; i++, kb0 += 8) {
+            one(kb0, 0, wa, wb);
+            one(kb0 + 4, 1, wb, wa);
+        }
+        if (n_steps & 1) one(kb0, 0, wa, wb);
+    } else {
+        static_assert(NW == 3, "two or three weight stages");
+        Raw<QT> wa[MATS], wb[MATS], wc[MATS];
+        {
+            AStage st;
+            fetch_a(0, st);
+            if (wlive) fetch_w(0, wa);
+            if (wlive) fetch_w(4, wb);
+            store_a(0, st);
+            lds_barrier();
+        }
+        // stage of step k: wa, wb, wc for k % 3 = 0, 1, 2; LDS buffer k & 1
+        int step = 0;
+        for (; step + 3 <= n_steps; step += 3, kb0 += 12) {
+            one(kb0, step & 1, wa, wc);
+            one(kb0 + 4, (step + 1) & 1, wb, wa);
+            one(kb0 + 8, step & 1, wc, wb);
+        }
+        if (step < n_steps) one(kb0, step & 1, wa, wc);
+        if (step + 1 < n_steps) one(kb0 + 4, (step + 1) & 1, wb, wa);
     }
-    if (n_steps & 1) one(kb0, 0, wa, wb);
 }
 
 // ---- gate/up ------------------------------------------------------------------------
@@ -506,7 +534,7 @@ __device__ void gate_up_item(const PrefillArgs& a, const TileRec& t, const uint8
             skeep[q] = m < t.M;
             srow[q] = row_token(a, t, skeep[q] ? m : 0);
         }
-        tile_product_lds<QT, XB, R, 2>(a.x, a.d, srow, skeep, G.nb_d, wlive, blk, acc);
+        tile_product_lds<QT, XB, R, 2, 2>(a.x, a.d, srow, skeep, G.nb_d, wlive, blk, acc);
     } else {
         int arow[R];
         bool alive[R];
@@ -585,7 +613,7 @@ __device__ void down_item(const PrefillArgs& a, const TileRec& t, const uint8_t*
             skeep[q] = m < t.M;
             srow[q] = row_slot(a, t, skeep[q] ? m : 0);
         }
-        tile_product_lds<QT, true, R, 1>(a.h, a.f, srow, skeep, G.nb_f, true, blk, acc);
+        tile_product_lds<QT, true, R, 1, 3>(a.h, a.f, srow, skeep, G.nb_f, true, blk, acc);
     } else {
         int arow[R];
         bool alive[R];
