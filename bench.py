@@ -609,6 +609,8 @@ def main() -> int:
                          "(its previous token's experts with routing weight >= 0.20), at most N payloads")
     ap.add_argument("--fill-streams", type=int, default=2, metavar="S",
                     help="stack: side streams the misses' copies alternate over")
+    ap.add_argument("--no-big-buckets", action="store_true",
+                    help="prefill: skip the big-bucket matrix-core run (profiler runs cover the chunk's calls only)")
     ap.add_argument("--big-gemm-min", type=int, default=0, metavar="M",
                     help="prefill: also time the big buckets with this gemm_min_tokens")
     ap.add_argument("--gemm-min", type=int, default=16, metavar="M",
@@ -787,7 +789,7 @@ def main() -> int:
         n, experts, offsets, _ = plan.host()
         sizes = np.diff(offsets)
         sel = [i for i in range(n) if sizes[i] >= BIG_BUCKET]
-        if sel:
+        if sel and not args.no_big_buckets:
             big = big_buckets_mfma([int(experts[i]) for i in sel], [int(sizes[i]) for i in sel], pack, wl,
                                    flush, flush_sink, spin_cycles, args.no_flush)
             if args.big_gemm_min:
