@@ -157,3 +157,23 @@ def test_prefill_unmapped_expert_fails_closed():
     y = y.cpu().numpy()
     hit = (c.ids == victim).any(axis=1)
     assert hit.any() and np.isnan(y[hit]).all(axis=1).all() and np.isfinite(y[~hit]).all()
+
+
+def test_prefill_large_chunk_sampled():
+    """A 4096-token chunk of the prefill layer (Zipf(1.1) routes, Q8_0, bf16
+    mode): more tiles than one launch's workgroups, so every tile kernel loops;
+    oracle on 24 sampled tokens, the first and last among them."""
+    wl = dict(synth.workload("prefill"), T=4096)
+    T = wl["T"]
+    lg = synth.zipf_gumbel_logits(wl["seed"] + 21, T, wl["E"], wl["zipf_s"])
+    c = Chunk(wl, T, lg, oracle.PREC_BF16)
+    sizes = c.bucket_sizes()
+    _say("prefill 4096: experts used", len(c.used), "largest buckets", sorted(sizes)[-3:])
+    c.place(list(range(len(c.used))))
+    y = c.run()
+    assert np.isfinite(y).all()
+    g = np.random.default_rng(8)
+    tokens = np.unique(np.concatenate([[0, T - 1], g.choice(T, size=22, replace=False)]))
+    err = H.max_rel_row_err(y[tokens], c.reference(tokens))
+    _say("  max rel row err", err)
+    assert err <= FFN_TOL
