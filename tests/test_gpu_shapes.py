@@ -1,0 +1,64 @@
+"""GPU parity at the corners of the supported layer shapes: d_model 128 to
+2048, d_ff 128 to 2048 (including a d_ff that is not a power of two), both
+weight formats and both activation types.  The decode path (T <= 4) and the
+chunk path (T > 4) are checked against the CPU oracle on every token.
+
+Bar: 1e-3 maximum relative error per token row.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not H.gpu_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from routed_expert_execution_amd import moe  # noqa: E402
+from tests.test_gpu_parity import Step  # noqa: E402
+from tests.test_gpu_prefill import Chunk  # noqa: E402
+
+FFN_TOL = 1e-3
+
+SHAPES = [  # d_model, d_ff, format, activations
+    (128, 128, synth.Q8_0, "f32"),
+    (512, 384, synth.Q4_0, "bf16"),
+    (1024, 2048, synth.Q8_0, "bf16"),
+    (2048, 2048, synth.Q4_0, "f32"),
+]
+
+
+def _wl(d, f, qt, xd):
+    return dict(d=d, f=f, qtype=qt, x_dtype=xd, shared=True, E=8, k=2)
+
+
+@pytest.mark.parametrize("d,f,qt,xd", SHAPES)
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_path_shapes(d, f, qt, xd, T):
+    print("decode shape", d, f, qt, xd, T, flush=True)
+    s = Step("tiny", T, 3, **_wl(d, f, qt, xd))
+    s.place()
+    y = s.run()
+    assert moe.moe_check(s.ctx) == moe.MOE_OK
+    err = H.max_rel_row_err(y, s.reference())
+    print("  max rel row err", err, flush=True)
+    assert np.isfinite(y).all() and err <= FFN_TOL
+
+
+@pytest.mark.parametrize("d,f,qt,xd", SHAPES)
+@pytest.mark.parametrize("prec", [oracle.PREC_BF16, oracle.PREC_F32])
+def test_chunk_path_shapes(d, f, qt, xd, prec):
+    print("chunk shape", d, f, qt, xd, prec, flush=True)
+    wl = dict(synth.workload("tiny"), **_wl(d, f, qt, xd))
+    T = 40
+    lg = synth.zipf_gumbel_logits(wl["seed"] + d + f, T, wl["E"], 1.1)
+    c = Chunk(wl, T, lg, prec)
+    c.place(list(range(len(c.used))))
+    y = c.run()
+    err = H.max_rel_row_err(y, c.reference(np.arange(T)))
+    print("  buckets", sorted(c.bucket_sizes()[c.used].tolist()), "max rel row err", err, flush=True)
+    assert np.isfinite(y).all() and err <= FFN_TOL
