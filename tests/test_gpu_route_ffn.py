@@ -111,7 +111,12 @@ def _same(a, b):
 CASES = [("tiny", 4, {}), ("tiny", 1, {}), ("decode", 1, {}), ("decode", 2, {}), ("decode", 3, {}),
          ("decode", 4, {}), ("mtp", 4, {}), ("mtp", 3, {}), ("mtp", 1, {}),
          ("decode", 4, dict(use_logits=True, E=64, k=32)), ("decode", 2, dict(prec=oracle.PREC_BF16)),
-         ("mtp", 4, dict(norm=0)), ("decode", 1, dict(E=100, k=7))]
+         ("mtp", 4, dict(norm=0)), ("decode", 1, dict(E=100, k=7)),
+         # corners of the supported shapes (router in the launch)
+         ("tiny", 1, dict(d=128, f=128, shared=True)),
+         ("tiny", 4, dict(d=512, f=384, qtype=synth.Q4_0, x_dtype="bf16", shared=True)),
+         ("tiny", 2, dict(d=1024, f=2048, x_dtype="bf16", shared=True, prec=oracle.PREC_BF16)),
+         ("tiny", 4, dict(d=2048, f=2048, qtype=synth.Q4_0, shared=True))]
 
 
 @pytest.mark.parametrize("name,T,kw", CASES)
