@@ -177,3 +177,22 @@ def test_prefill_large_chunk_sampled():
     err = H.max_rel_row_err(y[tokens], c.reference(tokens))
     _say("  max rel row err", err)
     assert err <= FFN_TOL
+
+
+def test_prefill_max_tokens_sampled():
+    """The largest chunk a context takes (max_tokens 65536) on the prefill layer:
+    buckets of tens of thousands of tokens, about 590K hidden rows; oracle on
+    16 sampled tokens, the first and last among them."""
+    wl = dict(synth.workload("prefill"), T=65536)
+    T = wl["T"]
+    lg = synth.zipf_gumbel_logits(wl["seed"] + 31, T, wl["E"], wl["zipf_s"])
+    c = Chunk(wl, T, lg, oracle.PREC_BF16)
+    _say("prefill 65536: largest buckets", sorted(c.bucket_sizes())[-2:])
+    c.place(list(range(len(c.used))))
+    y = c.run()
+    assert np.isfinite(y).all()
+    g = np.random.default_rng(9)
+    tokens = np.unique(np.concatenate([[0, T - 1], g.choice(T, size=14, replace=False)]))
+    err = H.max_rel_row_err(y[tokens], c.reference(tokens))
+    _say("  max rel row err", err)
+    assert err <= FFN_TOL
