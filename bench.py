@@ -321,7 +321,7 @@ def mfma_sweep(torch, moe, synth) -> int:
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
-    Ms = (16, 32, 64, 128, 256, 512)
+    Ms = (16, 32, 64, 128, 256, 512, 2048, 8192)
     cfg = moe.make_config(1, E, k, d, f, moe.MOE_Q8_0, k, max(Ms), device=-1)
     pb = moe.moe_payload_bytes(cfg)
     pool = torch.zeros(k * pb, dtype=torch.uint8, device=dev)
