@@ -95,9 +95,22 @@ __device__ int block_prefix(int v, int* wave_tot, int* total) {
 
 // Tile records of each size (sched_big, sched_small) and their counts (n_tiles);
 // the page table is read here, once per bucket.
+// The entry -> plan position inverse (for the combine) is written here too:
+// the first 4 blockDim.x entries are loaded before the schedule's own chain of
+// dependent loads (n_active, then offsets and experts, then the page table),
+// so that their round trips overlap.
+constexpr int kSchedInvAhead = 4;
+
 __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec) {
     __shared__ int wave_tot[16];
     __shared__ int tot_b, tot_s;
+    const int n_ent = a.T * a.k;
+    int ent_ahead[kSchedInvAhead];
+#pragma unroll
+    for (int q = 0; q < kSchedInvAhead; q++) {
+        const int p = threadIdx.x + q * (int)blockDim.x;
+        ent_ahead[q] = p < n_ent ? a.entries[p] : -1;
+    }
     const int na = *a.n_active;
     const int n_units = na + (a.shared ? 1 : 0);
     int base_b = 0, base_s = 0;
@@ -135,8 +148,12 @@ __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec)
         a.n_tiles[0] = base_b;
         a.n_tiles[1] = base_s;
     }
-    const int n_ent = a.T * a.k;
-    for (int p = threadIdx.x; p < n_ent; p += blockDim.x) {
+#pragma unroll
+    for (int q = 0; q < kSchedInvAhead; q++) {
+        const int ent = ent_ahead[q];
+        if (ent >= 0 && ent < n_ent) a.inv[ent] = threadIdx.x + q * (int)blockDim.x;
+    }
+    for (int p = threadIdx.x + kSchedInvAhead * (int)blockDim.x; p < n_ent; p += blockDim.x) {
         const int ent = a.entries[p];
         if (ent >= 0 && ent < n_ent) a.inv[ent] = p;
     }
