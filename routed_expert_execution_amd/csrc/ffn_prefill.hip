@@ -111,6 +111,19 @@ __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec)
         const int p = threadIdx.x + q * (int)blockDim.x;
         ent_ahead[q] = p < n_ent ? a.entries[p] : -1;
     }
+    // A unit's plan words and page-table entry, read at a clamped index (the
+    // plan arrays hold E units) so that the first pass's loads need not wait
+    // for n_active: one level of plan loads, then one of page-table loads.
+    struct UnitIn {
+        int p0, p1, e, sl;
+    };
+    auto unit_in = [&](int u) {
+        const int uc = min(u, a.E - 1);
+        UnitIn r{a.offsets[uc], a.offsets[uc + 1], a.experts[uc], -1};
+        if (r.e >= 0 && r.e < a.E) r.sl = a.pt[(int64_t)a.layer * a.E + r.e];
+        return r;
+    };
+    const UnitIn first = unit_in(threadIdx.x);
     const int na = *a.n_active;
     const int n_units = na + (a.shared ? 1 : 0);
     int base_b = 0, base_s = 0;
@@ -121,14 +134,11 @@ __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec)
             if (u == na) {
                 M = a.T;
             } else {
-                p0 = a.offsets[u];
-                M = a.offsets[u + 1] - p0;
-                const int e = a.experts[u];
+                const UnitIn in = u0 == 0 ? first : unit_in(u);
+                p0 = in.p0;
+                M = in.p1 - in.p0;
                 slot = kUnmapped;
-                if (e >= 0 && e < a.E) {
-                    const int sl = a.pt[(int64_t)a.layer * a.E + e];
-                    if (sl >= 0 && sl < a.n_slots) slot = sl;
-                }
+                if (in.e >= 0 && in.e < a.E && in.sl >= 0 && in.sl < a.n_slots) slot = in.sl;
                 if (slot == kUnmapped) atomicOr(a.err, kErrMiss);
             }
             if (prec == MOE_PREC_BF16 && M >= a.gemm_min) tb = (M + BIG - 1) / BIG;
