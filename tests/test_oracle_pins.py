@@ -277,6 +277,51 @@ def test_ffn_bf16_mode_closed_form():
     assert abs(expect - f * (2.0 ** -5 * 7) * _silu(g) * u) > 0
 
 
+def _bf16_nearest(v: float) -> float:
+    """The bfloat16 value nearest to v, ties to an even last significand bit:
+    found by comparing v with the bf16 neighbours around its float32 truncation
+    in exact double arithmetic (a search, not a formula)."""
+    t = torch.tensor([v], dtype=torch.float64).to(torch.float32)
+    b = int(t.view(torch.int32).item()) & 0xFFFF0000  # truncate toward zero in bf16 bits
+    cands = [b - 0x10000, b, b + 0x10000, b + 0x20000]
+    vals = [float(torch.tensor([c], dtype=torch.int64).to(torch.int32).view(torch.float32).item()) for c in cands]
+    best = None
+    for c, x in zip(cands, vals):
+        dist = abs(x - v)
+        key = (dist, (c >> 16) & 1)  # nearer first; on a tie the even significand
+        if best is None or key < best[0]:
+            best = (key, x)
+    return best[1]
+
+
+@pytest.mark.parametrize("qtype,codes", [(synth.Q8_0, (3, -5, 7)), (synth.Q4_0, (11, 2, 14))])
+def test_ffn_bf16_mode_rounds_activations_and_weights(qtype, codes):
+    """BF16 mode with inputs that are NOT bf16-exact: x = 1 + 2^-8 + 2^-10 rounds
+    up to 1 + 2^-7, and each d*q (fp16 scale ~0.1 times the code) rounds too.
+    The closed form of the constant expert then differs from the unrounded one
+    by far more than the tolerance, so dropping either rounding fails here."""
+    d, f = 256, 128
+    sbits = (0x2E66, 0x2A8F, 0x2C01)  # 0.0999755859375, 0.045013427734375, 0.06256103515625
+    rec = synth.expert_record_fixed(qtype, d, f, sbits, codes)
+    xv = 1.0 + 2.0 ** -8 + 2.0 ** -10
+    x = np.full(d, xv)
+    y = oracle.expert_ffn(qtype, oracle.PREC_BF16, rec, d, f, x)
+    val = [c if qtype == synth.Q8_0 else c - 8 for c in codes]
+    wg, wu, wd = (_bf16_nearest(_f16(b) * v) for b, v in zip(sbits, val))
+    xb = _bf16_nearest(xv)
+    assert xb == 1.0 + 2.0 ** -7
+    S = d * xb
+    h = _bf16_nearest(_silu(wg * S) * (wu * S))
+    expect = f * wd * h
+    np.testing.assert_allclose(y, expect, rtol=1e-14)
+    # the unrounded closed form is far away: each rounding matters
+    raw_w = [_f16(b) * v for b, v in zip(sbits, val)]
+    unrounded = f * raw_w[2] * _silu(raw_w[0] * d * xv) * (raw_w[1] * d * xv)
+    assert abs(unrounded - expect) > 1e-3 * abs(expect)
+    x_only = f * wd * _bf16_nearest(_silu(wg * d * xv) * (wu * d * xv))
+    assert abs(x_only - expect) > 1e-3 * abs(expect)
+
+
 def test_layer_linear_in_routing_weights():
     wl = synth.workload("tiny")
     d, f = wl["d"], wl["f"]
