@@ -84,6 +84,20 @@ static int block_code(int qtype, const uint8_t* blk, int j) {
     return (j < 16 ? (byte & 0x0f) : (byte >> 4)) - 8;
 }
 
+/* Nearest bfloat16 of a value that binary32 holds exactly and that is zero or
+ * normal in binary32 (every d*q: at most 18 significant bits, magnitude
+ * between 2^-24 and 2^23): round-to-nearest-even on the binary32 bits, i.e.
+ * add half of the dropped 16 bits' weight (minus one unless the kept last
+ * bit is odd) and truncate.  Same results as orc_bf16_round on such values. */
+static double bf16_round_exact_f32(double v) {
+    float f = (float)v;
+    uint32_t b;
+    memcpy(&b, &f, sizeof b);
+    b = (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
+    memcpy(&f, &b, sizeof f);
+    return (double)f;
+}
+
 void orc_dequant(int qtype, int prec, const uint8_t* blocks, int64_t n_elems, double* out) {
     size_t bb = orc_block_bytes(qtype);
     for (int64_t b = 0; b < n_elems / 32; b++) {
@@ -91,7 +105,7 @@ void orc_dequant(int qtype, int prec, const uint8_t* blocks, int64_t n_elems, do
         double d = orc_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
         for (int j = 0; j < 32; j++) {
             double w = d * (double)block_code(qtype, blk, j); /* exact: <= 18 significant bits */
-            out[b * 32 + j] = prec == ORC_PREC_BF16 ? orc_bf16_round(w) : w;
+            out[b * 32 + j] = prec == ORC_PREC_BF16 ? bf16_round_exact_f32(w) : w;
         }
     }
 }
