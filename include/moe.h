@@ -376,6 +376,18 @@ moe_status moe_probe_mfma(int32_t iters, int32_t grid, int32_t shape, float* sin
 /* Device address of the page table ([n_layers x n_experts] int32), for tests. */
 moe_status moe_page_table(const moe_ctx* ctx, int32_t** out);
 
+/* Inspection of the chunk path's hidden state (calls of more than 4 tokens;
+ * the SwiGLU hidden state h = silu(W_g x) * (W_u x) is the quantity that
+ * MOE_PREC_BF16 rounds to bf16).  *out receives the device address of the
+ * context's hidden-row workspace [max_tokens * top_k + max_tokens, d_ff] as
+ * the last such moe_expert_ffn left it: row p < T * top_k is plan position p
+ * (the entry plan.entries[p]), row T * top_k + t the shared expert on token t,
+ * where T is that call's token count.  *elem_bytes receives 2 (bf16, the
+ * codes of MOE_PREC_BF16) or 4 (fp32, MOE_PREC_F32) for the last call's mode.
+ * Read it after that call completes and before the next one.  MOE_EINVAL for
+ * a context whose max_tokens is at most 4 or that has not run such a call. */
+moe_status moe_hidden_rows(const moe_ctx* ctx, void** out, int32_t* elem_bytes);
+
 #ifdef __cplusplus
 }
 #endif

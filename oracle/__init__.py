@@ -35,6 +35,9 @@ def _load() -> C.CDLL:
     if not os.path.exists(_SO):
         build()
     lib = C.CDLL(_SO)
+    if not hasattr(lib, "orc_bf16_round_array"):  # built from an older oracle.c
+        build()
+        lib = C.CDLL(_SO)
     P = C.c_void_p
     sig = {
         "orc_set_threads": (C.c_int, [C.c_int]),
@@ -46,6 +49,9 @@ def _load() -> C.CDLL:
         "orc_topk": (C.c_int, [P, C.c_int64, C.c_int, C.c_int, C.c_int, P, P]),
         "orc_plan_union": (C.c_int, [P, C.c_int64, C.c_int, C.c_int, P, P, P, P]),
         "orc_expert_ffn": (None, [C.c_int, C.c_int, P, C.c_int, C.c_int, P, P]),
+        "orc_expert_hidden": (None, [C.c_int, C.c_int, P, C.c_int, C.c_int, P, P]),
+        "orc_expert_down": (None, [C.c_int, C.c_int, P, C.c_int, C.c_int, P, P]),
+        "orc_bf16_round_array": (None, [P, C.c_int64, P]),
         "orc_moe_layer": (C.c_int, [C.c_int, C.c_int, P, C.c_int, P, C.c_int, C.c_int,
                                     C.c_int64, C.c_int, P, P, P, P]),
     }
@@ -77,8 +83,10 @@ def f16_to_f64(bits) -> np.ndarray:
 
 
 def bf16_round(v) -> np.ndarray:
-    a = np.asarray(v, dtype=np.float64).reshape(-1)
-    return np.array([_lib.orc_bf16_round(float(x)) for x in a], dtype=np.float64)
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.float64).reshape(-1))
+    out = np.empty_like(a)
+    _lib.orc_bf16_round_array(_p(a), a.size, _p(out))
+    return out
 
 
 def x_to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -135,6 +143,24 @@ def expert_ffn(qtype: int, prec: int, rec: np.ndarray, d: int, f: int, x64: np.n
     x64 = np.ascontiguousarray(x64, dtype=np.float64).reshape(d)
     y = np.empty(d, dtype=np.float64)
     _lib.orc_expert_ffn(qtype, prec, _p(rec), d, f, _p(x64), _p(y))
+    return y
+
+
+def expert_hidden(qtype: int, prec: int, rec: np.ndarray, d: int, f: int, x64: np.ndarray) -> np.ndarray:
+    """h = silu(W_g x) * (W_u x) before any rounding of h (f values)."""
+    rec = np.ascontiguousarray(rec, dtype=np.uint8)
+    x64 = np.ascontiguousarray(x64, dtype=np.float64).reshape(d)
+    h = np.empty(f, dtype=np.float64)
+    _lib.orc_expert_hidden(qtype, prec, _p(rec), d, f, _p(x64), _p(h))
+    return h
+
+
+def expert_down(qtype: int, prec: int, rec: np.ndarray, d: int, f: int, h: np.ndarray) -> np.ndarray:
+    """y = W_d h for a given hidden state h (f values)."""
+    rec = np.ascontiguousarray(rec, dtype=np.uint8)
+    h = np.ascontiguousarray(h, dtype=np.float64).reshape(f)
+    y = np.empty(d, dtype=np.float64)
+    _lib.orc_expert_down(qtype, prec, _p(rec), d, f, _p(h), _p(y))
     return y
 
 

@@ -178,18 +178,17 @@ int orc_plan_union(const int32_t* ids, int64_t T, int k, int E, int32_t* n_activ
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
-void orc_expert_ffn(int qtype, int prec, const uint8_t* rec, int d, int f,
-                    const double* x_in, double* y) {
+/* The hidden state of one SwiGLU expert, before any rounding of it:
+ * h[r] = silu(g_r) * u_r with g = W_g x, u = W_u x (x rounded to bf16 first
+ * in bf16 mode). */
+void orc_expert_hidden(int qtype, int prec, const uint8_t* rec, int d, int f,
+                       const double* x_in, double* h) {
     size_t bb = orc_block_bytes(qtype);
     size_t row_in_d = (size_t)(d / 32) * bb; /* bytes of one gate/up row */
-    size_t row_in_f = (size_t)(f / 32) * bb; /* bytes of one down row */
     const uint8_t* gate = rec;
     const uint8_t* up = gate + (size_t)f * row_in_d;
-    const uint8_t* down = up + (size_t)f * row_in_d;
     double* x = (double*)malloc(sizeof(double) * (size_t)d);
-    double* h = (double*)malloc(sizeof(double) * (size_t)f);
     for (int i = 0; i < d; i++) x[i] = prec == ORC_PREC_BF16 ? orc_bf16_round(x_in[i]) : x_in[i];
-
 #pragma omp parallel
     {
         double* wg = (double*)malloc(sizeof(double) * (size_t)d);
@@ -203,11 +202,23 @@ void orc_expert_ffn(int qtype, int prec, const uint8_t* rec, int d, int f,
                 g += wg[i] * x[i];
                 u += wu[i] * x[i];
             }
-            double hr = silu(g) * u;
-            h[r] = prec == ORC_PREC_BF16 ? orc_bf16_round(hr) : hr;
+            h[r] = silu(g) * u;
         }
         free(wg);
         free(wu);
+    }
+    free(x);
+}
+
+/* The down projection of one expert on a given hidden state: y = W_d h. */
+void orc_expert_down(int qtype, int prec, const uint8_t* rec, int d, int f,
+                     const double* h, double* y) {
+    size_t bb = orc_block_bytes(qtype);
+    size_t row_in_d = (size_t)(d / 32) * bb;
+    size_t row_in_f = (size_t)(f / 32) * bb; /* bytes of one down row */
+    const uint8_t* down = rec + 2 * (size_t)f * row_in_d;
+#pragma omp parallel
+    {
         double* wd = (double*)malloc(sizeof(double) * (size_t)f);
 #pragma omp for schedule(static)
         for (int i = 0; i < d; i++) {
@@ -218,8 +229,22 @@ void orc_expert_ffn(int qtype, int prec, const uint8_t* rec, int d, int f,
         }
         free(wd);
     }
-    free(x);
+}
+
+/* The expert: its hidden state (rounded to bf16 in bf16 mode), then the down
+ * projection. */
+void orc_expert_ffn(int qtype, int prec, const uint8_t* rec, int d, int f,
+                    const double* x_in, double* y) {
+    double* h = (double*)malloc(sizeof(double) * (size_t)f);
+    orc_expert_hidden(qtype, prec, rec, d, f, x_in, h);
+    if (prec == ORC_PREC_BF16)
+        for (int r = 0; r < f; r++) h[r] = orc_bf16_round(h[r]);
+    orc_expert_down(qtype, prec, rec, d, f, h, y);
     free(h);
+}
+
+void orc_bf16_round_array(const double* v, int64_t n, double* out) {
+    for (int64_t i = 0; i < n; i++) out[i] = orc_bf16_round(v[i]);
 }
 
 int orc_moe_layer(int qtype, int prec, const uint8_t* const* experts, int E,

@@ -60,6 +60,16 @@ int orc_plan_union(const int32_t* ids, int64_t T, int k, int E, int32_t* n_activ
  * blocks along the row (the input dimension). */
 void orc_expert_ffn(int qtype, int prec, const uint8_t* rec, int d, int f,
                     const double* x, double* y);
+/* Its two halves: the hidden state h = silu(W_g x) * (W_u x) before any
+ * rounding of h (x rounded to bf16 first in bf16 mode; f values), and the
+ * down projection y = W_d h of a given hidden state.  orc_expert_ffn is the
+ * first, then (bf16 mode) orc_bf16_round of each h, then the second. */
+void orc_expert_hidden(int qtype, int prec, const uint8_t* rec, int d, int f,
+                       const double* x, double* h);
+void orc_expert_down(int qtype, int prec, const uint8_t* rec, int d, int f,
+                     const double* h, double* y);
+/* orc_bf16_round of each of n values */
+void orc_bf16_round_array(const double* v, int64_t n, double* out);
 
 /* Routed layer: y[t] = sum_j w[t,j] * FFN_{ids[t,j]}(x[t]) + FFN_shared(x[t]),
  * summed in double in rank order j, shared expert last, rounded to float.

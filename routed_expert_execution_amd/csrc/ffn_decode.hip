@@ -623,6 +623,7 @@ struct DownLds {
     int tok[kMaxRows];                // hidden row -> token
     float w[kMaxRows];                // hidden row -> weight
     int flag[4];
+    int cnt[kDecodeMaxT];             // plan positions the units cover, per token
     int64_t uoff[kMaxUnits + 3];      // unit -> payload offset in the pool (-1 absent, -2 shared)
     alignas(16) float red[kWaves][kDecodeMaxT][16];
     alignas(16) float zero[kQK];      // a zero block of activations (rows a bucket does not have)
@@ -669,6 +670,7 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         L.wbe[i1] = __uint_as_float(opaque(w1));
     }
     if (threadIdx.x == 0) L.flag[0] = 1;
+    if (threadIdx.x < kDecodeMaxT) L.cnt[threadIdx.x] = 0;
     if (threadIdx.x < kQK) L.zero[threadIdx.x] = 0.f;
     lds_barrier();
     const int par = __builtin_amdgcn_readfirstlane(launch_parity(opaque(count), g.n_down));
@@ -735,12 +737,16 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         td[i].load(tp ? tp : fallback, lane);
     }
     // Token and weight of every hidden row (the shared rows: token t, weight 1).
+    // A token counts the plan positions the units cover that are its own: a
+    // token with fewer than top_k (the plan dropped an out-of-range id) gets a
+    // NaN row, as the chunk path's combine gives it.
     if (threadIdx.x < kMaxRows) {
         const int v = threadIdx.x;
         if (v < n_ent) {
             const int ent = L.ent[v];
             L.tok[v] = ent / a.k;
             L.w[v] = L.wbe[ent];
+            if (v < L.off[na]) atomicAdd(&L.cnt[ent / a.k], 1);
         } else {
             L.tok[v] = v - n_ent;
             L.w[v] = 1.f;
@@ -784,9 +790,13 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         const int vb = min(v_end(ub - 1), va + g.nb_rows);  // (a valid plan never clips)
         // Stage rows [va, vb) straight into LDS with device-scope loads (1 KB
         // per wave instruction, no registers), until no pending word is left.
+        // Rows [off[na], T k) belong to no unit (entries the plan dropped) and
+        // are never written: the pending check skips them.
         const int n16 = max(vb - va, 0) * g.f / 4;  // 16-byte pieces
         const int n_ins = (n16 + 63) / 64;
         const float* src = hhalf + (int64_t)va * g.f;
+        const int gap0 = (max(min(L.off[na], n_ent), va) - va) * g.f / 4;  // pieces [gap0, gap1) unused
+        const int gap1 = (max(n_ent, va) - va) * g.f / 4;
         for (;;) {
             for (int j = wave; j < n_ins; j += kWaves)
                 __builtin_amdgcn_global_load_lds(src + 4 * min(j * 64 + lane, n16 - 1),
@@ -797,7 +807,8 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
             int pend = 0;
             for (int i = threadIdx.x; i < n16; i += kThreads) {
                 const uint4 b = *(const uint4*)(L.hs + 4 * i);
-                pend |= (b.x == kPending) | (b.y == kPending) | (b.z == kPending) | (b.w == kPending);
+                const bool used = i < gap0 || i >= gap1;
+                pend |= used && ((b.x == kPending) | (b.y == kPending) | (b.z == kPending) | (b.w == kPending));
             }
             if (!__syncthreads_or(pend) && a.wait_ticks >= 0) break;
             const int expired = threadIdx.x == 0 && (a.wait_ticks < 0 || (int64_t)(wall_clock64() - t0) > a.wait_ticks);
@@ -898,7 +909,7 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
         float y = 0.f;
         for (int w = 0; w < kWaves; w++) y += L.red[w][t][r];
-        a.y[(int64_t)t * g.d + 16 * R + r] = L.flag[0] ? y : __uint_as_float(0x7FC00000u);
+        a.y[(int64_t)t * g.d + 16 * R + r] = L.flag[0] && L.cnt[t] == a.k ? y : __uint_as_float(0x7FC00000u);
     }
     // This launch is done with its half: count it (no return needed), once every
     // gate/up workgroup of a launch that routes has arrived.

@@ -64,7 +64,7 @@ __device__ inline const uint8_t* tile_base(const PrefillArgs& a, const TileRec& 
 
 // Token and workspace row of tile row m.
 __device__ inline int row_token(const PrefillArgs& a, const TileRec& t, int m) {
-    return t.slot == kShared ? t.first + m : a.entries[t.first + m] / a.k;
+    return t.slot == kShared ? t.first + m : min(max(a.entries[t.first + m], 0), a.T * a.k - 1) / a.k;
 }
 __device__ inline int row_slot(const PrefillArgs& a, const TileRec& t, int m) {
     return t.slot == kShared ? a.T * a.k + t.first + m : t.first + m;
@@ -99,11 +99,21 @@ __device__ int block_prefix(int v, int* wave_tot, int* total) {
 // the first 4 blockDim.x entries are loaded before the schedule's own chain of
 // dependent loads (n_active, then offsets and experts, then the page table),
 // so that their round trips overlap.
+//
+// The plan is an input of the C ABI, so the schedule checks it rather than
+// trusting it: n_active is clamped to [0, min(E, T k)], each unit's offsets to
+// [0, T k] with offsets[u] <= offsets[u + 1], and records beyond the arrays'
+// capacity are dropped; any of these sets kErrBadId.  Only the plan positions
+// the units cover, [0, offsets[n_active]), enter the inverse map, and
+// n_tiles[2] tells the combine where that range ends, so an entry the plan
+// dropped (an out-of-range expert id) or a stale word past the range never
+// stands for another entry.
 constexpr int kSchedInvAhead = 4;
 
 __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec) {
     __shared__ int wave_tot[16];
     __shared__ int tot_b, tot_s;
+    __shared__ int s_bad, s_nvalid;
     const int n_ent = a.T * a.k;
     int ent_ahead[kSchedInvAhead];
 #pragma unroll
@@ -124,7 +134,13 @@ __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec)
         return r;
     };
     const UnitIn first = unit_in(threadIdx.x);
-    const int na = *a.n_active;
+    const int na_raw = *a.n_active;
+    const int na = min(max(na_raw, 0), min(a.E, n_ent));
+    if (threadIdx.x == 0) {
+        s_bad = na != na_raw;
+        s_nvalid = 0;
+    }
+    __syncthreads();
     const int n_units = na + (a.shared ? 1 : 0);
     int base_b = 0, base_s = 0;
     for (int u0 = 0; u0 < n_units; u0 += 1024) {
@@ -135,8 +151,11 @@ __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec)
                 M = a.T;
             } else {
                 const UnitIn in = u0 == 0 ? first : unit_in(u);
-                p0 = in.p0;
-                M = in.p1 - in.p0;
+                p0 = min(max(in.p0, 0), n_ent);
+                const int p1 = min(max(in.p1, 0), n_ent);
+                if (p0 != in.p0 || p1 != in.p1 || p1 < p0) s_bad = 1;
+                M = max(p1 - p0, 0);
+                if (u == na - 1) s_nvalid = p1;
                 slot = kUnmapped;
                 if (in.e >= 0 && in.e < a.E && in.sl >= 0 && in.sl < a.n_slots) slot = in.sl;
                 if (slot == kUnmapped) atomicOr(a.err, kErrMiss);
@@ -146,24 +165,32 @@ __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec)
         }
         const int fb = base_b + block_prefix(tb, wave_tot, &tot_b);
         const int fs = base_s + block_prefix(ts, wave_tot, &tot_s);
-        for (int i = 0; i < tb; i++)
+        for (int i = 0; i < tb; i++) {
+            if (fb + i >= a.cap_big) { s_bad = 1; break; }
             ((int4*)a.sched_big)[fb + i] = make_int4(slot, p0 + i * BIG, min(BIG, M - i * BIG), 0);
-        for (int i = 0; i < ts; i++)
+        }
+        for (int i = 0; i < ts; i++) {
+            if (fs + i >= a.cap_small) { s_bad = 1; break; }
             ((int4*)a.sched_small)[fs + i] = make_int4(slot, p0 + i * SMALL, min(SMALL, M - i * SMALL), 0);
+        }
         base_b += tot_b;
         base_s += tot_s;
         __syncthreads();
     }
+    const int n_valid = s_nvalid;
     if (threadIdx.x == 0) {
-        a.n_tiles[0] = base_b;
-        a.n_tiles[1] = base_s;
+        a.n_tiles[0] = min(base_b, a.cap_big);
+        a.n_tiles[1] = min(base_s, a.cap_small);
+        a.n_tiles[2] = n_valid;
+        if (s_bad) atomicOr(a.err, kErrBadId);
     }
 #pragma unroll
     for (int q = 0; q < kSchedInvAhead; q++) {
+        const int p = threadIdx.x + q * (int)blockDim.x;
         const int ent = ent_ahead[q];
-        if (ent >= 0 && ent < n_ent) a.inv[ent] = threadIdx.x + q * (int)blockDim.x;
+        if (p < n_valid && ent >= 0 && ent < n_ent) a.inv[ent] = p;
     }
-    for (int p = threadIdx.x + kSchedInvAhead * (int)blockDim.x; p < n_ent; p += blockDim.x) {
+    for (int p = threadIdx.x + kSchedInvAhead * (int)blockDim.x; p < n_valid; p += blockDim.x) {
         const int ent = a.entries[p];
         if (ent >= 0 && ent < n_ent) a.inv[ent] = p;
     }
@@ -682,20 +709,33 @@ __global__ __launch_bounds__(256, BIGT ? 2 : (PREC == MOE_PREC_BF16 ? 4 : 3)) vo
 
 // ---- combine ---------------------------------------------------------------------
 
+// A token's entry is taken only if the inverse map leads to a plan position
+// the units cover that holds that very entry; otherwise (the plan dropped it,
+// or the map holds a stale word from an earlier call) the row is quiet NaN.
 __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     const int t = blockIdx.y;
     const int i4 = blockIdx.x * blockDim.x + threadIdx.x;  // output quad
     if (i4 * 4 >= a.d) return;
+    const int n_valid = a.n_tiles[2];
     float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+    bool ok = true;
     for (int j = 0; j < a.k; j++) {
-        const int p = a.inv[t * a.k + j];
-        const float w = a.topk_w[t * a.k + j];
-        const float4 v = *(const float4*)(a.part + (int64_t)p * a.d + i4 * 4);
+        const int e = t * a.k + j;
+        const int p = a.inv[e];
+        const bool in = p >= 0 && p < n_valid;
+        const int pc = in ? p : 0;
+        const float w = a.topk_w[e];
+        const float4 v = *(const float4*)(a.part + (int64_t)pc * a.d + i4 * 4);
+        ok = ok && in && a.entries[pc] == e;
         y.x = fmaf(w, v.x, y.x); y.y = fmaf(w, v.y, y.y); y.z = fmaf(w, v.z, y.z); y.w = fmaf(w, v.w, y.w);
     }
     if (a.shared) {
         const float4 v = *(const float4*)(a.part + (int64_t)(a.T * a.k + t) * a.d + i4 * 4);
         y.x += v.x; y.y += v.y; y.z += v.z; y.w += v.w;
+    }
+    if (!ok) {
+        const float q = __uint_as_float(0x7FC00000u);
+        y = make_float4(q, q, q, q);
     }
     *(float4*)(a.y + (int64_t)t * a.d + i4 * 4) = y;
 }

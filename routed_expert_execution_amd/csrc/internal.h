@@ -173,9 +173,10 @@ struct PrefillArgs {
                            // bf16 in bf16 mode, fp32 otherwise
     float* part;           // [T*k + T, d] partial output rows
     int32_t* inv;          // [T*k] plan position of entry t*k + j
-    int32_t* sched_big;    // [4 * big_tiles] tile records (16-byte aligned), 64-token tiles
-    int32_t* sched_small;  // [4 * small_tiles] tile records (16-byte aligned), 16-token tiles
-    int32_t* n_tiles;      // [2] tiles of each size
+    int32_t* sched_big;    // [4 * cap_big] tile records (16-byte aligned), 64-token tiles
+    int32_t* sched_small;  // [4 * cap_small] tile records (16-byte aligned), 16-token tiles
+    int32_t* n_tiles;      // [4]: tiles of each size, the plan positions the units cover, unused
+    int cap_big, cap_small;  // records the two arrays hold
     float* y;
     int* err;
 };

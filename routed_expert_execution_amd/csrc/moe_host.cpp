@@ -31,8 +31,9 @@ struct moe_ctx {
     float* ph = nullptr;
     float* ppart = nullptr;
     int32_t* pinv = nullptr;
-    int32_t* psched = nullptr;  // big tiles, small tiles, 2 counts
+    int32_t* psched = nullptr;  // big tiles, small tiles, 4 counts
     int p_big = 0, p_small = 0;
+    int last_prefill_prec = -1; // mode of the last chunk call (-1: none yet)
     float* logits_ws = nullptr;// [max_T * E]
 
     // slot manager (host)
@@ -392,7 +393,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
             if (hipMalloc(&c->ph, sizeof(float) * rows * cfg->d_ff) != hipSuccess) return cleanup(MOE_ENOMEM);
             if (hipMalloc(&c->ppart, sizeof(float) * rows * cfg->d_model) != hipSuccess) return cleanup(MOE_ENOMEM);
             if (hipMalloc(&c->pinv, sizeof(int32_t) * (size_t)T * cfg->top_k) != hipSuccess) return cleanup(MOE_ENOMEM);
-            if (hipMalloc(&c->psched, sizeof(int32_t) * (4 * ((size_t)c->p_big + c->p_small) + 2)) != hipSuccess)
+            if (hipMalloc(&c->psched, sizeof(int32_t) * (4 * ((size_t)c->p_big + c->p_small) + 4)) != hipSuccess)
                 return cleanup(MOE_ENOMEM);
         }
         if (hipMemset(c->pt, 0xFF, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_EHIP);
@@ -918,9 +919,12 @@ moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     p.sched_big = c->psched;
     p.sched_small = c->psched + 4 * (size_t)c->p_big;
     p.n_tiles = p.sched_small + 4 * (size_t)c->p_small;
+    p.cap_big = c->p_big;
+    p.cap_small = c->p_small;
     p.y = y;
     p.err = c->err_word;
     HIP_TRY(c, moe::launch_ffn_prefill(p, prec, moe::PrefillStreams{s, c->aux, c->fork_ev, c->join_ev}));
+    c->last_prefill_prec = prec;
     return MOE_OK;
 }
 
@@ -1008,6 +1012,13 @@ moe_status moe_probe_mfma(int32_t iters, int32_t grid, int32_t shape, float* sin
 moe_status moe_page_table(const moe_ctx* c, int32_t** out) {
     if (!c || !out || c->host_only) return MOE_EINVAL;
     *out = c->pt;
+    return MOE_OK;
+}
+
+moe_status moe_hidden_rows(const moe_ctx* c, void** out, int32_t* elem_bytes) {
+    if (!c || !out || !elem_bytes || c->host_only || !c->ph || c->last_prefill_prec < 0) return MOE_EINVAL;
+    *out = c->ph;
+    *elem_bytes = c->last_prefill_prec == MOE_PREC_BF16 ? 2 : 4;
     return MOE_OK;
 }
 

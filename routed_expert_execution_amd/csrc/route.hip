@@ -8,11 +8,13 @@
 //   the logits are reproducible bit for bit.
 // route_union (T <= kFusedMaxT): the same logits, then top-k and the union in
 //   one single-workgroup launch (see below).
-// topk: one wave per token.  Each lane keeps its logits as 64-bit keys
-//   (order-preserving float bits << 32 | ~expert), so one unsigned max picks
-//   the larger logit and, on ties, the lower expert index; k rounds of a wave
-//   max select the experts.  Weights are the softmax over the selected logits
-//   (or over all, norm == 0), in fp32.
+// topk: one wave per token.  Each lane keeps its logits as order-preserving
+//   32-bit keys (-0 ranked with +0) and the best key it still has; a round
+//   takes the wave's largest key with one 32-bit DPP/permlane max, then every
+//   lane offers the lowest expert index holding that key and one DPP min picks
+//   the lowest of all (ties to the lower index); k rounds select the experts.
+//   Weights are the softmax over the selected logits (or over all, norm == 0),
+//   in fp32.
 #include "internal.h"
 #include "route_device.h"
 

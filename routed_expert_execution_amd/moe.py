@@ -81,6 +81,7 @@ def _load() -> C.CDLL:
         "moe_stats": (C.c_int, [P, C.POINTER(C.c_uint64)]),
         "moe_check": (C.c_int, [P, P]),
         "moe_page_table": (C.c_int, [P, C.POINTER(P)]),
+        "moe_hidden_rows": (C.c_int, [P, C.POINTER(P), C.POINTER(I32)]),
         "moe_probe_read": (C.c_int, [P, I64, I32, P, P]),
         "moe_probe_mfma": (C.c_int, [I32, I32, I32, P, C.POINTER(I64), P]),
     }
@@ -96,7 +97,7 @@ EXPORTS = ("moe_payload_bytes", "moe_plan_bytes", "moe_pack_expert", "moe_unpack
            "moe_destroy", "moe_last_error", "moe_status_string", "moe_route", "moe_plan_union", "moe_route_union",
            "moe_slot_map", "moe_slot_prefetch", "moe_prefetch_stats", "moe_slot_fill", "moe_slot_stage", "moe_slot_pull", "moe_route_pull", "moe_slot_release",
            "moe_slot_bind", "moe_expert_ffn",
-           "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table", "moe_probe_read",
+           "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table", "moe_hidden_rows", "moe_probe_read",
            "moe_probe_mfma")
 
 
@@ -498,6 +499,28 @@ def moe_page_table(ctx: Context) -> np.ndarray:
     if st != 0:
         raise MoeError(MOE_EHIP, f"hipMemcpy of the page table failed ({st})")
     return out
+
+
+def moe_hidden_rows(ctx: Context, rows: int):
+    """Copy of the first `rows` hidden rows the last chunk call (more than 4
+    tokens) left in the workspace, as float32 [rows, d_ff] (bf16 codes widened
+    exactly); synchronises the device."""
+    import torch
+    p = C.c_void_p()
+    eb = C.c_int32()
+    _call(ctx, _lib.moe_hidden_rows(ctx.handle, C.byref(p), C.byref(eb)))
+    f = ctx.cfg.d_ff
+    raw = np.empty(rows * f * eb.value, dtype=np.uint8)
+    torch.cuda.synchronize(ctx.device)
+    hip = C.CDLL("libamdhip64.so")
+    hip.hipMemcpy.restype = C.c_int
+    hip.hipMemcpy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int]
+    st = hip.hipMemcpy(raw.ctypes.data, p.value, raw.nbytes, 2)  # hipMemcpyDeviceToHost
+    if st != 0:
+        raise MoeError(MOE_EHIP, f"hipMemcpy of the hidden rows failed ({st})")
+    if eb.value == 4:
+        return raw.view(np.float32).reshape(rows, f).copy()
+    return (raw.view(np.uint16).astype(np.uint32) << 16).view(np.float32).reshape(rows, f)
 
 
 def moe_probe_read(src, sink, workgroups: int = 0, stream=None) -> None:

@@ -24,8 +24,9 @@ Policies:
     is evicted: the farthest-next-use bound the others are measured against
     ("Paging the Experts", §5.1), which needs the whole trace in advance.
 
-Synthetic traces: :func:`markov_trace` (per-layer Markov chains, the 40-layer
-stack's routes) and :func:`cyclic_trace` (one layer cycling through ``n``
+Traces come from the caller (the synthetic per-layer Markov chains of the
+40-layer stack are built by ``synth.markov_trace``); :func:`cyclic_trace`
+builds the capacity-cliff trace (one layer cycling through ``n``
 experts one at a time: with fewer than ``n`` slots, LRU evicts each expert
 just before it comes back and never hits, "Paging the Experts", §5.1).
 """
@@ -36,15 +37,6 @@ import random
 from collections import Counter, OrderedDict
 
 POLICIES = ("lru", "random", "static", "belady")
-
-
-def markov_trace(seed: int, n_layers: int, n_tokens: int, n_experts: int, k: int, p_repeat: float) -> list:
-    """Steps (layer, experts) for n_tokens tokens through n_layers layers, each
-    layer's route a Markov chain over tokens (the stack workload's routes)."""
-    import synth
-    chains = [synth.markov_route_sets(synth.rng(seed, 55, l), n_tokens, n_experts, k, p_repeat)
-              for l in range(n_layers)]
-    return [(l, sorted(int(e) for e in chains[l][t])) for t in range(n_tokens) for l in range(n_layers)]
 
 
 def cyclic_trace(n: int, cycles: int, layer: int = 0) -> list:

@@ -62,3 +62,23 @@ def max_rel_row_err(y: np.ndarray, ref: np.ndarray) -> float:
     ref = np.asarray(ref, np.float64).reshape(ref.shape[0], -1)
     den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
     return float((np.abs(y - ref).max(axis=1) / den).max())
+
+
+def elementwise_stats(y: np.ndarray, ref: np.ndarray) -> dict:
+    """Element-wise error statistics beside the per-row metric: the largest
+    absolute error, the largest error relative to its own element (over
+    elements at least 1e-3 of their row's largest magnitude), the relative
+    RMS error over all elements, and the fraction of elements whose error
+    exceeds 1e-3 of their row's largest magnitude."""
+    y = np.asarray(y, np.float64).reshape(ref.shape[0], -1)
+    ref = np.asarray(ref, np.float64).reshape(ref.shape[0], -1)
+    err = np.abs(y - ref)
+    rowmax = np.maximum(np.abs(ref).max(axis=1, keepdims=True), 1e-30)
+    big = np.abs(ref) >= 1e-3 * rowmax
+    return {
+        "max_rel_row": float((err.max(axis=1) / rowmax[:, 0]).max()),
+        "max_abs": float(err.max()),
+        "max_rel_elem": float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0,
+        "rel_rms": float(np.sqrt((err ** 2).sum() / max((ref ** 2).sum(), 1e-300))),
+        "frac_over_1e-3_of_row": float((err > 1e-3 * rowmax).mean()),
+    }

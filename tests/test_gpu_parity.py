@@ -82,7 +82,7 @@ def _delta_band(x64, wr):
     return 2 * gamma * (np.abs(x64) @ np.abs(wr.astype(np.float64)).T).max(axis=1)
 
 
-@pytest.mark.parametrize("name,T", [("tiny", 4), ("decode", 1), ("decode", 64)])
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("decode", 1), ("decode", 64), ("decode", 512)])
 def test_route_from_router_weights(name, T):
     wl = synth.workload(name)
     _say("route", name, T)
@@ -104,17 +104,29 @@ def test_route_from_router_weights(name, T):
     assert np.array_equal(g_ids, r_ids)
     np.testing.assert_allclose(g_w, r_w, rtol=1e-6, atol=1e-7)
     # (ii) end to end.  eps_t = this token's largest |gpu - oracle| logit difference
-    # (itself within the rounding band above).  Where every consecutive gap among the
-    # oracle's k+1 largest logits exceeds 2 eps_t, no perturbation of that size can
-    # change the ranked ids, so they must be identical; other tokens have several
-    # correct answers and are covered by (i).
+    # (itself within the rounding band above).  No perturbation of that size can
+    # reorder two logits more than 2 eps_t apart, so:
+    #  - where the gap between the oracle's k-th and (k+1)-th logits exceeds
+    #    2 eps_t, the selected SET must be identical;
+    #  - where every consecutive gap among the oracle's k + 1 largest exceeds
+    #    2 eps_t, the ranked ids must be identical too.
+    # Other tokens have several correct answers and are covered by (i).  The
+    # logits have a spread of about 0.02 sqrt(d) (about 0.9 at d = 2048), so
+    # neighbouring order statistics sit 1e-3 .. 1e-1 apart against eps_t of
+    # about 1e-6: a gap inside 2 eps_t has a chance of order 1e-4 per token, and
+    # at least 95 % of the tokens must be clear in both senses.
     o_ids, _ = oracle.topk(o_lo, wl["k"])
+    k = wl["k"]
     eps = np.abs(g_lo.astype(np.float64) - o_lo).max(axis=1)
-    srt = -np.sort(-o_lo.astype(np.float64), axis=1)[:, : wl["k"] + 1]
-    clear = (-np.diff(srt, axis=1)).min(axis=1) > 2 * eps
-    _say("  tokens with forced ranking:", int(clear.sum()), "of", T, "max eps", float(eps.max()))
-    assert clear.mean() >= 0.5
-    assert np.array_equal(g_ids[clear], o_ids[clear])
+    srt = -np.sort(-o_lo.astype(np.float64), axis=1)[:, : k + 1]
+    gaps = -np.diff(srt, axis=1)
+    set_clear = gaps[:, k - 1] > 2 * eps
+    ranked_clear = gaps.min(axis=1) > 2 * eps
+    _say("  tokens with a forced set:", int(set_clear.sum()), "forced ranking:", int(ranked_clear.sum()),
+         "of", T, "max eps", float(eps.max()))
+    assert set_clear.mean() >= 0.95 and ranked_clear.mean() >= 0.95
+    assert np.array_equal(np.sort(g_ids[set_clear], axis=1), np.sort(o_ids[set_clear], axis=1))
+    assert np.array_equal(g_ids[ranked_clear], o_ids[ranked_clear])
 
 
 @pytest.mark.parametrize("E,k", [(8, 2), (256, 8), (1024, 32), (100, 7)])

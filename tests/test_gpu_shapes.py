@@ -3,7 +3,8 @@
 weight formats and both activation types.  The decode path (T <= 4) and the
 chunk path (T > 4) are checked against the CPU oracle on every token.
 
-Bar: 1e-3 maximum relative error per token row.
+Bar: 1e-3 maximum relative error per token row (the chunk path in bf16 mode:
+split at the hidden state, as in tests/test_gpu_prefill.py).
 """
 import numpy as np
 import pytest
@@ -59,6 +60,5 @@ def test_chunk_path_shapes(d, f, qt, xd, prec):
     c = Chunk(wl, T, lg, prec)
     c.place(list(range(len(c.used))))
     y = c.run()
-    err = H.max_rel_row_err(y, c.reference(np.arange(T)))
-    print("  buckets", sorted(c.bucket_sizes()[c.used].tolist()), "max rel row err", err, flush=True)
-    assert np.isfinite(y).all() and err <= FFN_TOL
+    st = c.verify(y, np.arange(T))
+    print("  buckets", sorted(c.bucket_sizes()[c.used].tolist()), st, flush=True)

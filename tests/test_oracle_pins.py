@@ -382,3 +382,22 @@ def test_tiny_layer_dense_brute_force(with_shared):
                 y_dense[t] += p[list(order).index(e)] * Y[t]
     rel = np.abs(y - y_dense).max(1) / np.abs(y_dense).max(1)
     assert rel.max() < 1e-6
+
+
+@pytest.mark.parametrize("qtype,codes", [(synth.Q8_0, (3, -2, 5)), (synth.Q4_0, (11, 6, 13))])
+def test_expert_halves_closed_forms(qtype, codes):
+    """The hidden state and the down projection on their own: a constant
+    expert gives h_r = silu(s_g c_g S) * (s_u c_u S) for every r, and
+    W_d h = s_d c_d * sum(h) for any h."""
+    d, f = 256, 128
+    sbits = (0x2E66, 0x2A8F, 0x2C00)
+    rec = synth.expert_record_fixed(qtype, d, f, sbits, codes)
+    val = [c if qtype == synth.Q8_0 else c - 8 for c in codes]
+    sg, su, sd = (_f16(b) for b in sbits)
+    x = np.random.default_rng(3).standard_normal(d)
+    S = float(np.sum(x))
+    h = oracle.expert_hidden(qtype, oracle.PREC_F32, rec, d, f, x)
+    np.testing.assert_allclose(h, _silu(sg * val[0] * S) * (su * val[1] * S), rtol=1e-12)
+    hv = np.random.default_rng(4).standard_normal(f)
+    y = oracle.expert_down(qtype, oracle.PREC_F32, rec, d, f, hv)
+    np.testing.assert_allclose(y, sd * val[2] * hv.sum(), rtol=1e-12, atol=1e-12)

@@ -7,6 +7,8 @@ import itertools
 
 import pytest
 
+import synth
+
 from routed_expert_execution_amd import replay as R
 
 
@@ -74,7 +76,7 @@ def test_cyclic_trace_belady_closed_form():
 
 
 def test_library_lru_matches_python_lru_and_policies_order_on_markov_trace():
-    tr = R.markov_trace(5, n_layers=8, n_tokens=60, n_experts=64, k=8, p_repeat=0.6)
+    tr = synth.markov_trace(5, n_layers=8, n_tokens=60, n_experts=64, k=8, p_repeat=0.6)
     cap = 96
     lib = R.replay(tr, cap, "lru")
     h, m, ev = R._lru_keys(tr, cap)
@@ -88,7 +90,7 @@ def test_library_lru_matches_python_lru_and_policies_order_on_markov_trace():
 
 
 def test_random_is_seeded_and_static_keeps_its_set():
-    tr = R.markov_trace(7, n_layers=4, n_tokens=40, n_experts=32, k=4, p_repeat=0.6)
+    tr = synth.markov_trace(7, n_layers=4, n_tokens=40, n_experts=32, k=4, p_repeat=0.6)
     assert R.replay(tr, 24, "random", seed=1) == R.replay(tr, 24, "random", seed=1)
     # a static set wide enough for every expert a layer uses, with room: compulsory misses only
     distinct = len({(l, e) for l, ex in tr for e in ex})
