@@ -174,7 +174,7 @@ def big_buckets_mfma(experts, sizes, pack, wl, flush, flush_sink, spin_cycles, n
                     "no shared expert), bf16 mode, weights cold" % BIG_BUCKET}
 
 
-def cpu_baseline(wl: dict, budget_s: float = 10.0, max_steps: int = 100_000) -> dict:
+def cpu_baseline(wl: dict, budget_s: float = 10.0, max_steps: int = 100_000, threads: int = 0) -> dict:
     """The oracle, as it stands, timed on a bounded sample of the same steps.
 
     Only the oracle's own work is timed (router logits, top-k, union, the routed
@@ -182,8 +182,7 @@ def cpu_baseline(wl: dict, budget_s: float = 10.0, max_steps: int = 100_000) -> 
     import oracle
     import synth
 
-    threads = min(16, len(os.sched_getaffinity(0)))
-    threads = oracle.set_threads(threads)
+    threads = oracle.set_threads(threads or len(os.sched_getaffinity(0)))
     E, k, d, f, T = wl["E"], wl["k"], wl["d"], wl["f"], wl["T"]
     wr = synth.router_weights(wl["seed"], E, d) if wl["name"] == "decode" else None
     shared = synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True)
@@ -228,6 +227,15 @@ def cpu_baseline(wl: dict, budget_s: float = 10.0, max_steps: int = 100_000) -> 
                        else f"{steps} {wl['name']} steps ({steps * T} tokens)")
                       + f" of the same workload: fp64 C oracle, router/top-k/union + {k} routed experts + "
                       f"shared expert per token, {compute:.1f} s of CPU work"}
+
+
+def cpu_baseline_pair(wl: dict, budget_s: float = 10.0) -> dict:
+    """The oracle on every host core the process may use, and on one core: the
+    first is the reported baseline, the second rides along."""
+    allc = cpu_baseline(wl, budget_s, threads=len(os.sched_getaffinity(0)))
+    one = cpu_baseline(wl, budget_s, threads=1)
+    allc["one_core"] = {"value": one["value"], "cores": one["cores"], "sample": one["sample"]}
+    return allc
 
 
 def _median_us(pairs) -> float:
@@ -377,7 +385,7 @@ def replay_policies(args, synth, moe) -> int:
     cfg = moe.make_config(L, E, k, wl["d"], wl["f"], moe.MOE_Q8_0, wl["n_slots"], 1, device=-1)
     pb = moe.moe_payload_bytes(cfg)
     n_tok = args.steps
-    trace = R.markov_trace(wl["seed"], L, n_tok, E, k, wl["p_repeat"])
+    trace = synth.markov_trace(wl["seed"], L, n_tok, E, k, wl["p_repeat"])
     rows = []
     for cap in (wl["n_slots"], 2 * wl["n_slots"]):
         for pol, kw in (("lru", {}), ("random", dict(seed=1)), ("static", dict(width=16)),
@@ -629,6 +637,8 @@ def main() -> int:
     ap.add_argument("--ceilings", action="store_true",
                     help="print the peak references (streaming read, pinned H2D, matrix-core loop) instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="decode: skip the 512-token chunk that the default run also times")
     ap.add_argument("--no-flush", action="store_true", help="leave L2 / Infinity Cache warm (labelled)")
     ap.add_argument("--separate-calls", action="store_true",
                     help="time steps of up to 4 tokens as moe_route_union + moe_expert_ffn, not one launch")
@@ -656,7 +666,66 @@ def main() -> int:
     if args.workload == "stack":
         return run_stack(args, torch, moe, synth)
 
-    wl = dict(synth.workload(args.workload), name=args.workload)
+    line = layer_bench(args, torch, moe, synth, args.workload, args.steps, args.warmup, args.no_flush,
+                       big=not args.no_big_buckets, warm=args.workload == "decode")
+    if line is None:
+        return 1
+    if args.workload == "decode" and not args.decode_only:
+        # the batch-512 half of the metric in the same run: the prefill chunk,
+        # cold, with its big buckets on the matrix cores
+        pre = layer_bench(args, torch, moe, synth, "prefill", min(args.steps, 20), min(args.warmup, 3),
+                          args.no_flush, big=not args.no_big_buckets)
+        if pre is None:
+            return 1
+        bb = pre["detail"]["big_buckets"] or {}
+        line["detail"]["prefill_chunk_512"] = {
+            "tokens_per_s": pre["value"], "ms_per_chunk": pre["ms_per_step"], "chunks_timed": pre["steps"],
+            "ffn_us_mean": pre["detail"]["ffn_us_mean"], "ffn_GBps": pre["detail"]["ffn_GBps"],
+            "hbm_frac_spec": pre["roofline"]["frac"],
+            "hbm_frac_measured": pre["roofline"].get("frac_of_measured"),
+            "expert_bytes_per_chunk": pre["detail"]["expert_bytes_per_step"],
+            "unique_experts": pre["detail"]["unique_experts_per_step"],
+            "big_buckets_mfma_frac_spec": bb.get("mfma_frac"), "big_buckets": bb or None,
+            "workload": pre["config"]["workload"],
+        }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_pair(dict(synth.workload(args.workload), name=args.workload))
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def measured_read_ceiling(torch, moe, n_bytes: int, reps: int = 8) -> dict:
+    """The streaming-read reference for n_bytes: one launch reading that many
+    bytes from cold HBM (512 MiB read before each), best over workgroup counts."""
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    n = (int(n_bytes) + 15) // 16 * 16
+    buf = torch.ones(n, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    flush_sink = torch.empty((), dtype=torch.int32, device=dev)
+    best = None
+    for wgs in (256, 512, 1024, 2048):
+        pairs = []
+        for _ in range(reps):
+            flush_sink.copy_(flush.max())
+            torch.cuda._sleep(int(100e-6 * 2.4e9))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            moe.moe_probe_read(buf, sink, workgroups=wgs)
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = _median_us(pairs[2:])
+        if best is None or us < best[0]:
+            best = (us, wgs)
+    del buf
+    return {"bytes": n, "us": best[0], "GBps": n / (best[0] * 1e-6) / 1e9, "workgroups": best[1],
+            "note": "moe_probe_read: one launch streaming the same byte count from cold HBM (512 MiB read first)"}
+
+
+def layer_bench(args, torch, moe, synth, name, steps, warmup, no_flush, big=True, warm=False):
+    wl = dict(synth.workload(name), name=name)
     E, k, d, f, T = wl["E"], wl["k"], wl["d"], wl["f"], wl["T"]
     qt = moe.MOE_Q8_0 if wl["qtype"] == synth.Q8_0 else moe.MOE_Q4_0
     dev = torch.device("cuda", 0)
@@ -675,18 +744,18 @@ def main() -> int:
     shared = torch.from_numpy(moe.moe_pack_expert(
         ctx.cfg, synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True))).to(dev)
     t_gen = time.perf_counter() - t_gen
-    wr = torch.from_numpy(synth.router_weights(wl["seed"], E, d)).to(dev) if args.workload == "decode" else None
+    wr = torch.from_numpy(synth.router_weights(wl["seed"], E, d)).to(dev) if name == "decode" else None
     prec = moe.MOE_PREC_BF16 if wl["prec"] == "bf16" else moe.MOE_PREC_F32
 
-    n_steps = args.warmup + args.steps
+    n_steps = warmup + steps
     x_all = torch.stack([
         torch.from_numpy(synth.activations(wl["seed"], T, d, "bf16", s).view(np.int16)).view(torch.bfloat16)
         for s in range(n_steps)]).to(dev)  # [steps, T, d]
     lg_all = None
-    if args.workload == "mtp":
+    if name == "mtp":
         lg_all = torch.stack([torch.from_numpy(synth.mtp_logits(wl["seed"], s, T, E, k, wl["p_shared_route"]))
                               for s in range(n_steps)]).to(dev)
-    elif args.workload == "prefill":
+    elif name == "prefill":
         lg_all = torch.stack([torch.from_numpy(synth.zipf_gumbel_logits(wl["seed"] + s, T, E, wl["zipf_s"]))
                               for s in range(n_steps)]).to(dev)
     ids = torch.empty(T, k, dtype=torch.int32, device=dev)
@@ -719,8 +788,9 @@ def main() -> int:
 
     misses = 0
 
-    def prepare(s):
-        """Untimed: learn step s's experts, stage misses, flush caches, then spin."""
+    def prepare(s, cold=True):
+        """Untimed: learn step s's experts, stage misses, flush caches (unless
+        cold is False or the run is warm), then spin."""
         nonlocal misses
         route_plan(s)
         n, experts, _, _ = plan.host()
@@ -730,7 +800,7 @@ def main() -> int:
                 moe.moe_slot_fill(ctx, 0, int(e), int(sl), pack[int(e)], stream=side)
                 misses += 1
         side.synchronize()
-        if not args.no_flush:
+        if cold and not no_flush:
             flush_sink.copy_(flush.max())
         # keep the GPU busy while the host enqueues the timed kernels, so the
         # timed region measures GPU work, not Python launch latency
@@ -745,7 +815,7 @@ def main() -> int:
     n_unique = []
     torch.cuda.synchronize()
     for s in range(n_steps):
-        if s == args.warmup:
+        if s == warmup:
             torch.cuda.synchronize()
             wall_t0 = time.perf_counter()
         n = prepare(s)
@@ -760,10 +830,10 @@ def main() -> int:
     # Pass 2: the same steps as separate calls (route + union, then FFN).
     # Pass 3: the FFN launch alone between the events (route and union before
     # them, untimed).
-    n_ffn = min(args.steps, 100)
+    n_ffn = min(steps, 100)
     ev_sep, ev_ffn = new_events(n_ffn), new_events(n_ffn)
     for i in range(n_ffn):
-        s = args.warmup + i
+        s = warmup + i
         prepare(s)
         e1, e2 = ev_sep[i]
         e1.record(stream)
@@ -778,45 +848,69 @@ def main() -> int:
         moe.moe_expert_ffn(ctx, 0, x_all[s], plan, w, y, shared_payload=shared, prec=prec)
         e2.record(stream)
         moe.moe_slot_release(ctx, 0)
+    # Pass 4 (decode only, labelled warm): the whole step again on the first
+    # n_ffn steps with no cache flush before it, each step run twice in a row
+    # so the second finds its weights in the Infinity Cache and L2.
+    ev_warm = new_events(n_ffn) if warm else []
+    for i in range(len(ev_warm)):
+        s = warmup + i
+        prepare(s, cold=False)
+        whole_step(s)
+        torch.cuda._sleep(spin_cycles)
+        e1, e2 = ev_warm[i]
+        e1.record(stream)
+        whole_step(s)
+        e2.record(stream)
+        moe.moe_slot_release(ctx, 0)
     torch.cuda.synchronize()
     st = moe.moe_check(ctx)
     if st != moe.MOE_OK:
         print(f"device error word set: status {st}", file=sys.stderr)
-        return 1
-    big = None
-    if args.workload == "prefill":
-        route_plan(args.warmup)
+        return None
+    big_res = None
+    if name == "prefill":
+        route_plan(warmup)
         n, experts, offsets, _ = plan.host()
         sizes = np.diff(offsets)
         sel = [i for i in range(n) if sizes[i] >= BIG_BUCKET]
-        if sel and not args.no_big_buckets:
-            big = big_buckets_mfma([int(experts[i]) for i in sel], [int(sizes[i]) for i in sel], pack, wl,
-                                   flush, flush_sink, spin_cycles, args.no_flush)
+        if sel and big:
+            big_res = big_buckets_mfma([int(experts[i]) for i in sel], [int(sizes[i]) for i in sel], pack, wl,
+                                   flush, flush_sink, spin_cycles, no_flush)
             if args.big_gemm_min:
-                big["alt"] = big_buckets_mfma([int(experts[i]) for i in sel], [int(sizes[i]) for i in sel], pack, wl,
-                                              flush, flush_sink, spin_cycles, args.no_flush,
+                big_res["alt"] = big_buckets_mfma([int(experts[i]) for i in sel], [int(sizes[i]) for i in sel], pack, wl,
+                                              flush, flush_sink, spin_cycles, no_flush,
                                               gemm_min=args.big_gemm_min)
 
-    span = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(args.warmup, n_steps)]) * 1e3  # us
+    span = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(warmup, n_steps)]) * 1e3  # us
     sep = np.array([a.elapsed_time(b) for a, b in ev_sep]) * 1e3
     ffn = np.array([a.elapsed_time(b) for a, b in ev_ffn]) * 1e3
-    uniq = np.array(n_unique[args.warmup:])
+    uniq = np.array(n_unique[warmup:])
     uniq_ffn = uniq[:n_ffn]
     algo_bytes = (uniq + 1) * pb  # unique routed experts + the shared expert, per step
     ffn_gbs = ((uniq_ffn + 1) * pb).mean() / (ffn.mean() * 1e-6) / 1e9
     span_gbs = algo_bytes.mean() / (span.mean() * 1e-6) / 1e9
     # roofline kernel: the one launch of the whole step (T <= 4), else the FFN launch
     roof_gbs = span_gbs if one_launch else ffn_gbs
-    traffic = _traffic(args.workload)
+    traffic = _traffic(name)
+    # the achievable streaming rate for the same byte count, measured now
+    ceil = measured_read_ceiling(torch, moe, algo_bytes.mean()) if not no_flush else None
+    warm_res = None
+    if ev_warm:
+        wspan = np.array([a.elapsed_time(b) for a, b in ev_warm]) * 1e3
+        warm_res = {"label": "WARM: no cache flush; the same step run just before, so its weights sit in the "
+                             "Infinity Cache / L2 (not the headline)",
+                    "steps": len(ev_warm), "span_us_mean": float(wspan.mean()),
+                    "span_us_p50": float(np.percentile(wspan, 50)), "tokens_per_s": T / (wspan.mean() * 1e-6),
+                    "expert_GBps": float(((uniq[:len(ev_warm)] + 1) * pb).mean() / (wspan.mean() * 1e-6) / 1e9)}
 
     line = {
         "metric": "routed MoE-layer tokens/s (batch %d %s step: route + union + expert FFN)"
-                  % (T, "prefill" if args.workload == "prefill" else "decode"),
+                  % (T, "prefill" if name == "prefill" else "decode"),
         "value": T / (span.mean() * 1e-6),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": span.mean() * 1e-3,
         "higher_is_better": True,
         "scaling": "weak",
@@ -825,10 +919,10 @@ def main() -> int:
                   else "f32 (%s weights dequantised in registers)") % ("q8_0" if qt == moe.MOE_Q8_0 else "q4_0"),
         "data": "synthetic (seeded; no checkpoint)",
         "config": {
-            "workload": (f"{args.workload}: 1 MoE layer, {E} experts, top-{k} + 1 shared expert, d_model {d}, "
+            "workload": (f"{name}: 1 MoE layer, {E} experts, top-{k} + 1 shared expert, d_model {d}, "
                          f"d_ff {f}, {'Q8_0' if qt == moe.MOE_Q8_0 else 'Q4_0'}, {T} token(s)/step, "
                          f"{wl['n_slots']}-slot LRU cache, "
-                         + ("512 MiB read before every step (weights cold in L2 and Infinity Cache)" if not args.no_flush
+                         + ("512 MiB read before every step (weights cold in L2 and Infinity Cache)" if not no_flush
                             else "caches warm")),
             "global_batch": T,
             "parallelism": "single GPU",
@@ -843,6 +937,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": roof_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
+            "measured_peak": ceil["GBps"] if ceil else None,
+            "frac_of_measured": roof_gbs / ceil["GBps"] if ceil else None,
         },
         "detail": {
             "layer_span_us_p50": float(np.percentile(span, 50)),
@@ -862,16 +958,15 @@ def main() -> int:
             "assignments_per_step": T * k,
             "dedupe_fraction": float(1.0 - uniq.mean() / (T * k)),
             "slot_misses_staged": misses,
-            "big_buckets": big,
+            "big_buckets": big_res,
+            "measured_read_ceiling": ceil,
+            "warm_cache": warm_res,
             "wall_s_timed_loop_incl_staging_and_flush": wall,
             "setup_pack_s": t_gen,
         },
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl)
-    print(json.dumps(line), flush=True)
     ctx.close()
-    return 0
+    return line
 
 
 if __name__ == "__main__":

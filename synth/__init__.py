@@ -223,3 +223,11 @@ def markov_logits(seed: int, layer: int, n_tokens: int, E: int, k: int, p_repeat
     """[n_tokens, E] logits of one layer's Markov route chain."""
     g = rng(seed, _P_ROUTE, layer)
     return _realise(g, markov_route_sets(g, n_tokens, E, k, p_repeat), E)
+
+
+def markov_trace(seed: int, n_layers: int, n_tokens: int, n_experts: int, k: int, p_repeat: float) -> list:
+    """Replay trace: steps (layer, experts) for n_tokens tokens through n_layers
+    layers, token-major, each layer's route a Markov chain over tokens (the
+    stack workload's routes)."""
+    chains = [markov_route_sets(rng(seed, 55, l), n_tokens, n_experts, k, p_repeat) for l in range(n_layers)]
+    return [(l, sorted(int(e) for e in chains[l][t])) for t in range(n_tokens) for l in range(n_layers)]
