@@ -317,6 +317,31 @@ moe_status moe_expert_ffn(moe_ctx* ctx, int32_t layer, const void* x, int32_t x_
                           const moe_plan* plan, const float* topk_w, const void* shared_payload,
                           int32_t prec, float* y, moe_stream stream);
 
+/* Bytes of the device array behind moe_expert_ffn_static (one per GPU). */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_expert_ffn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, kernels and results bit for bit, but a call of more
+ * than 4 tokens keeps its scratch (hidden rows [T k + T, d_ff], partial rows
+ * [T k + T, d_model] fp32, the entry inverse and the tile records) in a
+ * fixed device array of MOE_STATIC_SCRATCH_BYTES per GPU that the library
+ * holds until the process ends, not in the context's workspace; so T is not
+ * limited by max_tokens but by that array: the call needs 256-byte-aligned
+ * sections of (T k + T) d_ff (2 bytes in MOE_PREC_BF16, 4 in MOE_PREC_F32)
+ * + (T k + T) d_model 4 + T k 4 + 16 bytes per tile record, and returns
+ * MOE_EINVAL (nothing enqueued) when that exceeds the array (at d_model
+ * 2048, d_ff 512, top-8 with a shared expert: T up to 808 in bf16 mode, 727
+ * in fp32 mode).
+ * Calls of up to 4 tokens run moe_expert_ffn itself (the decode kernel's
+ * workspace belongs to the context, created with it).  Nothing in the call
+ * allocates.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind: calls that overlap on one GPU (other contexts, other
+ * streams) race.  moe_hidden_rows does not show this call's hidden rows. */
+moe_status moe_expert_ffn_static(moe_ctx* ctx, int32_t layer, const void* x, int32_t x_dtype, int64_t T,
+                                 const moe_plan* plan, const float* topk_w, const void* shared_payload,
+                                 int32_t prec, float* y, moe_stream stream);
+
 /* The whole decode step of up to 4 tokens in ONE launch: moe_route_union and
  * then moe_expert_ffn, with the same results bit for bit ("Nanite for Experts",
  * §12, milestone 1: one expert-major operator for the step; §3.1: the router's

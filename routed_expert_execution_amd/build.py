@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["moe_host.cpp", "route.hip", "plan.hip", "dequant.hip", "ffn_decode.hip", "ffn_prefill.hip", "probe.hip", "slots.hip"]
+SOURCES = ["moe_host.cpp", "route.hip", "plan.hip", "dequant.hip", "ffn_decode.hip", "ffn_prefill.hip", "probe.hip", "slots.hip", "scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

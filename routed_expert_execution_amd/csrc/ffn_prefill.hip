@@ -789,6 +789,22 @@ void prefill_max_tiles(int64_t T, int k, int E, bool shared, int* big_tiles, int
     *small_tiles = (int)((rows + SMALL - 1) / SMALL + units);
 }
 
+PrefillLayout prefill_layout(int64_t T, int k, int E, int d, int f, bool bf16_hidden) {
+    PrefillLayout L{};
+    prefill_max_tiles(T, k, E, true, &L.cap_big, &L.cap_small);
+    auto up = [](size_t n) { return (n + 255) / 256 * 256; };
+    const size_t rows = (size_t)(T * k + T);
+    size_t o = 0;
+    L.h = o;           o += up(rows * (size_t)f * (bf16_hidden ? 2 : 4));
+    L.part = o;        o += up(rows * (size_t)d * 4);
+    L.inv = o;         o += up((size_t)T * k * 4);
+    L.sched_big = o;   o += up((size_t)L.cap_big * 16);
+    L.sched_small = o; o += up((size_t)L.cap_small * 16);
+    L.n_tiles = o;     o += 256;
+    L.total = o;
+    return L;
+}
+
 hipError_t launch_ffn_prefill(const PrefillArgs& a, int prec, const PrefillStreams& s) {
     if (a.d % COLS || a.f % 16) return hipErrorInvalidValue;
     int bt, st;

@@ -183,6 +183,20 @@ struct PrefillArgs {
 
 // Upper bounds on the tiles of each size a call of T tokens can need.
 void prefill_max_tiles(int64_t T, int k, int E, bool shared, int* big_tiles, int* small_tiles);
+
+// The chunk path's workspace carved out of one buffer (256-byte aligned
+// sections): hidden rows, partial rows, entry inverse, the two tile-record
+// arrays and the counts.  Returns the bytes needed for T tokens.
+struct PrefillLayout {
+    size_t h, part, inv, sched_big, sched_small, n_tiles, total;
+    int cap_big, cap_small;
+};
+PrefillLayout prefill_layout(int64_t T, int k, int E, int d, int f, bool bf16_hidden);
+
+// The fixed device array behind moe_expert_ffn_static, and its address on the
+// current device (taken once per device).
+constexpr size_t kStaticScratchBytes = MOE_STATIC_SCRATCH_BYTES;
+hipError_t static_scratch(void** out);
 // Streams of a prefill call: the caller's, and an auxiliary one (null: all on
 // s) on which the 64-token tile chain runs beside the 16-token one, forked
 // from and joined back into s with the two events.

@@ -872,26 +872,10 @@ static moe::FfnArgs ffn_args(moe_ctx* c, int32_t layer, const void* x, int32_t x
     return a;
 }
 
-moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dtype, int64_t T,
-                          const moe_plan* plan, const float* topk_w, const void* shared_payload,
-                          int32_t prec, float* y, moe_stream stream) {
-    if (moe_status st = need_device(c)) return st;
+// Arguments of the chunk path's kernels, workspace pointers aside.
+static moe::PrefillArgs prefill_args(moe_ctx* c, const moe::FfnArgs& a, int32_t layer, const void* x, int64_t T,
+                                     const float* topk_w, float* y) {
     const moe_config& cf = c->cfg;
-    if (layer < 0 || layer >= cf.n_layers) return fail(c, MOE_EINVAL, "moe_expert_ffn: bad layer");
-    if (T < 0 || T > cf.max_tokens) return fail(c, MOE_EINVAL, "moe_expert_ffn: T outside [0, max_tokens]");
-    if (prec != MOE_PREC_F32 && prec != MOE_PREC_BF16) return fail(c, MOE_EINVAL, "moe_expert_ffn: bad prec");
-    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(c, MOE_EINVAL, "moe_expert_ffn: bad x_dtype");
-    if (T > 0 && (!x || !plan || !plan->n_active || !plan->experts || !plan->offsets || !plan->entries || !topk_w || !y))
-        return fail(c, MOE_EINVAL, "moe_expert_ffn: null argument");
-    DeviceGuard dg(cf.device);
-    hipStream_t s = (hipStream_t)stream;
-    if (moe_status st = wait_pending_fills(c, s)) return st;
-    if (T == 0) return MOE_OK;
-    moe::FfnArgs a = ffn_args(c, layer, x, x_dtype, T, plan, topk_w, shared_payload, y);
-    if (T <= moe::kDecodeMaxT) {
-        HIP_TRY(c, moe::launch_ffn_decode(c->g, a, prec, s));
-        return MOE_OK;
-    }
     moe::PrefillArgs p{};
     p.g = c->g;
     p.pool = a.pool;
@@ -913,6 +897,41 @@ moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     p.d = cf.d_model;
     p.f = cf.d_ff;
     p.gemm_min = cf.gemm_min_tokens;
+    p.y = y;
+    p.err = c->err_word;
+    return p;
+}
+
+static moe_status ffn_check_args(moe_ctx* c, const char* fn, int32_t layer, const void* x, int32_t x_dtype,
+                                 int64_t T, int64_t T_max, const moe_plan* plan, const float* topk_w, int32_t prec,
+                                 float* y) {
+    const moe_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers) return fail(c, MOE_EINVAL, "%s: bad layer", fn);
+    if (T < 0 || T > T_max) return fail(c, MOE_EINVAL, "%s: T=%lld outside [0, %lld]", fn, (long long)T, (long long)T_max);
+    if (prec != MOE_PREC_F32 && prec != MOE_PREC_BF16) return fail(c, MOE_EINVAL, "%s: bad prec", fn);
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(c, MOE_EINVAL, "%s: bad x_dtype", fn);
+    if (T > 0 && (!x || !plan || !plan->n_active || !plan->experts || !plan->offsets || !plan->entries || !topk_w || !y))
+        return fail(c, MOE_EINVAL, "%s: null argument", fn);
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dtype, int64_t T,
+                          const moe_plan* plan, const float* topk_w, const void* shared_payload,
+                          int32_t prec, float* y, moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (moe_status st = ffn_check_args(c, "moe_expert_ffn", layer, x, x_dtype, T, cf.max_tokens, plan, topk_w, prec, y))
+        return st;
+    DeviceGuard dg(cf.device);
+    hipStream_t s = (hipStream_t)stream;
+    if (moe_status st = wait_pending_fills(c, s)) return st;
+    if (T == 0) return MOE_OK;
+    moe::FfnArgs a = ffn_args(c, layer, x, x_dtype, T, plan, topk_w, shared_payload, y);
+    if (T <= moe::kDecodeMaxT) {
+        HIP_TRY(c, moe::launch_ffn_decode(c->g, a, prec, s));
+        return MOE_OK;
+    }
+    moe::PrefillArgs p = prefill_args(c, a, layer, x, T, topk_w, y);
     p.h = c->ph;
     p.part = c->ppart;
     p.inv = c->pinv;
@@ -921,10 +940,42 @@ moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     p.n_tiles = p.sched_small + 4 * (size_t)c->p_small;
     p.cap_big = c->p_big;
     p.cap_small = c->p_small;
-    p.y = y;
-    p.err = c->err_word;
     HIP_TRY(c, moe::launch_ffn_prefill(p, prec, moe::PrefillStreams{s, c->aux, c->fork_ev, c->join_ev}));
     c->last_prefill_prec = prec;
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn_static(moe_ctx* c, int32_t layer, const void* x, int32_t x_dtype, int64_t T,
+                                 const moe_plan* plan, const float* topk_w, const void* shared_payload,
+                                 int32_t prec, float* y, moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (T >= 0 && T <= moe::kDecodeMaxT)  // the decode kernel, on the context's own workspace
+        return moe_expert_ffn(c, layer, x, x_dtype, T, plan, topk_w, shared_payload, prec, y, stream);
+    if (moe_status st = ffn_check_args(c, "moe_expert_ffn_static", layer, x, x_dtype, T, 65536, plan, topk_w, prec, y))
+        return st;
+    const moe::PrefillLayout L = moe::prefill_layout(T, cf.top_k, cf.n_experts, cf.d_model, cf.d_ff,
+                                                     prec == MOE_PREC_BF16);
+    if (L.total > moe::kStaticScratchBytes)
+        return fail(c, MOE_EINVAL, "moe_expert_ffn_static: T=%lld needs %zu bytes of scratch; the static array holds %zu",
+                    (long long)T, L.total, moe::kStaticScratchBytes);
+    DeviceGuard dg(cf.device);
+    void* base = nullptr;
+    HIP_TRY(c, moe::static_scratch(&base));
+    hipStream_t s = (hipStream_t)stream;
+    if (moe_status st = wait_pending_fills(c, s)) return st;
+    moe::FfnArgs a = ffn_args(c, layer, x, x_dtype, T, plan, topk_w, shared_payload, y);
+    moe::PrefillArgs p = prefill_args(c, a, layer, x, T, topk_w, y);
+    uint8_t* b = (uint8_t*)base;
+    p.h = b + L.h;
+    p.part = (float*)(b + L.part);
+    p.inv = (int32_t*)(b + L.inv);
+    p.sched_big = (int32_t*)(b + L.sched_big);
+    p.sched_small = (int32_t*)(b + L.sched_small);
+    p.n_tiles = (int32_t*)(b + L.n_tiles);
+    p.cap_big = L.cap_big;
+    p.cap_small = L.cap_small;
+    HIP_TRY(c, moe::launch_ffn_prefill(p, prec, moe::PrefillStreams{s, c->aux, c->fork_ev, c->join_ev}));
     return MOE_OK;
 }
 

@@ -76,6 +76,7 @@ def _load() -> C.CDLL:
         "moe_slot_release": (C.c_int, [P, I32, P]),
         "moe_slot_bind": (C.c_int, [P, I32, I32, I32, P]),
         "moe_expert_ffn": (C.c_int, [P, I32, P, I32, I64, planp, P, P, I32, P, P]),
+        "moe_expert_ffn_static": (C.c_int, [P, I32, P, I32, I64, planp, P, P, I32, P, P]),
         "moe_route_ffn": (C.c_int, [P, I32, P, I32, P, P, I64, P, P, planp, P, I32, P, P]),
         "moe_dequant": (C.c_int, [P, P, I32, P, P]),
         "moe_stats": (C.c_int, [P, C.POINTER(C.c_uint64)]),
@@ -96,7 +97,7 @@ _lib = _load()
 EXPORTS = ("moe_payload_bytes", "moe_plan_bytes", "moe_pack_expert", "moe_unpack_expert", "moe_create",
            "moe_destroy", "moe_last_error", "moe_status_string", "moe_route", "moe_plan_union", "moe_route_union",
            "moe_slot_map", "moe_slot_prefetch", "moe_prefetch_stats", "moe_slot_fill", "moe_slot_stage", "moe_slot_pull", "moe_route_pull", "moe_slot_release",
-           "moe_slot_bind", "moe_expert_ffn",
+           "moe_slot_bind", "moe_expert_ffn", "moe_expert_ffn_static",
            "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table", "moe_hidden_rows", "moe_probe_read",
            "moe_probe_mfma")
 
@@ -431,7 +432,9 @@ def moe_slot_bind(ctx: Context, layer: int, expert: int, slot: int, stream=None)
 
 
 def moe_expert_ffn(ctx: Context, layer: int, x, plan: Plan, topk_w, y, shared_payload=None,
-                   prec: int = MOE_PREC_F32, stream=None) -> None:
+                   prec: int = MOE_PREC_F32, stream=None, static: bool = False) -> None:
+    """static: call moe_expert_ffn_static (the chunk path's scratch in the
+    library's fixed device array instead of the context's workspace)."""
     import torch
     T = x.shape[0]
     if tuple(x.shape) != (T, ctx.d_model) or tuple(y.shape) != (T, ctx.d_model) or y.dtype != torch.float32:
@@ -443,8 +446,9 @@ def moe_expert_ffn(ctx: Context, layer: int, x, plan: Plan, topk_w, y, shared_pa
     if shared_payload is not None and shared_payload.numel() * shared_payload.element_size() < ctx.payload_bytes:
         raise ValueError("shared payload too small")
     _check_dev(ctx, x, topk_w, y, shared_payload)
-    _call(ctx, _lib.moe_expert_ffn(ctx.handle, layer, _ptr(x), _x_dtype(x), T, C.byref(plan.c), _ptr(topk_w),
-                                   _ptr(shared_payload), prec, _ptr(y), _stream(stream)))
+    fn = _lib.moe_expert_ffn_static if static else _lib.moe_expert_ffn
+    _call(ctx, fn(ctx.handle, layer, _ptr(x), _x_dtype(x), T, C.byref(plan.c), _ptr(topk_w),
+                  _ptr(shared_payload), prec, _ptr(y), _stream(stream)))
 
 
 def moe_route_ffn(ctx: Context, layer: int, x, topk_ids, topk_w, plan: Plan, y, w_router=None, logits_in=None,
