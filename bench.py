@@ -293,7 +293,8 @@ def ceilings(torch, moe) -> int:
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     fsink = torch.zeros(1, dtype=torch.float32, device=dev)
     mfma = {}
-    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+    for shape, name in ((0, "16x16x32 x4 chains"), (1, "32x32x16 x4 chains"), (2, "16x16x32 x8 chains"),
+                        (3, "32x32x16 x8 chains"), (4, "16x16x32 x16 chains"), (5, "32x32x16 x16 chains")):
         best = None
         for per_cu in (2, 4, 8):
             grid, iters = cus * per_cu, 20000 // per_cu
@@ -312,7 +313,25 @@ def ceilings(torch, moe) -> int:
                 best = {"TFLOPs": round(tf, 1), "frac": round(tf / 2500.0, 3), "workgroups": grid,
                         "waves_per_cu": 4 * per_cu, "kernel_us": round(us, 1)}
         mfma[name] = best
-    print(json.dumps({"metric": "peak references", "n_gpus": 1, "data": "synthetic",
+    lds = None
+    isink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for per_cu in (1, 2, 4):
+        grid = cus * per_cu
+        moe.moe_probe_lds(100, grid, isink)
+        pairs = []
+        for _ in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            nb = moe.moe_probe_lds(20000 // per_cu, grid, isink)
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = _median_us(pairs[1:])
+        bpc = nb / (us * 1e-6) / cus / 2.4e9
+        if lds is None or bpc > lds["bytes_per_clk_per_cu_at_2.4GHz"]:
+            lds = {"TBps": round(nb / (us * 1e-6) / 1e12, 1), "bytes_per_clk_per_cu_at_2.4GHz": round(bpc, 1),
+                   "waves_per_cu": 4 * per_cu}
+    print(json.dumps({"metric": "peak references", "n_gpus": 1, "data": "synthetic", "lds_read_b128": lds,
                       "hbm_streaming_read_cold": reads, "hbm_peak_spec_GBps": HBM_PEAK_GBS,
                       "pinned_h2d_hipMemcpyAsync": h2d,
                       "mfma_bf16_dense": dict(mfma, peak_spec_TFLOPs=2500.0)}), flush=True)

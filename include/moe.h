@@ -389,14 +389,20 @@ moe_status moe_check(moe_ctx* ctx, moe_stream stream);
  * device [1] uint32, written only on a value the caller cannot expect.  The
  * achievable streaming-read rate, to compare the expert kernels' bytes per
  * second with.
- * moe_probe_mfma: grid workgroups of 4 waves, each running iters rounds of 4
- * independent bf16 matrix-core products (shape 0: 16x16x32, 1: 32x32x16);
+ * moe_probe_mfma: grid workgroups of 4 waves, each running iters rounds of
+ * independent bf16 matrix-core products: shape % 2 selects the instruction
+ * (0: 16x16x32, 1: 32x32x16), shape / 2 the accumulators per wave (0: 4,
+ * 1: 8, 2: 16), shape 0..5;
  * *flops (host) receives the floating-point operations performed; sink:
  * device [1] fp32.  Both enqueue on `stream` and return MOE_EINVAL (nothing
  * enqueued) for bad arguments. */
 moe_status moe_probe_read(const void* src, int64_t bytes, int32_t workgroups, uint32_t* sink, moe_stream stream);
 moe_status moe_probe_mfma(int32_t iters, int32_t grid, int32_t shape, float* sink, int64_t* flops,
                           moe_stream stream);
+/* moe_probe_lds: grid workgroups of 4 waves, each lane reading 16 bytes per
+ * instruction from local data share memory (no bank conflicts), iters rounds
+ * of 8 reads; *bytes (host) receives the bytes read; sink: device [1] uint32. */
+moe_status moe_probe_lds(int32_t iters, int32_t grid, uint32_t* sink, int64_t* bytes, moe_stream stream);
 
 /* Device address of the page table ([n_layers x n_experts] int32), for tests. */
 moe_status moe_page_table(const moe_ctx* ctx, int32_t** out);

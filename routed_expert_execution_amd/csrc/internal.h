@@ -235,6 +235,7 @@ hipError_t launch_pull(const PullArgs& a, int32_t* pt, const PtWrites& w, hipStr
 
 hipError_t launch_probe_read(const void* src, int64_t bytes, int wgs, uint32_t* sink, hipStream_t s);
 hipError_t launch_probe_mfma(int iters, int grid, int shape, float* sink, hipStream_t s);
+hipError_t launch_probe_lds(int iters, int grid, uint32_t* sink, hipStream_t s);
 int64_t probe_mfma_flops(int iters, int grid, int shape);
 
 }  // namespace moe

@@ -1055,9 +1055,15 @@ moe_status moe_probe_read(const void* src, int64_t bytes, int32_t workgroups, ui
 }
 
 moe_status moe_probe_mfma(int32_t iters, int32_t grid, int32_t shape, float* sink, int64_t* flops, moe_stream stream) {
-    if (iters < 1 || grid < 1 || (shape != 0 && shape != 1) || !sink || !flops) return MOE_EINVAL;
+    if (iters < 1 || grid < 1 || shape < 0 || shape > 5 || !sink || !flops) return MOE_EINVAL;
     *flops = moe::probe_mfma_flops(iters, grid, shape);
     return moe::launch_probe_mfma(iters, grid, shape, sink, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+moe_status moe_probe_lds(int32_t iters, int32_t grid, uint32_t* sink, int64_t* bytes, moe_stream stream) {
+    if (iters < 1 || grid < 1 || !sink || !bytes) return MOE_EINVAL;
+    *bytes = (int64_t)grid * 256 * 8 * 16 * iters;
+    return moe::launch_probe_lds(iters, grid, sink, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 moe_status moe_page_table(const moe_ctx* c, int32_t** out) {

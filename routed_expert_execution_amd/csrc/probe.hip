@@ -37,11 +37,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Each wave runs `iters` rounds of kChains independent bf16 matrix-core
-// products, 16x16x32 (16,384 flops each) or 32x32x16 (32,768 flops); the sums
-// are stored only under a condition no finite input meets.
-constexpr int kChains = 4;
-template <int SHAPE>
+// Each wave runs `iters` rounds of CH independent bf16 matrix-core products,
+// 16x16x32 (16,384 flops each) or 32x32x16 (32,768 flops); the sums are
+// stored only under a condition no finite input meets.
+template <int SHAPE, int CH>
 __global__ __launch_bounds__(256) void mfma_kernel(int iters, float* __restrict__ sink) {
     bf16x8 a, b;
 #pragma unroll
@@ -51,30 +50,53 @@ __global__ __launch_bounds__(256) void mfma_kernel(int iters, float* __restrict_
     }
     float s = 0.f;
     if constexpr (SHAPE == 0) {
-        f32x4 acc[kChains];
+        f32x4 acc[CH];
 #pragma unroll
-        for (int c = 0; c < kChains; c++) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < CH; c++) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int it = 0; it < iters; it++) {
 #pragma unroll
-            for (int c = 0; c < kChains; c++) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+            for (int c = 0; c < CH; c++) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
         }
 #pragma unroll
-        for (int c = 0; c < kChains; c++) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+        for (int c = 0; c < CH; c++) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
     } else {
-        f32x16 acc[kChains];
+        f32x16 acc[CH];
 #pragma unroll
-        for (int c = 0; c < kChains; c++)
+        for (int c = 0; c < CH; c++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[c][r] = 0.f;
         for (int it = 0; it < iters; it++) {
 #pragma unroll
-            for (int c = 0; c < kChains; c++) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+            for (int c = 0; c < CH; c++) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
         }
 #pragma unroll
-        for (int c = 0; c < kChains; c++) s += acc[c][0] + acc[c][5] + acc[c][10] + acc[c][15];
+        for (int c = 0; c < CH; c++) s += acc[c][0] + acc[c][5] + acc[c][10] + acc[c][15];
     }
     if (s == -1.0f) sink[0] = s;
 }
+
+// LDS read rate: each of 4 waves reads 16 bytes per lane per instruction
+// (consecutive lanes, consecutive 16-byte words: no bank conflicts) from a
+// 32 KiB buffer, `iters` rounds of 8 reads, folded with xor.
+__global__ __launch_bounds__(256) void lds_kernel(int iters, uint32_t* __restrict__ sink) {
+    __shared__ uint4 buf[2048];
+    for (int i = threadIdx.x; i < 2048; i += 256) buf[i] = make_uint4(i, i * 3, i * 5, i * 7);
+    __syncthreads();
+    uint32_t acc = 0;
+    const int base = (threadIdx.x & 63) + (threadIdx.x >> 6) * 512;
+    for (int it = 0; it < iters; it++) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) v[u] = buf[(base + 64 * u + it) & 2047];
+#pragma unroll
+        for (int u = 0; u < 8; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+// variant v: instruction v % 2 (0: 16x16x32, 1: 32x32x16), independent
+// accumulators per wave 4 << (v / 2) (4, 8 or 16)
+int probe_chains(int v) { return 4 << (v / 2); }
 
 }  // namespace
 
@@ -87,13 +109,24 @@ hipError_t launch_probe_read(const void* src, int64_t bytes, int wgs, uint32_t* 
 }
 
 hipError_t launch_probe_mfma(int iters, int grid, int shape, float* sink, hipStream_t s) {
-    if (shape == 0) hipLaunchKernelGGL(mfma_kernel<0>, dim3(grid), dim3(256), 0, s, iters, sink);
-    else hipLaunchKernelGGL(mfma_kernel<1>, dim3(grid), dim3(256), 0, s, iters, sink);
+    switch (shape) {
+        case 0: hipLaunchKernelGGL((mfma_kernel<0, 4>), dim3(grid), dim3(256), 0, s, iters, sink); break;
+        case 1: hipLaunchKernelGGL((mfma_kernel<1, 4>), dim3(grid), dim3(256), 0, s, iters, sink); break;
+        case 2: hipLaunchKernelGGL((mfma_kernel<0, 8>), dim3(grid), dim3(256), 0, s, iters, sink); break;
+        case 3: hipLaunchKernelGGL((mfma_kernel<1, 8>), dim3(grid), dim3(256), 0, s, iters, sink); break;
+        case 4: hipLaunchKernelGGL((mfma_kernel<0, 16>), dim3(grid), dim3(256), 0, s, iters, sink); break;
+        default: hipLaunchKernelGGL((mfma_kernel<1, 16>), dim3(grid), dim3(256), 0, s, iters, sink); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_lds(int iters, int grid, uint32_t* sink, hipStream_t s) {
+    hipLaunchKernelGGL(lds_kernel, dim3(grid), dim3(256), 0, s, iters, sink);
     return hipGetLastError();
 }
 
 int64_t probe_mfma_flops(int iters, int grid, int shape) {
-    return (int64_t)grid * 4 * kChains * (shape == 0 ? 16384LL : 32768LL) * iters;
+    return (int64_t)grid * 4 * probe_chains(shape) * (shape % 2 == 0 ? 16384LL : 32768LL) * iters;
 }
 
 }  // namespace moe

@@ -85,6 +85,7 @@ def _load() -> C.CDLL:
         "moe_hidden_rows": (C.c_int, [P, C.POINTER(P), C.POINTER(I32)]),
         "moe_probe_read": (C.c_int, [P, I64, I32, P, P]),
         "moe_probe_mfma": (C.c_int, [I32, I32, I32, P, C.POINTER(I64), P]),
+        "moe_probe_lds": (C.c_int, [I32, I32, P, C.POINTER(I64), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -99,7 +100,7 @@ EXPORTS = ("moe_payload_bytes", "moe_plan_bytes", "moe_pack_expert", "moe_unpack
            "moe_slot_map", "moe_slot_prefetch", "moe_prefetch_stats", "moe_slot_fill", "moe_slot_stage", "moe_slot_pull", "moe_route_pull", "moe_slot_release",
            "moe_slot_bind", "moe_expert_ffn", "moe_expert_ffn_static",
            "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table", "moe_hidden_rows", "moe_probe_read",
-           "moe_probe_mfma")
+           "moe_probe_mfma", "moe_probe_lds")
 
 
 def library() -> C.CDLL:
@@ -532,6 +533,14 @@ def moe_probe_read(src, sink, workgroups: int = 0, stream=None) -> None:
     n = src.numel() * src.element_size()
     if _lib.moe_probe_read(_ptr(src), n, workgroups, _ptr(sink), _stream(stream)) != MOE_OK:
         raise ValueError("moe_probe_read: bad arguments (bytes must be a positive multiple of 16)")
+
+
+def moe_probe_lds(iters: int, grid: int, sink, stream=None) -> int:
+    """LDS read loop; returns the bytes it reads."""
+    b = C.c_int64()
+    if _lib.moe_probe_lds(iters, grid, _ptr(sink), C.byref(b), _stream(stream)) != MOE_OK:
+        raise ValueError("moe_probe_lds: bad arguments")
+    return int(b.value)
 
 
 def moe_probe_mfma(iters: int, grid: int, sink, shape: int = 0, stream=None) -> int:
