@@ -37,6 +37,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BIG = kPrefillBM;  // tokens per large tile (4 row groups of 16)
+constexpr int WIDE = kPrefillWide;  // tokens per wide tile
 constexpr int SMALL = 16;        // tokens per small tile
 constexpr int WAVES = 4;         // waves per workgroup, 16 features / rows each
 constexpr int COLS = WAVES * 16; // features / output rows per workgroup item
@@ -112,7 +113,7 @@ constexpr int kSchedInvAhead = 4;
 
 __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec) {
     __shared__ int wave_tot[16];
-    __shared__ int tot_b, tot_s;
+    __shared__ int tot_b, tot_s, tot_w;
     __shared__ int s_bad, s_nvalid;
     const int n_ent = a.T * a.k;
     int ent_ahead[kSchedInvAhead];
@@ -142,10 +143,10 @@ __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec)
     }
     __syncthreads();
     const int n_units = na + (a.shared ? 1 : 0);
-    int base_b = 0, base_s = 0;
+    int base_b = 0, base_s = 0, base_w = 0;
     for (int u0 = 0; u0 < n_units; u0 += 1024) {
         const int u = u0 + threadIdx.x;
-        int tb = 0, ts = 0, slot = kShared, p0 = 0, M = 0;
+        int tb = 0, ts = 0, tw = 0, slot = kShared, p0 = 0, M = 0;
         if (u < n_units) {
             if (u == na) {
                 M = a.T;
@@ -160,11 +161,17 @@ __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec)
                 if (in.e >= 0 && in.e < a.E && in.sl >= 0 && in.sl < a.n_slots) slot = in.sl;
                 if (slot == kUnmapped) atomicOr(a.err, kErrMiss);
             }
-            if (prec == MOE_PREC_BF16 && M >= a.gemm_min) tb = (M + BIG - 1) / BIG;
+            if (prec == MOE_PREC_BF16 && M >= a.wide_min) tw = (M + WIDE - 1) / WIDE;
+            else if (prec == MOE_PREC_BF16 && M >= a.gemm_min) tb = (M + BIG - 1) / BIG;
             else ts = (M + SMALL - 1) / SMALL;
         }
         const int fb = base_b + block_prefix(tb, wave_tot, &tot_b);
         const int fs = base_s + block_prefix(ts, wave_tot, &tot_s);
+        const int fw = base_w + block_prefix(tw, wave_tot, &tot_w);
+        for (int i = 0; i < tw; i++) {
+            if (fw + i >= a.cap_wide) { s_bad = 1; break; }
+            ((int4*)a.sched_wide)[fw + i] = make_int4(slot, p0 + i * WIDE, min(WIDE, M - i * WIDE), 0);
+        }
         for (int i = 0; i < tb; i++) {
             if (fb + i >= a.cap_big) { s_bad = 1; break; }
             ((int4*)a.sched_big)[fb + i] = make_int4(slot, p0 + i * BIG, min(BIG, M - i * BIG), 0);
@@ -175,6 +182,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec)
         }
         base_b += tot_b;
         base_s += tot_s;
+        base_w += tot_w;
         __syncthreads();
     }
     const int n_valid = s_nvalid;
@@ -182,6 +190,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec)
         a.n_tiles[0] = min(base_b, a.cap_big);
         a.n_tiles[1] = min(base_s, a.cap_small);
         a.n_tiles[2] = n_valid;
+        a.n_tiles[3] = min(base_w, a.cap_wide);
         if (s_bad) atomicOr(a.err, kErrBadId);
     }
 #pragma unroll
@@ -707,6 +716,221 @@ __global__ __launch_bounds__(256, BIGT ? 2 : (PREC == MOE_PREC_BF16 ? 4 : 3)) vo
     }
 }
 
+// ---- wide tiles: buckets of at least wide_min tokens (bf16 mode) -----------------
+//
+// A workgroup of 4 waves owns 128 token rows of one bucket and, per item, 64
+// hidden units of gate and up (gate/up) or 128 output rows (down).  Each K step
+// of 64 columns (two quant blocks per row) every thread dequantises one weight
+// block into bf16 in LDS, so a weight is dequantised once per 128 tokens
+// instead of once per 16 or 64; the token rows are staged in LDS beside it.
+// Wave w computes rows 64 (w % 2) .. + 64 against 32 hidden units of both
+// matrices (gate/up) or 64 output rows (down) with v_mfma_f32_32x32x16_bf16:
+// four 32 x 32 products per 16 columns, from two A and two B fragments.
+// The raw loads of a step (the thread's four 16-byte pieces of token rows and
+// its weight block) are issued WST steps ahead into registers; LDS holds two
+// steps (the one being multiplied and the next, written before the product).
+
+constexpr int WFEAT = 64;             // hidden units per wide gate/up item (both matrices: 128 LDS rows)
+constexpr int WROWS = 128;            // output rows per wide down item
+constexpr int WBK = 64;               // K columns per step: two blocks per row
+constexpr int WST = 3;                // steps of raw loads in registers
+constexpr int WPITCH = WBK + 8;       // bf16 per LDS row: 144 bytes, conflict-free 16-byte reads
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct WideLds {
+    __bf16 a[2][WIDE][WPITCH];
+    __bf16 b[2][128][WPITCH];
+};
+
+// One thread's raw loads for one step: four 8-element pieces of token rows
+// (rows (tid >> 3) + 32 i, columns 8 (tid & 7) of the step) and one weight block.
+template <int QT, bool XB> struct WideRaw;
+template <int QT> struct WideRaw<QT, true> {
+    uint4 x[4];
+    Raw<QT> w;
+};
+template <int QT> struct WideRaw<QT, false> {
+    float4 x[8];
+    Raw<QT> w;
+};
+
+// GATEUP: A = activation rows of the tile's tokens (x, bf16 or fp32 rounded to
+// bf16), B = gate rows (LDS rows 0..63) and up rows (64..127) of hidden units
+// c0 .. c0 + 63.  Otherwise (down): A = the tile's hidden rows (bf16), B = the
+// down rows r0 .. r0 + 127.
+template <int QT, bool XB, bool GATEUP>
+__device__ void wide_item(const PrefillArgs& a, const TileRec& t, const uint8_t* base, int c0, WideLds& L) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const Geom& G = a.g;
+    const int nk = (GATEUP ? G.nb_d : G.nb_f) / 2;  // steps
+    constexpr bool AXB = GATEUP ? XB : true;         // the hidden rows are bf16
+    // this thread's A rows (valid rows; padding rows staged as zeros)
+    int64_t arow[4];
+    bool akeep[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int m = (tid >> 3) + 32 * i;
+        akeep[i] = m < t.M;
+        const int mm = akeep[i] ? m : 0;
+        arow[i] = GATEUP ? (int64_t)row_token(a, t, mm) * a.d : (int64_t)row_slot(a, t, mm) * a.f;
+    }
+    const int ach = (tid & 7) * 8;  // column of the thread's pieces within a step
+    // this thread's weight block: LDS row brow, block kbit of each step
+    const int kbit = (tid >> 4) & 1;
+    int brow;
+    if constexpr (GATEUP) brow = (tid >> 7) * 64 + 16 * ((tid >> 5) & 3) + (tid & 15);
+    else brow = 16 * (tid >> 5) + (tid & 15);
+    auto blk_ptr = [&](int step, int* i) -> const uint8_t* {
+        int64_t tile;
+        if constexpr (GATEUP) {
+            const int fe = brow & 63;
+            G.gu_block(c0 + fe, 2 * step + kbit, &tile, i);
+            return base + ((brow >> 6) == 0 ? G.gate_tile(tile) : G.up_tile(tile));
+        } else {
+            G.down_block(c0 + brow, 2 * step + kbit, &tile, i);
+            return base + G.down_tile(tile);
+        }
+    };
+    const void* A = GATEUP ? a.x : a.h;
+    auto load = [&](WideRaw<QT, AXB>& r, int step) {
+        step = min(step, nk - 1);  // past the end: the last step again (unused)
+        const int col = step * WBK + ach;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            if constexpr (AXB) {
+                r.x[i] = *(const uint4*)((const uint16_t*)A + arow[i] + col);
+            } else {
+                const float* p = (const float*)A + arow[i] + col;
+                r.x[2 * i] = *(const float4*)p;
+                r.x[2 * i + 1] = *(const float4*)(p + 4);
+            }
+        }
+        int li;
+        const uint8_t* tp = blk_ptr(step, &li);
+        r.w.load(tp, li);
+    };
+    // piece i (0..3) of a step's stores: the thread's i-th activation piece
+    // (zeros for padding rows) and the i-th 8 weights of its block, bf16
+    auto store_piece = [&](const WideRaw<QT, AXB>& r, int buf, int i) {
+        uint4 v;
+        if constexpr (AXB) {
+            v = r.x[i];
+        } else {
+            const float4 f0 = r.x[2 * i], f1 = r.x[2 * i + 1];
+            v = make_uint4(pack_bf16(f0.x, f0.y), pack_bf16(f0.z, f0.w), pack_bf16(f1.x, f1.y), pack_bf16(f1.z, f1.w));
+        }
+        const uint32_t keep = akeep[i] ? 0xFFFFFFFFu : 0u;
+        v = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+        *(uint4*)&L.a[buf][(tid >> 3) + 32 * i][ach] = v;
+        *(bf16x8*)&L.b[buf][brow][kbit * kQK + 8 * i] = b_operand<QT>(r.w, i);
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
+    // B rows of this wave's two 32-column groups
+    const int bro0 = GATEUP ? 32 * wn : 64 * wn;
+    const int bro1 = GATEUP ? 64 + 32 * wn : 64 * wn + 32;
+    // the products of 16 columns (substep s) of the step in LDS buffer buf
+    auto compute_sub = [&](int buf, int s) {
+        const int r = lane & 31, kq = 8 * (lane >> 5);
+        const bf16x8 a0 = *(const bf16x8*)&L.a[buf][64 * wm + r][16 * s + kq];
+        const bf16x8 a1 = *(const bf16x8*)&L.a[buf][64 * wm + 32 + r][16 * s + kq];
+        const bf16x8 b0 = *(const bf16x8*)&L.b[buf][bro0 + r][16 * s + kq];
+        const bf16x8 b1 = *(const bf16x8*)&L.b[buf][bro1 + r][16 * s + kq];
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+    };
+    // step k: LDS buffer k & 1 holds it; the register stage of step k + 1 is
+    // written to the other buffer, a quarter beside each quarter of the
+    // products (independent work the matrix cores and the vector ALU can
+    // overlap), then reloaded with step k + 1 + WST
+    WideRaw<QT, AXB> st[WST];
+#pragma unroll
+    for (int q = 0; q < WST; q++) load(st[q], q);
+#pragma unroll
+    for (int i = 0; i < 4; i++) store_piece(st[0], 0, i);
+    load(st[0], WST);
+    lds_barrier();
+    auto iter = [&](int k, WideRaw<QT, AXB>& r) {
+        const int cur = k & 1, nxt = cur ^ 1;
+#pragma unroll
+        for (int s = 0; s < WBK / 16; s++) {
+            compute_sub(cur, s);
+            store_piece(r, nxt, s);
+        }
+        load(r, k + 1 + WST);
+        lds_barrier();
+    };
+    int k = 0;
+    for (; k + WST <= nk; k += WST) {
+        iter(k, st[1]);
+        iter(k + 1, st[2]);
+        iter(k + 2, st[0]);
+    }
+    if (k < nk) iter(k, st[1]);
+    if (k + 1 < nk) iter(k + 1, st[2]);
+    // C element e of product (i, j): row 64 wm + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,
+    // column lane % 32 of the j-th B row group
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+            const int m = 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            if (m >= t.M) continue;
+            const int64_t slot = row_slot(a, t, m);
+            if constexpr (GATEUP) {
+                const float z = acc[i][0][e];
+                const float hv = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) * acc[i][1][e];
+                ((__bf16*)a.h)[slot * a.f + c0 + 32 * wn + (lane & 31)] = (__bf16)hv;
+            } else {
+                a.part[slot * a.d + c0 + 64 * wn + (lane & 31)] = acc[i][0][e];
+                a.part[slot * a.d + c0 + 64 * wn + 32 + (lane & 31)] = acc[i][1][e];
+            }
+        }
+}
+
+// Workgroup b runs on XCD b % 8 (the dispatcher deals workgroups to the eight
+// XCDs in turn), and each XCD has its own L2.  The items, tile-major (a tile's
+// feature or row groups next to each other), are cut into eight contiguous
+// runs, one per XCD, so that the groups of one tile, which read the same
+// token rows, and the tiles of one bucket, which read the same weights, share
+// an L2 instead of each XCD fetching them again.  The grid is a multiple of 8.
+constexpr int kXcds = 8;
+
+template <int QT, bool XB, bool GATEUP>
+__global__ __launch_bounds__(256, 2) void prefill_wide_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(16))) WideLds L;
+    const int ngroups = GATEUP ? a.f / WFEAT : a.d / WROWS;
+    const int n_items = a.n_tiles[3] * ngroups;
+    const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
+    const int i0 = (int)((int64_t)n_items * xcd / kXcds), i1 = (int)((int64_t)n_items * (xcd + 1) / kXcds);
+    for (int it = i0 + (int)blockIdx.x / kXcds; it < i1; it += per_xcd) {
+        const TileRec t = load_rec(a.sched_wide, it / ngroups);
+        const int c0 = (it % ngroups) * (GATEUP ? WFEAT : WROWS);
+        const uint8_t* base = tile_base(a, t);
+        if (!base) {  // fail closed: NaN rows (the schedule set the error word)
+            const int ncol = GATEUP ? WFEAT : WROWS;
+            for (int j = threadIdx.x; j < t.M * ncol; j += blockDim.x) {
+                const int64_t slot = row_slot(a, t, j / ncol);
+                if (GATEUP) ((uint16_t*)a.h)[slot * a.f + c0 + j % ncol] = 0x7FC0;
+                else a.part[slot * a.d + c0 + j % ncol] = __uint_as_float(0x7FC00000u);
+            }
+            continue;
+        }
+        wide_item<QT, XB, GATEUP>(a, t, base, c0, L);
+        // the next item's first stores into LDS wait for this one's last reads
+        lds_barrier();
+    }
+}
+
 // ---- combine ---------------------------------------------------------------------
 
 // A token's entry is taken only if the inverse map leads to a plan position
@@ -750,8 +974,21 @@ hipError_t launch_items(K kernel, int64_t items, const PrefillArgs& a, hipStream
     return hipGetLastError();
 }
 
+// Wide-tile launches: a multiple of 8 workgroups (one run of items per XCD),
+// at most the 512 that are resident at once (2 per CU), each looping over its
+// XCD's items.
+constexpr int kWideGrid = 512;
+
+template <class K>
+hipError_t launch_wide(K kernel, int64_t items, const PrefillArgs& a, hipStream_t s) {
+    if (items <= 0) return hipSuccess;
+    const int64_t g = std::min<int64_t>((items + kXcds - 1) / kXcds * kXcds, kWideGrid);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)g), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int QT, int PREC, bool XB>
-hipError_t launch_qp(const PrefillArgs& a, int big_tiles, int small_tiles, const PrefillStreams& st) {
+hipError_t launch_qp(const PrefillArgs& a, int big_tiles, int small_tiles, int wide_tiles, const PrefillStreams& st) {
     const hipStream_t s = st.s;
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, s, a, PREC);
     hipError_t e = hipGetLastError();
@@ -761,10 +998,14 @@ hipError_t launch_qp(const PrefillArgs& a, int big_tiles, int small_tiles, const
         // The two tile sizes are independent chains (disjoint buckets: their own
         // hidden and partial rows): the 64-token one on the auxiliary stream, so
         // that the two share the GPU instead of running one after the other.
-        const bool two = st.aux != nullptr && big_tiles > 0;
+        const bool two = st.aux != nullptr && big_tiles + wide_tiles > 0;
         const hipStream_t sb = two ? st.aux : s;
         if (two && e == hipSuccess) e = hipEventRecord(st.fork, s);
         if (two && e == hipSuccess) e = hipStreamWaitEvent(sb, st.fork, 0);
+        if (e == hipSuccess)
+            e = launch_wide(prefill_wide_kernel<QT, XB, true>, (int64_t)wide_tiles * (a.f / WFEAT), a, sb);
+        if (e == hipSuccess)
+            e = launch_wide(prefill_wide_kernel<QT, XB, false>, (int64_t)wide_tiles * (a.d / WROWS), a, sb);
         if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, true>, (int64_t)big_tiles * gf, a, sb);
         if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, true>, (int64_t)big_tiles * gd, a, sb);
         if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, false>, (int64_t)small_tiles * gf, a, s);
@@ -782,16 +1023,17 @@ hipError_t launch_qp(const PrefillArgs& a, int big_tiles, int small_tiles, const
 
 }  // namespace
 
-void prefill_max_tiles(int64_t T, int k, int E, bool shared, int* big_tiles, int* small_tiles) {
+void prefill_max_tiles(int64_t T, int k, int E, bool shared, int* big_tiles, int* small_tiles, int* wide_tiles) {
     const int64_t units = (T * k < E ? T * k : E) + (shared ? 1 : 0);
     const int64_t rows = T * k + (shared ? T : 0);
     *big_tiles = (int)((rows + BIG - 1) / BIG + units);
     *small_tiles = (int)((rows + SMALL - 1) / SMALL + units);
+    *wide_tiles = (int)((rows + WIDE - 1) / WIDE + units);
 }
 
 PrefillLayout prefill_layout(int64_t T, int k, int E, int d, int f, bool bf16_hidden) {
     PrefillLayout L{};
-    prefill_max_tiles(T, k, E, true, &L.cap_big, &L.cap_small);
+    prefill_max_tiles(T, k, E, true, &L.cap_big, &L.cap_small, &L.cap_wide);
     auto up = [](size_t n) { return (n + 255) / 256 * 256; };
     const size_t rows = (size_t)(T * k + T);
     size_t o = 0;
@@ -800,6 +1042,7 @@ PrefillLayout prefill_layout(int64_t T, int k, int E, int d, int f, bool bf16_hi
     L.inv = o;         o += up((size_t)T * k * 4);
     L.sched_big = o;   o += up((size_t)L.cap_big * 16);
     L.sched_small = o; o += up((size_t)L.cap_small * 16);
+    L.sched_wide = o;  o += up((size_t)L.cap_wide * 16);
     L.n_tiles = o;     o += 256;
     L.total = o;
     return L;
@@ -807,19 +1050,19 @@ PrefillLayout prefill_layout(int64_t T, int k, int E, int d, int f, bool bf16_hi
 
 hipError_t launch_ffn_prefill(const PrefillArgs& a, int prec, const PrefillStreams& s) {
     if (a.d % COLS || a.f % 16) return hipErrorInvalidValue;
-    int bt, st;
-    prefill_max_tiles(a.T, a.k, a.E, a.shared != nullptr, &bt, &st);
+    int bt, st, wt;
+    prefill_max_tiles(a.T, a.k, a.E, a.shared != nullptr, &bt, &st, &wt);
     const bool xb = a.x_bf16 != 0, bf = prec == MOE_PREC_BF16;
     if (a.g.qtype == MOE_Q8_0) {
-        if (bf) return xb ? launch_qp<MOE_Q8_0, MOE_PREC_BF16, true>(a, bt, st, s)
-                          : launch_qp<MOE_Q8_0, MOE_PREC_BF16, false>(a, bt, st, s);
-        return xb ? launch_qp<MOE_Q8_0, MOE_PREC_F32, true>(a, bt, st, s)
-                  : launch_qp<MOE_Q8_0, MOE_PREC_F32, false>(a, bt, st, s);
+        if (bf) return xb ? launch_qp<MOE_Q8_0, MOE_PREC_BF16, true>(a, bt, st, wt, s)
+                          : launch_qp<MOE_Q8_0, MOE_PREC_BF16, false>(a, bt, st, wt, s);
+        return xb ? launch_qp<MOE_Q8_0, MOE_PREC_F32, true>(a, bt, st, wt, s)
+                  : launch_qp<MOE_Q8_0, MOE_PREC_F32, false>(a, bt, st, wt, s);
     }
-    if (bf) return xb ? launch_qp<MOE_Q4_0, MOE_PREC_BF16, true>(a, bt, st, s)
-                      : launch_qp<MOE_Q4_0, MOE_PREC_BF16, false>(a, bt, st, s);
-    return xb ? launch_qp<MOE_Q4_0, MOE_PREC_F32, true>(a, bt, st, s)
-              : launch_qp<MOE_Q4_0, MOE_PREC_F32, false>(a, bt, st, s);
+    if (bf) return xb ? launch_qp<MOE_Q4_0, MOE_PREC_BF16, true>(a, bt, st, wt, s)
+                      : launch_qp<MOE_Q4_0, MOE_PREC_BF16, false>(a, bt, st, wt, s);
+    return xb ? launch_qp<MOE_Q4_0, MOE_PREC_F32, true>(a, bt, st, wt, s)
+              : launch_qp<MOE_Q4_0, MOE_PREC_F32, false>(a, bt, st, wt, s);
 }
 
 }  // namespace moe

@@ -150,7 +150,9 @@ __host__ __device__ inline int64_t decode_h_floats(int k, int f, int E) { return
 hipError_t launch_ffn_decode(const Geom& g, const FfnArgs& a, int prec, hipStream_t s);
 
 // Prefill (T > kDecodeMaxT): bucket tiles on the matrix cores; see ffn_prefill.hip.
-constexpr int kPrefillBM = 64;  // tokens per large tile
+constexpr int kPrefillBM = 64;     // tokens per large tile
+constexpr int kPrefillWide = 128;  // tokens per wide tile (buckets of at least wide_min tokens)
+constexpr int kWideMinDefault = 1024;
 
 struct PrefillArgs {
     Geom g;
@@ -175,21 +177,24 @@ struct PrefillArgs {
     int32_t* inv;          // [T*k] plan position of entry t*k + j
     int32_t* sched_big;    // [4 * cap_big] tile records (16-byte aligned), 64-token tiles
     int32_t* sched_small;  // [4 * cap_small] tile records (16-byte aligned), 16-token tiles
-    int32_t* n_tiles;      // [4]: tiles of each size, the plan positions the units cover, unused
-    int cap_big, cap_small;  // records the two arrays hold
+    int32_t* sched_wide;   // [4 * cap_wide] tile records (16-byte aligned), 128-token tiles
+    int32_t* n_tiles;      // [4]: 64-token tiles, 16-token tiles, the plan positions the units
+                           // cover, 128-token tiles
+    int cap_big, cap_small, cap_wide;  // records the three arrays hold
+    int wide_min;          // bf16 mode: buckets with at least this many tokens use 128-token tiles
     float* y;
     int* err;
 };
 
 // Upper bounds on the tiles of each size a call of T tokens can need.
-void prefill_max_tiles(int64_t T, int k, int E, bool shared, int* big_tiles, int* small_tiles);
+void prefill_max_tiles(int64_t T, int k, int E, bool shared, int* big_tiles, int* small_tiles, int* wide_tiles);
 
 // The chunk path's workspace carved out of one buffer (256-byte aligned
 // sections): hidden rows, partial rows, entry inverse, the two tile-record
 // arrays and the counts.  Returns the bytes needed for T tokens.
 struct PrefillLayout {
-    size_t h, part, inv, sched_big, sched_small, n_tiles, total;
-    int cap_big, cap_small;
+    size_t h, part, inv, sched_big, sched_small, sched_wide, n_tiles, total;
+    int cap_big, cap_small, cap_wide;
 };
 PrefillLayout prefill_layout(int64_t T, int k, int E, int d, int f, bool bf16_hidden);
 

@@ -31,8 +31,9 @@ struct moe_ctx {
     float* ph = nullptr;
     float* ppart = nullptr;
     int32_t* pinv = nullptr;
-    int32_t* psched = nullptr;  // big tiles, small tiles, 4 counts
-    int p_big = 0, p_small = 0;
+    int32_t* psched = nullptr;  // big tiles, small tiles, wide tiles, 4 counts
+    int p_big = 0, p_small = 0, p_wide = 0;
+    int wide_min = moe::kWideMinDefault;  // bf16 chunk calls: buckets from which 128-token tiles run
     int last_prefill_prec = -1; // mode of the last chunk call (-1: none yet)
     float* logits_ws = nullptr;// [max_T * E]
 
@@ -365,6 +366,8 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     if (c->cfg.gemm_min_tokens == 0) c->cfg.gemm_min_tokens = 16;
     c->g = g;
     c->host_only = cfg->device < 0;
+    // measurement knob: the bucket size from which bf16 chunk calls use 128-token tiles
+    if (const char* e = getenv("MOE_WIDE_MIN_TOKENS")) c->wide_min = std::max(1, atoi(e));
     const int64_t n_keys = (int64_t)cfg->n_layers * cfg->n_experts;
     c->owner.assign(cfg->n_slots, -1);
     c->slot_of.assign(n_keys, -1);
@@ -389,11 +392,11 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
             return cleanup(MOE_ENOMEM);
         if (T > moe::kDecodeMaxT) {
             const size_t rows = (size_t)(T * cfg->top_k + T);
-            moe::prefill_max_tiles(T, cfg->top_k, cfg->n_experts, true, &c->p_big, &c->p_small);
+            moe::prefill_max_tiles(T, cfg->top_k, cfg->n_experts, true, &c->p_big, &c->p_small, &c->p_wide);
             if (hipMalloc(&c->ph, sizeof(float) * rows * cfg->d_ff) != hipSuccess) return cleanup(MOE_ENOMEM);
             if (hipMalloc(&c->ppart, sizeof(float) * rows * cfg->d_model) != hipSuccess) return cleanup(MOE_ENOMEM);
             if (hipMalloc(&c->pinv, sizeof(int32_t) * (size_t)T * cfg->top_k) != hipSuccess) return cleanup(MOE_ENOMEM);
-            if (hipMalloc(&c->psched, sizeof(int32_t) * (4 * ((size_t)c->p_big + c->p_small) + 4)) != hipSuccess)
+            if (hipMalloc(&c->psched, sizeof(int32_t) * (4 * ((size_t)c->p_big + c->p_small + c->p_wide) + 4)) != hipSuccess)
                 return cleanup(MOE_ENOMEM);
         }
         if (hipMemset(c->pt, 0xFF, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_EHIP);
@@ -897,6 +900,7 @@ static moe::PrefillArgs prefill_args(moe_ctx* c, const moe::FfnArgs& a, int32_t 
     p.d = cf.d_model;
     p.f = cf.d_ff;
     p.gemm_min = cf.gemm_min_tokens;
+    p.wide_min = c->wide_min;
     p.y = y;
     p.err = c->err_word;
     return p;
@@ -937,9 +941,11 @@ moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     p.inv = c->pinv;
     p.sched_big = c->psched;
     p.sched_small = c->psched + 4 * (size_t)c->p_big;
-    p.n_tiles = p.sched_small + 4 * (size_t)c->p_small;
+    p.sched_wide = p.sched_small + 4 * (size_t)c->p_small;
+    p.n_tiles = p.sched_wide + 4 * (size_t)c->p_wide;
     p.cap_big = c->p_big;
     p.cap_small = c->p_small;
+    p.cap_wide = c->p_wide;
     HIP_TRY(c, moe::launch_ffn_prefill(p, prec, moe::PrefillStreams{s, c->aux, c->fork_ev, c->join_ev}));
     c->last_prefill_prec = prec;
     return MOE_OK;
@@ -972,9 +978,11 @@ moe_status moe_expert_ffn_static(moe_ctx* c, int32_t layer, const void* x, int32
     p.inv = (int32_t*)(b + L.inv);
     p.sched_big = (int32_t*)(b + L.sched_big);
     p.sched_small = (int32_t*)(b + L.sched_small);
+    p.sched_wide = (int32_t*)(b + L.sched_wide);
     p.n_tiles = (int32_t*)(b + L.n_tiles);
     p.cap_big = L.cap_big;
     p.cap_small = L.cap_small;
+    p.cap_wide = L.cap_wide;
     HIP_TRY(c, moe::launch_ffn_prefill(p, prec, moe::PrefillStreams{s, c->aux, c->fork_ev, c->join_ev}));
     return MOE_OK;
 }

@@ -8,6 +8,8 @@ rounding midpoint, and y within 1e-3 per row of the oracle's down projection
 and combine of the GPU's own hidden codes; end-to-end statistics reported.
 Bitwise-identical outputs under any slot assignment.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -32,7 +34,7 @@ def _say(*a):
 
 
 class Chunk:
-    def __init__(self, wl, T, logits, prec, gemm_min=16, perm_seed=None, x_dtype=None):
+    def __init__(self, wl, T, logits, prec, gemm_min=16, perm_seed=None, x_dtype=None, wide_min=None):
         self.wl, self.T, self.prec = wl, T, prec
         E, k, d, f = wl["E"], wl["k"], wl["d"], wl["f"]
         self.x_dtype = x_dtype or wl["x_dtype"]
@@ -46,8 +48,20 @@ class Chunk:
         cfg = m.make_config(1, E, k, d, f, H.QT[wl["qtype"]], n, T, device=-1)
         pb = m.moe_payload_bytes(cfg)
         self.pool = torch.zeros(n * pb, dtype=torch.uint8, device="cuda")
-        self.ctx = m.Context(1, E, k, d, f, H.QT[wl["qtype"]], n, T, gemm_min_tokens=gemm_min, device=0,
-                             slot_pool=self.pool)
+        # wide_min: the bucket size from which bf16 calls use 128-token tiles
+        # (a context reads it when it is created)
+        old_env = os.environ.get("MOE_WIDE_MIN_TOKENS")
+        if wide_min is not None:
+            os.environ["MOE_WIDE_MIN_TOKENS"] = str(wide_min)
+        try:
+            self.ctx = m.Context(1, E, k, d, f, H.QT[wl["qtype"]], n, T, gemm_min_tokens=gemm_min, device=0,
+                                 slot_pool=self.pool)
+        finally:
+            if wide_min is not None:
+                if old_env is None:
+                    del os.environ["MOE_WIDE_MIN_TOKENS"]
+                else:
+                    os.environ["MOE_WIDE_MIN_TOKENS"] = old_env
         self.payloads = {e: torch.from_numpy(H.payload(self.ctx, r)).cuda() for e, r in self.recs.items()}
         self.sh_dev = H.device_payload(self.ctx, self.shared) if self.shared is not None else None
         self.x_dev = H.torch_x(self.x, self.x_dtype)
@@ -92,29 +106,32 @@ class Chunk:
         return np.bincount(self.ids.reshape(-1), minlength=self.wl["E"])
 
 
-@pytest.mark.parametrize("T,prec,gemm_min", [(37, oracle.PREC_BF16, 16), (37, oracle.PREC_F32, 16),
-                                             (100, oracle.PREC_BF16, 16), (100, oracle.PREC_BF16, 1000),
-                                             (5, oracle.PREC_BF16, 2), (200, oracle.PREC_F32, 16)])
-def test_prefill_tiny_shape(T, prec, gemm_min):
+@pytest.mark.parametrize("T,prec,gemm_min,wide_min", [
+    (37, oracle.PREC_BF16, 16, None), (37, oracle.PREC_F32, 16, None), (100, oracle.PREC_BF16, 16, None),
+    (100, oracle.PREC_BF16, 1000, None), (5, oracle.PREC_BF16, 2, None), (200, oracle.PREC_F32, 16, None),
+    (100, oracle.PREC_BF16, 16, 8), (300, oracle.PREC_BF16, 16, 60), (37, oracle.PREC_BF16, 2, 1)])
+def test_prefill_tiny_shape(T, prec, gemm_min, wide_min):
     """Tiny layer (8 experts, top-2, d 256, d_ff 128): buckets of ~9-50 tokens cover
-    both tile sizes, ragged tiles and fp32 mode."""
+    every tile size (16, 64 and, with wide_min lowered, 128 tokens), ragged tiles
+    and fp32 mode."""
     wl = dict(synth.workload("tiny"), shared=True)
     lg = synth.zipf_gumbel_logits(wl["seed"] + T, T, wl["E"], 1.1)
-    _say("prefill tiny", T, prec, gemm_min)
-    c = Chunk(wl, T, lg, prec, gemm_min)
+    _say("prefill tiny", T, prec, gemm_min, wide_min)
+    c = Chunk(wl, T, lg, prec, gemm_min, wide_min=wide_min)
     c.place(list(range(len(c.used))))
     y = c.run()
     st = c.verify(y, np.arange(T))
     _say("  buckets", sorted(c.bucket_sizes()[c.used].tolist()), st)
 
 
-@pytest.mark.parametrize("T,prec", [(24, oracle.PREC_BF16), (24, oracle.PREC_F32)])
-def test_prefill_mtp_q4(T, prec):
-    """Q4_0 experts through the chunk path."""
+@pytest.mark.parametrize("T,prec,wide_min", [(24, oracle.PREC_BF16, None), (24, oracle.PREC_F32, None),
+                                             (24, oracle.PREC_BF16, 2)])
+def test_prefill_mtp_q4(T, prec, wide_min):
+    """Q4_0 experts through the chunk path (with wide_min 2: on 128-token tiles)."""
     wl = synth.workload("mtp")
     lg = synth.zipf_gumbel_logits(wl["seed"], T, wl["E"], 1.1)
-    _say("prefill q4", T, prec)
-    c = Chunk(wl, T, lg, prec, gemm_min=4)
+    _say("prefill q4", T, prec, wide_min)
+    c = Chunk(wl, T, lg, prec, gemm_min=4, wide_min=wide_min)
     c.place(list(range(len(c.used))))
     y = c.run()
     _say("  ", c.verify(y, np.arange(T)))
@@ -155,11 +172,12 @@ def _tile_edge_tokens(c, gemm_min=16, big=64, small=16):
     toks.update({0, min(big, T) - 1, (T - 1) // big * big, T - 1})
     return np.array(sorted(toks))
 
-def test_prefill_cache_transparency():
+@pytest.mark.parametrize("wide_min", [None, 8])
+def test_prefill_cache_transparency(wide_min):
     wl = dict(synth.workload("tiny"), shared=True)
     T = 150
     lg = synth.zipf_gumbel_logits(wl["seed"] + 5, T, wl["E"], 1.1)
-    c = Chunk(wl, T, lg, oracle.PREC_BF16)
+    c = Chunk(wl, T, lg, oracle.PREC_BF16, wide_min=wide_min)
     n = len(c.used)
     c.place(list(range(n)))
     y0 = c.run()
@@ -171,11 +189,12 @@ def test_prefill_cache_transparency():
     assert np.array_equal(y0.view(np.uint32), y2.view(np.uint32))
 
 
-def test_prefill_unmapped_expert_fails_closed():
+@pytest.mark.parametrize("wide_min", [None, 4])
+def test_prefill_unmapped_expert_fails_closed(wide_min):
     wl = dict(synth.workload("tiny"), shared=True)
     T = 60
     lg = synth.zipf_gumbel_logits(wl["seed"] + 9, T, wl["E"], 1.1)
-    c = Chunk(wl, T, lg, oracle.PREC_BF16)
+    c = Chunk(wl, T, lg, oracle.PREC_BF16, wide_min=wide_min)
     c.place(list(range(len(c.used))))
     victim = c.used[-1]
     moe.moe_slot_bind(c.ctx, 0, victim, -1)

@@ -51,13 +51,14 @@ def test_decode_path_shapes(d, f, qt, xd, T):
 
 
 @pytest.mark.parametrize("d,f,qt,xd", SHAPES)
-@pytest.mark.parametrize("prec", [oracle.PREC_BF16, oracle.PREC_F32])
-def test_chunk_path_shapes(d, f, qt, xd, prec):
-    print("chunk shape", d, f, qt, xd, prec, flush=True)
+@pytest.mark.parametrize("prec,wide_min", [(oracle.PREC_BF16, None), (oracle.PREC_F32, None),
+                                           (oracle.PREC_BF16, 4)])
+def test_chunk_path_shapes(d, f, qt, xd, prec, wide_min):
+    print("chunk shape", d, f, qt, xd, prec, wide_min, flush=True)
     wl = dict(synth.workload("tiny"), **_wl(d, f, qt, xd))
     T = 40
     lg = synth.zipf_gumbel_logits(wl["seed"] + d + f, T, wl["E"], 1.1)
-    c = Chunk(wl, T, lg, prec)
+    c = Chunk(wl, T, lg, prec, wide_min=wide_min)
     c.place(list(range(len(c.used))))
     y = c.run()
     st = c.verify(y, np.arange(T))
