@@ -357,7 +357,15 @@ moe_status moe_expert_ffn_static(moe_ctx* ctx, int32_t layer, const void* x, int
  * top_k] int32, topk_w [T, top_k] fp32 and plan, as moe_route_union writes
  * them, and y [T, d_model] fp32 as moe_expert_ffn.  1 <= T <= min(4,
  * max_tokens) and n_experts <= 256, else MOE_EINVAL.  Waits on `stream` for
- * fills not yet awaited.  Calls on one context must not overlap. */
+ * fills not yet awaited.  Calls on one context must not overlap.
+ * Co-residency is not needed: workgroups wait only for workgroups of lower
+ * index that wait for none of higher index (router rows on the first
+ * workgroups, which exit; hidden rows from the gate/up workgroups), and
+ * workgroups are dispatched in index order, so kernels running beside it on
+ * other streams can delay the launch but not stall it.  If the launch itself
+ * fails, the call routes in a launch of its own (moe_route_union) and then
+ * runs the experts on that plan: the same results, two launches
+ * (moe_route_splits counts such calls). */
 moe_status moe_route_ffn(moe_ctx* ctx, int32_t layer, const void* x, int32_t x_dtype, const float* w_router,
                          const float* logits_in, int64_t T, int32_t* topk_ids, float* topk_w,
                          const moe_plan* plan, const void* shared_payload, int32_t prec, float* y,
@@ -403,6 +411,11 @@ moe_status moe_probe_mfma(int32_t iters, int32_t grid, int32_t shape, float* sin
  * instruction from local data share memory (no bank conflicts), iters rounds
  * of 8 reads; *bytes (host) receives the bytes read; sink: device [1] uint32. */
 moe_status moe_probe_lds(int32_t iters, int32_t grid, uint32_t* sink, int64_t* bytes, moe_stream stream);
+
+/* Calls of moe_route_ffn with router weights since moe_create that took the
+ * two-launch path (the one launch failed, or the MOE_SPLIT_ROUTE environment
+ * variable was set when the context was created). */
+moe_status moe_route_splits(const moe_ctx* ctx, uint64_t* out);
 
 /* Device address of the page table ([n_layers x n_experts] int32), for tests. */
 moe_status moe_page_table(const moe_ctx* ctx, int32_t** out);

@@ -26,13 +26,14 @@
 //     slots: per lane over its tiles in order, then the four lanes of a row,
 //     then the waves.
 //
-// A launch that routes takes the caller's logits, or computes them: wave 0 (or
-// more waves) of each gate/up workgroup whose first item is routed computes
-// about one router row and stores it with device scope into the workspace.
-// Every workgroup then reads the logits (polling until none is pending),
-// selects each token's top-k and forms the union itself, with the same code as
-// the route kernels; down workgroup 0 also writes ids, weights and plan out.
-// The shared expert's items start before the routing is known.
+// A launch that routes takes the caller's logits, or computes them: router
+// workgroups, the first in dispatch order, compute one router row per wave and
+// store it with device scope into the workspace, then exit.  Every other
+// workgroup then reads the logits (polling until none is pending), selects
+// each token's top-k and forms the union itself, with the same code as the
+// route kernels; down workgroup 0 also writes ids, weights and plan out.  The
+// shared expert's items start before the routing is known.  No workgroup ever
+// waits for one of higher index, so the launch needs no co-residency.
 //
 // Every weight byte of the step is requested as soon as its workgroup has the
 // unit's slot: each role reads what it needs from the plan and the whole
@@ -194,7 +195,8 @@ struct DGrid {
     int gu_tpr;      // gate (or up) tiles per 16 hidden units: d_model / 128
     int dn_tpr;      // down tiles per 16 output rows: d_ff / 128
     int nb_rows;     // hidden rows that fit the LDS at once
-    int n_gu_wg;     // gate/up workgroups (block indices [0, n_gu_wg))
+    int n_router;    // router workgroups (block indices [0, n_router)), a launch that computes the logits
+    int n_gu_wg;     // gate/up workgroups (block indices [n_router, n_router + n_gu_wg))
     int reset_per;   // pending words each down workgroup writes into the other half
     int64_t half;    // floats per workspace half
     int64_t lg_off;  // offset of the logits in a copy (after the hidden rows)
@@ -249,64 +251,33 @@ struct LgIn {
     }
 };
 
-// Router rows of gate/up workgroup h of the H that take them, in a launch that
-// routes from x: experts h + j H (j = wave, wave + 8, ...), every token, with
-// the route kernel's row dot, stored with device scope into the logits of the
-// workspace half of this launch (from `count`).  Spread one row per workgroup
-// over the chip, the 2 MiB of router weights of a 256-expert layer stream at
-// once.  A gate/up workgroup is never late (see gate_up_role), so it writes
-// the half the others read.
-__device__ void router_rows(const FfnArgs& a, const DGrid& g, uint32_t count, int h, int H) {
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for (int e = h + wave * H; e < a.E; e += kWaves * H) {
-        const float* row = a.w_router + (int64_t)e * g.d;
-        for (int t = 0; t < a.T; t++) {
-            const float v = row_dot(row, a.x, a.x_bf16, t, g.d, lane);
-            float* dst = a.hbuf + (int64_t)launch_parity(count, g.n_down) * g.half + g.lg_off + (int64_t)t * a.E + e;
-            if (lane < kDecodeCopies)
-                __hip_atomic_store(dst + lane * g.copy, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+// Router workgroups (a launch that computes the logits): the first n_router = E
+// workgroups in dispatch order, wave 0 of workgroup r computing expert row r
+// for every token with the route kernel's row dot (the same bits), so that the
+// router weights stream through as many CUs as there are rows (4 rows per
+// workgroup on 64 CUs finished the rows about 1 us later, 8 on 32 CUs later
+// still); the other waves exit at once.
+// The rows are stored with device scope into every copy of the logits of this
+// launch's workspace half (from the launch count).  They wait for nothing and exit, and
+// every workgroup that waits for the logits has a higher index: workgroups are
+// dispatched in index order, so the rows are always computed, whatever else
+// occupies the GPU, with no need for all workgroups to be resident at once.
+// A router workgroup reads the launch count before the down workgroups can
+// move it: they finish only after the gate/up workgroups have routed, which
+// needs every row.
+__device__ void router_role(const FfnArgs& a, const DGrid& g, int r) {
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x >= 64) return;
+    const uint32_t count = __hip_atomic_load(a.sync + kSyncCount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int e = r;
+    const float* row = a.w_router + (int64_t)e * g.d;
+    float* dst = a.hbuf + (int64_t)launch_parity(count, g.n_down) * g.half + g.lg_off + e;
+    for (int t = 0; t < a.T; t++) {
+        const float v = row_dot(row, a.x, a.x_bf16, t, g.d, lane);
+        if (lane < kDecodeCopies)
+            __hip_atomic_store(dst + (int64_t)t * a.E + lane * g.copy, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
-
-// A router row whose weights are loaded with the workgroup's first loads and
-// whose dot product is taken against the token's activations once they are in
-// LDS (one token; each wave at most one row, d <= 2048): the same slices per
-// lane, in the same order, as the route kernel's row dot, so the same bits.
-struct RouterRowLds {
-    float4 wv[8];
-    int e;
-    __device__ void load(const FfnArgs& a, const DGrid& g, int h, int H) {
-        const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        e = h + wave * H;
-        const float* row = a.w_router + (int64_t)min(e, a.E - 1) * g.d;  // a valid row either way
-#pragma unroll
-        for (int u = 0; u < 8; u++) wv[u] = *(const float4*)(row + min(lane * 4 + 256 * u, g.d - 4));
-    }
-    __device__ void finish(const FfnArgs& a, const DGrid& g, uint32_t count, const float* xl) const {
-        const int lane = threadIdx.x & 63;
-        if (e >= a.E) return;
-        float acc = 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const int c = lane * 4 + 256 * u;
-            if (c < g.d) {
-                const float4 xv = *(const float4*)(xl + c);
-                const float4 w = make_float4(__uint_as_float(opaque(__float_as_uint(wv[u].x))),
-                                             __uint_as_float(opaque(__float_as_uint(wv[u].y))),
-                                             __uint_as_float(opaque(__float_as_uint(wv[u].z))),
-                                             __uint_as_float(opaque(__float_as_uint(wv[u].w))));
-                acc = fmaf(w.x, xv.x, acc);
-                acc = fmaf(w.y, xv.y, acc);
-                acc = fmaf(w.z, xv.z, acc);
-                acc = fmaf(w.w, xv.w, acc);
-            }
-        }
-        const float v = seg_sum<64>(acc);
-        float* dst = a.hbuf + (int64_t)launch_parity(count, g.n_down) * g.half + g.lg_off + e;
-        if (lane < kDecodeCopies) __hip_atomic_store(dst + lane * g.copy, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-};
 
 // The step's routing, computed by this workgroup from the logits into LDS: the
 // top-k of token t on wave t, then the union (the same code and so the same
@@ -464,19 +435,7 @@ __device__ __forceinline__ void gate_up_role(const FfnArgs& a, const DGrid& g, i
     // ranges, entries) or the caller's logits, the page-table row and, for one
     // token, its activations.
     const uint32_t count = __hip_atomic_load(a.sync + kSyncCount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // router rows go to the first workgroups in dispatch order (one each on as
-    // many CUs as there are rows; later workgroups share CUs with the down
-    // workgroups and start later), the shared expert's included; with one token
-    // and at most one row per wave, against the activations this workgroup
-    // stages in LDS anyway (exact values: bf16 input, or fp32 kept in fp32)
     const int S = has_shared ? g.n_rg / RG : 0;  // items of the shared expert
-    const int h0 = 0, H = g.n_gu_wg;
-    const bool rows_here = a.route == kRouteRouter && wg >= h0;
-    constexpr bool kOneToken = TG == 1;
-    const bool rows_lds = kOneToken && (a.x_bf16 || PREC == MOE_PREC_F32) && H * kWaves >= a.E && g.d <= 2048;
-    RouterRowLds rr;
-    if (rows_here && rows_lds) rr.load(a, g, wg - h0, H);
-    if (rows_here && !rows_lds) router_rows(a, g, count, wg - h0, H);
     const bool plan_in = a.route == kRoutePlan;  // a launch that routes reads no plan
     const int na_raw = plan_in ? *a.n_active : 0;
     PtRow ptr;
@@ -496,8 +455,6 @@ __device__ __forceinline__ void gate_up_role(const FfnArgs& a, const DGrid& g, i
     if constexpr (TG == 1) x1.store(a, g.d, L.x[0]);
     lg1.store(a, L.lg);
     lds_barrier();
-    if constexpr (kOneToken)
-        if (rows_here && rows_lds) rr.finish(a, g, count, L.x[0]);
     const int par = __builtin_amdgcn_readfirstlane(launch_parity(opaque(count), g.n_down));
     // A launch that routes counts its gate/up workgroups in: the down workgroups
     // finish (and so move the launch count) only once all have read it, so no
@@ -944,8 +901,9 @@ template <int QT, int TG> constexpr int rows_per_item() { return TG > 1 ? 2 : 1;
 template <int QT, int PREC, int TG, int PPW, int DPW>
 __global__ __launch_bounds__(kThreads, 4) void ffn_decode_kernel(FfnArgs a, DGrid g) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-    const int b = blockIdx.x;
-    if (b < g.n_gu_wg) gate_up_role<QT, PREC, TG, rows_per_item<QT, TG>(), PPW>(a, g, b, lds);
+    const int b = blockIdx.x - g.n_router;
+    if (b < 0) router_role(a, g, blockIdx.x);
+    else if (b < g.n_gu_wg) gate_up_role<QT, PREC, TG, rows_per_item<QT, TG>(), PPW>(a, g, b, lds);
     else down_role<QT, PREC, TG, DPW>(a, g, b - g.n_gu_wg, lds);
 }
 
@@ -974,11 +932,20 @@ hipError_t launch_k(DGrid g, const FfnArgs& a, hipStream_t s) {
     // resident: no workgroup waits for a slot), at most one per item.
     const int items = g.units_max * (g.n_rg / rows_per_item<QT, TG>());
     const int cap = resident_capacity((const void*)kern);
-    // A launch that routes needs every workgroup resident: gate/up workgroups
-    // wait for router rows that other gate/up workgroups compute.
-    if (a.route != kRoutePlan && cap <= g.n_down) return hipErrorInvalidConfiguration;
-    g.n_gu_wg = cap > g.n_down ? std::min(items, cap - g.n_down) : items;
-    hipLaunchKernelGGL(kern, dim3(g.n_gu_wg + g.n_down), dim3(kThreads), 0, s, a, g);
+    // Every wait in a launch is for workgroups of lower index that wait for
+    // nothing of higher index: gate/up workgroups wait only for router
+    // workgroups (which wait for nothing), down workgroups for router and
+    // gate/up workgroups.  Workgroups are dispatched in index order, so what a
+    // workgroup waits for has been dispatched and finishes even when other
+    // kernels leave room for only part of the grid; sizing the grid to what is
+    // resident only keeps every workgroup running from the start.
+    // Router workgroups exit after one row, so the gate/up and down workgroups
+    // that do not fit beside them at first are dispatched a few microseconds
+    // in, long before the routing they wait for is complete.
+    g.n_router = a.route == kRouteRouter ? a.E : 0;
+    const int room = cap - g.n_down;
+    g.n_gu_wg = room > 0 ? std::min(items, room) : std::min(items, 64);
+    hipLaunchKernelGGL(kern, dim3(g.n_router + g.n_gu_wg + g.n_down), dim3(kThreads), 0, s, a, g);
     return hipGetLastError();
 }
 

@@ -34,6 +34,8 @@ struct moe_ctx {
     int32_t* psched = nullptr;  // big tiles, small tiles, wide tiles, 4 counts
     int p_big = 0, p_small = 0, p_wide = 0;
     int wide_min = moe::kWideMinDefault;  // bf16 chunk calls: buckets from which 128-token tiles run
+    bool split_route = false;  // moe_route_ffn with router weights: always the two-launch path (tests)
+    uint64_t route_splits = 0; // moe_route_ffn calls that took the two-launch path
     int last_prefill_prec = -1; // mode of the last chunk call (-1: none yet)
     float* logits_ws = nullptr;// [max_T * E]
 
@@ -368,6 +370,8 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     c->host_only = cfg->device < 0;
     // measurement knob: the bucket size from which bf16 chunk calls use 128-token tiles
     if (const char* e = getenv("MOE_WIDE_MIN_TOKENS")) c->wide_min = std::max(1, atoi(e));
+    // test knob: take moe_route_ffn's two-launch path even where the cooperative launch would run
+    if (const char* e = getenv("MOE_SPLIT_ROUTE")) c->split_route = atoi(e) != 0;
     const int64_t n_keys = (int64_t)cfg->n_layers * cfg->n_experts;
     c->owner.assign(cfg->n_slots, -1);
     c->slot_of.assign(n_keys, -1);
@@ -1015,7 +1019,28 @@ moe_status moe_route_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dty
     a.o_experts = plan->experts;
     a.o_offsets = plan->offsets;
     a.o_entries = plan->entries;
-    HIP_TRY(c, moe::launch_ffn_decode(c->g, a, prec, s));
+    if (a.route == moe::kRouteRouter && !c->split_route) {
+        const hipError_t e = moe::launch_ffn_decode(c->g, a, prec, s);
+        if (e == hipSuccess) return MOE_OK;
+        (void)hipGetLastError();  // a refused cooperative launch enqueued nothing
+    } else if (a.route != moe::kRouteRouter) {
+        HIP_TRY(c, moe::launch_ffn_decode(c->g, a, prec, s));
+        return MOE_OK;
+    }
+    // The router's logits in a launch of their own (with the top-k and the
+    // union), then the experts on that plan: the same results bit for bit,
+    // with no wait between workgroups of the routing.
+    c->route_splits++;
+    if (moe_status st = moe_route_union(c, x, x_dtype, w_router, nullptr, T, topk_ids, topk_w, nullptr, plan, stream))
+        return st;
+    moe::FfnArgs b = ffn_args(c, layer, x, x_dtype, T, plan, topk_w, shared_payload, y);
+    HIP_TRY(c, moe::launch_ffn_decode(c->g, b, prec, s));
+    return MOE_OK;
+}
+
+moe_status moe_route_splits(const moe_ctx* c, uint64_t* out) {
+    if (!c || !out) return MOE_EINVAL;
+    *out = c->route_splits;
     return MOE_OK;
 }
 

@@ -9,24 +9,33 @@
 namespace moe {
 
 // Lane's share of row . x[t] (float4 slices at a 1 KiB stride, in order), then
-// the fixed lane butterfly: every lane returns the same bits.
+// the fixed lane butterfly: every lane returns the same bits.  Every load of a
+// pass is issued before any is used, from a clamped (always valid) address:
+// a load under a condition makes the compiler wait for it before the next one
+// is issued, which turned one memory round trip into several.
 __device__ inline float row_dot(const float* row, const void* x, int x_bf16, int t, int d, int lane) {
     constexpr int U = 8;  // slices in flight per lane (d_model 2048 is 8 slices)
     float acc = 0.f;
     for (int c0 = lane * 4; c0 < d; c0 += 256 * U) {
         float4 wv[U], xv[U];
+        if (x_bf16) {
+            uint2 xb[U];
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int c = c0 + 256 * u;
-            if (c < d) {
+            for (int u = 0; u < U; u++) {
+                const int c = min(c0 + 256 * u, d - 4);
                 wv[u] = *(const float4*)(row + c);
-                if (x_bf16) {
-                    const uint2 b = *(const uint2*)((const uint16_t*)x + (int64_t)t * d + c);
-                    xv[u] = make_float4(bf16_bits_to_f32(b.x & 0xFFFF), bf16_bits_to_f32(b.x >> 16),
-                                        bf16_bits_to_f32(b.y & 0xFFFF), bf16_bits_to_f32(b.y >> 16));
-                } else {
-                    xv[u] = *(const float4*)((const float*)x + (int64_t)t * d + c);
-                }
+                xb[u] = *(const uint2*)((const uint16_t*)x + (int64_t)t * d + c);
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                xv[u] = make_float4(bf16_bits_to_f32(xb[u].x & 0xFFFF), bf16_bits_to_f32(xb[u].x >> 16),
+                                    bf16_bits_to_f32(xb[u].y & 0xFFFF), bf16_bits_to_f32(xb[u].y >> 16));
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int c = min(c0 + 256 * u, d - 4);
+                wv[u] = *(const float4*)(row + c);
+                xv[u] = *(const float4*)((const float*)x + (int64_t)t * d + c);
             }
         }
 #pragma unroll

@@ -82,6 +82,7 @@ def _load() -> C.CDLL:
         "moe_stats": (C.c_int, [P, C.POINTER(C.c_uint64)]),
         "moe_check": (C.c_int, [P, P]),
         "moe_page_table": (C.c_int, [P, C.POINTER(P)]),
+        "moe_route_splits": (C.c_int, [P, C.POINTER(C.c_uint64)]),
         "moe_hidden_rows": (C.c_int, [P, C.POINTER(P), C.POINTER(I32)]),
         "moe_probe_read": (C.c_int, [P, I64, I32, P, P]),
         "moe_probe_mfma": (C.c_int, [I32, I32, I32, P, C.POINTER(I64), P]),
@@ -99,7 +100,7 @@ EXPORTS = ("moe_payload_bytes", "moe_plan_bytes", "moe_pack_expert", "moe_unpack
            "moe_destroy", "moe_last_error", "moe_status_string", "moe_route", "moe_plan_union", "moe_route_union",
            "moe_slot_map", "moe_slot_prefetch", "moe_prefetch_stats", "moe_slot_fill", "moe_slot_stage", "moe_slot_pull", "moe_route_pull", "moe_slot_release",
            "moe_slot_bind", "moe_expert_ffn", "moe_expert_ffn_static",
-           "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table", "moe_hidden_rows", "moe_probe_read",
+           "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table", "moe_route_splits", "moe_hidden_rows", "moe_probe_read",
            "moe_probe_mfma", "moe_probe_lds")
 
 
@@ -504,6 +505,13 @@ def moe_page_table(ctx: Context) -> np.ndarray:
     if st != 0:
         raise MoeError(MOE_EHIP, f"hipMemcpy of the page table failed ({st})")
     return out
+
+
+def moe_route_splits(ctx: Context) -> int:
+    """moe_route_ffn calls (with router weights) that took the two-launch path."""
+    v = C.c_uint64()
+    _call(ctx, _lib.moe_route_splits(ctx.handle, C.byref(v)))
+    return int(v.value)
 
 
 def moe_hidden_rows(ctx: Context, rows: int):

@@ -185,3 +185,39 @@ def test_route_ffn_validation():
     with pytest.raises(Exception):  # more than 256 experts
         moe.moe_route_ffn(big, 0, x, ids, w, moe.Plan(big, 4), y,
                           logits_in=torch.zeros(4, 300, dtype=torch.float32, device="cuda"))
+
+
+def test_route_ffn_two_launch_path_matches(monkeypatch):
+    """The two-launch path a failed launch falls back to (forced here) gives the
+    same ids, weights, plan and outputs as the one launch."""
+    L = Layer("decode", 1, [0, 1])
+    want = {s: L.host(L.fused(s)) for s in (0, 1)}
+    assert moe.moe_route_splits(L.ctx) == 0, "the one launch failed"
+    monkeypatch.setenv("MOE_SPLIT_ROUTE", "1")
+    L2 = Layer("decode", 1, [0, 1])
+    monkeypatch.delenv("MOE_SPLIT_ROUTE")
+    for s in (0, 1, 0):
+        _same(want[s], L2.host(L2.fused(s)))
+    assert moe.moe_route_splits(L2.ctx) == 3
+    assert moe.moe_check(L2.ctx) == moe.MOE_OK
+
+
+@pytest.mark.parametrize("name,T", [("decode", 1), ("mtp", 4)])
+def test_route_ffn_beside_a_kernel_on_another_stream(name, T):
+    """The one-launch step while a kernel of many workgroups runs on another
+    stream (enqueued just before it): outputs finite and bit-identical to the
+    step run alone, no time-out."""
+    steps = [0, 1, 2]
+    L = Layer(name, T, steps)
+    want = {s: L.host(L.fused(s)) for s in steps}
+    big = torch.ones(256 << 20, dtype=torch.float32, device="cuda")  # 1 GiB
+    other = torch.cuda.Stream()
+    for _ in range(3):
+        for s in steps:
+            with torch.cuda.stream(other):
+                big.mul_(1.0000001)
+            got = L.host(L.fused(s))
+            assert np.isfinite(got["y"]).all()
+            _same(want[s], got)
+    torch.cuda.synchronize()
+    assert moe.moe_check(L.ctx) == moe.MOE_OK
