@@ -231,6 +231,10 @@ struct PlanLds {
 };
 
 static_assert(kDecodeMaxT * kRouteKpl * 64 <= 2 * kThreads, "a step's logits are two words per thread");
+// top-k scratch (128 64-bit words per token) in the logits' array, after the logits
+constexpr int kTopkScratch = kDecodeMaxT * kRouteKpl * 64;
+static_assert(kTopkScratch + kDecodeMaxT * 256 <= kDecodeMaxT * kMaxE && kTopkScratch % 4 == 0,
+              "the top-k scratch fits after a step's logits, 16-byte aligned");
 
 // The caller's logits (kRouteLogits), two words per thread, loaded with the
 // workgroup's first round of loads and stored to LDS after it.
@@ -251,12 +255,13 @@ struct LgIn {
     }
 };
 
-// Router workgroups (a launch that computes the logits): the first n_router = E
-// workgroups in dispatch order, wave 0 of workgroup r computing expert row r
-// for every token with the route kernel's row dot (the same bits), so that the
-// router weights stream through as many CUs as there are rows (4 rows per
-// workgroup on 64 CUs finished the rows about 1 us later, 8 on 32 CUs later
-// still); the other waves exit at once.
+// Router workgroups (a launch that computes the logits): the first n_router
+// workgroups in dispatch order, wave w of workgroup r computing expert row
+// r * kRouterRows + w for every token with the route kernel's row dot (the same
+// bits), so that the router weights stream through as many CUs as there are
+// rows; the other waves exit at once.  (With 2 rows per workgroup the decode
+// step took as long; with 4 and 8 the rows came about 1.5 us later and the
+// step 0.8 and 2.2 us later, although the grid was dispatched sooner.)
 // The rows are stored with device scope into every copy of the logits of this
 // launch's workspace half (from the launch count).  They wait for nothing and exit, and
 // every workgroup that waits for the logits has a higher index: workgroups are
@@ -265,11 +270,12 @@ struct LgIn {
 // A router workgroup reads the launch count before the down workgroups can
 // move it: they finish only after the gate/up workgroups have routed, which
 // needs every row.
+constexpr int kRouterRows = 1;  // rows per router workgroup (one per wave)
 __device__ void router_role(const FfnArgs& a, const DGrid& g, int r) {
-    const int lane = threadIdx.x & 63;
-    if (threadIdx.x >= 64) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = r * kRouterRows + wave;
+    if (wave >= kRouterRows || e >= a.E) return;
     const uint32_t count = __hip_atomic_load(a.sync + kSyncCount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int e = r;
     const float* row = a.w_router + (int64_t)e * g.d;
     float* dst = a.hbuf + (int64_t)launch_parity(count, g.n_down) * g.half + g.lg_off + e;
     for (int t = 0; t < a.T; t++) {
@@ -317,7 +323,8 @@ __device__ bool plan_from_logits(const FfnArgs& a, const DGrid& g, int par, int 
     }
     const int t = threadIdx.x >> 6;
     if (t < a.T) {
-        topk_wave<kRouteKpl>(P.lg + t * a.E, a.E, a.k, a.norm, P.ids + t * a.k, P.w + t * a.k);
+        topk_wave<kRouteKpl>(P.lg + t * a.E, a.E, a.k, a.norm, P.ids + t * a.k, P.w + t * a.k,
+                             (uint64_t*)(P.lg + kTopkScratch) + t * 128);
     }
     __syncthreads();
     const int N = a.T * a.k;
@@ -642,21 +649,6 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         if (!plan_from_logits(a, g, par, g.n_gu_wg + R, P, R == 0) && threadIdx.x == 0) L.flag[0] = 0;
         na = min(L.na, na_max);
     }
-    // The arrivals of this launch's gate/up workgroups, read now (they arrive
-    // as they start, long before this) and checked at the end, so that the end
-    // does not wait for a round trip.
-    const uint32_t arrived0 = a.route == kRouteRouter && threadIdx.x == 0
-                                  ? __hip_atomic_load(a.sync + kSyncArrive + par, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT)
-                                  : 0u;
-    // This workgroup's share of the other half back to pending for the next
-    // launch (no one uses that half during this one).
-    {
-        float* nxt = a.hbuf + (int64_t)(par ^ 1) * g.half;
-        const int64_t r0 = (int64_t)R * g.reset_per;
-        for (int j = threadIdx.x; j < g.reset_per; j += kThreads)
-            if (r0 + j < g.half) nxt[r0 + j] = __uint_as_float(kPending);
-    }
 
     // Level 2: this workgroup's W_d tiles of every unit.  Tile p is (unit
     // p / dn_tpr, column group p % dn_tpr); wave w holds tiles w + 8 i.  Each
@@ -693,6 +685,13 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         const uint8_t* tp = p < P ? tile_ptr(p) : nullptr;
         td[i].load(tp ? tp : fallback, lane);
     }
+    // The arrivals of this launch's gate/up workgroups, read now (they arrive
+    // as they start, long before this; the load waits with the tiles') and
+    // checked at the end, so that the end does not wait for a round trip.
+    const uint32_t arrived0 = a.route == kRouteRouter && threadIdx.x == 0
+                                  ? __hip_atomic_load(a.sync + kSyncArrive + par, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                                  : 0u;
     // Token and weight of every hidden row (the shared rows: token t, weight 1).
     // A token counts the plan positions the units cover that are its own: a
     // token with fewer than top_k (the plan dropped an out-of-range id) gets a
@@ -741,10 +740,12 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
     // the compiler hoist work on their loaded values above it, and so wait for
     // the tiles before the poll.
     auto group = [&](const int ua) __attribute__((always_inline)) -> int {
-        const int va = v_begin(ua);
+        const int va = __builtin_amdgcn_readfirstlane(v_begin(ua));
         int ub = ua + 1;
         while (ub < U && v_end(ub) - va <= g.nb_rows) ub++;
-        const int vb = min(v_end(ub - 1), va + g.nb_rows);  // (a valid plan never clips)
+        ub = __builtin_amdgcn_readfirstlane(ub);
+        // (a valid plan never clips)
+        const int vb = __builtin_amdgcn_readfirstlane(min(v_end(ub - 1), va + g.nb_rows));
         // Stage rows [va, vb) straight into LDS with device-scope loads (1 KB
         // per wave instruction, no registers), until no pending word is left.
         // Rows [off[na], T k) belong to no unit (entries the plan dropped) and
@@ -868,6 +869,15 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         for (int w = 0; w < kWaves; w++) y += L.red[w][t][r];
         a.y[(int64_t)t * g.d + 16 * R + r] = L.flag[0] && L.cnt[t] == a.k ? y : __uint_as_float(0x7FC00000u);
     }
+    // This workgroup's share of the other half back to pending for the next
+    // launch (no one uses that half during this one).  Done last: a store loop
+    // before the tile loads made them wait for every earlier load.
+    {
+        float* nxt = a.hbuf + (int64_t)(par ^ 1) * g.half;
+        const int64_t r0 = (int64_t)R * g.reset_per;
+        for (int j = threadIdx.x; j < g.reset_per; j += kThreads)
+            if (r0 + j < g.half) nxt[r0 + j] = __uint_as_float(kPending);
+    }
     // This launch is done with its half: count it (no return needed), once every
     // gate/up workgroup of a launch that routes has arrived.
     if (threadIdx.x == 0) {
@@ -942,7 +952,7 @@ hipError_t launch_k(DGrid g, const FfnArgs& a, hipStream_t s) {
     // Router workgroups exit after one row, so the gate/up and down workgroups
     // that do not fit beside them at first are dispatched a few microseconds
     // in, long before the routing they wait for is complete.
-    g.n_router = a.route == kRouteRouter ? a.E : 0;
+    g.n_router = a.route == kRouteRouter ? (a.E + kRouterRows - 1) / kRouterRows : 0;
     const int room = cap - g.n_down;
     g.n_gu_wg = room > 0 ? std::min(items, room) : std::min(items, 64);
     hipLaunchKernelGGL(kern, dim3(g.n_router + g.n_gu_wg + g.n_down), dim3(kThreads), 0, s, a, g);

@@ -8,13 +8,13 @@
 //   the logits are reproducible bit for bit.
 // route_union (T <= kFusedMaxT): the same logits, then top-k and the union in
 //   one single-workgroup launch (see below).
-// topk: one wave per token.  Each lane keeps its logits as order-preserving
-//   32-bit keys (-0 ranked with +0) and the best key it still has; a round
-//   takes the wave's largest key with one 32-bit DPP/permlane max, then every
-//   lane offers the lowest expert index holding that key and one DPP min picks
-//   the lowest of all (ties to the lower index); k rounds select the experts.
-//   Weights are the softmax over the selected logits (or over all, norm == 0),
-//   in fp32.
+// topk: one wave per token, on order-preserving 32-bit keys (-0 ranked with
+//   +0), ties to the lower index.  Up to 256 experts and top-32: a lower bound
+//   of the k-th largest key (the smallest of 8 group maxima) leaves a few
+//   candidates, which rank themselves by counting; otherwise (or with more
+//   than 64 candidates) k rounds, each a DPP/permlane max of the keys and a
+//   min of the indices holding it.  Weights are the softmax over the selected
+//   logits (or over all, norm == 0), in fp32.
 #include "internal.h"
 #include "route_device.h"
 
@@ -41,9 +41,11 @@ template <int KPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                    int norm, int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
+    __shared__ uint64_t sc[4][128];
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    topk_wave<KPL>(logits + (int64_t)t * E, E, k, norm, ids + (int64_t)t * k, w + (int64_t)t * k);
+    topk_wave<KPL>(logits + (int64_t)t * E, E, k, norm, ids + (int64_t)t * k, w + (int64_t)t * k,
+                   sc[threadIdx.x >> 6]);
 }
 
 struct RouteUnion {
@@ -63,8 +65,10 @@ __device__ void topk_union_wg(const float* logits, const RouteUnion& r) {
     static_assert(kFusedMaxT * 32 <= 128, "union_small holds two entries per lane of one wave");
     __shared__ int32_t s_ids[kFusedMaxT * 32];
     __shared__ float s_w[kFusedMaxT * 32];
+    __shared__ uint64_t sc[4][128];
     const int t = threadIdx.x >> 6;
-    if (t < r.T) topk_wave<KPL>(logits + (int64_t)t * r.E, r.E, r.k, r.norm, s_ids + t * r.k, s_w + t * r.k);
+    if (t < r.T)
+        topk_wave<KPL>(logits + (int64_t)t * r.E, r.E, r.k, r.norm, s_ids + t * r.k, s_w + t * r.k, sc[t]);
     __syncthreads();
     const int N = r.T * r.k;
     if ((int)threadIdx.x < N) {

@@ -60,50 +60,149 @@ __device__ inline float unorder_bits(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-// One wave: top-k of one token's E logits (KPL = ceil(E / 64) keys per lane).
+// Selection on a candidate set, for E <= 256 (KPL <= 4) and k <= 32.  The
+// keys split into 8 groups: key slot m of the lanes of one half-wave.  Every
+// group that holds an expert has a largest key, and the smallest of those
+// maxima, tau, is a lower bound of the k-th largest key as soon as there are
+// at least k such groups (k keys are >= tau).  So every selected key is >= tau,
+// and the top-k of the candidates (keys >= tau) is the top-k of all.  The
+// candidates (usually a small fraction of E) are packed into one slot each
+// of the wave's scratch as 64-bit keys (key, then the complemented expert
+// index, so that equal keys rank the lower index first) and each candidate
+// counts the candidates above it: its rank.  The candidate of rank j goes to
+// lane j.  A wave's LDS accesses complete in order, so no barrier is needed
+// between the writes and the reads of its own scratch.  Returns false (the
+// caller then takes the k rounds below) when the bound does not apply or there
+// are more than 64 candidates.
 template <int KPL>
-__device__ inline void topk_wave(const float* l, int E, int k, int norm, int32_t* ids, float* w) {
+__device__ inline bool topk_candidates(const uint32_t (&val)[KPL], uint32_t avail, int E, int k, int lane,
+                                       uint64_t* sc, float& my_logit, int& my_id) {
+    if constexpr (KPL > 4) {
+        return false;
+    } else {
+        if (k > 32) return false;
+        const int half = lane >> 5;
+        uint32_t gm[KPL];
+#pragma unroll
+        for (int m = 0; m < KPL; m++) gm[m] = ((avail >> m) & 1u) ? val[m] : 0u;
+        // the groups' maxima: the max steps of seg_sum<32>, the slots interleaved
+#pragma unroll
+        for (int m = 0; m < KPL; m++) gm[m] = max(gm[m], (uint32_t)__builtin_amdgcn_update_dpp(0u, gm[m], 0xB1, 0xF, 0xF, false));
+#pragma unroll
+        for (int m = 0; m < KPL; m++) gm[m] = max(gm[m], (uint32_t)__builtin_amdgcn_update_dpp(0u, gm[m], 0x4E, 0xF, 0xF, false));
+#pragma unroll
+        for (int m = 0; m < KPL; m++) gm[m] = max(gm[m], (uint32_t)__builtin_amdgcn_update_dpp(0u, gm[m], 0x141, 0xF, 0xF, false));
+#pragma unroll
+        for (int m = 0; m < KPL; m++) gm[m] = max(gm[m], (uint32_t)__builtin_amdgcn_update_dpp(0u, gm[m], 0x140, 0xF, 0xF, false));
+#pragma unroll
+        for (int m = 0; m < KPL; m++) {
+            const auto r = __builtin_amdgcn_permlane16_swap(gm[m], gm[m], false, false);
+            gm[m] = max((uint32_t)r[0], (uint32_t)r[1]);
+        }
+        // tau over the groups that hold an expert (group (m, h) holds 64 m + 32 h < E)
+        uint32_t tmin = 0xFFFFFFFFu;
+#pragma unroll
+        for (int m = 0; m < KPL; m++) tmin = 64 * m + 32 * half < E ? min(tmin, gm[m]) : tmin;
+        const auto r = __builtin_amdgcn_permlane32_swap(tmin, tmin, false, false);
+        tmin = min((uint32_t)r[0], (uint32_t)r[1]);
+        const int n_groups = min(2 * KPL, (E + 31) / 32);
+        const uint32_t tau = n_groups >= k ? tmin : 0u;  // too few groups: every expert is a candidate
+        uint64_t B[KPL];
+        int base[KPL];
+        int C = 0;
+#pragma unroll
+        for (int m = 0; m < KPL; m++) {
+            B[m] = __ballot(((avail >> m) & 1u) && val[m] >= tau);
+            base[m] = C;
+            C += __popcll(B[m]);
+        }
+        if (C > 64) return false;
+        // slots [0, C): the candidates; [C, 64): zero (above no key); [64, 128): a
+        // place for the others' writes
+        if (lane >= C) sc[lane] = 0ull;
+#pragma unroll
+        for (int m = 0; m < KPL; m++) {
+            const bool c = (B[m] >> lane) & 1u;
+            const int pos = c ? base[m] + lanes_below(B[m]) : 64 + lane;
+            sc[pos] = ((uint64_t)val[m] << 32) | (uint32_t)~(uint32_t)(lane + 64 * m);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint64_t mine = sc[min(lane, C - 1)];
+        int rank = 0;
+        for (int c0 = 0; c0 < C; c0 += 8) {
+            uint64_t o[8];
+#pragma unroll
+            for (int q = 0; q < 8; q++) o[q] = sc[c0 + q];  // (c0 <= 56: slots below 64)
+#pragma unroll
+            for (int q = 0; q < 8; q++) rank += o[q] > mine ? 1 : 0;
+        }
+        // the candidate of rank j to lane j (the others to lane 63, unused: k <= 32)
+        const int to = 4 * (lane < C && rank < k ? rank : 63);
+        const uint64_t sel = ((uint64_t)(uint32_t)__builtin_amdgcn_ds_permute(to, (int)(mine >> 32)) << 32) |
+                             (uint32_t)__builtin_amdgcn_ds_permute(to, (int)(uint32_t)mine);
+        if (lane < k) {
+            my_id = (int)~(uint32_t)sel;
+            my_logit = unorder_bits((uint32_t)(sel >> 32));
+        }
+        return true;
+    }
+}
+
+// One wave: top-k of one token's E logits (KPL = ceil(E / 64) keys per lane).
+// `sc`: 128 64-bit words of LDS for this wave (or null: the rounds only).
+template <int KPL>
+__device__ inline void topk_wave(const float* l, int E, int k, int norm, int32_t* ids, float* w,
+                                 uint64_t* sc = nullptr) {
     const int lane = threadIdx.x & 63;
     // Expert e = lane + 64 m is value val[m] (order-preserving bits) while bit m
-    // of avail is set.  Each lane keeps the best of its available values.  A
-    // round takes the wave's largest value (one 32-bit DPP max); every lane
-    // offers its lowest expert index holding it, and one DPP min picks the
-    // lowest of all (ties to the lower index); only the winning lane then
-    // recomputes its best.
+    // of avail is set.
     uint32_t val[KPL];
     uint32_t avail = 0;
+    float lv[KPL];
+#pragma unroll
+    for (int m = 0; m < KPL; m++) lv[m] = l[min(lane + 64 * m, E - 1)];  // all loads first
 #pragma unroll
     for (int m = 0; m < KPL; m++) {
         const int e = lane + 64 * m;
-        val[m] = e < E ? order_bits(l[e]) : 0u;
+        val[m] = e < E ? order_bits(lv[m]) : 0u;
         avail |= (e < E ? 1u : 0u) << m;
     }
-    auto lane_best = [&]() __attribute__((always_inline)) {
-        uint32_t b = 0;
-#pragma unroll
-        for (int m = 0; m < KPL; m++) b = ((avail >> m) & 1u) ? max(b, val[m]) : b;
-        return b;
-    };
-    uint32_t best = lane_best();
     float my_logit = 0.f;  // lane j keeps the j-th selected logit
     int my_id = 0;
-    for (int j = 0; j < k; j++) {
-        const uint32_t top = wave_max_u32(best);
-        uint32_t cand = 0xFFFFFFFFu;  // 64 m + lane of this lane's lowest m holding top
+    if (!sc || !topk_candidates<KPL>(val, avail, E, k, lane, sc, my_logit, my_id)) {
+        // k rounds.  Each lane keeps the best of its available values.  A round
+        // takes the wave's largest value (one 32-bit DPP max); every lane offers
+        // its lowest expert index holding it, and one DPP min picks the lowest
+        // of all (ties to the lower index); only the winning lane then
+        // recomputes its best.
+        auto lane_best = [&]() __attribute__((always_inline)) {
+            uint32_t b = 0;
 #pragma unroll
-        for (int m = KPL - 1; m >= 0; m--)
-            cand = (((avail >> m) & 1u) && val[m] == top) ? (uint32_t)(64 * m + lane) : cand;
-        const uint32_t sel = wave_min_u32(cand);
-        if (sel != 0xFFFFFFFFu && (int)(sel & 63u) == lane) {  // (some key is always left: k <= E)
-            avail &= ~(1u << (sel >> 6));
-            best = lane_best();
-        }
-        if (lane == j) {
-            my_id = (int)sel;
-            my_logit = unorder_bits(top);
+            for (int m = 0; m < KPL; m++) b = ((avail >> m) & 1u) ? max(b, val[m]) : b;
+            return b;
+        };
+        uint32_t best = lane_best();
+        for (int j = 0; j < k; j++) {
+            const uint32_t top = wave_max_u32(best);
+            uint32_t cand = 0xFFFFFFFFu;  // 64 m + lane of this lane's lowest m holding top
+#pragma unroll
+            for (int m = KPL - 1; m >= 0; m--)
+                cand = (((avail >> m) & 1u) && val[m] == top) ? (uint32_t)(64 * m + lane) : cand;
+            const uint32_t sel = wave_min_u32(cand);
+            if (sel != 0xFFFFFFFFu && (int)(sel & 63u) == lane) {  // (some key is always left: k <= E)
+                avail &= ~(1u << (sel >> 6));
+                best = lane_best();
+            }
+            if (lane == j) {
+                my_id = (int)sel;
+                my_logit = unorder_bits(top);
+            }
         }
     }
-    const float lmax = __shfl(my_logit, 0, 64);
+    // the largest selected logit (lane 0), then the softmax in a fixed order
+    const float lmax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(my_logit)));
     float z;
     if (norm) {
         float ex = lane < k ? expf(my_logit - lmax) : 0.f;

@@ -130,12 +130,19 @@ def test_route_from_router_weights(name, T):
 
 
 @pytest.mark.parametrize("E,k", [(8, 2), (256, 8), (1024, 32), (100, 7)])
-@pytest.mark.parametrize("kind", ["ties", "equal", "signed_zero", "normal", "one_ulp"])
+@pytest.mark.parametrize("kind", ["ties", "equal", "signed_zero", "normal", "one_ulp", "c64", "c65"])
 @pytest.mark.parametrize("norm", [1, 0])
 def test_route_logits_in_bit_exact(E, k, kind, norm):
+    """Top-k on edge cases.  c64 / c65: 64 or 65 equal largest logits, one in
+    every group of 32 keys, so that at 256 experts the candidate selection takes
+    exactly 64 candidates, or falls back to the k rounds at 65."""
     T = 37  # ragged against the 4 tokens per workgroup
     g = np.random.default_rng(E * 31 + k)
-    if kind == "ties":
+    if kind in ("c64", "c65"):
+        n = min(int(kind[1:]), E)
+        lg = (-1.0 - g.uniform(0, 1, size=(T, E))).astype(np.float32)
+        lg[:, (np.arange(n) * E) // n] = 1.0
+    elif kind == "ties":
         lg = g.integers(-2, 3, size=(T, E)).astype(np.float32)
     elif kind == "equal":
         lg = np.full((T, E), 1.25, np.float32)
