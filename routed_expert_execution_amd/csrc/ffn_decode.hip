@@ -532,7 +532,28 @@ __device__ __forceinline__ void gate_up_role(const FfnArgs& a, const DGrid& g, i
             for (int gi = 0; gi < TG; gi++) xv[gi] = L.x[gi] + cb * kQK;
             const Tile<QT> pair[2] = {tg[q], tu[q]};
             float dd[2][TG];
-            tile_dots<QT, PREC, 2, TG, TG == 1 ? 4 : TG == 2 ? 2 : 1, TG == 1 ? 8 : 4>(pair, xv, dd);
+            // only the bucket's tokens (most buckets of a few tokens hold one)
+            if (TG > 1 && nb == 1) {
+                const float* x1[1] = {xv[0]};
+                float d1[2][1];
+                tile_dots<QT, PREC, 2, 1, 4, 8>(pair, x1, d1);
+#pragma unroll
+                for (int gi = 0; gi < TG; gi++) {
+                    dd[0][gi] = gi == 0 ? d1[0][0] : 0.f;
+                    dd[1][gi] = gi == 0 ? d1[1][0] : 0.f;
+                }
+            } else if (TG > 2 && nb == 2) {
+                const float* x2[2] = {xv[0], xv[1]};
+                float d2[2][2];
+                tile_dots<QT, PREC, 2, 2, 2, 4>(pair, x2, d2);
+#pragma unroll
+                for (int gi = 0; gi < TG; gi++) {
+                    dd[0][gi] = gi < 2 ? d2[0][gi < 2 ? gi : 0] : 0.f;
+                    dd[1][gi] = gi < 2 ? d2[1][gi < 2 ? gi : 0] : 0.f;
+                }
+            } else {
+                tile_dots<QT, PREC, 2, TG, TG == 1 ? 4 : TG == 2 ? 2 : 1, TG == 1 ? 8 : 4>(pair, xv, dd);
+            }
 #pragma unroll
             for (int r = 0; r < RG; r++)
 #pragma unroll
@@ -545,6 +566,7 @@ __device__ __forceinline__ void gate_up_role(const FfnArgs& a, const DGrid& g, i
         for (int r = 0; r < RG; r++)
 #pragma unroll
             for (int gi = 0; gi < TG; gi++) {
+                if (gi >= nb) break;  // (rows of tokens the bucket does not have are not read)
                 const float gs = cross_row_sum(accg[r][gi]), us = cross_row_sum(accu[r][gi]);
                 if (jb == 0) {
                     L.red[0][wave][r * TG + gi][n] = gs;
@@ -589,6 +611,7 @@ struct DownLds {
     int flag[4];
     int cnt[kDecodeMaxT];             // plan positions the units cover, per token
     int64_t uoff[kMaxUnits + 3];      // unit -> payload offset in the pool (-1 absent, -2 shared)
+    uint8_t rdone[kMaxRows];          // hidden row -> every word of it staged (or a row no unit has)
     alignas(16) float red[kWaves][kDecodeMaxT][16];
     alignas(16) float zero[kQK];      // a zero block of activations (rows a bucket does not have)
     int ids[kMaxEnt];                 // routing inside the launch: selected experts by entry
@@ -698,6 +721,7 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
     // NaN row, as the chunk path's combine gives it.
     if (threadIdx.x < kMaxRows) {
         const int v = threadIdx.x;
+        L.rdone[v] = v >= L.off[na] && v < n_ent;  // rows [off[na], T k): entries the plan dropped
         if (v < n_ent) {
             const int ent = L.ent[v];
             L.tok[v] = ent / a.k;
@@ -748,25 +772,73 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         const int vb = __builtin_amdgcn_readfirstlane(min(v_end(ub - 1), va + g.nb_rows));
         // Stage rows [va, vb) straight into LDS with device-scope loads (1 KB
         // per wave instruction, no registers), until no pending word is left.
-        // Rows [off[na], T k) belong to no unit (entries the plan dropped) and
-        // are never written: the pending check skips them.
-        const int n16 = max(vb - va, 0) * g.f / 4;  // 16-byte pieces
+        // Wave w takes rows w, w + 8, ... of the group: it stages a row until
+        // one read finds every word of it written (the words are final then)
+        // and not again, so that later reads carry only the rows still
+        // pending.  (With rows not a whole number of 1 KB instructions, or one
+        // token, whose few rows come in together, every row is staged each
+        // time: one token's step was 0.3 us slower staging by row.)  Rows no
+        // unit has (entries the plan dropped) are never written and never
+        // checked.
+        const int nrows = max(vb - va, 0);
+        const int n16 = nrows * g.f / 4;  // 16-byte pieces
         const int n_ins = (n16 + 63) / 64;
+        const int ppr = g.f / 4;          // pieces per row
+        const bool by_row = TG > 1 && g.f % 256 == 0;
+        const int ipr = g.f / 256;        // instructions per row (by_row)
         const float* src = hhalf + (int64_t)va * g.f;
-        const int gap0 = (max(min(L.off[na], n_ent), va) - va) * g.f / 4;  // pieces [gap0, gap1) unused
+        const int gap0 = (max(min(L.off[na], n_ent), va) - va) * g.f / 4;  // pieces [gap0, gap1): no unit's
         const int gap1 = (max(n_ent, va) - va) * g.f / 4;
+        // Tiles beyond the registers (more units than DPW * 8 / dn_tpr): this
+        // wave's tiles p = p0, p0 + 8, ... below pe, two loads in flight, the
+        // first issued before the wait.
+        const int pe = ub * g.dn_tpr;
+        int p0 = kWaves * DPW + wave;
+        if (p0 < ua * g.dn_tpr) p0 += (ua * g.dn_tpr - p0 + kWaves - 1) / kWaves * kWaves;
+        p0 = __builtin_amdgcn_readfirstlane(p0);
+        auto beyond_ptr = [&](int p) __attribute__((always_inline)) -> const uint8_t* {
+            const uint8_t* tp = p < pe ? tile_ptr(p) : nullptr;
+            return tp ? tp : fallback;
+        };
+        Tile<QT> ta[1], tb[1];
+        if (TG > 1 && p0 < pe) ta[0].load(beyond_ptr(p0), lane);  // (one token: after the wait)
         for (;;) {
-            for (int j = wave; j < n_ins; j += kWaves)
-                __builtin_amdgcn_global_load_lds(src + 4 * min(j * 64 + lane, n16 - 1),
-                                                  (__attribute__((address_space(3))) void*)(L.hs + j * 256), 16, 0,
-                                                  kDeviceScope);
+            if (by_row) {
+                for (int r = wave; r < nrows; r += kWaves) {
+                    if (__builtin_amdgcn_readfirstlane(L.rdone[va + r])) continue;
+                    for (int q = 0; q < ipr; q++) {
+                        const int j = r * ipr + q;
+                        __builtin_amdgcn_global_load_lds(src + 4 * (j * 64 + lane),
+                                                          (__attribute__((address_space(3))) void*)(L.hs + j * 256),
+                                                          16, 0, kDeviceScope);
+                    }
+                }
+            } else {
+                for (int j = wave; j < n_ins; j += kWaves)
+                    __builtin_amdgcn_global_load_lds(src + 4 * min(j * 64 + lane, n16 - 1),
+                                                      (__attribute__((address_space(3))) void*)(L.hs + j * 256), 16,
+                                                      0, kDeviceScope);
+            }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             int pend = 0;
-            for (int i = threadIdx.x; i < n16; i += kThreads) {
-                const uint4 b = *(const uint4*)(L.hs + 4 * i);
-                const bool used = i < gap0 || i >= gap1;
-                pend |= used && ((b.x == kPending) | (b.y == kPending) | (b.z == kPending) | (b.w == kPending));
+            if (by_row) {
+                for (int r = wave; r < nrows; r += kWaves) {
+                    if (__builtin_amdgcn_readfirstlane(L.rdone[va + r])) continue;
+                    bool pr = false;
+                    for (int q = lane; q < ppr; q += 64) {
+                        const uint4 b = *(const uint4*)(L.hs + 4 * (r * ppr + q));
+                        pr |= (b.x == kPending) | (b.y == kPending) | (b.z == kPending) | (b.w == kPending);
+                    }
+                    if (__ballot(pr)) pend = 1;
+                    else if (lane == 0) L.rdone[va + r] = 1;
+                }
+            } else {
+                for (int i = threadIdx.x; i < n16; i += kThreads) {
+                    const uint4 b = *(const uint4*)(L.hs + 4 * i);
+                    const bool used = i < gap0 || i >= gap1;
+                    pend |= used && ((b.x == kPending) | (b.y == kPending) | (b.z == kPending) | (b.w == kPending));
+                }
             }
             if (!__syncthreads_or(pend) && a.wait_ticks >= 0) break;
             const int expired = threadIdx.x == 0 && (a.wait_ticks < 0 || (int64_t)(wall_clock64() - t0) > a.wait_ticks);
@@ -833,12 +905,9 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
                 }
             }
         }
-        // tiles beyond the registers (more units than DPW * 8 / dn_tpr)
-        for (int p = kWaves * DPW + wave; p < ub * g.dn_tpr; p += kWaves) {
-            if (p < ua * g.dn_tpr) continue;
-            const uint8_t* tp = tile_ptr(p);
-            Tile<QT> t[1];
-            t[0].load(tp ? tp : fallback, lane);
+        // the tiles beyond the registers, in order (a non-resident unit's
+        // tiles read the fallback; its rows are NaN through h)
+        auto beyond = [&](const Tile<QT> (&t)[1], int p) __attribute__((always_inline)) {
             const int u = p / g.dn_tpr, c = p - u * g.dn_tpr;
             const int v0 = max(v_begin(u), va), v1 = min(v_end(u), vb);
             for (int v = v0; v < v1; v++) {
@@ -850,6 +919,16 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
 #pragma unroll
                 for (int q = 0; q < TG; q++) acc[q] += tk == q ? dw : 0.f;
             }
+        };
+        if (TG == 1 && p0 < pe) ta[0].load(beyond_ptr(p0), lane);
+        for (int p = p0; p < pe;) {
+            if (p + kWaves < pe) tb[0].load(beyond_ptr(p + kWaves), lane);
+            beyond(ta, p);
+            p += kWaves;
+            if (p >= pe) break;
+            if (p + kWaves < pe) ta[0].load(beyond_ptr(p + kWaves), lane);
+            beyond(tb, p);
+            p += kWaves;
         }
         __syncthreads();
         return ub;
@@ -904,9 +983,11 @@ static_assert(offsetof(DownLds, hs) % 16 == 0 && offsetof(DownLds, zero) % 16 ==
 
 constexpr int kLdsBytes = sizeof(DownLds) > sizeof(GuLds<kDecodeMaxT, 2>) ? sizeof(DownLds) : sizeof(GuLds<kDecodeMaxT, 2>);
 
-// Hidden-unit groups of 16 per gate/up item: 2 for steps of several tokens
-// (fewer, larger items: one round of workgroups holds the step).
-template <int QT, int TG> constexpr int rows_per_item() { return TG > 1 ? 2 : 1; }
+// Hidden-unit groups of 16 per gate/up item.  (Two for steps of several tokens,
+// so that one round of workgroups held the step, left 32 tile pairs per item,
+// 4 per wave in registers, and spilled: the four-token Q4_0 step's gate/up
+// phase took 8 us longer than with one group and two rounds.)
+template <int QT, int TG> constexpr int rows_per_item() { return 1; }
 
 template <int QT, int PREC, int TG, int PPW, int DPW>
 __global__ __launch_bounds__(kThreads, 4) void ffn_decode_kernel(FfnArgs a, DGrid g) {
