@@ -434,7 +434,12 @@ def run_stack(args, torch, moe, synth) -> int:
     back, its misses staged from pinned host memory on a side stream, and its
     experts run, one token at a time."""
     wl = dict(synth.workload("stack40"), name="stack")
+    if args.slots:
+        wl["n_slots"] = args.slots
     L, E, k, d, f, n_slots = wl["n_layers"], wl["E"], wl["k"], wl["d"], wl["f"], wl["n_slots"]
+    if args.prefetch and args.staging != "native":
+        print("--prefetch needs --staging native (moe_prefetch_next follows moe_route_pull)", file=sys.stderr)
+        return 2
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     n_tok = args.warmup + args.steps
@@ -453,9 +458,13 @@ def run_stack(args, torch, moe, synth) -> int:
         ctx.cfg, synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True))).to(dev)
     lg = torch.stack([torch.from_numpy(synth.markov_logits(wl["seed"], l, n_tok, E, k, wl["p_repeat"]))
                       for l in range(L)]).to(dev)  # [L, tokens, E]
-    xs = torch.stack([torch.stack([torch.from_numpy(synth.activations(wl["seed"], 1, d, "bf16", t, l)
-                                                    .view(np.int16)).view(torch.bfloat16) for l in range(L)])
-                      for t in range(n_tok)]).to(dev)  # [tokens, L, 1, d]
+    # layer 0's input per token (and, with --fresh-inputs, every layer's);
+    # otherwise x_{l+1} = bf16(y_l / rms(y_l)), eps 1e-6, no weight
+    n_in = L if args.fresh_inputs else 1
+    xs = torch.stack([torch.stack([torch.from_numpy(
+        (synth.activations(wl["seed"], 1, d, "bf16", t, l) if args.fresh_inputs
+         else synth.activations(wl["seed"], 1, d, "bf16", t)).view(np.int16)).view(torch.bfloat16)
+        for l in range(n_in)]) for t in range(n_tok)]).to(dev)  # [tokens, n_in, 1, d]
     t_gen = time.perf_counter() - t_gen
     ids = torch.empty(1, k, dtype=torch.int32, device=dev)
     w = torch.empty(1, k, dtype=torch.float32, device=dev)
@@ -469,10 +478,11 @@ def run_stack(args, torch, moe, synth) -> int:
     pull_ev = []  # (event before the pull, misses): the pull ends where the FFN's first event is
     n_fill = 0
     unique = 0
-    last_route = [None] * L  # per layer: (ids, weights) of its previous token
+    pred_n = [0, 0]  # candidates processed, copies queued by moe_prefetch_next
 
     def token(t, timed):
         nonlocal unique, n_fill
+        x = xs[t, 0]
         for l in range(L):
             ev = timed and l % 8 == 0  # kernel times on every 8th layer
             if args.staging == "native":  # route, mirror, host map and pull in one library call
@@ -501,38 +511,38 @@ def run_stack(args, torch, moe, synth) -> int:
                         moe.moe_slot_fill(ctx, l, int(e), int(sl), packs[l % n_alias][int(e)],
                                           stream=sides[n_fill % len(sides)])
                         n_fill += 1
-            if args.prefetch:
-                last_route[l] = (ids.cpu().numpy()[0], w.cpu().numpy()[0])
-                nl = (l + 1) % L  # the next layer to run (layer 0 of the next token after the last)
-                if last_route[nl] is not None:
-                    pid, pw = last_route[nl]
-                    pred = [int(e) for e, ww in sorted(zip(pid, pw), key=lambda q: -q[1]) if ww >= 0.20]
-                    if pred:
-                        ps, fill = moe.moe_slot_prefetch(ctx, nl, pred, args.prefetch * pb)
-                        for e, sl, fl in zip(pred, ps, fill):
-                            if fl:
-                                moe.moe_slot_fill(ctx, nl, e, int(sl), packs[nl % n_alias][e],
-                                                  stream=sides[n_fill % len(sides)])
-                                n_fill += 1
+            if args.prefetch:  # the next layer's predictions, copied on a side stream while this layer runs
+                nl = (l + 1) % L  # (layer 0 of the next token after the last)
+                ex_p, fl_p = moe.moe_prefetch_next(ctx, l, tables[nl % n_alias], args.prefetch * pb,
+                                                   min_weight=args.prefetch_min_weight,
+                                                   transitions=not args.no_transitions, stream=side)
+                pred_n[0] += len(ex_p)
+                pred_n[1] += int(fl_p.sum())
             if ev:
-                # the FFN waits for the layer's side-stream fills anyway; waiting
-                # before the first event keeps the copies out of the kernel's time
-                if args.staging not in ("pull", "native") or args.prefetch:
+                # the FFN waits for fills it needs anyway; waiting for the side
+                # streams before the first event keeps their copies out of the
+                # kernel's time (this layer's own misses; prefetches of the next
+                # layer overlap it otherwise)
+                if args.staging not in ("pull", "native"):
                     for sd in sides:
                         stream.wait_stream(sd)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            moe.moe_expert_ffn(ctx, l, xs[t, l], plan, w, y, shared_payload=shared)
+            moe.moe_expert_ffn(ctx, l, xs[t, l] if args.fresh_inputs else x, plan, w, y, shared_payload=shared)
             if ev:
                 e1.record(stream)
                 ffn_ev.append((e0, e1))
                 unique += n
             moe.moe_slot_release(ctx, l)
+            if not args.fresh_inputs:
+                x = torch.nn.functional.rms_norm(y, (d,), eps=1e-6).to(torch.bfloat16)
 
     for t in range(args.warmup):
         token(t, False)
     torch.cuda.synchronize()
     st0 = moe.moe_stats(ctx)
+    pf0 = moe.moe_prefetch_stats(ctx)
+    pred0 = list(pred_n)
     wall0 = time.perf_counter()
     for t in range(args.warmup, n_tok):
         token(t, True)
@@ -543,7 +553,10 @@ def run_stack(args, torch, moe, synth) -> int:
     if st != moe.MOE_OK:
         print(f"device error word set: status {st}", file=sys.stderr)
         return 1
-    pf = moe.moe_prefetch_stats(ctx)
+    pf1 = moe.moe_prefetch_stats(ctx)
+    pf = {kk: pf1[kk] - pf0[kk] for kk in pf1}  # over the timed tokens
+    pf["candidates"] = pred_n[0] - pred0[0]
+    pf["copies_queued"] = pred_n[1] - pred0[1]
     hits, misses = st1["hits"] - st0["hits"], st1["misses"] - st0["misses"]
     staged = st1["bytes_staged"] - st0["bytes_staged"]
     ffn = np.array([a.elapsed_time(b) for a, b in ffn_ev]) * 1e3
@@ -576,8 +589,13 @@ def run_stack(args, torch, moe, synth) -> int:
                          f"Q8_0, 1 token/step, one {n_slots}-slot LRU pool shared by the layers, Markov routes "
                          f"(p_repeat {wl['p_repeat']}), misses staged from pinned host memory "
                          f"after each layer's plan readback; payload sets alias mod {n_alias} layers"
-                         + (f"; lookahead prefetch of up to {args.prefetch} predicted payloads per layer"
-                            if args.prefetch else "")
+                         + ("; fresh synthetic input per layer" if args.fresh_inputs
+                            else "; layers chained: x_{l+1} = bf16(y_l / rms(y_l)), eps 1e-6")
+                         + (f"; moe_prefetch_next after each moe_route_pull: up to {args.prefetch} payloads of the "
+                            f"next layer's predicted experts (previous token's weight >= "
+                            f"{args.prefetch_min_weight}" + ("" if args.no_transitions
+                                                             else ", then layer-to-layer transition scores")
+                            + ") copied on a side stream while the layer computes" if args.prefetch else "")
                          + (f"; copies alternate over {args.fill_streams} side streams"
                             if args.fill_streams > 1 and args.staging != "pull" else "")
                          + {"native": "; one moe_route_pull per layer: routing, expert readback through pinned "
@@ -609,8 +627,11 @@ def run_stack(args, torch, moe, synth) -> int:
             "layer_steps_timed": len(ffn_ev),
             "pull": pull,
             "setup_pack_s": t_gen,
-            "prefetch": ({"cap_payloads_per_layer": args.prefetch, "threshold": 0.20, **pf} if args.prefetch
-                         else None),
+            "prefetch": ({"cap_payloads_per_layer": args.prefetch, "min_weight": args.prefetch_min_weight,
+                          "transitions": not args.no_transitions, **pf,
+                          "note": "fills/useful/wasted/bytes over the timed tokens (useful: a later demand map "
+                                  "found it; wasted: evicted unused)"} if args.prefetch else None),
+            "n_slots": n_slots,
             "pages_context": "end-to-end 52.03 tok/s (best layer split) and 14.66 tok/s (exact RAM prefetch) "
                              "on an RTX 3080 PC, a different model and machine",
         },
@@ -632,8 +653,18 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode", choices=["decode", "mtp", "prefill", "stack", "replay"])
     ap.add_argument("--prefetch", type=int, default=0, metavar="N",
-                    help="stack: after each layer's demand fills, prefetch the next layer's predicted experts "
-                         "(its previous token's experts with routing weight >= 0.20), at most N payloads")
+                    help="stack: after each layer's moe_route_pull, moe_prefetch_next stages up to N payloads "
+                         "of the next layer's predicted experts on a side stream while the layer computes")
+    ap.add_argument("--prefetch-min-weight", type=float, default=0.20, metavar="W",
+                    help="stack: prediction threshold (the previous token's experts of the next layer with "
+                         "routing weight >= W; transition scores >= W)")
+    ap.add_argument("--no-transitions", action="store_true",
+                    help="stack: predict from the previous token only (no layer-to-layer transition counts)")
+    ap.add_argument("--slots", type=int, default=0, metavar="S",
+                    help="stack: slots in the pool (default: the workload's 1,536)")
+    ap.add_argument("--fresh-inputs", action="store_true",
+                    help="stack: a fresh synthetic input per layer instead of the chained x_{l+1} = "
+                         "bf16(y_l / rms(y_l))")
     ap.add_argument("--fill-streams", type=int, default=2, metavar="S",
                     help="stack: side streams the misses' copies alternate over")
     ap.add_argument("--no-big-buckets", action="store_true",

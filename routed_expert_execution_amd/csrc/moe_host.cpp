@@ -49,9 +49,19 @@ struct moe_ctx {
     uint64_t clock = 0;
     uint64_t stats[5] = {0, 0, 0, 0, 0};
     uint64_t pstats[4] = {0, 0, 0, 0};  // prefetch fills, useful, wasted, bytes
+    // lookahead prediction: moe_route_pull records each layer's last routing
+    // and counts, per pair of consecutive layers of one step, which expert of
+    // the second followed which of the first; moe_prefetch_next reads them
+    std::vector<int32_t> last_ids;  // [L][4 * top_k]
+    std::vector<float> last_w;      // [L][4 * top_k]
+    std::vector<int32_t> last_n;    // [L] entries recorded (T * top_k; 0: none yet)
+    std::vector<uint32_t> trans;    // [L - 1][E][E] (allocated by the first moe_route_pull)
+    std::vector<uint64_t> trans_row;  // [L - 1][E] row sums
+    int32_t prev_pull_layer = -1;
 
     // ordering
-    int32_t* hmirror = nullptr;       // pinned [1 + E]: n_active and experts of the last moe_route_pull
+    int32_t* hmirror = nullptr;       // pinned [1 + E + 2 * 4 * top_k]: n_active, experts, ids and
+                                      // weights of the last moe_route_pull
     int32_t* hmirror_dev = nullptr;   // the same memory as kernels address it
     hipEvent_t route_ev = nullptr;    // moe_route_pull: the routing is done
     hipStream_t aux = nullptr;        // prefill: the 64-token tile chain beside the caller's stream
@@ -409,7 +419,9 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         if (hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff, cfg->n_experts)) != hipSuccess)
             return cleanup(MOE_EHIP);
         if (hipEventCreateWithFlags(&c->release_ev, hipEventDisableTiming) != hipSuccess) return cleanup(MOE_EHIP);
-        if (hipHostMalloc((void**)&c->hmirror, sizeof(int32_t) * (size_t)(cfg->n_experts + 1), hipHostMallocDefault) !=
+        if (hipHostMalloc((void**)&c->hmirror,
+                          sizeof(int32_t) * (size_t)(cfg->n_experts + 1 + 2 * moe::kFusedMaxT * cfg->top_k),
+                          hipHostMallocDefault) !=
                 hipSuccess ||
             hipEventCreateWithFlags(&c->route_ev, hipEventDisableTiming) != hipSuccess)
             return cleanup(MOE_EHIP);
@@ -495,6 +507,45 @@ moe_status moe_route_union(moe_ctx* c, const void* x, int32_t x_dtype, const flo
     return MOE_OK;
 }
 
+// The routing of the moe_route_pull just done (ids and weights from the pinned
+// mirror) as this layer's last, and, when the previous call routed the layer
+// before with as many tokens (the same step), one count per (token, earlier
+// expert, expert) in that pair of layers' transition table.
+static void record_routing(moe_ctx* c, int32_t layer, int T) {
+    const moe_config& cf = c->cfg;
+    const int E = cf.n_experts, k = cf.top_k, N = T * k, stride = moe::kFusedMaxT * k;
+    if (c->last_n.empty()) {
+        c->last_ids.assign((size_t)cf.n_layers * stride, 0);
+        c->last_w.assign((size_t)cf.n_layers * stride, 0.f);
+        c->last_n.assign(cf.n_layers, 0);
+        if (cf.n_layers > 1) {
+            c->trans.assign((size_t)(cf.n_layers - 1) * E * E, 0u);
+            c->trans_row.assign((size_t)(cf.n_layers - 1) * E, 0u);
+        }
+    }
+    const int32_t* ids = c->hmirror + 1 + E;
+    const float* w = (const float*)(ids + N);
+    int32_t* li = &c->last_ids[(size_t)layer * stride];
+    float* lw = &c->last_w[(size_t)layer * stride];
+    for (int i = 0; i < N; i++) {
+        li[i] = std::min(std::max(ids[i], 0), E - 1);
+        lw[i] = w[i];
+    }
+    c->last_n[layer] = N;
+    if (layer > 0 && c->prev_pull_layer == layer - 1 && c->last_n[layer - 1] == N) {
+        const int32_t* pi = &c->last_ids[(size_t)(layer - 1) * stride];
+        uint32_t* tr = &c->trans[(size_t)(layer - 1) * E * E];
+        uint64_t* rs = &c->trans_row[(size_t)(layer - 1) * E];
+        for (int t = 0; t < T; t++)
+            for (int a = 0; a < k; a++)
+                for (int b = 0; b < k; b++) {
+                    tr[(size_t)pi[t * k + a] * E + li[t * k + b]]++;
+                    rs[pi[t * k + a]]++;
+                }
+    }
+    c->prev_pull_layer = layer;
+}
+
 moe_status moe_route_pull(moe_ctx* c, int32_t layer, const void* x, int32_t x_dtype, const float* w_router,
                           const float* logits_in, int64_t T, int32_t* topk_ids, float* topk_w, float* logits_out,
                           const moe_plan* plan, const void* const* payloads, int32_t* n_out, int32_t* experts_out,
@@ -527,6 +578,7 @@ moe_status moe_route_pull(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     if (n < 0 || n > cf.n_experts) return fail(c, MOE_EHIP, "moe_route_pull: routing returned %d experts", n);
     std::memcpy(experts_out, c->hmirror + 1, sizeof(int32_t) * (size_t)n);
     *n_out = n;
+    record_routing(c, layer, (int)T);
     return moe_slot_pull(c, layer, experts_out, n, payloads, slots_out, miss_out, stream);
 }
 
@@ -594,6 +646,10 @@ moe_status moe_slot_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32
     return MOE_OK;
 }
 
+// The mapping of moe_slot_prefetch (arguments already checked).
+static void prefetch_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int64_t max_bytes,
+                         int32_t* slots_out, uint8_t* fill_out, int32_t* n_done);
+
 moe_status moe_slot_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int64_t max_bytes,
                              int32_t* slots_out, uint8_t* fill_out, int32_t* n_done) {
     if (!c) return MOE_EINVAL;
@@ -607,6 +663,13 @@ moe_status moe_slot_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts, 
         for (int32_t j = 0; j < i; j++)
             if (experts[j] == experts[i]) return fail(c, MOE_EINVAL, "moe_slot_prefetch: experts must be distinct");
     }
+    prefetch_map(c, layer, experts, n, max_bytes, slots_out, fill_out, n_done);
+    return MOE_OK;
+}
+
+static void prefetch_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int64_t max_bytes,
+                         int32_t* slots_out, uint8_t* fill_out, int32_t* n_done) {
+    const moe_config& cf = c->cfg;
     const int64_t base = (int64_t)layer * cf.n_experts;
     int64_t bytes = 0;
     int32_t done = 0;
@@ -646,6 +709,68 @@ moe_status moe_slot_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts, 
         slots_out[done] = s;
     }
     *n_done = done;
+}
+
+moe_status moe_prefetch_next(moe_ctx* c, int32_t layer, const void* const* payloads, int64_t max_bytes,
+                             float min_weight, int32_t transitions, moe_stream side, int32_t* n_out,
+                             int32_t* experts_out, uint8_t* fill_out) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (layer < 0 || layer >= cf.n_layers) return fail(c, MOE_EINVAL, "moe_prefetch_next: bad layer");
+    if (max_bytes < 0 || !(min_weight >= 0.f) || !(min_weight < 1e30f))
+        return fail(c, MOE_EINVAL, "moe_prefetch_next: bad max_bytes or min_weight");
+    if (!payloads || !n_out || !experts_out || !fill_out) return fail(c, MOE_EINVAL, "moe_prefetch_next: null argument");
+    *n_out = 0;
+    if (c->last_n.empty()) return MOE_OK;  // nothing routed yet
+    const int E = cf.n_experts, k = cf.top_k, stride = moe::kFusedMaxT * k;
+    const int32_t next = (layer + 1) % cf.n_layers;
+    // candidate -> score; the previous step's routing of `next` first (its
+    // weights), then transitions from this step's experts of `layer`
+    std::vector<std::pair<float, int32_t>> prev, trans;
+    std::vector<char> taken(E, 0);
+    {
+        const int N = c->last_n[next];
+        const int32_t* ids = &c->last_ids[(size_t)next * stride];
+        const float* w = &c->last_w[(size_t)next * stride];
+        std::vector<float> best(E, -1.f);
+        for (int i = 0; i < N; i++) best[ids[i]] = std::max(best[ids[i]], w[i]);
+        for (int e = 0; e < E; e++)
+            if (best[e] >= min_weight && best[e] >= 0.f) prev.push_back({best[e], e});
+    }
+    if (transitions && next == layer + 1 && c->last_n[layer] > 0 && !c->trans.empty()) {
+        const int N = c->last_n[layer];
+        const int32_t* ids = &c->last_ids[(size_t)layer * stride];
+        const float* w = &c->last_w[(size_t)layer * stride];
+        const uint32_t* tr = &c->trans[(size_t)layer * E * E];
+        const uint64_t* rs = &c->trans_row[(size_t)layer * E];
+        std::vector<double> score(E, 0.0);
+        for (int i = 0; i < N; i++) {
+            const uint64_t tot = rs[ids[i]];
+            if (!tot) continue;
+            const uint32_t* row = tr + (size_t)ids[i] * E;
+            for (int e = 0; e < E; e++)
+                if (row[e]) score[e] += (double)w[i] * row[e] / (double)tot;
+        }
+        for (int e = 0; e < E; e++)
+            if (score[e] >= min_weight && score[e] > 0.0) trans.push_back({(float)score[e], e});
+    }
+    auto by_score = [](const std::pair<float, int32_t>& a, const std::pair<float, int32_t>& b) {
+        return a.first != b.first ? a.first > b.first : a.second < b.second;
+    };
+    std::sort(prev.begin(), prev.end(), by_score);
+    std::sort(trans.begin(), trans.end(), by_score);
+    std::vector<int32_t> pred;
+    for (auto& q : prev) if (!taken[q.second] && payloads[q.second]) { taken[q.second] = 1; pred.push_back(q.second); }
+    for (auto& q : trans) if (!taken[q.second] && payloads[q.second]) { taken[q.second] = 1; pred.push_back(q.second); }
+    std::vector<int32_t> slots(pred.size());
+    int32_t done = 0;
+    prefetch_map(c, next, pred.data(), (int32_t)pred.size(), max_bytes, slots.data(), fill_out, &done);
+    for (int32_t i = 0; i < done; i++) {
+        experts_out[i] = pred[i];
+        if (fill_out[i])
+            if (moe_status st = moe_slot_fill(c, next, pred[i], slots[i], payloads[pred[i]], side)) return st;
+    }
+    *n_out = done;
     return MOE_OK;
 }
 
@@ -672,7 +797,7 @@ moe_status moe_slot_fill(moe_ctx* c, int32_t layer, int32_t expert, int32_t slot
         c->evicted[slot] = -1;
     }
     uint8_t* dst = (uint8_t*)cf.slot_pool + (size_t)slot * (size_t)c->g.payload;
-    HIP_TRY(c, hipMemcpyAsync(dst, host_payload, (size_t)c->g.payload, hipMemcpyHostToDevice, s));
+    HIP_TRY(c, hipMemcpyAsync(dst, host_payload, (size_t)c->g.payload, hipMemcpyDefault, s));
     HIP_TRY(c, hipMemsetD32Async((hipDeviceptr_t)(c->pt + key), slot, 1, s));
     if (moe_status st = mark_filled(c, s, &slot, nullptr, 1)) return st;
     moe_ctx::Pending* p = nullptr;

@@ -56,7 +56,8 @@ struct RouteUnion {
     int32_t* experts;
     int32_t* offsets;
     int32_t* entries;
-    int32_t* mirror;  // or null: [0] n_active, [1 ..] the experts (pinned host memory)
+    int32_t* mirror;  // or null (pinned host memory): [0] n_active, [1, 1 + E) the experts, then
+                      // the T k selected ids and the T k weights (float bits), entry t k + j
 };
 
 // Top-k of the T tokens (one wave each), then the union; one workgroup of 256.
@@ -80,6 +81,10 @@ __device__ void topk_union_wg(const float* logits, const RouteUnion& r) {
         __syncthreads();
         const int na = *r.n_active;
         for (int i = threadIdx.x; i <= na; i += blockDim.x) r.mirror[i] = i ? r.experts[i - 1] : na;
+        for (int i = threadIdx.x; i < N; i += blockDim.x) {
+            r.mirror[1 + r.E + i] = s_ids[i];
+            r.mirror[1 + r.E + N + i] = __float_as_int(s_w[i]);
+        }
     }
 }
 

@@ -73,6 +73,7 @@ def _load() -> C.CDLL:
         "moe_route_pull": (C.c_int, [P, I32, P, I32, P, P, I64, P, P, P, planp, P, P, P, P, P, P]),
         "moe_slot_prefetch": (C.c_int, [P, I32, P, I32, I64, P, P, P]),
         "moe_prefetch_stats": (C.c_int, [P, C.POINTER(C.c_uint64)]),
+        "moe_prefetch_next": (C.c_int, [P, I32, P, I64, C.c_float, I32, P, P, P, P]),
         "moe_slot_release": (C.c_int, [P, I32, P]),
         "moe_slot_bind": (C.c_int, [P, I32, I32, I32, P]),
         "moe_expert_ffn": (C.c_int, [P, I32, P, I32, I64, planp, P, P, I32, P, P]),
@@ -98,7 +99,7 @@ def _load() -> C.CDLL:
 _lib = _load()
 EXPORTS = ("moe_payload_bytes", "moe_plan_bytes", "moe_pack_expert", "moe_unpack_expert", "moe_create",
            "moe_destroy", "moe_last_error", "moe_status_string", "moe_route", "moe_plan_union", "moe_route_union",
-           "moe_slot_map", "moe_slot_prefetch", "moe_prefetch_stats", "moe_slot_fill", "moe_slot_stage", "moe_slot_pull", "moe_route_pull", "moe_slot_release",
+           "moe_slot_map", "moe_slot_prefetch", "moe_prefetch_stats", "moe_prefetch_next", "moe_slot_fill", "moe_slot_stage", "moe_slot_pull", "moe_route_pull", "moe_slot_release",
            "moe_slot_bind", "moe_expert_ffn", "moe_expert_ffn_static",
            "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table", "moe_route_splits", "moe_hidden_rows", "moe_probe_read",
            "moe_probe_mfma", "moe_probe_lds")
@@ -352,6 +353,22 @@ def moe_prefetch_stats(ctx: Context) -> dict:
     out = (C.c_uint64 * 4)()
     _call(ctx, _lib.moe_prefetch_stats(ctx.handle, out))
     return dict(fills=out[0], useful=out[1], wasted=out[2], bytes=out[3])
+
+
+def moe_prefetch_next(ctx: Context, layer: int, table: np.ndarray, max_bytes: int, min_weight: float = 0.20,
+                      transitions: bool = True, stream=None) -> tuple:
+    """After moe_route_pull of `layer`: predict layer (layer + 1) % n_layers's
+    experts and queue copies of the missing ones on `stream` from `table`
+    (payload_table of that layer, pinned host payloads); returns (experts,
+    filled) of the candidates processed, in priority order."""
+    _table(ctx, table)
+    n = C.c_int32()
+    ex = np.empty(ctx.n_experts, dtype=np.int32)
+    fill = np.empty(ctx.n_experts, dtype=np.uint8)
+    _call(ctx, _lib.moe_prefetch_next(ctx.handle, layer, table.ctypes.data, int(max_bytes), float(min_weight),
+                                      int(bool(transitions)), _stream(stream), C.byref(n), ex.ctypes.data,
+                                      fill.ctypes.data))
+    return ex[: n.value].copy(), fill[: n.value].astype(bool)
 
 
 def moe_slot_fill(ctx: Context, layer: int, expert: int, slot: int, host_payload, stream=None) -> None:

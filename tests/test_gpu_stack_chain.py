@@ -1,0 +1,125 @@
+"""A layer stack as the 40-layer workload runs it, on 3 layers: per layer one
+moe_route_pull (routing from Markov logits, readback, map, pull of the
+misses), the expert FFN, and the next layer's input chained from this
+layer's output, x_{l+1} = bf16(y_l / rms(y_l)) (eps 1e-6, no weight).  Every
+layer's output meets the oracle's bar given the GPU's own x_l, ids and
+weights.  Lookahead staging (moe_prefetch_next) leaves the outputs bit for
+bit as they are, predicts only what its rules allow, and is counted."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not H.gpu_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from routed_expert_execution_amd import moe  # noqa: E402
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def chain_next(y):
+    """The stack's glue between layers: bf16(y / rms(y)), eps 1e-6, no weight."""
+    return torch.nn.functional.rms_norm(y, (y.shape[-1],), eps=1e-6).to(torch.bfloat16)
+
+
+def _run(L=3, n_tok=5, n_slots=24, prefetch=None, cap=3):
+    """prefetch: None, or (min_weight, transitions) for moe_prefetch_next after
+    every moe_route_pull.  Returns per (token, layer): x_l bits, ids, weights,
+    y, and the predictions made after it."""
+    wl = synth.workload("stack40")
+    E, k, d, f = wl["E"], wl["k"], wl["d"], wl["f"]
+    ctx = H.make_ctx(wl, n_slots=n_slots, max_tokens=1, n_layers=L)
+    lg = [synth.markov_logits(wl["seed"], l, n_tok, E, k, wl["p_repeat"]) for l in range(L)]
+    recs = {}
+    pays = {}
+    for l in range(L):  # payloads of the experts the layer's routes select (no other is staged)
+        for e in sorted(set(np.argsort(-lg[l], axis=1)[:, :k].reshape(-1).tolist())):
+            recs[(l, e)] = synth.expert_record(wl["seed"], l, e, wl["qtype"], d, f)
+            pays[(l, e)] = torch.from_numpy(H.payload(ctx, recs[(l, e)])).pin_memory()
+    tables = [moe.payload_table(ctx, [pays.get((l, e)) for e in range(E)]) for l in range(L)]
+    shared = synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True)
+    sh_dev = H.device_payload(ctx, shared)
+    side = torch.cuda.Stream()
+    plan = moe.Plan(ctx, 1)
+    out = []
+    for t in range(n_tok):
+        x = H.torch_x(synth.activations(wl["seed"], 1, d, "bf16", t), "bf16")
+        for l in range(L):
+            ids = torch.empty(1, k, dtype=torch.int32, device="cuda")
+            w = torch.empty(1, k, dtype=torch.float32, device="cuda")
+            moe.moe_route_pull(ctx, l, ids, w, plan, tables[l],
+                               logits_in=torch.from_numpy(lg[l][t:t + 1]).cuda())
+            pred = None
+            if prefetch is not None:
+                nl = (l + 1) % L
+                pred = moe.moe_prefetch_next(ctx, l, tables[nl], cap * ctx.payload_bytes,
+                                             min_weight=prefetch[0], transitions=prefetch[1], stream=side)
+            y = torch.empty(1, d, dtype=torch.float32, device="cuda")
+            moe.moe_expert_ffn(ctx, l, x, plan, w, y, shared_payload=sh_dev)
+            moe.moe_slot_release(ctx, l)
+            out.append((t, l, x.view(torch.int16).cpu().numpy().copy(), ids.cpu().numpy(), w.cpu().numpy(),
+                        y.cpu().numpy(), pred))
+            x = chain_next(y)
+    torch.cuda.synchronize()
+    assert moe.moe_check(ctx) == moe.MOE_OK
+    return out, moe.moe_stats(ctx), moe.moe_prefetch_stats(ctx), recs, shared
+
+
+def test_chained_stack_meets_the_oracle_per_layer():
+    _say("chained 3-layer stack")
+    out, st, _, recs, shared = _run()
+    wl = synth.workload("stack40")
+    assert st["evictions"] > 0 and st["misses"] > 0
+    for t, l, xb, ids, w, y, _ in out:
+        assert np.isfinite(y).all()
+        x64 = oracle.x_to_f64(xb.view(np.uint16), "bf16")
+        records = [recs.get((l, e)) for e in range(wl["E"])]
+        ref = oracle.moe_layer(wl["qtype"], oracle.PREC_F32, records, shared, wl["d"], wl["f"], x64, ids, w)
+        err = H.max_rel_row_err(y, ref)
+        assert err <= 1e-3, (t, l, err)
+    # the chain carries the layers' outputs forward: layer l+1's input is bf16(y_l / rms(y_l))
+    for (t, l, _, _, _, y, _), (t2, l2, xb2, _, _, _, _) in zip(out, out[1:]):
+        if t2 != t:
+            continue
+        y64 = y.astype(np.float64)
+        ref = y64 / np.sqrt((y64 * y64).mean(axis=-1, keepdims=True) + 1e-6)
+        got = oracle.x_to_f64(xb2.view(np.uint16), "bf16")
+        assert np.abs(got - ref).max() <= 2 ** -7 * np.abs(ref).max()  # within a bf16 rounding
+
+
+@pytest.mark.parametrize("min_weight,transitions", [(0.20, False), (0.0, False), (0.0, True)])
+def test_prefetch_next_is_transparent_and_follows_its_rules(min_weight, transitions):
+    _say("prefetch_next", min_weight, transitions)
+    base, st0, ps0, _, _ = _run()
+    pre, st1, ps1, _, _ = _run(prefetch=(min_weight, transitions))
+    assert ps0["fills"] == 0
+    assert ps1["useful"] + ps1["wasted"] <= ps1["fills"]
+    assert st1["fills"] == st1["misses"] + ps1["fills"]
+    L = 3
+    last = {}  # layer -> (ids, w) of its previous step
+    for (t, l, xa, ida, wa, ya, _), (_, _, xb, idb, wb, yb, pred) in zip(base, pre):
+        assert np.array_equal(xa, xb) and np.array_equal(ida, idb)
+        assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32)), (t, l)
+        nl = (l + 1) % L
+        ex, filled = pred
+        assert len(set(ex.tolist())) == len(ex)
+        prev = last.get(nl)
+        allowed = set()
+        if prev is not None:
+            allowed |= {int(e) for e, ww in zip(prev[0][0], prev[1][0]) if ww >= min_weight}
+        if not transitions or nl != l + 1:
+            assert set(ex.tolist()) <= allowed, (t, l, ex, allowed)
+            if prev is not None:  # highest weight first
+                wmap = {int(e): float(ww) for e, ww in zip(prev[0][0], prev[1][0])}
+                ws = [wmap[int(e)] for e in ex]
+                assert ws == sorted(ws, reverse=True)
+        last[l] = (ida, wa)
+    assert ps1["fills"] > 0
