@@ -456,8 +456,12 @@ def run_stack(args, torch, moe, synth) -> int:
                                 out=packs[a].numpy()[e])
     shared = torch.from_numpy(moe.moe_pack_expert(
         ctx.cfg, synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True))).to(dev)
-    lg = torch.stack([torch.from_numpy(synth.markov_logits(wl["seed"], l, n_tok, E, k, wl["p_repeat"]))
-                      for l in range(L)]).to(dev)  # [L, tokens, E]
+    if args.follow_routes > 0:
+        lg = torch.from_numpy(synth.follow_stack_logits(wl["seed"], L, n_tok, E, k, wl["p_repeat"],
+                                                        args.follow_routes)).to(dev)
+    else:
+        lg = torch.stack([torch.from_numpy(synth.markov_logits(wl["seed"], l, n_tok, E, k, wl["p_repeat"]))
+                          for l in range(L)]).to(dev)  # [L, tokens, E]
     # layer 0's input per token (and, with --fresh-inputs, every layer's);
     # otherwise x_{l+1} = bf16(y_l / rms(y_l)), eps 1e-6, no weight
     n_in = L if args.fresh_inputs else 1
@@ -515,7 +519,7 @@ def run_stack(args, torch, moe, synth) -> int:
                 nl = (l + 1) % L  # (layer 0 of the next token after the last)
                 ex_p, fl_p = moe.moe_prefetch_next(ctx, l, tables[nl % n_alias], args.prefetch * pb,
                                                    min_weight=args.prefetch_min_weight,
-                                                   transitions=not args.no_transitions, stream=side)
+                                                   min_transition=args.prefetch_min_transition, stream=side)
                 pred_n[0] += len(ex_p)
                 pred_n[1] += int(fl_p.sum())
             if ev:
@@ -589,12 +593,15 @@ def run_stack(args, torch, moe, synth) -> int:
                          f"Q8_0, 1 token/step, one {n_slots}-slot LRU pool shared by the layers, Markov routes "
                          f"(p_repeat {wl['p_repeat']}), misses staged from pinned host memory "
                          f"after each layer's plan readback; payload sets alias mod {n_alias} layers"
+                         + (f"; routes also follow the layer below (p_follow {args.follow_routes}; not the "
+                            f"pages' workload)" if args.follow_routes > 0 else "")
                          + ("; fresh synthetic input per layer" if args.fresh_inputs
                             else "; layers chained: x_{l+1} = bf16(y_l / rms(y_l)), eps 1e-6")
                          + (f"; moe_prefetch_next after each moe_route_pull: up to {args.prefetch} payloads of the "
                             f"next layer's predicted experts (previous token's weight >= "
-                            f"{args.prefetch_min_weight}" + ("" if args.no_transitions
-                                                             else ", then layer-to-layer transition scores")
+                            f"{args.prefetch_min_weight}" + (f", then layer-to-layer transition scores >= "
+                                                             f"{args.prefetch_min_transition}"
+                                                             if args.prefetch_min_transition > 0 else "")
                             + ") copied on a side stream while the layer computes" if args.prefetch else "")
                          + (f"; copies alternate over {args.fill_streams} side streams"
                             if args.fill_streams > 1 and args.staging != "pull" else "")
@@ -628,7 +635,7 @@ def run_stack(args, torch, moe, synth) -> int:
             "pull": pull,
             "setup_pack_s": t_gen,
             "prefetch": ({"cap_payloads_per_layer": args.prefetch, "min_weight": args.prefetch_min_weight,
-                          "transitions": not args.no_transitions, **pf,
+                          "min_transition": args.prefetch_min_transition, **pf,
                           "note": "fills/useful/wasted/bytes over the timed tokens (useful: a later demand map "
                                   "found it; wasted: evicted unused)"} if args.prefetch else None),
             "n_slots": n_slots,
@@ -658,10 +665,13 @@ def main() -> int:
     ap.add_argument("--prefetch-min-weight", type=float, default=0.20, metavar="W",
                     help="stack: prediction threshold (the previous token's experts of the next layer with "
                          "routing weight >= W; transition scores >= W)")
-    ap.add_argument("--no-transitions", action="store_true",
-                    help="stack: predict from the previous token only (no layer-to-layer transition counts)")
+    ap.add_argument("--prefetch-min-transition", type=float, default=0.0, metavar="S",
+                    help="stack: also predict from layer-to-layer transition counts, scores >= S (0: off)")
     ap.add_argument("--slots", type=int, default=0, metavar="S",
                     help="stack: slots in the pool (default: the workload's 1,536)")
+    ap.add_argument("--follow-routes", type=float, default=0.0, metavar="P",
+                    help="stack: routes that also follow the layer below (new picks the image of an expert of "
+                         "the same token one layer down with probability P; not the pages' workload)")
     ap.add_argument("--fresh-inputs", action="store_true",
                     help="stack: a fresh synthetic input per layer instead of the chained x_{l+1} = "
                          "bf16(y_l / rms(y_l))")

@@ -286,26 +286,30 @@ moe_status moe_prefetch_stats(const moe_ctx* ctx, uint64_t out[4]);
  * in this order, each once:
  *   1. the experts that the last moe_route_pull of `next` (the previous step)
  *      selected with weight >= min_weight, highest weight first;
- *   2. if `transitions` and next == layer + 1: the experts e' with
- *      sum over this step's entries (e, w) at `layer` of
- *      w * count(e -> e') / count(e -> any) >= min_weight, highest first, where
+ *   2. if min_transition > 0 and next == layer + 1: the experts e' with
+ *      score(e') = sum over this step's entries (e, w) at `layer` of
+ *      w * count(e -> e') / count(e -> any) >= min_transition, highest first
+ *      (the scores sum to at most 1 over e'), where
  *      count(e -> e') is how often a token that selected e at `layer` selected
  *      e' at `next` in earlier steps (every moe_route_pull of `next` right
  *      after one of `layer` with as many tokens adds one per pair).
- * Candidates without a payload (null entry) are skipped.  They are mapped as
- * moe_slot_prefetch maps them (never into a pinned slot; stops at max_bytes of
- * fills), and each that must be filled is copied as moe_slot_fill copies it, on
- * `side` (its page-table entry is written after the copy; moe_expert_ffn of
- * `next` waits for it).
+ * Candidates without a payload (null entry) are skipped.  A resident candidate
+ * is left as it is (not touched); a missing one takes a free slot, else the
+ * least recently touched slot that no moe_route_pull of the last n_layers
+ * calls touched (a slot idle for a whole step) and no layer has pinned, and is
+ * copied as moe_slot_fill copies it, on `side` (its page-table entry is written
+ * after the copy; moe_expert_ffn of `next` waits for it).  The staging stops at
+ * the first candidate that finds no such slot or would exceed max_bytes of
+ * copies.  Counted as moe_slot_prefetch's fills (useful / wasted).
  * payloads: host array of n_experts pointers for layer `next`, each to a
  *   payload in pinned host memory, or null.
  * n_out (host [1]): candidates processed; experts_out (host [n_experts]) and
  *   fill_out (host [n_experts]): those candidates in order, and 1 where a copy
  *   was queued.  Nothing is predicted before the first moe_route_pull.
- * MOE_EINVAL: bad layer, max_bytes < 0, min_weight negative or not finite, or
- *   a null argument, with nothing mapped. */
+ * MOE_EINVAL: bad layer, max_bytes < 0, min_weight negative or not finite,
+ *   min_transition NaN or infinite, or a null argument, with nothing mapped. */
 moe_status moe_prefetch_next(moe_ctx* ctx, int32_t layer, const void* const* payloads, int64_t max_bytes,
-                             float min_weight, int32_t transitions, moe_stream side, int32_t* n_out,
+                             float min_weight, float min_transition, moe_stream side, int32_t* n_out,
                              int32_t* experts_out, uint8_t* fill_out);
 
 /* Unpin every slot pinned to `layer` and record, on `compute`, the point after

@@ -58,6 +58,8 @@ struct moe_ctx {
     std::vector<uint32_t> trans;    // [L - 1][E][E] (allocated by the first moe_route_pull)
     std::vector<uint64_t> trans_row;  // [L - 1][E] row sums
     int32_t prev_pull_layer = -1;
+    std::vector<uint64_t> pull_clock;  // [L] slot clock when each of the last L moe_route_pull calls routed
+    int32_t pull_pos = 0;
 
     // ordering
     int32_t* hmirror = nullptr;       // pinned [1 + E + 2 * 4 * top_k]: n_active, experts, ids and
@@ -544,6 +546,10 @@ static void record_routing(moe_ctx* c, int32_t layer, int T) {
                 }
     }
     c->prev_pull_layer = layer;
+    // the clock at the start of each of the last n_layers calls (pull_pos: the oldest)
+    if (c->pull_clock.empty()) c->pull_clock.assign(cf.n_layers, 0);
+    c->pull_clock[c->pull_pos] = c->clock;
+    c->pull_pos = (c->pull_pos + 1) % cf.n_layers;
 }
 
 moe_status moe_route_pull(moe_ctx* c, int32_t layer, const void* x, int32_t x_dtype, const float* w_router,
@@ -648,7 +654,7 @@ moe_status moe_slot_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32
 
 // The mapping of moe_slot_prefetch (arguments already checked).
 static void prefetch_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int64_t max_bytes,
-                         int32_t* slots_out, uint8_t* fill_out, int32_t* n_done);
+                         int32_t* slots_out, uint8_t* fill_out, int32_t* n_done, uint64_t horizon = UINT64_MAX);
 
 moe_status moe_slot_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int64_t max_bytes,
                              int32_t* slots_out, uint8_t* fill_out, int32_t* n_done) {
@@ -667,8 +673,9 @@ moe_status moe_slot_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts, 
     return MOE_OK;
 }
 
+// horizon: a victim must not have been touched at or after this clock value.
 static void prefetch_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int64_t max_bytes,
-                         int32_t* slots_out, uint8_t* fill_out, int32_t* n_done) {
+                         int32_t* slots_out, uint8_t* fill_out, int32_t* n_done, uint64_t horizon) {
     const moe_config& cf = c->cfg;
     const int64_t base = (int64_t)layer * cf.n_experts;
     int64_t bytes = 0;
@@ -685,7 +692,7 @@ static void prefetch_map(moe_ctx* c, int32_t layer, const int32_t* experts, int3
             if (pick < 0) {
                 uint64_t best = UINT64_MAX;
                 for (int q = 0; q < cf.n_slots; q++)
-                    if (c->pin_layer[q] < 0 && c->last[q] < best) { best = c->last[q]; pick = q; }
+                    if (c->pin_layer[q] < 0 && c->last[q] < best && c->last[q] < horizon) { best = c->last[q]; pick = q; }
                 if (pick < 0) break;
                 c->slot_of[c->owner[pick]] = -1;
                 c->evicted[pick] = c->owner[pick];
@@ -704,6 +711,10 @@ static void prefetch_map(moe_ctx* c, int32_t layer, const int32_t* experts, int3
             fill_out[done] = 1;
         } else {
             fill_out[done] = 0;
+            if (horizon != UINT64_MAX) {  // moe_prefetch_next: a resident prediction keeps its place
+                slots_out[done] = s;
+                continue;
+            }
         }
         c->last[s] = ++c->clock;  // predicted: kept until the demand that should follow
         slots_out[done] = s;
@@ -712,13 +723,14 @@ static void prefetch_map(moe_ctx* c, int32_t layer, const int32_t* experts, int3
 }
 
 moe_status moe_prefetch_next(moe_ctx* c, int32_t layer, const void* const* payloads, int64_t max_bytes,
-                             float min_weight, int32_t transitions, moe_stream side, int32_t* n_out,
+                             float min_weight, float min_transition, moe_stream side, int32_t* n_out,
                              int32_t* experts_out, uint8_t* fill_out) {
     if (moe_status st = need_device(c)) return st;
     const moe_config& cf = c->cfg;
     if (layer < 0 || layer >= cf.n_layers) return fail(c, MOE_EINVAL, "moe_prefetch_next: bad layer");
-    if (max_bytes < 0 || !(min_weight >= 0.f) || !(min_weight < 1e30f))
-        return fail(c, MOE_EINVAL, "moe_prefetch_next: bad max_bytes or min_weight");
+    if (max_bytes < 0 || !(min_weight >= 0.f) || !(min_weight < 1e30f) || !(min_transition < 1e30f) ||
+        min_transition != min_transition)
+        return fail(c, MOE_EINVAL, "moe_prefetch_next: bad max_bytes, min_weight or min_transition");
     if (!payloads || !n_out || !experts_out || !fill_out) return fail(c, MOE_EINVAL, "moe_prefetch_next: null argument");
     *n_out = 0;
     if (c->last_n.empty()) return MOE_OK;  // nothing routed yet
@@ -737,7 +749,7 @@ moe_status moe_prefetch_next(moe_ctx* c, int32_t layer, const void* const* paylo
         for (int e = 0; e < E; e++)
             if (best[e] >= min_weight && best[e] >= 0.f) prev.push_back({best[e], e});
     }
-    if (transitions && next == layer + 1 && c->last_n[layer] > 0 && !c->trans.empty()) {
+    if (min_transition > 0.f && next == layer + 1 && c->last_n[layer] > 0 && !c->trans.empty()) {
         const int N = c->last_n[layer];
         const int32_t* ids = &c->last_ids[(size_t)layer * stride];
         const float* w = &c->last_w[(size_t)layer * stride];
@@ -752,7 +764,7 @@ moe_status moe_prefetch_next(moe_ctx* c, int32_t layer, const void* const* paylo
                 if (row[e]) score[e] += (double)w[i] * row[e] / (double)tot;
         }
         for (int e = 0; e < E; e++)
-            if (score[e] >= min_weight && score[e] > 0.0) trans.push_back({(float)score[e], e});
+            if (score[e] >= min_transition) trans.push_back({(float)score[e], e});
     }
     auto by_score = [](const std::pair<float, int32_t>& a, const std::pair<float, int32_t>& b) {
         return a.first != b.first ? a.first > b.first : a.second < b.second;
@@ -764,7 +776,15 @@ moe_status moe_prefetch_next(moe_ctx* c, int32_t layer, const void* const* paylo
     for (auto& q : trans) if (!taken[q.second] && payloads[q.second]) { taken[q.second] = 1; pred.push_back(q.second); }
     std::vector<int32_t> slots(pred.size());
     int32_t done = 0;
-    prefetch_map(c, next, pred.data(), (int32_t)pred.size(), max_bytes, slots.data(), fill_out, &done);
+    // Victims: only slots untouched for a whole step (the last n_layers
+    // moe_route_pull calls), which the next step would not use either; a
+    // prediction that needs any other stops the staging.  A prediction already
+    // resident is left where it is in the recency order.  (Evicting the least
+    // recently touched slot regardless, or touching resident predictions, cost
+    // a pool of one step's experts most of its hits: each moved another layer's
+    // expert of the step to the front of the eviction order.)
+    const uint64_t horizon = c->pull_clock.empty() ? 0 : c->pull_clock[c->pull_pos];
+    prefetch_map(c, next, pred.data(), (int32_t)pred.size(), max_bytes, slots.data(), fill_out, &done, horizon);
     for (int32_t i = 0; i < done; i++) {
         experts_out[i] = pred[i];
         if (fill_out[i])

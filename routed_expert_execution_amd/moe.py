@@ -73,7 +73,7 @@ def _load() -> C.CDLL:
         "moe_route_pull": (C.c_int, [P, I32, P, I32, P, P, I64, P, P, P, planp, P, P, P, P, P, P]),
         "moe_slot_prefetch": (C.c_int, [P, I32, P, I32, I64, P, P, P]),
         "moe_prefetch_stats": (C.c_int, [P, C.POINTER(C.c_uint64)]),
-        "moe_prefetch_next": (C.c_int, [P, I32, P, I64, C.c_float, I32, P, P, P, P]),
+        "moe_prefetch_next": (C.c_int, [P, I32, P, I64, C.c_float, C.c_float, P, P, P, P]),
         "moe_slot_release": (C.c_int, [P, I32, P]),
         "moe_slot_bind": (C.c_int, [P, I32, I32, I32, P]),
         "moe_expert_ffn": (C.c_int, [P, I32, P, I32, I64, planp, P, P, I32, P, P]),
@@ -356,17 +356,19 @@ def moe_prefetch_stats(ctx: Context) -> dict:
 
 
 def moe_prefetch_next(ctx: Context, layer: int, table: np.ndarray, max_bytes: int, min_weight: float = 0.20,
-                      transitions: bool = True, stream=None) -> tuple:
+                      min_transition: float = 0.0, stream=None) -> tuple:
     """After moe_route_pull of `layer`: predict layer (layer + 1) % n_layers's
-    experts and queue copies of the missing ones on `stream` from `table`
-    (payload_table of that layer, pinned host payloads); returns (experts,
-    filled) of the candidates processed, in priority order."""
+    experts (the previous step's at weight >= min_weight, then transition
+    scores >= min_transition; 0 turns those off) and queue copies of the
+    missing ones on `stream` from `table` (payload_table of that layer, pinned
+    host payloads); returns (experts, filled) of the candidates processed, in
+    priority order."""
     _table(ctx, table)
     n = C.c_int32()
     ex = np.empty(ctx.n_experts, dtype=np.int32)
     fill = np.empty(ctx.n_experts, dtype=np.uint8)
     _call(ctx, _lib.moe_prefetch_next(ctx.handle, layer, table.ctypes.data, int(max_bytes), float(min_weight),
-                                      int(bool(transitions)), _stream(stream), C.byref(n), ex.ctypes.data,
+                                      float(min_transition), _stream(stream), C.byref(n), ex.ctypes.data,
                                       fill.ctypes.data))
     return ex[: n.value].copy(), fill[: n.value].astype(bool)
 

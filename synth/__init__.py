@@ -225,6 +225,34 @@ def markov_logits(seed: int, layer: int, n_tokens: int, E: int, k: int, p_repeat
     return _realise(g, markov_route_sets(g, n_tokens, E, k, p_repeat), E)
 
 
+def follow_stack_logits(seed: int, n_layers: int, n_tokens: int, E: int, k: int, p_repeat: float,
+                        p_follow: float) -> np.ndarray:
+    """[n_layers, n_tokens, E] logits of Markov route chains that also follow
+    the layer below: a token keeps each expert of its previous set at a layer
+    with probability p_repeat (as markov_route_sets); each other pick is, with
+    probability p_follow, the image under a fixed map of a random expert the
+    same token selected one layer down (e -> (37 e + 11 l) mod E at layer l),
+    else uniform.  Not a workload of the pages: routes whose new experts a
+    layer-to-layer table can predict."""
+    g = rng(seed, _P_ROUTE, 1000)
+    sets = [[None] * n_tokens for _ in range(n_layers)]
+    for t in range(n_tokens):
+        for l in range(n_layers):
+            prev = sets[l][t - 1] if t > 0 else []
+            cur = [e for e in prev if g.uniform() < p_repeat]
+            below = sets[l - 1][t] if l > 0 else []
+            while len(cur) < k:
+                e = -1
+                if below and g.uniform() < p_follow:
+                    e = (37 * below[g.integers(len(below))] + 11 * l) % E
+                if e < 0 or e in cur:
+                    free = np.setdiff1d(np.arange(E), np.array(cur, dtype=np.int64))
+                    e = int(free[g.integers(free.size)])
+                cur.append(int(e))
+            sets[l][t] = sorted(cur)
+    return np.stack([_realise(g, sets[l], E) for l in range(n_layers)])
+
+
 def markov_trace(seed: int, n_layers: int, n_tokens: int, n_experts: int, k: int, p_repeat: float) -> list:
     """Replay trace: steps (layer, experts) for n_tokens tokens through n_layers
     layers, token-major, each layer's route a Markov chain over tokens (the
