@@ -74,8 +74,15 @@ hipError_t launch_router_gemv(const void* x, int x_bf16, const float* w_r, int64
                               float* logits, hipStream_t s);
 hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int norm, int32_t* ids,
                        float* w, hipStream_t s);
+// Up to kPlanOneWgMax assignments one workgroup sorts them; more take three
+// launches over segments of 4096, with a workspace of plan_workspace_ints()
+// ints (without one, the one-workgroup kernel, however large).  Measured
+// (event time): 16,384 assignments 25.7 us in one workgroup, 21.5 us in
+// segments; 524,288 in segments 63 us.
+constexpr int64_t kPlanOneWgMax = 8192;
+int64_t plan_workspace_ints(int64_t T, int k, int E);
 hipError_t launch_plan(const int32_t* ids, int64_t T, int k, int E, const moe_plan& plan, int* err,
-                       hipStream_t s);
+                       hipStream_t s, int* ws = nullptr);
 hipError_t launch_dequant(const Geom& g, const uint8_t* payload, int prec, float* out, hipStream_t s);
 // Route and union of at most kFusedMaxT tokens: router logits (unless
 // logits_in), then top-k and the union in one single-workgroup launch.  Same

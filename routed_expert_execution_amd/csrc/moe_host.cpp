@@ -38,6 +38,7 @@ struct moe_ctx {
     uint64_t route_splits = 0; // moe_route_ffn calls that took the two-launch path
     int last_prefill_prec = -1; // mode of the last chunk call (-1: none yet)
     float* logits_ws = nullptr;// [max_T * E]
+    int* plan_ws = nullptr;    // per-segment expert counts of a large plan (or null)
 
     // slot manager (host)
     std::vector<int64_t> owner;     // slot -> key = layer*E + expert, or -1
@@ -353,6 +354,7 @@ void moe_destroy(moe_ctx* c) {
         if (c->pinv) (void)hipFree(c->pinv);
         if (c->psched) (void)hipFree(c->psched);
         if (c->logits_ws) (void)hipFree(c->logits_ws);
+        if (c->plan_ws) (void)hipFree(c->plan_ws);
         if (c->release_ev) (void)hipEventDestroy(c->release_ev);
         if (c->fork_ev) (void)hipEventDestroy(c->fork_ev);
         if (c->route_ev) (void)hipEventDestroy(c->route_ev);
@@ -406,6 +408,8 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         if (hipMalloc(&c->sync, sizeof(uint32_t) * moe::kSyncInts) != hipSuccess) return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->logits_ws, sizeof(float) * (size_t)T * cfg->n_experts) != hipSuccess)
             return cleanup(MOE_ENOMEM);
+        if (const int64_t pw = moe::plan_workspace_ints(T, cfg->top_k, cfg->n_experts))
+            if (hipMalloc(&c->plan_ws, sizeof(int) * (size_t)pw) != hipSuccess) return cleanup(MOE_ENOMEM);
         if (T > moe::kDecodeMaxT) {
             const size_t rows = (size_t)(T * cfg->top_k + T);
             moe::prefill_max_tiles(T, cfg->top_k, cfg->n_experts, true, &c->p_big, &c->p_small, &c->p_wide);
@@ -479,7 +483,8 @@ moe_status moe_plan_union(moe_ctx* c, const int32_t* topk_ids, int64_t T, const 
         return fail(c, MOE_EINVAL, "moe_plan_union: null plan array");
     if (T > 0 && !topk_ids) return fail(c, MOE_EINVAL, "moe_plan_union: null topk_ids");
     DeviceGuard dg(cf.device);
-    HIP_TRY(c, moe::launch_plan(topk_ids, T, cf.top_k, cf.n_experts, *plan, c->err_word, (hipStream_t)stream));
+    HIP_TRY(c, moe::launch_plan(topk_ids, T, cf.top_k, cf.n_experts, *plan, c->err_word, (hipStream_t)stream,
+                                c->plan_ws));
     return MOE_OK;
 }
 

@@ -172,8 +172,13 @@ def test_route_logits_in_bit_exact(E, k, kind, norm):
 @pytest.mark.parametrize("T,k,E,kind", [(1, 8, 256, "uniform"), (4, 8, 256, "uniform"), (4, 2, 8, "uniform"),
                                         (37, 8, 256, "uniform"), (512, 8, 256, "zipf"), (513, 8, 256, "zipf"),
                                         (300, 2, 8, "same"), (200, 32, 1024, "uniform"), (0, 8, 256, "uniform"),
-                                        (4096, 8, 256, "zipf")])
+                                        (4096, 8, 256, "zipf"), (1024, 8, 256, "zipf"), (1025, 8, 256, "zipf"),
+                                        (2048, 32, 1024, "uniform"), (65536, 8, 256, "zipf"),
+                                        (6000, 2, 8, "same")])
 def test_plan_union_bit_exact(T, k, E, kind):
+    """Up to 8192 assignments one workgroup sorts them (1024 x 8 is the
+    last such); more run as per-segment counts, one scan and per-segment
+    scatters (1025 x 8: a ragged last segment; 65536 x 8: 128 segments)."""
     _say("plan", T, k, E, kind)
     wl = dict(synth.workload("decode"), E=E, k=k)
     ctx = H.make_ctx(wl, n_slots=1, max_tokens=max(T, 1))
@@ -190,6 +195,30 @@ def test_plan_union_bit_exact(T, k, E, kind):
     n, ex, off, ent = plan.host()
     rn, rex, roff, rent = oracle.plan_union(ids_np, E)
     assert n == rn and np.array_equal(ex, rex) and np.array_equal(off, roff) and np.array_equal(ent, rent)
+
+
+@pytest.mark.parametrize("T", [37, 4096])
+def test_plan_union_drops_out_of_range_ids(T):
+    """Out-of-range ids are dropped (the plan is the oracle's union of the
+    other entries, at their own positions) and set the error word, on the
+    one-workgroup path and the segmented one."""
+    wl = dict(synth.workload("decode"))
+    E, k = wl["E"], wl["k"]
+    ctx = H.make_ctx(wl, n_slots=1, max_tokens=T)
+    lg = synth.zipf_gumbel_logits(T + 5, T, E, 1.1)
+    ids_np = np.argsort(-lg, axis=1, kind="stable")[:, :k].astype(np.int32)
+    g = np.random.default_rng(T)
+    bad = g.choice(T * k, size=max(3, T // 64), replace=False)
+    flat = ids_np.reshape(-1).copy()
+    flat[bad] = np.where(np.arange(bad.size) % 2 == 0, E + 3, -1)
+    plan = moe.Plan(ctx, T)
+    moe.moe_plan_union(ctx, torch.from_numpy(flat.reshape(T, k)).cuda(), plan)
+    n, ex, off, ent = plan.host()
+    valid = np.flatnonzero((flat >= 0) & (flat < E))
+    rn, rex, roff, rent = oracle.plan_union(flat[valid].reshape(-1, 1), E)
+    assert n == rn and np.array_equal(ex, rex) and np.array_equal(off, roff)
+    assert np.array_equal(ent[: valid.size], valid[rent])
+    assert moe.moe_check(ctx) == moe.MOE_EINVAL
 
 
 # ---------------------------------------------------------------------------
