@@ -207,6 +207,18 @@ __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec)
 
 // ---- weights ------------------------------------------------------------------
 
+// Raw buffer loads (gfx9 buffer resource word 3: untyped 32-bit data).  A load
+// past the resource's size returns zeros.
+constexpr int kBufWord3 = 0x00020000;
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 as_float4(uint4 v) {
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+
 // One lane's block: its codes and scale, as stored in a tile.
 template <int QT> struct Raw;
 template <> struct Raw<MOE_Q8_0> {
@@ -216,6 +228,12 @@ template <> struct Raw<MOE_Q8_0> {
         lo = *(const uint4*)(t + q8_lo(i));
         hi = *(const uint4*)(t + q8_hi(i));
         s = *(const uint16_t*)(t + q8_scale(i));
+    }
+    // the same block through a buffer resource: codes at voff + so, scale at vs + ss
+    __device__ void load_buf(__amdgpu_buffer_rsrc_t r, int voff, int vs, int so, int ss) {
+        lo = buf_load16(r, voff + q8_lo(0), so);
+        hi = buf_load16(r, voff + q8_hi(0), so);
+        s = __builtin_amdgcn_raw_buffer_load_b16(r, vs, ss, 0);
     }
     __device__ void zero() { lo = hi = make_uint4(0, 0, 0, 0); s = 0; }
     // Elements 8j..8j+7 as biased bytes (q + 128), 4 per word.
@@ -245,6 +263,10 @@ template <> struct Raw<MOE_Q4_0> {
     __device__ void load(const uint8_t* t, int i) {
         nib = *(const uint4*)(t + q4_nib(i));
         s = *(const uint16_t*)(t + q4_scale(i));
+    }
+    __device__ void load_buf(__amdgpu_buffer_rsrc_t r, int voff, int vs, int so, int ss) {
+        nib = buf_load16(r, voff, so);
+        s = __builtin_amdgcn_raw_buffer_load_b16(r, vs, ss, 0);
     }
     __device__ void zero() { nib = make_uint4(0, 0, 0, 0); s = 0; }
     // Elements 8j..8j+7 as biased bytes (q + 8), 4 per word: low nibbles of
@@ -766,53 +788,71 @@ __device__ void wide_item(const PrefillArgs& a, const TileRec& t, const uint8_t*
     const Geom& G = a.g;
     const int nk = (GATEUP ? G.nb_d : G.nb_f) / 2;  // steps
     constexpr bool AXB = GATEUP ? XB : true;         // the hidden rows are bf16
-    // this thread's A rows (valid rows; padding rows staged as zeros)
-    int64_t arow[4];
-    bool akeep[4];
+    // Loads go through buffer resources (a base and a size in scalar registers):
+    // each thread keeps fixed 32-bit offsets, and a step adds one uniform
+    // scalar offset, so a step's addressing costs no vector instructions.
+    // A: x (gate/up; token rows) or the tile's hidden rows (down; rows
+    // row_slot(0) .. + M - 1, which are consecutive).  Padding rows (m >= M)
+    // read row 0 again: a product row depends only on its own A row, and the
+    // epilogue drops those rows.
+    constexpr int AE = AXB ? 2 : 4;  // bytes per activation element
+    const int64_t a_row0 = GATEUP ? 0 : (int64_t)row_slot(a, t, 0);
+    const int a_rowlen = GATEUP ? a.d : a.f;
+    const uint8_t* A = GATEUP ? (const uint8_t*)a.x : (const uint8_t*)a.h + a_row0 * a.f * 2;
+    const int a_bytes = GATEUP ? a.T * a.d * AE : t.M * a.f * 2;
+    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, a_bytes, kBufWord3);
+    const int ach = (tid & 7) * 8;  // column of the thread's pieces within a step
+    int aoff[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int m = (tid >> 3) + 32 * i;
-        akeep[i] = m < t.M;
-        const int mm = akeep[i] ? m : 0;
-        arow[i] = GATEUP ? (int64_t)row_token(a, t, mm) * a.d : (int64_t)row_slot(a, t, mm) * a.f;
+        const int mm = m < t.M ? m : 0;
+        const int row = GATEUP ? row_token(a, t, mm) : mm;
+        aoff[i] = (row * a_rowlen + ach) * AE;
     }
-    const int ach = (tid & 7) * 8;  // column of the thread's pieces within a step
-    // this thread's weight block: LDS row brow, block kbit of each step
+    // this thread's weight block: LDS row brow, block kbit of each step.  Step
+    // s reads column block 2 s + kbit: tile s / 2 of the row group's run of
+    // tiles, lane 16 (2 (s % 2) + kbit) + brow % 16 of it.
     const int kbit = (tid >> 4) & 1;
     int brow;
     if constexpr (GATEUP) brow = (tid >> 7) * 64 + 16 * ((tid >> 5) & 3) + (tid & 15);
     else brow = 16 * (tid >> 5) + (tid & 15);
-    auto blk_ptr = [&](int step, int* i) -> const uint8_t* {
-        int64_t tile;
-        if constexpr (GATEUP) {
-            const int fe = brow & 63;
-            G.gu_block(c0 + fe, 2 * step + kbit, &tile, i);
-            return base + ((brow >> 6) == 0 ? G.gate_tile(tile) : G.up_tile(tile));
-        } else {
-            G.down_block(c0 + brow, 2 * step + kbit, &tile, i);
-            return base + G.down_tile(tile);
-        }
-    };
-    const void* A = GATEUP ? a.x : a.h;
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)G.payload, kBufWord3);
+    int64_t t0;  // the row group's first tile and the matrix's tile stride
+    int tstride;
+    if constexpr (GATEUP) {
+        int li;
+        G.gu_block(c0 + (brow & 63), 0, &t0, &li);
+        tstride = 2 * (int)G.tile_bytes;
+    } else {
+        int li;
+        G.down_block(c0 + brow, 0, &t0, &li);
+        tstride = (int)G.tile_bytes;
+    }
+    const int64_t mat0 = GATEUP ? ((brow >> 6) == 0 ? G.gate_tile(t0) : G.up_tile(t0)) : G.down_tile(t0);
+    const int li0 = 16 * kbit + (brow & 15);
+    const int woff = (int)mat0 + (QT == MOE_Q8_0 ? q8_lo(li0) : q4_nib(li0));
+    const int soff_w = (int)mat0 + (QT == MOE_Q8_0 ? q8_scale(li0) : q4_scale(li0));
     auto load = [&](WideRaw<QT, AXB>& r, int step) {
         step = min(step, nk - 1);  // past the end: the last step again (unused)
-        const int col = step * WBK + ach;
+        const int sa = step * WBK * AE;
+        const int sw = (step >> 1) * tstride, odd = step & 1;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             if constexpr (AXB) {
-                r.x[i] = *(const uint4*)((const uint16_t*)A + arow[i] + col);
+                r.x[i] = buf_load16(ar, aoff[i], sa);
             } else {
-                const float* p = (const float*)A + arow[i] + col;
-                r.x[2 * i] = *(const float4*)p;
-                r.x[2 * i + 1] = *(const float4*)(p + 4);
+                r.x[2 * i] = as_float4(buf_load16(ar, aoff[i], sa));
+                r.x[2 * i + 1] = as_float4(buf_load16(ar, aoff[i] + 16, sa));
             }
         }
-        int li;
-        const uint8_t* tp = blk_ptr(step, &li);
-        r.w.load(tp, li);
+        // lanes 2 (s % 2) + kbit: 32 lanes further on odd steps
+        r.w.load_buf(wr, woff, soff_w, sw + odd * (QT == MOE_Q8_0 ? q8_lo(32) : q4_nib(32)),
+                     sw + odd * (QT == MOE_Q8_0 ? q8_scale(32) - q8_scale(0) : q4_scale(32) - q4_scale(0)));
     };
     // piece i (0..3) of a step's stores: the thread's i-th activation piece
-    // (zeros for padding rows) and the i-th 8 weights of its block, bf16
+    // and the i-th 8 weights of its block, bf16
     auto store_piece = [&](const WideRaw<QT, AXB>& r, int buf, int i) {
         uint4 v;
         if constexpr (AXB) {
@@ -821,8 +861,6 @@ __device__ void wide_item(const PrefillArgs& a, const TileRec& t, const uint8_t*
             const float4 f0 = r.x[2 * i], f1 = r.x[2 * i + 1];
             v = make_uint4(pack_bf16(f0.x, f0.y), pack_bf16(f0.z, f0.w), pack_bf16(f1.x, f1.y), pack_bf16(f1.z, f1.w));
         }
-        const uint32_t keep = akeep[i] ? 0xFFFFFFFFu : 0u;
-        v = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
         *(uint4*)&L.a[buf][(tid >> 3) + 32 * i][ach] = v;
         *(bf16x8*)&L.b[buf][brow][kbit * kQK + 8 * i] = b_operand<QT>(r.w, i);
     };
