@@ -755,7 +755,9 @@ __global__ __launch_bounds__(256, BIGT ? 2 : (PREC == MOE_PREC_BF16 ? 4 : 3)) vo
 constexpr int WFEAT = 64;             // hidden units per wide gate/up item (both matrices: 128 LDS rows)
 constexpr int WROWS = 128;            // output rows per wide down item
 constexpr int WBK = 64;               // K columns per step: two blocks per row
-constexpr int WST = 3;                // steps of raw loads in registers
+// steps of raw loads in registers: 4 with bf16 activations (244 registers),
+// 3 with fp32 ones (twice the bytes per stage; 4 would spill)
+template <bool AXB> constexpr int WST = AXB ? 4 : 3;
 constexpr int WPITCH = WBK + 8;       // bf16 per LDS row: 144 bytes, conflict-free 16-byte reads
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -890,12 +892,12 @@ __device__ void wide_item(const PrefillArgs& a, const TileRec& t, const uint8_t*
     // written to the other buffer, a quarter beside each quarter of the
     // products (independent work the matrix cores and the vector ALU can
     // overlap), then reloaded with step k + 1 + WST
-    WideRaw<QT, AXB> st[WST];
+    WideRaw<QT, AXB> st[WST<AXB>];
 #pragma unroll
-    for (int q = 0; q < WST; q++) load(st[q], q);
+    for (int q = 0; q < WST<AXB>; q++) load(st[q], q);
 #pragma unroll
     for (int i = 0; i < 4; i++) store_piece(st[0], 0, i);
-    load(st[0], WST);
+    load(st[0], WST<AXB>);
     lds_barrier();
     auto iter = [&](int k, WideRaw<QT, AXB>& r) {
         const int cur = k & 1, nxt = cur ^ 1;
@@ -904,17 +906,18 @@ __device__ void wide_item(const PrefillArgs& a, const TileRec& t, const uint8_t*
             compute_sub(cur, s);
             store_piece(r, nxt, s);
         }
-        load(r, k + 1 + WST);
+        load(r, k + 1 + WST<AXB>);
         lds_barrier();
     };
+    // step k + 1 is in register stage (k + 1) % WST<AXB>
     int k = 0;
-    for (; k + WST <= nk; k += WST) {
-        iter(k, st[1]);
-        iter(k + 1, st[2]);
-        iter(k + 2, st[0]);
+    for (; k + WST<AXB> <= nk; k += WST<AXB>) {
+#pragma unroll
+        for (int q = 0; q < WST<AXB>; q++) iter(k + q, st[(q + 1) % WST<AXB>]);
     }
-    if (k < nk) iter(k, st[1]);
-    if (k + 1 < nk) iter(k + 1, st[2]);
+#pragma unroll
+    for (int q = 0; q + 1 < WST<AXB>; q++)
+        if (k + q < nk) iter(k + q, st[(q + 1) % WST<AXB>]);
     // C element e of product (i, j): row 64 wm + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,
     // column lane % 32 of the j-th B row group
 #pragma unroll
