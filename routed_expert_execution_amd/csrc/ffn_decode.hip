@@ -189,7 +189,7 @@ __device__ __forceinline__ void tile_dots(const Tile<QT> (&t)[M], const float* c
 }
 
 struct DGrid {
-    int n_down;      // down workgroups: d / 16
+    int n_down;      // down workgroups: d / 16, twice that for steps of three or four tokens
     int n_rg;        // gate/up workgroups per unit: d_ff / 16
     int units_max;   // routed units allotted (T * top_k, at most E) + shared
     int gu_tpr;      // gate (or up) tiles per 16 hidden units: d_model / 128
@@ -277,7 +277,7 @@ __device__ void router_role(const FfnArgs& a, const DGrid& g, int r) {
     if (wave >= kRouterRows || e >= a.E) return;
     const uint32_t count = __hip_atomic_load(a.sync + kSyncCount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float* row = a.w_router + (int64_t)e * g.d;
-    float* dst = a.hbuf + (int64_t)launch_parity(count, g.n_down) * g.half + g.lg_off + e;
+    float* dst = a.hbuf + (int64_t)launch_parity(count, g.d / 16) * g.half + g.lg_off + e;
     for (int t = 0; t < a.T; t++) {
         const float v = row_dot(row, a.x, a.x_bf16, t, g.d, lane);
         if (lane < kDecodeCopies)
@@ -462,7 +462,7 @@ __device__ __forceinline__ void gate_up_role(const FfnArgs& a, const DGrid& g, i
     if constexpr (TG == 1) x1.store(a, g.d, L.x[0]);
     lg1.store(a, L.lg);
     lds_barrier();
-    const int par = __builtin_amdgcn_readfirstlane(launch_parity(opaque(count), g.n_down));
+    const int par = __builtin_amdgcn_readfirstlane(launch_parity(opaque(count), g.d / 16));
     // A launch that routes counts its gate/up workgroups in: the down workgroups
     // finish (and so move the launch count) only once all have read it, so no
     // workgroup, not even one left without items, reads the next launch's half.
@@ -627,8 +627,13 @@ struct DownLds {
 };
 
 template <int QT, int PREC, int TG, int DPW>
-__device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int R, unsigned char* lds_raw) {
+__device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int D, unsigned char* lds_raw) {
     DownLds& L = *(DownLds*)lds_raw;
+    // Down workgroup D: rows 16 R .. 16 R + 15 of the output, half hv of the
+    // units (steps of three or four tokens split each row group in two)
+    constexpr int kSplit = TG == kDecodeMaxT ? 2 : 1;
+    const int R = kSplit == 1 ? D : D % (g.d / 16), hv = kSplit == 1 ? 0 : D / (g.d / 16);
+    const bool last = hv == kSplit - 1;  // the half that writes y (and counts the launch done)
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, jb = lane >> 4;
     const bool has_shared = a.shared != nullptr;
@@ -660,24 +665,27 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
     if (threadIdx.x < kDecodeMaxT) L.cnt[threadIdx.x] = 0;
     if (threadIdx.x < kQK) L.zero[threadIdx.x] = 0.f;
     lds_barrier();
-    const int par = __builtin_amdgcn_readfirstlane(launch_parity(opaque(count), g.n_down));
+    const int par = __builtin_amdgcn_readfirstlane(launch_parity(opaque(count), g.d / 16));
     // the arrivals of the next launch start from zero
-    if (R == 0 && threadIdx.x == 0)
+    if (D == 0 && threadIdx.x == 0)
         __hip_atomic_store(a.sync + kSyncArrive + (par ^ 1), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int na_max = g.units_max - (has_shared ? 1 : 0);
     int na = min(max((int)opaque((uint32_t)na_raw), 0), na_max);
     if (a.route != kRoutePlan) {
         // the routing of the step, computed here (workgroup 0 also hands it to the caller)
         const PlanLds P{L.pre.lg, L.ids, L.wbe, L.exp, L.off, L.ent, &L.na};
-        if (!plan_from_logits(a, g, par, g.n_gu_wg + R, P, R == 0) && threadIdx.x == 0) L.flag[0] = 0;
+        if (!plan_from_logits(a, g, par, g.n_gu_wg + D, P, D == 0) && threadIdx.x == 0) L.flag[0] = 0;
         na = min(L.na, na_max);
     }
 
-    // Level 2: this workgroup's W_d tiles of every unit.  Tile p is (unit
-    // p / dn_tpr, column group p % dn_tpr); wave w holds tiles w + 8 i.  Each
-    // unit's payload offset is looked up once (-1: not resident).
+    // Level 2: this workgroup's W_d tiles of every unit of its half.  Tile p
+    // is (unit p / dn_tpr, column group p % dn_tpr); wave w holds tiles
+    // p_lo + w + 8 i.  Each unit's payload offset is looked up once (-1: not
+    // resident).  With two halves, the first takes units [0, ceil(U / 2)).
     const int U = na + (has_shared ? 1 : 0);
-    const int P = U * g.dn_tpr;
+    const int u_mid = (U + 1) / 2;
+    const int u_lo = kSplit == 2 && hv == 1 ? u_mid : 0, u_hi = kSplit == 2 && hv == 0 ? u_mid : U;
+    const int p_lo = u_lo * g.dn_tpr, P = u_hi * g.dn_tpr;
     if (threadIdx.x < U) {
         const int u = threadIdx.x;
         int64_t off = -1;
@@ -704,7 +712,7 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
     Tile<QT> td[DPW];
 #pragma unroll
     for (int i = 0; i < DPW; i++) {
-        const int p = wave + kWaves * i;
+        const int p = p_lo + wave + kWaves * i;
         const uint8_t* tp = p < P ? tile_ptr(p) : nullptr;
         td[i].load(tp ? tp : fallback, lane);
     }
@@ -743,18 +751,18 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
     int sv0[DPW], sv1[DPW], stok[DPW], scol[DPW];
 #pragma unroll
     for (int i = 0; i < DPW; i++) {
-        const int p = wave + kWaves * i;
-        const int u = min(p, max(P - 1, 0)) / g.dn_tpr;
+        const int p = p_lo + wave + kWaves * i;
+        const int u = min(p, max(P - 1, p_lo)) / g.dn_tpr;
         const int v0 = v_begin(u), v1 = min(v_end(u), v0 + kDecodeMaxT);
         int tp = 0;
         for (int v = v0; v < v1; v++) tp |= (L.tok[v] & 3) << (2 * (v - v0));
         sv0[i] = __builtin_amdgcn_readfirstlane(v0);
         sv1[i] = __builtin_amdgcn_readfirstlane(p < P ? v1 : v0);
         stok[i] = __builtin_amdgcn_readfirstlane(tp);
-        scol[i] = __builtin_amdgcn_readfirstlane(min(p, max(P - 1, 0)) - u * g.dn_tpr);
+        scol[i] = __builtin_amdgcn_readfirstlane(min(p, max(P - 1, p_lo)) - u * g.dn_tpr);
     }
 
-    const float* hhalf = a.hbuf + (int64_t)par * g.half + (R % kDecodeCopies) * g.copy;
+    const float* hhalf = a.hbuf + (int64_t)par * g.half + (D % kDecodeCopies) * g.copy;
     const uint64_t t0 = wall_clock64();
     float acc[TG];
 #pragma unroll
@@ -766,7 +774,7 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
     auto group = [&](const int ua) __attribute__((always_inline)) -> int {
         const int va = __builtin_amdgcn_readfirstlane(v_begin(ua));
         int ub = ua + 1;
-        while (ub < U && v_end(ub) - va <= g.nb_rows) ub++;
+        while (ub < u_hi && v_end(ub) - va <= g.nb_rows) ub++;
         ub = __builtin_amdgcn_readfirstlane(ub);
         // (a valid plan never clips)
         const int vb = __builtin_amdgcn_readfirstlane(min(v_end(ub - 1), va + g.nb_rows));
@@ -793,7 +801,7 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         // wave's tiles p = p0, p0 + 8, ... below pe, two loads in flight, the
         // first issued before the wait.
         const int pe = ub * g.dn_tpr;
-        int p0 = kWaves * DPW + wave;
+        int p0 = p_lo + kWaves * DPW + wave;
         if (p0 < ua * g.dn_tpr) p0 += (ua * g.dn_tpr - p0 + kWaves - 1) / kWaves * kWaves;
         p0 = __builtin_amdgcn_readfirstlane(p0);
         auto beyond_ptr = [&](int p) __attribute__((always_inline)) -> const uint8_t* {
@@ -933,8 +941,10 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         __syncthreads();
         return ub;
     };
-    int ua = group(0);
-    while (ua < U) ua = group(ua);
+    if (u_lo < u_hi) {
+        int ua = group(u_lo);
+        while (ua < u_hi) ua = group(ua);
+    }
     // The four lanes of a row, then the waves in order.
 #pragma unroll
     for (int t = 0; t < TG; t++) {
@@ -942,24 +952,64 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         if (jb == 0) L.red[wave][t][n] = s;
     }
     __syncthreads();
-    if (threadIdx.x < 16 * a.T) {
-        const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
-        float y = 0.f;
-        for (int w = 0; w < kWaves; w++) y += L.red[w][t][r];
-        a.y[(int64_t)t * g.d + 16 * R + r] = L.flag[0] && L.cnt[t] == a.k ? y : __uint_as_float(0x7FC00000u);
+    // The first half of a split row group hands its sums to the second with
+    // device scope (a NaN as the canonical NaN, never the pending word); the
+    // second adds them first, then its own: one fixed order.
+    // (the partial rows follow the copies in each half)
+    uint32_t* prow = (uint32_t*)(a.hbuf + (int64_t)par * g.half + kDecodeCopies * g.copy) + 16 * R;
+    const int tq = threadIdx.x >> 4, rq = threadIdx.x & 15;
+    float y = 0.f;
+    if (threadIdx.x < 16 * a.T)
+        for (int w = 0; w < kWaves; w++) y += L.red[w][tq][rq];
+    if (!last) {
+        if (threadIdx.x < 16 * a.T) {
+            const float v = L.flag[0] && y == y ? y : __uint_as_float(0x7FC00000u);
+            __hip_atomic_store(prow + (int64_t)tq * g.d + rq, __float_as_uint(v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+        bool ok = true;
+        if constexpr (kSplit == 2) {
+            float y0 = 0.f;
+            const uint64_t t1 = wall_clock64();
+            for (;;) {
+                int pend = 0;
+                if (threadIdx.x < 16 * a.T) {
+                    const uint32_t v = __hip_atomic_load(prow + (int64_t)tq * g.d + rq, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+                    pend = v == kPending;
+                    y0 = __uint_as_float(v);
+                }
+                if (!__syncthreads_or(pend) && a.wait_ticks >= 0) break;
+                const int expired =
+                    threadIdx.x == 0 && (a.wait_ticks < 0 || (int64_t)(wall_clock64() - t1) > a.wait_ticks);
+                if (__syncthreads_or(expired)) {
+                    if (threadIdx.x == 0) atomicOr(a.err, kErrSync);
+                    ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            y = y0 + y;
+        }
+        if (threadIdx.x < 16 * a.T)
+            a.y[(int64_t)tq * g.d + 16 * R + rq] =
+                ok && L.flag[0] && L.cnt[tq] == a.k ? y : __uint_as_float(0x7FC00000u);
     }
     // This workgroup's share of the other half back to pending for the next
     // launch (no one uses that half during this one).  Done last: a store loop
     // before the tile loads made them wait for every earlier load.
     {
         float* nxt = a.hbuf + (int64_t)(par ^ 1) * g.half;
-        const int64_t r0 = (int64_t)R * g.reset_per;
+        const int64_t r0 = (int64_t)D * g.reset_per;
         for (int j = threadIdx.x; j < g.reset_per; j += kThreads)
             if (r0 + j < g.half) nxt[r0 + j] = __uint_as_float(kPending);
     }
     // This launch is done with its half: count it (no return needed), once every
-    // gate/up workgroup of a launch that routes has arrived.
-    if (threadIdx.x == 0) {
+    // gate/up workgroup of a launch that routes has arrived.  Only the row
+    // groups' last halves count, so that a launch moves the count by d / 16
+    // whatever its token count, and a last half finishes only after its first.
+    if (threadIdx.x == 0 && last) {
         if (a.route == kRouteRouter && (a.wait_ticks < 0 || arrived0 < (uint32_t)g.n_gu_wg)) {
             const uint64_t t1 = wall_clock64();
             while (a.wait_ticks < 0 ||
@@ -1072,7 +1122,10 @@ hipError_t launch_ffn_decode(const Geom& geo, const FfnArgs& a, int prec, hipStr
     if (a.T < 1 || a.T > kDecodeMaxT || a.E > kMaxE || a.k > 32 || geo.d > kMaxD) return hipErrorInvalidValue;
     DGrid g{};
     g.units_max = min(a.T * a.k, a.E) + (a.shared ? 1 : 0);
-    g.n_down = geo.d / 16;
+    // Steps of three or four tokens (the four-token kernel; about 20 units of
+    // Q4_0 products per row group) split each row group's units over two
+    // down workgroups.
+    g.n_down = geo.d / 16 * (a.T > 2 ? 2 : 1);
     g.n_rg = geo.f / 16;
     g.gu_tpr = geo.nb_d / 4;
     g.dn_tpr = geo.nb_f / 4;
@@ -1081,7 +1134,7 @@ hipError_t launch_ffn_decode(const Geom& geo, const FfnArgs& a, int prec, hipStr
     g.tile_bytes = geo.tile_bytes;
     g.down_off = 2 * geo.gu_tiles * geo.tile_bytes;
     g.nb_rows = kHCap / (4 * geo.f);
-    g.half = decode_half_floats(a.k, geo.f, a.E);
+    g.half = decode_half_floats(a.k, geo.f, a.E, geo.d);
     g.copy = decode_copy_floats(a.k, geo.f, a.E);
     g.lg_off = decode_h_rows_floats(a.k, geo.f);
     g.reset_per = (int)((g.half + g.n_down - 1) / g.n_down);

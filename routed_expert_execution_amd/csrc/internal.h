@@ -148,11 +148,15 @@ __host__ __device__ inline int64_t decode_h_rows_floats(int k, int f) { return (
 __host__ __device__ inline int64_t decode_copy_floats(int k, int f, int E) {
     return (decode_h_rows_floats(k, f) + (int64_t)kDecodeMaxT * E + 1023) / 1024 * 1024;
 }
-__host__ __device__ inline int64_t decode_half_floats(int k, int f, int E) {
-    return kDecodeCopies * decode_copy_floats(k, f, E);
+// A half: the copies, then one copy of partial output rows (T x d) that the
+// first down workgroup of a split row group hands to the second.
+__host__ __device__ inline int64_t decode_half_floats(int k, int f, int E, int d) {
+    return kDecodeCopies * decode_copy_floats(k, f, E) + ((int64_t)kDecodeMaxT * d + 1023) / 1024 * 1024;
 }
 // Floats of the whole decode workspace (both halves).
-__host__ __device__ inline int64_t decode_h_floats(int k, int f, int E) { return 2 * decode_half_floats(k, f, E); }
+__host__ __device__ inline int64_t decode_h_floats(int k, int f, int E, int d) {
+    return 2 * decode_half_floats(k, f, E, d);
+}
 
 hipError_t launch_ffn_decode(const Geom& g, const FfnArgs& a, int prec, hipStream_t s);
 

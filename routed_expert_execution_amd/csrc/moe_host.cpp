@@ -403,7 +403,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         const int64_t T = cfg->max_tokens;
         if (hipMalloc(&c->pt, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->err_word, sizeof(int)) != hipSuccess) return cleanup(MOE_ENOMEM);
-        if (hipMalloc(&c->hbuf, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff, cfg->n_experts)) != hipSuccess)
+        if (hipMalloc(&c->hbuf, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff, cfg->n_experts, cfg->d_model)) != hipSuccess)
             return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->sync, sizeof(uint32_t) * moe::kSyncInts) != hipSuccess) return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->logits_ws, sizeof(float) * (size_t)T * cfg->n_experts) != hipSuccess)
@@ -422,7 +422,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         if (hipMemset(c->pt, 0xFF, sizeof(int32_t) * n_keys) != hipSuccess) return cleanup(MOE_EHIP);
         if (hipMemset(c->err_word, 0, sizeof(int)) != hipSuccess) return cleanup(MOE_EHIP);
         if (hipMemset(c->sync, 0, sizeof(uint32_t) * moe::kSyncInts) != hipSuccess) return cleanup(MOE_EHIP);
-        if (hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff, cfg->n_experts)) != hipSuccess)
+        if (hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff, cfg->n_experts, cfg->d_model)) != hipSuccess)
             return cleanup(MOE_EHIP);
         if (hipEventCreateWithFlags(&c->release_ev, hipEventDisableTiming) != hipSuccess) return cleanup(MOE_EHIP);
         if (hipHostMalloc((void**)&c->hmirror,
@@ -1222,7 +1222,7 @@ moe_status moe_check(moe_ctx* c, moe_stream stream) {
         // after a timed-out wait the workspace halves may hold rows of the wrong
         // launch: start both afresh (pending) with the count at zero
         HIP_TRY(c, hipMemset(c->sync, 0, sizeof(uint32_t) * moe::kSyncInts));
-        HIP_TRY(c, hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(c->cfg.top_k, c->cfg.d_ff, c->cfg.n_experts)));
+        HIP_TRY(c, hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(c->cfg.top_k, c->cfg.d_ff, c->cfg.n_experts, c->cfg.d_model)));
         HIP_TRY(c, hipDeviceSynchronize());
         return fail(c, MOE_ETIMEOUT, "a decode workgroup timed out waiting for the hidden rows or the logits (error word 0x%x)", w);
     }

@@ -300,6 +300,88 @@ def test_ffn_decode_wide_topk_parity(k, T):
     assert np.isfinite(y).all() and err <= FFN_TOL
 
 
+@pytest.mark.parametrize("name", ["mtp", "tiny"])
+def test_decode_mixed_token_counts_share_one_workspace(name):
+    """Steps of 4, 1, 3, 2, 4, 1, 3, 2 tokens on one context (one hand-off
+    workspace and launch count; steps of three or four tokens split each row
+    group's down work over two workgroups, the others do not): every output
+    matches its reference and repeats bit for bit when its step comes again."""
+    wl = synth.workload(name)
+    E, k, d, f = wl["E"], wl["k"], wl["d"], wl["f"]
+    Ts = [4, 1, 3, 2]
+    steps = {}
+    used = set()
+    for T in Ts:
+        x = synth.activations(wl["seed"], T, d, wl["x_dtype"], 50 + T)
+        if name == "tiny":
+            lg = oracle.router_logits(oracle.x_to_f64(x, wl["x_dtype"]), synth.router_weights(wl["seed"], E, d))
+        else:
+            lg = synth.mtp_logits(wl["seed"], 50 + T, T, E, k, wl.get("p_shared_route", 0.5))
+        ids, w = oracle.topk(lg, k)
+        steps[T] = (x, ids, w)
+        used |= set(ids.reshape(-1).tolist())
+    used = sorted(used)
+    recs = {e: synth.expert_record(wl["seed"], 0, e, wl["qtype"], d, f) for e in used}
+    shared = synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True) if wl["shared"] else None
+    ctx = H.make_ctx(wl, n_slots=len(used), max_tokens=4)
+    for i, e in enumerate(used):
+        H.put_expert(ctx, i, recs[e])
+        moe.moe_slot_bind(ctx, 0, e, i)
+    sh_dev = H.device_payload(ctx, shared) if shared is not None else None
+    records = [recs.get(e) for e in range(E)]
+    dev, refs = {}, {}
+    for T, (x, ids, w) in steps.items():
+        plan = moe.Plan(ctx, T)
+        ids_dev = torch.from_numpy(ids).cuda()
+        moe.moe_plan_union(ctx, ids_dev, plan)
+        dev[T] = (H.torch_x(x, wl["x_dtype"]), plan, torch.from_numpy(w).cuda())
+        refs[T] = oracle.moe_layer(wl["qtype"], oracle.PREC_F32, records, shared, d, f,
+                                   oracle.x_to_f64(x, wl["x_dtype"]), ids, w)
+    first = {}
+    for T in Ts + Ts:
+        _say("mixed", name, T)
+        xd, plan, wd = dev[T]
+        y = torch.full((T, d), float("nan"), dtype=torch.float32, device="cuda")
+        moe.moe_expert_ffn(ctx, 0, xd, plan, wd, y, shared_payload=sh_dev, prec=oracle.PREC_F32)
+        torch.cuda.synchronize()
+        y = y.cpu().numpy()
+        assert moe.moe_check(ctx) == moe.MOE_OK
+        assert np.isfinite(y).all() and H.max_rel_row_err(y, refs[T]) <= FFN_TOL
+        if T in first:
+            assert np.array_equal(y.view(np.uint32), first[T].view(np.uint32))
+        else:
+            first[T] = y
+
+
+@pytest.mark.parametrize("T,shared", [(4, False), (3, True), (4, True)])
+def test_decode_split_down_with_one_or_two_units(T, shared):
+    """Every token of a three- or four-token step picks the same single expert
+    (top-1): one unit, or two with the shared expert, so a row group's second
+    down workgroup has no unit (or one) of its own."""
+    _say("one unit", T, shared)
+    wl = dict(synth.workload("tiny"), k=1, shared=shared)
+    d, f = wl["d"], wl["f"]
+    x = synth.activations(wl["seed"], T, d, wl["x_dtype"], 31)
+    ids = np.full((T, 1), 5, dtype=np.int32)
+    w = np.ones((T, 1), dtype=np.float32)
+    rec = synth.expert_record(wl["seed"], 0, 5, wl["qtype"], d, f)
+    sh = synth.expert_record(wl["seed"], 0, 0, wl["qtype"], d, f, shared=True) if shared else None
+    ctx = H.make_ctx(wl, n_slots=1, max_tokens=4)
+    H.put_expert(ctx, 0, rec)
+    moe.moe_slot_bind(ctx, 0, 5, 0)
+    plan = moe.Plan(ctx, T)
+    moe.moe_plan_union(ctx, torch.from_numpy(ids).cuda(), plan)
+    y = torch.full((T, d), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn(ctx, 0, H.torch_x(x, wl["x_dtype"]), plan, torch.from_numpy(w).cuda(), y,
+                       shared_payload=H.device_payload(ctx, sh) if shared else None, prec=oracle.PREC_F32)
+    torch.cuda.synchronize()
+    assert moe.moe_check(ctx) == moe.MOE_OK
+    records = [rec if e == 5 else None for e in range(wl["E"])]
+    ref = oracle.moe_layer(wl["qtype"], oracle.PREC_F32, records, sh, d, f, oracle.x_to_f64(x, wl["x_dtype"]), ids, w)
+    y = y.cpu().numpy()
+    assert np.isfinite(y).all() and H.max_rel_row_err(y, ref) <= FFN_TOL
+
+
 @pytest.mark.parametrize("name,T", [("decode", 1), ("mtp", 4)])
 def test_decode_alternating_inputs_see_fresh_hidden_rows(name, T):
     """Launches alternating between two activation sets on one context (same
@@ -325,12 +407,15 @@ def test_decode_alternating_inputs_see_fresh_hidden_rows(name, T):
     assert moe.moe_check(s.ctx) == moe.MOE_OK
 
 
-def test_decode_wait_timeout_fails_closed_and_recovers(monkeypatch):
+@pytest.mark.parametrize("name,T", [("decode", 1), ("mtp", 4), ("tiny", 3)])
+def test_decode_wait_timeout_fails_closed_and_recovers(monkeypatch, name, T):
     """A negative wait bound (set from the host) makes every down workgroup give up
-    at its first check: the launch still completes, rows whose wait ran out are
-    NaN, moe_check reports MOE_ETIMEOUT and resets the hand-off workspace, and
-    the next launches are exact again."""
-    s = Step("decode", 1, 0)
+    at its first check (with three or four tokens also the wait of a row
+    group's second half for the first half's sums): the launch still
+    completes, rows whose wait ran out are NaN, moe_check reports MOE_ETIMEOUT
+    and resets the hand-off workspace, and the next launches are exact again."""
+    _say("timeout", name, T)
+    s = Step(name, T, 0)
     s.place()
     ref = s.reference()
     monkeypatch.setenv("MOE_SYNC_WAIT_TICKS", "-1")
