@@ -681,9 +681,11 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
     // Level 2: this workgroup's W_d tiles of every unit of its half.  Tile p
     // is (unit p / dn_tpr, column group p % dn_tpr); wave w holds tiles
     // p_lo + w + 8 i.  Each unit's payload offset is looked up once (-1: not
-    // resident).  With two halves, the first takes units [0, ceil(U / 2)).
+    // resident).  With two halves, the first takes units [0, ceil(0.55 U)):
+    // the later units' hidden rows come last (their gate/up items are last),
+    // so the second half, which also waits for the first's sums, gets fewer.
     const int U = na + (has_shared ? 1 : 0);
-    const int u_mid = (U + 1) / 2;
+    const int u_mid = (11 * U + 19) / 20;
     const int u_lo = kSplit == 2 && hv == 1 ? u_mid : 0, u_hi = kSplit == 2 && hv == 0 ? u_mid : U;
     const int p_lo = u_lo * g.dn_tpr, P = u_hi * g.dn_tpr;
     if (threadIdx.x < U) {
