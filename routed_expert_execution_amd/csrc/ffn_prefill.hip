@@ -161,7 +161,8 @@ __global__ __launch_bounds__(1024) void schedule_kernel(PrefillArgs a, int prec)
                 if (in.e >= 0 && in.e < a.E && in.sl >= 0 && in.sl < a.n_slots) slot = in.sl;
                 if (slot == kUnmapped) atomicOr(a.err, kErrMiss);
             }
-            if (prec == MOE_PREC_BF16 && M >= a.wide_min) tw = (M + WIDE - 1) / WIDE;
+            // (a call of fewer than wide_min tokens launches no 128-token tiles)
+            if (prec == MOE_PREC_BF16 && M >= a.wide_min && a.T >= a.wide_min) tw = (M + WIDE - 1) / WIDE;
             else if (prec == MOE_PREC_BF16 && M >= a.gemm_min) tb = (M + BIG - 1) / BIG;
             else ts = (M + SMALL - 1) / SMALL;
         }
@@ -1036,19 +1037,22 @@ hipError_t launch_qp(const PrefillArgs& a, int big_tiles, int small_tiles, int w
     const int gf = (a.f + COLS - 1) / COLS, gd = a.d / COLS;
     constexpr bool BF = PREC == MOE_PREC_BF16;  // 64-token tiles only in bf16 mode
     if constexpr (BF) {
-        // The two tile sizes are independent chains (disjoint buckets: their own
-        // hidden and partial rows): the 64-token one on the auxiliary stream, so
-        // that the two share the GPU instead of running one after the other.
-        const bool two = st.aux != nullptr && big_tiles + wide_tiles > 0;
+        // The tile sizes are independent chains (disjoint buckets: their own
+        // hidden and partial rows): the 64-token one on the auxiliary stream,
+        // the 128- and 16-token ones on the caller's, so that the two streams
+        // share the GPU instead of running one after the other.  (Most calls
+        // have work in only one or two sizes; a size's empty launches then run
+        // beside the other stream's work.)
+        const bool two = st.aux != nullptr && big_tiles > 0;
         const hipStream_t sb = two ? st.aux : s;
         if (two && e == hipSuccess) e = hipEventRecord(st.fork, s);
         if (two && e == hipSuccess) e = hipStreamWaitEvent(sb, st.fork, 0);
-        if (e == hipSuccess)
-            e = launch_wide(prefill_wide_kernel<QT, XB, true>, (int64_t)wide_tiles * (a.f / WFEAT), a, sb);
-        if (e == hipSuccess)
-            e = launch_wide(prefill_wide_kernel<QT, XB, false>, (int64_t)wide_tiles * (a.d / WROWS), a, sb);
         if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, true>, (int64_t)big_tiles * gf, a, sb);
         if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, true>, (int64_t)big_tiles * gd, a, sb);
+        if (e == hipSuccess)
+            e = launch_wide(prefill_wide_kernel<QT, XB, true>, (int64_t)wide_tiles * (a.f / WFEAT), a, s);
+        if (e == hipSuccess)
+            e = launch_wide(prefill_wide_kernel<QT, XB, false>, (int64_t)wide_tiles * (a.d / WROWS), a, s);
         if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, false>, (int64_t)small_tiles * gf, a, s);
         if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, false>, (int64_t)small_tiles * gd, a, s);
         if (two && e == hipSuccess) e = hipEventRecord(st.join, sb);
@@ -1093,6 +1097,9 @@ hipError_t launch_ffn_prefill(const PrefillArgs& a, int prec, const PrefillStrea
     if (a.d % COLS || a.f % 16) return hipErrorInvalidValue;
     int bt, st, wt;
     prefill_max_tiles(a.T, a.k, a.E, a.shared != nullptr, &bt, &st, &wt);
+    // A bucket holds at most T tokens (a token picks an expert once; the shared
+    // expert's bucket is all T): below wide_min no 128-token tile can exist.
+    if (a.T < a.wide_min) wt = 0;
     const bool xb = a.x_bf16 != 0, bf = prec == MOE_PREC_BF16;
     if (a.g.qtype == MOE_Q8_0) {
         if (bf) return xb ? launch_qp<MOE_Q8_0, MOE_PREC_BF16, true>(a, bt, st, wt, s)
