@@ -54,11 +54,21 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_decode_traffic.json")
 CAL_BYTES = 64 << 20  # the plain device-to-device copy each run makes once, for counter calibration
 
 
+def _code_text(path: str) -> str:
+    """A source file without its comments and blank space: what the compiler
+    sees, so that editing a comment keeps the counters taken on the code."""
+    import re
+    s = open(path, encoding="utf-8").read()
+    s = re.sub(r"/\*.*?\*/", " ", s, flags=re.S)
+    s = re.sub(r"//[^\n]*", "", s)
+    return "\n".join(" ".join(line.split()) for line in s.splitlines() if line.strip())
+
+
 def _kernel_source_digest(workload: str = "decode") -> str:
     h = hashlib.sha256()
     main = "ffn_prefill.hip" if workload == "prefill" else "ffn_decode.hip"
     for f in (main, "device_util.h", "internal.h", "route_device.h"):
-        h.update(open(os.path.join(ROOT, "routed_expert_execution_amd", "csrc", f), "rb").read())
+        h.update(_code_text(os.path.join(ROOT, "routed_expert_execution_amd", "csrc", f)).encode())
     return h.hexdigest()[:16]
 
 

@@ -24,7 +24,10 @@
 //     y[t, rows] = sum over t's hidden rows of w * (W_d[rows] h)
 //     in one fixed order that depends only on expert ids and ranks, never on
 //     slots: per lane over its tiles in order, then the four lanes of a row,
-//     then the waves.
+//     then the waves.  Steps of three or four tokens give each 16 output rows
+//     two down workgroups, the first taking the first units in plan order and
+//     the second the rest; the second adds the first's sums (handed over like
+//     the hidden rows), then its own.
 //
 // A launch that routes takes the caller's logits, or computes them: router
 // workgroups, the first in dispatch order, compute one router row per wave and
@@ -47,9 +50,10 @@
 // readers load half p with device-scope loads until no "pending" word
 // 0xFFFFFFFF (a NaN no arithmetic on finite values produces) is left, and the
 // down workgroups refill half p ^ 1 with it for the next launch.  p is the
-// parity of the launch count, a device word each down workgroup increments
-// (without return) when it is done: it reaches the next launch's value only
-// once every down workgroup of this one has read it.  Every gate/up workgroup
+// parity of the launch count, a device word that each down workgroup writing
+// output rows increments (without return) when it is done, d/16 per launch: it
+// reaches the next launch's value only once every down workgroup of this one
+// has read it (a row group's first workgroup finishes before its second).  Every gate/up workgroup
 // with rows to write has read it before any down workgroup can finish; in a
 // launch that routes from x, where a gate/up workgroup reads logits before it
 // knows whether it has items, the gate/up workgroups also count their arrival

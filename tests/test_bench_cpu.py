@@ -72,3 +72,14 @@ def test_traffic_from_counter_runs(tmp_path, monkeypatch, workload):
     r["kernel_source_sha"] = "0" * 16
     json.dump({workload: r}, open(tf, "w"))
     assert bench._traffic(workload) is None
+
+
+def test_source_digest_ignores_comments_only(tmp_path):
+    """The traffic file is keyed by the kernel code: comments and blank space
+    do not change the key, a changed statement does."""
+    a, b, c = tmp_path / "a.hip", tmp_path / "b.hip", tmp_path / "c.hip"
+    a.write_text("int f(int x) {\n    return x + 1;  // one more\n}\n")
+    b.write_text("/* a note\n   over lines */\nint f(int x) {\n\n    return x + 1;\n}\n")
+    c.write_text("int f(int x) {\n    return x + 2;\n}\n")
+    assert bench._code_text(str(a)) == bench._code_text(str(b))
+    assert bench._code_text(str(a)) != bench._code_text(str(c))
