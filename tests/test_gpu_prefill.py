@@ -124,6 +124,29 @@ def test_prefill_tiny_shape(T, prec, gemm_min, wide_min):
     _say("  buckets", sorted(c.bucket_sizes()[c.used].tolist()), st)
 
 
+@pytest.mark.parametrize("T,wide_min", [(24, 40), (48, 40)])
+def test_prefill_bucket_larger_than_chunk(T, wide_min):
+    """Both ranks of every token name the same expert (a plan the C ABI accepts),
+    so its bucket holds 2 T entries, at least wide_min.  A call of fewer than
+    wide_min tokens launches no 128-token tiles, and its schedule must not
+    make any (the bucket goes to 64-token tiles); a call of at least wide_min
+    tokens takes them.  Both match the oracle on every row."""
+    wl = dict(synth.workload("tiny"), shared=True)
+    lg = synth.zipf_gumbel_logits(wl["seed"] + T, T, wl["E"], 1.1)
+    _say("prefill duplicate ranks", T, wide_min)
+    c = Chunk(wl, T, lg, oracle.PREC_BF16, 16, wide_min=wide_min)
+    c.place(list(range(len(c.used))))
+    e = c.used[0]
+    c.ids = np.full((T, wl["k"]), e, dtype=np.int32)
+    c.w = np.full((T, wl["k"]), 1.0 / wl["k"], dtype=np.float32)
+    c.w_dev = torch.from_numpy(c.w).cuda()
+    c.plan = moe.Plan(c.ctx, T)
+    moe.moe_plan_union(c.ctx, torch.from_numpy(c.ids).cuda(), c.plan)
+    y = c.run()
+    st = c.verify(y, np.arange(T))
+    _say("  ", st)
+
+
 @pytest.mark.parametrize("T,prec,wide_min", [(24, oracle.PREC_BF16, None), (24, oracle.PREC_F32, None),
                                              (24, oracle.PREC_BF16, 2)])
 def test_prefill_mtp_q4(T, prec, wide_min):
