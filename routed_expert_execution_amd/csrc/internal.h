@@ -140,9 +140,10 @@ constexpr int kSyncInts = 32, kSyncCount = 0, kSyncArrive = 16;  // one 128-byte
 // A workspace half holds kDecodeCopies copies of the same words, each starting
 // on its own 4 KiB: every value is stored into all of them and each reader reads
 // one, so that hundreds of workgroups reading the same few KiB spread over
-// several memory channels instead of queueing on one (4 measured best of 2, 4,
-// 6, 8 and 16 for the one- and four-token steps).
-constexpr int kDecodeCopies = 4;
+// several memory channels instead of queueing on one (8 measured best of 4, 8
+// and 16 for the one- and four-token steps, once the four-token step split its
+// down work over twice the workgroups; 4 before).
+constexpr int kDecodeCopies = 8;
 // Floats of one copy: hidden rows for top_k and d_ff, then the logits of E experts.
 __host__ __device__ inline int64_t decode_h_rows_floats(int k, int f) { return (int64_t)kDecodeMaxT * (k + 1) * f; }
 __host__ __device__ inline int64_t decode_copy_floats(int k, int f, int E) {
