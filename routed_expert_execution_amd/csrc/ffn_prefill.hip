@@ -1038,23 +1038,29 @@ hipError_t launch_qp(const PrefillArgs& a, int big_tiles, int small_tiles, int w
     constexpr bool BF = PREC == MOE_PREC_BF16;  // 64-token tiles only in bf16 mode
     if constexpr (BF) {
         // The tile sizes are independent chains (disjoint buckets: their own
-        // hidden and partial rows): the 64-token one on the auxiliary stream,
-        // the 128- and 16-token ones on the caller's, so that the two streams
-        // share the GPU instead of running one after the other.  (Most calls
-        // have work in only one or two sizes; a size's empty launches then run
-        // beside the other stream's work.)
-        const bool two = st.aux != nullptr && big_tiles > 0;
+        // hidden and partial rows) on two streams, so that they share the GPU
+        // instead of running one after the other.  The chain expected to be
+        // longer runs on the caller's stream, right after the schedule; the
+        // other waits for the fork.  With a mean routed bucket of at least 64
+        // tokens most rows are in 64- or 128-token tiles; below, in 16-token
+        // tiles.  (A size with no tiles in a call still launches, beside the
+        // other stream's work.)
+        const int64_t rows = (int64_t)a.T * a.k;
+        const bool big_main = rows >= (int64_t)BIG * std::min<int64_t>(rows, a.E);
+        const bool two = st.aux != nullptr;
         const hipStream_t sb = two ? st.aux : s;
+        const hipStream_t s_big = big_main ? s : sb, s_small = big_main ? sb : s;
         if (two && e == hipSuccess) e = hipEventRecord(st.fork, s);
         if (two && e == hipSuccess) e = hipStreamWaitEvent(sb, st.fork, 0);
-        if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, true>, (int64_t)big_tiles * gf, a, sb);
-        if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, true>, (int64_t)big_tiles * gd, a, sb);
         if (e == hipSuccess)
-            e = launch_wide(prefill_wide_kernel<QT, XB, true>, (int64_t)wide_tiles * (a.f / WFEAT), a, s);
+            e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, false>, (int64_t)small_tiles * gf, a, s_small);
+        if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, false>, (int64_t)small_tiles * gd, a, s_small);
+        if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, true>, (int64_t)big_tiles * gf, a, s_big);
+        if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, true>, (int64_t)big_tiles * gd, a, s_big);
         if (e == hipSuccess)
-            e = launch_wide(prefill_wide_kernel<QT, XB, false>, (int64_t)wide_tiles * (a.d / WROWS), a, s);
-        if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, false>, (int64_t)small_tiles * gf, a, s);
-        if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, false>, (int64_t)small_tiles * gd, a, s);
+            e = launch_wide(prefill_wide_kernel<QT, XB, true>, (int64_t)wide_tiles * (a.f / WFEAT), a, s_big);
+        if (e == hipSuccess)
+            e = launch_wide(prefill_wide_kernel<QT, XB, false>, (int64_t)wide_tiles * (a.d / WROWS), a, s_big);
         if (two && e == hipSuccess) e = hipEventRecord(st.join, sb);
         if (two && e == hipSuccess) e = hipStreamWaitEvent(s, st.join, 0);
     } else {
