@@ -1039,28 +1039,34 @@ hipError_t launch_qp(const PrefillArgs& a, int big_tiles, int small_tiles, int w
     if constexpr (BF) {
         // The tile sizes are independent chains (disjoint buckets: their own
         // hidden and partial rows) on two streams, so that they share the GPU
-        // instead of running one after the other.  The chain expected to be
-        // longer runs on the caller's stream, right after the schedule; the
-        // other waits for the fork.  With a mean routed bucket of at least 64
-        // tokens most rows are in 64- or 128-token tiles; below, in 16-token
-        // tiles.  (A size with no tiles in a call still launches, beside the
-        // other stream's work.)
-        const int64_t rows = (int64_t)a.T * a.k;
-        const bool big_main = rows >= (int64_t)BIG * std::min<int64_t>(rows, a.E);
+        // instead of running one after the other.  The chains expected to be
+        // busy run on the caller's stream, right after the schedule; the
+        // others wait for the fork on the auxiliary stream.  A chain with no
+        // tiles in a call still launches: there it runs beside the busy ones.
+        // Expected from the mean routed bucket, T k / min(T k, E): 128-token
+        // tiles if it reaches wide_min, 64-token tiles if it reaches 64
+        // tokens, else 16-token tiles.
+        const int64_t rows = (int64_t)a.T * a.k, units = std::min<int64_t>(rows, a.E);
+        const bool wide_main = rows >= (int64_t)a.wide_min * units;
+        const bool big_main = rows >= (int64_t)BIG * units;
         const bool two = st.aux != nullptr;
         const hipStream_t sb = two ? st.aux : s;
-        const hipStream_t s_big = big_main ? s : sb, s_small = big_main ? sb : s;
+        const hipStream_t s_wide = wide_main ? s : sb, s_big = big_main ? s : sb, s_small = big_main ? sb : s;
         if (two && e == hipSuccess) e = hipEventRecord(st.fork, s);
         if (two && e == hipSuccess) e = hipStreamWaitEvent(sb, st.fork, 0);
+        if (e == hipSuccess && wide_main)
+            e = launch_wide(prefill_wide_kernel<QT, XB, true>, (int64_t)wide_tiles * (a.f / WFEAT), a, s_wide);
+        if (e == hipSuccess && wide_main)
+            e = launch_wide(prefill_wide_kernel<QT, XB, false>, (int64_t)wide_tiles * (a.d / WROWS), a, s_wide);
         if (e == hipSuccess)
             e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, false>, (int64_t)small_tiles * gf, a, s_small);
         if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, false>, (int64_t)small_tiles * gd, a, s_small);
         if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, true>, (int64_t)big_tiles * gf, a, s_big);
         if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, true>, (int64_t)big_tiles * gd, a, s_big);
-        if (e == hipSuccess)
-            e = launch_wide(prefill_wide_kernel<QT, XB, true>, (int64_t)wide_tiles * (a.f / WFEAT), a, s_big);
-        if (e == hipSuccess)
-            e = launch_wide(prefill_wide_kernel<QT, XB, false>, (int64_t)wide_tiles * (a.d / WROWS), a, s_big);
+        if (e == hipSuccess && !wide_main)
+            e = launch_wide(prefill_wide_kernel<QT, XB, true>, (int64_t)wide_tiles * (a.f / WFEAT), a, s_wide);
+        if (e == hipSuccess && !wide_main)
+            e = launch_wide(prefill_wide_kernel<QT, XB, false>, (int64_t)wide_tiles * (a.d / WROWS), a, s_wide);
         if (two && e == hipSuccess) e = hipEventRecord(st.join, sb);
         if (two && e == hipSuccess) e = hipStreamWaitEvent(s, st.join, 0);
     } else {
