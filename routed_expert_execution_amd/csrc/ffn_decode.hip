@@ -307,10 +307,14 @@ __device__ bool plan_from_logits(const FfnArgs& a, const DGrid& g, int par, int 
         const uint64_t t0 = wall_clock64();
         for (;;) {
             int pend = 0;
+            // (the second word only where there is one: a clamped duplicate
+            // would add requests to the few lines every workgroup polls)
             for (int i = threadIdx.x; i < n; i += 2 * kThreads) {
-                const int i2 = min(i + kThreads, n - 1);
+                const bool two = i + kThreads < n;
+                const int i2 = two ? i + kThreads : i;
                 const uint32_t v0 = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint32_t v1 = __hip_atomic_load(src + i2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint32_t v1 =
+                    two ? __hip_atomic_load(src + i2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : v0;
                 pend |= (v0 == kPending) | (v1 == kPending);
                 P.lg[i] = __uint_as_float(v0);
                 P.lg[i2] = __uint_as_float(v1);
