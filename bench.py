@@ -450,6 +450,9 @@ def run_stack(args, torch, moe, synth) -> int:
     if args.prefetch and args.staging != "native":
         print("--prefetch needs --staging native (moe_prefetch_next follows moe_route_pull)", file=sys.stderr)
         return 2
+    if args.split and args.staging != "native":
+        print("--split needs --staging native (moe_expert_ffn_split follows moe_route_pull)", file=sys.stderr)
+        return 2
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     n_tok = args.warmup + args.steps
@@ -487,6 +490,7 @@ def run_stack(args, torch, moe, synth) -> int:
     tables = [moe.payload_table(ctx, [packs[a][e] for e in range(E)]) for a in range(n_alias)]
     sides = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.fill_streams))]
     side = sides[0]
+    split_side = torch.cuda.Stream(device=dev)  # the resident units of a split layer
     stream = torch.cuda.current_stream(dev)
     ffn_ev = []
     pull_ev = []  # (event before the pull, misses): the pull ends where the FFN's first event is
@@ -542,7 +546,11 @@ def run_stack(args, torch, moe, synth) -> int:
                         stream.wait_stream(sd)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            moe.moe_expert_ffn(ctx, l, xs[t, l] if args.fresh_inputs else x, plan, w, y, shared_payload=shared)
+            if args.split:  # the resident units on split_side while the pull runs, the pulled ones after it
+                moe.moe_expert_ffn_split(ctx, l, xs[t, l] if args.fresh_inputs else x, plan, w, y, experts[miss],
+                                         shared_payload=shared, side=split_side, stream=stream)
+            else:
+                moe.moe_expert_ffn(ctx, l, xs[t, l] if args.fresh_inputs else x, plan, w, y, shared_payload=shared)
             if ev:
                 e1.record(stream)
                 ffn_ev.append((e0, e1))
@@ -615,6 +623,8 @@ def run_stack(args, torch, moe, synth) -> int:
                             + ") copied on a side stream while the layer computes" if args.prefetch else "")
                          + (f"; copies alternate over {args.fill_streams} side streams"
                             if args.fill_streams > 1 and args.staging != "pull" else "")
+                         + ("; hit/miss split: moe_expert_ffn_split runs the resident experts on a second "
+                            "stream while the pull runs, the pulled ones after it" if args.split else "")
                          + {"native": "; one moe_route_pull per layer: routing, expert readback through pinned "
                                       "memory, mapping and a pull kernel in one library call",
                             "pull": "; one moe_slot_pull per layer: a kernel on the compute stream copies the misses",
@@ -695,6 +705,9 @@ def main() -> int:
                     help="prefill, bf16 mode: buckets of at least M tokens use 64-token tiles")
     ap.add_argument("--spin-readback", action="store_true",
                     help="stack: poll for the plan readback instead of a blocking synchronise")
+    ap.add_argument("--split", action="store_true",
+                    help="stack: moe_expert_ffn_split instead of moe_expert_ffn (the resident experts on a second "
+                         "stream while the misses are pulled, the pulled ones after)")
     ap.add_argument("--staging", choices=("native", "pull", "stage", "fill"), default="native",
                     help="stack: one moe_route_pull per layer (routing, mapping and pull in one call), "
                          "one moe_slot_pull per layer (kernel copies on the compute stream), one "

@@ -351,6 +351,35 @@ moe_status moe_expert_ffn(moe_ctx* ctx, int32_t layer, const void* x, int32_t x_
                           const moe_plan* plan, const float* topk_w, const void* shared_payload,
                           int32_t prec, float* y, moe_stream stream);
 
+/* Hit/miss split of a one-token step ("Nanite for Experts", §5.5: the experts
+ * already resident run while the missing ones are still being copied in, and
+ * the results are merged into the token's row).  Call it once after each
+ * moe_route_pull, for the same layer and on the same stream (MOE_EINVAL
+ * otherwise), with the experts that call copied in (its experts_out where
+ * miss_out is 1):
+ *   - `side` waits for that call's routing and for fills still pending on
+ *     other streams, then runs the resident units (the shared expert too);
+ *     x, topk_w and plan must be ready by the end of that routing (written on
+ *     its stream before it, or by it);
+ *   - `stream`, after the copies moe_route_pull queued on it, waits for
+ *     `side` and runs the copied units, then merges.
+ * With no miss, or with every unit a miss, or side == stream, it is one
+ * launch on `stream`.  Either way
+ *   y[t] = sum over the units in plan order, the shared expert last, of
+ *          w * (W_d (silu(W_g x) * (W_u x)))
+ * with each unit's term computed by the same code whichever launch takes it,
+ * so y is bitwise the same for any split of the units (and any slot
+ * assignment); it is moe_expert_ffn's result up to summation order, not bit
+ * for bit.  Arguments as moe_expert_ffn, with T = 1 and
+ * (top_k + 1) * d_ff / 128 <= 40 (every down tile of the step in registers),
+ * else MOE_EINVAL.  miss_experts: host [n_miss] expert ids; every expert whose
+ * copy may still be in flight must be listed.  Calls on one context must not
+ * overlap. */
+moe_status moe_expert_ffn_split(moe_ctx* ctx, int32_t layer, const void* x, int32_t x_dtype, int64_t T,
+                                const moe_plan* plan, const float* topk_w, const void* shared_payload,
+                                int32_t prec, const int32_t* miss_experts, int32_t n_miss, float* y,
+                                moe_stream side, moe_stream stream);
+
 /* Bytes of the device array behind moe_expert_ffn_static (one per GPU). */
 #define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 

@@ -218,6 +218,18 @@ __device__ inline const uint8_t* slot_base(const FfnArgs& a, int e, const int* p
 // Launch parity: which workspace half this launch writes.
 __device__ inline int launch_parity(uint32_t count, int n_down) { return (int)((count / (uint32_t)n_down) & 1u); }
 
+// Whether a split launch computes the unit of expert e (-1: the shared
+// expert).  The mask word is picked by comparison, so that the argument array
+// is only ever indexed by constants.
+__device__ inline bool split_takes(const SplitSel& s, int e) {
+    if (s.which == kSplitAll) return true;
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < kSplitMaskWords; j++) word = (e >> 5) == j ? s.miss[j] : word;
+    const bool miss = e >= 0 && ((word >> (e & 31)) & 1u);
+    return s.which == kSplitHits ? !miss : miss;
+}
+
 // ---- routing inside the launch --------------------------------------------------
 
 // Experts a launch that routes takes: kRouteKpl logits per lane of a wave.
@@ -438,8 +450,10 @@ struct GuLds {
 // groups of 16 hidden units of one unit: the shared expert's items come first
 // (they need no routing, so a launch that routes starts them at once), then
 // those of the routed units in plan order.
-template <int QT, int PREC, int TG, int RG, int PPW>
-__device__ __forceinline__ void gate_up_role(const FfnArgs& a, const DGrid& g, int wg, unsigned char* lds_raw) {
+// The split variant (SPLIT) skips the items of the units the launch does not take.
+template <int QT, int PREC, int TG, int RG, int PPW, bool SPLIT>
+__device__ __forceinline__ void gate_up_role(const FfnArgs& a, const DGrid& g, int wg, unsigned char* lds_raw,
+                                             const SplitSel* sel) {
     GuLds<TG, RG>& L = *(GuLds<TG, RG>*)lds_raw;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, jb = lane >> 4;
@@ -493,6 +507,9 @@ __device__ __forceinline__ void gate_up_role(const FfnArgs& a, const DGrid& g, i
         }
         const int ui = routed ? item - S : item;  // item within the routed items, or the shared ones
         const int u = ui / per_unit, rg0 = (ui - u * per_unit) * RG;
+        if constexpr (SPLIT) {
+            if (!split_takes(*sel, routed ? L.exp[u] : -1)) continue;
+        }
         // The slot, then every weight load of the item.  Pair pi is column group
         // pi % gu_tpr of row group rg0 + pi / gu_tpr (gate tile and up tile);
         // lane (n, jb) holds block 4 (pi % gu_tpr) + jb of hidden unit n of that
@@ -634,8 +651,12 @@ struct DownLds {
     };
 };
 
-template <int QT, int PREC, int TG, int DPW>
-__device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int D, unsigned char* lds_raw) {
+// The split variant (SPLIT, one token, every tile in registers) computes each
+// unit's term on its own and merges them at the end; see SplitSel.
+template <int QT, int PREC, int TG, int DPW, bool SPLIT>
+__device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int D, unsigned char* lds_raw,
+                                          const SplitSel* sel) {
+    static_assert(!SPLIT || TG == 1, "the split variant takes one token");
     DownLds& L = *(DownLds*)lds_raw;
     // Down workgroup D: rows 16 R .. 16 R + 15 of the output, half hv of the
     // units (steps of three or four tokens split each row group in two)
@@ -705,6 +726,9 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
             const int slot = (ex >= 0 && ex < a.E) ? L.pre.pts[ex] : -1;
             if (slot >= 0 && slot < a.n_slots) off = (int64_t)slot * a.payload_bytes;
         }
+        if constexpr (SPLIT) {
+            if (!split_takes(*sel, u < na ? L.exp[u] : -1)) off = -3;  // a unit the other launch takes
+        }
         L.uoff[u] = off;
     }
     lds_barrier();
@@ -725,6 +749,15 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         const int p = p_lo + wave + kWaves * i;
         const uint8_t* tp = p < P ? tile_ptr(p) : nullptr;
         td[i].load(tp ? tp : fallback, lane);
+    }
+    // A split launch that merges reads the terms of the units it does not take
+    // (written by the launch before it): thread 16 u + r holds unit u's row r.
+    float pre = 0.f;
+    if constexpr (SPLIT) {
+        const int u = threadIdx.x >> 4;
+        const bool want = sel->which == kSplitMisses && u < U && L.uoff[u] == -3;
+        const int v = u < na ? L.off[min(u, na)] : n_ent;
+        pre = *(want ? sel->part + (int64_t)v * g.d + 16 * R + (threadIdx.x & 15) : sel->part);
     }
     // The arrivals of this launch's gate/up workgroups, read now (they arrive
     // as they start, long before this; the load waits with the tiles') and
@@ -755,6 +788,12 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
     auto v_begin = [&](int u) __attribute__((always_inline)) { return u < na ? L.off[u] : n_ent; };
     auto v_end = [&](int u) __attribute__((always_inline)) { return u < na ? L.off[u + 1] : n_ent + a.T; };
     lds_barrier();
+    if constexpr (SPLIT) {
+        // rows of the units the other launch takes: never written here, never waited for
+        if (threadIdx.x < U && L.uoff[threadIdx.x] == -3)
+            for (int v = v_begin(threadIdx.x); v < v_end(threadIdx.x); v++) L.rdone[v] = 1;
+        lds_barrier();
+    }
     // Per register slot, read before the wait (wave-uniform, so scalar): the
     // unit's rows [sv0, sv1), their tokens (2 bits each; a bucket has at most
     // 4 rows) and the tile's column group.
@@ -767,7 +806,7 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         int tp = 0;
         for (int v = v0; v < v1; v++) tp |= (L.tok[v] & 3) << (2 * (v - v0));
         sv0[i] = __builtin_amdgcn_readfirstlane(v0);
-        sv1[i] = __builtin_amdgcn_readfirstlane(p < P ? v1 : v0);
+        sv1[i] = __builtin_amdgcn_readfirstlane(p < P && !(SPLIT && L.uoff[u] == -3) ? v1 : v0);
         stok[i] = __builtin_amdgcn_readfirstlane(tp);
         scol[i] = __builtin_amdgcn_readfirstlane(min(p, max(P - 1, p_lo)) - u * g.dn_tpr);
     }
@@ -777,6 +816,9 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
     float acc[TG];
 #pragma unroll
     for (int t = 0; t < TG; t++) acc[t] = 0.f;
+    float dv[SPLIT ? DPW : 1];  // split: each register slot's dot, kept apart
+#pragma unroll
+    for (int i = 0; i < (SPLIT ? DPW : 1); i++) dv[i] = 0.f;
     // Groups of units whose hidden rows fit the LDS, in plan order.  The first
     // group is peeled out of the loop: computing on the tiles inside a loop lets
     // the compiler hoist work on their loaded values above it, and so wait for
@@ -854,7 +896,7 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
             } else {
                 for (int i = threadIdx.x; i < n16; i += kThreads) {
                     const uint4 b = *(const uint4*)(L.hs + 4 * i);
-                    const bool used = i < gap0 || i >= gap1;
+                    const bool used = SPLIT ? !L.rdone[va + i / ppr] : i < gap0 || i >= gap1;
                     pend |= used && ((b.x == kPending) | (b.y == kPending) | (b.z == kPending) | (b.w == kPending));
                 }
             }
@@ -884,6 +926,10 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
                     hr[r] = v0 + r < v1 ? L.hs + (v0 + r - va) * g.f + (4 * scol[i] + jb) * kQK : L.zero;
                 float dr[1][TG];
                 tile_dots<QT, PREC, 1, TG, TG == 1 ? 4 : 2>(one, hr, dr);
+                if constexpr (SPLIT) {
+                    dv[i] = dr[0][0];
+                    continue;
+                }
 #pragma unroll
                 for (int r = 0; r < TG; r++) {
                     if (v0 + r >= v1) break;
@@ -955,6 +1001,41 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
         int ua = group(u_lo);
         while (ua < u_hi) ua = group(ua);
     }
+    if constexpr (SPLIT) {
+        // Unit u's term for row r: per tile the row's four lanes, then the
+        // unit's tiles in order, times the routing weight (one fixed order in
+        // either launch).  The staged rows are done with, so the LDS holds the
+        // tile sums [P][16] and then the merged terms [U][16].
+        float* tv = L.hs;
+        float* tu = L.hs + 16 * P;
+#pragma unroll
+        for (int i = 0; i < DPW; i++) {
+            const int p = wave + kWaves * i;
+            const float s = cross_row_sum(dv[i]);
+            if (jb == 0 && p < P) tv[16 * p + n] = s;
+        }
+        __syncthreads();
+        const int u = threadIdx.x >> 4, r = threadIdx.x & 15;
+        const bool ok = L.flag[0];
+        if (u < U) {
+            float t = 0.f;
+            for (int c = 0; c < g.dn_tpr; c++) t += tv[16 * (u * g.dn_tpr + c) + r];
+            t *= L.w[v_begin(u)];
+            const bool mine = L.uoff[u] != -3;
+            if (sel->which == kSplitHits) {
+                if (mine)
+                    sel->part[(int64_t)v_begin(u) * g.d + 16 * R + r] = ok ? t : __uint_as_float(0x7FC00000u);
+            } else {
+                tu[16 * u + r] = mine ? t : pre;
+            }
+        }
+        __syncthreads();
+        if (sel->which != kSplitHits && threadIdx.x < 16) {
+            float y = 0.f;
+            for (int q = 0; q < U; q++) y += tu[16 * q + r];
+            a.y[16 * R + r] = ok && L.cnt[0] == a.k ? y : __uint_as_float(0x7FC00000u);
+        }
+    } else {
     // The four lanes of a row, then the waves in order.
 #pragma unroll
     for (int t = 0; t < TG; t++) {
@@ -1006,6 +1087,7 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
             a.y[(int64_t)tq * g.d + 16 * R + rq] =
                 ok && L.flag[0] && L.cnt[tq] == a.k ? y : __uint_as_float(0x7FC00000u);
     }
+    }
     // This workgroup's share of the other half back to pending for the next
     // launch (no one uses that half during this one).  Done last: a store loop
     // before the tile loads made them wait for every earlier load.
@@ -1054,8 +1136,18 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_decode_kernel(FfnArgs a, DGri
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
     const int b = blockIdx.x - g.n_router;
     if (b < 0) router_role(a, g, blockIdx.x);
-    else if (b < g.n_gu_wg) gate_up_role<QT, PREC, TG, rows_per_item<QT, TG>(), PPW>(a, g, b, lds);
-    else down_role<QT, PREC, TG, DPW>(a, g, b - g.n_gu_wg, lds);
+    else if (b < g.n_gu_wg) gate_up_role<QT, PREC, TG, rows_per_item<QT, TG>(), PPW, false>(a, g, b, lds, nullptr);
+    else down_role<QT, PREC, TG, DPW, false>(a, g, b - g.n_gu_wg, lds, nullptr);
+}
+
+// The hit/miss split's launches (one token, the plan given): the same roles,
+// each unit's term kept apart (SplitSel).
+template <int QT, int PREC, int PPW, int DPW>
+__global__ __launch_bounds__(kThreads, 4) void ffn_split_kernel(FfnArgs a, DGrid g, SplitSel s) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+    const int b = blockIdx.x;
+    if (b < g.n_gu_wg) gate_up_role<QT, PREC, 1, rows_per_item<QT, 1>(), PPW, true>(a, g, b, lds, &s);
+    else down_role<QT, PREC, 1, DPW, true>(a, g, b - g.n_gu_wg, lds, &s);
 }
 
 // Workgroups of `kern` the device holds at once (0 if unknown).
@@ -1126,10 +1218,35 @@ hipError_t launch_tg(const DGrid& g, const FfnArgs& a, hipStream_t s) {
     return launch_w<QT, PREC, 4>(g, a, s);
 }
 
-}  // namespace
+// The split variant: grid as launch_k's (no router workgroups), every W_d tile
+// of the step in registers.
+template <int QT, int PREC, int PPW>
+hipError_t launch_split_k(DGrid g, const FfnArgs& a, const SplitSel& sel, hipStream_t s) {
+    constexpr int D = down_per_wave<QT, 1>();
+    static_assert(kWaves * D >= kSplitMaxTiles, "every tile of a split step in registers");
+    auto kern = ffn_split_kernel<QT, PREC, PPW, D>;
+    const int items = g.units_max * (g.n_rg / rows_per_item<QT, 1>());
+    const int cap = resident_capacity((const void*)kern);
+    g.n_router = 0;
+    const int room = cap - g.n_down;
+    g.n_gu_wg = room > 0 ? std::min(items, room) : std::min(items, 64);
+    hipLaunchKernelGGL(kern, dim3(g.n_gu_wg + g.n_down), dim3(kThreads), 0, s, a, g, sel);
+    return hipGetLastError();
+}
 
-hipError_t launch_ffn_decode(const Geom& geo, const FfnArgs& a, int prec, hipStream_t s) {
-    if (a.T < 1 || a.T > kDecodeMaxT || a.E > kMaxE || a.k > 32 || geo.d > kMaxD) return hipErrorInvalidValue;
+template <int QT, int PREC>
+hipError_t launch_split_w(const DGrid& g, const FfnArgs& a, const SplitSel& sel, hipStream_t s) {
+    const int pairs = rows_per_item<QT, 1>() * g.gu_tpr;
+    if (pairs <= kWaves) return launch_split_k<QT, PREC, 1>(g, a, sel, s);
+    if (pairs <= 2 * kWaves) return launch_split_k<QT, PREC, 2>(g, a, sel, s);
+    if (pairs <= 4 * kWaves) return launch_split_k<QT, PREC, 4>(g, a, sel, s);
+    return hipErrorInvalidValue;
+}
+
+// Grid and workspace geometry of a decode launch (false: a shape the kernel
+// does not take).
+bool decode_grid(const Geom& geo, const FfnArgs& a, DGrid* out) {
+    if (a.T < 1 || a.T > kDecodeMaxT || a.E > kMaxE || a.k > 32 || geo.d > kMaxD) return false;
     DGrid g{};
     g.units_max = min(a.T * a.k, a.E) + (a.shared ? 1 : 0);
     // Steps of three or four tokens (the four-token kernel; about 20 units of
@@ -1148,12 +1265,33 @@ hipError_t launch_ffn_decode(const Geom& geo, const FfnArgs& a, int prec, hipStr
     g.copy = decode_copy_floats(a.k, geo.f, a.E);
     g.lg_off = decode_h_rows_floats(a.k, geo.f);
     g.reset_per = (int)((g.half + g.n_down - 1) / g.n_down);
-    if (g.nb_rows < kDecodeMaxT) return hipErrorInvalidValue;
+    if (g.nb_rows < kDecodeMaxT) return false;
+    *out = g;
+    return true;
+}
+
+}  // namespace
+
+hipError_t launch_ffn_decode(const Geom& geo, const FfnArgs& a, int prec, hipStream_t s) {
+    DGrid g{};
+    if (!decode_grid(geo, a, &g)) return hipErrorInvalidValue;
     if (geo.qtype == MOE_Q8_0)
         return prec == MOE_PREC_BF16 ? launch_tg<MOE_Q8_0, MOE_PREC_BF16>(g, a, s)
                                      : launch_tg<MOE_Q8_0, MOE_PREC_F32>(g, a, s);
     return prec == MOE_PREC_BF16 ? launch_tg<MOE_Q4_0, MOE_PREC_BF16>(g, a, s)
                                  : launch_tg<MOE_Q4_0, MOE_PREC_F32>(g, a, s);
+}
+
+hipError_t launch_ffn_split(const Geom& geo, const FfnArgs& a, int prec, const SplitSel& sel, hipStream_t s) {
+    DGrid g{};
+    if (a.T != 1 || a.route != kRoutePlan || !sel.part || !decode_grid(geo, a, &g) ||
+        g.units_max * g.dn_tpr > kSplitMaxTiles)
+        return hipErrorInvalidValue;
+    if (geo.qtype == MOE_Q8_0)
+        return prec == MOE_PREC_BF16 ? launch_split_w<MOE_Q8_0, MOE_PREC_BF16>(g, a, sel, s)
+                                     : launch_split_w<MOE_Q8_0, MOE_PREC_F32>(g, a, sel, s);
+    return prec == MOE_PREC_BF16 ? launch_split_w<MOE_Q4_0, MOE_PREC_BF16>(g, a, sel, s)
+                                 : launch_split_w<MOE_Q4_0, MOE_PREC_F32>(g, a, sel, s);
 }
 
 }  // namespace moe

@@ -161,6 +161,29 @@ __host__ __device__ inline int64_t decode_h_floats(int k, int f, int E, int d) {
 
 hipError_t launch_ffn_decode(const Geom& g, const FfnArgs& a, int prec, hipStream_t s);
 
+// Hit/miss split of a one-token step ("Nanite for Experts", §5.5: the experts
+// already resident run while the missing ones are still being copied in; the
+// results are merged into the token's row).  Two launches of the decode
+// kernel's split variant: the resident units first, the copied ones after
+// their copies.  Each unit's term w (W_d h) comes from the same code in either
+// launch, and the merge adds the terms in plan order with the shared expert
+// last, so y does not depend on which units were resident.
+enum { kSplitAll = 0, kSplitHits = 1, kSplitMisses = 2 };
+constexpr int kSplitMaskWords = 1024 / 32;  // one bit per expert id (E <= 1024)
+struct SplitSel {
+    uint32_t miss[kSplitMaskWords];  // bit e: expert e is copied in by the step
+    int which;     // kSplitAll: every unit, y written;
+                   // kSplitHits: the units whose bit is clear and the shared expert, their terms
+                   //   written to part, y untouched;
+                   // kSplitMisses: the units whose bit is set; the other terms read from part; y written
+    float* part;   // [top_k + 1, d] terms by hidden row (plan position; the shared expert's last)
+};
+inline int64_t split_part_floats(int k, int d) { return (int64_t)(k + 1) * d; }
+// The split variant holds every W_d tile of the step in registers: (units) x
+// (d_ff / 128) tiles at most kSplitMaxTiles.
+constexpr int kSplitMaxTiles = 40;
+hipError_t launch_ffn_split(const Geom& g, const FfnArgs& a, int prec, const SplitSel& sel, hipStream_t s);
+
 // Prefill (T > kDecodeMaxT): bucket tiles on the matrix cores; see ffn_prefill.hip.
 constexpr int kPrefillBM = 64;     // tokens per large tile
 constexpr int kPrefillWide = 128;  // tokens per wide tile (buckets of at least wide_min tokens)

@@ -26,6 +26,9 @@ struct moe_ctx {
     int* err_word = nullptr;
     float* hbuf = nullptr;     // decode hidden rows
     uint32_t* sync = nullptr;  // decode launch count
+    float* split_part = nullptr;  // hit/miss split: the resident units' terms [top_k + 1, d_model]
+    hipEvent_t split_ev = nullptr;  // hit/miss split: the resident units' launch is done
+    int32_t route_pull_layer = -1;  // layer of the last moe_route_pull (-1: none)
 
     // prefill workspace (max_tokens > 4)
     float* ph = nullptr;
@@ -349,6 +352,8 @@ void moe_destroy(moe_ctx* c) {
         if (c->err_word) (void)hipFree(c->err_word);
         if (c->hbuf) (void)hipFree(c->hbuf);
         if (c->sync) (void)hipFree(c->sync);
+        if (c->split_part) (void)hipFree(c->split_part);
+        if (c->split_ev) (void)hipEventDestroy(c->split_ev);
         if (c->ph) (void)hipFree(c->ph);
         if (c->ppart) (void)hipFree(c->ppart);
         if (c->pinv) (void)hipFree(c->pinv);
@@ -406,6 +411,9 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         if (hipMalloc(&c->hbuf, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff, cfg->n_experts, cfg->d_model)) != hipSuccess)
             return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->sync, sizeof(uint32_t) * moe::kSyncInts) != hipSuccess) return cleanup(MOE_ENOMEM);
+        if (hipMalloc(&c->split_part, sizeof(float) * (size_t)moe::split_part_floats(cfg->top_k, cfg->d_model)) !=
+            hipSuccess)
+            return cleanup(MOE_ENOMEM);
         if (hipMalloc(&c->logits_ws, sizeof(float) * (size_t)T * cfg->n_experts) != hipSuccess)
             return cleanup(MOE_ENOMEM);
         if (const int64_t pw = moe::plan_workspace_ints(T, cfg->top_k, cfg->n_experts))
@@ -425,6 +433,10 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         if (hipMemset(c->hbuf, 0xFF, sizeof(float) * (size_t)moe::decode_h_floats(cfg->top_k, cfg->d_ff, cfg->n_experts, cfg->d_model)) != hipSuccess)
             return cleanup(MOE_EHIP);
         if (hipEventCreateWithFlags(&c->release_ev, hipEventDisableTiming) != hipSuccess) return cleanup(MOE_EHIP);
+        // (they order kernels of one device, which fence their own memory: no
+        // system-scope fence)
+        if (hipEventCreateWithFlags(&c->split_ev, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess)
+            return cleanup(MOE_EHIP);
         if (hipHostMalloc((void**)&c->hmirror,
                           sizeof(int32_t) * (size_t)(cfg->n_experts + 1 + 2 * moe::kFusedMaxT * cfg->top_k),
                           hipHostMallocDefault) !=
@@ -590,7 +602,10 @@ moe_status moe_route_pull(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     std::memcpy(experts_out, c->hmirror + 1, sizeof(int32_t) * (size_t)n);
     *n_out = n;
     record_routing(c, layer, (int)T);
-    return moe_slot_pull(c, layer, experts_out, n, payloads, slots_out, miss_out, stream);
+    c->route_pull_layer = -1;
+    if (moe_status st = moe_slot_pull(c, layer, experts_out, n, payloads, slots_out, miss_out, stream)) return st;
+    c->route_pull_layer = layer;
+    return MOE_OK;
 }
 
 moe_status moe_slot_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n,
@@ -1102,6 +1117,59 @@ moe_status moe_expert_ffn(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     p.cap_wide = c->p_wide;
     HIP_TRY(c, moe::launch_ffn_prefill(p, prec, moe::PrefillStreams{s, c->aux, c->fork_ev, c->join_ev}));
     c->last_prefill_prec = prec;
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn_split(moe_ctx* c, int32_t layer, const void* x, int32_t x_dtype, int64_t T,
+                                const moe_plan* plan, const float* topk_w, const void* shared_payload,
+                                int32_t prec, const int32_t* miss_experts, int32_t n_miss, float* y,
+                                moe_stream side, moe_stream stream) {
+    if (moe_status st = need_device(c)) return st;
+    const moe_config& cf = c->cfg;
+    if (moe_status st = ffn_check_args(c, "moe_expert_ffn_split", layer, x, x_dtype, T, 1, plan, topk_w, prec, y))
+        return st;
+    if (T != 1) return fail(c, MOE_EINVAL, "moe_expert_ffn_split: T must be 1");
+    if (layer != c->route_pull_layer)
+        return fail(c, MOE_EINVAL, "moe_expert_ffn_split: layer %d is not that of a moe_route_pull not yet split",
+                    layer);
+    if (n_miss < 0 || n_miss > cf.n_experts || (n_miss > 0 && !miss_experts))
+        return fail(c, MOE_EINVAL, "moe_expert_ffn_split: bad miss list");
+    if ((int64_t)(std::min(cf.top_k, cf.n_experts) + 1) * (cf.d_ff / 128) > moe::kSplitMaxTiles)
+        return fail(c, MOE_EINVAL, "moe_expert_ffn_split: (top_k + 1) * d_ff / 128 exceeds %d", moe::kSplitMaxTiles);
+    moe::SplitSel sel{};
+    for (int32_t i = 0; i < n_miss; i++) {
+        const int32_t e = miss_experts[i];
+        if (e < 0 || e >= cf.n_experts) return fail(c, MOE_EINVAL, "moe_expert_ffn_split: expert id out of range");
+        sel.miss[e >> 5] |= 1u << (e & 31);
+    }
+    sel.part = c->split_part;
+    DeviceGuard dg(cf.device);
+    hipStream_t s = (hipStream_t)stream, sd = (hipStream_t)side;
+    moe::FfnArgs a = ffn_args(c, layer, x, x_dtype, T, plan, topk_w, shared_payload, y);
+    // Units the step takes: its routed experts (at most top_k) and the shared one.
+    if (n_miss > 0 && n_miss < cf.top_k + (shared_payload ? 1 : 0) && sd != s) {
+        // The resident units on `side` as soon as the routing is done (which
+        // follows the context's earlier work on `stream`, the last split's
+        // launches among it: launches of the decode kernel never overlap, as
+        // they share the context's workspace); the fills still pending on
+        // other streams first (copies the routing does not follow), not the
+        // copies `stream` received after the routing.
+        HIP_TRY(c, hipStreamWaitEvent(sd, c->route_ev, 0));
+        for (auto& p : c->fills)
+            if (p.pending && p.s != s && p.s != sd) HIP_TRY(c, hipStreamWaitEvent(sd, p.ev, 0));
+        sel.which = moe::kSplitHits;
+        HIP_TRY(c, moe::launch_ffn_split(c->g, a, prec, sel, sd));
+        HIP_TRY(c, hipEventRecord(c->split_ev, sd));
+        if (moe_status st = wait_pending_fills(c, s)) return st;
+        HIP_TRY(c, hipStreamWaitEvent(s, c->split_ev, 0));
+        sel.which = moe::kSplitMisses;
+    } else {
+        // every unit resident, or every routed one copied in: one launch after the copies
+        if (moe_status st = wait_pending_fills(c, s)) return st;
+        sel.which = moe::kSplitAll;
+    }
+    HIP_TRY(c, moe::launch_ffn_split(c->g, a, prec, sel, s));
+    c->route_pull_layer = -1;  // one split per moe_route_pull
     return MOE_OK;
 }
 

@@ -78,6 +78,7 @@ def _load() -> C.CDLL:
         "moe_slot_bind": (C.c_int, [P, I32, I32, I32, P]),
         "moe_expert_ffn": (C.c_int, [P, I32, P, I32, I64, planp, P, P, I32, P, P]),
         "moe_expert_ffn_static": (C.c_int, [P, I32, P, I32, I64, planp, P, P, I32, P, P]),
+        "moe_expert_ffn_split": (C.c_int, [P, I32, P, I32, I64, planp, P, P, I32, P, I32, P, P, P]),
         "moe_route_ffn": (C.c_int, [P, I32, P, I32, P, P, I64, P, P, planp, P, I32, P, P]),
         "moe_dequant": (C.c_int, [P, P, I32, P, P]),
         "moe_stats": (C.c_int, [P, C.POINTER(C.c_uint64)]),
@@ -100,7 +101,7 @@ _lib = _load()
 EXPORTS = ("moe_payload_bytes", "moe_plan_bytes", "moe_pack_expert", "moe_unpack_expert", "moe_create",
            "moe_destroy", "moe_last_error", "moe_status_string", "moe_route", "moe_plan_union", "moe_route_union",
            "moe_slot_map", "moe_slot_prefetch", "moe_prefetch_stats", "moe_prefetch_next", "moe_slot_fill", "moe_slot_stage", "moe_slot_pull", "moe_route_pull", "moe_slot_release",
-           "moe_slot_bind", "moe_expert_ffn", "moe_expert_ffn_static",
+           "moe_slot_bind", "moe_expert_ffn", "moe_expert_ffn_static", "moe_expert_ffn_split",
            "moe_route_ffn", "moe_dequant", "moe_stats", "moe_check", "moe_page_table", "moe_route_splits", "moe_hidden_rows", "moe_probe_read",
            "moe_probe_mfma", "moe_probe_lds")
 
@@ -470,6 +471,27 @@ def moe_expert_ffn(ctx: Context, layer: int, x, plan: Plan, topk_w, y, shared_pa
     fn = _lib.moe_expert_ffn_static if static else _lib.moe_expert_ffn
     _call(ctx, fn(ctx.handle, layer, _ptr(x), _x_dtype(x), T, C.byref(plan.c), _ptr(topk_w),
                   _ptr(shared_payload), prec, _ptr(y), _stream(stream)))
+
+
+def moe_expert_ffn_split(ctx: Context, layer: int, x, plan: Plan, topk_w, y, miss_experts, shared_payload=None,
+                         prec: int = MOE_PREC_F32, side=None, stream=None) -> None:
+    """Hit/miss split of a one-token step, right after moe_route_pull of the
+    same layer: the resident units on `side`, the copied ones (miss_experts)
+    on `stream` after their copies, merged in plan order."""
+    import torch
+    if tuple(x.shape) != (1, ctx.d_model) or tuple(y.shape) != (1, ctx.d_model) or y.dtype != torch.float32:
+        raise ValueError("x must be [1, d_model]; y float32 [1, d_model]")
+    if topk_w.dtype != torch.float32 or tuple(topk_w.shape) != (1, ctx.top_k):
+        raise ValueError("topk_w must be float32 [1, top_k]")
+    if plan.entries.numel() < ctx.top_k:
+        raise ValueError("plan is too small for T")
+    if shared_payload is not None and shared_payload.numel() * shared_payload.element_size() < ctx.payload_bytes:
+        raise ValueError("shared payload too small")
+    _check_dev(ctx, x, topk_w, y, shared_payload)
+    m = np.ascontiguousarray(np.asarray(miss_experts, dtype=np.int32).reshape(-1))
+    _call(ctx, _lib.moe_expert_ffn_split(ctx.handle, layer, _ptr(x), _x_dtype(x), 1, C.byref(plan.c), _ptr(topk_w),
+                                         _ptr(shared_payload), prec, m.ctypes.data if m.size else None, m.size,
+                                         _ptr(y), _stream(side), _stream(stream)))
 
 
 def moe_route_ffn(ctx: Context, layer: int, x, topk_ids, topk_w, plan: Plan, y, w_router=None, logits_in=None,

@@ -125,6 +125,8 @@ def test_host_only_context_rejects_device_calls():
     assert lib.moe_dequant(ctx.handle, None, 0, None, None) == moe.MOE_EINVAL
     assert lib.moe_route_ffn(ctx.handle, 0, None, 0, None, None, 1, None, None, None, None, 0, None,
                              None) == moe.MOE_EINVAL
+    assert lib.moe_expert_ffn_split(ctx.handle, 0, None, 0, 1, None, None, None, 0, None, 0, None, None,
+                                    None) == moe.MOE_EINVAL
 
 
 @pytest.mark.parametrize("field,value", [("d_model", 96), ("d_ff", 100), ("top_k", 0), ("top_k", 33),
