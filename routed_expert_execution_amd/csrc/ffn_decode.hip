@@ -1036,57 +1036,57 @@ __device__ __forceinline__ void down_role(const FfnArgs& a, const DGrid& g, int 
             a.y[16 * R + r] = ok && L.cnt[0] == a.k ? y : __uint_as_float(0x7FC00000u);
         }
     } else {
-    // The four lanes of a row, then the waves in order.
+        // The four lanes of a row, then the waves in order.
 #pragma unroll
-    for (int t = 0; t < TG; t++) {
-        const float s = cross_row_sum(acc[t]);
-        if (jb == 0) L.red[wave][t][n] = s;
-    }
-    __syncthreads();
-    // The first half of a split row group hands its sums to the second with
-    // device scope (a NaN as the canonical NaN, never the pending word); the
-    // second adds them first, then its own: one fixed order.
-    // (the partial rows follow the copies in each half)
-    uint32_t* prow = (uint32_t*)(a.hbuf + (int64_t)par * g.half + kDecodeCopies * g.copy) + 16 * R;
-    const int tq = threadIdx.x >> 4, rq = threadIdx.x & 15;
-    float y = 0.f;
-    if (threadIdx.x < 16 * a.T)
-        for (int w = 0; w < kWaves; w++) y += L.red[w][tq][rq];
-    if (!last) {
-        if (threadIdx.x < 16 * a.T) {
-            const float v = L.flag[0] && y == y ? y : __uint_as_float(0x7FC00000u);
-            __hip_atomic_store(prow + (int64_t)tq * g.d + rq, __float_as_uint(v), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        for (int t = 0; t < TG; t++) {
+            const float s = cross_row_sum(acc[t]);
+            if (jb == 0) L.red[wave][t][n] = s;
         }
-    } else {
-        bool ok = true;
-        if constexpr (kSplit == 2) {
-            float y0 = 0.f;
-            const uint64_t t1 = wall_clock64();
-            for (;;) {
-                int pend = 0;
-                if (threadIdx.x < 16 * a.T) {
-                    const uint32_t v = __hip_atomic_load(prow + (int64_t)tq * g.d + rq, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-                    pend = v == kPending;
-                    y0 = __uint_as_float(v);
-                }
-                if (!__syncthreads_or(pend) && a.wait_ticks >= 0) break;
-                const int expired =
-                    threadIdx.x == 0 && (a.wait_ticks < 0 || (int64_t)(wall_clock64() - t1) > a.wait_ticks);
-                if (__syncthreads_or(expired)) {
-                    if (threadIdx.x == 0) atomicOr(a.err, kErrSync);
-                    ok = false;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-            y = y0 + y;
-        }
+        __syncthreads();
+        // The first half of a split row group hands its sums to the second with
+        // device scope (a NaN as the canonical NaN, never the pending word); the
+        // second adds them first, then its own: one fixed order.
+        // (the partial rows follow the copies in each half)
+        uint32_t* prow = (uint32_t*)(a.hbuf + (int64_t)par * g.half + kDecodeCopies * g.copy) + 16 * R;
+        const int tq = threadIdx.x >> 4, rq = threadIdx.x & 15;
+        float y = 0.f;
         if (threadIdx.x < 16 * a.T)
-            a.y[(int64_t)tq * g.d + 16 * R + rq] =
-                ok && L.flag[0] && L.cnt[tq] == a.k ? y : __uint_as_float(0x7FC00000u);
-    }
+            for (int w = 0; w < kWaves; w++) y += L.red[w][tq][rq];
+        if (!last) {
+            if (threadIdx.x < 16 * a.T) {
+                const float v = L.flag[0] && y == y ? y : __uint_as_float(0x7FC00000u);
+                __hip_atomic_store(prow + (int64_t)tq * g.d + rq, __float_as_uint(v), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+            bool ok = true;
+            if constexpr (kSplit == 2) {
+                float y0 = 0.f;
+                const uint64_t t1 = wall_clock64();
+                for (;;) {
+                    int pend = 0;
+                    if (threadIdx.x < 16 * a.T) {
+                        const uint32_t v = __hip_atomic_load(prow + (int64_t)tq * g.d + rq, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT);
+                        pend = v == kPending;
+                        y0 = __uint_as_float(v);
+                    }
+                    if (!__syncthreads_or(pend) && a.wait_ticks >= 0) break;
+                    const int expired =
+                        threadIdx.x == 0 && (a.wait_ticks < 0 || (int64_t)(wall_clock64() - t1) > a.wait_ticks);
+                    if (__syncthreads_or(expired)) {
+                        if (threadIdx.x == 0) atomicOr(a.err, kErrSync);
+                        ok = false;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                y = y0 + y;
+            }
+            if (threadIdx.x < 16 * a.T)
+                a.y[(int64_t)tq * g.d + 16 * R + rq] =
+                    ok && L.flag[0] && L.cnt[tq] == a.k ? y : __uint_as_float(0x7FC00000u);
+        }
     }
     // This workgroup's share of the other half back to pending for the next
     // launch (no one uses that half during this one).  Done last: a store loop
