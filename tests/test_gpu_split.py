@@ -25,8 +25,10 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def _setup(n_slots=20):
+def _setup(n_slots=20, qtype=None):
     wl = synth.workload("stack40")
+    if qtype is not None:
+        wl["qtype"] = qtype
     E, k, d, f = wl["E"], wl["k"], wl["d"], wl["f"]
     ctx = H.make_ctx(wl, n_slots=n_slots, max_tokens=1, n_layers=1)
     host = {}
@@ -41,16 +43,21 @@ def _setup(n_slots=20):
     return wl, ctx, host, payload, shared, H.device_payload(ctx, shared)
 
 
-@pytest.mark.parametrize("prec", [moe.MOE_PREC_F32, moe.MOE_PREC_BF16])
-def test_split_matches_oracle_for_any_claimed_split(prec):
-    wl, ctx, host, payload, shared, sh_dev = _setup()
+@pytest.mark.parametrize("qtype,prec,with_shared", [(synth.Q8_0, moe.MOE_PREC_F32, True),
+                                                     (synth.Q8_0, moe.MOE_PREC_BF16, True),
+                                                     (synth.Q4_0, moe.MOE_PREC_F32, True),
+                                                     (synth.Q8_0, moe.MOE_PREC_F32, False)])
+def test_split_matches_oracle_for_any_claimed_split(qtype, prec, with_shared):
+    wl, ctx, host, payload, shared, sh_dev = _setup(qtype=qtype)
+    if not with_shared:
+        shared = sh_dev = None
     E, k, d, f = wl["E"], wl["k"], wl["d"], wl["f"]
     chain = synth.markov_route_sets(synth.rng(wl["seed"], 91, 0), 7, E, k, wl["p_repeat"])
     side = torch.cuda.Stream()
     plan = moe.Plan(ctx, 1)
     seen_partial = seen_none = seen_all = False
     for t in range(len(chain)):
-        _say("split step", t, "prec", prec)
+        _say("split step", t, "qtype", qtype, "prec", prec, "shared", with_shared)
         lg = np.full((1, E), -1.0, np.float32)
         lg[0, chain[t]] = 2.0 + np.arange(k, dtype=np.float32) / 16
         ids = torch.empty(1, k, dtype=torch.int32, device="cuda")
