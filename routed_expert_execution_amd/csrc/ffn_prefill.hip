@@ -485,21 +485,35 @@ __device__ void tile_product(const void* A, int64_t a_pitch, const int (&arow)[R
 
 constexpr int APITCH = 128 + 8;  // bf16 per LDS row: 272 bytes, conflict-free 16-byte reads
 
-// srow[q]: source row of tile row threadIdx.x / 16 + 16 q (a valid row; skeep[q]
-// false for padding rows, staged as zeros).  Waves with wlive false take part in
-// the staging and barriers only.
-template <int QT, bool XB, int R, int MATS, int NW, class BlockAt>
+// srow[q]: source row of tile row (threadIdx.x % 256) / 16 + 16 q (a valid row;
+// skeep[q] false for padding rows, staged as zeros).  Waves with wlive false
+// take part in the staging and barriers only.
+//
+// KH = 2: a workgroup of 8 waves splits K in two halves, waves w and w + 4
+// taking the same 16 columns over the first and the second half (threads 256
+// and up stage the second half's activations); at the end the second half's
+// sums are added to the first's (first + second, a fixed order) and only
+// waves 0-3 hold the result.  It doubles the waves of a launch that has few
+// items, each with half the K steps.
+template <int QT, bool XB, int R, int MATS, int NW, int KH, class BlockAt>
 __device__ void tile_product_lds(const void* A, int64_t a_pitch, const int (&srow)[R], const bool (&skeep)[R],
                                  int nkb, bool wlive, BlockAt blk, f32x4 (&acc)[MATS][R]) {
-    __shared__ __attribute__((aligned(16))) __bf16 abuf[2][16 * R][APITCH];
+    static_assert(KH == 1 || KH == 2, "K in one or two halves");
+    __shared__ __attribute__((aligned(16))) __bf16 abuf[2][KH][16 * R][APITCH];
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-    const int srow_t = threadIdx.x >> 4, scol = (threadIdx.x & 15) * 8;  // staging: 8 columns per thread
+    const int tt = threadIdx.x & 255, th = KH == 1 ? 0 : threadIdx.x >> 8;  // staging thread, its half
+    const int wh = th;                                                       // this wave's half
+    const int srow_t = tt >> 4, scol = (tt & 15) * 8;  // staging: 8 columns per thread
+    // K blocks [kbeg, kend) of a half
+    const int nkh = (nkb + KH - 1) / KH;
+    const int kbeg_w = wh * nkh, kend_w = min(kbeg_w + nkh, nkb);
+    const int kbeg_t = th * nkh, kend_t = min(kbeg_t + nkh, nkb);
 #pragma unroll
     for (int mt = 0; mt < MATS; mt++)
 #pragma unroll
         for (int r = 0; r < R; r++) acc[mt][r] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto fetch_w = [&](int kb0, Raw<QT>(&w)[MATS]) {
-        const int kb = min(kb0 + g, nkb - 1);
+        const int kb = min(kbeg_w + kb0 + g, kend_w - 1);
 #pragma unroll
         for (int mt = 0; mt < MATS; mt++) {
             const uint8_t* t;
@@ -508,14 +522,14 @@ __device__ void tile_product_lds(const void* A, int64_t a_pitch, const int (&sro
             w[mt].load(t, i);
         }
     };
-    // columns [kb0 * 32, kb0 * 32 + 128) of this thread's staging rows; blocks
-    // past nkb (a ragged last step) are zeros
+    // columns [kb0 * 32, kb0 * 32 + 128) of the half of this thread's staging
+    // rows; blocks past the half (a ragged last step) are zeros
     struct AStage {
         uint4 q[R];
     };
     auto fetch_a = [&](int kb0, AStage& st) {
-        const int c = kb0 * kQK + scol;
-        const bool in = (kb0 + scol / kQK) < nkb;
+        const int c = (kbeg_t + kb0) * kQK + scol;
+        const bool in = (kbeg_t + kb0 + scol / kQK) < kend_t;
         const int cc = in ? c : 0;
 #pragma unroll
         for (int q = 0; q < R; q++) {
@@ -533,7 +547,7 @@ __device__ void tile_product_lds(const void* A, int64_t a_pitch, const int (&sro
     };
     auto store_a = [&](int buf, const AStage& st) {
 #pragma unroll
-        for (int q = 0; q < R; q++) *(uint4*)&abuf[buf][srow_t + 16 * q][scol] = st.q[q];
+        for (int q = 0; q < R; q++) *(uint4*)&abuf[buf][th][srow_t + 16 * q][scol] = st.q[q];
     };
     auto compute = [&](int buf, const Raw<QT>(&w)[MATS]) {
 #pragma unroll
@@ -543,7 +557,7 @@ __device__ void tile_product_lds(const void* A, int64_t a_pitch, const int (&sro
             for (int mt = 0; mt < MATS; mt++) b[mt] = b_operand<QT>(w[mt], s);
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                const bf16x8 av = *(const bf16x8*)&abuf[buf][16 * r + n][kQK * g + 8 * s];
+                const bf16x8 av = *(const bf16x8*)&abuf[buf][wh][16 * r + n][kQK * g + 8 * s];
 #pragma unroll
                 for (int mt = 0; mt < MATS; mt++)
                     acc[mt][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[mt], acc[mt][r], 0, 0, 0);
@@ -560,7 +574,7 @@ __device__ void tile_product_lds(const void* A, int64_t a_pitch, const int (&sro
         store_a(buf ^ 1, st);
         lds_barrier();
     };
-    const int n_steps = (nkb + 3) / 4;
+    const int n_steps = (nkh + 3) / 4;
     int kb0 = 0;
     if constexpr (NW == 2) {
         Raw<QT> wa[MATS], wb[MATS];
@@ -597,11 +611,34 @@ __device__ void tile_product_lds(const void* A, int64_t a_pitch, const int (&sro
         if (step < n_steps) one(kb0, step & 1, wa, wc);
         if (step + 1 < n_steps) one(kb0 + 4, (step + 1) & 1, wb, wa);
     }
+    if constexpr (KH == 2) {
+        // the second half's sums through LDS (no wave reads the activations
+        // any more after the last step's barrier), added to the first's
+        float* red = (float*)&abuf[0][0][0][0];
+        static_assert(sizeof(abuf) >= sizeof(float) * 4 * 64 * MATS * R * 4, "the sums fit the buffers");
+        const int w4 = (threadIdx.x >> 6) & 3;
+        if (wh == 1)
+#pragma unroll
+            for (int mt = 0; mt < MATS; mt++)
+#pragma unroll
+                for (int r = 0; r < R; r++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) red[((mt * R + r) * 4 + e) * 256 + w4 * 64 + lane] = acc[mt][r][e];
+        lds_barrier();
+        if (wh == 0)
+#pragma unroll
+            for (int mt = 0; mt < MATS; mt++)
+#pragma unroll
+                for (int r = 0; r < R; r++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) acc[mt][r][e] += red[((mt * R + r) * 4 + e) * 256 + w4 * 64 + lane];
+        lds_barrier();  // (the LDS is the next item's staging)
+    }
 }
 
 // ---- gate/up ------------------------------------------------------------------------
 
-template <int QT, int PREC, bool XB, int R>
+template <int QT, int PREC, bool XB, int R, int KH>
 __device__ void gate_up_item(const PrefillArgs& a, const TileRec& t, const uint8_t* base, int n0, bool wlive) {
     const int lane = threadIdx.x & 63, n = lane & 15;
     const Geom& G = a.g;
@@ -616,11 +653,11 @@ __device__ void gate_up_item(const PrefillArgs& a, const TileRec& t, const uint8
         bool skeep[R];
 #pragma unroll
         for (int q = 0; q < R; q++) {
-            const int m = (threadIdx.x >> 4) + 16 * q;
+            const int m = ((threadIdx.x & 255) >> 4) + 16 * q;
             skeep[q] = m < t.M;
             srow[q] = row_token(a, t, skeep[q] ? m : 0);
         }
-        tile_product_lds<QT, XB, R, 2, 2>(a.x, a.d, srow, skeep, G.nb_d, wlive, blk, acc);
+        tile_product_lds<QT, XB, R, 2, 2, KH>(a.x, a.d, srow, skeep, G.nb_d, wlive, blk, acc);
     } else {
         int arow[R];
         bool alive[R];
@@ -632,7 +669,7 @@ __device__ void gate_up_item(const PrefillArgs& a, const TileRec& t, const uint8
         }
         tile_product<QT, PREC, XB, R, 2>(a.x, a.d, arow, alive, G.nb_d, blk, acc);
     }
-    if (!wlive) return;
+    if (!wlive || (KH == 2 && threadIdx.x >= 256)) return;  // (the second K half's waves hold no result)
     // C register e of row group r: token row 16 r + 4 (lane / 16) + e, feature lane % 16
 #pragma unroll
     for (int r = 0; r < R; r++)
@@ -650,11 +687,13 @@ __device__ void gate_up_item(const PrefillArgs& a, const TileRec& t, const uint8
 
 // BIGT: the 64-token tiles (bf16 mode), else the 16-token tiles.  Each size is
 // its own launch so that the 16-token one keeps to 128 registers (the 64-token
-// one to 168).
-template <int QT, int PREC, bool XB, bool BIGT>
-__global__ __launch_bounds__(256, BIGT ? 3 : (PREC == MOE_PREC_BF16 ? 4 : 3)) void prefill_gate_up_kernel(PrefillArgs a) {
+// one to 168).  KH = 2 (64-token tiles of a call with few of them): 8 waves
+// per workgroup, K in two halves (tile_product_lds).
+template <int QT, int PREC, bool XB, bool BIGT, int KH>
+__global__ __launch_bounds__(256 * KH, KH == 2 ? 1 : BIGT ? 3 : (PREC == MOE_PREC_BF16 ? 4 : 3)) void prefill_gate_up_kernel(PrefillArgs a) {
+    static_assert(KH == 1 || (BIGT && PREC == MOE_PREC_BF16), "K halves: 64-token tiles only");
     const int ngroups = (a.f + COLS - 1) / COLS;
-    const int wave = threadIdx.x >> 6;
+    const int wave = (threadIdx.x >> 6) & (WAVES - 1);
     const int n_items = a.n_tiles[BIGT ? 0 : 1] * ngroups;
     const int32_t* recs = BIGT ? a.sched_big : a.sched_small;
     for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
@@ -666,7 +705,7 @@ __global__ __launch_bounds__(256, BIGT ? 3 : (PREC == MOE_PREC_BF16 ? 4 : 3)) vo
         const int n0 = wlive ? c0 + 16 * wave : a.f - 16;
         const uint8_t* base = tile_base(a, t);
         if (!base) {  // fail closed: NaN hidden rows (the schedule set the error word)
-            if (!wlive) continue;
+            if (!wlive || (KH == 2 && threadIdx.x >= 256)) continue;
             for (int j = threadIdx.x & 63; j < t.M * 16; j += 64) {
                 const int64_t idx = (int64_t)row_slot(a, t, j / 16) * a.f + n0 + j % 16;
                 if (PREC == MOE_PREC_BF16) ((uint16_t*)a.h)[idx] = 0x7FC0;
@@ -674,7 +713,7 @@ __global__ __launch_bounds__(256, BIGT ? 3 : (PREC == MOE_PREC_BF16 ? 4 : 3)) vo
             }
             continue;
         }
-        gate_up_item<QT, PREC, XB, BIGT ? BIG / 16 : 1>(a, t, base, n0, wlive);
+        gate_up_item<QT, PREC, XB, BIGT ? BIG / 16 : 1, KH>(a, t, base, n0, wlive);
     }
 }
 
@@ -699,7 +738,7 @@ __device__ void down_item(const PrefillArgs& a, const TileRec& t, const uint8_t*
             skeep[q] = m < t.M;
             srow[q] = row_slot(a, t, skeep[q] ? m : 0);
         }
-        tile_product_lds<QT, true, R, 1, 3>(a.h, a.f, srow, skeep, G.nb_f, true, blk, acc);
+        tile_product_lds<QT, true, R, 1, 3, 1>(a.h, a.f, srow, skeep, G.nb_f, true, blk, acc);
     } else {
         int arow[R];
         bool alive[R];
@@ -1009,10 +1048,23 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
 // Workgroups per product launch: several per CU; each loops over the items.
 constexpr int kGrid = 2048;
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int cu_count() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <class K>
-hipError_t launch_items(K kernel, int64_t items, const PrefillArgs& a, hipStream_t s) {
+hipError_t launch_items(K kernel, int64_t items, const PrefillArgs& a, hipStream_t s, int threads = 256) {
     if (items <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)std::min<int64_t>(items, kGrid)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)std::min<int64_t>(items, kGrid)), dim3(threads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1059,9 +1111,18 @@ hipError_t launch_qp(const PrefillArgs& a, int big_tiles, int small_tiles, int w
         if (e == hipSuccess && wide_main)
             e = launch_wide(prefill_wide_kernel<QT, XB, false>, (int64_t)wide_tiles * (a.d / WROWS), a, s_wide);
         if (e == hipSuccess)
-            e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, false>, (int64_t)small_tiles * gf, a, s_small);
+            e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, false, 1>, (int64_t)small_tiles * gf, a, s_small);
         if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, false>, (int64_t)small_tiles * gd, a, s_small);
-        if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, true>, (int64_t)big_tiles * gf, a, s_big);
+        // 64-token gate/up items in K halves when the call would have at most
+        // one item per CU (so one wave per SIMD at most) otherwise, counting
+        // 64-token tiles as if every routed and shared row were in one
+        if (e == hipSuccess) {
+            const int64_t est = ((rows + (a.shared ? a.T : 0) + BIG - 1) / BIG) * gf;
+            e = est <= cu_count() ? launch_items(prefill_gate_up_kernel<QT, PREC, XB, true, 2>, (int64_t)big_tiles * gf,
+                                                 a, s_big, 512)
+                                  : launch_items(prefill_gate_up_kernel<QT, PREC, XB, true, 1>, (int64_t)big_tiles * gf,
+                                                 a, s_big);
+        }
         if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, true>, (int64_t)big_tiles * gd, a, s_big);
         if (e == hipSuccess && !wide_main)
             e = launch_wide(prefill_wide_kernel<QT, XB, true>, (int64_t)wide_tiles * (a.f / WFEAT), a, s_wide);
@@ -1070,7 +1131,7 @@ hipError_t launch_qp(const PrefillArgs& a, int big_tiles, int small_tiles, int w
         if (two && e == hipSuccess) e = hipEventRecord(st.join, sb);
         if (two && e == hipSuccess) e = hipStreamWaitEvent(s, st.join, 0);
     } else {
-        if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, false>, (int64_t)small_tiles * gf, a, s);
+        if (e == hipSuccess) e = launch_items(prefill_gate_up_kernel<QT, PREC, XB, false, 1>, (int64_t)small_tiles * gf, a, s);
         if (e == hipSuccess) e = launch_items(prefill_down_kernel<QT, PREC, false>, (int64_t)small_tiles * gd, a, s);
     }
     if (e != hipSuccess) return e;
