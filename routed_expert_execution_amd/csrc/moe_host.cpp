@@ -79,7 +79,9 @@ struct moe_ctx {
     // copies (the default event), or after kernels (moe_slot_pull: kernels of
     // one device fence their own memory, so the event skips the system-scope
     // fence, a cache write-back only the host and other devices would need).
-    struct Pending { hipStream_t s; hipEvent_t ev; bool pending; bool kern; };
+    // A stream's pending fill is the completion mark (below) of its last fill
+    // call (mark, gen); ev is the stream's own event for other uses.
+    struct Pending { hipStream_t s; hipEvent_t ev; bool pending; bool kern; int32_t mark; uint64_t gen; };
     std::vector<Pending> fills;
     // Completion marks of fill calls: a ring of events, each recorded after one
     // call's writes (payloads and page-table entries); a slot remembers the mark
@@ -242,7 +244,7 @@ moe_status fill_event(moe_ctx* c, hipStream_t s, moe_ctx::Pending** out, bool ke
         }
     hipEvent_t ev;
     HIP_TRY(c, hipEventCreateWithFlags(&ev, fill_event_flags(kern)));
-    c->fills.push_back({s, ev, false, kern});
+    c->fills.push_back({s, ev, false, kern, -1, 0});
     *out = &c->fills.back();
     return MOE_OK;
 }
@@ -268,7 +270,7 @@ moe_status order_before_fill(moe_ctx* c, hipStream_t s, const int32_t* slots, co
 // Records the next mark on s after a fill call's writes (kern: written by
 // kernels) and assigns it to the filled slots.
 moe_status mark_filled(moe_ctx* c, hipStream_t s, const int32_t* slots, const uint8_t* use, int32_t n,
-                       bool kern = false) {
+                       bool kern = false, int32_t* mark_out = nullptr) {
     static_assert(kMarks <= 64, "order_before_fill keeps one bit per mark");
     if (c->marks.empty()) c->marks.resize(kMarks);
     const int32_t m = (int32_t)(c->mark_next++ % kMarks);
@@ -285,12 +287,37 @@ moe_status mark_filled(moe_ctx* c, hipStream_t s, const int32_t* slots, const ui
         c->slot_mark[slots[i]] = m;
         c->slot_gen[slots[i]] = k.gen;
     }
+    if (mark_out) *mark_out = m;
     return MOE_OK;
+}
+
+// After a fill call's writes on s: one completion mark for the filled slots,
+// which also stands for the call as s's pending fill (one event recorded on s,
+// not two).
+moe_status fill_done(moe_ctx* c, hipStream_t s, const int32_t* slots, const uint8_t* use, int32_t n,
+                     bool kern = false) {
+    int32_t m = -1;
+    if (moe_status st = mark_filled(c, s, slots, use, n, kern, &m)) return st;
+    moe_ctx::Pending* p = nullptr;
+    if (moe_status st = fill_event(c, s, &p, kern)) return st;
+    p->mark = m;
+    p->gen = c->marks[m].gen;
+    p->pending = true;
+    return MOE_OK;
+}
+
+// The event a wait for pending fill p needs, or null: its mark has been
+// reused, which happens only once the fill it marked has completed.
+hipEvent_t pending_event(const moe_ctx* c, const moe_ctx::Pending& p) {
+    if (p.mark < 0) return p.ev;
+    const moe_ctx::Mark& k = c->marks[p.mark];
+    return k.gen == p.gen ? k.last() : nullptr;
 }
 
 moe_status wait_pending_fills(moe_ctx* c, hipStream_t s) {
     for (auto& p : c->fills) {
-        if (p.pending && p.s != s) HIP_TRY(c, hipStreamWaitEvent(s, p.ev, 0));
+        if (p.pending && p.s != s)
+            if (hipEvent_t e = pending_event(c, p)) HIP_TRY(c, hipStreamWaitEvent(s, e, 0));
         p.pending = false;
     }
     return MOE_OK;
@@ -839,11 +866,7 @@ moe_status moe_slot_fill(moe_ctx* c, int32_t layer, int32_t expert, int32_t slot
     uint8_t* dst = (uint8_t*)cf.slot_pool + (size_t)slot * (size_t)c->g.payload;
     HIP_TRY(c, hipMemcpyAsync(dst, host_payload, (size_t)c->g.payload, hipMemcpyDefault, s));
     HIP_TRY(c, hipMemsetD32Async((hipDeviceptr_t)(c->pt + key), slot, 1, s));
-    if (moe_status st = mark_filled(c, s, &slot, nullptr, 1)) return st;
-    moe_ctx::Pending* p = nullptr;
-    if (moe_status st = fill_event(c, s, &p)) return st;
-    HIP_TRY(c, hipEventRecord(p->ev, s));
-    p->pending = true;
+    if (moe_status st = fill_done(c, s, &slot, nullptr, 1)) return st;
     c->stats[4]++;
     return MOE_OK;
 }
@@ -908,11 +931,7 @@ moe_status moe_slot_stage(moe_ctx* c, int32_t layer, const int32_t* experts, int
         if (moe_status st = put(base + experts[i], sl)) return st;
     }
     HIP_TRY(c, moe::launch_pt_write(c->pt, w, s0));
-    if (moe_status st = mark_filled(c, s0, slots_out, miss_out, n)) return st;
-    moe_ctx::Pending* p = nullptr;
-    if (moe_status st = fill_event(c, s0, &p)) return st;
-    HIP_TRY(c, hipEventRecord(p->ev, s0));
-    p->pending = true;
+    if (moe_status st = fill_done(c, s0, slots_out, miss_out, n)) return st;
     c->stats[4] += (uint64_t)n_miss;
     return MOE_OK;
 }
@@ -973,11 +992,7 @@ moe_status moe_slot_pull(moe_ctx* c, int32_t layer, const int32_t* experts, int3
     }
     if (a.n)
         if (moe_status st = flush()) return st;
-    if (moe_status st = mark_filled(c, s, slots_out, miss_out, n, true)) return st;
-    moe_ctx::Pending* p = nullptr;
-    if (moe_status st = fill_event(c, s, &p, true)) return st;
-    HIP_TRY(c, hipEventRecord(p->ev, s));
-    p->pending = true;
+    if (moe_status st = fill_done(c, s, slots_out, miss_out, n, true)) return st;
     c->stats[4] += (uint64_t)n_miss;
     return MOE_OK;
 }
@@ -1156,7 +1171,8 @@ moe_status moe_expert_ffn_split(moe_ctx* c, int32_t layer, const void* x, int32_
         // copies `stream` received after the routing.
         HIP_TRY(c, hipStreamWaitEvent(sd, c->route_ev, 0));
         for (auto& p : c->fills)
-            if (p.pending && p.s != s && p.s != sd) HIP_TRY(c, hipStreamWaitEvent(sd, p.ev, 0));
+            if (p.pending && p.s != s && p.s != sd)
+                if (hipEvent_t e = pending_event(c, p)) HIP_TRY(c, hipStreamWaitEvent(sd, e, 0));
         sel.which = moe::kSplitHits;
         HIP_TRY(c, moe::launch_ffn_split(c->g, a, prec, sel, sd));
         HIP_TRY(c, hipEventRecord(c->split_ev, sd));
