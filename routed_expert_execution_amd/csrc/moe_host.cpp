@@ -464,9 +464,11 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
         // system-scope fence)
         if (hipEventCreateWithFlags(&c->split_ev, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess)
             return cleanup(MOE_EHIP);
+        // (coherent: the union kernel's stores reach host memory, where the
+        // host polls the count, without waiting for the kernel's end)
         if (hipHostMalloc((void**)&c->hmirror,
                           sizeof(int32_t) * (size_t)(cfg->n_experts + 1 + 2 * moe::kFusedMaxT * cfg->top_k),
-                          hipHostMallocDefault) !=
+                          hipHostMallocCoherent) !=
                 hipSuccess ||
             hipEventCreateWithFlags(&c->route_ev, hipEventDisableTiming) != hipSuccess)
             return cleanup(MOE_EHIP);
@@ -616,15 +618,27 @@ moe_status moe_route_pull(moe_ctx* c, int32_t layer, const void* x, int32_t x_dt
     DeviceGuard dg(cf.device);
     hipStream_t s = (hipStream_t)stream;
     float* lo = logits_out ? logits_out : c->logits_ws;
-    c->hmirror[0] = -1;
+    __atomic_store_n(&c->hmirror[0], -1, __ATOMIC_RELEASE);
     HIP_TRY(c, moe::launch_route_union(x, x_dtype == MOE_BF16, w_router, logits_in, T, cf.n_experts, cf.d_model,
                                        cf.top_k, cf.norm_topk, lo, topk_ids, topk_w, *plan, s, c->hmirror_dev));
     HIP_TRY(c, hipEventRecord(c->route_ev, s));
-    hipError_t q;
-    while ((q = hipEventQuery(c->route_ev)) == hipErrorNotReady) {
+    // The union kernel stores the count last, with system scope, after the
+    // experts, ids and weights: the host proceeds when it sees the count,
+    // before the kernel has ended.  The event reports a failed launch (and,
+    // done with no count seen, a kernel that never wrote it).
+    int32_t n = -1;
+    for (uint32_t spin = 0;; spin++) {
+        n = __atomic_load_n(&c->hmirror[0], __ATOMIC_ACQUIRE);
+        if (n != -1) break;
+        if ((spin & 255) == 255) {
+            const hipError_t q = hipEventQuery(c->route_ev);
+            if (q == hipSuccess) {
+                n = __atomic_load_n(&c->hmirror[0], __ATOMIC_ACQUIRE);
+                break;
+            }
+            if (q != hipErrorNotReady) HIP_TRY(c, q);
+        }
     }
-    HIP_TRY(c, q);
-    const int32_t n = c->hmirror[0];
     if (n < 0 || n > cf.n_experts) return fail(c, MOE_EHIP, "moe_route_pull: routing returned %d experts", n);
     std::memcpy(experts_out, c->hmirror + 1, sizeof(int32_t) * (size_t)n);
     *n_out = n;

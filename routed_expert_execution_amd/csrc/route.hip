@@ -80,11 +80,16 @@ __device__ void topk_union_wg(const float* logits, const RouteUnion& r) {
     if (r.mirror) {  // the units, for a host that maps them (written after the union is complete)
         __syncthreads();
         const int na = *r.n_active;
-        for (int i = threadIdx.x; i <= na; i += blockDim.x) r.mirror[i] = i ? r.experts[i - 1] : na;
+        for (int i = threadIdx.x; i < na; i += blockDim.x) r.mirror[1 + i] = r.experts[i];
         for (int i = threadIdx.x; i < N; i += blockDim.x) {
             r.mirror[1 + r.E + i] = s_ids[i];
             r.mirror[1 + r.E + N + i] = __float_as_int(s_w[i]);
         }
+        // The host polls the count: every word above reaches host memory
+        // first (each thread's own stores, then the barrier), then the count.
+        __threadfence_system();
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_store(r.mirror, na, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 }
 
