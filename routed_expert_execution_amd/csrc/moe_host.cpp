@@ -8,7 +8,9 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <set>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "internal.h"
@@ -48,6 +50,16 @@ struct moe_ctx {
     std::vector<int32_t> slot_of;   // key -> slot, or -1
     std::vector<uint64_t> last;     // recency stamp per slot
     std::vector<int32_t> pin_layer; // layer pinning the slot, or -1
+    // The same state indexed for the map's choices, so that a step costs
+    // O(log n_slots) per miss, not a pass over every slot: slots are taken
+    // lowest first and never freed, so [first_free, n_slots) are the free
+    // ones; the owned slots ordered by last touch (stamps are unique); the
+    // pinned count and each layer's pinned slots.
+    int32_t first_free = 0;
+    std::set<std::pair<uint64_t, int32_t>> lru;
+    int32_t n_pinned = 0;
+    std::vector<std::vector<int32_t>> pinned_of;  // [L]
+    std::vector<char> step_hit;                   // [n_slots] scratch of one map call
     std::vector<int64_t> evicted;   // key evicted by the last map of this slot (fill invalidates it)
     std::vector<char> spec;         // slot filled by a prefetch and not yet used by a demand map
     uint64_t clock = 0;
@@ -291,6 +303,30 @@ moe_status mark_filled(moe_ctx* c, hipStream_t s, const int32_t* slots, const ui
     return MOE_OK;
 }
 
+// Slot state changes that keep the map's indexes (first_free, lru, n_pinned,
+// pinned_of) in step.
+void slot_touch(moe_ctx* c, int32_t s, uint64_t stamp) {
+    c->lru.erase({c->last[s], s});  // (absent for a slot just taken from the free ones)
+    c->last[s] = stamp;
+    c->lru.insert({stamp, s});
+}
+void slot_pin(moe_ctx* c, int32_t s, int32_t layer) {
+    if (c->pin_layer[s] < 0) {
+        c->n_pinned++;
+        c->pinned_of[layer].push_back(s);
+    }
+    c->pin_layer[s] = layer;  // (a slot's pin is always its key's layer)
+}
+// The least recently touched owned slot that is unpinned and not a hit of the
+// current step (step_hit), touched before `horizon`; -1 if there is none.
+int32_t slot_victim(const moe_ctx* c, uint64_t horizon) {
+    for (const auto& e : c->lru) {
+        if (e.first >= horizon) return -1;
+        if (c->pin_layer[e.second] < 0 && !c->step_hit[e.second]) return e.second;
+    }
+    return -1;
+}
+
 // After a fill call's writes on s: one completion mark for the filled slots,
 // which also stands for the call as s's pending fill (one event recorded on s,
 // not two).
@@ -423,6 +459,8 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     c->slot_of.assign(n_keys, -1);
     c->last.assign(cfg->n_slots, 0);
     c->pin_layer.assign(cfg->n_slots, -1);
+    c->pinned_of.assign(cfg->n_layers, {});
+    c->step_hit.assign(cfg->n_slots, 0);
     c->evicted.assign(cfg->n_slots, -1);
     c->spec.assign(cfg->n_slots, 0);
     c->slot_mark.assign(cfg->n_slots, -1);
@@ -661,16 +699,28 @@ moe_status moe_slot_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32
         if (i && experts[i] <= experts[i - 1]) return fail(c, MOE_EINVAL, "moe_slot_map: experts must be ascending and distinct");
     }
     const int64_t base = (int64_t)layer * cf.n_experts;
-    // capacity check first, so a refused step changes nothing
-    int need = 0;
-    std::vector<char> is_hit_slot(cf.n_slots, 0);
+    // capacity check first, so a refused step changes nothing: the slots
+    // neither pinned nor holding one of this step's experts
+    int need = 0, unpinned_hits = 0;
     for (int32_t i = 0; i < n; i++) {
         int32_t s = c->slot_of[base + experts[i]];
-        if (s < 0) need++; else is_hit_slot[s] = 1;
+        if (s < 0) need++;
+        else {
+            c->step_hit[s] = 1;
+            unpinned_hits += c->pin_layer[s] < 0;
+        }
     }
-    int avail = 0;
-    for (int s = 0; s < cf.n_slots; s++) avail += (c->pin_layer[s] < 0 && !is_hit_slot[s]);
-    if (need > avail) return fail(c, MOE_ENOSLOT, "moe_slot_map: %d misses but %d free or unpinned slots", need, avail);
+    const int avail = cf.n_slots - c->n_pinned - unpinned_hits;
+    auto clear_hits = [&]() {
+        for (int32_t i = 0; i < n; i++) {
+            const int32_t s = c->slot_of[base + experts[i]];
+            if (s >= 0) c->step_hit[s] = 0;
+        }
+    };
+    if (need > avail) {
+        clear_hits();
+        return fail(c, MOE_ENOSLOT, "moe_slot_map: %d misses but %d free or unpinned slots", need, avail);
+    }
     for (int32_t i = 0; i < n; i++) {
         const int64_t key = base + experts[i];
         c->clock++;
@@ -683,12 +733,9 @@ moe_status moe_slot_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32
                 c->spec[s] = 0;
             }
         } else {
-            int32_t pick = -1;
-            for (int q = 0; q < cf.n_slots; q++) if (c->owner[q] < 0) { pick = q; break; }
+            int32_t pick = c->first_free < cf.n_slots ? c->first_free++ : -1;  // the lowest free slot
             if (pick < 0) {  // never a slot holding one of this step's experts
-                uint64_t best = UINT64_MAX;
-                for (int q = 0; q < cf.n_slots; q++)
-                    if (c->pin_layer[q] < 0 && !is_hit_slot[q] && c->last[q] < best) { best = c->last[q]; pick = q; }
+                pick = slot_victim(c, UINT64_MAX);
                 c->slot_of[c->owner[pick]] = -1;
                 c->evicted[pick] = c->owner[pick];
                 c->stats[3]++;
@@ -706,10 +753,11 @@ moe_status moe_slot_map(moe_ctx* c, int32_t layer, const int32_t* experts, int32
             c->stats[2] += (uint64_t)c->g.payload;
             miss_out[i] = 1;
         }
-        c->last[s] = c->clock;
-        c->pin_layer[s] = layer;
+        slot_touch(c, s, c->clock);
+        slot_pin(c, s, layer);
         slots_out[i] = s;
     }
+    clear_hits();
     return MOE_OK;
 }
 
@@ -748,12 +796,9 @@ static void prefetch_map(moe_ctx* c, int32_t layer, const int32_t* experts, int3
             if (bytes + c->g.payload > max_bytes) break;
             // a free slot, else the least recently touched unpinned one; never one
             // that a layer in flight has pinned (demand outranks prediction)
-            int32_t pick = -1;
-            for (int q = 0; q < cf.n_slots; q++) if (c->owner[q] < 0) { pick = q; break; }
+            int32_t pick = c->first_free < cf.n_slots ? c->first_free++ : -1;
             if (pick < 0) {
-                uint64_t best = UINT64_MAX;
-                for (int q = 0; q < cf.n_slots; q++)
-                    if (c->pin_layer[q] < 0 && c->last[q] < best && c->last[q] < horizon) { best = c->last[q]; pick = q; }
+                pick = slot_victim(c, horizon);
                 if (pick < 0) break;
                 c->slot_of[c->owner[pick]] = -1;
                 c->evicted[pick] = c->owner[pick];
@@ -777,7 +822,7 @@ static void prefetch_map(moe_ctx* c, int32_t layer, const int32_t* experts, int3
                 continue;
             }
         }
-        c->last[s] = ++c->clock;  // predicted: kept until the demand that should follow
+        slot_touch(c, s, ++c->clock);  // predicted: kept until the demand that should follow
         slots_out[done] = s;
     }
     *n_done = done;
@@ -1015,7 +1060,12 @@ moe_status moe_slot_release(moe_ctx* c, int32_t layer, moe_stream compute) {
     if (!c) return MOE_EINVAL;
     const moe_config& cf = c->cfg;
     if (layer < 0 || layer >= cf.n_layers) return fail(c, MOE_EINVAL, "moe_slot_release: bad layer");
-    for (int s = 0; s < cf.n_slots; s++) if (c->pin_layer[s] == layer) c->pin_layer[s] = -1;
+    for (const int32_t s : c->pinned_of[layer])
+        if (c->pin_layer[s] == layer) {
+            c->pin_layer[s] = -1;
+            c->n_pinned--;
+        }
+    c->pinned_of[layer].clear();
     if (!c->host_only) {
         DeviceGuard dg(cf.device);
         HIP_TRY(c, hipEventRecord(c->release_ev, (hipStream_t)compute));

@@ -76,6 +76,45 @@ def test_slot_manager_matches_lru_model_on_markov_trace():
         assert st["bytes_staged"] == st["misses"] * ctx.payload_bytes
 
 
+def test_slot_manager_matches_lru_model_with_held_pins_and_refusals():
+    """Random steps on a tight pool where layers stay pinned for a while (two
+    or three layers in flight), so some steps are refused: every slot, miss,
+    refusal and counter matches the model, and a refused step changes
+    nothing."""
+    rng = np.random.default_rng(17)
+    for n_slots, E, n_layers in ((12, 16, 4), (24, 32, 6)):
+        ctx = _host_ctx(n_layers, E, n_slots)
+        model = LruModel(n_slots, ctx.payload_bytes)
+        held = []  # layers mapped and not yet released, oldest first
+        refusals = 0
+        for step in range(400):
+            layer = int(rng.integers(n_layers))
+            if layer in held:
+                moe.moe_slot_release(ctx, layer)
+                model.release(layer)
+                held.remove(layer)
+            ex = sorted(rng.choice(E, size=int(rng.integers(1, 9)), replace=False).tolist())
+            try:
+                ms, mm, _ = model.map(layer, ex)
+            except NoSlot:
+                with pytest.raises(moe.MoeError) as ei:
+                    moe.moe_slot_map(ctx, layer, ex)
+                assert ei.value.status == moe.MOE_ENOSLOT
+                refusals += 1
+            else:
+                slots, miss = moe.moe_slot_map(ctx, layer, ex)
+                assert list(slots) == ms and list(miss) == mm, step
+                held.append(layer)
+            while len(held) > int(rng.integers(1, 5)):
+                old = held.pop(0)
+                moe.moe_slot_release(ctx, old)
+                model.release(old)
+        st = moe.moe_stats(ctx)
+        c = model.counters()
+        assert (st["hits"], st["misses"], st["evictions"]) == (c["hits"], c["misses"], c["evictions"])
+        assert refusals > 0 and st["evictions"] > 0
+
+
 def test_slot_manager_keeps_the_steps_own_experts():
     """The least recently touched slot holds an expert that the same step lists
     later: the library, like the model, evicts the next one instead."""
