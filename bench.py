@@ -35,6 +35,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -650,6 +651,8 @@ def run_stack(args, torch, moe, synth) -> int:
             "bytes_staged_equals_misses_x_payload": staged == misses * pb,
             "h2d_GBps_achieved": staged / wall / 1e9,
             "ffn_us_mean": float(ffn.mean()),
+            "ffn_us_p50": float(np.median(ffn)),
+            "ffn_us_max": float(ffn.max()),
             "ffn_GBps": ffn_gbs,
             "layer_steps_timed": len(ffn_ev),
             "pull": pull,
@@ -739,6 +742,12 @@ def main() -> int:
 
     import synth
     from routed_expert_execution_amd import moe
+
+    # No cyclic garbage collection while measuring (as timeit does): a full
+    # collection of this process's heap stops the host for tens of ms, and a
+    # stop between a step's launches leaves the GPU idle inside its timing.
+    gc.collect()
+    gc.disable()
 
     if args.workload == "replay":
         return replay_policies(args, synth, moe)
