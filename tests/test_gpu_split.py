@@ -104,6 +104,45 @@ def test_split_matches_oracle_for_any_claimed_split(qtype, prec, with_shared):
     assert moe.moe_check(ctx) == moe.MOE_OK
 
 
+def test_split_is_slot_independent():
+    """The same steps through two pools whose slots hold the experts in
+    different places (the second pool larger and first filled with other
+    experts): bitwise the same outputs."""
+    outs = []
+    for n_slots, warm in ((20, []), (33, [200, 201, 202, 203, 204, 205, 206])):
+        wl, ctx, host, payload, shared, sh_dev = _setup(n_slots=n_slots)
+        E, k, d = wl["E"], wl["k"], wl["d"]
+        if warm:
+            table = moe.payload_table(ctx, [payload(e) if e in warm else None for e in range(E)])
+            moe.moe_slot_pull(ctx, 0, warm, table)
+            moe.moe_slot_release(ctx, 0)
+        chain = synth.markov_route_sets(synth.rng(wl["seed"], 93, 0), 5, E, k, wl["p_repeat"])
+        side = torch.cuda.Stream()
+        plan = moe.Plan(ctx, 1)
+        ys, slots_seen = [], []
+        for t in range(len(chain)):
+            lg = np.full((1, E), -1.0, np.float32)
+            lg[0, chain[t]] = 2.0 + np.arange(k, dtype=np.float32) / 16
+            ids = torch.empty(1, k, dtype=torch.int32, device="cuda")
+            w = torch.empty(1, k, dtype=torch.float32, device="cuda")
+            step = set(int(e) for e in chain[t])
+            table = moe.payload_table(ctx, [payload(e) if e in step else None for e in range(E)])
+            x = H.torch_x(synth.activations(wl["seed"], 1, d, "bf16", t, 6), "bf16")
+            ex, sl, miss = moe.moe_route_pull(ctx, 0, ids, w, plan, table, logits_in=torch.from_numpy(lg).cuda())
+            y = torch.empty(1, d, dtype=torch.float32, device="cuda")
+            moe.moe_expert_ffn_split(ctx, 0, x, plan, w, y, ex[miss], shared_payload=sh_dev, side=side)
+            moe.moe_slot_release(ctx, 0)
+            ys.append(y)
+            slots_seen.append(list(sl))
+        torch.cuda.synchronize()
+        assert moe.moe_check(ctx) == moe.MOE_OK
+        outs.append(([y.cpu().numpy() for y in ys], slots_seen))
+    (ya, sa), (yb, sb) = outs
+    assert sa != sb  # the experts did land in other slots
+    for t, (a, b) in enumerate(zip(ya, yb)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), t
+
+
 def test_split_refusals():
     wl, ctx, host, payload, shared, sh_dev = _setup()
     E, k, d = wl["E"], wl["k"], wl["d"]
