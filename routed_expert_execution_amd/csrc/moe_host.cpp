@@ -50,11 +50,12 @@ struct moe_ctx {
     std::vector<int32_t> slot_of;   // key -> slot, or -1
     std::vector<uint64_t> last;     // recency stamp per slot
     std::vector<int32_t> pin_layer; // layer pinning the slot, or -1
-    // The same state indexed for the map's choices, so that a step costs
-    // O(log n_slots) per miss, not a pass over every slot: slots are taken
-    // lowest first and never freed, so [first_free, n_slots) are the free
-    // ones; the owned slots ordered by last touch (stamps are unique); the
-    // pinned count and each layer's pinned slots.
+    // The same state indexed for the map's choices, so that a miss costs
+    // O(log n_slots) plus the pinned or same-step slots the LRU walk skips,
+    // not a pass over every slot: slots are taken lowest first and never
+    // freed, so [first_free, n_slots) are the free ones; the owned slots
+    // ordered by last touch (stamps are unique); the pinned count and each
+    // layer's pinned slots.
     int32_t first_free = 0;
     std::set<std::pair<uint64_t, int32_t>> lru;
     int32_t n_pinned = 0;
